@@ -1,0 +1,343 @@
+"""Pins for the CPU oracle: each test ties it to something other than itself.
+
+Kinds of pin used: hand-worked cases (tests/golden/), closed forms, brute force
+on tiny inputs, special cases that reduce to a library routine
+(torch scaled_dot_product_attention in float64, torch's e4m3fn cast), and
+invariants of the definition.  Each is chosen so that a plausible slip in the
+oracle (dropped term, wrong sign or index, transposed operand, off-by-one
+window, wrong tie order, wrong GQA map) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_decode_full_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------- golden
+def test_page_constants_match_oracle_defaults():
+    c = _load("page_constants.json")
+    import inspect
+    sig = inspect.signature(oracle.hybrid_block_token)
+    assert sig.parameters["window"].default == c["window"]["value"]
+    assert sig.parameters["topk"].default == c["global_tokens"]["value"]
+    assert c["window"]["value"] + c["global_tokens"]["value"] == c["budget"]["value"]
+    assert sig.parameters["block"].default == c["block_baseline"]["block_size"]
+    assert sig.parameters["n_blocks"].default == c["block_baseline"]["n_blocks"]
+    assert c["block_baseline"]["block_size"] * c["block_baseline"]["n_blocks"] == c["budget"]["value"]
+
+
+@pytest.mark.parametrize("case", _load("worked_cases.json")["token_cases"])
+def test_select_hand_worked(case):
+    got = oracle.select_tokens(np.array(case["s"]), case["window"], case["topk"])
+    assert got.tolist() == case["idx"]
+
+
+@pytest.mark.parametrize("case", _load("worked_cases.json")["block_cases"])
+def test_block_hand_worked(case):
+    got = oracle.block_select(np.array(case["s"]), case["block"], case["n_blocks"])
+    assert got.tolist() == case["idx"]
+
+
+def test_attention_hand_worked():
+    c = _load("worked_cases.json")["attention_case"]
+    q = np.array([c["q"]])
+    K = np.array([[0.0, 0, 0, 0], [math.log(3.0), 0, 0, 0]])
+    V = np.array(c["V"])
+    out, P = oracle.full_attention(q, K, V, c["sm_scale"])
+    assert np.allclose(P[0], c["P"], rtol=0, atol=1e-15)
+    assert np.allclose(out[0], c["out"], rtol=0, atol=1e-14)
+    # a second head with the opposite query: probabilities swap; group score sums to G
+    q2 = np.array([c["q"], [-x for x in c["q"]]])
+    _, P2 = oracle.full_attention(q2, K, V, c["sm_scale"])
+    assert np.allclose(P2[1], [0.75, 0.25], atol=1e-15)
+    assert np.allclose(oracle.group_scores(P2), [1.0, 1.0], atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- helpers
+def _rand_group(rng, G, n, D=128):
+    q = rng.standard_normal((G, D))
+    K = rng.standard_normal((n, D))
+    V = rng.standard_normal((n, D))
+    return q, K, V
+
+
+def _sdpa(q, K, V, scale):
+    """torch SDPA in float64 on CPU; q [Hq, D], K/V [Hkv, n, D] with GQA h -> h // G."""
+    Hq = q.shape[0]
+    Hkv = K.shape[0]
+    G = Hq // Hkv
+    qt = torch.from_numpy(q).reshape(1, Hq, 1, -1)
+    Kt = torch.from_numpy(K).repeat_interleave(G, dim=0).unsqueeze(0).contiguous()
+    Vt = torch.from_numpy(V).repeat_interleave(G, dim=0).unsqueeze(0).contiguous()
+    o = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, scale=scale)
+    return o.reshape(Hq, -1).numpy()
+
+
+def _brute_top(s, window, topk):
+    """Rank count: t is kept iff fewer than kk candidates beat it (greater score, or
+    equal score and lower index).  Pure loops, independent of any sort."""
+    n = len(s)
+    w0 = max(0, n - window)
+    kk = min(topk, w0)
+    keep = []
+    for t in range(w0):
+        beat = 0
+        for u in range(w0):
+            if s[u] > s[t] or (s[u] == s[t] and u < t):
+                beat += 1
+        if beat < kk:
+            keep.append(t)
+    return sorted(keep + list(range(w0, n)))
+
+
+# ----------------------------------------------------------------------------- P1
+@pytest.mark.parametrize("n", [1, 5, 127, 128, 129, 1151, 1152])
+def test_p1_short_context_selects_all_and_sparse_equals_dense(n):
+    rng = np.random.default_rng(n)
+    q, K, V = _rand_group(rng, 4, n)
+    out, P = oracle.full_attention(q, K, V, 1 / math.sqrt(128))
+    idx = oracle.select_tokens(oracle.group_scores(P), 128, 1024)
+    assert idx[:n].tolist() == list(range(n)) and np.all(idx[n:] == -1)
+    qs = rng.standard_normal(q.shape)
+    dense, _ = oracle.full_attention(qs, K, V, 1 / math.sqrt(128))
+    sp = oracle.sparse_attention(qs, K, V, idx, 1 / math.sqrt(128))
+    assert np.max(np.abs(sp - dense)) <= 1e-12
+
+
+def test_p1_boundary_1153_drops_exactly_one():
+    n = 1153
+    rng = np.random.default_rng(7)
+    q, K, V = _rand_group(rng, 2, n)
+    _, P = oracle.full_attention(q, K, V, 1 / math.sqrt(128))
+    s = oracle.group_scores(P)
+    idx = oracle.select_tokens(s, 128, 1024)
+    assert np.all(idx >= 0) and len(set(idx.tolist())) == 1152
+    missing = sorted(set(range(n)) - set(idx.tolist()))
+    assert len(missing) == 1
+    cand = np.arange(n - 128)
+    assert missing[0] == cand[np.lexsort((-cand, s[cand]))][0]  # lowest score, higher index on a tie
+
+
+# ----------------------------------------------------------------------------- P2
+@pytest.mark.parametrize("n,window,topk", [(3000, 128, 1024), (200, 128, 16), (129, 128, 1024),
+                                           (64, 8, 16), (10, 16, 4)])
+def test_p2_window_always_selected(n, window, topk):
+    rng = np.random.default_rng(n + window)
+    s = rng.random(n)
+    s[-window:] = 0.0                            # the window must win even with zero scores
+    idx = oracle.select_tokens(s, window, topk)
+    got = set(idx[idx >= 0].tolist())
+    assert set(range(max(0, n - window), n)) <= got
+    assert len(got) == min(n, window + topk)
+    valid = idx[idx >= 0]
+    assert np.all(np.diff(valid) > 0)            # ascending, no duplicates
+    assert np.all(idx[len(valid):] == -1)
+
+
+# ----------------------------------------------------------------------------- P3
+def test_p3_probabilities_sum_to_one_and_group_sum_to_G():
+    rng = np.random.default_rng(3)
+    for G, n in [(8, 5000), (1, 17), (4, 1)]:
+        q, K, V = _rand_group(rng, G, n)
+        q *= 3.0
+        _, P = oracle.full_attention(q, K, V, 1 / math.sqrt(128))
+        assert np.all(P >= 0)
+        assert np.max(np.abs(P.sum(axis=1) - 1.0)) <= 1e-12
+        assert abs(oracle.group_scores(P).sum() - G) <= 1e-11
+
+
+# ----------------------------------------------------------------------------- P4
+@pytest.mark.parametrize("window,topk", [(8, 16), (0, 5), (16, 48), (128, 1024)])
+@pytest.mark.parametrize("dup", [False, True])
+def test_p4_bruteforce_rank_count(window, topk, dup):
+    rng = np.random.default_rng(window * 7 + topk + int(dup))
+    n = 64
+    q, K, V = _rand_group(rng, 8, n, D=16)
+    if dup:                                      # planted duplicate rows -> exactly equal scores
+        for a, b in [(3, 40), (5, 6), (10, 11), (10, 12), (0, 63)]:
+            K[b] = K[a]
+    _, P = oracle.full_attention(q, K, V, 0.25)
+    s = oracle.group_scores(P)
+    idx = oracle.select_tokens(s, window, topk)
+    assert idx[idx >= 0].tolist() == _brute_top(s, window, topk)
+
+
+def test_p4_bruteforce_with_quantised_ties():
+    rng = np.random.default_rng(11)
+    for trial in range(20):
+        s = np.round(rng.random(64) * 4) / 4         # many exact ties
+        for window, topk in [(4, 10), (0, 31), (20, 30)]:
+            idx = oracle.select_tokens(s, window, topk)
+            assert idx[idx >= 0].tolist() == _brute_top(s, window, topk)
+
+
+# ----------------------------------------------------------------------------- P5
+@pytest.mark.parametrize("Hq,Hkv,n", [(16, 2, 300), (32, 4, 77), (8, 8, 5)])
+def test_p5_full_attention_matches_torch_sdpa(Hq, Hkv, n):
+    rng = np.random.default_rng(Hq + n)
+    q = rng.standard_normal((Hq, 128))
+    K = rng.standard_normal((Hkv, n, 128))
+    V = rng.standard_normal((Hkv, n, 128))
+    ref = _sdpa(q, K, V, 1 / math.sqrt(128))
+    G = Hq // Hkv
+    for g in range(Hkv):
+        out, _ = oracle.full_attention(q[g * G:(g + 1) * G], K[g], V[g], 1 / math.sqrt(128))
+        assert np.max(np.abs(out - ref[g * G:(g + 1) * G])) <= 1e-12
+
+
+def test_p5_sparse_matches_sdpa_on_gathered_rows():
+    rng = np.random.default_rng(55)
+    n, G = 2000, 8
+    q, K, V = _rand_group(rng, G, n)
+    _, P = oracle.full_attention(q, K, V, 1 / math.sqrt(128))
+    idx = oracle.select_tokens(oracle.group_scores(P), 128, 1024)
+    qs = rng.standard_normal((G, 128))
+    I = idx[idx >= 0]
+    ref = _sdpa(qs, K[I][None], V[I][None], 1 / math.sqrt(128))
+    got = oracle.sparse_attention(qs, K, V, idx, 1 / math.sqrt(128))
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_p5_gqa_map_is_contiguous_groups():
+    """Heads of group g must use KV head g (h // G), not h % Hkv."""
+    w = wl.Workload("t", 1, 1, 8, 2, ctx_lens=[300], seed=9)
+    inp = wl.make_inputs(w)
+    res = oracle.hybrid_block_token(inp, 0, 0, window=16, topk=32)
+    q = oracle.bf16_to_f64(inp["q_full"][0, 0])
+    K = np.stack([oracle.bf16_to_f64(inp["k"][0, g]) for g in range(2)])
+    V = np.stack([oracle.bf16_to_f64(inp["v"][0, g]) for g in range(2)])
+    ref = _sdpa(q, K, V, inp["sm_scale"])
+    assert np.max(np.abs(res["out_full"] - ref)) <= 1e-12
+
+
+# ----------------------------------------------------------------------------- P6
+@pytest.mark.parametrize("mode", ["identical_keys", "zero_q"])
+def test_p6_uniform_attention_closed_form(mode):
+    n, G = 3000, 8
+    rng = np.random.default_rng(6)
+    q, K, V = _rand_group(rng, G, n)
+    if mode == "identical_keys":
+        K[:] = K[0]
+    else:
+        q[:] = 0.0
+    out, P = oracle.full_attention(q, K, V, 1 / math.sqrt(128))
+    assert np.max(np.abs(P - 1.0 / n)) <= 1e-15
+    s = oracle.group_scores(P)
+    assert np.max(np.abs(s - G / n)) <= 1e-14
+    idx = oracle.select_tokens(s, 128, 1024)
+    expect = list(range(1024)) + list(range(n - 128, n))    # lowest indices win every tie
+    assert idx.tolist() == expect
+    assert np.max(np.abs(out - V.mean(axis=0)[None])) <= 1e-12
+
+
+# ----------------------------------------------------------------------------- P7
+def test_p7_dominant_needle_one_hot():
+    n, G = 5000, 8
+    rng = np.random.default_rng(77)
+    q, K, V = _rand_group(rng, G, n)
+    pos = 1234
+    u = q.sum(axis=0)
+    K[pos] = 100.0 * u / np.linalg.norm(u) * math.sqrt(128)
+    out, P = oracle.full_attention(q, K, V, 1 / math.sqrt(128))
+    assert np.all(P[:, pos] > 1 - 1e-9)
+    assert np.max(np.abs(out - V[pos][None])) <= 1e-6
+    idx = oracle.select_tokens(oracle.group_scores(P), 128, 1024)
+    assert pos in idx.tolist()
+
+
+# ----------------------------------------------------------------------------- P8
+def test_p8_single_head_selection_is_logit_order():
+    """G = 1: softmax is monotone, so the top-k by probability is the top-k by raw logit."""
+    rng = np.random.default_rng(8)
+    n = 6000
+    q, K, V = _rand_group(rng, 1, n)
+    _, P = oracle.full_attention(q, K, V, 1 / math.sqrt(128))
+    idx = oracle.select_tokens(oracle.group_scores(P), 128, 1024)
+    logits = (K[: n - 128] @ q[0])
+    top = np.argsort(-logits, kind="stable")[:1024]
+    expect = sorted(top.tolist()) + list(range(n - 128, n))
+    assert idx.tolist() == expect
+
+
+# ----------------------------------------------------------------------------- P9
+def test_p9_e4m3fn_table_matches_torch_and_spec():
+    tab = oracle.e4m3fn_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(tab), nan)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(tab[~nan], ref[~nan])
+    assert tab[0x7E] == 448.0 and tab[0x08] == 2.0 ** -6 and tab[0x01] == 2.0 ** -9
+    assert tab[0x80] == 0.0 and math.copysign(1, tab[0x80]) == -1 and tab[0xFE] == -448.0
+
+
+def test_p9_dequant_is_code_times_scale():
+    codes = np.array([[0x38, 0x40, 0xB8, 0x01]], dtype=np.uint8)     # 1, 2, -1, 2^-9
+    got = oracle.dequant_fp8(codes, np.array([0.5], dtype=np.float32))
+    assert got.tolist() == [[0.5, 1.0, -0.5, 2.0 ** -10]]
+
+
+# ----------------------------------------------------------------------------- P10
+def test_p10_block_bruteforce_tiny():
+    rng = np.random.default_rng(10)
+    for trial in range(30):
+        n = int(rng.integers(1, 256))
+        s = rng.random(n)
+        if trial % 3 == 0:
+            s = np.round(s * 4) / 4          # dyadic: block sums exact in any order
+        block, nb = 16, 4
+        got = oracle.block_select(s, block, nb)
+        # brute force over every subset of min(nb, blocks) blocks: best total mass set with
+        # the tie rule is the greedy rank count per block
+        nblk = (n + block - 1) // block
+        mass = [sum(s[b * block: min((b + 1) * block, n)]) for b in range(nblk)]
+        keep = [b for b in range(nblk)
+                if sum(1 for c in range(nblk) if mass[c] > mass[b] or (mass[c] == mass[b] and c < b))
+                < min(nb, nblk)]
+        toks = [t for b in sorted(keep) for t in range(b * block, min((b + 1) * block, n))]
+        assert got[got >= 0].tolist() == toks
+        assert np.all(got[len(toks):] == -1)
+
+
+def test_p10_short_context_selects_every_block():
+    n = 1152
+    s = np.random.default_rng(1).random(n)
+    got = oracle.block_select(s, 64, 18)
+    assert got.tolist() == list(range(n))
+
+
+# ----------------------------------------------------------------------------- chunk / workload
+def test_chunk_positions_are_causal():
+    """R8: query token j of a chunk sees exactly ctx_len - Lq + j + 1 positions."""
+    w = wl.Workload("t", 2, 4, 8, 2, ctx_lens=[200, 150], seed=4)
+    inp = wl.make_inputs(w)
+    for b in range(2):
+        for j in range(4):
+            r = oracle.hybrid_block_token(inp, b, j, window=16, topk=32)
+            assert r["n"] == inp["ctx_len"][b] - 4 + j + 1
+            for g in range(2):
+                assert len(r["s"][g]) == r["n"]
+                assert r["idx"][g].max() == r["n"] - 1
+
+
+def test_fp8_path_uses_dequantised_values():
+    w = wl.Workload("t", 1, 1, 8, 2, ctx_lens=[500], kv_dtype="fp8", n_needles=4, seed=12)
+    inp = wl.make_inputs(w)
+    K, V = oracle.kv_rows(inp, 0, 1, 500)
+    tab = oracle.e4m3fn_table()
+    assert K[17, 3] == tab[inp["k"][0, 1, 17, 3]] * float(inp["k_scale"][0, 1, 17])
+    # the per-row scale maps the largest magnitude to 448 (up to fp32 rounding of the scale)
+    assert np.all(np.abs(np.abs(K).max(axis=1) / inp["k_scale"][0, 1] - 448) <= 448 * 2 ** -3)
