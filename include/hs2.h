@@ -1,0 +1,148 @@
+/*
+ * hs2.h -- C ABI of the HySparse2 Hybrid-Block decode library for MI355X (gfx950).
+ *
+ * What it computes (HySparse2 article, Xiaomi MiMo, reprinted by IT Home; the
+ * AIHOT.vn translation numbers its sections 01-05):
+ *   section 02, "KV Reuse": a Hybrid Block is one Full Attention layer followed
+ *     by several Sparse Attention layers.  While the full layer computes its own
+ *     output it picks important positions from its attention scores, and the
+ *     sparse layers reuse its KV cache and its index set.
+ *   section 03: selection is per token (not per block).  The 128 most recent
+ *     tokens are always kept, plus 1,024 global tokens from outside that window,
+ *     and both go through one sparse attention computation over the shared cache.
+ * The article does not say how scores become a selection.  This library takes,
+ * per KV head, the softmax probabilities of the full layer (normalised over
+ * every visible position) summed over the query heads of that KV head's GQA
+ * group, and keeps the top-k of them with ties going to the lower position.
+ *
+ * Conventions shared by every call
+ *   - Pointers named q, k, v, k_scale, v_scale, ctx_len, idx, out, probs and
+ *     workspace are DEVICE pointers; `desc` and `bytes` are HOST pointers.
+ *   - The caller allocates and owns every buffer, including the workspace.  The
+ *     library allocates nothing, never synchronises, and keeps no pointer after
+ *     a call returns.  Work is enqueued on `stream`; buffers must stay valid
+ *     until the stream has executed it.
+ *   - Every argument is checked on the host before anything is enqueued.  A
+ *     failed check returns its status and enqueues nothing.  A launch failure
+ *     returns HS2_ERR_LAUNCH.  Nothing is printed and nothing aborts.
+ *   - The library is stateless apart from the optional kernel timer below;
+ *     concurrent calls on different streams need distinct workspaces and
+ *     outputs.
+ *
+ * Layouts (row-major; B batch, Lq query tokens per sequence, Hq query heads,
+ * Hkv KV heads, G = Hq / Hkv, D = head_dim = 128, cap = kv_capacity,
+ * S = window + topk in token mode or block_size * n_blocks in block mode):
+ *   q        [B, Lq, Hq, D]    bfloat16                               16-B aligned
+ *   k, v     [B, Hkv, cap, D]  bfloat16, or OCP E4M3FN bytes          16-B aligned
+ *   k_scale, v_scale [B, Hkv, cap] float32, one per token (E4M3FN only; NULL for bf16)
+ *   ctx_len  [B] int32: visible positions of sequence b, INCLUDING its Lq query
+ *            tokens, which occupy positions ctx_len[b]-Lq .. ctx_len[b]-1.  Query
+ *            token j sees positions [0, ctx_len[b]-Lq+j] (causal inside the chunk).
+ *            Values are clamped to [0, cap] on the device.
+ *   out      [B, Lq, Hq, D]    float32                                16-B aligned
+ *   idx      [B, Lq, Hkv, S]   int32, ascending positions, -1 padding at the end
+ *   probs    [B, Lq, Hkv, cap] float32 group-summed probabilities (optional)
+ */
+#ifndef HS2_H
+#define HS2_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hs2_status {
+  HS2_OK = 0,
+  HS2_ERR_INVALID_ARG = 1,   /* null pointer, bad size or inconsistent descriptor    */
+  HS2_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head_dim != 128, G > 8 ..) */
+  HS2_ERR_WORKSPACE = 3,     /* workspace_bytes smaller than hs2_workspace_size()      */
+  HS2_ERR_ALIGNMENT = 4,     /* a device pointer is not aligned as required            */
+  HS2_ERR_LAUNCH = 5         /* the HIP runtime refused a launch                        */
+} hs2_status;
+
+enum { HS2_KV_BF16 = 0, HS2_KV_FP8_E4M3FN = 1 };
+enum { HS2_SELECT_TOKEN = 0, HS2_SELECT_BLOCK = 1 };
+
+typedef struct hs2_attn_desc {
+  int32_t batch;          /* B >= 1                                                    */
+  int32_t q_len;          /* Lq >= 1: 1 at decode, e.g. 64 for an appended chunk       */
+  int32_t n_q_heads;      /* Hq                                                         */
+  int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0 and G = Hq / Hkv <= 8                    */
+  int32_t head_dim;       /* must be 128                                                */
+  int32_t kv_dtype;       /* HS2_KV_BF16 or HS2_KV_FP8_E4M3FN                            */
+  int64_t kv_capacity;    /* cap: rows allocated per (sequence, KV head)                */
+  int64_t max_ctx_len;    /* host-side upper bound of ctx_len[]; Lq <= max_ctx_len <= cap */
+  int32_t window;         /* forced recent window, 128 in the article (>= 0)            */
+  int32_t topk;           /* global tokens outside the window, 1,024 in the article     */
+  int32_t select_mode;    /* HS2_SELECT_TOKEN, or HS2_SELECT_BLOCK (comparator)          */
+  int32_t block_size;     /* block mode only: positions per block (64)                   */
+  int32_t n_blocks;       /* block mode only: blocks kept (18)                           */
+  float sm_scale;         /* softmax scale, normally 1/sqrt(head_dim); must be > 0       */
+} hs2_attn_desc;
+
+/* Host only, touches no GPU: checks a descriptor.  Limits: head_dim == 128,
+ * 1 <= G <= 8, window + topk <= 4096 (token mode), block_size in [1, 4096] and
+ * block_size * n_blocks <= 4096 (block mode), 1 <= q_len <= max_ctx_len <= cap,
+ * cap < 2^31. */
+hs2_status hs2_validate(const hs2_attn_desc* desc);
+
+/* Host only: bytes of device workspace that hs2_full_attn_select and
+ * hs2_sparse_attn need for this descriptor (the larger of the two). */
+hs2_status hs2_workspace_size(const hs2_attn_desc* desc, size_t* bytes);
+
+/* The Full Attention layer of a Hybrid Block plus its selection (section 02
+ * "KV Reuse"; section 03 window + global tokens).  For every sequence b, query
+ * token j and query head h (KV head g = h / G):
+ *   out[b,j,h]  = softmax_t(sm_scale * q[b,j,h] . K[b,g,t]) . V[b,g,t]  over visible t
+ *   s[b,j,g,t]  = sum over the G heads of group g of their softmax probability at t
+ *   idx[b,j,g]  = token mode: the `window` most recent visible positions plus the
+ *                 `topk` positions outside the window with the largest s (ties to the
+ *                 lower position; all of them if fewer), ascending, -1 padded.
+ *                 block mode: the n_blocks aligned blocks with the largest sum of s over
+ *                 their visible positions (ties to the lower block), expanded to visible
+ *                 positions, ascending, -1 padded.  No forced window.
+ * probs may be NULL; otherwise s is written there (positions >= the visible count of a
+ * row are left untouched).  q/k/v/out/idx/workspace must be 16-byte aligned, probs
+ * 4-byte aligned.  With ctx_len[b]-Lq+j+1 <= 0 the row's out is 0 and idx is all -1. */
+hs2_status hs2_full_attn_select(const hs2_attn_desc* desc,
+                                const void* q, const void* k, const void* v,
+                                const float* k_scale, const float* v_scale,
+                                const int32_t* ctx_len,
+                                float* out, int32_t* idx, float* probs,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* One Sparse Attention layer of the Hybrid Block (section 02 "KV Reuse": same KV
+ * cache, same index set; section 03: one softmax over window and global tokens).
+ *   out[b,j,h] = softmax over t in idx[b,j,g] of (sm_scale * q[b,j,h] . K[b,g,t]) . V[b,g,t]
+ * Entries of idx that are negative or not below the row's visible count are skipped.
+ * A row with no valid entry gets out = 0.  Same alignment rules as above. */
+hs2_status hs2_sparse_attn(const hs2_attn_desc* desc,
+                           const void* q, const void* k, const void* v,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* ctx_len, const int32_t* idx,
+                           float* out,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Static English text for a status; never NULL. */
+const char* hs2_status_string(hs2_status status);
+
+/* Benchmark support.  While enabled (enable != 0), each call records two HIP events
+ * on its stream around its dominant kernel (the context scan of
+ * hs2_full_attn_select, the gather kernel of hs2_sparse_attn).  The events are
+ * created by the library (host-side bookkeeping, no device memory) and kept until
+ * hs2_timer_collect, which waits for them and returns the summed milliseconds and
+ * the number of launches timed for each kind, then forgets them.  Not thread-safe;
+ * meant for single-threaded benchmark drivers. */
+hs2_status hs2_timer_enable(int enable);
+hs2_status hs2_timer_collect(double* scan_ms, int32_t* scan_count,
+                             double* gather_ms, int32_t* gather_count);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HS2_H */

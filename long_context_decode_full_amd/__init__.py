@@ -1,0 +1,176 @@
+"""HySparse2 Hybrid-Block decode for MI355X (gfx950): Python binding of libhs2.so.
+
+The binding only marshals arguments (descriptor struct, device pointers, stream)
+into the C ABI declared in include/hs2.h; every step of the computation runs in
+the HIP kernels of libhs2.so.  There is no fallback: if the library is missing,
+every call raises.
+
+Pointer arguments accept a torch tensor (its data_ptr() is passed), a plain
+integer address, or None (NULL).  `stream` accepts a torch.cuda.Stream, a raw
+hipStream_t integer, or None for torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "HS2_OK", "HS2_ERR_INVALID_ARG", "HS2_ERR_UNSUPPORTED", "HS2_ERR_WORKSPACE",
+    "HS2_ERR_ALIGNMENT", "HS2_ERR_LAUNCH", "HS2_KV_BF16", "HS2_KV_FP8_E4M3FN",
+    "HS2_SELECT_TOKEN", "HS2_SELECT_BLOCK", "Hs2AttnDesc", "Hs2Error", "make_desc",
+    "hs2_validate", "hs2_workspace_size", "hs2_full_attn_select", "hs2_sparse_attn",
+    "hs2_status_string", "hs2_timer_enable", "hs2_timer_collect", "library_path", "load_library",
+    "EXPORTED_SYMBOLS",
+]
+
+HS2_OK = 0
+HS2_ERR_INVALID_ARG = 1
+HS2_ERR_UNSUPPORTED = 2
+HS2_ERR_WORKSPACE = 3
+HS2_ERR_ALIGNMENT = 4
+HS2_ERR_LAUNCH = 5
+HS2_KV_BF16 = 0
+HS2_KV_FP8_E4M3FN = 1
+HS2_SELECT_TOKEN = 0
+HS2_SELECT_BLOCK = 1
+
+EXPORTED_SYMBOLS = ("hs2_validate", "hs2_workspace_size", "hs2_full_attn_select",
+                    "hs2_sparse_attn", "hs2_status_string", "hs2_timer_enable",
+                    "hs2_timer_collect")
+
+
+class Hs2AttnDesc(ctypes.Structure):
+    """Mirror of hs2_attn_desc (include/hs2.h)."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("kv_capacity", ctypes.c_int64),
+        ("max_ctx_len", ctypes.c_int64),
+        ("window", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("select_mode", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("n_blocks", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+    ]
+
+
+class Hs2Error(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = status
+        super().__init__(f"{where}: {hs2_status_string(status)} (status {status})")
+
+
+def make_desc(batch, q_len, n_q_heads, n_kv_heads, kv_capacity, max_ctx_len, head_dim=128,
+              kv_dtype=HS2_KV_BF16, window=128, topk=1024, select_mode=HS2_SELECT_TOKEN,
+              block_size=64, n_blocks=18, sm_scale=None) -> Hs2AttnDesc:
+    return Hs2AttnDesc(int(batch), int(q_len), int(n_q_heads), int(n_kv_heads), int(head_dim),
+                       int(kv_dtype), int(kv_capacity), int(max_ctx_len), int(window), int(topk),
+                       int(select_mode), int(block_size), int(n_blocks),
+                       float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(head_dim)))
+
+
+# --------------------------------------------------------------------------- loading
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhs2.so")
+
+
+def load_library():
+    """Load libhs2.so (built in-tree by build.py).  Raises if it is absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950) first")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(Hs2AttnDesc)
+    lib.hs2_validate.argtypes = [D]
+    lib.hs2_validate.restype = ctypes.c_int
+    lib.hs2_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.hs2_workspace_size.restype = ctypes.c_int
+    lib.hs2_full_attn_select.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.hs2_full_attn_select.restype = ctypes.c_int
+    lib.hs2_sparse_attn.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.hs2_sparse_attn.restype = ctypes.c_int
+    lib.hs2_status_string.argtypes = [ctypes.c_int]
+    lib.hs2_status_string.restype = ctypes.c_char_p
+    lib.hs2_timer_enable.argtypes = [ctypes.c_int]
+    lib.hs2_timer_enable.restype = ctypes.c_int
+    lib.hs2_timer_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32),
+                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
+    lib.hs2_timer_collect.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+# --------------------------------------------------------------------------- C ABI
+def hs2_validate(desc: Hs2AttnDesc) -> int:
+    return load_library().hs2_validate(ctypes.byref(desc))
+
+
+def hs2_workspace_size(desc: Hs2AttnDesc):
+    """Returns (status, bytes)."""
+    n = ctypes.c_size_t(0)
+    st = load_library().hs2_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    return st, n.value
+
+
+def hs2_full_attn_select(desc, q, k, v, k_scale, v_scale, ctx_len, out, idx, probs,
+                         workspace, workspace_bytes, stream=None) -> int:
+    return load_library().hs2_full_attn_select(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
+        _ptr(ctx_len), _ptr(out), _ptr(idx), _ptr(probs), _ptr(workspace),
+        int(workspace_bytes), _stream(stream))
+
+
+def hs2_sparse_attn(desc, q, k, v, k_scale, v_scale, ctx_len, idx, out, workspace,
+                    workspace_bytes, stream=None) -> int:
+    return load_library().hs2_sparse_attn(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
+        _ptr(ctx_len), _ptr(idx), _ptr(out), _ptr(workspace), int(workspace_bytes),
+        _stream(stream))
+
+
+def hs2_status_string(status: int) -> str:
+    return load_library().hs2_status_string(int(status)).decode()
+
+
+def hs2_timer_enable(enable: bool) -> int:
+    return load_library().hs2_timer_enable(1 if enable else 0)
+
+
+def hs2_timer_collect():
+    """Returns (status, scan_ms, scan_count, gather_ms, gather_count)."""
+    a, c = ctypes.c_double(0), ctypes.c_int32(0)
+    b, d = ctypes.c_double(0), ctypes.c_int32(0)
+    st = load_library().hs2_timer_collect(ctypes.byref(a), ctypes.byref(c), ctypes.byref(b),
+                                          ctypes.byref(d))
+    return st, a.value, c.value, b.value, d.value

@@ -1,0 +1,356 @@
+// C-ABI host layer: descriptor validation, workspace layout, launch sequences.
+// Contract of every entry point: include/hs2.h.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "hs2.h"
+#include "hs2_internal.h"
+
+#define HS2_API extern "C" __attribute__((visibility("default")))
+
+namespace hs2 {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kScanTargetWorkgroups = 512;   // 2 per CU at 2 waves/SIMD on 256 CUs
+constexpr int kMaxSplits = 2048;             // combine kernel keeps one weight per split in LDS
+constexpr int kSparseSplitLen = 64;          // index entries per sparse workgroup
+constexpr int kSelectChunk = 4096;           // positions per workgroup in the selection passes
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Layout {
+  int64_t n_sel = 0;
+  int64_t logit_stride = 0;
+  int32_t G = 0, S = 0;
+  int32_t split_len = 0, n_split = 0;
+  int32_t split_len_sp = 0, n_split_sp = 0;
+  int32_t chunk_len = 0, n_chunks = 0;
+  size_t off_logits = 0, off_part = 0, off_mz = 0, off_s = 0, off_selblk = 0, off_hist2 = 0,
+         off_hist3 = 0, off_winners = 0, off_boundary = 0, total = 0;
+};
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (v == nullptr || *v == '\0') return dflt;
+  const int x = std::atoi(v);
+  return x > 0 ? x : dflt;
+}
+
+hs2_status validate_desc(const hs2_attn_desc* d) {
+  if (d == nullptr) return HS2_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->q_len < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1)
+    return HS2_ERR_INVALID_ARG;
+  if (d->n_q_heads % d->n_kv_heads != 0) return HS2_ERR_INVALID_ARG;
+  if (d->kv_dtype != HS2_KV_BF16 && d->kv_dtype != HS2_KV_FP8_E4M3FN) return HS2_ERR_INVALID_ARG;
+  if (d->kv_capacity < 1 || d->max_ctx_len < d->q_len || d->max_ctx_len > d->kv_capacity)
+    return HS2_ERR_INVALID_ARG;
+  if (!(d->sm_scale > 0.0f) || !std::isfinite(d->sm_scale)) return HS2_ERR_INVALID_ARG;
+  if (d->select_mode == HS2_SELECT_TOKEN) {
+    if (d->window < 0 || d->topk < 0 || (int64_t)d->window + d->topk < 1) return HS2_ERR_INVALID_ARG;
+    if ((int64_t)d->window + d->topk > 4096) return HS2_ERR_UNSUPPORTED;
+  } else if (d->select_mode == HS2_SELECT_BLOCK) {
+    if (d->block_size < 1 || d->n_blocks < 1) return HS2_ERR_INVALID_ARG;
+    if ((int64_t)d->block_size * d->n_blocks > 4096) return HS2_ERR_UNSUPPORTED;
+    if (ceil_div(d->max_ctx_len, d->block_size) > kMaxBlocksLds) return HS2_ERR_UNSUPPORTED;
+  } else {
+    return HS2_ERR_INVALID_ARG;
+  }
+  if (d->head_dim != kHeadDim) return HS2_ERR_UNSUPPORTED;
+  if (d->n_q_heads / d->n_kv_heads > kSlots) return HS2_ERR_UNSUPPORTED;
+  if (d->kv_capacity >= (int64_t(1) << 31)) return HS2_ERR_UNSUPPORTED;
+  if ((int64_t)d->batch * d->q_len > 65535) return HS2_ERR_UNSUPPORTED;
+  if (d->n_kv_heads > 65535) return HS2_ERR_UNSUPPORTED;
+  return HS2_OK;
+}
+
+Layout make_layout(const hs2_attn_desc* d) {
+  Layout L;
+  L.n_sel = (int64_t)d->batch * d->q_len * d->n_kv_heads;
+  L.G = d->n_q_heads / d->n_kv_heads;
+  L.S = d->select_mode == HS2_SELECT_TOKEN ? d->window + d->topk : d->block_size * d->n_blocks;
+  L.logit_stride = ceil_div(d->max_ctx_len, 64) * 64;
+
+  // Dense scan: enough splits to give ~2 workgroups per CU in one residency round.
+  const int64_t rows = L.n_sel * d->max_ctx_len;
+  int64_t split = ceil_div(ceil_div(rows, kScanTargetWorkgroups), 256) * 256;
+  split = env_int("HS2_SPLIT_LEN", (int)std::min<int64_t>(split, 1 << 30));
+  split = ceil_div(split, 256) * 256;
+  if (split < 256) split = 256;
+  while (ceil_div(d->max_ctx_len, split) > kMaxSplits) split *= 2;
+  L.split_len = (int32_t)split;
+  L.n_split = (int32_t)ceil_div(d->max_ctx_len, split);
+
+  int64_t sp = env_int("HS2_SPARSE_SPLIT_LEN", kSparseSplitLen);
+  sp = ceil_div(sp, 32) * 32;
+  while (ceil_div(L.S, sp) > kMaxSplits) sp *= 2;
+  L.split_len_sp = (int32_t)sp;
+  L.n_split_sp = (int32_t)ceil_div(L.S, sp);
+
+  L.chunk_len = kSelectChunk;
+  L.n_chunks = (int32_t)ceil_div(d->max_ctx_len, kSelectChunk);
+
+  const int64_t n = L.n_sel;
+  const int64_t nsplit_max = std::max(L.n_split, L.n_split_sp);
+  size_t off = 0;
+  L.off_logits = off; off = align_up(off + (size_t)n * L.logit_stride * 8 * sizeof(float));
+  L.off_part = off;   off = align_up(off + (size_t)n * nsplit_max * L.G * kPartStride * sizeof(float));
+  L.off_mz = off;     off = align_up(off + (size_t)n * 16 * sizeof(float));
+  L.off_s = off;      off = align_up(off + (size_t)n * L.logit_stride * sizeof(float));
+  L.off_selblk = off; off = align_up(off + (size_t)n * kSelWords * sizeof(uint32_t));
+  L.off_hist2 = off;  off = align_up(off + (size_t)n * kHist2Bins * sizeof(uint32_t));
+  L.off_hist3 = off;  off = align_up(off + (size_t)n * kHist3Bins * sizeof(uint32_t));
+  L.off_winners = off; off = align_up(off + (size_t)n * std::max(d->topk, 1) * sizeof(int32_t));
+  L.off_boundary = off; off = align_up(off + (size_t)n * kBoundaryCap * sizeof(uint2));
+  L.total = off;
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---------------------------------------------------------------- kernel timer
+struct TimerRec {
+  hipEvent_t a, b;
+  int kind;   // 0 scan, 1 gather
+};
+std::mutex g_timer_mu;
+bool g_timer_on = false;
+std::vector<TimerRec> g_timer;
+
+bool timer_begin(hipStream_t st, int kind, TimerRec* rec) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  if (!g_timer_on) return false;
+  if (hipEventCreate(&rec->a) != hipSuccess) return false;
+  if (hipEventCreate(&rec->b) != hipSuccess) {
+    (void)hipEventDestroy(rec->a);
+    return false;
+  }
+  rec->kind = kind;
+  (void)hipEventRecord(rec->a, st);
+  return true;
+}
+
+void timer_end(hipStream_t st, TimerRec* rec) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  (void)hipEventRecord(rec->b, st);
+  g_timer.push_back(*rec);
+}
+
+}  // namespace
+}  // namespace hs2
+
+using namespace hs2;
+
+HS2_API hs2_status hs2_validate(const hs2_attn_desc* desc) { return validate_desc(desc); }
+
+HS2_API hs2_status hs2_workspace_size(const hs2_attn_desc* desc, size_t* bytes) {
+  const hs2_status s = validate_desc(desc);
+  if (s != HS2_OK) return s;
+  if (bytes == nullptr) return HS2_ERR_INVALID_ARG;
+  *bytes = make_layout(desc).total;
+  return HS2_OK;
+}
+
+HS2_API const char* hs2_status_string(hs2_status status) {
+  switch (status) {
+    case HS2_OK: return "ok";
+    case HS2_ERR_INVALID_ARG: return "invalid argument";
+    case HS2_ERR_UNSUPPORTED: return "unsupported configuration";
+    case HS2_ERR_WORKSPACE: return "workspace too small";
+    case HS2_ERR_ALIGNMENT: return "misaligned pointer";
+    case HS2_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+static hs2_status check_common(const hs2_attn_desc* d, const void* q, const void* k, const void* v,
+                               const float* ks, const float* vs, const int32_t* ctx_len,
+                               const void* out, const void* idx, void* ws, size_t ws_bytes,
+                               Layout* L) {
+  hs2_status s = validate_desc(d);
+  if (s != HS2_OK) return s;
+  if (!q || !k || !v || !ctx_len || !out || !idx || !ws) return HS2_ERR_INVALID_ARG;
+  if (d->kv_dtype == HS2_KV_FP8_E4M3FN && (!ks || !vs)) return HS2_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(idx, 16) || !aligned(ws, 16) || !aligned(ctx_len, 4))
+    return HS2_ERR_ALIGNMENT;
+  if (d->kv_dtype == HS2_KV_FP8_E4M3FN && (!aligned(ks, 4) || !aligned(vs, 4)))
+    return HS2_ERR_ALIGNMENT;
+  *L = make_layout(d);
+  if (ws_bytes < L->total) return HS2_ERR_WORKSPACE;
+  return HS2_OK;
+}
+
+static ScanArgs scan_args(const hs2_attn_desc* d, const Layout& L, const void* q, const void* k,
+                          const void* v, const float* ks, const float* vs, const int32_t* ctx_len,
+                          uint8_t* ws) {
+  ScanArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint8_t*>(k);
+  a.v = static_cast<const uint8_t*>(v);
+  a.k_scale = ks;
+  a.v_scale = vs;
+  a.ctx_len = ctx_len;
+  a.part = reinterpret_cast<float*>(ws + L.off_part);
+  a.cap = d->kv_capacity;
+  a.ctx_max = d->max_ctx_len;
+  a.logit_stride = L.logit_stride;
+  a.Lq = d->q_len;
+  a.Hq = d->n_q_heads;
+  a.Hkv = d->n_kv_heads;
+  a.G = L.G;
+  a.S = L.S;
+  a.scale_log2 = d->sm_scale * 1.44269504088896340736f;
+  return a;
+}
+
+HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q, const void* k,
+                                        const void* v, const float* k_scale, const float* v_scale,
+                                        const int32_t* ctx_len, float* out, int32_t* idx,
+                                        float* probs, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  Layout L;
+  hs2_status s = check_common(desc, q, k, v, k_scale, v_scale, ctx_len, out, idx, workspace,
+                              workspace_bytes, &L);
+  if (s != HS2_OK) return s;
+  if (probs != nullptr && !aligned(probs, 4)) return HS2_ERR_ALIGNMENT;
+  const bool fp8 = desc->kv_dtype == HS2_KV_FP8_E4M3FN;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+
+  ScanArgs sa = scan_args(desc, L, q, k, v, k_scale, v_scale, ctx_len, ws);
+  sa.logits = reinterpret_cast<float*>(ws + L.off_logits);
+  sa.n_split = L.n_split;
+  sa.split_len = L.split_len;
+
+  TimerRec rec;
+  const bool timed = timer_begin(stream, 0, &rec);
+  hipError_t e = launch_scan_dense(sa, fp8, desc->batch, stream);
+  if (timed) timer_end(stream, &rec);
+  if (e != hipSuccess) return HS2_ERR_LAUNCH;
+
+  CombineArgs ca{};
+  ca.part = sa.part;
+  ca.out = out;
+  ca.mz = reinterpret_cast<float*>(ws + L.off_mz);
+  ca.sel_zero = reinterpret_cast<uint32_t*>(ws + L.off_selblk);
+  ca.sel_zero_words = kSelWords;
+  ca.n_sel = (int32_t)L.n_sel;
+  ca.Hkv = desc->n_kv_heads;
+  ca.G = L.G;
+  ca.Hq = desc->n_q_heads;
+  ca.n_split = L.n_split;
+  if (launch_combine(ca, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+
+  SelectArgs sl{};
+  sl.logits = sa.logits;
+  sl.mz = ca.mz;
+  sl.s = probs != nullptr ? probs : reinterpret_cast<float*>(ws + L.off_s);
+  sl.s_stride = probs != nullptr ? desc->kv_capacity : L.logit_stride;
+  sl.logit_stride = L.logit_stride;
+  sl.ctx_len = ctx_len;
+  sl.ctx_max = desc->max_ctx_len;
+  sl.selblk = ca.sel_zero;
+  sl.hist2 = reinterpret_cast<uint32_t*>(ws + L.off_hist2);
+  sl.hist3 = reinterpret_cast<uint32_t*>(ws + L.off_hist3);
+  sl.winners = reinterpret_cast<int32_t*>(ws + L.off_winners);
+  sl.boundary = reinterpret_cast<uint2*>(ws + L.off_boundary);
+  sl.idx = idx;
+  sl.n_sel = (int32_t)L.n_sel;
+  sl.Lq = desc->q_len;
+  sl.Hkv = desc->n_kv_heads;
+  sl.G = L.G;
+  sl.window = desc->window;
+  sl.topk = desc->topk;
+  sl.S = L.S;
+  sl.block_size = desc->block_size;
+  sl.n_blocks = desc->n_blocks;
+  sl.chunk_len = L.chunk_len;
+  sl.n_chunks = L.n_chunks;
+
+  if (desc->select_mode == HS2_SELECT_TOKEN) {
+    sl.with_hist = 1;
+    if (launch_groupsum(sl, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+    if (launch_refine(sl, 2, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+    if (launch_refine(sl, 3, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+    if (launch_collect(sl, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+    if (launch_finalize(sl, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+  } else {
+    sl.with_hist = 0;
+    if (launch_groupsum(sl, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+    if (launch_block_select(sl, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+  }
+  return HS2_OK;
+}
+
+HS2_API hs2_status hs2_sparse_attn(const hs2_attn_desc* desc, const void* q, const void* k,
+                                   const void* v, const float* k_scale, const float* v_scale,
+                                   const int32_t* ctx_len, const int32_t* idx, float* out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Layout L;
+  hs2_status s = check_common(desc, q, k, v, k_scale, v_scale, ctx_len, out, idx, workspace,
+                              workspace_bytes, &L);
+  if (s != HS2_OK) return s;
+  const bool fp8 = desc->kv_dtype == HS2_KV_FP8_E4M3FN;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+
+  ScanArgs sa = scan_args(desc, L, q, k, v, k_scale, v_scale, ctx_len, ws);
+  sa.idx = idx;
+  sa.n_split = L.n_split_sp;
+  sa.split_len = L.split_len_sp;
+
+  TimerRec rec;
+  const bool timed = timer_begin(stream, 1, &rec);
+  hipError_t e = launch_scan_sparse(sa, fp8, desc->batch, stream);
+  if (timed) timer_end(stream, &rec);
+  if (e != hipSuccess) return HS2_ERR_LAUNCH;
+
+  CombineArgs ca{};
+  ca.part = sa.part;
+  ca.out = out;
+  ca.n_sel = (int32_t)L.n_sel;
+  ca.Hkv = desc->n_kv_heads;
+  ca.G = L.G;
+  ca.Hq = desc->n_q_heads;
+  ca.n_split = L.n_split_sp;
+  if (launch_combine(ca, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+  return HS2_OK;
+}
+
+HS2_API hs2_status hs2_timer_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  g_timer_on = enable != 0;
+  return HS2_OK;
+}
+
+HS2_API hs2_status hs2_timer_collect(double* scan_ms, int32_t* scan_count, double* gather_ms,
+                                     int32_t* gather_count) {
+  if (!scan_ms || !scan_count || !gather_ms || !gather_count) return HS2_ERR_INVALID_ARG;
+  std::vector<TimerRec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    recs.swap(g_timer);
+  }
+  double ms[2] = {0.0, 0.0};
+  int32_t cnt[2] = {0, 0};
+  hs2_status st = HS2_OK;
+  for (const TimerRec& r : recs) {
+    float t = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+      st = HS2_ERR_LAUNCH;
+    ms[r.kind] += t;
+    cnt[r.kind] += 1;
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  *scan_ms = ms[0];
+  *scan_count = cnt[0];
+  *gather_ms = ms[1];
+  *gather_count = cnt[1];
+  return st;
+}

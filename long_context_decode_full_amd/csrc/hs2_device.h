@@ -1,0 +1,68 @@
+// Device helpers shared by the HIP kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs2 {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// v_dot2_f32_bf16: c + a.lo*b.lo + a.hi*b.hi; bf16 x bf16 products are exact in fp32.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// DPP lane permutations inside a row of 16 lanes.
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppXor3 = 0x1B;   // quad_perm [3,2,1,0]
+constexpr int kDppMirror8 = 0x141;  // row_half_mirror: lane i <-> 7-i inside each 8
+constexpr int kDppRor8 = 0x128;  // row_ror:8: lane i <-> i^8 inside each 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bool wave_any(bool p) {
+  return __builtin_amdgcn_ballot_w64(p) != 0;
+}
+
+// bf16 pair word -> two fp32 values (low element, high element).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// Two OCP E4M3FN codes (bytes 0-1 or 2-3 of w) -> two fp32 values (exact).
+__device__ __forceinline__ f32x2_t fp8x2_to_f32(uint32_t w, bool high) {
+  return high ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true)
+              : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+}
+
+// Two OCP E4M3FN codes -> one bf16 pair word (exact: 3 mantissa bits fit in 7).
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool high) {
+  bf16x2_t r = high ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                    : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+template <typename T>
+__device__ __forceinline__ T atomic_load_relaxed(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace hs2

@@ -1,0 +1,99 @@
+// Internal interface between the C-ABI host layer (hs2_api.cpp) and the HIP
+// kernels.  Host-visible argument structs plus one launcher per kernel; every
+// launcher enqueues on the given stream and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs2 {
+
+constexpr int kHeadDim = 128;
+constexpr int kSlots = 8;             // head slots per KV group handled by one wave
+constexpr int kPartStride = 132;      // floats per (split, head) partial: m, z, pad, pad, o[128]
+constexpr int kHist1Bins = 2048;      // score bits 30..20
+constexpr int kHist2Bins = 4096;      // score bits 19..8
+constexpr int kHist3Bins = 256;       // score bits 7..0
+constexpr int kBoundaryCap = 4096;    // boundary-bin entries resolved by one sort
+constexpr int kStateWords = 16;       // u32 per selection state
+// Per-selection control block (u32 words), cleared by the combine kernel of every
+// call: [0,16) state, [16,20) pass tickets, [32, 32+kHist1Bins) first histogram.
+constexpr int kSelCounterOff = 16;
+constexpr int kSelHist1Off = 32;
+constexpr int kSelWords = kSelHist1Off + kHist1Bins;
+constexpr int kMaxBlocksLds = 16384;  // block mode: blocks per row held in LDS
+
+// Per-selection state words (u32).
+enum StateWord {
+  kStTakeAll = 0,    // 1: candidates <= topk, every candidate is selected
+  kStResolved = 1,   // 1: boundary bin small enough (or all bits fixed)
+  kStPrefix = 2,     // fixed high bits of the threshold key
+  kStPrefixLen = 3,  // number of fixed bits below the sign bit (11, 23, 31)
+  kStAbove = 4,      // candidates whose key prefix is strictly greater
+  kStInBin = 5,      // candidates in the threshold bin
+  kStWinCount = 6,   // collect: winners appended
+  kStBndCount = 7,   // collect: boundary entries appended (may exceed the cap)
+  kStKK = 8,         // number of global positions to select
+};
+
+struct ScanArgs {
+  const uint16_t* q;        // [B, Lq, Hq, D] bf16 bits
+  const uint8_t* k;         // [B, Hkv, cap, D] bf16 bits or e4m3fn codes
+  const uint8_t* v;
+  const float* k_scale;     // [B, Hkv, cap] (fp8 only)
+  const float* v_scale;
+  const int32_t* ctx_len;   // [B]
+  const int32_t* idx;       // sparse mode: [n_sel, S]
+  float* logits;            // dense mode: [n_sel, logit_stride, 8] log2-domain logits
+  float* part;              // [n_sel, n_split, G, kPartStride]
+  int64_t cap;              // rows per (sequence, KV head)
+  int64_t ctx_max;          // ctx_len[] is clamped to [0, ctx_max] (ctx_max <= cap)
+  int64_t logit_stride;
+  int32_t Lq, Hq, Hkv, G;
+  int32_t S;                // sparse mode: index row length
+  int32_t n_split;
+  int32_t split_len;        // positions per split (dense: tokens, sparse: idx entries)
+  float scale_log2;         // sm_scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* part;        // [n_sel, n_split, G, kPartStride]
+  float* out;               // [B, Lq, Hq, D]
+  float* mz;                // [n_sel, 8, 2] (M, 1/Z) or nullptr
+  uint32_t* sel_zero;       // selection words to clear per selection, or nullptr
+  int32_t sel_zero_words;   // words per selection in sel_zero
+  int32_t n_sel, Hkv, G, Hq, n_split;
+};
+
+struct SelectArgs {
+  const float* logits;      // [n_sel, logit_stride, 8]
+  const float* mz;          // [n_sel, 8, 2]
+  float* s;                 // [n_sel, s_stride] group-summed probabilities
+  int64_t s_stride;
+  int64_t logit_stride;
+  const int32_t* ctx_len;
+  int64_t ctx_max;          // ctx_len[] is clamped to [0, ctx_max]
+  uint32_t* selblk;         // [n_sel, kSelWords] control blocks
+  uint32_t* hist2;          // [n_sel, kHist2Bins]
+  uint32_t* hist3;          // [n_sel, kHist3Bins]
+  int32_t* winners;         // [n_sel, topk]
+  uint2* boundary;          // [n_sel, kBoundaryCap] (score bits, position)
+  int32_t* idx;             // [n_sel, S]
+  int32_t n_sel, Lq, Hkv, G;
+  int32_t window, topk, S;
+  int32_t block_size, n_blocks;
+  int32_t chunk_len;        // positions per workgroup in the streaming passes
+  int32_t n_chunks;
+  int32_t with_hist;        // token mode: build the first histogram
+};
+
+hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, int B, hipStream_t st);
+hipError_t launch_scan_sparse(const ScanArgs& a, bool fp8, int B, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+hipError_t launch_groupsum(const SelectArgs& a, hipStream_t st);
+hipError_t launch_refine(const SelectArgs& a, int pass, hipStream_t st);
+hipError_t launch_collect(const SelectArgs& a, hipStream_t st);
+hipError_t launch_finalize(const SelectArgs& a, hipStream_t st);
+hipError_t launch_block_select(const SelectArgs& a, hipStream_t st);
+
+}  // namespace hs2

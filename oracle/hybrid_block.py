@@ -157,9 +157,10 @@ def block_select(s, block: int, n_blocks: int):
 
 # --------------------------------------------------------------------------- one Hybrid Block
 def hybrid_block_token(inp: dict, b: int, j: int, window=128, topk=1024, mode="token",
-                       block=64, n_blocks=18, want_scores=True):
+                       block=64, n_blocks=18, want_scores=True, groups=None):
     """Everything the Hybrid Block computes for query token j of sequence b, per KV group g:
-    full-layer output, group scores, index set, and each sparse layer's output."""
+    full-layer output, group scores, index set, and each sparse layer's output.
+    `groups` restricts the work to some KV groups (others are left zero / -1)."""
     q_full = bf16_to_f64(inp["q_full"][b, j])            # [Hq, D]
     qs = [bf16_to_f64(q[b, j]) for q in inp["q_sparse"]]
     Hq = q_full.shape[0]
@@ -174,7 +175,7 @@ def hybrid_block_token(inp: dict, b: int, j: int, window=128, topk=1024, mode="t
     out_sp = [np.zeros_like(out_full) for _ in qs]
     idx_all = np.full((Hkv, S), -1, dtype=np.int64)
     s_all = []
-    for g in range(Hkv):
+    for g in (range(Hkv) if groups is None else groups):
         heads = slice(g * G, (g + 1) * G)                  # R5
         K, V = kv_rows(inp, b, g, n)
         o, P = full_attention(q_full[heads], K, V, sm)

@@ -1,0 +1,168 @@
+"""CPU-only checks of the C ABI: the library loads, exports what include/hs2.h declares,
+and every argument check returns its status before anything is enqueued.
+
+No call here reaches a kernel launch: each one fails validation first, so these
+run without a GPU.  Fake device addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_decode_full_amd as hs2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hs2.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hs2.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return hs2.load_library()
+
+
+def _desc(**kw):
+    base = dict(batch=1, q_len=1, n_q_heads=32, n_kv_heads=4, kv_capacity=1 << 20,
+                max_ctx_len=1 << 20)
+    base.update(kw)
+    return hs2.make_desc(**base)
+
+
+def test_header_symbols_are_exported(lib):
+    text = open(HEADER).read()
+    declared = sorted(set(re.findall(r"\b(hs2_[a-z_]+)\s*\(", text)))
+    assert declared, "no declarations found"
+    assert sorted(hs2.EXPORTED_SYMBOLS) == declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+        ctypes.cast(getattr(lib, name), ctypes.c_void_p)
+
+
+def test_status_strings(lib):
+    for st in range(6):
+        assert hs2.hs2_status_string(st)
+    assert hs2.hs2_status_string(0) == "ok"
+    assert hs2.hs2_status_string(99) == "unknown status"
+
+
+def test_desc_struct_layout_matches_header():
+    # int32 x6, int64 x2, int32 x5, float -> 24 + 16 + 20 + 4 = 64 bytes with alignment
+    assert ctypes.sizeof(hs2.Hs2AttnDesc) == 64
+    assert hs2.Hs2AttnDesc.kv_capacity.offset == 24
+    assert hs2.Hs2AttnDesc.sm_scale.offset == 60
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), hs2.HS2_OK),
+    (dict(batch=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(q_len=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(n_q_heads=30), hs2.HS2_ERR_INVALID_ARG),          # Hq % Hkv != 0
+    (dict(n_q_heads=64, n_kv_heads=4), hs2.HS2_ERR_UNSUPPORTED),   # G = 16 > 8
+    (dict(head_dim=64), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(kv_dtype=7), hs2.HS2_ERR_INVALID_ARG),
+    (dict(max_ctx_len=(1 << 20) + 1), hs2.HS2_ERR_INVALID_ARG),   # beyond capacity
+    (dict(q_len=64, max_ctx_len=32), hs2.HS2_ERR_INVALID_ARG),    # chunk longer than context
+    (dict(window=-1), hs2.HS2_ERR_INVALID_ARG),
+    (dict(window=0, topk=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(window=128, topk=4000), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(select_mode=5), hs2.HS2_ERR_INVALID_ARG),
+    (dict(select_mode=1, block_size=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(select_mode=1, block_size=64, n_blocks=100), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(select_mode=1, block_size=16, n_blocks=18), hs2.HS2_ERR_UNSUPPORTED),  # > 16384 blocks
+    (dict(select_mode=1), hs2.HS2_OK),
+    (dict(sm_scale=0.0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(sm_scale=float("nan")), hs2.HS2_ERR_INVALID_ARG),
+    (dict(kv_capacity=1 << 31, max_ctx_len=1 << 20), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(batch=1100, q_len=64, kv_capacity=4096, max_ctx_len=4096), hs2.HS2_ERR_UNSUPPORTED),
+])
+def test_validate(lib, kw, status):
+    assert hs2.hs2_validate(_desc(**kw)) == status
+
+
+def test_validate_null_desc(lib):
+    assert lib.hs2_validate(None) == hs2.HS2_ERR_INVALID_ARG
+    n = ctypes.c_size_t(0)
+    assert lib.hs2_workspace_size(None, ctypes.byref(n)) == hs2.HS2_ERR_INVALID_ARG
+    assert lib.hs2_workspace_size(ctypes.byref(_desc()), None) == hs2.HS2_ERR_INVALID_ARG
+
+
+def test_workspace_monotone_in_context(lib):
+    prev = 0
+    for ctx in [1, 100, 4096, 65536, 1 << 20]:
+        st, nbytes = hs2.hs2_workspace_size(_desc(kv_capacity=1 << 20, max_ctx_len=ctx))
+        assert st == hs2.HS2_OK
+        assert nbytes >= prev
+        prev = nbytes
+    # logits (32 B per position per KV head) dominate at long context
+    st, nbytes = hs2.hs2_workspace_size(_desc())
+    assert nbytes >= 4 * (1 << 20) * 8 * 4
+
+
+FAKE = 0x7F0000000000   # 16-byte aligned fake device address, never dereferenced
+
+
+def _full(d, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, k_scale=None, v_scale=None, ctx_len=FAKE, out=FAKE,
+                idx=FAKE, probs=None, workspace=FAKE, workspace_bytes=1 << 40)
+    args.update(over)
+    return hs2.hs2_full_attn_select(d, stream=0, **args)
+
+
+def _sparse(d, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, k_scale=None, v_scale=None, ctx_len=FAKE, idx=FAKE,
+                out=FAKE, workspace=FAKE, workspace_bytes=1 << 40)
+    args.update(over)
+    return hs2.hs2_sparse_attn(d, stream=0, **args)
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "ctx_len", "out", "idx", "workspace"])
+def test_null_pointers_rejected(lib, field):
+    assert _full(_desc(), **{field: None}) == hs2.HS2_ERR_INVALID_ARG
+    assert _sparse(_desc(), **{field: None}) == hs2.HS2_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "out", "idx", "workspace"])
+def test_misaligned_pointers_rejected(lib, field):
+    assert _full(_desc(), **{field: FAKE + 4}) == hs2.HS2_ERR_ALIGNMENT
+    assert _sparse(_desc(), **{field: FAKE + 8}) == hs2.HS2_ERR_ALIGNMENT
+    assert _full(_desc(), probs=FAKE + 2) == hs2.HS2_ERR_ALIGNMENT
+
+
+def test_fp8_needs_scales(lib):
+    d = _desc(kv_dtype=hs2.HS2_KV_FP8_E4M3FN)
+    assert _full(d) == hs2.HS2_ERR_INVALID_ARG
+    assert _full(d, k_scale=FAKE) == hs2.HS2_ERR_INVALID_ARG
+    assert _sparse(d, v_scale=FAKE) == hs2.HS2_ERR_INVALID_ARG
+    assert _full(d, k_scale=FAKE + 2, v_scale=FAKE) == hs2.HS2_ERR_ALIGNMENT
+
+
+def test_workspace_too_small(lib):
+    d = _desc()
+    st, nbytes = hs2.hs2_workspace_size(d)
+    assert st == 0
+    assert _full(d, workspace_bytes=nbytes - 1) == hs2.HS2_ERR_WORKSPACE
+    assert _sparse(d, workspace_bytes=16) == hs2.HS2_ERR_WORKSPACE
+
+
+def test_invalid_desc_checked_before_pointers(lib):
+    assert _full(_desc(head_dim=96), q=None) == hs2.HS2_ERR_UNSUPPORTED
+
+
+def test_timer_collect_empty(lib):
+    assert hs2.hs2_timer_enable(False) == 0
+    st, a, c, b, d = hs2.hs2_timer_collect()
+    assert st == 0 and c == 0 and d == 0 and a == 0.0 and b == 0.0
+    assert lib.hs2_timer_collect(None, None, None, None) == hs2.HS2_ERR_INVALID_ARG
+
+
+def test_product_path_has_no_fallback():
+    """The binding and runner must not reach the CPU oracle."""
+    pkg = os.path.dirname(hs2.__file__)
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            src = open(os.path.join(pkg, name)).read()
+            assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), name
+            assert "hybrid_block(" not in src, name

@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 CPU oracle.
+
+Every case prints its name, shapes and seed before touching the GPU.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_decode_full_amd import workloads as wl
+from parity import assert_out_close, check_block_row, check_idx_row
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu_only():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _announce(tag, w):
+    print(f"\n[gpu case] {tag}: {w.name} B={w.batch} Lq={w.q_len} Hq={w.n_q_heads} "
+          f"Hkv={w.n_kv_heads} ctx={w.ctx_lens or w.ctx_log_uniform} kv={w.kv_dtype} seed={w.seed}",
+          flush=True)
+
+
+def run_and_compare(w, tag, tokens=None, window=128, topk=1024, mode="token", block_size=64,
+                    n_blocks=18, with_probs=True, max_ctx_len=None, max_swaps=None):
+    from long_context_decode_full_amd.runner import HybridBlockDevice
+    _announce(tag, w)
+    inp = wl.make_inputs(w)
+    dev = HybridBlockDevice(inp, window=window, topk=topk, mode=mode, block_size=block_size,
+                            n_blocks=n_blocks, with_probs=with_probs, max_ctx_len=max_ctx_len)
+    dev.step()
+    got = dev.results()
+    B, Lq = inp["q_full"].shape[:2]
+    if tokens is None:
+        tokens = [(b, j) for b in range(B) for j in range(Lq)]
+    ref = oracle.hybrid_block(inp, tokens=tokens, window=window, topk=topk, mode=mode,
+                              block=block_size, n_blocks=n_blocks)
+    # sparse layers again, fed the oracle's index sets (independent of the GPU selection)
+    ref_idx = np.full(got["idx"].shape, -1, dtype=np.int32)
+    for (b, j), r in ref.items():
+        ref_idx[b, j] = r["idx"].astype(np.int32)
+    sp_on_ref = []
+    ridx_dev = torch.from_numpy(ref_idx).to(dev.device)
+    for layer in range(len(dev.q_sparse)):
+        dev.sparse(layer, idx=ridx_dev)
+        torch.cuda.synchronize()
+        sp_on_ref.append(dev.out_sparse[layer].cpu().numpy())
+
+    Hkv = inp["k"].shape[1]
+    G = inp["q_full"].shape[2] // Hkv
+    swaps = 0
+    rows_equal = 0
+    worst = {"full": 0.0, "sparse": 0.0, "e2e": 0.0, "probs": 0.0}
+    for (b, j), r in ref.items():
+        n = r["n"]
+        worst["full"] = max(worst["full"], assert_out_close(got["out_full"][b, j], r["out_full"],
+                                                            what=f"out_full[{b},{j}]"))
+        for layer in range(len(r["out_sparse"])):
+            worst["sparse"] = max(worst["sparse"], assert_out_close(
+                sp_on_ref[layer][b, j], r["out_sparse"][layer], what=f"sparse{layer}[{b},{j}]"))
+        for g in range(Hkv):
+            s = r["s"][g]
+            if mode == "block":
+                swaps += check_block_row(got["idx"][b, j, g], r["idx"][g], s, n, block_size, n_blocks)
+            else:
+                swaps += check_idx_row(got["idx"][b, j, g], r["idx"][g], s, n, window, topk)
+            same = np.array_equal(got["idx"][b, j, g], r["idx"][g])
+            rows_equal += int(same)
+            if same:
+                heads = slice(g * G, (g + 1) * G)
+                for layer in range(len(r["out_sparse"])):
+                    worst["e2e"] = max(worst["e2e"], assert_out_close(
+                        got["out_sparse"][layer][b, j, heads], r["out_sparse"][layer][heads],
+                        what=f"e2e sparse{layer}[{b},{j},{g}]"))
+            if got["probs"] is not None and n > 0:
+                gp = got["probs"][b, j, g, :n].astype(np.float64)
+                mask = s > 1e-30
+                rel = np.abs(gp[mask] - s[mask]) / s[mask]
+                worst["probs"] = max(worst["probs"], float(rel.max(initial=0.0)))
+                assert rel.max(initial=0.0) <= 1e-5, f"probs row ({b},{j},{g}) rel err {rel.max()}"
+    if max_swaps is not None:
+        assert swaps <= max_swaps
+    print(f"[gpu case] {tag}: worst rel errors {worst}, tie-band swaps {swaps}, "
+          f"identical idx rows {rows_equal}/{len(ref) * Hkv}", flush=True)
+    return got, ref
+
+
+# ------------------------------------------------------------------ the five configurations
+def test_tiny_decode():
+    w = wl.standard_workloads()["tiny"]
+    run_and_compare(w, "tiny")
+
+
+def test_batched_decode():
+    w = wl.standard_workloads()["batched"]
+    run_and_compare(w, "batched")
+
+
+def test_fp8_256k_decode():
+    w = wl.standard_workloads()["fp8_256k"]
+    run_and_compare(w, "fp8_256k")
+
+
+def test_million_token_decode():
+    w = wl.standard_workloads()["million"]
+    run_and_compare(w, "million")
+
+
+def test_chunk_small_valu_path():
+    """64-token causal chunk on the per-token scan path, reduced lengths, sampled tokens."""
+    w = wl.Workload("chunk reduced", 2, 64, 32, 4, ctx_lens=[5000, 9000], n_needles=16, seed=2005)
+    run_and_compare(w, "chunk-small", tokens=[(0, 0), (0, 1), (0, 40), (0, 63), (1, 0), (1, 63)])
+
+
+# ------------------------------------------------------------------ edges
+@pytest.mark.parametrize("ctx", [1, 127, 128, 129, 1151, 1152, 1153, 5000])
+def test_short_and_boundary_contexts(ctx):
+    w = wl.Workload(f"ctx{ctx}", 1, 1, 16, 2, ctx_lens=[ctx], n_needles=min(4, ctx), seed=3000 + ctx)
+    got, ref = run_and_compare(w, f"ctx{ctx}")
+    if ctx <= 1152:   # every position selected; sparse layers equal dense attention
+        for g in range(2):
+            assert got["idx"][0, 0, g, :ctx].tolist() == list(range(ctx))
+
+
+def test_ragged_batch_with_poisoned_tail():
+    """Rows past ctx_len hold NaN; they must never be read.  Capacity > every length."""
+    w = wl.Workload("ragged", 4, 1, 16, 2, ctx_lens=[3000, 1, 1300, 7777], n_needles=8,
+                    capacity=8192, poison_tail=True, seed=3100)
+    run_and_compare(w, "ragged-poison")
+
+
+def test_ragged_fp8_with_poisoned_tail():
+    w = wl.Workload("ragged fp8", 3, 1, 32, 4, ctx_lens=[4100, 200, 9000], n_needles=8,
+                    kv_dtype="fp8", capacity=9216, poison_tail=True, seed=3150)
+    run_and_compare(w, "ragged-fp8")
+
+
+def test_identical_keys_ties_go_to_lower_positions():
+    w = wl.Workload("identical keys", 1, 1, 16, 2, ctx_lens=[6000], identical_keys=True, seed=3200)
+    got, _ = run_and_compare(w, "identical-keys")
+    for g in range(2):
+        assert got["idx"][0, 0, g].tolist() == list(range(1024)) + list(range(6000 - 128, 6000))
+
+
+def test_identical_keys_large_tie_set():
+    """More equal scores than the boundary buffer holds: the ordered fallback path."""
+    w = wl.Workload("identical keys 20k", 1, 1, 16, 2, ctx_lens=[20000], identical_keys=True,
+                    seed=3201)
+    got, _ = run_and_compare(w, "identical-keys-20k", with_probs=False)
+    for g in range(2):
+        assert got["idx"][0, 0, g].tolist() == list(range(1024)) + list(range(20000 - 128, 20000))
+
+
+def test_zero_queries_uniform_attention():
+    w = wl.Workload("zero q", 1, 1, 16, 2, ctx_lens=[3000], zero_q=True, seed=3300)
+    got, _ = run_and_compare(w, "zero-q")
+    for g in range(2):
+        assert got["idx"][0, 0, g].tolist() == list(range(1024)) + list(range(3000 - 128, 3000))
+
+
+def test_dominant_needle():
+    w = wl.Workload("needle x100", 1, 1, 16, 2, ctx_lens=[4096], n_needles=1, needle_scale=100.0,
+                    seed=3400)
+    run_and_compare(w, "needle-x100")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4), (12, 2)])
+def test_smaller_groups(hq, hkv):
+    w = wl.Workload(f"G{hq // hkv}", 2, 1, hq, hkv, ctx_lens=[2500, 4000], n_needles=4, seed=3500 + hq)
+    run_and_compare(w, f"G{hq // hkv}")
+
+
+@pytest.mark.parametrize("window,topk", [(0, 64), (16, 8), (512, 2048)])
+def test_other_window_and_topk(window, topk):
+    w = wl.Workload("window/topk", 1, 1, 16, 2, ctx_lens=[6000], n_needles=8, seed=3600 + topk)
+    run_and_compare(w, f"w{window}-k{topk}", window=window, topk=topk)
+
+
+def test_block_baseline_mode():
+    w = wl.Workload("block baseline", 2, 1, 32, 4, ctx_lens=[20000, 3001], n_needles=16, seed=3700)
+    run_and_compare(w, "block", mode="block")
+
+
+def test_block_baseline_chunk():
+    w = wl.Workload("block chunk", 1, 16, 32, 4, ctx_lens=[9000], n_needles=16, seed=3701)
+    run_and_compare(w, "block-chunk", mode="block", tokens=[(0, 0), (0, 7), (0, 15)])
+
+
+def test_rows_with_no_visible_position():
+    """ctx_len < Lq leaves the first query tokens with nothing visible: out = 0, idx = -1."""
+    w = wl.Workload("empty rows", 2, 4, 16, 2, ctx_lens=[6, 3000], seed=3800)
+    from long_context_decode_full_amd.runner import HybridBlockDevice
+    _announce("empty-rows", w)
+    inp = wl.make_inputs(w)
+    inp["ctx_len"][0] = 2          # rows j = 0, 1 of sequence 0 see nothing
+    dev = HybridBlockDevice(inp, max_ctx_len=3000)
+    dev.step()
+    got = dev.results()
+    assert np.all(got["out_full"][0, :2] == 0) and np.all(got["idx"][0, :2] == -1)
+    for layer in range(3):
+        assert np.all(got["out_sparse"][layer][0, :2] == 0)
+    ref = oracle.hybrid_block(inp, tokens=[(0, 2), (0, 3), (1, 0), (1, 3)])
+    for (b, j), r in ref.items():
+        assert_out_close(got["out_full"][b, j], r["out_full"])
+        for g in range(2):
+            check_idx_row(got["idx"][b, j, g], r["idx"][g], r["s"][g], r["n"], 128, 1024)
+
+
+# ------------------------------------------------------------------ properties
+def test_deterministic_and_split_invariant(monkeypatch):
+    from long_context_decode_full_amd.runner import HybridBlockDevice
+    w = wl.Workload("split invariance", 1, 1, 32, 4, ctx_lens=[70000], n_needles=32, seed=3900)
+    _announce("split-invariance", w)
+    inp = wl.make_inputs(w)
+    outs = []
+    for split in ("", "256", "4096", "20480"):
+        if split:
+            monkeypatch.setenv("HS2_SPLIT_LEN", split)
+        else:
+            monkeypatch.delenv("HS2_SPLIT_LEN", raising=False)
+        print(f"[gpu case] split-invariance HS2_SPLIT_LEN={split or 'default'}", flush=True)
+        dev = HybridBlockDevice(inp)
+        for rep in range(2):
+            dev.step()
+            outs.append((split, rep, dev.results()))
+    base = outs[0][2]
+    for split, rep, r in outs[1:]:
+        assert np.array_equal(r["idx"], base["idx"]), f"idx changed (split {split}, rep {rep})"
+        if split == outs[0][0]:
+            assert np.array_equal(r["out_full"], base["out_full"]), "not bitwise deterministic"
+        assert np.max(np.abs(r["out_full"] - base["out_full"])) <= 1e-5
+        for layer in range(3):
+            assert np.max(np.abs(r["out_sparse"][layer] - base["out_sparse"][layer])) <= 1e-5
+
+
+def test_sparse_over_all_positions_equals_dense():
+    """An index row naming every visible position turns a sparse layer into dense attention."""
+    from long_context_decode_full_amd.runner import HybridBlockDevice
+    w = wl.Workload("sparse=dense", 1, 1, 32, 4, ctx_lens=[1000], n_needles=4, seed=4000)
+    _announce("sparse-equals-dense", w)
+    inp = wl.make_inputs(w)
+    dev = HybridBlockDevice(inp, window=1000, topk=2000)
+    dev.step()
+    got = dev.results()
+    inp2 = dict(inp)
+    inp2["q_full"] = inp["q_sparse"][0]
+    dev2 = HybridBlockDevice(inp2, window=1000, topk=2000)
+    dev2.full()
+    dense = dev2.results()["out_full"]
+    assert np.max(np.abs(got["out_sparse"][0] - dense)) <= 2e-6
