@@ -91,6 +91,8 @@ def main():
     ap.add_argument("--workload", default="million",
                     help="tiny | batched | fp8_256k | million")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -98,6 +100,17 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        # A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
+        # counters give the factor between counter readings and bytes moved.
+        nbytes = 1 << 30
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": 5}), flush=True)
+        return
     from long_context_decode_full_amd import hs2_timer_collect, hs2_timer_enable
     from long_context_decode_full_amd import workloads as wl
     from long_context_decode_full_amd.runner import HybridBlockDevice

@@ -75,7 +75,8 @@ Layout make_layout(const hs2_attn_desc* d) {
   L.n_sel = (int64_t)d->batch * d->q_len * d->n_kv_heads;
   L.G = d->n_q_heads / d->n_kv_heads;
   L.S = d->select_mode == HS2_SELECT_TOKEN ? d->window + d->topk : d->block_size * d->n_blocks;
-  L.logit_stride = ceil_div(d->max_ctx_len, 64) * 64;
+  // one spare row per selection receives the scan's masked logit stores
+  L.logit_stride = ceil_div(d->max_ctx_len + 1, 64) * 64;
 
   // Dense scan: enough splits to give ~2 workgroups per CU in one residency round.
   const int64_t rows = L.n_sel * d->max_ctx_len;

@@ -12,19 +12,22 @@
 //
 // Work decomposition (wave64, 4 waves per workgroup):
 //   grid = (split, KV head g, b*Lq + j); a workgroup owns `split_len` consecutive
-//   positions, each wave a contiguous quarter, walked 8 rows per step.
-//   Inside a wave, lane = 8*tg + r: the 8 lanes of token group tg share one row,
-//   lane r holds 16 of its 128 dims (two 16-byte loads of bf16, one of fp8), so a
-//   step reads 8 whole rows = 2 KiB (bf16) with 128-bit coalesced loads.
+//   positions, each wave a contiguous quarter, walked 4 rows per step.
+//   Inside a wave, lane = 16*rg + r: the 16 lanes of row group rg share one row and
+//   lane r holds dims [8r, 8r+8) (one 16-byte load of bf16, 8 bytes of fp8), so a
+//   step reads 4 whole rows (1 KiB of K and 1 KiB of V in bf16) with coalesced
+//   loads.  Loads run kPrefetch steps ahead through a register ring, so a wave keeps
+//   several KiB in flight while it computes.
 //   QK: each lane forms 8 partial dot products (one per head slot) with
-//   v_dot2_f32_bf16, then a 3-step DPP butterfly (row_half_mirror, quad_perm x2,
-//   quad_perm x1) reduce-scatters them so lane r ends with the full logit of head
-//   code(r).  A matching DPP all-gather hands every lane the 8 probabilities of
-//   its row for the P.V update into its 8x16 fp32 accumulators.
-//   Each token group runs its own online softmax (no cross-group traffic in the
+//   v_dot2_f32_bf16; a 4-step DPP butterfly (row_ror:8, row_half_mirror,
+//   quad_perm x2 halving, then quad_perm x1 adding) reduce-scatters them so each
+//   lane ends with the full logit of head P(r) (lanes r and r^1 share a head).  The
+//   reverse DPP all-gather gives every lane the 8 probabilities of its row for the
+//   P.V update into its 8 x 8 fp32 accumulators.
+//   Each row group runs its own online softmax (no cross-group traffic in the
 //   loop); the running max is only raised when a logit exceeds it by 8 (log2
 //   units), so rescales are rare.  Streams are merged at the end of the split:
-//   DPP/shuffles across token groups, LDS across the 4 waves.
+//   shuffles across the 4 row groups, LDS across the 4 waves.
 #include "hs2_device.h"
 #include "hs2_internal.h"
 
@@ -33,65 +36,162 @@ namespace {
 
 constexpr float kSlack = 8.0f;
 constexpr int kThreads = 256;
+constexpr int kPrefetch = 4;
 
-// Head held in register slot i of lane r is (i ^ code(r)); the butterfly below
-// leaves lane r with the complete sum for head code(r).
-__device__ __forceinline__ int lane_code(int r) { return r ^ ((r >> 2) * 3); }
+// LDS of one workgroup: per-wave logit staging during the scan, reused for the
+// cross-wave merge afterwards.
+#ifndef HS2_LOGIT_STORE
+#define HS2_LOGIT_STORE(ptr, val) (*reinterpret_cast<float2*>(ptr) = (val))
+#endif
 
-// Element e (0..15) of lane r's slice of a 128-dim row.
-template <bool kFp8>
-__device__ __forceinline__ int elem_dim(int r, int e) {
-  if (kFp8) return 16 * r + e;
-  return 64 * (e >> 3) + 8 * r + (e & 7);
+union ScanLds {
+  float logit[4][kPrefetch * 4 * 8];
+  struct {
+    float o[4][8][kHeadDim];
+    float m[4][8];
+    float z[4][8];
+  } merge;
+};
+
+// Head whose logit lane r (0..15 inside its row group) holds after the butterfly;
+// register slot i of lane r holds head i ^ head_of(r).  head_of is the linear map
+// with head_of(8) = 4, head_of(7) = 2, head_of(2) = 1, head_of(1) = 0, which makes
+// every butterfly partner hold the matching head in the matching slot.
+__device__ __forceinline__ int head_of(int r) {
+  const int a = (r >> 3) & 1;
+  const int r1 = r ^ (a * 8);
+  const int b = (r1 >> 2) & 1;
+  const int r2 = r1 ^ (b * 7);
+  const int c = (r2 >> 1) & 1;
+  return (4 * a) ^ (2 * b) ^ c;
 }
 
-// All-gather within the 8-lane group: out[i] = value of the lane holding head i ^ code(r).
+// All-gather inside the 16-lane row group: out[i] = probability of head i ^ head_of(r).
 __device__ __forceinline__ void gather8(float x, float (&out)[8]) {
   out[0] = x;
-  out[1] = dpp<kDppXor1>(out[0]);
-  out[2] = dpp<kDppXor2>(out[0]);
-  out[3] = dpp<kDppXor2>(out[1]);
-  out[4] = dpp<kDppMirror8>(out[0]);
-  out[5] = dpp<kDppMirror8>(out[1]);
-  out[6] = dpp<kDppMirror8>(out[2]);
-  out[7] = dpp<kDppMirror8>(out[3]);
+  out[1] = dpp<kDppXor2>(out[0]);
+  out[2] = dpp<kDppMirror8>(out[0]);
+  out[3] = dpp<kDppMirror8>(out[1]);
+  out[4] = dpp<kDppRor8>(out[0]);
+  out[5] = dpp<kDppRor8>(out[1]);
+  out[6] = dpp<kDppRor8>(out[2]);
+  out[7] = dpp<kDppRor8>(out[3]);
 }
 
 struct RowData {
-  uint32_t k[8];   // bf16 pairs of the lane's 16 dims (fp8 codes decoded to bf16)
-  uint32_t v[8];   // raw words: bf16 pairs, or fp8 codes in v[0..3]
-  float ks, vs;    // fp8 scales
+  uint32_t k[4];   // bf16: 4 pairs of the lane's 8 dims; fp8: k[0..1] hold 8 codes
+  uint32_t v[4];
+  float ks, vs;    // fp8 per-token scales
 };
 
 template <bool kFp8>
 __device__ __forceinline__ void load_row(const uint8_t* __restrict__ kb, const uint8_t* __restrict__ vb,
                                          const float* __restrict__ ksb, const float* __restrict__ vsb,
-                                         int64_t t, int r, RowData& d) {
+                                         uint32_t t, int r, RowData& d) {
   if (kFp8) {
-    const uint4 kw = *reinterpret_cast<const uint4*>(kb + t * 128 + 16 * r);
-    const uint4 vw = *reinterpret_cast<const uint4*>(vb + t * 128 + 16 * r);
-    d.k[0] = kw.x; d.k[1] = kw.y; d.k[2] = kw.z; d.k[3] = kw.w;
-    d.v[0] = vw.x; d.v[1] = vw.y; d.v[2] = vw.z; d.v[3] = vw.w;
+    const uint2 kw = *reinterpret_cast<const uint2*>(kb + (uint64_t)t * 128 + 8 * r);
+    const uint2 vw = *reinterpret_cast<const uint2*>(vb + (uint64_t)t * 128 + 8 * r);
+    d.k[0] = kw.x; d.k[1] = kw.y; d.k[2] = 0u; d.k[3] = 0u;
+    d.v[0] = vw.x; d.v[1] = vw.y; d.v[2] = 0u; d.v[3] = 0u;
     d.ks = ksb[t];
     d.vs = vsb[t];
   } else {
-    const uint8_t* kr = kb + t * 256;
-    const uint8_t* vr = vb + t * 256;
-    const uint4 k0 = *reinterpret_cast<const uint4*>(kr + 16 * r);
-    const uint4 k1 = *reinterpret_cast<const uint4*>(kr + 128 + 16 * r);
-    const uint4 v0 = *reinterpret_cast<const uint4*>(vr + 16 * r);
-    const uint4 v1 = *reinterpret_cast<const uint4*>(vr + 128 + 16 * r);
-    d.k[0] = k0.x; d.k[1] = k0.y; d.k[2] = k0.z; d.k[3] = k0.w;
-    d.k[4] = k1.x; d.k[5] = k1.y; d.k[6] = k1.z; d.k[7] = k1.w;
-    d.v[0] = v0.x; d.v[1] = v0.y; d.v[2] = v0.z; d.v[3] = v0.w;
-    d.v[4] = v1.x; d.v[5] = v1.y; d.v[6] = v1.z; d.v[7] = v1.w;
+    const uint4 kw = *reinterpret_cast<const uint4*>(kb + (uint64_t)t * 256 + 16 * r);
+    const uint4 vw = *reinterpret_cast<const uint4*>(vb + (uint64_t)t * 256 + 16 * r);
+    d.k[0] = kw.x; d.k[1] = kw.y; d.k[2] = kw.z; d.k[3] = kw.w;
+    d.v[0] = vw.x; d.v[1] = vw.y; d.v[2] = vw.z; d.v[3] = vw.w;
     d.ks = 1.0f;
     d.vs = 1.0f;
   }
 }
 
+// Online-softmax state of one lane plus its 8 x 8 output accumulators.
+struct LaneState {
+  float o[8][8];
+  float m, z;
+};
+
+// One row for this lane's row group: logits of the 8 heads (returned: the logit of
+// head `hown`, log2 domain), online-softmax update and P.V accumulation.
+template <bool kFp8>
+__device__ __forceinline__ float process_row(const uint32_t (&qp)[8][4], const RowData& cur,
+                                             bool cur_valid, float scale_log2, LaneState& ls) {
+  uint32_t kw[4];
+  if (kFp8) {
+    kw[0] = fp8x2_to_bf16x2(cur.k[0], false);
+    kw[1] = fp8x2_to_bf16x2(cur.k[0], true);
+    kw[2] = fp8x2_to_bf16x2(cur.k[1], false);
+    kw[3] = fp8x2_to_bf16x2(cur.k[1], true);
+  } else {
+    kw[0] = cur.k[0]; kw[1] = cur.k[1]; kw[2] = cur.k[2]; kw[3] = cur.k[3];
+  }
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float s = dot2_bf16(qp[i][0], kw[0], 0.0f);
+    s = dot2_bf16(qp[i][1], kw[1], s);
+    s = dot2_bf16(qp[i][2], kw[2], s);
+    acc[i] = dot2_bf16(qp[i][3], kw[3], s);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] += dpp<kDppRor8>(acc[i + 4]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) acc[i] += dpp<kDppMirror8>(acc[i + 2]);
+  acc[0] += dpp<kDppXor2>(acc[1]);
+  acc[0] += dpp<kDppXor1>(acc[0]);
+
+  float l = acc[0] * scale_log2;
+  if (kFp8) l *= cur.ks;
+  l = cur_valid ? l : kNegInf;
+
+  const bool up = l > ls.m + kSlack;
+  if (wave_any(up)) {
+    const float mn = up ? l : ls.m;
+    const float alpha = up ? fast_exp2(ls.m - mn) : 1.0f;
+    float al[8];
+    gather8(alpha, al);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ls.o[i][e] *= al[i];
+    ls.z *= alpha;
+    ls.m = mn;
+  }
+  const float p = cur_valid ? fast_exp2(l - ls.m) : 0.0f;
+  ls.z += p;
+  float pv[8];
+  gather8(kFp8 ? p * cur.vs : p, pv);
+  if (kFp8) {
+#pragma unroll
+    for (int u2 = 0; u2 < 2; ++u2) {
+      const f32x2_t lo = fp8x2_to_f32(cur.v[u2], false);
+      const f32x2_t hi = fp8x2_to_f32(cur.v[u2], true);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ls.o[i][4 * u2 + 0] = __builtin_fmaf(pv[i], lo.x, ls.o[i][4 * u2 + 0]);
+        ls.o[i][4 * u2 + 1] = __builtin_fmaf(pv[i], lo.y, ls.o[i][4 * u2 + 1]);
+        ls.o[i][4 * u2 + 2] = __builtin_fmaf(pv[i], hi.x, ls.o[i][4 * u2 + 2]);
+        ls.o[i][4 * u2 + 3] = __builtin_fmaf(pv[i], hi.y, ls.o[i][4 * u2 + 3]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float v0 = bf16_lo(cur.v[w]);
+      const float v1 = bf16_hi(cur.v[w]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ls.o[i][2 * w] = __builtin_fmaf(pv[i], v0, ls.o[i][2 * w]);
+        ls.o[i][2 * w + 1] = __builtin_fmaf(pv[i], v1, ls.o[i][2 * w + 1]);
+      }
+    }
+  }
+  return l;
+}
+
 template <bool kSparse, bool kFp8>
-__global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
+  __shared__ ScanLds lds_u;
   const int split = blockIdx.x;
   const int g = blockIdx.y;
   const int bj = blockIdx.z;
@@ -99,11 +199,12 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a) {
   const int j = bj - b * a.Lq;
   const int64_t sel = (int64_t)bj * a.Hkv + g;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave-uniform: keeps the wave's ranges and buffer descriptors in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int tg = lane >> 3;
-  const int r = lane & 7;
-  const int code = lane_code(r);
+  const int rg = lane >> 4;
+  const int r = lane & 15;
+  const int hown = head_of(r);
 
   int64_t ctx = a.ctx_len[b];
   ctx = ctx < 0 ? 0 : (ctx > a.ctx_max ? a.ctx_max : ctx);
@@ -118,23 +219,19 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a) {
   const int64_t w_begin = p_begin + (int64_t)wave * wave_len;
   int64_t w_end = w_begin + wave_len;
   w_end = w_end < p_end ? w_end : p_end;
-  const int nsteps = w_end > w_begin ? (int)((w_end - w_begin + 7) >> 3) : 0;
+  const int nsteps = w_end > w_begin ? (int)((w_end - w_begin + 3) >> 2) : 0;
 
-  // Query slice: slot i holds head i ^ code (zero for slots beyond the group).
-  uint32_t qp[8][8];
+  // Query slice: slot i holds dims [8r, 8r+8) of head i ^ hown (zero beyond the group).
+  uint32_t qp[8][4];
   const uint16_t* qrow = a.q + ((int64_t)bj * a.Hq + (int64_t)g * a.G) * kHeadDim;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int head = i ^ code;
+    const int head = i ^ hown;
     if (head < a.G) {
-      const uint16_t* qh = qrow + head * kHeadDim;
-      const uint4 x0 = *reinterpret_cast<const uint4*>(qh + (kFp8 ? 16 * r : 8 * r));
-      const uint4 x1 = *reinterpret_cast<const uint4*>(qh + (kFp8 ? 16 * r + 8 : 64 + 8 * r));
-      qp[i][0] = x0.x; qp[i][1] = x0.y; qp[i][2] = x0.z; qp[i][3] = x0.w;
-      qp[i][4] = x1.x; qp[i][5] = x1.y; qp[i][6] = x1.z; qp[i][7] = x1.w;
+      const uint4 x = *reinterpret_cast<const uint4*>(qrow + head * kHeadDim + 8 * r);
+      qp[i][0] = x.x; qp[i][1] = x.y; qp[i][2] = x.z; qp[i][3] = x.w;
     } else {
-#pragma unroll
-      for (int w = 0; w < 8; ++w) qp[i][w] = 0u;
+      qp[i][0] = qp[i][1] = qp[i][2] = qp[i][3] = 0u;
     }
   }
 
@@ -147,129 +244,85 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a) {
   const int32_t* irow = kSparse ? a.idx + sel * a.S : nullptr;
   float* lrow = kSparse ? nullptr : a.logits + sel * a.logit_stride * 8;
 
-  float o[8][16];
+  LaneState ls;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[i][e] = 0.0f;
-  float m = kNegInf;
-  float z = 0.0f;
+    for (int e = 0; e < 8; ++e) ls.o[i][e] = 0.0f;
+  ls.m = kNegInf;
+  ls.z = 0.0f;
 
-  auto row_of = [&](int st, bool& valid) -> int64_t {
-    const int64_t pos = w_begin + (int64_t)st * 8 + tg;
-    valid = pos < w_end;
-    if (kSparse) {
-      const int ti = valid ? irow[pos] : -1;
-      valid = valid && ti >= 0 && (int64_t)ti < n;
-      return valid ? (int64_t)ti : 0;
+  // Rows are < cap < 2^31, so 32-bit row numbers suffice.
+  const int32_t wb = (int32_t)w_begin;
+  const int32_t we = (int32_t)w_end;
+  const int32_t n32 = (int32_t)n;
+
+  // Both loops below are straight-line per step: every prefetch load is issued
+  // (steps past the end read a harmless row and are masked), and there are no
+  // loads or stores under branches, so the waitcnt pass keeps kPrefetch steps of
+  // loads in flight.
+  if (!kSparse) {
+    // Logits of one ring turn (kPrefetch steps x 4 rows x 8 heads) are staged in LDS
+    // and written with one 8-byte store per lane: 512 contiguous bytes per wave.
+    float* mylog = lds_u.logit[wave];
+    const uint32_t span = we > wb ? (uint32_t)(we - wb) : 0u;
+    // rows past the wave's range re-read its last row (in bounds) and are masked
+    const uint32_t last = span > 0 ? span - 1 : 0u;
+    const int nsteps_pad = (nsteps + kPrefetch - 1) / kPrefetch * kPrefetch;
+    RowData buf[kPrefetch];
+    if (nsteps > 0) {
+#pragma unroll
+      for (int u = 0; u < kPrefetch; ++u)
+        load_row<kFp8>(kb, vb, ksb, vsb, (uint32_t)wb + min((uint32_t)(u * 4 + rg), last), r, buf[u]);
     }
-    return valid ? pos : w_begin;
-  };
-
-  RowData cur, nxt;
-  bool cur_valid = false, nxt_valid = false;
-  int64_t cur_t = 0, nxt_t = 0;
-  if (nsteps > 0) {
-    cur_t = row_of(0, cur_valid);
-    load_row<kFp8>(kb, vb, ksb, vsb, cur_t, r, cur);
+    for (int base = 0; base < nsteps_pad; base += kPrefetch) {
+#pragma unroll
+      for (int u = 0; u < kPrefetch; ++u) {
+        // consume ring slot u, then refill it kPrefetch steps ahead (no register copy)
+        const uint32_t rel = (uint32_t)((base + u) * 4 + rg);
+        const float l = process_row<kFp8>(qp, buf[u], rel < span, a.scale_log2, ls);
+        load_row<kFp8>(kb, vb, ksb, vsb, (uint32_t)wb + min(rel + 4 * kPrefetch, last), r, buf[u]);
+        if ((r & 1) == 0) mylog[(u * 4 + rg) * 8 + hown] = l;
+      }
+      // lane -> row base*4 + lane/4, heads 2*(lane%4) .. +1
+      const uint32_t rel = (uint32_t)(base * 4 + (lane >> 2));
+      const uint64_t row = rel < span ? (uint64_t)(uint32_t)wb + rel : (uint64_t)a.logit_stride - 1;
+      const float2 x = *reinterpret_cast<const float2*>(mylog + lane * 2);
+      HS2_LOGIT_STORE(lrow + row * 8 + 2 * (lane & 3), x);
+    }
+  } else {
+    // Sparse mode: index entries first (one batch per ring of kPrefetch steps), then
+    // the gathered rows, so no row load waits behind an index load.
+    for (int base = 0; base < nsteps; base += kPrefetch) {
+      int32_t trow[kPrefetch];
+      bool tval[kPrefetch];
+#pragma unroll
+      for (int u = 0; u < kPrefetch; ++u) {
+        const int32_t pos = wb + (base + u) * 4 + rg;
+        tval[u] = pos < we;
+        trow[u] = tval[u] ? irow[pos] : -1;
+      }
+      RowData buf[kPrefetch];
+#pragma unroll
+      for (int u = 0; u < kPrefetch; ++u) {
+        tval[u] = tval[u] && trow[u] >= 0 && trow[u] < n32;
+        load_row<kFp8>(kb, vb, ksb, vsb, tval[u] ? (uint32_t)trow[u] : 0u, r, buf[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kPrefetch; ++u)
+        (void)process_row<kFp8>(qp, buf[u], tval[u], a.scale_log2, ls);
+    }
   }
+  float (&o)[8][8] = ls.o;
+  const float m = ls.m;
+  const float z = ls.z;
 
-  for (int st = 0; st < nsteps; ++st) {
-    if (st + 1 < nsteps) {
-      nxt_t = row_of(st + 1, nxt_valid);
-      load_row<kFp8>(kb, vb, ksb, vsb, nxt_t, r, nxt);
-    }
-
-    // ---- logits: 8 partial dot products, then DPP reduce-scatter over the 8 lanes
-    uint32_t kw[8];
-    if (kFp8) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        kw[2 * u] = fp8x2_to_bf16x2(cur.k[u], false);
-        kw[2 * u + 1] = fp8x2_to_bf16x2(cur.k[u], true);
-      }
-    } else {
-#pragma unroll
-      for (int w = 0; w < 8; ++w) kw[w] = cur.k[w];
-    }
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float s = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) s = dot2_bf16(qp[i][w], kw[w], s);
-      acc[i] = s;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += dpp<kDppMirror8>(acc[i + 4]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) acc[i] += dpp<kDppXor2>(acc[i + 2]);
-    acc[0] += dpp<kDppXor1>(acc[1]);
-
-    float l = acc[0] * a.scale_log2;
-    if (kFp8) l *= cur.ks;
-    l = cur_valid ? l : kNegInf;
-    if (!kSparse && cur_valid) lrow[cur_t * 8 + code] = l;
-
-    // ---- online softmax of this token group's stream for head `code`
-    const bool up = l > m + kSlack;
-    if (wave_any(up)) {
-      const float mn = up ? l : m;
-      const float alpha = up ? fast_exp2(m - mn) : 1.0f;
-      float al[8];
-      gather8(alpha, al);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[i][e] *= al[i];
-      z *= alpha;
-      m = mn;
-    }
-    const float p = cur_valid ? fast_exp2(l - m) : 0.0f;
-    z += p;
-    float pv[8];
-    gather8(kFp8 ? p * cur.vs : p, pv);
-
-    // ---- P.V into the lane's 8 x 16 accumulators
-    if (kFp8) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const f32x2_t lo = fp8x2_to_f32(cur.v[u], false);
-        const f32x2_t hi = fp8x2_to_f32(cur.v[u], true);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          o[i][4 * u + 0] = __builtin_fmaf(pv[i], lo.x, o[i][4 * u + 0]);
-          o[i][4 * u + 1] = __builtin_fmaf(pv[i], lo.y, o[i][4 * u + 1]);
-          o[i][4 * u + 2] = __builtin_fmaf(pv[i], hi.x, o[i][4 * u + 2]);
-          o[i][4 * u + 3] = __builtin_fmaf(pv[i], hi.y, o[i][4 * u + 3]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const float v0 = bf16_lo(cur.v[w]);
-        const float v1 = bf16_hi(cur.v[w]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          o[i][2 * w] = __builtin_fmaf(pv[i], v0, o[i][2 * w]);
-          o[i][2 * w + 1] = __builtin_fmaf(pv[i], v1, o[i][2 * w + 1]);
-        }
-      }
-    }
-
-    cur = nxt;
-    cur_valid = nxt_valid;
-    cur_t = nxt_t;
-  }
-
-  // ---- merge the 8 token-group streams of this wave (same head = same r)
+  // ---- merge the 4 row-group streams of this wave (same r = same head)
   float M = m;
-  M = fmaxf(M, dpp<kDppRor8>(M));
   M = fmaxf(M, shfl_xor(M, 16));
   M = fmaxf(M, shfl_xor(M, 32));
   const float f = (m == kNegInf) ? 0.0f : fast_exp2(m - M);
   float zz = z * f;
-  zz += dpp<kDppRor8>(zz);
   zz += shfl_xor(zz, 16);
   zz += shfl_xor(zz, 32);
   float fg[8];
@@ -277,26 +330,28 @@ __global__ __launch_bounds__(kThreads, 2) void scan_kernel(ScanArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < 8; ++e) {
       float x = o[i][e] * fg[i];
-      x += dpp<kDppRor8>(x);
       x += shfl_xor(x, 16);
       x += shfl_xor(x, 32);
       o[i][e] = x;
     }
 
-  __shared__ float lds_o[4][8][kHeadDim];
-  __shared__ float lds_m[4][8];
-  __shared__ float lds_z[4][8];
-  if (tg == 0) {
+  float (&lds_o)[4][8][kHeadDim] = lds_u.merge.o;
+  float (&lds_m)[4][8] = lds_u.merge.m;
+  float (&lds_z)[4][8] = lds_u.merge.z;
+  __syncthreads();   // every wave is done with its logit staging area
+  if (rg == 0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int head = i ^ code;
+      const int head = i ^ hown;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) lds_o[wave][head][elem_dim<kFp8>(r, e)] = o[i][e];
+      for (int e = 0; e < 8; ++e) lds_o[wave][head][8 * r + e] = o[i][e];
     }
-    lds_m[wave][code] = M;
-    lds_z[wave][code] = zz;
+    if ((r & 1) == 0) {
+      lds_m[wave][hown] = M;
+      lds_z[wave][hown] = zz;
+    }
   }
   __syncthreads();
 
