@@ -140,6 +140,16 @@ def main():
     st, scan_ms, scan_n, gather_ms, gather_n = hs2_timer_collect()
     assert st == 0 and scan_n == args.steps, (st, scan_n)
 
+    # per-launch distribution of the scan (each step collected on its own)
+    per_scan = []
+    hs2_timer_enable(True)
+    for _ in range(min(args.steps, 30)):
+        dev.step()
+        st2, sm, sn, _, _ = hs2_timer_collect()
+        per_scan.append(sm * 1e3 / max(sn, 1))
+    hs2_timer_enable(False)
+    per_scan.sort()
+
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     ctx = int(np.sum(inp["ctx_len"]))
     value = ctx / (ms_per_step * 1e-3)
@@ -172,6 +182,7 @@ def main():
         },
         "kv_gbps": achieved,
         "scan_us": scan_avg_s * 1e6,
+        "scan_us_min_med_max": [per_scan[0], per_scan[len(per_scan) // 2], per_scan[-1]],
         "sparse_layer_us": gather_ms * 1e3 / max(gather_n, 1),
         "roofline": {
             "bound": "hbm",

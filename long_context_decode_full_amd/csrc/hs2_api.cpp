@@ -17,10 +17,10 @@ namespace hs2 {
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kScanTargetWorkgroups = 512;   // 2 per CU at 2 waves/SIMD on 256 CUs
+constexpr int kScanTargetWorkgroups = 768;   // 3 per CU (3 waves/SIMD) on 256 CUs
 constexpr int kMaxSplits = 2048;             // combine kernel keeps one weight per split in LDS
 constexpr int kSparseSplitLen = 64;          // index entries per sparse workgroup
-constexpr int kSelectChunk = 4096;           // positions per workgroup in the selection passes
+constexpr int kSelectChunk = kSelectChunkLen;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -32,6 +32,9 @@ struct Layout {
   int32_t split_len = 0, n_split = 0;
   int32_t split_len_sp = 0, n_split_sp = 0;
   int32_t chunk_len = 0, n_chunks = 0;
+  int32_t rec_split_len = 0, rec_n_split = 0;   // scan geometry of the record path
+  bool fast_ok = false;                         // record path usable for this descriptor
+  size_t off_cand_pos = 0, off_cand_s = 0, off_cand_count = 0, off_hist_part = 0;
   size_t off_logits = 0, off_part = 0, off_mz = 0, off_s = 0, off_selblk = 0, off_hist2 = 0,
          off_hist3 = 0, off_winners = 0, off_boundary = 0, total = 0;
 };
@@ -88,6 +91,18 @@ Layout make_layout(const hs2_attn_desc* d) {
   L.split_len = (int32_t)split;
   L.n_split = (int32_t)ceil_div(d->max_ctx_len, split);
 
+  // Record path: a split's records stay in LDS until it is done, which bounds the split.
+  int64_t rsplit = ceil_div(ceil_div(rows, kScanTargetWorkgroups), 256) * 256;
+  rsplit = env_int("HS2_SPLIT_LEN", (int)std::min<int64_t>(rsplit, 1 << 30));
+  rsplit = ceil_div(rsplit, 256) * 256;
+  if (rsplit < 256) rsplit = 256;
+  if (rsplit > kMaxRecordSplit) rsplit = kMaxRecordSplit;
+  L.rec_split_len = (int32_t)rsplit;
+  L.rec_n_split = (int32_t)ceil_div(d->max_ctx_len, rsplit);
+  L.fast_ok = d->select_mode == HS2_SELECT_TOKEN &&
+              ceil_div(d->max_ctx_len, kSelectChunk) <= kMaxFastChunks &&
+              L.rec_n_split <= kMaxSplits;
+
   int64_t sp = env_int("HS2_SPARSE_SPLIT_LEN", kSparseSplitLen);
   sp = ceil_div(sp, 32) * 32;
   while (ceil_div(L.S, sp) > kMaxSplits) sp *= 2;
@@ -98,7 +113,7 @@ Layout make_layout(const hs2_attn_desc* d) {
   L.n_chunks = (int32_t)ceil_div(d->max_ctx_len, kSelectChunk);
 
   const int64_t n = L.n_sel;
-  const int64_t nsplit_max = std::max(L.n_split, L.n_split_sp);
+  const int64_t nsplit_max = std::max({L.n_split, L.n_split_sp, L.rec_n_split});
   size_t off = 0;
   L.off_logits = off; off = align_up(off + (size_t)n * L.logit_stride * 8 * sizeof(float));
   L.off_part = off;   off = align_up(off + (size_t)n * nsplit_max * L.G * kPartStride * sizeof(float));
@@ -109,6 +124,13 @@ Layout make_layout(const hs2_attn_desc* d) {
   L.off_hist3 = off;  off = align_up(off + (size_t)n * kHist3Bins * sizeof(uint32_t));
   L.off_winners = off; off = align_up(off + (size_t)n * std::max(d->topk, 1) * sizeof(int32_t));
   L.off_boundary = off; off = align_up(off + (size_t)n * kBoundaryCap * sizeof(uint2));
+  if (L.fast_ok) {
+    const size_t slots = (size_t)n * L.n_chunks * kSelectChunk;
+    L.off_cand_pos = off; off = align_up(off + slots * sizeof(int32_t));
+    L.off_cand_s = off;   off = align_up(off + slots * sizeof(float));
+    L.off_cand_count = off; off = align_up(off + (size_t)n * L.n_chunks * sizeof(int32_t));
+    L.off_hist_part = off; off = align_up(off + (size_t)n * L.rec_n_split * kFastBins * sizeof(uint16_t));
+  }
   L.total = off;
   return L;
 }
@@ -224,14 +246,21 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   const bool fp8 = desc->kv_dtype == HS2_KV_FP8_E4M3FN;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
 
+  // Record path (default for token selection): compact bound records, exact
+  // re-scoring of the candidates.  Logits path: every position's logits, needed
+  // when the caller wants all probabilities (probs) or for the block comparator.
+  const bool fast = L.fast_ok && probs == nullptr && env_int("HS2_FORCE_LOGITS", 0) == 0;
   ScanArgs sa = scan_args(desc, L, q, k, v, k_scale, v_scale, ctx_len, ws);
   sa.logits = reinterpret_cast<float*>(ws + L.off_logits);
-  sa.n_split = L.n_split;
-  sa.split_len = L.split_len;
+  sa.records = reinterpret_cast<uint16_t*>(ws + L.off_logits);
+  sa.hist_part = reinterpret_cast<uint16_t*>(ws + L.off_hist_part);
+  sa.window = desc->window;
+  sa.n_split = fast ? L.rec_n_split : L.n_split;
+  sa.split_len = fast ? L.rec_split_len : L.split_len;
 
   TimerRec rec;
   const bool timed = timer_begin(stream, 0, &rec);
-  hipError_t e = launch_scan_dense(sa, fp8, desc->batch, stream);
+  hipError_t e = launch_scan_dense(sa, fp8, fast, desc->batch, stream);
   if (timed) timer_end(stream, &rec);
   if (e != hipSuccess) return HS2_ERR_LAUNCH;
 
@@ -239,14 +268,49 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   ca.part = sa.part;
   ca.out = out;
   ca.mz = reinterpret_cast<float*>(ws + L.off_mz);
-  ca.sel_zero = reinterpret_cast<uint32_t*>(ws + L.off_selblk);
+  // the logits path clears the selection control blocks here; the record path
+  // overwrites every histogram bin it reads, so it needs no clearing
+  ca.sel_zero = fast ? nullptr : reinterpret_cast<uint32_t*>(ws + L.off_selblk);
   ca.sel_zero_words = kSelWords;
+  ca.hist_part = fast ? sa.hist_part : nullptr;
+  ca.hist_out = reinterpret_cast<uint32_t*>(ws + L.off_selblk);
   ca.n_sel = (int32_t)L.n_sel;
   ca.Hkv = desc->n_kv_heads;
   ca.G = L.G;
   ca.Hq = desc->n_q_heads;
-  ca.n_split = L.n_split;
+  ca.n_split = sa.n_split;
   if (launch_combine(ca, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+
+  if (fast) {
+    FastSelArgs fa{};
+    fa.records = sa.records;
+    fa.rec_stride = L.logit_stride;
+    fa.mz = ca.mz;
+    fa.ctx_len = ctx_len;
+    fa.ctx_max = desc->max_ctx_len;
+    fa.selblk = ca.hist_out;
+    fa.cand_pos = reinterpret_cast<int32_t*>(ws + L.off_cand_pos);
+    fa.cand_s = reinterpret_cast<float*>(ws + L.off_cand_s);
+    fa.cand_count = reinterpret_cast<int32_t*>(ws + L.off_cand_count);
+    fa.idx = idx;
+    fa.q = static_cast<const uint16_t*>(q);
+    fa.k = static_cast<const uint8_t*>(k);
+    fa.k_scale = k_scale;
+    fa.cap = desc->kv_capacity;
+    fa.scale_log2 = sa.scale_log2;
+    fa.n_chunks = L.n_chunks;
+    fa.n_sel = (int32_t)L.n_sel;
+    fa.Lq = desc->q_len;
+    fa.Hq = desc->n_q_heads;
+    fa.Hkv = desc->n_kv_heads;
+    fa.G = L.G;
+    fa.window = desc->window;
+    fa.topk = desc->topk;
+    fa.S = L.S;
+    if (launch_fast_candidates(fa, fp8, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+    if (launch_fast_final(fa, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+    return HS2_OK;
+  }
 
   SelectArgs sl{};
   sl.logits = sa.logits;

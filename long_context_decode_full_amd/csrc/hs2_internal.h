@@ -16,12 +16,18 @@ constexpr int kHist2Bins = 4096;      // score bits 19..8
 constexpr int kHist3Bins = 256;       // score bits 7..0
 constexpr int kBoundaryCap = 4096;    // boundary-bin entries resolved by one sort
 constexpr int kStateWords = 16;       // u32 per selection state
+// Record-based selection (default token-mode path).
+constexpr int kSelectChunkLen = 4096; // positions per workgroup in the selection passes
+constexpr int kFastBins = 4096;       // histogram of the record keys (top 12 of 16 bits)
+constexpr int kFastShift = 4;
+constexpr int kMaxFastChunks = 8192;  // positions per row <= kMaxFastChunks * kSelectChunkLen
 // Per-selection control block (u32 words), cleared by the combine kernel of every
-// call: [0,16) state, [16,20) pass tickets, [32, 32+kHist1Bins) first histogram.
+// call: [0,16) state, [16,20) pass tickets, [32, 32+4096) first histogram.
 constexpr int kSelCounterOff = 16;
 constexpr int kSelHist1Off = 32;
-constexpr int kSelWords = kSelHist1Off + kHist1Bins;
+constexpr int kSelWords = kSelHist1Off + (kFastBins > kHist1Bins ? kFastBins : kHist1Bins);
 constexpr int kMaxBlocksLds = 16384;  // block mode: blocks per row held in LDS
+constexpr int kMaxRecordSplit = 16384; // records mode: positions per scan workgroup (LDS bound)
 
 // Per-selection state words (u32).
 enum StateWord {
@@ -34,6 +40,7 @@ enum StateWord {
   kStWinCount = 6,   // collect: winners appended
   kStBndCount = 7,   // collect: boundary entries appended (may exceed the cap)
   kStKK = 8,         // number of global positions to select
+  kStLambda = 9,     // record path: fp32 bits of the candidate threshold
 };
 
 struct ScanArgs {
@@ -44,7 +51,10 @@ struct ScanArgs {
   const float* v_scale;
   const int32_t* ctx_len;   // [B]
   const int32_t* idx;       // sparse mode: [n_sel, S]
-  float* logits;            // dense mode: [n_sel, logit_stride, 8] log2-domain logits
+  float* logits;            // logits mode: [n_sel, logit_stride, 8] log2-domain logits
+  uint16_t* records;        // records mode: [n_sel, logit_stride] binary16 bound records
+  uint16_t* hist_part;      // records mode: [n_sel, n_split, kFastBins] key histograms
+  int32_t window;           // records mode: positions >= ctx - window are not candidates
   float* part;              // [n_sel, n_split, G, kPartStride]
   int64_t cap;              // rows per (sequence, KV head)
   int64_t ctx_max;          // ctx_len[] is clamped to [0, ctx_max] (ctx_max <= cap)
@@ -62,6 +72,8 @@ struct CombineArgs {
   float* mz;                // [n_sel, 8, 2] (M, 1/Z) or nullptr
   uint32_t* sel_zero;       // selection words to clear per selection, or nullptr
   int32_t sel_zero_words;   // words per selection in sel_zero
+  const uint16_t* hist_part;  // records mode: per-split key histograms to merge, or nullptr
+  uint32_t* hist_out;       // merged histogram of selection `sel` at hist_out + sel*kSelWords
   int32_t n_sel, Hkv, G, Hq, n_split;
 };
 
@@ -87,7 +99,30 @@ struct SelectArgs {
   int32_t with_hist;        // token mode: build the first histogram
 };
 
-hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, int B, hipStream_t st);
+struct FastSelArgs {
+  const uint16_t* records;  // [n_sel, rec_stride] binary16 bound records
+  int64_t rec_stride;
+  const float* mz;          // [n_sel, 8, 2] (M, 1/Z)
+  const int32_t* ctx_len;
+  int64_t ctx_max;
+  uint32_t* selblk;         // [n_sel, kSelWords]
+  int32_t* cand_pos;        // [n_sel, n_chunks, kSelectChunkLen]
+  float* cand_s;            // same shape: exact scores of the candidates
+  int32_t* cand_count;      // [n_sel, n_chunks]
+  int32_t* idx;             // [n_sel, S]
+  const uint16_t* q;        // full-layer queries (exact re-score)
+  const uint8_t* k;
+  const float* k_scale;
+  int64_t cap;
+  float scale_log2;
+  int32_t n_chunks;
+  int32_t n_sel, Lq, Hq, Hkv, G;
+  int32_t window, topk, S;
+};
+
+hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st);
+hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t st);
+hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st);
 hipError_t launch_scan_sparse(const ScanArgs& a, bool fp8, int B, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_groupsum(const SelectArgs& a, hipStream_t st);

@@ -1,11 +1,16 @@
 // Split-K attention scan for one KV group of G <= 8 query heads, and the split combine.
 //
-// Dense mode: the Full Attention layer of a Hybrid Block (HySparse2 article,
+// Dense modes: the Full Attention layer of a Hybrid Block (HySparse2 article,
 // section 02 "KV Reuse": the full layer computes its own output over the shared
 // cache and, from its attention scores, the positions the sparse layers reuse).
-// Besides the online-softmax partials it stores every position's logits so the
-// selection kernels can form normalised probabilities once the global softmax
-// statistics are known.
+// Besides the online-softmax partials it leaves per-position information for the
+// selection, which needs the global softmax statistics and so runs afterwards:
+//   records mode: a 2-byte bound record per position (row_record) and a histogram
+//     of the record keys of the split's selection candidates, both kept in LDS for
+//     the whole split and written when the split is done (writes interleaved with
+//     the HBM read stream cost far more than their byte count);
+//   logits mode: all 8 head logits per position (32 bytes), for callers that ask
+//     for every position's group-summed probability, and the block comparator.
 // Sparse mode: a Sparse Attention layer gathering the rows named by the index set
 // (section 02: same KV cache, same index set; section 03: window and global
 // tokens share one softmax).
@@ -28,8 +33,7 @@
 //   loop); the running max is only raised when a logit exceeds it by 8 (log2
 //   units), so rescales are rare.  Streams are merged at the end of the split:
 //   shuffles across the 4 row groups, LDS across the 4 waves.
-#include "hs2_device.h"
-#include "hs2_internal.h"
+#include "hs2_rowops.h"
 
 namespace hs2 {
 namespace {
@@ -38,72 +42,17 @@ constexpr float kSlack = 8.0f;
 constexpr int kThreads = 256;
 constexpr int kPrefetch = 4;
 
-// LDS of one workgroup: per-wave logit staging during the scan, reused for the
+enum ScanMode { kDenseLogits = 0, kDenseRecords = 1, kSparseGather = 2 };
+
+// LDS of one workgroup: logit or record staging during the scan, reused for the
 // cross-wave merge afterwards.
-#ifndef HS2_LOGIT_STORE
-#define HS2_LOGIT_STORE(ptr, val) (*reinterpret_cast<float2*>(ptr) = (val))
-#endif
-
-union ScanLds {
-  float logit[4][kPrefetch * 4 * 8];
-  struct {
-    float o[4][8][kHeadDim];
-    float m[4][8];
-    float z[4][8];
-  } merge;
+template <int kMode>
+struct ScanLds {
+  static constexpr int kStage = kMode == kDenseRecords ? kMaxRecordSplit * 2 + kFastBins * 4
+                              : kMode == kDenseLogits ? 4 * 4 * 4 * 8 * 4 : 0;
+  static constexpr int kMerge = (4 * 8 * kHeadDim + 2 * 4 * 8) * 4;
+  static constexpr int kBytes = kStage > kMerge ? kStage : kMerge;
 };
-
-// Head whose logit lane r (0..15 inside its row group) holds after the butterfly;
-// register slot i of lane r holds head i ^ head_of(r).  head_of is the linear map
-// with head_of(8) = 4, head_of(7) = 2, head_of(2) = 1, head_of(1) = 0, which makes
-// every butterfly partner hold the matching head in the matching slot.
-__device__ __forceinline__ int head_of(int r) {
-  const int a = (r >> 3) & 1;
-  const int r1 = r ^ (a * 8);
-  const int b = (r1 >> 2) & 1;
-  const int r2 = r1 ^ (b * 7);
-  const int c = (r2 >> 1) & 1;
-  return (4 * a) ^ (2 * b) ^ c;
-}
-
-// All-gather inside the 16-lane row group: out[i] = probability of head i ^ head_of(r).
-__device__ __forceinline__ void gather8(float x, float (&out)[8]) {
-  out[0] = x;
-  out[1] = dpp<kDppXor2>(out[0]);
-  out[2] = dpp<kDppMirror8>(out[0]);
-  out[3] = dpp<kDppMirror8>(out[1]);
-  out[4] = dpp<kDppRor8>(out[0]);
-  out[5] = dpp<kDppRor8>(out[1]);
-  out[6] = dpp<kDppRor8>(out[2]);
-  out[7] = dpp<kDppRor8>(out[3]);
-}
-
-struct RowData {
-  uint32_t k[4];   // bf16: 4 pairs of the lane's 8 dims; fp8: k[0..1] hold 8 codes
-  uint32_t v[4];
-  float ks, vs;    // fp8 per-token scales
-};
-
-template <bool kFp8>
-__device__ __forceinline__ void load_row(const uint8_t* __restrict__ kb, const uint8_t* __restrict__ vb,
-                                         const float* __restrict__ ksb, const float* __restrict__ vsb,
-                                         uint32_t t, int r, RowData& d) {
-  if (kFp8) {
-    const uint2 kw = *reinterpret_cast<const uint2*>(kb + (uint64_t)t * 128 + 8 * r);
-    const uint2 vw = *reinterpret_cast<const uint2*>(vb + (uint64_t)t * 128 + 8 * r);
-    d.k[0] = kw.x; d.k[1] = kw.y; d.k[2] = 0u; d.k[3] = 0u;
-    d.v[0] = vw.x; d.v[1] = vw.y; d.v[2] = 0u; d.v[3] = 0u;
-    d.ks = ksb[t];
-    d.vs = vsb[t];
-  } else {
-    const uint4 kw = *reinterpret_cast<const uint4*>(kb + (uint64_t)t * 256 + 16 * r);
-    const uint4 vw = *reinterpret_cast<const uint4*>(vb + (uint64_t)t * 256 + 16 * r);
-    d.k[0] = kw.x; d.k[1] = kw.y; d.k[2] = kw.z; d.k[3] = kw.w;
-    d.v[0] = vw.x; d.v[1] = vw.y; d.v[2] = vw.z; d.v[3] = vw.w;
-    d.ks = 1.0f;
-    d.vs = 1.0f;
-  }
-}
 
 // Online-softmax state of one lane plus its 8 x 8 output accumulators.
 struct LaneState {
@@ -116,32 +65,7 @@ struct LaneState {
 template <bool kFp8>
 __device__ __forceinline__ float process_row(const uint32_t (&qp)[8][4], const RowData& cur,
                                              bool cur_valid, float scale_log2, LaneState& ls) {
-  uint32_t kw[4];
-  if (kFp8) {
-    kw[0] = fp8x2_to_bf16x2(cur.k[0], false);
-    kw[1] = fp8x2_to_bf16x2(cur.k[0], true);
-    kw[2] = fp8x2_to_bf16x2(cur.k[1], false);
-    kw[3] = fp8x2_to_bf16x2(cur.k[1], true);
-  } else {
-    kw[0] = cur.k[0]; kw[1] = cur.k[1]; kw[2] = cur.k[2]; kw[3] = cur.k[3];
-  }
-  float acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float s = dot2_bf16(qp[i][0], kw[0], 0.0f);
-    s = dot2_bf16(qp[i][1], kw[1], s);
-    s = dot2_bf16(qp[i][2], kw[2], s);
-    acc[i] = dot2_bf16(qp[i][3], kw[3], s);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] += dpp<kDppRor8>(acc[i + 4]);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) acc[i] += dpp<kDppMirror8>(acc[i + 2]);
-  acc[0] += dpp<kDppXor2>(acc[1]);
-  acc[0] += dpp<kDppXor1>(acc[0]);
-
-  float l = acc[0] * scale_log2;
-  if (kFp8) l *= cur.ks;
+  float l = row_logit<kFp8>(qp, cur, scale_log2);
   l = cur_valid ? l : kNegInf;
 
   const bool up = l > ls.m + kSlack;
@@ -189,9 +113,10 @@ __device__ __forceinline__ float process_row(const uint32_t (&qp)[8][4], const R
   return l;
 }
 
-template <bool kSparse, bool kFp8>
+template <int kMode, bool kFp8>
 __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
-  __shared__ ScanLds lds_u;
+  constexpr bool kSparse = kMode == kSparseGather;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[ScanLds<kMode>::kBytes];
   const int split = blockIdx.x;
   const int g = blockIdx.y;
   const int bj = blockIdx.z;
@@ -199,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
   const int j = bj - b * a.Lq;
   const int64_t sel = (int64_t)bj * a.Hkv + g;
   const int tid = threadIdx.x;
-  // wave-uniform: keeps the wave's ranges and buffer descriptors in SGPRs
+  // wave-uniform: keeps the wave's ranges in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int rg = lane >> 4;
@@ -221,19 +146,8 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
   w_end = w_end < p_end ? w_end : p_end;
   const int nsteps = w_end > w_begin ? (int)((w_end - w_begin + 3) >> 2) : 0;
 
-  // Query slice: slot i holds dims [8r, 8r+8) of head i ^ hown (zero beyond the group).
   uint32_t qp[8][4];
-  const uint16_t* qrow = a.q + ((int64_t)bj * a.Hq + (int64_t)g * a.G) * kHeadDim;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int head = i ^ hown;
-    if (head < a.G) {
-      const uint4 x = *reinterpret_cast<const uint4*>(qrow + head * kHeadDim + 8 * r);
-      qp[i][0] = x.x; qp[i][1] = x.y; qp[i][2] = x.z; qp[i][3] = x.w;
-    } else {
-      qp[i][0] = qp[i][1] = qp[i][2] = qp[i][3] = 0u;
-    }
-  }
+  load_query(a.q + ((int64_t)bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);
 
   const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
   const int rowbytes = kFp8 ? 128 : 256;
@@ -241,8 +155,6 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
   const uint8_t* vb = a.v + head_row0 * rowbytes;
   const float* ksb = kFp8 ? a.k_scale + head_row0 : nullptr;
   const float* vsb = kFp8 ? a.v_scale + head_row0 : nullptr;
-  const int32_t* irow = kSparse ? a.idx + sel * a.S : nullptr;
-  float* lrow = kSparse ? nullptr : a.logits + sel * a.logit_stride * 8;
 
   LaneState ls;
 #pragma unroll
@@ -257,18 +169,27 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
   const int32_t we = (int32_t)w_end;
   const int32_t n32 = (int32_t)n;
 
-  // Both loops below are straight-line per step: every prefetch load is issued
-  // (steps past the end read a harmless row and are masked), and there are no
-  // loads or stores under branches, so the waitcnt pass keeps kPrefetch steps of
-  // loads in flight.
+  // The step loops are straight-line per step: every prefetch load is issued (steps
+  // past the end re-read a valid row and are masked) and no load or store sits under
+  // a branch, so the waitcnt pass keeps kPrefetch steps of loads in flight.
   if (!kSparse) {
-    // Logits of one ring turn (kPrefetch steps x 4 rows x 8 heads) are staged in LDS
-    // and written with one 8-byte store per lane: 512 contiguous bytes per wave.
-    float* mylog = lds_u.logit[wave];
     const uint32_t span = we > wb ? (uint32_t)(we - wb) : 0u;
-    // rows past the wave's range re-read its last row (in bounds) and are masked
     const uint32_t last = span > 0 ? span - 1 : 0u;
     const int nsteps_pad = (nsteps + kPrefetch - 1) / kPrefetch * kPrefetch;
+    float* mylog = reinterpret_cast<float*>(lds_raw) + wave * (kPrefetch * 4 * 8);
+    uint16_t* srec = reinterpret_cast<uint16_t*>(lds_raw);
+    uint16_t* myrec = srec + wave * wave_len;
+    uint32_t* shist = reinterpret_cast<uint32_t*>(lds_raw + kMaxRecordSplit * 2);
+    float* lrow = a.logits + sel * a.logit_stride * 8;
+    // candidates are the positions before the forced window
+    int64_t w0 = n - a.window;
+    w0 = w0 < 0 ? 0 : w0;
+    uint32_t cand_span = w0 > wb ? (uint32_t)(w0 - wb) : 0u;
+    cand_span = cand_span < span ? cand_span : span;
+    if (kMode == kDenseRecords) {
+      for (int i = tid; i < kFastBins; i += kThreads) shist[i] = 0u;
+      __syncthreads();
+    }
     RowData buf[kPrefetch];
     if (nsteps > 0) {
 #pragma unroll
@@ -282,17 +203,41 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
         const uint32_t rel = (uint32_t)((base + u) * 4 + rg);
         const float l = process_row<kFp8>(qp, buf[u], rel < span, a.scale_log2, ls);
         load_row<kFp8>(kb, vb, ksb, vsb, (uint32_t)wb + min(rel + 4 * kPrefetch, last), r, buf[u]);
-        if ((r & 1) == 0) mylog[(u * 4 + rg) * 8 + hown] = l;
+        if (kMode == kDenseLogits) {
+          if ((r & 1) == 0) mylog[(u * 4 + rg) * 8 + hown] = l;
+        } else {
+          const uint16_t rec = row_record(l, r, hown, a.G);
+          if (r == 0) {
+            myrec[rel] = rec;
+            if (rel < cand_span) atomicAdd(&shist[half_order_key(rec) >> kFastShift], 1u);
+          }
+        }
       }
-      // lane -> row base*4 + lane/4, heads 2*(lane%4) .. +1
-      const uint32_t rel = (uint32_t)(base * 4 + (lane >> 2));
-      const uint64_t row = rel < span ? (uint64_t)(uint32_t)wb + rel : (uint64_t)a.logit_stride - 1;
-      const float2 x = *reinterpret_cast<const float2*>(mylog + lane * 2);
-      HS2_LOGIT_STORE(lrow + row * 8 + 2 * (lane & 3), x);
+      if (kMode == kDenseLogits) {
+        // one ring turn of logits (16 rows x 8 heads): lane -> row base*4 + lane/4,
+        // heads 2*(lane%4) .. +1; 512 contiguous bytes per wave
+        const uint32_t rel = (uint32_t)(base * 4 + (lane >> 2));
+        const uint64_t row = rel < span ? (uint64_t)(uint32_t)wb + rel : (uint64_t)a.logit_stride - 1;
+        const float2 x = *reinterpret_cast<const float2*>(mylog + lane * 2);
+        *reinterpret_cast<float2*>(lrow + row * 8 + 2 * (lane & 3)) = x;
+      }
+    }
+    if (kMode == kDenseRecords) {
+      // the split's records and key histogram leave once every wave is done
+      __syncthreads();
+      const int cnt = p_end > p_begin ? (int)(p_end - p_begin) : 0;
+      uint16_t* grec = a.records + sel * a.logit_stride + p_begin;   // 512-byte aligned
+      for (int i = tid; 2 * i + 1 < cnt; i += kThreads)
+        reinterpret_cast<uint32_t*>(grec)[i] = reinterpret_cast<const uint32_t*>(srec)[i];
+      if ((cnt & 1) && tid == 0) grec[cnt - 1] = srec[cnt - 1];
+      uint32_t* ghist = reinterpret_cast<uint32_t*>(a.hist_part + (sel * a.n_split + split) * kFastBins);
+      for (int i = tid; i < kFastBins / 2; i += kThreads)
+        ghist[i] = (shist[2 * i] & 0xFFFFu) | (shist[2 * i + 1] << 16);   // counts < 2^16
     }
   } else {
     // Sparse mode: index entries first (one batch per ring of kPrefetch steps), then
     // the gathered rows, so no row load waits behind an index load.
+    const int32_t* irow = a.idx + sel * a.S;
     for (int base = 0; base < nsteps; base += kPrefetch) {
       int32_t trow[kPrefetch];
       bool tval[kPrefetch];
@@ -337,10 +282,10 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
       o[i][e] = x;
     }
 
-  float (&lds_o)[4][8][kHeadDim] = lds_u.merge.o;
-  float (&lds_m)[4][8] = lds_u.merge.m;
-  float (&lds_z)[4][8] = lds_u.merge.z;
-  __syncthreads();   // every wave is done with its logit staging area
+  float(*lds_o)[8][kHeadDim] = reinterpret_cast<float(*)[8][kHeadDim]>(lds_raw);
+  float(*lds_m)[8] = reinterpret_cast<float(*)[8]>(lds_raw + 4 * 8 * kHeadDim * 4);
+  float(*lds_z)[8] = reinterpret_cast<float(*)[8]>(lds_raw + (4 * 8 * kHeadDim + 4 * 8) * 4);
+  __syncthreads();   // every wave is done with its staging area
   if (rg == 0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -388,12 +333,34 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
 // One workgroup per (selection row, head, 32-dim chunk): merges the split partials
 // into the normalised output and records the row's softmax statistics (M, 1/Z),
 // which the selection kernels need to turn logits into probabilities.
+//
+// Records mode adds workgroups (blockIdx.y >= 4) that merge the per-split record-key
+// histograms of a selection row: 16 bins per workgroup, 16 split groups per bin.
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int sh = blockIdx.x;
   const int sel = sh / a.G;
   const int h = sh - sel * a.G;
   const int chunk = blockIdx.y;
   const int tid = threadIdx.x;
+  if (chunk >= kHeadDim / 32) {
+    const int part = (chunk - kHeadDim / 32) * a.G + h;
+    if (a.hist_part == nullptr || part >= kFastBins / 16) return;
+    __shared__ uint32_t red16[16][16];
+    const int bin = part * 16 + (tid & 15);
+    const int grp = tid >> 4;
+    const uint16_t* hp = a.hist_part + (int64_t)sel * a.n_split * kFastBins + bin;
+    uint32_t acc = 0;
+    for (int s = grp; s < a.n_split; s += 16) acc += hp[(int64_t)s * kFastBins];
+    red16[grp][tid & 15] = acc;
+    __syncthreads();
+    if (tid < 16) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int g2 = 0; g2 < 16; ++g2) t += red16[g2][tid];
+      a.hist_out[(int64_t)sel * kSelWords + kSelHist1Off + part * 16 + tid] = t;
+    }
+    return;
+  }
   const int64_t split_stride = (int64_t)a.G * kPartStride;
   const float* base = a.part + ((int64_t)sel * a.n_split * a.G + h) * kPartStride;
 
@@ -455,26 +422,34 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 }  // namespace
 
-hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, int B, hipStream_t st) {
+hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st) {
   dim3 grid(a.n_split, a.Hkv, B * a.Lq);
-  if (fp8)
-    hipLaunchKernelGGL((scan_kernel<false, true>), grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((scan_kernel<false, false>), grid, dim3(kThreads), 0, st, a);
+  if (records) {
+    if (fp8)
+      hipLaunchKernelGGL((scan_kernel<kDenseRecords, true>), grid, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((scan_kernel<kDenseRecords, false>), grid, dim3(kThreads), 0, st, a);
+  } else {
+    if (fp8)
+      hipLaunchKernelGGL((scan_kernel<kDenseLogits, true>), grid, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((scan_kernel<kDenseLogits, false>), grid, dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_scan_sparse(const ScanArgs& a, bool fp8, int B, hipStream_t st) {
   dim3 grid(a.n_split, a.Hkv, B * a.Lq);
   if (fp8)
-    hipLaunchKernelGGL((scan_kernel<true, true>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((scan_kernel<kSparseGather, true>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((scan_kernel<true, false>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((scan_kernel<kSparseGather, false>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
-  dim3 grid(a.n_sel * a.G, kHeadDim / 32);
+  const int extra = a.hist_part != nullptr ? (kFastBins / 16 + a.G - 1) / a.G : 0;
+  dim3 grid(a.n_sel * a.G, kHeadDim / 32 + extra);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }

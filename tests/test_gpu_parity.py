@@ -28,9 +28,11 @@ def _announce(tag, w):
 
 
 def run_and_compare(w, tag, tokens=None, window=128, topk=1024, mode="token", block_size=64,
-                    n_blocks=18, with_probs=True, max_ctx_len=None, max_swaps=None):
+                    n_blocks=18, with_probs=False, max_ctx_len=None, max_swaps=None):
+    """with_probs=False runs the default record-based selection; with_probs=True makes the
+    library keep every logit and also returns all group-summed probabilities."""
     from long_context_decode_full_amd.runner import HybridBlockDevice
-    _announce(tag, w)
+    _announce(tag + (" [logits path]" if with_probs else " [record path]"), w)
     inp = wl.make_inputs(w)
     dev = HybridBlockDevice(inp, window=window, topk=topk, mode=mode, block_size=block_size,
                             n_blocks=n_blocks, with_probs=with_probs, max_ctx_len=max_ctx_len)
@@ -92,19 +94,22 @@ def run_and_compare(w, tag, tokens=None, window=128, topk=1024, mode="token", bl
 
 
 # ------------------------------------------------------------------ the five configurations
-def test_tiny_decode():
+@pytest.mark.parametrize("with_probs", [False, True])
+def test_tiny_decode(with_probs):
     w = wl.standard_workloads()["tiny"]
-    run_and_compare(w, "tiny")
+    run_and_compare(w, "tiny", with_probs=with_probs)
 
 
-def test_batched_decode():
+@pytest.mark.parametrize("with_probs", [False, True])
+def test_batched_decode(with_probs):
     w = wl.standard_workloads()["batched"]
-    run_and_compare(w, "batched")
+    run_and_compare(w, "batched", with_probs=with_probs)
 
 
-def test_fp8_256k_decode():
+@pytest.mark.parametrize("with_probs", [False, True])
+def test_fp8_256k_decode(with_probs):
     w = wl.standard_workloads()["fp8_256k"]
-    run_and_compare(w, "fp8_256k")
+    run_and_compare(w, "fp8_256k", with_probs=with_probs)
 
 
 def test_million_token_decode():
@@ -128,46 +133,53 @@ def test_short_and_boundary_contexts(ctx):
             assert got["idx"][0, 0, g, :ctx].tolist() == list(range(ctx))
 
 
-def test_ragged_batch_with_poisoned_tail():
+@pytest.mark.parametrize("with_probs", [False, True])
+def test_ragged_batch_with_poisoned_tail(with_probs):
     """Rows past ctx_len hold NaN; they must never be read.  Capacity > every length."""
     w = wl.Workload("ragged", 4, 1, 16, 2, ctx_lens=[3000, 1, 1300, 7777], n_needles=8,
                     capacity=8192, poison_tail=True, seed=3100)
-    run_and_compare(w, "ragged-poison")
+    run_and_compare(w, "ragged-poison", with_probs=with_probs)
 
 
-def test_ragged_fp8_with_poisoned_tail():
+@pytest.mark.parametrize("with_probs", [False, True])
+def test_ragged_fp8_with_poisoned_tail(with_probs):
     w = wl.Workload("ragged fp8", 3, 1, 32, 4, ctx_lens=[4100, 200, 9000], n_needles=8,
                     kv_dtype="fp8", capacity=9216, poison_tail=True, seed=3150)
-    run_and_compare(w, "ragged-fp8")
+    run_and_compare(w, "ragged-fp8", with_probs=with_probs)
 
 
-def test_identical_keys_ties_go_to_lower_positions():
+@pytest.mark.parametrize("with_probs", [False, True])
+def test_identical_keys_ties_go_to_lower_positions(with_probs):
     w = wl.Workload("identical keys", 1, 1, 16, 2, ctx_lens=[6000], identical_keys=True, seed=3200)
-    got, _ = run_and_compare(w, "identical-keys")
+    got, _ = run_and_compare(w, "identical-keys", with_probs=with_probs)
     for g in range(2):
         assert got["idx"][0, 0, g].tolist() == list(range(1024)) + list(range(6000 - 128, 6000))
 
 
-def test_identical_keys_large_tie_set():
-    """More equal scores than the boundary buffer holds: the ordered fallback path."""
+@pytest.mark.parametrize("with_probs", [False, True])
+def test_identical_keys_large_tie_set(with_probs):
+    """Every position ties: the record path re-scores every candidate, the logits path
+    takes its ordered fallback for tie sets larger than its boundary buffer."""
     w = wl.Workload("identical keys 20k", 1, 1, 16, 2, ctx_lens=[20000], identical_keys=True,
                     seed=3201)
-    got, _ = run_and_compare(w, "identical-keys-20k", with_probs=False)
+    got, _ = run_and_compare(w, "identical-keys-20k", with_probs=with_probs)
     for g in range(2):
         assert got["idx"][0, 0, g].tolist() == list(range(1024)) + list(range(20000 - 128, 20000))
 
 
-def test_zero_queries_uniform_attention():
+@pytest.mark.parametrize("with_probs", [False, True])
+def test_zero_queries_uniform_attention(with_probs):
     w = wl.Workload("zero q", 1, 1, 16, 2, ctx_lens=[3000], zero_q=True, seed=3300)
-    got, _ = run_and_compare(w, "zero-q")
+    got, _ = run_and_compare(w, "zero-q", with_probs=with_probs)
     for g in range(2):
         assert got["idx"][0, 0, g].tolist() == list(range(1024)) + list(range(3000 - 128, 3000))
 
 
-def test_dominant_needle():
+@pytest.mark.parametrize("with_probs", [False, True])
+def test_dominant_needle(with_probs):
     w = wl.Workload("needle x100", 1, 1, 16, 2, ctx_lens=[4096], n_needles=1, needle_scale=100.0,
                     seed=3400)
-    run_and_compare(w, "needle-x100")
+    run_and_compare(w, "needle-x100", with_probs=with_probs)
 
 
 @pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4), (12, 2)])
@@ -184,7 +196,7 @@ def test_other_window_and_topk(window, topk):
 
 def test_block_baseline_mode():
     w = wl.Workload("block baseline", 2, 1, 32, 4, ctx_lens=[20000, 3001], n_needles=16, seed=3700)
-    run_and_compare(w, "block", mode="block")
+    run_and_compare(w, "block", mode="block", with_probs=True)
 
 
 def test_block_baseline_chunk():
