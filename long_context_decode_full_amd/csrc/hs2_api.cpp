@@ -33,6 +33,7 @@ struct Layout {
   int32_t split_len_sp = 0, n_split_sp = 0;
   int32_t chunk_len = 0, n_chunks = 0;
   int32_t rec_split_len = 0, rec_n_split = 0;   // scan geometry of the record path
+  int32_t n_cchunks = 0;                        // record path: candidate chunks per row
   bool fast_ok = false;                         // record path usable for this descriptor
   size_t off_cand_pos = 0, off_cand_s = 0, off_cand_count = 0, off_hist_part = 0;
   size_t off_logits = 0, off_part = 0, off_mz = 0, off_s = 0, off_selblk = 0, off_hist2 = 0,
@@ -99,8 +100,8 @@ Layout make_layout(const hs2_attn_desc* d) {
   if (rsplit > kMaxRecordSplit) rsplit = kMaxRecordSplit;
   L.rec_split_len = (int32_t)rsplit;
   L.rec_n_split = (int32_t)ceil_div(d->max_ctx_len, rsplit);
-  L.fast_ok = d->select_mode == HS2_SELECT_TOKEN &&
-              ceil_div(d->max_ctx_len, kSelectChunk) <= kMaxFastChunks &&
+  L.n_cchunks = (int32_t)ceil_div(d->max_ctx_len, kCandChunkLen);
+  L.fast_ok = d->select_mode == HS2_SELECT_TOKEN && L.n_cchunks <= kMaxFastChunks &&
               L.rec_n_split <= kMaxSplits;
 
   int64_t sp = env_int("HS2_SPARSE_SPLIT_LEN", kSparseSplitLen);
@@ -125,10 +126,10 @@ Layout make_layout(const hs2_attn_desc* d) {
   L.off_winners = off; off = align_up(off + (size_t)n * std::max(d->topk, 1) * sizeof(int32_t));
   L.off_boundary = off; off = align_up(off + (size_t)n * kBoundaryCap * sizeof(uint2));
   if (L.fast_ok) {
-    const size_t slots = (size_t)n * L.n_chunks * kSelectChunk;
+    const size_t slots = (size_t)n * L.n_cchunks * kCandChunkLen;
     L.off_cand_pos = off; off = align_up(off + slots * sizeof(int32_t));
     L.off_cand_s = off;   off = align_up(off + slots * sizeof(float));
-    L.off_cand_count = off; off = align_up(off + (size_t)n * L.n_chunks * sizeof(int32_t));
+    L.off_cand_count = off; off = align_up(off + (size_t)n * L.n_cchunks * sizeof(int32_t));
     L.off_hist_part = off; off = align_up(off + (size_t)n * L.rec_n_split * kFastBins * sizeof(uint16_t));
   }
   L.total = off;
@@ -298,7 +299,7 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
     fa.k_scale = k_scale;
     fa.cap = desc->kv_capacity;
     fa.scale_log2 = sa.scale_log2;
-    fa.n_chunks = L.n_chunks;
+    fa.n_chunks = L.n_cchunks;
     fa.n_sel = (int32_t)L.n_sel;
     fa.Lq = desc->q_len;
     fa.Hq = desc->n_q_heads;

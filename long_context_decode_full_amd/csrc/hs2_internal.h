@@ -20,7 +20,8 @@ constexpr int kStateWords = 16;       // u32 per selection state
 constexpr int kSelectChunkLen = 4096; // positions per workgroup in the selection passes
 constexpr int kFastBins = 4096;       // histogram of the record keys (top 12 of 16 bits)
 constexpr int kFastShift = 4;
-constexpr int kMaxFastChunks = 8192;  // positions per row <= kMaxFastChunks * kSelectChunkLen
+constexpr int kCandChunkLen = 16384;  // record path: positions per candidate workgroup
+constexpr int kMaxFastChunks = 8192;  // positions per row <= kMaxFastChunks * kCandChunkLen
 // Per-selection control block (u32 words), cleared by the combine kernel of every
 // call: [0,16) state, [16,20) pass tickets, [32, 32+4096) first histogram.
 constexpr int kSelCounterOff = 16;
@@ -106,7 +107,7 @@ struct FastSelArgs {
   const int32_t* ctx_len;
   int64_t ctx_max;
   uint32_t* selblk;         // [n_sel, kSelWords]
-  int32_t* cand_pos;        // [n_sel, n_chunks, kSelectChunkLen]
+  int32_t* cand_pos;        // [n_sel, n_chunks, kCandChunkLen]
   float* cand_s;            // same shape: exact scores of the candidates
   int32_t* cand_count;      // [n_sel, n_chunks]
   int32_t* idx;             // [n_sel, S]

@@ -349,9 +349,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const int bin = part * 16 + (tid & 15);
     const int grp = tid >> 4;
     const uint16_t* hp = a.hist_part + (int64_t)sel * a.n_split * kFastBins + bin;
-    uint32_t acc = 0;
-    for (int s = grp; s < a.n_split; s += 16) acc += hp[(int64_t)s * kFastBins];
-    red16[grp][tid & 15] = acc;
+    uint32_t acc[4] = {0u, 0u, 0u, 0u};
+    int s = grp;
+    for (; s + 48 < a.n_split; s += 64) {   // four independent loads in flight
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] += hp[(int64_t)(s + 16 * u) * kFastBins];
+    }
+    for (; s < a.n_split; s += 16) acc[0] += hp[(int64_t)s * kFastBins];
+    red16[grp][tid & 15] = acc[0] + acc[1] + acc[2] + acc[3];
     __syncthreads();
     if (tid < 16) {
       uint32_t t = 0;

@@ -62,45 +62,48 @@ __device__ __forceinline__ void load_mz(const FastSelArgs& a, int64_t sel, float
 }
 
 // Largest bin B with (entries in bins >= B) >= need; also the count strictly above.
-// Block-wide over kThreads threads.  If fewer than `need` entries exist, B = 0 and
-// `above` is the total.
+// Block-wide over kThreads threads (wave suffix scans + one cross-wave step).  If
+// fewer than `need` entries exist, B = 0 and `above` is the total.
 template <int NB>
-__device__ void threshold_bin(const uint32_t* h, bool global, uint32_t need, uint32_t& bin,
-                              uint32_t& above, uint32_t& inbin) {
-  constexpr int PER = NB / kThreads > 0 ? NB / kThreads : 1;
-  __shared__ uint32_t tsum[kThreads];
-  __shared__ uint32_t res[3];
-  const int tid = threadIdx.x;
+__device__ void threshold_bin(const uint32_t* h, uint32_t need, uint32_t& bin, uint32_t& above) {
+  constexpr int PER = NB / kThreads;
+  __shared__ uint32_t wtot[kThreads / 64];
+  __shared__ uint32_t res[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t loc[PER];
-  uint32_t total = 0;
+  uint32_t tot = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int b = tid * PER + i;
-    loc[i] = b < NB ? (global ? atomic_load_relaxed(h + b) : h[b]) : 0u;
-    total += loc[i];
+  for (int i = 0; i < PER; i += 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(h + tid * PER + i);
+    loc[i] = v.x; loc[i + 1] = v.y; loc[i + 2] = v.z; loc[i + 3] = v.w;
   }
-  tsum[tid] = total;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) tot += loc[i];
+  uint32_t x = tot;   // inclusive suffix sum within the wave
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_down(x, off, 64);
+    if (lane + off < 64) x += y;
+  }
+  if (lane == 0) wtot[wave] = x;
   if (tid == 0) {
     res[0] = 0u;
     res[1] = 0u;
-    res[2] = 0u;
   }
   __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const uint32_t v = (tid + off < kThreads) ? tsum[tid + off] : 0u;
-    __syncthreads();
-    tsum[tid] += v;
-    __syncthreads();
+  uint32_t higher = x - tot;
+  for (int w = wave + 1; w < kThreads / 64; ++w) higher += wtot[w];
+  if (tid == 0) {
+    uint32_t all = 0;
+    for (int w = 0; w < kThreads / 64; ++w) all += wtot[w];
+    if (all < need) res[1] = all;
   }
-  if (tid == 0 && tsum[0] < need) res[1] = tsum[0];
-  uint32_t cum = (tid + 1 < kThreads) ? tsum[tid + 1] : 0u;
-  if (cum < need && cum + total >= need) {
+  if (higher < need && higher + tot >= need) {
+    uint32_t cum = higher;
 #pragma unroll
     for (int i = PER - 1; i >= 0; --i) {
       if (cum + loc[i] >= need) {
         res[0] = (uint32_t)(tid * PER + i);
         res[1] = cum;
-        res[2] = loc[i];
         break;
       }
       cum += loc[i];
@@ -109,11 +112,10 @@ __device__ void threshold_bin(const uint32_t* h, bool global, uint32_t need, uin
   __syncthreads();
   bin = res[0];
   above = res[1];
-  inbin = res[2];
   __syncthreads();
 }
 
-constexpr int kRecPerThread = kSelectChunkLen / kThreads;   // 16
+constexpr int kRecPerThread = kCandChunkLen / kThreads;   // 64
 
 // ------------------------------------------------------------------ candidates + exact re-score
 template <bool kFp8>
@@ -125,20 +127,49 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   const int wave = tid >> 6;
   const RowGeom rg = row_geom(a, sel);
   if (rg.w0 <= a.topk || a.topk == 0) return;
-  const int64_t c0 = (int64_t)chunk * kSelectChunkLen;
+  const int64_t c0 = (int64_t)chunk * kCandChunkLen;
   if (c0 >= rg.w0) {
     if (tid == 0) a.cand_count[sel * a.n_chunks + chunk] = 0;
     return;
   }
 
-  __shared__ int32_t cpos[kSelectChunkLen];
+  __shared__ int32_t cpos[kCandChunkLen];
   __shared__ int32_t total_s;
   float Mh[8], iz[8];
   load_mz(a, sel, Mh, iz);
+  const int64_t bj = sel / a.Hkv;
+  const int g = (int)(sel - bj * a.Hkv);
+  const int b = (int)(bj / a.Lq);
+  const int r = lane & 15;
+  const int rgrp = lane >> 4;
+  const int hown = head_of(r);
+  uint32_t qp[8][4];   // issued early: its latency overlaps the threshold and the filter
+  load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);
 
+  const uint16_t* rrow = a.records + sel * a.rec_stride;
+  // Each thread owns kRecPerThread consecutive positions (128 bytes of records, one
+  // batch of 16-byte loads); a block-wide exclusive scan of the per-thread hit counts
+  // places the candidates in LDS in position order.
+  const int64_t t0 = c0 + (int64_t)tid * kRecPerThread;
+  uint32_t words[kRecPerThread / 2];
+  if (t0 + kRecPerThread <= rg.w0) {
+#pragma unroll
+    for (int v = 0; v < kRecPerThread / 8; ++v) {
+      const uint4 x = *reinterpret_cast<const uint4*>(rrow + t0 + 8 * v);
+      words[4 * v + 0] = x.x; words[4 * v + 1] = x.y; words[4 * v + 2] = x.z; words[4 * v + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kRecPerThread / 2; ++i) {
+      const int64_t t = t0 + 2 * i;
+      const uint32_t lo = t < rg.w0 ? (uint32_t)rrow[t] : 0u;
+      const uint32_t hi = t + 1 < rg.w0 ? (uint32_t)rrow[t + 1] : 0u;
+      words[i] = lo | (hi << 16);
+    }
+  }
   // threshold: bin of the k-th largest record key in the merged histogram
-  uint32_t tb, above, inbin;
-  threshold_bin<kFastBins>(sel_block(a, sel) + kSelHist1Off, false, (uint32_t)a.topk, tb, above, inbin);
+  uint32_t tb, above;
+  threshold_bin<kFastBins>(sel_block(a, sel) + kSelHist1Off, (uint32_t)a.topk, tb, above);
   const uint32_t ebits = half_bits_of_key(tb << kFastShift);   // smallest record in the bin
   float lwmin = __builtin_huge_valf(), lwmax = -__builtin_huge_valf();
 #pragma unroll
@@ -152,63 +183,39 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   // candidate  <=>  e + u(e) + log2 max w  >=  e* - u(e*) + log2 min w  (with slack)
   const float thr = half_bits_to_float(ebits) - half_ulp(ebits) - (lwmax - lwmin) - 2.0f * kBoundSlack;
 
-  const uint16_t* rrow = a.records + sel * a.rec_stride;
-  // membership masks of the 16 rounds (256 consecutive positions each), then one
-  // prefix over (round, wave) counts: candidates land in LDS in position order
-  __shared__ int32_t rcnt[kRecPerThread][kThreads / 64];
-  uint64_t masks[kRecPerThread];
-#pragma unroll
-  for (int i0 = 0; i0 < kRecPerThread; i0 += 8) {
-    uint32_t rb[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t t = c0 + tid + (i0 + u) * kThreads;
-      rb[u] = t < rg.w0 ? (uint32_t)rrow[t] : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t t = c0 + tid + (i0 + u) * kThreads;
-      const bool hit = t < rg.w0 && half_bits_to_float(rb[u]) + half_ulp(rb[u]) >= thr;
-      masks[i0 + u] = __builtin_amdgcn_ballot_w64(hit);
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int i = 0; i < kRecPerThread; ++i) rcnt[i][wave] = __builtin_popcountll(masks[i]);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < kRecPerThread; ++i)
-      for (int w = 0; w < kThreads / 64; ++w) {
-        const int c = rcnt[i][w];
-        rcnt[i][w] = run;
-        run += c;
-      }
-    total_s = run;
-  }
-  __syncthreads();
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t hitmask = 0ull;
 #pragma unroll
   for (int i = 0; i < kRecPerThread; ++i) {
-    if ((masks[i] >> lane) & 1ull)
-      cpos[rcnt[i][wave] + __builtin_popcountll(masks[i] & below)] = (int32_t)(c0 + tid + i * kThreads);
+    const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    const bool hit = t0 + i < rg.w0 && half_bits_to_float(rb) + half_ulp(rb) >= thr;
+    hitmask |= (uint64_t)hit << i;
+  }
+  const uint32_t nhit = (uint32_t)__builtin_popcountll(hitmask);
+  // block exclusive scan of nhit
+  __shared__ uint32_t wscan[kThreads / 64];
+  uint32_t x = nhit;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wscan[wave] = x;
+  __syncthreads();
+  uint32_t before = x - nhit;
+  for (int w = 0; w < wave; ++w) before += wscan[w];
+  if (tid == kThreads - 1) total_s = (int)(before + nhit);
+  uint64_t hm = hitmask;
+  while (hm) {
+    const int i = __builtin_ctzll(hm);
+    hm &= hm - 1;
+    cpos[before++] = (int32_t)(t0 + i);
   }
   __syncthreads();
   const int cnt = total_s;
-  const int64_t slot0 = (sel * a.n_chunks + chunk) * (int64_t)kSelectChunkLen;
+  const int64_t slot0 = (sel * a.n_chunks + chunk) * (int64_t)kCandChunkLen;
   if (tid == 0) a.cand_count[sel * a.n_chunks + chunk] = cnt;
   if (cnt == 0) return;
 
   // exact re-score: 4 rows per wave step, the scan's lane layout and arithmetic
-  const int64_t bj = sel / a.Hkv;
-  const int g = (int)(sel - bj * a.Hkv);
-  const int b = (int)(bj / a.Lq);
-  const int r = lane & 15;
-  const int rgrp = lane >> 4;
-  const int hown = head_of(r);
-  uint32_t qp[8][4];
-  load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);
   const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
   const uint8_t* kb = a.k + head_row0 * (kFp8 ? 128 : 256);
   const float* ksb = kFp8 ? a.k_scale + head_row0 : nullptr;
@@ -233,6 +240,53 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
 // ------------------------------------------------------------------ exact top-k + output
 constexpr int kFinThreads = 1024;
 constexpr int kFinStage = 6144;   // candidates staged in LDS (larger sets read global memory)
+constexpr int kFinBnd = 1024;     // threshold-bin entries ranked by brute force
+
+// Largest bin B of an LDS histogram with (entries in bins >= B) >= need, and the
+// count strictly above B.  Block-wide over kFinThreads threads (nb <= 4 per thread).
+__device__ void block_threshold(const uint32_t* lh, uint32_t nb, uint32_t need, uint32_t& bin,
+                                uint32_t& above) {
+  __shared__ uint32_t wtot[kFinThreads / 64];
+  __shared__ uint32_t res[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t per = nb / kFinThreads > 0 ? nb / kFinThreads : 1;
+  uint32_t loc[4];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t bidx = tid * per + q;
+    loc[q] = (q < (int)per && bidx < nb) ? lh[bidx] : 0u;
+    tot += loc[q];
+  }
+  uint32_t x = tot;   // inclusive suffix sum within the wave
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_down(x, off, 64);
+    if (lane + off < 64) x += y;
+  }
+  if (lane == 0) wtot[wave] = x;
+  if (tid == 0) {
+    res[0] = 0u;
+    res[1] = 0u;
+  }
+  __syncthreads();
+  uint32_t higher = x - tot;
+  for (int w = wave + 1; w < kFinThreads / 64; ++w) higher += wtot[w];
+  if (higher < need && higher + tot >= need) {
+    uint32_t cum = higher;
+    for (int q = (int)per - 1; q >= 0; --q) {
+      if (cum + loc[q] >= need) {
+        res[0] = tid * per + q;
+        res[1] = cum;
+        break;
+      }
+      cum += loc[q];
+    }
+  }
+  __syncthreads();
+  bin = res[0];
+  above = res[1];
+  __syncthreads();
+}
 
 __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
   const int64_t sel = blockIdx.x;
@@ -248,6 +302,11 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
   __shared__ uint32_t lh[kFastBins];
   __shared__ int32_t st_pos[kFinStage];
   __shared__ uint32_t st_s[kFinStage];
+  __shared__ uint8_t flag[kFinStage];
+  __shared__ uint32_t blist[kFinBnd];
+  __shared__ uint32_t bnd_s[kFinBnd];
+  __shared__ int32_t bnd_p[kFinBnd];
+  __shared__ uint32_t nbnd;
   __shared__ uint32_t wsum[kFinThreads / 64][2];
   __shared__ uint32_t carry[2];
 
@@ -257,7 +316,7 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
     for (int i = tid; i < kk; i += kFinThreads) out[i] = i;
   } else {
     kk = a.topk;
-    const int nch = (w0 + kSelectChunkLen - 1) / kSelectChunkLen;
+    const int nch = (w0 + kCandChunkLen - 1) / kCandChunkLen;
     const int32_t* cc = a.cand_count + sel * a.n_chunks;
     // exclusive prefix of the per-chunk counts (serial per 1024 chunks, then fix-up)
     for (int base = 0; base < nch; base += kFinThreads) {
@@ -283,7 +342,7 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
       __syncthreads();
     }
     const uint32_t m = pref[nch];
-    const int64_t lbase = sel * a.n_chunks * (int64_t)kSelectChunkLen;
+    const int64_t lbase = sel * a.n_chunks * (int64_t)kCandChunkLen;
     // flat index -> candidate slot (binary search over the chunk prefix)
     auto slot_of = [&](uint32_t fi) -> int64_t {
       int lo = 0, hi = nch - 1;
@@ -291,7 +350,7 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
         const int mid = (lo + hi + 1) >> 1;
         if (pref[mid] <= fi) lo = mid; else hi = mid - 1;
       }
-      return lbase + (int64_t)lo * kSelectChunkLen + (fi - pref[lo]);
+      return lbase + (int64_t)lo * kCandChunkLen + (fi - pref[lo]);
     };
     const uint32_t need0 = (uint32_t)kk < m ? (uint32_t)kk : m;
     // stage the candidates in LDS (position order) when they fit; the passes below
@@ -312,79 +371,107 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
       return staged ? st_pos[fi] : a.cand_pos[slot_of(fi)];
     };
 
-    // three-digit radix select on the score bits: [30:19], [18:7], [6:0]
-    uint32_t prefix = 0, above = 0, need = need0;
-    const int shifts[3] = {19, 7, 0};
-    const int widths[3] = {12, 12, 7};
-    for (int d = 0; d < 3; ++d) {
-      const int sh = shifts[d];
-      const uint32_t nb = 1u << widths[d];
-      for (uint32_t i = tid; i < nb; i += kFinThreads) lh[i] = 0u;
-      __syncthreads();
-      const int shp = d == 0 ? 31 : shifts[d - 1];
-      for (uint32_t fi = tid; fi < m; fi += kFinThreads) {
-        const uint32_t u = score_bits(fi);
-        const bool match = d == 0 || (u >> shp) == prefix;
-        if (match) atomicAdd(&lh[(u >> sh) & (nb - 1)], 1u);
-      }
-      __syncthreads();
-      // threshold over nb bins, block-wide (1024 threads, <= 4 bins each)
-      uint32_t loc[4];
-      uint32_t tot = 0;
-      const uint32_t per = nb / kFinThreads > 0 ? nb / kFinThreads : 1;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t bidx = tid * per + q;
-        loc[q] = (q < (int)per && bidx < nb) ? lh[bidx] : 0u;
-        tot += loc[q];
-      }
-      // suffix sums over threads: wave scan (from the top) + cross-wave
-      uint32_t x = tot;
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_down(x, off, 64);
-        if (lane + off < 64) x += y;
-      }
-      if (lane == 0) wsum[wave][1] = x;
-      __syncthreads();
-      uint32_t higher = x - tot;
-      for (int w = wave + 1; w < kFinThreads / 64; ++w) higher += wsum[w][1];
-      if (higher < need && higher + tot >= need) {
-        uint32_t cum = higher;
-        for (int q = (int)per - 1; q >= 0; --q) {
-          if (cum + loc[q] >= need) {
-            carry[0] = tid * per + q;
-            carry[1] = cum;
-            break;
-          }
-          cum += loc[q];
-        }
-      }
-      __syncthreads();
-      const uint32_t bsel = carry[0];
-      above += carry[1];
-      need -= carry[1];
-      prefix = (prefix << widths[d]) | bsel;
-      __syncthreads();
+    // Radix digit 1 (score bits 30..19) finds the bin B holding the k-th largest
+    // score.  If that bin is small and the candidates are staged, its entries are
+    // ranked exactly by brute force (score desc, position asc); otherwise two more
+    // digits give the exact k-th value and ties are taken in position order.
+    for (uint32_t i = tid; i < (uint32_t)kFastBins; i += kFinThreads) lh[i] = 0u;
+    if (tid == 0) {
+      carry[0] = 0u;
+      carry[1] = 0u;
+      nbnd = 0u;
     }
-    const uint32_t vk = prefix;   // bits of the k-th largest score
-    // ordered output: chosen = (s > vk) or (s == vk and among the first `need` ties)
+    __syncthreads();
+    for (uint32_t fi = tid; fi < m; fi += kFinThreads) atomicAdd(&lh[score_bits(fi) >> 19], 1u);
+    __syncthreads();
+    uint32_t b1, above1;
+    block_threshold(lh, kFastBins, need0, b1, above1);
+    const uint32_t need1 = need0 - above1;
+    bool brute = false;
+    if (staged) {
+      // entries of bin b1, compacted in position order by ballot prefix sums
+      for (uint32_t base = 0; base < m; base += kFinThreads) {
+        const uint32_t fi = base + tid;
+        const bool in = fi < m;
+        if (in) flag[fi] = 0u;
+        const bool hit = in && (st_s[fi] >> 19) == b1;
+        const uint64_t hmask = __builtin_amdgcn_ballot_w64(hit);
+        if (lane == 0) wsum[wave][0] = __builtin_popcountll(hmask);
+        __syncthreads();
+        uint32_t slot = nbnd + __builtin_popcountll(hmask & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+        for (int w = 0; w < wave; ++w) slot += wsum[w][0];
+        if (hit && slot < (uint32_t)kFinBnd) blist[slot] = fi;
+        __syncthreads();
+        if (tid == 0) {
+          uint32_t t = nbnd;
+          for (int w = 0; w < kFinThreads / 64; ++w) t += wsum[w][0];
+          nbnd = t;
+        }
+        __syncthreads();
+      }
+      brute = nbnd <= (uint32_t)kFinBnd;
+    }
+    uint32_t vk = 0u, need = need1;
+    if (brute) {
+      const uint32_t nb = nbnd;
+      for (uint32_t e = tid; e < nb; e += kFinThreads) {
+        bnd_s[e] = st_s[blist[e]];
+        bnd_p[e] = st_pos[blist[e]];
+      }
+      __syncthreads();
+      for (uint32_t e = tid; e < nb; e += kFinThreads) {
+        const uint32_t se = bnd_s[e];
+        const int32_t pe = bnd_p[e];
+        uint32_t rank = 0;
+        for (uint32_t f = 0; f < nb; ++f) {   // broadcast LDS reads, independent iterations
+          const uint32_t sf = bnd_s[f];
+          const int32_t pf = bnd_p[f];
+          rank += (sf > se || (sf == se && pf < pe)) ? 1u : 0u;
+        }
+        flag[blist[e]] = rank < need1 ? 1u : 0u;
+      }
+      __syncthreads();
+    } else {
+      uint32_t prefix = b1;
+      const int shifts[2] = {7, 0};
+      const int widths[2] = {12, 7};
+      for (int d = 0; d < 2; ++d) {
+        const int sh = shifts[d];
+        const uint32_t nb = 1u << widths[d];
+        const int shp = d == 0 ? 19 : 7;
+        for (uint32_t i = tid; i < nb; i += kFinThreads) lh[i] = 0u;
+        __syncthreads();
+        for (uint32_t fi = tid; fi < m; fi += kFinThreads) {
+          const uint32_t u = score_bits(fi);
+          if ((u >> shp) == prefix) atomicAdd(&lh[(u >> sh) & (nb - 1)], 1u);
+        }
+        __syncthreads();
+        uint32_t bd, ab;
+        block_threshold(lh, nb, need, bd, ab);
+        need -= ab;
+        prefix = (prefix << widths[d]) | bd;
+      }
+      vk = prefix;   // bits of the k-th largest score
+    }
+    // ordered output of the chosen candidates
     if (tid == 0) {
       carry[0] = 0u;   // chosen so far
-      carry[1] = 0u;   // ties so far
+      carry[1] = 0u;   // ties so far (general path)
     }
     __syncthreads();
     for (uint32_t base = 0; base < m; base += kFinThreads) {
       const uint32_t fi = base + tid;
       const bool in = fi < m;
       const uint32_t u = in ? score_bits(fi) : 0u;
-      const bool tie = in && u == vk;
+      const bool tie = !brute && in && u == vk;
       const uint64_t tmask = __builtin_amdgcn_ballot_w64(tie);
       const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
       if (lane == 0) wsum[wave][0] = __builtin_popcountll(tmask);
       __syncthreads();
       uint32_t tie_rank = carry[1] + __builtin_popcountll(tmask & below);
       for (int w = 0; w < wave; ++w) tie_rank += wsum[w][0];
-      const bool chosen = in && (u > vk || (tie && tie_rank < need));
+      const bool chosen = in && (brute ? ((u >> 19) > b1 || flag[fi] != 0u)
+                                       : (u > vk || (tie && tie_rank < need)));
       const uint64_t cmask = __builtin_amdgcn_ballot_w64(chosen);
       __syncthreads();
       if (lane == 0) wsum[wave][1] = __builtin_popcountll(cmask);
