@@ -35,7 +35,7 @@ struct Layout {
   int32_t rec_split_len = 0, rec_n_split = 0;   // scan geometry of the record path
   int32_t n_cchunks = 0;                        // record path: candidate chunks per row
   bool fast_ok = false;                         // record path usable for this descriptor
-  size_t off_cand_pos = 0, off_cand_s = 0, off_cand_count = 0, off_hist_part = 0;
+  size_t off_cand_keys = 0, off_cand_count = 0, off_hist_part = 0;
   size_t off_logits = 0, off_part = 0, off_mz = 0, off_s = 0, off_selblk = 0, off_hist2 = 0,
          off_hist3 = 0, off_winners = 0, off_boundary = 0, total = 0;
 };
@@ -127,8 +127,7 @@ Layout make_layout(const hs2_attn_desc* d) {
   L.off_boundary = off; off = align_up(off + (size_t)n * kBoundaryCap * sizeof(uint2));
   if (L.fast_ok) {
     const size_t slots = (size_t)n * L.n_cchunks * kCandChunkLen;
-    L.off_cand_pos = off; off = align_up(off + slots * sizeof(int32_t));
-    L.off_cand_s = off;   off = align_up(off + slots * sizeof(float));
+    L.off_cand_keys = off; off = align_up(off + slots * sizeof(uint64_t));
     L.off_cand_count = off; off = align_up(off + (size_t)n * L.n_cchunks * sizeof(int32_t));
     L.off_hist_part = off; off = align_up(off + (size_t)n * L.rec_n_split * kFastBins * sizeof(uint16_t));
   }
@@ -255,6 +254,7 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   sa.logits = reinterpret_cast<float*>(ws + L.off_logits);
   sa.records = reinterpret_cast<uint16_t*>(ws + L.off_logits);
   sa.hist_part = reinterpret_cast<uint16_t*>(ws + L.off_hist_part);
+  sa.hist_merged = reinterpret_cast<uint32_t*>(ws + L.off_selblk);
   sa.window = desc->window;
   sa.n_split = fast ? L.rec_n_split : L.n_split;
   sa.split_len = fast ? L.rec_split_len : L.split_len;
@@ -269,8 +269,8 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   ca.part = sa.part;
   ca.out = out;
   ca.mz = reinterpret_cast<float*>(ws + L.off_mz);
-  // the logits path clears the selection control blocks here; the record path
-  // overwrites every histogram bin it reads, so it needs no clearing
+  // the logits path clears the selection control blocks here; on the record path
+  // the scan has cleared the merged key histograms that the combine sums into
   ca.sel_zero = fast ? nullptr : reinterpret_cast<uint32_t*>(ws + L.off_selblk);
   ca.sel_zero_words = kSelWords;
   ca.hist_part = fast ? sa.hist_part : nullptr;
@@ -290,8 +290,7 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
     fa.ctx_len = ctx_len;
     fa.ctx_max = desc->max_ctx_len;
     fa.selblk = ca.hist_out;
-    fa.cand_pos = reinterpret_cast<int32_t*>(ws + L.off_cand_pos);
-    fa.cand_s = reinterpret_cast<float*>(ws + L.off_cand_s);
+    fa.cand_keys = reinterpret_cast<uint64_t*>(ws + L.off_cand_keys);
     fa.cand_count = reinterpret_cast<int32_t*>(ws + L.off_cand_count);
     fa.idx = idx;
     fa.q = static_cast<const uint16_t*>(q);

@@ -18,12 +18,14 @@ constexpr int kBoundaryCap = 4096;    // boundary-bin entries resolved by one so
 constexpr int kStateWords = 16;       // u32 per selection state
 // Record-based selection (default token-mode path).
 constexpr int kSelectChunkLen = 4096; // positions per workgroup in the selection passes
-constexpr int kFastBins = 4096;       // histogram of the record keys (top 12 of 16 bits)
-constexpr int kFastShift = 4;
+constexpr int kFastBins = 1024;       // histogram of the record keys (top 10 of 16 bits)
+constexpr int kFastShift = 6;
+constexpr int kHistMergeSplits = 16;  // per-split histograms summed by one combine workgroup
 constexpr int kCandChunkLen = 16384;  // record path: positions per candidate workgroup
 constexpr int kMaxFastChunks = 8192;  // positions per row <= kMaxFastChunks * kCandChunkLen
-// Per-selection control block (u32 words), cleared by the combine kernel of every
-// call: [0,16) state, [16,20) pass tickets, [32, 32+4096) first histogram.
+// Per-selection control block (u32 words): [0,16) state, [16,20) pass tickets,
+// [32, 32+2048) first histogram.  The logits path clears it in the combine kernel;
+// the record path's scan clears the kFastBins words of the merged key histogram.
 constexpr int kSelCounterOff = 16;
 constexpr int kSelHist1Off = 32;
 constexpr int kSelWords = kSelHist1Off + (kFastBins > kHist1Bins ? kFastBins : kHist1Bins);
@@ -55,6 +57,8 @@ struct ScanArgs {
   float* logits;            // logits mode: [n_sel, logit_stride, 8] log2-domain logits
   uint16_t* records;        // records mode: [n_sel, logit_stride] binary16 bound records
   uint16_t* hist_part;      // records mode: [n_sel, n_split, kFastBins] key histograms
+  uint32_t* hist_merged;    // records mode: merged histograms at + sel*kSelWords + kSelHist1Off,
+                            // cleared by split 0 of each selection
   int32_t window;           // records mode: positions >= ctx - window are not candidates
   float* part;              // [n_sel, n_split, G, kPartStride]
   int64_t cap;              // rows per (sequence, KV head)
@@ -75,6 +79,7 @@ struct CombineArgs {
   int32_t sel_zero_words;   // words per selection in sel_zero
   const uint16_t* hist_part;  // records mode: per-split key histograms to merge, or nullptr
   uint32_t* hist_out;       // merged histogram of selection `sel` at hist_out + sel*kSelWords
+                            // + kSelHist1Off (atomic sums into words the scan cleared)
   int32_t n_sel, Hkv, G, Hq, n_split;
 };
 
@@ -107,8 +112,8 @@ struct FastSelArgs {
   const int32_t* ctx_len;
   int64_t ctx_max;
   uint32_t* selblk;         // [n_sel, kSelWords]
-  int32_t* cand_pos;        // [n_sel, n_chunks, kCandChunkLen]
-  float* cand_s;            // same shape: exact scores of the candidates
+  uint64_t* cand_keys;      // [n_sel, n_chunks, kCandChunkLen] candidate keys: fp32 bits of
+                            // the exact score << 32 | (2^31 - 1 - position)
   int32_t* cand_count;      // [n_sel, n_chunks]
   int32_t* idx;             // [n_sel, S]
   const uint16_t* q;        // full-layer queries (exact re-score)

@@ -188,6 +188,10 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
     cand_span = cand_span < span ? cand_span : span;
     if (kMode == kDenseRecords) {
       for (int i = tid; i < kFastBins; i += kThreads) shist[i] = 0u;
+      if (split == 0) {   // the combine kernel sums every split's histogram into these words
+        uint32_t* hm = a.hist_merged + sel * kSelWords + kSelHist1Off;
+        for (int i = tid; i < kFastBins; i += kThreads) hm[i] = 0u;
+      }
       __syncthreads();
     }
     RowData buf[kPrefetch];
@@ -336,88 +340,128 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
 //
 // Records mode adds workgroups (blockIdx.y >= 4) that merge the per-split record-key
 // histograms of a selection row: 16 bins per workgroup, 16 split groups per bin.
+// Merges the split partials of one (selection, head) for 32 output dims: every
+// thread takes whole splits (one pass of loads), folds them with the online-softmax
+// rule, and the block merges the 256 states (wave DPP reductions + LDS).  Workgroups
+// with blockIdx.y >= 4 instead sum kHistMergeSplits per-split key histograms
+// (records mode) into the selection's merged histogram.
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int sh = blockIdx.x;
   const int sel = sh / a.G;
   const int h = sh - sel * a.G;
   const int chunk = blockIdx.y;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   if (chunk >= kHeadDim / 32) {
-    const int part = (chunk - kHeadDim / 32) * a.G + h;
-    if (a.hist_part == nullptr || part >= kFastBins / 16) return;
-    __shared__ uint32_t red16[16][16];
-    const int bin = part * 16 + (tid & 15);
-    const int grp = tid >> 4;
-    const uint16_t* hp = a.hist_part + (int64_t)sel * a.n_split * kFastBins + bin;
-    uint32_t acc[4] = {0u, 0u, 0u, 0u};
-    int s = grp;
-    for (; s + 48 < a.n_split; s += 64) {   // four independent loads in flight
+    if (a.hist_part == nullptr) return;
+    const int mg = (chunk - kHeadDim / 32) * a.G + h;
+    const int s0 = mg * kHistMergeSplits;
+    if (s0 >= a.n_split) return;
+    __shared__ __attribute__((aligned(16))) uint32_t hred[4][kFastBins];
+    // wave w: splits s0 + 4w .. s0 + 4w + 3; lane l: bins [16 l, 16 l + 16)
+    const uint16_t* hp = a.hist_part + (int64_t)sel * a.n_split * kFastBins + lane * 16;
+    uint4 wv[4][2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] += hp[(int64_t)(s + 16 * u) * kFastBins];
+    for (int u = 0; u < 4; ++u) {
+      const int s = s0 + wave * 4 + u;
+      if (s < a.n_split) {
+        wv[u][0] = *reinterpret_cast<const uint4*>(hp + (int64_t)s * kFastBins);
+        wv[u][1] = *reinterpret_cast<const uint4*>(hp + (int64_t)s * kFastBins + 8);
+      } else {
+        wv[u][0] = make_uint4(0u, 0u, 0u, 0u);
+        wv[u][1] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
-    for (; s < a.n_split; s += 16) acc[0] += hp[(int64_t)s * kFastBins];
-    red16[grp][tid & 15] = acc[0] + acc[1] + acc[2] + acc[3];
-    __syncthreads();
-    if (tid < 16) {
-      uint32_t t = 0;
+    uint32_t acc[16];
 #pragma unroll
-      for (int g2 = 0; g2 < 16; ++g2) t += red16[g2][tid];
-      a.hist_out[(int64_t)sel * kSelWords + kSelHist1Off + part * 16 + tid] = t;
+    for (int i = 0; i < 16; ++i) acc[i] = 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t w4[4] = {wv[u][q].x, wv[u][q].y, wv[u][q].z, wv[u][q].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[q * 8 + 2 * c] += w4[c] & 0xFFFFu;
+          acc[q * 8 + 2 * c + 1] += w4[c] >> 16;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; i += 4)
+      *reinterpret_cast<uint4*>(&hred[wave][lane * 16 + i]) = make_uint4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+    __syncthreads();
+    uint32_t* ho = a.hist_out + (int64_t)sel * kSelWords + kSelHist1Off;
+    for (int bin = tid; bin < kFastBins; bin += 256) {
+      const uint32_t t = hred[0][bin] + hred[1][bin] + hred[2][bin] + hred[3][bin];
+      if (t != 0u) atomicAdd(ho + bin, t);
     }
     return;
   }
   const int64_t split_stride = (int64_t)a.G * kPartStride;
   const float* base = a.part + ((int64_t)sel * a.n_split * a.G + h) * kPartStride;
 
-  __shared__ float w_lds[2048];
-  __shared__ float red[256];
-  __shared__ float acc_lds[8][32];
-
-  float mx = kNegInf;
-  for (int s = tid; s < a.n_split; s += 256) mx = fmaxf(mx, base[s * split_stride]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-
-  float zs = 0.0f;
+  // per-thread online merge of its splits
+  float m_loc = kNegInf, z_loc = 0.0f;
+  float o[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) o[i] = 0.0f;
   for (int s = tid; s < a.n_split; s += 256) {
-    const float ms = base[s * split_stride];
-    const float w = (ms == kNegInf) ? 0.0f : fast_exp2(ms - M);
-    w_lds[s] = w;
-    zs += w * base[s * split_stride + 1];
+    const float* ps = base + (int64_t)s * split_stride;
+    const float ms = ps[0];
+    const float zs = ps[1];
+    float4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const float4*>(ps + 4 + chunk * 32 + 4 * i);
+    if (ms == kNegInf) continue;   // split without visible rows: z = 0, o = 0
+    const float mn = fmaxf(m_loc, ms);
+    const float fo = fast_exp2(m_loc - mn);   // 0 while m_loc = -inf
+    const float fn = fast_exp2(ms - mn);
+    z_loc = z_loc * fo + zs * fn;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o[4 * i + 0] = o[4 * i + 0] * fo + v[i].x * fn;
+      o[4 * i + 1] = o[4 * i + 1] * fo + v[i].y * fn;
+      o[4 * i + 2] = o[4 * i + 2] * fo + v[i].z * fn;
+      o[4 * i + 3] = o[4 * i + 3] * fo + v[i].w * fn;
+    }
+    m_loc = mn;
   }
-  red[tid] = zs;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  const float Z = red[0];
 
-  const int dl = tid & 31;
-  const int sg = tid >> 5;
-  const int d = chunk * 32 + dl;
-  float acc = 0.0f;
-  for (int s = sg; s < a.n_split; s += 8) acc += w_lds[s] * base[s * split_stride + 4 + d];
-  acc_lds[sg][dl] = acc;
+  __shared__ float wmax[4];
+  __shared__ float red[16][33];
+  const float wm = wave_max(m_loc);
+  if (lane == 0) wmax[wave] = wm;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float f = m_loc == kNegInf ? 0.0f : fast_exp2(m_loc - M);
+  // sums over each row of 16 lanes, then over the 16 rows of the block
+  const float zr = rowgroup_sum16(z_loc * f);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) o[i] = rowgroup_sum16(o[i] * f);
+  if ((lane & 15) == 0) {
+    const int row = wave * 4 + (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) red[row][i] = o[i];
+    red[row][32] = zr;
+  }
   __syncthreads();
   if (tid < 32) {
-    float t = 0.0f;
+    float t = 0.0f, Z = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) t += acc_lds[i][tid];
+    for (int r = 0; r < 16; ++r) {
+      t += red[r][tid];
+      Z += red[r][32];
+    }
     const int bj = sel / a.Hkv;
     const int g = sel - bj * a.Hkv;
     a.out[((int64_t)bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim + chunk * 32 + tid] =
         Z > 0.0f ? t / Z : 0.0f;
-  }
-  if (a.mz != nullptr && chunk == 0 && tid == 0) {
-    a.mz[((int64_t)sel * 8 + h) * 2 + 0] = M;
-    a.mz[((int64_t)sel * 8 + h) * 2 + 1] = Z > 0.0f ? 1.0f / Z : 0.0f;
+    if (a.mz != nullptr && chunk == 0 && tid == 0) {
+      a.mz[((int64_t)sel * 8 + h) * 2 + 0] = M;
+      a.mz[((int64_t)sel * 8 + h) * 2 + 1] = Z > 0.0f ? 1.0f / Z : 0.0f;
+    }
   }
   if (a.sel_zero != nullptr && h == 0 && chunk == 0) {
     uint32_t* zp = a.sel_zero + (int64_t)sel * a.sel_zero_words;
@@ -453,7 +497,8 @@ hipError_t launch_scan_sparse(const ScanArgs& a, bool fp8, int B, hipStream_t st
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
-  const int extra = a.hist_part != nullptr ? (kFastBins / 16 + a.G - 1) / a.G : 0;
+  const int n_groups = (a.n_split + kHistMergeSplits - 1) / kHistMergeSplits;
+  const int extra = a.hist_part != nullptr ? (n_groups + a.G - 1) / a.G : 0;
   dim3 grid(a.n_sel * a.G, kHeadDim / 32 + extra);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, a);
   return hipGetLastError();

@@ -19,10 +19,12 @@
 //                     with the scan's own arithmetic (row_logit), so s is
 //                     bit-identical to the value the scan's logits would give.
 //   final_kernel:     exact top-k of the candidates by (s desc, position asc): a
-//                     three-digit radix select on the fp32 bit pattern of s (s >= 0
-//                     orders like its bits), then an ordered pass that emits the
-//                     chosen positions ascending (ties taken in position order),
-//                     followed by the window.
+//                     radix digit on the fp32 bit pattern of s (s >= 0 orders like
+//                     its bits) finds the bin of the k-th score, the entries of that
+//                     bin are ranked pairwise by a unique (s, position) key, and one
+//                     block-wide scan emits the chosen positions ascending, followed
+//                     by the window.  Oversized candidate sets or bins fall back to
+//                     two more digits with ties taken in position order.
 #include "hs2_rowops.h"
 
 namespace hs2 {
@@ -61,42 +63,41 @@ __device__ __forceinline__ void load_mz(const FastSelArgs& a, int64_t sel, float
   }
 }
 
-// Largest bin B with (entries in bins >= B) >= need; also the count strictly above.
-// Block-wide over kThreads threads (wave suffix scans + one cross-wave step).  If
-// fewer than `need` entries exist, B = 0 and `above` is the total.
-template <int NB>
-__device__ void threshold_bin(const uint32_t* h, uint32_t need, uint32_t& bin, uint32_t& above) {
-  constexpr int PER = NB / kThreads;
-  __shared__ uint32_t wtot[kThreads / 64];
+// Largest bin B of the histogram h[0, nb) with (entries in bins >= B) >= need, and
+// the count strictly above B; if fewer than `need` entries exist, B = 0 and `above`
+// is the total.  Block-wide over NT threads, thread t holding bins [t*PER, t*PER+PER):
+// a DPP prefix sum per wave plus one cross-wave step through LDS.
+template <int NT, int PER>
+__device__ void block_threshold(const uint32_t* h, int nb, uint32_t need, uint32_t& bin,
+                                uint32_t& above) {
+  __shared__ uint32_t wtot[NT / 64];
   __shared__ uint32_t res[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t loc[PER];
   uint32_t tot = 0;
 #pragma unroll
-  for (int i = 0; i < PER; i += 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(h + tid * PER + i);
-    loc[i] = v.x; loc[i + 1] = v.y; loc[i + 2] = v.z; loc[i + 3] = v.w;
+  for (int i = 0; i < PER; ++i) {
+    const int bi = tid * PER + i;
+    loc[i] = bi < nb ? h[bi] : 0u;
+    tot += loc[i];
   }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) tot += loc[i];
-  uint32_t x = tot;   // inclusive suffix sum within the wave
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_down(x, off, 64);
-    if (lane + off < 64) x += y;
-  }
-  if (lane == 0) wtot[wave] = x;
+  const uint32_t p = wave_prefix_incl(tot);
+  const uint32_t wt = (uint32_t)__builtin_amdgcn_readlane((int)p, 63);
+  if (lane == 0) wtot[wave] = wt;
   if (tid == 0) {
     res[0] = 0u;
     res[1] = 0u;
   }
   __syncthreads();
-  uint32_t higher = x - tot;
-  for (int w = wave + 1; w < kThreads / 64; ++w) higher += wtot[w];
-  if (tid == 0) {
-    uint32_t all = 0;
-    for (int w = 0; w < kThreads / 64; ++w) all += wtot[w];
-    if (all < need) res[1] = all;
+  uint32_t higher = wt - p;   // bins held by the later lanes of this wave
+  uint32_t all = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const uint32_t v = wtot[w];
+    all += v;
+    higher += w > wave ? v : 0u;
   }
+  if (tid == 0 && all < need) res[1] = all;
   if (higher < need && higher + tot >= need) {
     uint32_t cum = higher;
 #pragma unroll
@@ -112,7 +113,15 @@ __device__ void threshold_bin(const uint32_t* h, uint32_t need, uint32_t& bin, u
   __syncthreads();
   bin = res[0];
   above = res[1];
-  __syncthreads();
+  __syncthreads();   // res and wtot are reused by the next call
+}
+
+// Unique 64-bit order key of a candidate: larger score first, then lower position.
+__device__ __forceinline__ uint64_t cand_key(uint32_t sbits, int32_t pos) {
+  return ((uint64_t)sbits << 32) | (uint32_t)(0x7FFFFFFF - pos);
+}
+__device__ __forceinline__ int32_t key_pos(uint64_t key) {
+  return 0x7FFFFFFF - (int32_t)(uint32_t)key;
 }
 
 constexpr int kRecPerThread = kCandChunkLen / kThreads;   // 64
@@ -169,7 +178,8 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   }
   // threshold: bin of the k-th largest record key in the merged histogram
   uint32_t tb, above;
-  threshold_bin<kFastBins>(sel_block(a, sel) + kSelHist1Off, (uint32_t)a.topk, tb, above);
+  block_threshold<kThreads, kFastBins / kThreads>(sel_block(a, sel) + kSelHist1Off, kFastBins,
+                                                  (uint32_t)a.topk, tb, above);
   const uint32_t ebits = half_bits_of_key(tb << kFastShift);   // smallest record in the bin
   float lwmin = __builtin_huge_valf(), lwmax = -__builtin_huge_valf();
 #pragma unroll
@@ -193,11 +203,7 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   const uint32_t nhit = (uint32_t)__builtin_popcountll(hitmask);
   // block exclusive scan of nhit
   __shared__ uint32_t wscan[kThreads / 64];
-  uint32_t x = nhit;
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  const uint32_t x = wave_prefix_incl(nhit);
   if (lane == 63) wscan[wave] = x;
   __syncthreads();
   uint32_t before = x - nhit;
@@ -231,119 +237,113 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
     float part = ((r & 1) == 0 && hown < a.G) ? fast_exp2(l - Mown) * izown : 0.0f;
     const float s = rowgroup_sum16(part);
     if (valid && r == 0) {
-      a.cand_pos[slot0 + i] = t;
-      a.cand_s[slot0 + i] = s;
+      a.cand_keys[slot0 + i] = cand_key(__float_as_uint(s), t);
     }
   }
 }
 
 // ------------------------------------------------------------------ exact top-k + output
 constexpr int kFinThreads = 1024;
+constexpr int kFinWaves = kFinThreads / 64;
 constexpr int kFinStage = 6144;   // candidates staged in LDS (larger sets read global memory)
-constexpr int kFinBnd = 1024;     // threshold-bin entries ranked by brute force
+constexpr int kFinRun = kFinStage / kFinThreads;   // consecutive candidates per thread
+constexpr int kFinBnd = 1024;     // threshold-bin entries ranked pairwise
+constexpr int kDigitBins = 4096;  // first radix digit: score bits 30..19
 
-// Largest bin B of an LDS histogram with (entries in bins >= B) >= need, and the
-// count strictly above B.  Block-wide over kFinThreads threads (nb <= 4 per thread).
-__device__ void block_threshold(const uint32_t* lh, uint32_t nb, uint32_t need, uint32_t& bin,
-                                uint32_t& above) {
-  __shared__ uint32_t wtot[kFinThreads / 64];
-  __shared__ uint32_t res[2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint32_t per = nb / kFinThreads > 0 ? nb / kFinThreads : 1;
-  uint32_t loc[4];
-  uint32_t tot = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t bidx = tid * per + q;
-    loc[q] = (q < (int)per && bidx < nb) ? lh[bidx] : 0u;
-    tot += loc[q];
-  }
-  uint32_t x = tot;   // inclusive suffix sum within the wave
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_down(x, off, 64);
-    if (lane + off < 64) x += y;
-  }
-  if (lane == 0) wtot[wave] = x;
-  if (tid == 0) {
-    res[0] = 0u;
-    res[1] = 0u;
-  }
-  __syncthreads();
-  uint32_t higher = x - tot;
-  for (int w = wave + 1; w < kFinThreads / 64; ++w) higher += wtot[w];
-  if (higher < need && higher + tot >= need) {
-    uint32_t cum = higher;
-    for (int q = (int)per - 1; q >= 0; --q) {
-      if (cum + loc[q] >= need) {
-        res[0] = tid * per + q;
-        res[1] = cum;
-        break;
-      }
-      cum += loc[q];
-    }
-  }
-  __syncthreads();
-  bin = res[0];
-  above = res[1];
-  __syncthreads();
-}
 
+// One workgroup per selection.  Stages the candidates (position order) in LDS,
+// finds the bin of the k-th largest score with one 4096-bin digit, ranks the
+// entries of that bin pairwise by their unique keys to get the k-th key exactly,
+// and writes the chosen positions ascending with one block-wide scan, then the
+// window.  Candidate sets beyond the LDS stage or threshold bins beyond kFinBnd
+// entries take two more radix digits and resolve equal scores in position order.
 __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
   const int64_t sel = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const RowGeom rg = row_geom(a, sel);
   const int n = (int)rg.n;
   const int w0 = (int)rg.w0;
   int32_t* out = a.idx + sel * a.S;
 
   __shared__ uint32_t pref[kMaxFastChunks + 1];
-  __shared__ uint32_t lh[kFastBins];
-  __shared__ int32_t st_pos[kFinStage];
-  __shared__ uint32_t st_s[kFinStage];
-  __shared__ uint8_t flag[kFinStage];
-  __shared__ uint32_t blist[kFinBnd];
-  __shared__ uint32_t bnd_s[kFinBnd];
-  __shared__ int32_t bnd_p[kFinBnd];
-  __shared__ uint32_t nbnd;
-  __shared__ uint32_t wsum[kFinThreads / 64][2];
+  __shared__ uint32_t lh[kDigitBins];
+  __shared__ uint64_t st_key[kFinStage];
+  __shared__ uint64_t bkey[kFinBnd];
+  __shared__ uint32_t wsum[kFinWaves][2];
   __shared__ uint32_t carry[2];
+  __shared__ uint32_t nbnd;
+  __shared__ uint64_t kth;
 
   int kk;
   if (w0 <= a.topk || a.topk == 0) {
     kk = a.topk == 0 ? 0 : w0;
     for (int i = tid; i < kk; i += kFinThreads) out[i] = i;
   } else {
-    kk = a.topk;
+    for (int i = tid; i < kDigitBins; i += kFinThreads) lh[i] = 0u;
+    if (tid == 0) {
+      nbnd = 0u;
+      kth = ~0ull;
+    }
     const int nch = (w0 + kCandChunkLen - 1) / kCandChunkLen;
     const int32_t* cc = a.cand_count + sel * a.n_chunks;
-    // exclusive prefix of the per-chunk counts (serial per 1024 chunks, then fix-up)
-    for (int base = 0; base < nch; base += kFinThreads) {
-      const int c = base + tid;
-      const uint32_t v = c < nch ? (uint32_t)cc[c] : 0u;
-      // wave-level inclusive scan
-      uint32_t x = v;
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-      }
-      if (lane == 63) wsum[wave][0] = x;
-      __syncthreads();
-      uint32_t wpre = base == 0 ? 0u : pref[base];
-      for (int w = 0; w < wave; ++w) wpre += wsum[w][0];
-      if (c < nch) pref[c] = wpre + x - v;
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t t = base == 0 ? 0u : pref[base];
-        for (int w = 0; w < kFinThreads / 64; ++w) t += wsum[w][0];
-        pref[min(base + kFinThreads, nch)] = t;
-      }
-      __syncthreads();
-    }
-    const uint32_t m = pref[nch];
     const int64_t lbase = sel * a.n_chunks * (int64_t)kCandChunkLen;
-    // flat index -> candidate slot (binary search over the chunk prefix)
+    constexpr int kU = 4;   // chunks per wave in the single-round copy (64 = 16 waves x 4)
+    uint32_t m = 0;
+    bool staged;
+    if (nch <= kFinWaves * kU) {
+      // one round of loads: every wave reads the 64 counts and, speculatively, the
+      // first 64 keys of its chunks wave, wave + 16, ... (slots exist whether or
+      // not they hold candidates)
+      const uint32_t cnt = lane < nch ? (uint32_t)cc[lane] : 0u;
+      uint64_t kv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int c = wave + u * kFinWaves;
+        kv[u] = c < nch ? a.cand_keys[lbase + (int64_t)c * kCandChunkLen + lane] : 0ull;
+      }
+      const uint32_t incl = wave_prefix_incl(cnt);
+      m = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      if (wave == 0) {
+        if (lane < nch) pref[lane] = incl - cnt;
+        if (lane == 0) pref[nch] = m;
+      }
+      staged = m <= (uint32_t)kFinStage;
+      if (staged) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int c = wave + u * kFinWaves;   // wave-uniform
+          const uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)(incl - cnt), c & 63);
+          const uint32_t cn = c < nch ? (uint32_t)__builtin_amdgcn_readlane((int)cnt, c & 63) : 0u;
+          if ((uint32_t)lane < cn) st_key[off + lane] = kv[u];
+          const uint64_t* src = a.cand_keys + lbase + (int64_t)c * kCandChunkLen;
+          for (uint32_t j = 64 + lane; j < cn; j += 64) st_key[off + j] = src[j];
+        }
+      }
+      __syncthreads();
+    } else {
+      for (int cb = 0; cb < nch; cb += 64) {
+        const int c = cb + lane;
+        const uint32_t cnt = c < nch ? (uint32_t)cc[c] : 0u;
+        const uint32_t incl = wave_prefix_incl(cnt);
+        if (wave == 0 && c < nch) pref[c] = m + incl - cnt;
+        m += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      }
+      if (tid == 0) pref[nch] = m;
+      __syncthreads();
+      staged = m <= (uint32_t)kFinStage;
+      if (staged) {
+        for (int c = wave; c < nch; c += kFinWaves) {
+          const uint32_t off = pref[c], cn = pref[c + 1] - off;
+          const uint64_t* src = a.cand_keys + lbase + (int64_t)c * kCandChunkLen;
+          for (uint32_t j = lane; j < cn; j += 64) st_key[off + j] = src[j];
+        }
+        __syncthreads();
+      }
+    }
+    const uint32_t need0 = (uint32_t)a.topk < m ? (uint32_t)a.topk : m;
+    // flat candidate index -> slot in the per-chunk lists (unstaged sets)
     auto slot_of = [&](uint32_t fi) -> int64_t {
       int lo = 0, hi = nch - 1;
       while (lo < hi) {
@@ -352,87 +352,94 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
       }
       return lbase + (int64_t)lo * kCandChunkLen + (fi - pref[lo]);
     };
-    const uint32_t need0 = (uint32_t)kk < m ? (uint32_t)kk : m;
-    // stage the candidates in LDS (position order) when they fit; the passes below
-    // then read LDS instead of chasing per-chunk lists in global memory
-    const bool staged = m <= (uint32_t)kFinStage;
-    if (staged) {
-      for (uint32_t fi = tid; fi < m; fi += kFinThreads) {
-        const int64_t slot = slot_of(fi);
-        st_pos[fi] = a.cand_pos[slot];
-        st_s[fi] = __float_as_uint(a.cand_s[slot]);
-      }
-      __syncthreads();
-    }
-    auto score_bits = [&](uint32_t fi) -> uint32_t {
-      return staged ? st_s[fi] : __float_as_uint(a.cand_s[slot_of(fi)]);
+    auto key_of = [&](uint32_t fi) -> uint64_t {
+      return staged ? st_key[fi] : a.cand_keys[slot_of(fi)];
     };
-    auto position = [&](uint32_t fi) -> int32_t {
-      return staged ? st_pos[fi] : a.cand_pos[slot_of(fi)];
-    };
+    auto score_bits = [&](uint32_t fi) -> uint32_t { return (uint32_t)(key_of(fi) >> 32); };
+    auto position = [&](uint32_t fi) -> int32_t { return key_pos(key_of(fi)); };
 
-    // Radix digit 1 (score bits 30..19) finds the bin B holding the k-th largest
-    // score.  If that bin is small and the candidates are staged, its entries are
-    // ranked exactly by brute force (score desc, position asc); otherwise two more
-    // digits give the exact k-th value and ties are taken in position order.
-    for (uint32_t i = tid; i < (uint32_t)kFastBins; i += kFinThreads) lh[i] = 0u;
-    if (tid == 0) {
-      carry[0] = 0u;
-      carry[1] = 0u;
-      nbnd = 0u;
-    }
-    __syncthreads();
+    // digit 1: bin b1 of the need0-th largest score
     for (uint32_t fi = tid; fi < m; fi += kFinThreads) atomicAdd(&lh[score_bits(fi) >> 19], 1u);
     __syncthreads();
     uint32_t b1, above1;
-    block_threshold(lh, kFastBins, need0, b1, above1);
-    const uint32_t need1 = need0 - above1;
-    bool brute = false;
-    if (staged) {
-      // entries of bin b1, compacted in position order by ballot prefix sums
+    block_threshold<kFinThreads, kDigitBins / kFinThreads>(lh, kDigitBins, need0, b1, above1);
+    const uint32_t need1 = need0 - above1;   // >= 1: the bin holds the need0-th entry
+    const uint32_t nb1 = lh[b1];
+    const bool fastk = staged && nb1 <= (uint32_t)kFinBnd;
+    if (fastk) {
+      // the bin's entries (any order: their keys are unique)
       for (uint32_t base = 0; base < m; base += kFinThreads) {
         const uint32_t fi = base + tid;
-        const bool in = fi < m;
-        if (in) flag[fi] = 0u;
-        const bool hit = in && (st_s[fi] >> 19) == b1;
-        const uint64_t hmask = __builtin_amdgcn_ballot_w64(hit);
-        if (lane == 0) wsum[wave][0] = __builtin_popcountll(hmask);
-        __syncthreads();
-        uint32_t slot = nbnd + __builtin_popcountll(hmask & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-        for (int w = 0; w < wave; ++w) slot += wsum[w][0];
-        if (hit && slot < (uint32_t)kFinBnd) blist[slot] = fi;
-        __syncthreads();
-        if (tid == 0) {
-          uint32_t t = nbnd;
-          for (int w = 0; w < kFinThreads / 64; ++w) t += wsum[w][0];
-          nbnd = t;
+        uint64_t key = 0;
+        bool hit = false;
+        if (fi < m) {
+          key = st_key[fi];
+          hit = (uint32_t)(key >> 51) == b1;
         }
-        __syncthreads();
-      }
-      brute = nbnd <= (uint32_t)kFinBnd;
-    }
-    uint32_t vk = 0u, need = need1;
-    if (brute) {
-      const uint32_t nb = nbnd;
-      for (uint32_t e = tid; e < nb; e += kFinThreads) {
-        bnd_s[e] = st_s[blist[e]];
-        bnd_p[e] = st_pos[blist[e]];
+        const uint64_t hm = __builtin_amdgcn_ballot_w64(hit);
+        if (hm != 0ull) {
+          uint32_t wbase = 0;
+          if (lane == 0) wbase = atomicAdd(&nbnd, (uint32_t)__builtin_popcountll(hm));
+          wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase);
+          if (hit) bkey[wbase + lanes_below(hm)] = key;
+        }
       }
       __syncthreads();
-      for (uint32_t e = tid; e < nb; e += kFinThreads) {
-        const uint32_t se = bnd_s[e];
-        const int32_t pe = bnd_p[e];
-        uint32_t rank = 0;
-        for (uint32_t f = 0; f < nb; ++f) {   // broadcast LDS reads, independent iterations
-          const uint32_t sf = bnd_s[f];
-          const int32_t pf = bnd_p[f];
-          rank += (sf > se || (sf == se && pf < pe)) ? 1u : 0u;
+      // rank of entry e = number of bin entries with a larger key; rank need1-1 is
+      // the k-th.  Lanes hold the comparands, waves take the entries, a ballot counts.
+      {
+        constexpr int kJ = kFinBnd / 64;
+        const uint32_t nj = (nb1 + 63) / 64;
+        uint64_t kf[kJ];
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+          const uint32_t f = (uint32_t)(lane + 64 * j);
+          kf[j] = ((uint32_t)j < nj && f < nb1) ? bkey[f] : 0ull;   // keys are > 0
         }
-        flag[blist[e]] = rank < need1 ? 1u : 0u;
+        for (uint32_t e = wave; e < nb1; e += kFinWaves) {
+          const uint64_t ke = bkey[e];
+          uint32_t rank = 0;
+#pragma unroll
+          for (int j = 0; j < kJ; ++j)
+            if ((uint32_t)j < nj) rank += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(kf[j] > ke));
+          if (rank == need1 - 1 && lane == 0) kth = ke;
+        }
       }
       __syncthreads();
+      // chosen = key >= kth: each thread takes a run of consecutive candidates
+      const uint64_t kt = kth;
+      const uint32_t run = (m + kFinThreads - 1) / kFinThreads;
+      const uint32_t f0 = tid * run;
+      uint32_t mine = 0;
+      for (uint32_t i = 0; i < run; ++i) {
+        const uint32_t fi = f0 + i;
+        mine += (fi < m && st_key[fi] >= kt) ? 1u : 0u;
+      }
+      const uint32_t incl = wave_prefix_incl(mine);
+      if (lane == 63) wsum[wave][0] = incl;
+      __syncthreads();
+      uint32_t opos = incl - mine, total = 0;
+#pragma unroll
+      for (int w = 0; w < kFinWaves; ++w) {
+        const uint32_t v = wsum[w][0];
+        total += v;
+        opos += w < wave ? v : 0u;
+      }
+      for (uint32_t i = 0; i < run; ++i) {
+        const uint32_t fi = f0 + i;
+        if (fi < m) {
+          const uint64_t key = st_key[fi];
+          if (key >= kt) {
+            if (opos < need0) out[opos] = key_pos(key);
+            ++opos;
+          }
+        }
+      }
+      kk = (int)(total < need0 ? total : need0);
     } else {
-      uint32_t prefix = b1;
+      // general path: two more digits give the exact k-th score value vk; equal
+      // scores are taken in position order by the ordered pass
+      uint32_t prefix = b1, need = need1;
       const int shifts[2] = {7, 0};
       const int widths[2] = {12, 7};
       for (int d = 0; d < 2; ++d) {
@@ -447,51 +454,47 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
         }
         __syncthreads();
         uint32_t bd, ab;
-        block_threshold(lh, nb, need, bd, ab);
+        block_threshold<kFinThreads, kDigitBins / kFinThreads>(lh, (int)nb, need, bd, ab);
         need -= ab;
         prefix = (prefix << widths[d]) | bd;
       }
-      vk = prefix;   // bits of the k-th largest score
-    }
-    // ordered output of the chosen candidates
-    if (tid == 0) {
-      carry[0] = 0u;   // chosen so far
-      carry[1] = 0u;   // ties so far (general path)
-    }
-    __syncthreads();
-    for (uint32_t base = 0; base < m; base += kFinThreads) {
-      const uint32_t fi = base + tid;
-      const bool in = fi < m;
-      const uint32_t u = in ? score_bits(fi) : 0u;
-      const bool tie = !brute && in && u == vk;
-      const uint64_t tmask = __builtin_amdgcn_ballot_w64(tie);
-      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-      if (lane == 0) wsum[wave][0] = __builtin_popcountll(tmask);
-      __syncthreads();
-      uint32_t tie_rank = carry[1] + __builtin_popcountll(tmask & below);
-      for (int w = 0; w < wave; ++w) tie_rank += wsum[w][0];
-      const bool chosen = in && (brute ? ((u >> 19) > b1 || flag[fi] != 0u)
-                                       : (u > vk || (tie && tie_rank < need)));
-      const uint64_t cmask = __builtin_amdgcn_ballot_w64(chosen);
-      __syncthreads();
-      if (lane == 0) wsum[wave][1] = __builtin_popcountll(cmask);
-      __syncthreads();
-      uint32_t opos = carry[0] + __builtin_popcountll(cmask & below);
-      for (int w = 0; w < wave; ++w) opos += wsum[w][1];
-      if (chosen && opos < (uint32_t)kk) out[opos] = position(fi);
-      __syncthreads();
+      const uint32_t vk = prefix;   // bits of the k-th largest score
       if (tid == 0) {
-        uint32_t tc = 0, cs = 0;
-        for (int w = 0; w < kFinThreads / 64; ++w) {
-          tc += wsum[w][0];
-          cs += wsum[w][1];
-        }
-        carry[0] += cs;
-        carry[1] += tc;
+        carry[0] = 0u;   // chosen so far
+        carry[1] = 0u;   // ties so far
       }
       __syncthreads();
+      for (uint32_t base = 0; base < m; base += kFinThreads) {
+        const uint32_t fi = base + tid;
+        const bool in = fi < m;
+        const uint32_t u = in ? score_bits(fi) : 0u;
+        const bool tie = in && u == vk;
+        const uint64_t tmask = __builtin_amdgcn_ballot_w64(tie);
+        if (lane == 0) wsum[wave][0] = __builtin_popcountll(tmask);
+        __syncthreads();
+        uint32_t tie_rank = carry[1] + lanes_below(tmask);
+        for (int w = 0; w < wave; ++w) tie_rank += wsum[w][0];
+        const bool chosen = in && (u > vk || (tie && tie_rank < need));
+        const uint64_t cmask = __builtin_amdgcn_ballot_w64(chosen);
+        if (lane == 0) wsum[wave][1] = __builtin_popcountll(cmask);
+        __syncthreads();
+        uint32_t opos = carry[0] + lanes_below(cmask);
+        for (int w = 0; w < wave; ++w) opos += wsum[w][1];
+        if (chosen && opos < need0) out[opos] = position(fi);
+        __syncthreads();
+        if (tid == 0) {
+          uint32_t tc = 0, cs = 0;
+          for (int w = 0; w < kFinWaves; ++w) {
+            tc += wsum[w][0];
+            cs += wsum[w][1];
+          }
+          carry[0] += cs;
+          carry[1] += tc;
+        }
+        __syncthreads();
+      }
+      kk = (int)min(need0, carry[0]);
     }
-    kk = (int)min((uint32_t)kk, carry[0]);
   }
   const int nwin = n - w0;
   for (int i = tid; i < nwin; i += kFinThreads) out[kk + i] = w0 + i;
