@@ -18,6 +18,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kScanTargetWorkgroups = 768;   // 3 per CU (3 waves/SIMD) on 256 CUs
+constexpr int kMfmaTargetWorkgroups = 512;   // matrix-core scan: 2 per CU
 constexpr int kMaxSplits = 2048;             // combine kernel keeps one weight per split in LDS
 constexpr int kSparseSplitLen = 64;          // index entries per sparse workgroup
 constexpr int kSelectChunk = kSelectChunkLen;
@@ -93,7 +94,9 @@ Layout make_layout(const hs2_attn_desc* d) {
   L.n_split = (int32_t)ceil_div(d->max_ctx_len, split);
 
   // Record path: a split's records stay in LDS until it is done, which bounds the split.
-  int64_t rsplit = ceil_div(ceil_div(rows, kScanTargetWorkgroups), 256) * 256;
+  // The matrix-core scan holds 2 workgroups per CU: one residency round of 512.
+  const int64_t rec_target = env_int("HS2_SCAN_VALU", 0) ? kScanTargetWorkgroups : kMfmaTargetWorkgroups;
+  int64_t rsplit = ceil_div(ceil_div(rows, rec_target), 256) * 256;
   rsplit = env_int("HS2_SPLIT_LEN", (int)std::min<int64_t>(rsplit, 1 << 30));
   rsplit = ceil_div(rsplit, 256) * 256;
   if (rsplit < 256) rsplit = 256;
@@ -261,7 +264,10 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
 
   TimerRec rec;
   const bool timed = timer_begin(stream, 0, &rec);
-  hipError_t e = launch_scan_dense(sa, fp8, fast, desc->batch, stream);
+  // record path: matrix-core scan (HS2_SCAN_VALU=1 selects the VALU scan instead)
+  const bool mfma = fast && env_int("HS2_SCAN_VALU", 0) == 0;
+  hipError_t e = mfma ? launch_scan_mfma(sa, fp8, desc->batch, stream)
+                      : launch_scan_dense(sa, fp8, fast, desc->batch, stream);
   if (timed) timer_end(stream, &rec);
   if (e != hipSuccess) return HS2_ERR_LAUNCH;
 

@@ -334,13 +334,10 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
   }
 }
 
-// One workgroup per (selection row, head, 32-dim chunk): merges the split partials
+// One workgroup per (selection row, head, 32-dim chunk) merges the split partials
 // into the normalised output and records the row's softmax statistics (M, 1/Z),
-// which the selection kernels need to turn logits into probabilities.
-//
-// Records mode adds workgroups (blockIdx.y >= 4) that merge the per-split record-key
-// histograms of a selection row: 16 bins per workgroup, 16 split groups per bin.
-// Merges the split partials of one (selection, head) for 32 output dims: every
+// which the selection kernels need to turn logits into probabilities.  It merges the
+// split partials of one (selection, head) for 32 output dims: every
 // thread takes whole splits (one pass of loads), folds them with the online-softmax
 // rule, and the block merges the 256 states (wave DPP reductions + LDS).  Workgroups
 // with blockIdx.y >= 4 instead sum kHistMergeSplits per-split key histograms

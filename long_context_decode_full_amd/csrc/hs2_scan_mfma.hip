@@ -1,0 +1,437 @@
+// Matrix-core scan of the Full Attention layer (records mode): the same work as the
+// records mode of the VALU scan (online-softmax partials, a 2-byte bound record per
+// position and a histogram of the candidate keys per split), with both contractions
+// on v_mfma_f32_16x16x32_bf16.
+//
+// HySparse2 article, section 02 "KV Reuse": the full layer attends over the whole
+// cache and its attention scores decide the positions the sparse layers reuse.
+//
+// Per wave step of 32 rows (two 16-row tiles), with lane = 16*grp + w16:
+//   QK   D[row][head] = K[row][:] . Q[head][:]: A = K tile (lane: row w16, 16 bytes
+//        at dims 32s + 8grp of each 32-dim slice s), B = Q^T (lane: head w16, same
+//        dims; heads >= G are zero), four MFMAs per tile.  The accumulator lane
+//        holds rows 4grp+v (v = 0..3) of head w16.
+//   softmax per head: the 8 logits of a lane plus two permlane swaps give the step
+//        maximum of head w16; the running maximum is raised only when a logit
+//        exceeds it by 8 (log2 units).
+//   record per row: log2 of the sum over the group's heads of 2^logit, reduced
+//        over the 8 head lanes of each 16-lane row with DPP.
+//   PV   O^T[dim][head] += V^T[dim][rows] . P[rows][head]: B = P, exactly the
+//        lane's 8 probabilities (rows 4grp+v of both tiles), split into a bf16 high
+//        part and a bf16 residual so the product keeps fp32 accuracy; A = V^T, read
+//        from the wave's LDS copy of the V tile with ds_read_b64_tr_b16 (each lane
+//        gets 4 rows of one dim per read).  Eight 16-dim blocks, two MFMAs each.
+// The K loads feed the MFMA directly (each load instruction covers 16 rows x 64
+// contiguous bytes); V rows are loaded whole (16 lanes per row) and stored to LDS.
+// Loads run one step ahead through a two-buffer ring.
+#include "hs2_rowops.h"
+
+namespace hs2 {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2v_t;
+
+constexpr int kMThreads = 256;
+constexpr int kStepRows = 32;
+constexpr float kMSlack = 8.0f;
+constexpr int kVRow = 272;                    // bytes per staged V row (256 + 16 pad)
+constexpr int kVTile = kStepRows * kVRow;     // per wave
+constexpr int kRecBytes = kMaxRecordSplit * 2;
+constexpr int kHistBytes = kFastBins * 4;
+constexpr int kMergeStride = kPartStride;     // floats per head in the wave merge area: m, z, -, -, o[128]
+constexpr int kMLds = kRecBytes + kHistBytes + 4 * kVTile;
+static_assert(8 * kMergeStride * 4 <= kVTile, "a wave's merge record fits its V tile");
+
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// Two fp32 -> one word of two bf16 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2v_t x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+}
+
+// Max / sum over the 8 lanes w16 = 0..7 (and separately 8..15) of each 16-lane row.
+__device__ __forceinline__ float max8(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppMirror8>(x));
+  return x;
+}
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppMirror8>(x);
+  return x;
+}
+
+// Combine the 4 lanes w16, w16+16, w16+32, w16+48 (the four row groups) with the
+// gfx950 permlane swaps.  The swap results are copied to scalars before any bit
+// cast: a bit cast of a vector element reads element 0 here.
+template <bool kMax>
+__device__ __forceinline__ float reduce_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t a0 = s32[0], a1 = s32[1];
+  x = kMax ? fmaxf(__uint_as_float(a0), __uint_as_float(a1)) : __uint_as_float(a0) + __uint_as_float(a1);
+  const uint32_t w = __float_as_uint(x);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  const uint32_t c0 = s16[0], c1 = s16[1];
+  return kMax ? fmaxf(__uint_as_float(c0), __uint_as_float(c1)) : __uint_as_float(c0) + __uint_as_float(c1);
+}
+__device__ __forceinline__ float max_groups(float x) { return reduce_groups<true>(x); }
+__device__ __forceinline__ float sum_groups(float x) { return reduce_groups<false>(x); }
+
+// One step's loads.  bf16: k[t][q] = 16 bytes of row (tile t, w16), v[i] = 16 bytes
+// of row 4i + grp.  fp8: k[t][q] = 8 codes, v[i] = 16 codes of row 8i + lane/8, plus
+// the per-row scales of the lane's 8 accumulator rows.
+template <bool kFp8>
+struct StepBuf;
+template <>
+struct StepBuf<false> {
+  uint4 k[2][4];
+  uint4 v[8];
+};
+template <>
+struct StepBuf<true> {
+  uint2 k[2][4];
+  uint4 v[4];
+  float ks[2][4], vs[2][4];
+};
+
+template <bool kFp8>
+__device__ __forceinline__ void load_step(StepBuf<kFp8>& s, const uint8_t* __restrict__ kb,
+                                          const uint8_t* __restrict__ vb, const float* __restrict__ ksb,
+                                          const float* __restrict__ vsb, int32_t base, int32_t last,
+                                          int grp, int w16, int lane) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t row = (uint32_t)min(base + 16 * t + w16, last);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (kFp8)
+        s.k[t][q] = *reinterpret_cast<const uint2*>(kb + (uint64_t)row * 128 + 32 * q + 8 * grp);
+      else
+        s.k[t][q] = *reinterpret_cast<const uint4*>(kb + (uint64_t)row * 256 + 64 * q + 16 * grp);
+    }
+  }
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t row = (uint32_t)min(base + 8 * i + (lane >> 3), last);
+      s.v[i] = *reinterpret_cast<const uint4*>(vb + (uint64_t)row * 128 + 16 * (lane & 7));
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t row = (uint32_t)min(base + 16 * t + 4 * grp + v, last);
+        s.ks[t][v] = ksb[row];
+        s.vs[t][v] = vsb[row];
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t row = (uint32_t)min(base + 4 * i + grp, last);
+      s.v[i] = *reinterpret_cast<const uint4*>(vb + (uint64_t)row * 256 + 16 * w16);
+    }
+  }
+}
+
+struct HeadState {
+  f32x4_t o[8];   // o[b][v]: dim 16b + 4grp + v of head w16
+  float m;        // running maximum of head w16 (log2 domain; equal in the 4 groups)
+  float z;        // this lane's share of the softmax denominator
+};
+
+template <bool kFp8>
+__device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x8_t (&qf)[4], uint8_t* vt,
+                                             int32_t base, int32_t w_begin, int32_t w_end, uint32_t cand_span,
+                                             float scale_log2, int G, int grp, int w16, int lane,
+                                             uint16_t* myrec, uint32_t* shist, HeadState& hs) {
+  // V tile -> LDS (row-major, padded rows)
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 c = s.v[i];
+      const uint4 lo = make_uint4(fp8x2_to_bf16x2(c.x, false), fp8x2_to_bf16x2(c.x, true),
+                                  fp8x2_to_bf16x2(c.y, false), fp8x2_to_bf16x2(c.y, true));
+      const uint4 hi = make_uint4(fp8x2_to_bf16x2(c.z, false), fp8x2_to_bf16x2(c.z, true),
+                                  fp8x2_to_bf16x2(c.w, false), fp8x2_to_bf16x2(c.w, true));
+      uint8_t* dst = vt + (8 * i + (lane >> 3)) * kVRow + 32 * (lane & 7);
+      *reinterpret_cast<uint4*>(dst) = lo;
+      *reinterpret_cast<uint4*>(dst + 16) = hi;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(vt + (4 * i + grp) * kVRow + 16 * w16) = s.v[i];
+  }
+
+  // QK
+  f32x4_t d[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    d[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint4 kw;
+      if constexpr (kFp8) {
+        const uint2 c = s.k[t][q];
+        kw = make_uint4(fp8x2_to_bf16x2(c.x, false), fp8x2_to_bf16x2(c.x, true), fp8x2_to_bf16x2(c.y, false),
+                        fp8x2_to_bf16x2(c.y, true));
+      } else {
+        kw = s.k[t][q];
+      }
+      d[t] = mfma16(as_bf16x8(kw), qf[q], d[t]);
+    }
+  }
+  float l[2][4];
+  float mx = kNegInf;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int32_t row = base + 16 * t + 4 * grp + v;
+      float x = d[t][v] * scale_log2;
+      if constexpr (kFp8) x *= s.ks[t][v];
+      l[t][v] = row < w_end ? x : kNegInf;
+      mx = fmaxf(mx, l[t][v]);
+    }
+
+  // bound records: e = log2 sum over the group's heads of 2^l
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float lm = w16 < G ? l[t][v] : kNegInf;
+      const float rmax = max8(lm);
+      const float ex = lm != kNegInf ? fast_exp2(lm - rmax) : 0.0f;
+      const float sum = sum8(ex);
+      const float e = rmax + __builtin_amdgcn_logf(sum);
+      const int32_t row = base + 16 * t + 4 * grp + v;
+      const uint32_t rel = (uint32_t)(row - w_begin);
+      if (w16 == 0 && row < w_end) {
+        const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)e);
+        myrec[rel] = rec;
+        if (rel < cand_span) atomicAdd(&shist[half_order_key(rec) >> kFastShift], 1u);
+      }
+    }
+
+  // online softmax of head w16
+  mx = max_groups(mx);
+  const bool up = mx > hs.m + kMSlack;
+  if (wave_any(up)) {
+    const float mn = up ? mx : hs.m;
+    const float alpha = up ? fast_exp2(hs.m - mn) : 1.0f;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) hs.o[b] *= alpha;
+    hs.z *= alpha;
+    hs.m = mn;
+  }
+  float p[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      p[t][v] = l[t][v] != kNegInf ? fast_exp2(l[t][v] - hs.m) : 0.0f;
+      hs.z += p[t][v];
+      if constexpr (kFp8) p[t][v] *= s.vs[t][v];
+    }
+
+  // P as bf16 high part + bf16 residual (B operand, k slot u <-> tile u/4, row 4grp + u%4)
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float x0 = p[u >> 1][2 * (u & 1)];
+    const float x1 = p[u >> 1][2 * (u & 1) + 1];
+    hw[u] = pack_bf16(x0, x1);
+    lw[u] = pack_bf16(x0 - __builtin_bit_cast(float, hw[u] << 16), x1 - __builtin_bit_cast(float, hw[u] & 0xFFFF0000u));
+  }
+  const bf16x8_t phi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+  const bf16x8_t plo = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+
+  // PV: A = V^T of dim block b, rows 4grp..4grp+3 of both tiles (transposed LDS reads)
+  const uint8_t* tr0 = vt + (4 * grp + (w16 >> 2)) * kVRow + 8 * (w16 & 3);
+  const uint8_t* tr1 = tr0 + 16 * kVRow;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(tr0 + 32 * b));
+    const s16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(tr1 + 32 * b));
+    const uint2 w0 = __builtin_bit_cast(uint2, x0);
+    const uint2 w1 = __builtin_bit_cast(uint2, x1);
+    const bf16x8_t av = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+    hs.o[b] = mfma16(av, phi, hs.o[b]);
+    hs.o[b] = mfma16(av, plo, hs.o[b]);
+  }
+}
+
+template <bool kFp8>
+__global__ __launch_bounds__(kMThreads, 2) void scan_mfma_kernel(ScanArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kMLds];
+  uint16_t* srec = reinterpret_cast<uint16_t*>(lds);
+  uint32_t* shist = reinterpret_cast<uint32_t*>(lds + kRecBytes);
+  uint8_t* vt_all = lds + kRecBytes + kHistBytes;
+
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int bj = blockIdx.z;
+  const int b = bj / a.Lq;
+  const int j = bj - b * a.Lq;
+  const int64_t sel = (int64_t)bj * a.Hkv + g;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int grp = lane >> 4;
+  const int w16 = lane & 15;
+  uint8_t* vt = vt_all + wave * kVTile;
+
+  int64_t ctx = a.ctx_len[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.ctx_max ? a.ctx_max : ctx);
+  int64_t n = ctx - a.Lq + j + 1;
+  n = n < 0 ? 0 : n;
+  const int64_t p_begin = (int64_t)split * a.split_len;
+  int64_t p_end = p_begin + a.split_len;
+  p_end = p_end < n ? p_end : n;
+  const int wave_len = a.split_len >> 2;
+  const int64_t wb64 = p_begin + (int64_t)wave * wave_len;
+  int64_t we64 = wb64 + wave_len;
+  we64 = we64 < p_end ? we64 : p_end;
+  const int32_t w_begin = (int32_t)wb64;   // rows < cap < 2^31
+  const int32_t w_end = (int32_t)(we64 > wb64 ? we64 : wb64);
+  const int nsteps = (w_end - w_begin + kStepRows - 1) / kStepRows;
+
+  // Q^T fragments: head w16, dims 32q + 8grp .. +8
+  bf16x8_t qf[4];
+  {
+    const uint16_t* qh = a.q + ((int64_t)bj * a.Hq + (int64_t)g * a.G + w16) * kHeadDim + 8 * grp;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      qf[q] = as_bf16x8(w16 < a.G ? *reinterpret_cast<const uint4*>(qh + 32 * q) : make_uint4(0u, 0u, 0u, 0u));
+  }
+
+  const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
+  const int rowbytes = kFp8 ? 128 : 256;
+  const uint8_t* kb = a.k + head_row0 * rowbytes;
+  const uint8_t* vb = a.v + head_row0 * rowbytes;
+  const float* ksb = kFp8 ? a.k_scale + head_row0 : nullptr;
+  const float* vsb = kFp8 ? a.v_scale + head_row0 : nullptr;
+
+  // candidates are the positions before the forced window
+  int64_t w0 = n - a.window;
+  w0 = w0 < 0 ? 0 : w0;
+  const uint32_t span = (uint32_t)(w_end - w_begin);
+  uint32_t cand_span = w0 > wb64 ? (uint32_t)(w0 - wb64) : 0u;
+  cand_span = cand_span < span ? cand_span : span;
+  uint16_t* myrec = srec + wave * wave_len;
+
+  for (int i = tid; i < kFastBins; i += kMThreads) shist[i] = 0u;
+  if (split == 0) {   // the combine kernel sums every split's histogram into these words
+    uint32_t* hm = a.hist_merged + sel * kSelWords + kSelHist1Off;
+    for (int i = tid; i < kFastBins; i += kMThreads) hm[i] = 0u;
+  }
+  __syncthreads();
+
+  HeadState hs;
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) hs.o[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  hs.m = kNegInf;
+  hs.z = 0.0f;
+
+  if (nsteps > 0) {
+    const int32_t last = w_end - 1;
+    StepBuf<kFp8> s0, s1;
+    load_step<kFp8>(s0, kb, vb, ksb, vsb, w_begin, last, grp, w16, lane);
+    for (int st = 0; st < nsteps; st += 2) {
+      // straight-line ring: every load is issued (rows past the end re-read `last`)
+      const int32_t b0 = w_begin + st * kStepRows;
+      load_step<kFp8>(s1, kb, vb, ksb, vsb, b0 + kStepRows, last, grp, w16, lane);
+      process_step<kFp8>(s0, qf, vt, b0, w_begin, w_end, cand_span, a.scale_log2, a.G, grp, w16, lane, myrec,
+                         shist, hs);
+      load_step<kFp8>(s0, kb, vb, ksb, vsb, b0 + 2 * kStepRows, last, grp, w16, lane);
+      // a step past the end (odd step count) has every row masked: no effect
+      process_step<kFp8>(s1, qf, vt, b0 + kStepRows, w_begin, w_end, cand_span, a.scale_log2, a.G, grp, w16,
+                         lane, myrec, shist, hs);
+    }
+  }
+
+  // ---- merge: the 4 row groups (shares of z), then the 4 waves through LDS
+  const float zt = sum_groups(hs.z);
+  float* mrec = reinterpret_cast<float*>(vt);   // this wave's tile: its last reads are done
+  if (w16 < 8) {
+    float* mr = mrec + w16 * kMergeStride;
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb)
+      *reinterpret_cast<float4*>(mr + 4 + 16 * bb + 4 * grp) =
+          make_float4(hs.o[bb][0], hs.o[bb][1], hs.o[bb][2], hs.o[bb][3]);
+    if (grp == 0) {
+      mr[0] = hs.m;
+      mr[1] = zt;
+    }
+  }
+  __syncthreads();
+
+  // the split's records and key histogram
+  {
+    const int cnt = p_end > p_begin ? (int)(p_end - p_begin) : 0;
+    uint16_t* grec = a.records + sel * a.logit_stride + p_begin;   // 512-byte aligned
+    for (int i = tid; 2 * i + 1 < cnt; i += kMThreads)
+      reinterpret_cast<uint32_t*>(grec)[i] = reinterpret_cast<const uint32_t*>(srec)[i];
+    if ((cnt & 1) && tid == 0) grec[cnt - 1] = srec[cnt - 1];
+    uint32_t* ghist = reinterpret_cast<uint32_t*>(a.hist_part + (sel * a.n_split + split) * kFastBins);
+    for (int i = tid; i < kFastBins / 2; i += kMThreads)
+      ghist[i] = (shist[2 * i] & 0xFFFFu) | (shist[2 * i + 1] << 16);   // counts < 2^16
+  }
+
+  // merge the 4 waves: thread -> (head, 4 dims)
+  {
+    const int h = tid >> 5;
+    const int dd = (tid & 31) * 4;
+    float Mw = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      Mw = fmaxf(Mw, reinterpret_cast<const float*>(vt_all + w * kVTile)[h * kMergeStride]);
+    float Z = 0.0f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* mr = reinterpret_cast<const float*>(vt_all + w * kVTile) + h * kMergeStride;
+      const float mw = mr[0];
+      const float fw = (mw == kNegInf) ? 0.0f : fast_exp2(mw - Mw);
+      Z += fw * mr[1];
+      const float4 ov = *reinterpret_cast<const float4*>(mr + 4 + dd);
+      acc.x += fw * ov.x;
+      acc.y += fw * ov.y;
+      acc.z += fw * ov.z;
+      acc.w += fw * ov.w;
+    }
+    if (h < a.G) {
+      float* pp = a.part + ((sel * a.n_split + split) * a.G + h) * kPartStride;
+      *reinterpret_cast<float4*>(pp + 4 + dd) = acc;
+      if (dd == 0) {
+        pp[0] = Mw;
+        pp[1] = Z;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_scan_mfma(const ScanArgs& a, bool fp8, int B, hipStream_t st) {
+  dim3 grid(a.n_split, a.Hkv, B * a.Lq);
+  if (fp8)
+    hipLaunchKernelGGL((scan_mfma_kernel<true>), grid, dim3(kMThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((scan_mfma_kernel<false>), grid, dim3(kMThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace hs2
