@@ -25,7 +25,7 @@ METRIC = "Hybrid-Block decode ctx-tokens/s & KV GB/s (%HBM peak) at 1M context"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 SCAN_SOURCES = [os.path.join(ROOT, "long_context_decode_full_amd", "csrc", f)
-                for f in ("hs2_scan.hip", "hs2_device.h", "hs2_internal.h")]
+                for f in ("hs2_scan_mfma.hip", "hs2_rowops.h", "hs2_device.h", "hs2_internal.h")]
 
 
 def log(msg):
@@ -112,7 +112,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": 5}), flush=True)
         return
-    from long_context_decode_full_amd import hs2_timer_collect, hs2_timer_enable
+    from long_context_decode_full_amd import (HS2_TIMER_GATHER, HS2_TIMER_SCAN, hs2_timer_collect,
+                                              hs2_timer_enable)
     from long_context_decode_full_amd import workloads as wl
     from long_context_decode_full_amd.runner import HybridBlockDevice
 
@@ -130,7 +131,7 @@ def main():
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
-    hs2_timer_enable(True)
+    hs2_timer_enable(HS2_TIMER_SCAN)   # events around the context scan only
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -141,13 +142,17 @@ def main():
     st, scan_ms, scan_n, gather_ms, gather_n = hs2_timer_collect()
     assert st == 0 and scan_n == args.steps, (st, scan_n)
 
-    # per-launch distribution of the scan (each step collected on its own)
+    # per-launch distribution of the scan (each step collected on its own), and the
+    # sparse layers' gather kernel, outside the timed region
     per_scan = []
-    hs2_timer_enable(True)
+    hs2_timer_enable(HS2_TIMER_SCAN | HS2_TIMER_GATHER)
+    gather_ms, gather_n = 0.0, 0
     for _ in range(min(args.steps, 30)):
         dev.step()
-        st2, sm, sn, _, _ = hs2_timer_collect()
+        st2, sm, sn, gm, gn = hs2_timer_collect()
         per_scan.append(sm * 1e3 / max(sn, 1))
+        gather_ms += gm
+        gather_n += gn
     hs2_timer_enable(False)
     per_scan.sort()
 
@@ -192,7 +197,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": measured_traffic(args.workload),
-            "kernel": "scan_kernel (split-K full-attention scan)",
+            "kernel": "scan_mfma_kernel (split-K full-attention scan on the matrix cores)",
             "algorithmic_bytes_per_launch": algo,
         },
         "cpu_baseline": None,

@@ -131,14 +131,16 @@ hs2_status hs2_sparse_attn(const hs2_attn_desc* desc,
 /* Static English text for a status; never NULL. */
 const char* hs2_status_string(hs2_status status);
 
-/* Benchmark support.  While enabled (enable != 0), each call records two HIP events
- * on its stream around its dominant kernel (the context scan of
- * hs2_full_attn_select, the gather kernel of hs2_sparse_attn).  The events are
- * created by the library (host-side bookkeeping, no device memory) and kept until
- * hs2_timer_collect, which waits for them and returns the summed milliseconds and
- * the number of launches timed for each kind, then forgets them.  Not thread-safe;
- * meant for single-threaded benchmark drivers. */
-hs2_status hs2_timer_enable(int enable);
+/* Benchmark support.  `mask` selects the kernels timed from now on: HS2_TIMER_SCAN
+ * (the context scan of hs2_full_attn_select), HS2_TIMER_GATHER (the gather kernel of
+ * hs2_sparse_attn), both, or 0 for none.  Each timed call records two HIP events on
+ * its stream around that kernel.  The events are created by the library (host-side
+ * bookkeeping, no device memory) and kept until hs2_timer_collect, which waits for
+ * them and returns the summed milliseconds and the number of launches timed for
+ * each kind, then forgets them.  Not thread-safe; meant for single-threaded
+ * benchmark drivers. */
+enum { HS2_TIMER_SCAN = 1, HS2_TIMER_GATHER = 2 };
+hs2_status hs2_timer_enable(int mask);
 hs2_status hs2_timer_collect(double* scan_ms, int32_t* scan_count,
                              double* gather_ms, int32_t* gather_count);
 

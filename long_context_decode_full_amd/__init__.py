@@ -20,7 +20,8 @@ __all__ = [
     "HS2_ERR_ALIGNMENT", "HS2_ERR_LAUNCH", "HS2_KV_BF16", "HS2_KV_FP8_E4M3FN",
     "HS2_SELECT_TOKEN", "HS2_SELECT_BLOCK", "Hs2AttnDesc", "Hs2Error", "make_desc",
     "hs2_validate", "hs2_workspace_size", "hs2_full_attn_select", "hs2_sparse_attn",
-    "hs2_status_string", "hs2_timer_enable", "hs2_timer_collect", "library_path", "load_library",
+    "hs2_status_string", "hs2_timer_enable", "hs2_timer_collect", "HS2_TIMER_SCAN",
+    "HS2_TIMER_GATHER", "library_path", "load_library",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -163,8 +164,15 @@ def hs2_status_string(status: int) -> str:
     return load_library().hs2_status_string(int(status)).decode()
 
 
-def hs2_timer_enable(enable: bool) -> int:
-    return load_library().hs2_timer_enable(1 if enable else 0)
+HS2_TIMER_SCAN = 1
+HS2_TIMER_GATHER = 2
+
+
+def hs2_timer_enable(mask) -> int:
+    """mask: HS2_TIMER_* bits; True times both kernels, False none."""
+    if mask is True:
+        mask = HS2_TIMER_SCAN | HS2_TIMER_GATHER
+    return load_library().hs2_timer_enable(int(mask))
 
 
 def hs2_timer_collect():

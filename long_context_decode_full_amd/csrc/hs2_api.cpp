@@ -146,12 +146,12 @@ struct TimerRec {
   int kind;   // 0 scan, 1 gather
 };
 std::mutex g_timer_mu;
-bool g_timer_on = false;
+int g_timer_mask = 0;   // HS2_TIMER_* bits
 std::vector<TimerRec> g_timer;
 
 bool timer_begin(hipStream_t st, int kind, TimerRec* rec) {
   std::lock_guard<std::mutex> lk(g_timer_mu);
-  if (!g_timer_on) return false;
+  if ((g_timer_mask & (1 << kind)) == 0) return false;
   if (hipEventCreate(&rec->a) != hipSuccess) return false;
   if (hipEventCreate(&rec->b) != hipSuccess) {
     (void)hipEventDestroy(rec->a);
@@ -393,9 +393,9 @@ HS2_API hs2_status hs2_sparse_attn(const hs2_attn_desc* desc, const void* q, con
   return HS2_OK;
 }
 
-HS2_API hs2_status hs2_timer_enable(int enable) {
+HS2_API hs2_status hs2_timer_enable(int mask) {
   std::lock_guard<std::mutex> lk(g_timer_mu);
-  g_timer_on = enable != 0;
+  g_timer_mask = mask & (HS2_TIMER_SCAN | HS2_TIMER_GATHER);
   return HS2_OK;
 }
 
