@@ -75,6 +75,14 @@ hs2_status validate_desc(const hs2_attn_desc* d) {
   return HS2_OK;
 }
 
+// Token selection for a chunk of query tokens (q_len > 1, bf16 cache) runs the
+// matrix-core chunk kernel, which reads each KV row once for 32 tokens.
+// HS2_CHUNK_PER_TOKEN=1 runs the decode scan once per token instead (comparison).
+bool chunk_path(const hs2_attn_desc* d) {
+  return d->q_len > 1 && d->kv_dtype == HS2_KV_BF16 && d->select_mode == HS2_SELECT_TOKEN &&
+         env_int("HS2_CHUNK_PER_TOKEN", 0) == 0;
+}
+
 Layout make_layout(const hs2_attn_desc* d) {
   Layout L;
   L.n_sel = (int64_t)d->batch * d->q_len * d->n_kv_heads;
@@ -94,9 +102,17 @@ Layout make_layout(const hs2_attn_desc* d) {
   L.n_split = (int32_t)ceil_div(d->max_ctx_len, split);
 
   // Record path: a split's records stay in LDS until it is done, which bounds the split.
-  // The matrix-core scan holds 2 workgroups per CU: one residency round of 512.
-  const int64_t rec_target = env_int("HS2_SCAN_VALU", 0) ? kScanTargetWorkgroups : kMfmaTargetWorkgroups;
-  int64_t rsplit = ceil_div(ceil_div(rows, rec_target), 256) * 256;
+  // The matrix-core scan holds 2 workgroups per CU: one residency round of 512.  The
+  // chunk kernel (one workgroup per CU, 32 query tokens each) takes about 16 splits
+  // of the longest context per (sequence, KV head).
+  int64_t rsplit;
+  if (chunk_path(d)) {
+    rsplit = ceil_div(ceil_div(d->max_ctx_len, 16), 256) * 256;
+    rsplit = std::max<int64_t>(rsplit, 1024);
+  } else {
+    const int64_t rec_target = env_int("HS2_SCAN_VALU", 0) ? kScanTargetWorkgroups : kMfmaTargetWorkgroups;
+    rsplit = ceil_div(ceil_div(rows, rec_target), 256) * 256;
+  }
   rsplit = env_int("HS2_SPLIT_LEN", (int)std::min<int64_t>(rsplit, 1 << 30));
   rsplit = ceil_div(rsplit, 256) * 256;
   if (rsplit < 256) rsplit = 256;
@@ -266,8 +282,9 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   const bool timed = timer_begin(stream, 0, &rec);
   // record path: matrix-core scan (HS2_SCAN_VALU=1 selects the VALU scan instead)
   const bool mfma = fast && env_int("HS2_SCAN_VALU", 0) == 0;
-  hipError_t e = mfma ? launch_scan_mfma(sa, fp8, desc->batch, stream)
-                      : launch_scan_dense(sa, fp8, fast, desc->batch, stream);
+  hipError_t e = (fast && chunk_path(desc)) ? launch_chunk_mfma(sa, desc->batch, stream)
+                 : mfma                     ? launch_scan_mfma(sa, fp8, desc->batch, stream)
+                                            : launch_scan_dense(sa, fp8, fast, desc->batch, stream);
   if (timed) timer_end(stream, &rec);
   if (e != hipSuccess) return HS2_ERR_LAUNCH;
 

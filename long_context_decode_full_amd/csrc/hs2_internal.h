@@ -130,6 +130,7 @@ hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st
 hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t st);
 hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st);
 hipError_t launch_scan_mfma(const ScanArgs& a, bool fp8, int B, hipStream_t st);
+hipError_t launch_chunk_mfma(const ScanArgs& a, int B, hipStream_t st);
 hipError_t launch_scan_sparse(const ScanArgs& a, bool fp8, int B, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_groupsum(const SelectArgs& a, hipStream_t st);

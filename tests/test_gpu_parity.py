@@ -117,10 +117,45 @@ def test_million_token_decode():
     run_and_compare(w, "million")
 
 
-def test_chunk_small_valu_path():
-    """64-token causal chunk on the per-token scan path, reduced lengths, sampled tokens."""
+def test_chunk_small_mfma_path():
+    """64-token causal chunk on the matrix-core chunk kernel, reduced lengths, sampled
+    tokens from both halves of the chunk (one workgroup holds 32 tokens)."""
     w = wl.Workload("chunk reduced", 2, 64, 32, 4, ctx_lens=[5000, 9000], n_needles=16, seed=2005)
-    run_and_compare(w, "chunk-small", tokens=[(0, 0), (0, 1), (0, 40), (0, 63), (1, 0), (1, 63)])
+    run_and_compare(w, "chunk-small", tokens=[(0, 0), (0, 1), (0, 31), (0, 32), (0, 40), (0, 63),
+                                              (1, 0), (1, 33), (1, 63)])
+
+
+def test_chunk_per_token_route(monkeypatch):
+    """The same chunk with HS2_CHUNK_PER_TOKEN=1: the decode scan once per token."""
+    monkeypatch.setenv("HS2_CHUNK_PER_TOKEN", "1")
+    w = wl.Workload("chunk per token", 1, 64, 32, 4, ctx_lens=[6000], n_needles=16, seed=2006)
+    run_and_compare(w, "chunk-per-token", tokens=[(0, 0), (0, 31), (0, 32), (0, 63)])
+
+
+@pytest.mark.parametrize("lq,ctx,hq,hkv", [(16, [3000, 700], 32, 4), (40, [4100], 16, 2),
+                                           (64, [1300, 20000], 16, 16)])
+def test_chunk_shapes(lq, ctx, hq, hkv):
+    """Partial halves (q_len 16, 40), a context shorter than window + top-k, and G = 1."""
+    w = wl.Workload(f"chunk lq{lq}", len(ctx), lq, hq, hkv, ctx_lens=ctx, n_needles=8, seed=2100 + lq)
+    toks = sorted({(b, j) for b in range(len(ctx)) for j in (0, lq // 2, lq - 1)})
+    run_and_compare(w, f"chunk-lq{lq}", tokens=toks)
+
+
+def test_chunk_split_invariant(monkeypatch):
+    """Chunk kernel: several position splits and one split give the same outputs."""
+    from long_context_decode_full_amd.runner import HybridBlockDevice
+    w = wl.Workload("chunk splits", 1, 64, 32, 4, ctx_lens=[9000], n_needles=16, seed=2200)
+    _announce("chunk-split-invariance", w)
+    inp = wl.make_inputs(w)
+    outs = []
+    for sl in ("1024", "16384"):
+        monkeypatch.setenv("HS2_SPLIT_LEN", sl)
+        dev = HybridBlockDevice(inp)
+        dev.step()
+        outs.append(dev.results())
+    a, b = outs
+    assert np.array_equal(a["idx"], b["idx"])
+    assert np.max(np.abs(a["out_full"] - b["out_full"])) <= 2e-6 * max(1.0, np.max(np.abs(b["out_full"])))
 
 
 # ------------------------------------------------------------------ edges
