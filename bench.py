@@ -22,7 +22,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "Hybrid-Block decode ctx-tokens/s & KV GB/s (%HBM peak) at 1M context"
+CHUNK_METRIC = "Hybrid-Block 64-token chunk query-tokens/s & scan MFMA TFLOP/s (%bf16 dense peak)"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 SCAN_SOURCES = [os.path.join(ROOT, "long_context_decode_full_amd", "csrc", f)
                 for f in ("hs2_scan_mfma.hip", "hs2_rowops.h", "hs2_device.h", "hs2_internal.h")]
@@ -64,6 +66,18 @@ def measured_traffic(workload):
     return e.get("hbm_bytes_per_launch")
 
 
+def scan_flops(inp):
+    """Algorithmic FLOPs of one full-attention scan: q.k and p.v (2 x 128 multiply-adds)
+    for every query head and every position visible to its token."""
+    B, Lq, Hq = inp["q_full"].shape[:3]
+    D = inp["q_full"].shape[3]
+    total = 0
+    for b in range(B):
+        for j in range(Lq):
+            total += max(0, int(inp["ctx_len"][b]) - Lq + j + 1)
+    return total * Hq * 4 * D
+
+
 def cpu_baseline(inp, groups, min_s=10.0, max_reps=20):
     """The float64 oracle, as it is, on KV groups `groups` of sequence 0 / token 0,
     repeated until about `min_s` seconds of CPU work; returns seconds per repetition."""
@@ -90,7 +104,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps first: the GPU reaches its sustained clocks after a few tens of ms")
     ap.add_argument("--workload", default="million",
-                    help="tiny | batched | fp8_256k | million")
+                    help="tiny | batched | fp8_256k | million | chunk")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
@@ -158,17 +172,20 @@ def main():
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     ctx = int(np.sum(inp["ctx_len"]))
-    value = ctx / (ms_per_step * 1e-3)
+    chunk = w.q_len > 1
+    # decode: context tokens per second; chunk: query tokens per second
+    value = (w.batch * w.q_len if chunk else ctx) / (ms_per_step * 1e-3)
     scan_avg_s = scan_ms * 1e-3 / scan_n
     algo = kv_bytes(inp)
     achieved = algo / scan_avg_s / 1e9
+    flops = scan_flops(inp)
     idx = dev.idx.cpu().numpy()
     assert np.all((idx >= -1)), "invalid index output"
 
     result = {
-        "metric": METRIC,
+        "metric": CHUNK_METRIC if chunk else METRIC,
         "value": value,
-        "unit": "ctx-tokens/s",
+        "unit": "query-tokens/s" if chunk else "ctx-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -202,22 +219,40 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if chunk:
+        tflops = flops / scan_avg_s / 1e12
+        result["roofline"] = {
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": None,
+            "kernel": "chunk_mfma_kernel (64-token chunk full-attention scan on the matrix cores)",
+            "algorithmic_flops_per_launch": flops,
+            "kv_gbps": achieved,
+        }
+        result["config"]["ctx_lens"] = [int(c) for c in inp["ctx_len"]]
 
     if not args.no_cpu_baseline:
         Hkv = inp["k"].shape[1]
         groups = list(range(Hkv))
         log(f"cpu oracle on KV groups {groups} of {Hkv}")
         dt, cores, reps = cpu_baseline(inp, groups)
-        full_est = dt * Hkv / len(groups) * (w.batch * w.q_len)
+        # the oracle's cost per (sequence, query token) row grows with its visible length
+        n00 = max(1, int(inp["ctx_len"][0]) - w.q_len + 1)
+        rows_scale = sum(max(0, int(inp["ctx_len"][b]) - w.q_len + j + 1)
+                         for b in range(w.batch) for j in range(w.q_len)) / n00
+        full_est = dt * Hkv / len(groups) * rows_scale
         result["cpu_baseline"] = {
-            "value": ctx / full_est,
-            "unit": "ctx-tokens/s",
+            "value": (w.batch * w.q_len if chunk else ctx) / full_est,
+            "unit": "query-tokens/s" if chunk else "ctx-tokens/s",
             "cores": cores,
             "kind": "oracle",
             "sample": (f"float64 numpy oracle, full layer + selection + {w.n_sparse_layers} sparse "
                        f"layers for {len(groups)} of {Hkv} KV groups of sequence 0 / token 0, "
-                       f"{reps} repetition(s) of {dt:.2f}s, scaled by {w.batch * w.q_len} "
-                       f"(sequence, query token) rows to the whole step"),
+                       f"{reps} repetition(s) of {dt:.2f}s, scaled by {rows_scale:.1f} (the step's "
+                       f"visible positions over all (sequence, query token) rows / this row's)"),
         }
     print(json.dumps(result), flush=True)
 

@@ -90,7 +90,10 @@ typedef struct hs2_attn_desc {
 hs2_status hs2_validate(const hs2_attn_desc* desc);
 
 /* Host only: bytes of device workspace that hs2_full_attn_select and
- * hs2_sparse_attn need for this descriptor (the larger of the two). */
+ * hs2_sparse_attn need for this descriptor (the larger of the two).  Requesting probs,
+ * or block mode, keeps 36 bytes of scores per (selection row, position); when that
+ * exceeds 16 GiB (long contexts times many query tokens) those calls return
+ * HS2_ERR_UNSUPPORTED and the size leaves that space out. */
 hs2_status hs2_workspace_size(const hs2_attn_desc* desc, size_t* bytes);
 
 /* The Full Attention layer of a Hybrid Block plus its selection (section 02

@@ -19,6 +19,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kScanTargetWorkgroups = 768;   // 3 per CU (3 waves/SIMD) on 256 CUs
 constexpr int kMfmaTargetWorkgroups = 512;   // matrix-core scan: 2 per CU
+constexpr double kMaxLogitsBytes = 16.0 * (1 << 30);   // logits-path workspace budget
 constexpr int kMaxSplits = 2048;             // combine kernel keeps one weight per split in LDS
 constexpr int kSparseSplitLen = 64;          // index entries per sparse workgroup
 constexpr int kSelectChunk = kSelectChunkLen;
@@ -36,6 +37,8 @@ struct Layout {
   int32_t rec_split_len = 0, rec_n_split = 0;   // scan geometry of the record path
   int32_t n_cchunks = 0;                        // record path: candidate chunks per row
   bool fast_ok = false;                         // record path usable for this descriptor
+  bool logits_ok = false;                       // logits path (probs, block mode) fits its budget
+  size_t off_records = 0;
   size_t off_cand_keys = 0, off_cand_count = 0, off_hist_part = 0;
   size_t off_logits = 0, off_part = 0, off_mz = 0, off_s = 0, off_selblk = 0, off_hist2 = 0,
          off_hist3 = 0, off_winners = 0, off_boundary = 0, total = 0;
@@ -134,16 +137,24 @@ Layout make_layout(const hs2_attn_desc* d) {
 
   const int64_t n = L.n_sel;
   const int64_t nsplit_max = std::max({L.n_split, L.n_split_sp, L.rec_n_split});
+  // The logits path keeps 36 bytes per (selection row, position); beyond kMaxLogitsBytes
+  // (chunk configurations with long contexts) it is not offered and not reserved.
+  L.logits_ok = (double)n * (double)L.logit_stride * 36.0 <= (double)kMaxLogitsBytes;
   size_t off = 0;
-  L.off_logits = off; off = align_up(off + (size_t)n * L.logit_stride * 8 * sizeof(float));
   L.off_part = off;   off = align_up(off + (size_t)n * nsplit_max * L.G * kPartStride * sizeof(float));
   L.off_mz = off;     off = align_up(off + (size_t)n * 16 * sizeof(float));
-  L.off_s = off;      off = align_up(off + (size_t)n * L.logit_stride * sizeof(float));
   L.off_selblk = off; off = align_up(off + (size_t)n * kSelWords * sizeof(uint32_t));
-  L.off_hist2 = off;  off = align_up(off + (size_t)n * kHist2Bins * sizeof(uint32_t));
-  L.off_hist3 = off;  off = align_up(off + (size_t)n * kHist3Bins * sizeof(uint32_t));
-  L.off_winners = off; off = align_up(off + (size_t)n * std::max(d->topk, 1) * sizeof(int32_t));
-  L.off_boundary = off; off = align_up(off + (size_t)n * kBoundaryCap * sizeof(uint2));
+  if (L.logits_ok) {
+    L.off_logits = off; off = align_up(off + (size_t)n * L.logit_stride * 8 * sizeof(float));
+    L.off_records = L.off_logits;   // the record path's 2-byte records share that area
+    L.off_s = off;      off = align_up(off + (size_t)n * L.logit_stride * sizeof(float));
+    L.off_hist2 = off;  off = align_up(off + (size_t)n * kHist2Bins * sizeof(uint32_t));
+    L.off_hist3 = off;  off = align_up(off + (size_t)n * kHist3Bins * sizeof(uint32_t));
+    L.off_winners = off; off = align_up(off + (size_t)n * std::max(d->topk, 1) * sizeof(int32_t));
+    L.off_boundary = off; off = align_up(off + (size_t)n * kBoundaryCap * sizeof(uint2));
+  } else {
+    L.off_records = off; off = align_up(off + (size_t)n * L.logit_stride * sizeof(uint16_t));
+  }
   if (L.fast_ok) {
     const size_t slots = (size_t)n * L.n_cchunks * kCandChunkLen;
     L.off_cand_keys = off; off = align_up(off + slots * sizeof(uint64_t));
@@ -269,9 +280,10 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   // re-scoring of the candidates.  Logits path: every position's logits, needed
   // when the caller wants all probabilities (probs) or for the block comparator.
   const bool fast = L.fast_ok && probs == nullptr && env_int("HS2_FORCE_LOGITS", 0) == 0;
+  if (!fast && !L.logits_ok) return HS2_ERR_UNSUPPORTED;
   ScanArgs sa = scan_args(desc, L, q, k, v, k_scale, v_scale, ctx_len, ws);
   sa.logits = reinterpret_cast<float*>(ws + L.off_logits);
-  sa.records = reinterpret_cast<uint16_t*>(ws + L.off_logits);
+  sa.records = reinterpret_cast<uint16_t*>(ws + L.off_records);
   sa.hist_part = reinterpret_cast<uint16_t*>(ws + L.off_hist_part);
   sa.hist_merged = reinterpret_cast<uint32_t*>(ws + L.off_selblk);
   sa.window = desc->window;

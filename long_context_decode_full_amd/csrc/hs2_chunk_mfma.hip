@@ -41,6 +41,7 @@ constexpr int kCWaves = kCThreads / 64;
 constexpr int kCTokens = 32;                   // query tokens per workgroup
 constexpr int kCPos = 64;                      // positions per iteration
 constexpr float kCSlack = 8.0f;
+constexpr float kMFloor = -1.0e30f;            // initial running maximum (below any logit)
 constexpr int kKRow = 272;                     // bytes per staged K/V row (256 + 16 pad)
 constexpr int kKTile = kCPos * kKRow;
 constexpr int kPRow = 72;                      // bytes per staged P row: 32 query rows bf16 + pad
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
     for (int d = 0; d < 8; ++d) o[qt][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      m[qt][v] = kNegInf;
+      m[qt][v] = kMFloor;   // finite, so exp2(l - m) needs no -inf test
       z[qt][v] = 0.0f;
     }
   }
@@ -211,18 +212,25 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
         sacc[qt][pt] = d;
       }
     }
-    // logits (log2 domain) with the causal mask of each row's token
-    const bool need_mask = (int64_t)P0 + kCPos - 1 > ctx - a.Lq + tok0;   // some position beyond the first token's
+    // logits (log2 domain); the causal mask of each row's token only where some
+    // position lies beyond the first token's (wave-uniform branch)
     float l[2][4][4];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const int64_t pos = (int64_t)P0 + pt * 16 + li;
-        const bool vis = !need_mask || pos <= pj[qt];
+      for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) l[qt][pt][v] = vis ? sacc[qt][pt][v] * a.scale_log2 : kNegInf;
-      }
+        for (int v = 0; v < 4; ++v) l[qt][pt][v] = sacc[qt][pt][v] * a.scale_log2;
+    if ((int64_t)P0 + kCPos - 1 > ctx - a.Lq + tok0) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          const bool vis = (int64_t)P0 + pt * 16 + li <= pj[qt];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) l[qt][pt][v] = vis ? l[qt][pt][v] : kNegInf;
+        }
+    }
 
     // ---- bound records and candidate-key histograms (per token, position)
 #pragma unroll
@@ -237,12 +245,13 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
           lm[v] = hb + v < a.G ? l[qt][pt][v] : kNegInf;
           r = fmaxf(r, lm[v]);
         }
-        r = fmaxf(r, partner(r));
+        // a finite reference (the floor when every head is masked): exp2 of -inf is 0
+        r = fmaxf(fmaxf(r, partner(r)), kMFloor);
         float sum = 0.0f;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) sum += lm[v] != kNegInf ? fast_exp2(lm[v] - r) : 0.0f;
+        for (int v = 0; v < 4; ++v) sum += fast_exp2(lm[v] - r);
         sum += partner(sum);
-        const float e = r + __builtin_amdgcn_logf(sum);
+        const float e = r + __builtin_amdgcn_logf(sum);   // -inf when nothing is visible
         const int64_t pos = (int64_t)P0 + pt * 16 + li;
         const int tl = tokl[qt];
         if ((grp & 1) == 0 && tl < ntok && pos <= pj[qt]) {
@@ -256,29 +265,33 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
       }
     }
 
-    // ---- online softmax per query row
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      float mx[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float x = fmaxf(fmaxf(l[qt][0][v], l[qt][1][v]), fmaxf(l[qt][2][v], l[qt][3][v]));
-        mx[v] = max16(x);
-      }
+    // ---- online softmax per query row.  The running maximum m only needs raising
+    // when some logit exceeds m + 8: a per-lane test and one ballot per step; the
+    // exact row maximum (DPP over the row group) only on that rare path.
+    {
+      float x[2][4];
       bool up_any = false;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) up_any |= mx[v] > m[qt][v] + kCSlack;
-      if (wave_any(up_any)) {
+      for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const bool up = mx[v] > m[qt][v] + kCSlack;
-          const float mn = up ? mx[v] : m[qt][v];
-          const float alpha = up ? fast_exp2(m[qt][v] - mn) : 1.0f;
-#pragma unroll
-          for (int d = 0; d < 8; ++d) o[qt][d][v] *= alpha;
-          z[qt][v] *= alpha;
-          m[qt][v] = mn;
+          x[qt][v] = fmaxf(fmaxf(l[qt][0][v], l[qt][1][v]), fmaxf(l[qt][2][v], l[qt][3][v]));
+          up_any |= x[qt][v] > m[qt][v] + kCSlack;
         }
+      if (wave_any(up_any)) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float mx = max16(x[qt][v]);
+            const bool up = mx > m[qt][v] + kCSlack;
+            const float mn = up ? mx : m[qt][v];
+            const float alpha = up ? fast_exp2(m[qt][v] - mn) : 1.0f;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) o[qt][d][v] *= alpha;
+            z[qt][v] *= alpha;
+            m[qt][v] = mn;
+          }
       }
     }
 
@@ -294,7 +307,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
           float p[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            p[v] = l[qt][pt][v] != kNegInf ? fast_exp2(l[qt][pt][v] - m[qt][v]) : 0.0f;
+            p[v] = fast_exp2(l[qt][pt][v] - m[qt][v]);   // m is finite: -inf logits give 0
             z[qt][v] += p[v];
           }
           const uint32_t h01 = pack_bf16(p[0], p[1]);
@@ -345,7 +358,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
 #pragma unroll
         for (int d = 0; d < 8; ++d) pp[4 + 16 * d + li] = o[qt][d][v];
         if (li == 0) {
-          pp[0] = m[qt][v];
+          pp[0] = m[qt][v] == kMFloor ? kNegInf : m[qt][v];   // no visible position: -inf
           pp[1] = zz;
         }
       }

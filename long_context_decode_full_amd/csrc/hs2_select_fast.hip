@@ -227,17 +227,27 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   const float* ksb = kFp8 ? a.k_scale + head_row0 : nullptr;
   const float Mown = Mh[hown];
   const float izown = iz[hown];
-  for (int i0 = wave * 4; i0 < cnt; i0 += 16) {
-    const int i = i0 + rgrp;
-    const bool valid = i < cnt;
-    const int32_t t = cpos[valid ? i : i0];
-    RowData d;
-    load_key<kFp8>(kb, ksb, (uint32_t)t, r, d);
-    const float l = row_logit<kFp8>(qp, d, a.scale_log2);
-    float part = ((r & 1) == 0 && hown < a.G) ? fast_exp2(l - Mown) * izown : 0.0f;
-    const float s = rowgroup_sum16(part);
-    if (valid && r == 0) {
-      a.cand_keys[slot0 + i] = cand_key(__float_as_uint(s), t);
+  // Batches of kRescoreBatch wave steps: all their key loads are issued before the
+  // first row is scored, so a long candidate list does not wait on one load per step.
+  constexpr int kRescoreBatch = 4;
+  for (int i0 = wave * 4; i0 < cnt; i0 += 16 * kRescoreBatch) {
+    RowData d[kRescoreBatch];
+    int32_t tpos[kRescoreBatch];
+#pragma unroll
+    for (int u = 0; u < kRescoreBatch; ++u) {
+      const int ib = i0 + 16 * u;
+      const int i = ib + rgrp;
+      // past the end: re-read the batch's first row (valid), the result is dropped
+      tpos[u] = cpos[i < cnt ? i : i0];
+      load_key<kFp8>(kb, ksb, (uint32_t)tpos[u], r, d[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRescoreBatch; ++u) {
+      const int i = i0 + 16 * u + rgrp;
+      const float l = row_logit<kFp8>(qp, d[u], a.scale_log2);
+      const float part = ((r & 1) == 0 && hown < a.G) ? fast_exp2(l - Mown) * izown : 0.0f;
+      const float s = rowgroup_sum16(part);
+      if (i < cnt && r == 0) a.cand_keys[slot0 + i] = cand_key(__float_as_uint(s), tpos[u]);
     }
   }
 }
