@@ -39,6 +39,8 @@ struct Layout {
   bool fast_ok = false;                         // record path usable for this descriptor
   bool logits_ok = false;                       // logits path (probs, block mode) fits its budget
   size_t off_records = 0;
+  size_t off_blse = 0;                          // chunk block mode: per-block sums
+  int64_t blse_stride = 0;
   size_t off_cand_keys = 0, off_cand_count = 0, off_hist_part = 0;
   size_t off_logits = 0, off_part = 0, off_mz = 0, off_s = 0, off_selblk = 0, off_hist2 = 0,
          off_hist3 = 0, off_winners = 0, off_boundary = 0, total = 0;
@@ -85,6 +87,12 @@ bool chunk_path(const hs2_attn_desc* d) {
   return d->q_len > 1 && d->kv_dtype == HS2_KV_BF16 && d->select_mode == HS2_SELECT_TOKEN &&
          env_int("HS2_CHUNK_PER_TOKEN", 0) == 0;
 }
+// The block comparator for a chunk (block sizes that are multiples of 64) takes its
+// block masses from the same kernel's per-block sums instead of per-position logits.
+bool chunk_block_path(const hs2_attn_desc* d) {
+  return d->q_len > 1 && d->kv_dtype == HS2_KV_BF16 && d->select_mode == HS2_SELECT_BLOCK &&
+         d->block_size % 64 == 0 && env_int("HS2_CHUNK_PER_TOKEN", 0) == 0;
+}
 
 Layout make_layout(const hs2_attn_desc* d) {
   Layout L;
@@ -109,7 +117,7 @@ Layout make_layout(const hs2_attn_desc* d) {
   // chunk kernel (one workgroup per CU, 32 query tokens each) takes about 16 splits
   // of the longest context per (sequence, KV head).
   int64_t rsplit;
-  if (chunk_path(d)) {
+  if (chunk_path(d) || chunk_block_path(d)) {
     rsplit = ceil_div(ceil_div(d->max_ctx_len, 16), 256) * 256;
     rsplit = std::max<int64_t>(rsplit, 1024);
   } else {
@@ -154,6 +162,10 @@ Layout make_layout(const hs2_attn_desc* d) {
     L.off_boundary = off; off = align_up(off + (size_t)n * kBoundaryCap * sizeof(uint2));
   } else {
     L.off_records = off; off = align_up(off + (size_t)n * L.logit_stride * sizeof(uint16_t));
+  }
+  if (chunk_block_path(d)) {
+    L.blse_stride = ceil_div(d->max_ctx_len, 64);
+    L.off_blse = off; off = align_up(off + (size_t)n * L.blse_stride * 8 * sizeof(float));
   }
   if (L.fast_ok) {
     const size_t slots = (size_t)n * L.n_cchunks * kCandChunkLen;
@@ -263,6 +275,57 @@ static ScanArgs scan_args(const hs2_attn_desc* d, const Layout& L, const void* q
   return a;
 }
 
+// Block comparator for a chunk: the chunk kernel's per-block sums, the split combine,
+// then the block selection on those sums.
+hs2_status chunk_block_select(const hs2_attn_desc* desc, const Layout& L, ScanArgs sa,
+                              const int32_t* ctx_len, float* out, int32_t* idx, uint8_t* ws,
+                              hipStream_t stream) {
+  sa.records = nullptr;
+  sa.hist_part = nullptr;
+  sa.hist_merged = nullptr;
+  sa.blse = reinterpret_cast<float*>(ws + L.off_blse);
+  sa.blse_stride = L.blse_stride;
+  sa.window = 0;
+  sa.n_split = L.rec_n_split;
+  sa.split_len = L.rec_split_len;
+  TimerRec rec;
+  const bool timed = timer_begin(stream, 0, &rec);
+  const hipError_t e = launch_chunk_mfma(sa, desc->batch, stream);
+  if (timed) timer_end(stream, &rec);
+  if (e != hipSuccess) return HS2_ERR_LAUNCH;
+
+  CombineArgs ca{};
+  ca.part = sa.part;
+  ca.out = out;
+  ca.mz = reinterpret_cast<float*>(ws + L.off_mz);
+  ca.hist_out = reinterpret_cast<uint32_t*>(ws + L.off_selblk);
+  ca.n_sel = (int32_t)L.n_sel;
+  ca.Hkv = desc->n_kv_heads;
+  ca.G = L.G;
+  ca.Hq = desc->n_q_heads;
+  ca.n_split = sa.n_split;
+  if (launch_combine(ca, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+
+  SelectArgs sl{};
+  sl.mz = ca.mz;
+  sl.ctx_len = ctx_len;
+  sl.ctx_max = desc->max_ctx_len;
+  sl.idx = idx;
+  sl.n_sel = (int32_t)L.n_sel;
+  sl.Lq = desc->q_len;
+  sl.Hkv = desc->n_kv_heads;
+  sl.G = L.G;
+  sl.window = desc->window;
+  sl.topk = desc->topk;
+  sl.S = L.S;
+  sl.block_size = desc->block_size;
+  sl.n_blocks = desc->n_blocks;
+  sl.blse = sa.blse;
+  sl.blse_stride = L.blse_stride;
+  if (launch_block_select(sl, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+  return HS2_OK;
+}
+
 HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q, const void* k,
                                         const void* v, const float* k_scale, const float* v_scale,
                                         const int32_t* ctx_len, float* out, int32_t* idx,
@@ -280,8 +343,10 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   // re-scoring of the candidates.  Logits path: every position's logits, needed
   // when the caller wants all probabilities (probs) or for the block comparator.
   const bool fast = L.fast_ok && probs == nullptr && env_int("HS2_FORCE_LOGITS", 0) == 0;
-  if (!fast && !L.logits_ok) return HS2_ERR_UNSUPPORTED;
+  const bool cblock = chunk_block_path(desc) && probs == nullptr;
+  if (!fast && !cblock && !L.logits_ok) return HS2_ERR_UNSUPPORTED;
   ScanArgs sa = scan_args(desc, L, q, k, v, k_scale, v_scale, ctx_len, ws);
+  if (cblock) return chunk_block_select(desc, L, sa, ctx_len, out, idx, ws, stream);
   sa.logits = reinterpret_cast<float*>(ws + L.off_logits);
   sa.records = reinterpret_cast<uint16_t*>(ws + L.off_records);
   sa.hist_part = reinterpret_cast<uint16_t*>(ws + L.off_hist_part);

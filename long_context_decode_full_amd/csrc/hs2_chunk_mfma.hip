@@ -115,9 +115,11 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   if (ntok <= 0) return;
   const int64_t sel_tok0 = ((int64_t)b * a.Lq + tok0) * a.Hkv + g;   // sel of token tok0; +Hkv per token
 
+  const bool want_rec = a.records != nullptr;   // token selection: records + histograms
+  const bool want_blk = a.blse != nullptr;      // block comparator: per-block sums
   // histograms of this workgroup's tokens; split 0 also clears the merged ones
   for (int i = tid; i < kCTokens * kHistWords; i += kCThreads) shist[i] = 0u;
-  if (split == 0) {
+  if (want_rec && split == 0) {
     for (int i = tid; i < ntok * kFastBins; i += kCThreads) {
       const int t = i / kFastBins;
       a.hist_merged[(sel_tok0 + (int64_t)t * a.Hkv) * kSelWords + kSelHist1Off + (i - t * kFastBins)] = 0u;
@@ -233,6 +235,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
     }
 
     // ---- bound records and candidate-key histograms (per token, position)
+    if (want_rec) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       const int hb = 4 * (grp & 1);   // heads of this lane's rows: hb .. hb+3
@@ -263,6 +266,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
           }
         }
       }
+    }
     }
 
     // ---- online softmax per query row.  The running maximum m only needs raising
@@ -296,6 +300,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
     }
 
     // ---- P V, one half of the positions at a time
+    float bsum[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // this block's sums
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       // P of position tiles 2hf, 2hf+1 -> LDS [position][query row], high part and residual
@@ -309,6 +314,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
           for (int v = 0; v < 4; ++v) {
             p[v] = fast_exp2(l[qt][pt][v] - m[qt][v]);   // m is finite: -inf logits give 0
             z[qt][v] += p[v];
+            bsum[qt][v] += p[v];
           }
           const uint32_t h01 = pack_bf16(p[0], p[1]);
           const uint32_t h23 = pack_bf16(p[2], p[3]);
@@ -339,6 +345,27 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
         }
       }
     }
+    if (want_blk) {
+      // log2 of the sum of 2^logit over this 64-position block, per (token, head)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        float lse[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float x = bsum[qt][v];
+          x += dpp<kDppXor1>(x);
+          x += dpp<kDppXor2>(x);
+          x += dpp<kDppMirror8>(x);
+          x += dpp<kDppRor8>(x);
+          lse[v] = m[qt][v] + __builtin_amdgcn_logf(x);   // -inf for an empty block
+        }
+        const int tl = tokl[qt];
+        if (li == 0 && tl < ntok) {
+          float* dst = a.blse + ((sel_tok0 + (int64_t)tl * a.Hkv) * a.blse_stride + P0 / kCPos) * 8 + 4 * (grp & 1);
+          *reinterpret_cast<float4*>(dst) = make_float4(lse[0], lse[1], lse[2], lse[3]);
+        }
+      }
+    }
   }
 
   // ---- partials per (token, head): rows 4grp+v of tile qt
@@ -365,6 +392,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
     }
   }
   // ---- per-token key histograms of this split
+  if (!want_rec) return;
   __syncthreads();
   for (int i = tid; i < ntok * kHistWords; i += kCThreads) {
     const int t = i / kHistWords;

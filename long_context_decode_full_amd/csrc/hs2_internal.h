@@ -59,6 +59,9 @@ struct ScanArgs {
   uint16_t* hist_part;      // records mode: [n_sel, n_split, kFastBins] key histograms
   uint32_t* hist_merged;    // records mode: merged histograms at + sel*kSelWords + kSelHist1Off,
                             // cleared by split 0 of each selection
+  float* blse;              // chunk block mode: [n_sel, blse_stride, 8] log2 of the sum of
+                            // 2^logit over each aligned 64-position block, per head
+  int64_t blse_stride;
   int32_t window;           // records mode: positions >= ctx - window are not candidates
   float* part;              // [n_sel, n_split, G, kPartStride]
   int64_t cap;              // rows per (sequence, KV head)
@@ -103,6 +106,8 @@ struct SelectArgs {
   int32_t chunk_len;        // positions per workgroup in the streaming passes
   int32_t n_chunks;
   int32_t with_hist;        // token mode: build the first histogram
+  const float* blse;        // block mode from the chunk kernel's block sums, else nullptr
+  int64_t blse_stride;
 };
 
 struct FastSelArgs {

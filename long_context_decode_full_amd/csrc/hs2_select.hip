@@ -414,12 +414,37 @@ __global__ __launch_bounds__(kBlkThreads) void block_select_kernel(SelectArgs a)
   __shared__ int32_t red_i[kBlkThreads / 64];
   __shared__ int32_t cnt[4097];
 
-  for (int blk = tid; blk < nb; blk += kBlkThreads) {
-    const int t0 = blk * bs;
-    const int t1 = (t0 + bs < n) ? t0 + bs : n;
-    float acc = 0.0f;
-    for (int t = t0; t < t1; ++t) acc += srow[t];
-    mass[blk] = acc;
+  if (a.blse != nullptr) {
+    // chunk kernel: per 64-position block and head h, L_h = log2 sum 2^logit, so the
+    // block's share of head h's softmax is 2^(L_h - M_h) / Z_h (bs is a multiple of 64)
+    float Mh[8], iz[8];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      Mh[h] = a.mz[(sel * 8 + h) * 2 + 0];
+      iz[h] = a.mz[(sel * 8 + h) * 2 + 1];
+    }
+    const int sub = bs / 64;
+    const int nsub = (n + 63) / 64;   // 64-blocks holding visible positions
+    const float* brow = a.blse + sel * a.blse_stride * 8;
+    for (int blk = tid; blk < nb; blk += kBlkThreads) {
+      float acc = 0.0f;
+      for (int u = 0; u < sub; ++u) {
+        const int sb = blk * sub + u;
+        if (sb >= nsub) break;
+#pragma unroll
+        for (int h = 0; h < 8; ++h)
+          if (h < a.G) acc += fast_exp2(brow[(int64_t)sb * 8 + h] - Mh[h]) * iz[h];
+      }
+      mass[blk] = acc;
+    }
+  } else {
+    for (int blk = tid; blk < nb; blk += kBlkThreads) {
+      const int t0 = blk * bs;
+      const int t1 = (t0 + bs < n) ? t0 + bs : n;
+      float acc = 0.0f;
+      for (int t = t0; t < t1; ++t) acc += srow[t];
+      mass[blk] = acc;
+    }
   }
   __syncthreads();
   const int take = a.n_blocks < nb ? a.n_blocks : nb;

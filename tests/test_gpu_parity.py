@@ -239,6 +239,16 @@ def test_block_baseline_chunk():
     run_and_compare(w, "block-chunk", mode="block", tokens=[(0, 0), (0, 7), (0, 15)])
 
 
+@pytest.mark.parametrize("lq,ctx,bs,nb", [(64, [5000, 12000], 64, 18), (40, [4100], 128, 9),
+                                           (16, [700], 64, 18)])
+def test_block_baseline_chunk_kernel(lq, ctx, bs, nb):
+    """Block comparator on the chunk kernel's per-block sums (block sizes that are
+    multiples of 64), including a context shorter than the block budget."""
+    w = wl.Workload(f"block chunk lq{lq}", len(ctx), lq, 32, 4, ctx_lens=ctx, n_needles=8, seed=3710 + lq)
+    toks = sorted({(b, j) for b in range(len(ctx)) for j in (0, lq // 2, lq - 1)})
+    run_and_compare(w, f"block-chunk-lq{lq}", mode="block", block_size=bs, n_blocks=nb, tokens=toks)
+
+
 def test_rows_with_no_visible_position():
     """ctx_len < Lq leaves the first query tokens with nothing visible: out = 0, idx = -1."""
     w = wl.Workload("empty rows", 2, 4, 16, 2, ctx_lens=[6, 3000], seed=3800)
