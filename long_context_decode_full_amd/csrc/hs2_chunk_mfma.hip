@@ -91,6 +91,8 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   uint8_t* pst_all = lds + 2 * kKTile;
   uint32_t* shist = reinterpret_cast<uint32_t*>(lds + 2 * kKTile + kCWaves * kPWave);
 
+  // (Placing the two token halves of a split on one XCD, 8 workgroups apart, was
+  // measured slower: the pair then contends for the same L2 lines at the same time.)
   const int half = blockIdx.x & 1;
   const int split = blockIdx.x >> 1;
   const int g = blockIdx.y;

@@ -83,6 +83,7 @@ struct CombineArgs {
   const uint16_t* hist_part;  // records mode: per-split key histograms to merge, or nullptr
   uint32_t* hist_out;       // merged histogram of selection `sel` at hist_out + sel*kSelWords
                             // + kSelHist1Off (atomic sums into words the scan cleared)
+  int32_t hist_only;        // launch-internal: blockIdx.y indexes histogram groups only
   int32_t n_sel, Hkv, G, Hq, n_split;
 };
 

@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int sh = blockIdx.x;
   const int sel = sh / a.G;
   const int h = sh - sel * a.G;
-  const int chunk = blockIdx.y;
+  const int chunk = blockIdx.y + (a.hist_only ? kHeadDim / 32 : 0);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -466,6 +466,60 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
 }
 
+// Few splits (sparse layers, chunk rows): one thread per (row, head, 4 dims) folds
+// every split itself, four splits of loads in flight; no cross-thread reduction.
+constexpr int kSmallSplits = 32;
+__global__ __launch_bounds__(256) void combine_small_kernel(CombineArgs a) {
+  const int tid = threadIdx.x;
+  const int64_t pair = (int64_t)blockIdx.x * 8 + (tid >> 5);   // sel * G + h
+  const int dq = tid & 31;
+  if (pair >= (int64_t)a.n_sel * a.G) return;
+  const int sel = (int)(pair / a.G);
+  const int h = (int)(pair - (int64_t)sel * a.G);
+  const int64_t split_stride = (int64_t)a.G * kPartStride;
+  const float* base = a.part + ((int64_t)sel * a.n_split * a.G + h) * kPartStride;
+  float m_loc = kNegInf, z_loc = 0.0f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < a.n_split; s0 += 4) {
+    float ms[4], zs[4];
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = min(s0 + u, a.n_split - 1);
+      const float* ps = base + (int64_t)s * split_stride;
+      ms[u] = s0 + u < a.n_split ? ps[0] : kNegInf;
+      zs[u] = ps[1];
+      v[u] = *reinterpret_cast<const float4*>(ps + 4 + 4 * dq);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (ms[u] == kNegInf) continue;
+      const float mn = fmaxf(m_loc, ms[u]);
+      const float fo = fast_exp2(m_loc - mn);
+      const float fn = fast_exp2(ms[u] - mn);
+      z_loc = z_loc * fo + zs[u] * fn;
+      o.x = o.x * fo + v[u].x * fn;
+      o.y = o.y * fo + v[u].y * fn;
+      o.z = o.z * fo + v[u].z * fn;
+      o.w = o.w * fo + v[u].w * fn;
+      m_loc = mn;
+    }
+  }
+  const float iz = z_loc > 0.0f ? 1.0f / z_loc : 0.0f;
+  const int bj = sel / a.Hkv;
+  const int g = sel - bj * a.Hkv;
+  *reinterpret_cast<float4*>(a.out + ((int64_t)bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim + 4 * dq) =
+      make_float4(o.x * iz, o.y * iz, o.z * iz, o.w * iz);
+  if (a.mz != nullptr && dq == 0) {
+    a.mz[((int64_t)sel * 8 + h) * 2 + 0] = m_loc;
+    a.mz[((int64_t)sel * 8 + h) * 2 + 1] = iz;
+  }
+  if (a.sel_zero != nullptr && h == 0) {
+    uint32_t* zp = a.sel_zero + (int64_t)sel * a.sel_zero_words;
+    for (int w = dq; w < a.sel_zero_words; w += 32) zp[w] = 0u;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st) {
@@ -496,6 +550,16 @@ hipError_t launch_scan_sparse(const ScanArgs& a, bool fp8, int B, hipStream_t st
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   const int n_groups = (a.n_split + kHistMergeSplits - 1) / kHistMergeSplits;
   const int extra = a.hist_part != nullptr ? (n_groups + a.G - 1) / a.G : 0;
+  if (a.n_split <= kSmallSplits) {
+    const int64_t pairs = (int64_t)a.n_sel * a.G;
+    hipLaunchKernelGGL(combine_small_kernel, dim3((unsigned)((pairs + 7) / 8)), dim3(256), 0, st, a);
+    if (extra > 0) {   // histogram merge only
+      CombineArgs h = a;
+      h.hist_only = 1;
+      hipLaunchKernelGGL(combine_kernel, dim3(a.n_sel * a.G, extra), dim3(256), 0, st, h);
+    }
+    return hipGetLastError();
+  }
   dim3 grid(a.n_sel * a.G, kHeadDim / 32 + extra);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, a);
   return hipGetLastError();
