@@ -36,6 +36,7 @@ struct Layout {
   int32_t chunk_len = 0, n_chunks = 0;
   int32_t rec_split_len = 0, rec_n_split = 0;   // scan geometry of the record path
   int32_t n_cchunks = 0;                        // record path: candidate chunks per row
+  int32_t cand_chunk_len = 0;                   // positions per candidate chunk
   bool fast_ok = false;                         // record path usable for this descriptor
   bool logits_ok = false;                       // logits path (probs, block mode) fits its budget
   size_t off_records = 0;
@@ -130,7 +131,11 @@ Layout make_layout(const hs2_attn_desc* d) {
   if (rsplit > kMaxRecordSplit) rsplit = kMaxRecordSplit;
   L.rec_split_len = (int32_t)rsplit;
   L.rec_n_split = (int32_t)ceil_div(d->max_ctx_len, rsplit);
-  L.n_cchunks = (int32_t)ceil_div(d->max_ctx_len, kCandChunkLen);
+  // candidate workgroups: ~64 per row, 2048..16384 positions each (a power of two)
+  int64_t clen = kMinCandChunkLen;
+  while (clen < kCandChunkLen && clen * 64 < d->max_ctx_len) clen *= 2;
+  L.cand_chunk_len = (int32_t)clen;
+  L.n_cchunks = (int32_t)ceil_div(d->max_ctx_len, clen);
   L.fast_ok = d->select_mode == HS2_SELECT_TOKEN && L.n_cchunks <= kMaxFastChunks &&
               L.rec_n_split <= kMaxSplits;
 
@@ -168,7 +173,7 @@ Layout make_layout(const hs2_attn_desc* d) {
     L.off_blse = off; off = align_up(off + (size_t)n * L.blse_stride * 8 * sizeof(float));
   }
   if (L.fast_ok) {
-    const size_t slots = (size_t)n * L.n_cchunks * kCandChunkLen;
+    const size_t slots = (size_t)n * L.n_cchunks * L.cand_chunk_len;
     L.off_cand_keys = off; off = align_up(off + slots * sizeof(uint64_t));
     L.off_cand_count = off; off = align_up(off + (size_t)n * L.n_cchunks * sizeof(int32_t));
     L.off_hist_part = off; off = align_up(off + (size_t)n * L.rec_n_split * kFastBins * sizeof(uint16_t));
@@ -399,6 +404,7 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
     fa.cap = desc->kv_capacity;
     fa.scale_log2 = sa.scale_log2;
     fa.n_chunks = L.n_cchunks;
+    fa.chunk_len = L.cand_chunk_len;
     fa.n_sel = (int32_t)L.n_sel;
     fa.Lq = desc->q_len;
     fa.Hq = desc->n_q_heads;

@@ -21,7 +21,8 @@ constexpr int kSelectChunkLen = 4096; // positions per workgroup in the selectio
 constexpr int kFastBins = 1024;       // histogram of the record keys (top 10 of 16 bits)
 constexpr int kFastShift = 6;
 constexpr int kHistMergeSplits = 16;  // per-split histograms summed by one combine workgroup
-constexpr int kCandChunkLen = 16384;  // record path: positions per candidate workgroup
+constexpr int kCandChunkLen = 16384;  // record path: most positions per candidate workgroup
+constexpr int kMinCandChunkLen = 2048;  // fewest (a power of two in between is chosen per call)
 constexpr int kMaxFastChunks = 8192;  // positions per row <= kMaxFastChunks * kCandChunkLen
 // Per-selection control block (u32 words): [0,16) state, [16,20) pass tickets,
 // [32, 32+2048) first histogram.  The logits path clears it in the combine kernel;
@@ -118,8 +119,8 @@ struct FastSelArgs {
   const int32_t* ctx_len;
   int64_t ctx_max;
   uint32_t* selblk;         // [n_sel, kSelWords]
-  uint64_t* cand_keys;      // [n_sel, n_chunks, kCandChunkLen] candidate keys: fp32 bits of
-                            // the exact score << 32 | (2^31 - 1 - position)
+  uint64_t* cand_keys;      // [n_sel, n_chunks, chunk_len] candidate keys: fp32 bits of the
+                            // exact score (+inf when certainly selected) << 32 | (2^31-1-position)
   int32_t* cand_count;      // [n_sel, n_chunks]
   int32_t* idx;             // [n_sel, S]
   const uint16_t* q;        // full-layer queries (exact re-score)
@@ -128,6 +129,7 @@ struct FastSelArgs {
   int64_t cap;
   float scale_log2;
   int32_t n_chunks;
+  int32_t chunk_len;        // positions per candidate workgroup (power of two, 2048..16384)
   int32_t n_sel, Lq, Hq, Hkv, G;
   int32_t window, topk, S;
 };

@@ -124,10 +124,15 @@ __device__ __forceinline__ int32_t key_pos(uint64_t key) {
   return 0x7FFFFFFF - (int32_t)(uint32_t)key;
 }
 
-constexpr int kRecPerThread = kCandChunkLen / kThreads;   // 64
-
 // ------------------------------------------------------------------ candidates + exact re-score
-template <bool kFp8>
+// One workgroup per (row, chunk of chunk_len positions).  The threshold bin of the
+// k-th record gives two tests per position (records are bounds, see above):
+//   candidate: its upper bound reaches the lower bound of the k-th score;
+//   certain:   its lower bound exceeds the upper bound of the k-th score (built from
+//              the bin's upper edge), so it is selected whatever the exact scores are.
+// Certain positions get an infinite score key without re-scoring; only the uncertain
+// candidates re-read their key rows.  Keys stay in position order per chunk.
+template <bool kFp8, int R>   // R = records per thread = chunk_len / 256 (8..64)
 __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   const int chunk = blockIdx.x;
   const int64_t sel = blockIdx.y;
@@ -136,14 +141,17 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   const int wave = tid >> 6;
   const RowGeom rg = row_geom(a, sel);
   if (rg.w0 <= a.topk || a.topk == 0) return;
-  const int64_t c0 = (int64_t)chunk * kCandChunkLen;
+  constexpr int clen = R * kThreads;
+  constexpr int nv = R / 8;       // 16-byte loads per thread
+  const int64_t c0 = (int64_t)chunk * clen;
   if (c0 >= rg.w0) {
     if (tid == 0) a.cand_count[sel * a.n_chunks + chunk] = 0;
     return;
   }
 
-  __shared__ int32_t cpos[kCandChunkLen];
-  __shared__ int32_t total_s;
+  __shared__ uint16_t cpos[kCandChunkLen];    // chunk-relative positions of the candidates
+  __shared__ uint16_t ulist[kCandChunkLen];   // indices into cpos of the uncertain ones
+  __shared__ uint32_t total_s;
   float Mh[8], iz[8];
   load_mz(a, sel, Mh, iz);
   const int64_t bj = sel / a.Hkv;
@@ -156,20 +164,19 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);
 
   const uint16_t* rrow = a.records + sel * a.rec_stride;
-  // Each thread owns kRecPerThread consecutive positions (128 bytes of records, one
-  // batch of 16-byte loads); a block-wide exclusive scan of the per-thread hit counts
-  // places the candidates in LDS in position order.
-  const int64_t t0 = c0 + (int64_t)tid * kRecPerThread;
-  uint32_t words[kRecPerThread / 2];
-  if (t0 + kRecPerThread <= rg.w0) {
+  // Each thread owns R consecutive positions (one batch of 16-byte loads); a
+  // block-wide exclusive scan of the per-thread counts keeps position order.
+  const int64_t t0 = c0 + (int64_t)tid * R;
+  uint32_t words[R / 2];
+  if (t0 + R <= rg.w0) {
 #pragma unroll
-    for (int v = 0; v < kRecPerThread / 8; ++v) {
+    for (int v = 0; v < nv; ++v) {
       const uint4 x = *reinterpret_cast<const uint4*>(rrow + t0 + 8 * v);
       words[4 * v + 0] = x.x; words[4 * v + 1] = x.y; words[4 * v + 2] = x.z; words[4 * v + 3] = x.w;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kRecPerThread / 2; ++i) {
+    for (int i = 0; i < R / 2; ++i) {
       const int64_t t = t0 + 2 * i;
       const uint32_t lo = t < rg.w0 ? (uint32_t)rrow[t] : 0u;
       const uint32_t hi = t + 1 < rg.w0 ? (uint32_t)rrow[t + 1] : 0u;
@@ -180,7 +187,8 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   uint32_t tb, above;
   block_threshold<kThreads, kFastBins / kThreads>(sel_block(a, sel) + kSelHist1Off, kFastBins,
                                                   (uint32_t)a.topk, tb, above);
-  const uint32_t ebits = half_bits_of_key(tb << kFastShift);   // smallest record in the bin
+  const uint32_t ebits = half_bits_of_key(tb << kFastShift);                  // smallest record in the bin
+  const uint32_t ebits_hi = half_bits_of_key(((tb + 1) << kFastShift) - 1);   // largest
   float lwmin = __builtin_huge_valf(), lwmax = -__builtin_huge_valf();
 #pragma unroll
   for (int h = 0; h < 8; ++h) {
@@ -192,34 +200,57 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   }
   // candidate  <=>  e + u(e) + log2 max w  >=  e* - u(e*) + log2 min w  (with slack)
   const float thr = half_bits_to_float(ebits) - half_ulp(ebits) - (lwmax - lwmin) - 2.0f * kBoundSlack;
+  // certain    <=>  e - u(e) + log2 min w  >   e_hi + u(e_hi) + log2 max w  (with slack)
+  const float thr_in = half_bits_to_float(ebits_hi) + half_ulp(ebits_hi) + (lwmax - lwmin) + 2.0f * kBoundSlack;
 
-  uint64_t hitmask = 0ull;
+  // The certain test pays off where candidates are dense: rows whose candidate range
+  // is short next to top-k (row-uniform); long rows have a few per workgroup.
+  const bool use_cert = rg.w0 < (int64_t)a.topk * 64;
+  uint64_t hitmask = 0ull, certmask = 0ull;
+  if (use_cert) {
 #pragma unroll
-  for (int i = 0; i < kRecPerThread; ++i) {
-    const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-    const bool hit = t0 + i < rg.w0 && half_bits_to_float(rb) + half_ulp(rb) >= thr;
-    hitmask |= (uint64_t)hit << i;
+    for (int i = 0; i < R; ++i) {
+      const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      const float e = half_bits_to_float(rb), u = half_ulp(rb);
+      const bool hit = t0 + i < rg.w0 && e + u >= thr;
+      hitmask |= (uint64_t)hit << i;
+      certmask |= (uint64_t)(hit && e - u > thr_in) << i;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      hitmask |= (uint64_t)(t0 + i < rg.w0 && half_bits_to_float(rb) + half_ulp(rb) >= thr) << i;
+    }
   }
-  const uint32_t nhit = (uint32_t)__builtin_popcountll(hitmask);
-  // block exclusive scan of nhit
+  const uint64_t uncmask = hitmask & ~certmask;
+  // block exclusive scan of (hits, uncertain hits), packed in one word (each < 2^16)
+  const uint32_t mine = (uint32_t)__builtin_popcountll(hitmask) | ((uint32_t)__builtin_popcountll(uncmask) << 16);
   __shared__ uint32_t wscan[kThreads / 64];
-  const uint32_t x = wave_prefix_incl(nhit);
+  const uint32_t x = wave_prefix_incl(mine);
   if (lane == 63) wscan[wave] = x;
   __syncthreads();
-  uint32_t before = x - nhit;
+  uint32_t before = x - mine;
   for (int w = 0; w < wave; ++w) before += wscan[w];
-  if (tid == kThreads - 1) total_s = (int)(before + nhit);
+  if (tid == kThreads - 1) total_s = before + mine;
+  const int64_t slot0 = (sel * a.n_chunks + chunk) * (int64_t)clen;
+  uint32_t ih = before & 0xFFFFu, iu = before >> 16;
   uint64_t hm = hitmask;
   while (hm) {
     const int i = __builtin_ctzll(hm);
     hm &= hm - 1;
-    cpos[before++] = (int32_t)(t0 + i);
+    cpos[ih] = (uint16_t)(t0 + i - c0);
+    if ((uncmask >> i) & 1ull)
+      ulist[iu++] = (uint16_t)ih;
+    else
+      a.cand_keys[slot0 + ih] = cand_key(0x7F800000u, (int32_t)(t0 + i));   // certainly selected
+    ++ih;
   }
   __syncthreads();
-  const int cnt = total_s;
-  const int64_t slot0 = (sel * a.n_chunks + chunk) * (int64_t)kCandChunkLen;
+  const int cnt = (int)(total_s & 0xFFFFu);   // candidates
+  const int unc = (int)(total_s >> 16);       // of which uncertain
   if (tid == 0) a.cand_count[sel * a.n_chunks + chunk] = cnt;
-  if (cnt == 0) return;
+  if (unc == 0) return;
 
   // exact re-score: 4 rows per wave step, the scan's lane layout and arithmetic
   const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
@@ -230,15 +261,16 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   // Batches of kRescoreBatch wave steps: all their key loads are issued before the
   // first row is scored, so a long candidate list does not wait on one load per step.
   constexpr int kRescoreBatch = 4;
-  for (int i0 = wave * 4; i0 < cnt; i0 += 16 * kRescoreBatch) {
+  for (int i0 = wave * 4; i0 < unc; i0 += 16 * kRescoreBatch) {
     RowData d[kRescoreBatch];
     int32_t tpos[kRescoreBatch];
+    int tidx[kRescoreBatch];
 #pragma unroll
     for (int u = 0; u < kRescoreBatch; ++u) {
-      const int ib = i0 + 16 * u;
-      const int i = ib + rgrp;
+      const int i = i0 + 16 * u + rgrp;
       // past the end: re-read the batch's first row (valid), the result is dropped
-      tpos[u] = cpos[i < cnt ? i : i0];
+      tidx[u] = ulist[i < unc ? i : i0];
+      tpos[u] = (int32_t)(c0 + cpos[tidx[u]]);
       load_key<kFp8>(kb, ksb, (uint32_t)tpos[u], r, d[u]);
     }
 #pragma unroll
@@ -247,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
       const float l = row_logit<kFp8>(qp, d[u], a.scale_log2);
       const float part = ((r & 1) == 0 && hown < a.G) ? fast_exp2(l - Mown) * izown : 0.0f;
       const float s = rowgroup_sum16(part);
-      if (i < cnt && r == 0) a.cand_keys[slot0 + i] = cand_key(__float_as_uint(s), tpos[u]);
+      if (i < unc && r == 0) a.cand_keys[slot0 + tidx[u]] = cand_key(__float_as_uint(s), tpos[u]);
     }
   }
 }
@@ -296,9 +328,10 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
       nbnd = 0u;
       kth = ~0ull;
     }
-    const int nch = (w0 + kCandChunkLen - 1) / kCandChunkLen;
+    const int clen = a.chunk_len;
+    const int nch = (w0 + clen - 1) / clen;
     const int32_t* cc = a.cand_count + sel * a.n_chunks;
-    const int64_t lbase = sel * a.n_chunks * (int64_t)kCandChunkLen;
+    const int64_t lbase = sel * a.n_chunks * (int64_t)clen;
     constexpr int kU = 4;   // chunks per wave in the single-round copy (64 = 16 waves x 4)
     uint32_t m = 0;
     bool staged;
@@ -311,7 +344,7 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int c = wave + u * kFinWaves;
-        kv[u] = c < nch ? a.cand_keys[lbase + (int64_t)c * kCandChunkLen + lane] : 0ull;
+        kv[u] = c < nch ? a.cand_keys[lbase + (int64_t)c * clen + lane] : 0ull;
       }
       const uint32_t incl = wave_prefix_incl(cnt);
       m = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
@@ -327,7 +360,7 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
           const uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)(incl - cnt), c & 63);
           const uint32_t cn = c < nch ? (uint32_t)__builtin_amdgcn_readlane((int)cnt, c & 63) : 0u;
           if ((uint32_t)lane < cn) st_key[off + lane] = kv[u];
-          const uint64_t* src = a.cand_keys + lbase + (int64_t)c * kCandChunkLen;
+          const uint64_t* src = a.cand_keys + lbase + (int64_t)c * clen;
           for (uint32_t j = 64 + lane; j < cn; j += 64) st_key[off + j] = src[j];
         }
       }
@@ -346,7 +379,7 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
       if (staged) {
         for (int c = wave; c < nch; c += kFinWaves) {
           const uint32_t off = pref[c], cn = pref[c + 1] - off;
-          const uint64_t* src = a.cand_keys + lbase + (int64_t)c * kCandChunkLen;
+          const uint64_t* src = a.cand_keys + lbase + (int64_t)c * clen;
           for (uint32_t j = lane; j < cn; j += 64) st_key[off + j] = src[j];
         }
         __syncthreads();
@@ -360,7 +393,7 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
         const int mid = (lo + hi + 1) >> 1;
         if (pref[mid] <= fi) lo = mid; else hi = mid - 1;
       }
-      return lbase + (int64_t)lo * kCandChunkLen + (fi - pref[lo]);
+      return lbase + (int64_t)lo * clen + (fi - pref[lo]);
     };
     auto key_of = [&](uint32_t fi) -> uint64_t {
       return staged ? st_key[fi] : a.cand_keys[slot_of(fi)];
@@ -513,11 +546,22 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
 
 }  // namespace
 
+template <bool kFp8>
+void launch_candidates_r(const FastSelArgs& a, hipStream_t st) {
+  const dim3 grid(a.n_chunks, a.n_sel);
+  switch (a.chunk_len / kThreads) {
+    case 8: hipLaunchKernelGGL((candidate_kernel<kFp8, 8>), grid, dim3(kThreads), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((candidate_kernel<kFp8, 16>), grid, dim3(kThreads), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((candidate_kernel<kFp8, 32>), grid, dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((candidate_kernel<kFp8, 64>), grid, dim3(kThreads), 0, st, a); break;
+  }
+}
+
 hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st) {
   if (fp8)
-    hipLaunchKernelGGL(candidate_kernel<true>, dim3(a.n_chunks, a.n_sel), dim3(kThreads), 0, st, a);
+    launch_candidates_r<true>(a, st);
   else
-    hipLaunchKernelGGL(candidate_kernel<false>, dim3(a.n_chunks, a.n_sel), dim3(kThreads), 0, st, a);
+    launch_candidates_r<false>(a, st);
   return hipGetLastError();
 }
 
