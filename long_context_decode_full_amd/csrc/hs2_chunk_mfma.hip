@@ -20,8 +20,11 @@
 //   softmax per query row: maxima over the 16 lanes of a row group (DPP), lazy
 //     raise by 8 (log2 units) as in the decode scan.
 //   record per (token, position): log2 of the sum over the token's heads of
-//     2^logit: 4 heads in the lane, the other 4 in the partner row group
-//     (permlane16 swap).
+//     2^logit, from the probabilities already formed for P.V: with U the largest
+//     running maximum of the token's heads, e = U + log2 sum_h p_h 2^(m_h - U)
+//     (4 heads in the lane, 4 in the partner row group via a permlane16 swap);
+//     sums below 2^-100 (terms lost to underflow could matter there) take the
+//     exact form on a wave-uniform branch.
 //   O = P V: P (bf16 high part + bf16 residual) is staged per wave in LDS position-
 //     major and read back as the A operand with ds_read_b64_tr_b16; B = V read from
 //     the V tile with the same transposed read.
@@ -83,7 +86,39 @@ __device__ __forceinline__ float partner(float x) {
   return __uint_as_float((__lane_id() & 16) ? a0 : a1);
 }
 
-template <bool kFp8Unused>
+// U per query tile and c per accumulator row, after the running maxima m changed.
+__device__ __forceinline__ void update_record_scale(const float (&m)[2][4], int hbase, int G,
+                                                    float (&U)[2], float (&c)[2][4]) {
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float u = kMFloor;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) u = hbase + v < G ? fmaxf(u, m[qt][v]) : u;
+    u = fmaxf(u, partner(u));
+    U[qt] = u;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) c[qt][v] = hbase + v < G ? fast_exp2(m[qt][v] - u) : 0.0f;
+  }
+}
+// log2 of the sum over the token's valid heads of 2^l (this lane's 4 + the partner's 4),
+// with the per-position maximum as reference.
+__device__ __forceinline__ float exact_record(const float (&lv)[4], int hbase, int G) {
+  float lm[4];
+  float r = kNegInf;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    lm[v] = hbase + v < G ? lv[v] : kNegInf;
+    r = fmaxf(r, lm[v]);
+  }
+  r = fmaxf(fmaxf(r, partner(r)), kMFloor);   // finite: exp2 of -inf is 0
+  float sum = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) sum += fast_exp2(lm[v] - r);
+  sum += partner(sum);
+  return r + __builtin_amdgcn_logf(sum);
+}
+
+template <bool kBlockMode>   // false: records + key histograms; true: per-block sums
 __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kCLds];
   uint8_t* ktile = lds;
@@ -117,8 +152,8 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   if (ntok <= 0) return;
   const int64_t sel_tok0 = ((int64_t)b * a.Lq + tok0) * a.Hkv + g;   // sel of token tok0; +Hkv per token
 
-  const bool want_rec = a.records != nullptr;   // token selection: records + histograms
-  const bool want_blk = a.blse != nullptr;      // block comparator: per-block sums
+  constexpr bool want_rec = !kBlockMode;   // token selection: records + histograms
+  constexpr bool want_blk = kBlockMode;    // block comparator: per-block sums
   // histograms of this workgroup's tokens; split 0 also clears the merged ones
   for (int i = tid; i < kCTokens * kHistWords; i += kCThreads) shist[i] = 0u;
   if (want_rec && split == 0) {
@@ -143,16 +178,21 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   }
   // per accumulator row (qt, v): token, head, visibility limits
   int tokl[2];        // token of the lane's rows in tile qt (within the workgroup)
-  int64_t pj[2];      // last visible position of that token
-  int64_t w0j[2];     // first window position (candidates are < w0j)
+  int32_t pj[2];      // last visible position of that token (positions < cap < 2^31)
+  int32_t w0j[2];     // first window position (candidates are < w0j)
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     tokl[qt] = 2 * (2 * wave + qt) + (grp >> 1);
     const int64_t pp = ctx - a.Lq + tok0 + tokl[qt];
-    pj[qt] = pp;
+    pj[qt] = (int32_t)pp;
     int64_t w0 = pp + 1 - a.window;
-    w0j[qt] = w0 < 0 ? 0 : w0;
+    w0j[qt] = (int32_t)(w0 < 0 ? 0 : w0);
   }
+
+  // record scale: U = the largest running maximum over the token's heads, c_v =
+  // 2^(m_v - U) for this lane's 4 heads (0 for head slots >= G)
+  const int hbase = 4 * (grp & 1);   // heads of this lane's accumulator rows: hbase .. hbase+3
+  float U[2], c[2][4];
 
   const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
   const uint8_t* kb = a.k + head_row0 * 256;
@@ -170,6 +210,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
       z[qt][v] = 0.0f;
     }
   }
+  update_record_scale(m, hbase, a.G, U, c);
   __syncthreads();
 
   const int nit = p_end > p_begin ? (int)((p_end - p_begin + kCPos - 1) / kCPos) : 0;
@@ -230,45 +271,10 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
-          const bool vis = (int64_t)P0 + pt * 16 + li <= pj[qt];
+          const bool vis = P0 + pt * 16 + li <= pj[qt];
 #pragma unroll
           for (int v = 0; v < 4; ++v) l[qt][pt][v] = vis ? l[qt][pt][v] : kNegInf;
         }
-    }
-
-    // ---- bound records and candidate-key histograms (per token, position)
-    if (want_rec) {
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const int hb = 4 * (grp & 1);   // heads of this lane's rows: hb .. hb+3
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        float lm[4];
-        float r = kNegInf;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          lm[v] = hb + v < a.G ? l[qt][pt][v] : kNegInf;
-          r = fmaxf(r, lm[v]);
-        }
-        // a finite reference (the floor when every head is masked): exp2 of -inf is 0
-        r = fmaxf(fmaxf(r, partner(r)), kMFloor);
-        float sum = 0.0f;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) sum += fast_exp2(lm[v] - r);
-        sum += partner(sum);
-        const float e = r + __builtin_amdgcn_logf(sum);   // -inf when nothing is visible
-        const int64_t pos = (int64_t)P0 + pt * 16 + li;
-        const int tl = tokl[qt];
-        if ((grp & 1) == 0 && tl < ntok && pos <= pj[qt]) {
-          const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)e);
-          a.records[(sel_tok0 + (int64_t)tl * a.Hkv) * a.logit_stride + pos] = rec;
-          if (pos < w0j[qt]) {
-            const uint32_t bin = half_order_key(rec) >> kFastShift;
-            atomicAdd(&shist[tl * kHistWords + (bin >> 1)], (bin & 1) ? 65536u : 1u);
-          }
-        }
-      }
-    }
     }
 
     // ---- online softmax per query row.  The running maximum m only needs raising
@@ -298,6 +304,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
             z[qt][v] *= alpha;
             m[qt][v] = mn;
           }
+        update_record_scale(m, hbase, a.G, U, c);
       }
     }
 
@@ -316,7 +323,27 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
           for (int v = 0; v < 4; ++v) {
             p[v] = fast_exp2(l[qt][pt][v] - m[qt][v]);   // m is finite: -inf logits give 0
             z[qt][v] += p[v];
-            bsum[qt][v] += p[v];
+            if constexpr (want_blk) bsum[qt][v] += p[v];
+          }
+          if constexpr (want_rec) {
+            // record: e = U + log2 sum_h p_h 2^(m_h - U) over the token's heads (4 here, 4 in
+            // the partner row group); the exact form when that sum is below 2^-100
+            const int32_t pos = P0 + pt * 16 + li;
+            const bool vis = pos <= pj[qt];
+            float sum = p[0] * c[qt][0] + p[1] * c[qt][1] + p[2] * c[qt][2] + p[3] * c[qt][3];
+            sum += partner(sum);
+            float e = U[qt] + __builtin_amdgcn_logf(sum);
+            const bool tiny = vis && sum < 0x1p-100f;
+            if (wave_any(tiny)) e = tiny ? exact_record(l[qt][pt], hbase, a.G) : e;
+            const int tl = tokl[qt];
+            if ((grp & 1) == 0 && tl < ntok && vis) {
+              const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)e);
+              a.records[(sel_tok0 + (int64_t)tl * a.Hkv) * a.logit_stride + pos] = rec;
+              if (pos < w0j[qt]) {
+                const uint32_t bin = half_order_key(rec) >> kFastShift;
+                atomicAdd(&shist[tl * kHistWords + (bin >> 1)], (bin & 1) ? 65536u : 1u);
+              }
+            }
           }
           const uint32_t h01 = pack_bf16(p[0], p[1]);
           const uint32_t h23 = pack_bf16(p[2], p[3]);
@@ -347,7 +374,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
         }
       }
     }
-    if (want_blk) {
+    if constexpr (want_blk) {
       // log2 of the sum of 2^logit over this 64-position block, per (token, head)
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
@@ -408,7 +435,10 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
 
 hipError_t launch_chunk_mfma(const ScanArgs& a, int B, hipStream_t st) {
   dim3 grid(a.n_split * 2, a.Hkv, B);
-  hipLaunchKernelGGL((chunk_mfma_kernel<false>), grid, dim3(kCThreads), 0, st, a);
+  if (a.blse != nullptr)
+    hipLaunchKernelGGL((chunk_mfma_kernel<true>), grid, dim3(kCThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((chunk_mfma_kernel<false>), grid, dim3(kCThreads), 0, st, a);
   return hipGetLastError();
 }
 
