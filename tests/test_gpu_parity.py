@@ -117,6 +117,16 @@ def test_million_token_decode():
     run_and_compare(w, "million")
 
 
+@pytest.mark.parametrize("mode", ["token", "block"])
+def test_chunk_full_config(mode):
+    """The ragged 64-token chunk at full size (16 sequences, contexts 8K-512K) in the
+    benchmark's launch configuration; tokens sampled from the longest and a short
+    sequence and from both halves of the chunk."""
+    w = wl.standard_workloads()["chunk"]
+    run_and_compare(w, f"chunk-full-{mode}", mode=mode,
+                    tokens=[(6, 0), (6, 63), (0, 31), (12, 32), (13, 5)])
+
+
 def test_chunk_small_mfma_path():
     """64-token causal chunk on the matrix-core chunk kernel, reduced lengths, sampled
     tokens from both halves of the chunk (one workgroup holds 32 tokens)."""
