@@ -78,7 +78,7 @@ def scan_flops(inp):
     return total * Hq * 4 * D
 
 
-def cpu_baseline(inp, groups, min_s=10.0, max_reps=20):
+def cpu_baseline(inp, groups, min_s=10.0, max_reps=20, mode="token"):
     """The float64 oracle, as it is, on KV groups `groups` of sequence 0 / token 0,
     repeated until about `min_s` seconds of CPU work; returns seconds per repetition."""
     import oracle
@@ -90,7 +90,7 @@ def cpu_baseline(inp, groups, min_s=10.0, max_reps=20):
     reps = 0
     t0 = time.perf_counter()
     while reps < max_reps:
-        oracle.hybrid_block_token(inp, 0, 0, groups=groups)
+        oracle.hybrid_block_token(inp, 0, 0, groups=groups, mode=mode)
         reps += 1
         if time.perf_counter() - t0 >= min_s:
             break
@@ -105,6 +105,9 @@ def main():
                     help="untimed steps first: the GPU reaches its sustained clocks after a few tens of ms")
     ap.add_argument("--workload", default="million",
                     help="tiny | batched | fp8_256k | million | chunk")
+    ap.add_argument("--select", default="token", choices=["token", "block"],
+                    help="token selection (window 128 + top-k 1024) or the first-generation block "
+                         "comparator (18 blocks of 64, no forced window)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
@@ -136,7 +139,7 @@ def main():
     t0 = time.perf_counter()
     inp = wl.make_inputs(w, threads=16)
     log(f"inputs ready in {time.perf_counter() - t0:.1f}s; uploading")
-    dev = HybridBlockDevice(inp, device="cuda:0")
+    dev = HybridBlockDevice(inp, device="cuda:0", mode=args.select)
     torch.cuda.synchronize()
 
     log(f"warmup {args.warmup}")
@@ -198,8 +201,10 @@ def main():
         "config": {
             "workload": f"{w.name}: B={w.batch}, ctx_len={w.ctx_lens}, q_len={w.q_len}, "
                         f"Hq={w.n_q_heads}/Hkv={w.n_kv_heads}, head_dim={w.head_dim}, "
-                        f"{w.kv_dtype} KV, window 128 + top-k 1024, 1 full + "
-                        f"{w.n_sparse_layers} sparse layers",
+                        f"{w.kv_dtype} KV, "
+                        + ("window 128 + top-k 1024" if args.select == "token" else
+                           "block comparator: 18 blocks of 64")
+                        + f", 1 full + {w.n_sparse_layers} sparse layers",
             "batch": w.batch, "ctx_tokens": ctx, "q_len": w.q_len,
             "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "kv_dtype": w.kv_dtype,
         },
@@ -238,7 +243,7 @@ def main():
         Hkv = inp["k"].shape[1]
         groups = list(range(Hkv))
         log(f"cpu oracle on KV groups {groups} of {Hkv}")
-        dt, cores, reps = cpu_baseline(inp, groups)
+        dt, cores, reps = cpu_baseline(inp, groups, mode=args.select)
         # the oracle's cost per (sequence, query token) row grows with its visible length
         n00 = max(1, int(inp["ctx_len"][0]) - w.q_len + 1)
         rows_scale = sum(max(0, int(inp["ctx_len"][b]) - w.q_len + j + 1)

@@ -112,6 +112,15 @@ def test_fp8_256k_decode(with_probs):
     run_and_compare(w, "fp8_256k", with_probs=with_probs)
 
 
+@pytest.mark.parametrize("wname", ["tiny", "fp8_256k"])
+def test_record_path_on_valu_scan(monkeypatch, wname):
+    """HS2_SCAN_VALU=1: the record path's scan on the VALU kernel (dot2 + DPP butterfly)
+    instead of the matrix cores; same parity bar."""
+    monkeypatch.setenv("HS2_SCAN_VALU", "1")
+    w = wl.standard_workloads()[wname]
+    run_and_compare(w, f"{wname}-valu-scan")
+
+
 def test_million_token_decode():
     w = wl.standard_workloads()["million"]
     run_and_compare(w, "million")
