@@ -35,6 +35,21 @@ __device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
 
+// Streaming loads with the non-temporal hint (global_load ... nt): data read once is
+// not kept for reuse in the caches.  On MI355X a 2 GiB stream read this way runs at
+// ~7.0 TB/s against ~6.2 TB/s with ordinary loads.
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ uint2 load_nt(const uint2* p) {
+  const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(t[0], t[1]);
+}
+__device__ __forceinline__ float load_nt(const float* p) { return __builtin_nontemporal_load(p); }
+
 __device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -64,20 +64,27 @@ struct RowData {
   float ks, vs;    // fp8 per-token scales
 };
 
-template <bool kFp8>
+// kStream: the rows are read once (the dense scan), so they take the non-temporal
+// hint; the 16 lanes of a row cover whole cache lines.  Scales stay ordinary loads
+// (4 bytes per row: a line serves 32 rows).
+template <bool kFp8, bool kStream = false>
 __device__ __forceinline__ void load_row(const uint8_t* __restrict__ kb, const uint8_t* __restrict__ vb,
                                          const float* __restrict__ ksb, const float* __restrict__ vsb,
                                          uint32_t t, int r, RowData& d) {
   if (kFp8) {
-    const uint2 kw = *reinterpret_cast<const uint2*>(kb + (uint64_t)t * 128 + 8 * r);
-    const uint2 vw = *reinterpret_cast<const uint2*>(vb + (uint64_t)t * 128 + 8 * r);
+    const uint2* kp = reinterpret_cast<const uint2*>(kb + (uint64_t)t * 128 + 8 * r);
+    const uint2* vp = reinterpret_cast<const uint2*>(vb + (uint64_t)t * 128 + 8 * r);
+    const uint2 kw = kStream ? load_nt(kp) : *kp;
+    const uint2 vw = kStream ? load_nt(vp) : *vp;
     d.k[0] = kw.x; d.k[1] = kw.y; d.k[2] = 0u; d.k[3] = 0u;
     d.v[0] = vw.x; d.v[1] = vw.y; d.v[2] = 0u; d.v[3] = 0u;
     d.ks = ksb[t];
     d.vs = vsb[t];
   } else {
-    const uint4 kw = *reinterpret_cast<const uint4*>(kb + (uint64_t)t * 256 + 16 * r);
-    const uint4 vw = *reinterpret_cast<const uint4*>(vb + (uint64_t)t * 256 + 16 * r);
+    const uint4* kp = reinterpret_cast<const uint4*>(kb + (uint64_t)t * 256 + 16 * r);
+    const uint4* vp = reinterpret_cast<const uint4*>(vb + (uint64_t)t * 256 + 16 * r);
+    const uint4 kw = kStream ? load_nt(kp) : *kp;
+    const uint4 vw = kStream ? load_nt(vp) : *vp;
     d.k[0] = kw.x; d.k[1] = kw.y; d.k[2] = kw.z; d.k[3] = kw.w;
     d.v[0] = vw.x; d.v[1] = vw.y; d.v[2] = vw.z; d.v[3] = vw.w;
     d.ks = 1.0f;

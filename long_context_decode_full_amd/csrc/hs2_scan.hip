@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
     if (nsteps > 0) {
 #pragma unroll
       for (int u = 0; u < kPrefetch; ++u)
-        load_row<kFp8>(kb, vb, ksb, vsb, (uint32_t)wb + min((uint32_t)(u * 4 + rg), last), r, buf[u]);
+        load_row<kFp8, true>(kb, vb, ksb, vsb, (uint32_t)wb + min((uint32_t)(u * 4 + rg), last), r, buf[u]);
     }
     for (int base = 0; base < nsteps_pad; base += kPrefetch) {
 #pragma unroll
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
         // consume ring slot u, then refill it kPrefetch steps ahead (no register copy)
         const uint32_t rel = (uint32_t)((base + u) * 4 + rg);
         const float l = process_row<kFp8>(qp, buf[u], rel < span, a.scale_log2, ls);
-        load_row<kFp8>(kb, vb, ksb, vsb, (uint32_t)wb + min(rel + 4 * kPrefetch, last), r, buf[u]);
+        load_row<kFp8, true>(kb, vb, ksb, vsb, (uint32_t)wb + min(rel + 4 * kPrefetch, last), r, buf[u]);
         if (kMode == kDenseLogits) {
           if ((r & 1) == 0) mylog[(u * 4 + rg) * 8 + hown] = l;
         } else {

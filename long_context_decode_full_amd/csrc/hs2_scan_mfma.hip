@@ -118,14 +118,14 @@ __device__ __forceinline__ void load_step(StepBuf<kFp8>& s, const uint8_t* __res
       if constexpr (kFp8)
         s.k[t][q] = *reinterpret_cast<const uint2*>(kb + (uint64_t)row * 128 + 32 * q + 8 * grp);
       else
-        s.k[t][q] = *reinterpret_cast<const uint4*>(kb + (uint64_t)row * 256 + 64 * q + 16 * grp);
+        s.k[t][q] = load_nt(reinterpret_cast<const uint4*>(kb + (uint64_t)row * 256 + 64 * q + 16 * grp));
     }
   }
   if constexpr (kFp8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t row = (uint32_t)min(base + 8 * i + (lane >> 3), last);
-      s.v[i] = *reinterpret_cast<const uint4*>(vb + (uint64_t)row * 128 + 16 * (lane & 7));
+      s.v[i] = load_nt(reinterpret_cast<const uint4*>(vb + (uint64_t)row * 128 + 16 * (lane & 7)));
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -139,7 +139,7 @@ __device__ __forceinline__ void load_step(StepBuf<kFp8>& s, const uint8_t* __res
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t row = (uint32_t)min(base + 4 * i + grp, last);
-      s.v[i] = *reinterpret_cast<const uint4*>(vb + (uint64_t)row * 256 + 16 * w16);
+      s.v[i] = load_nt(reinterpret_cast<const uint4*>(vb + (uint64_t)row * 256 + 16 * w16));
     }
   }
 }
