@@ -23,7 +23,7 @@
 //        gets 4 rows of one dim per read).  Eight 16-dim blocks, two MFMAs each.
 // The K loads feed the MFMA directly (each load instruction covers 16 rows x 64
 // contiguous bytes); V rows are loaded whole (16 lanes per row) and stored to LDS.
-// Loads run one step ahead through a two-buffer ring.
+// Loads run one step ahead through a two-buffer ring, with the non-temporal hint.
 #include "hs2_rowops.h"
 
 namespace hs2 {
@@ -35,6 +35,7 @@ typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2v_t;
 
 constexpr int kMThreads = 256;
+constexpr int kMWaves = kMThreads / 64;
 constexpr int kStepRows = 32;
 constexpr float kMSlack = 8.0f;
 constexpr int kVRow = 272;                    // bytes per staged V row (256 + 16 pad)
@@ -154,7 +155,7 @@ template <bool kFp8>
 __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x8_t (&qf)[4], uint8_t* vt,
                                              int32_t base, int32_t w_begin, int32_t w_end, uint32_t cand_span,
                                              float scale_log2, int G, int grp, int w16, int lane,
-                                             uint16_t* myrec, uint32_t* shist, HeadState& hs) {
+                                             uint16_t* recs, uint32_t* shist, HeadState& hs) {
   // V tile -> LDS (row-major, padded rows)
   if constexpr (kFp8) {
 #pragma unroll
@@ -218,7 +219,7 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
       const uint32_t rel = (uint32_t)(row - w_begin);
       if (w16 == 0 && row < w_end) {
         const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)e);
-        myrec[rel] = rec;
+        recs[rel] = rec;
         if (rel < cand_span) atomicAdd(&shist[half_order_key(rec) >> kFastShift], 1u);
       }
     }
@@ -300,13 +301,14 @@ __global__ __launch_bounds__(kMThreads, 2) void scan_mfma_kernel(ScanArgs a) {
   const int64_t p_begin = (int64_t)split * a.split_len;
   int64_t p_end = p_begin + a.split_len;
   p_end = p_end < n ? p_end : n;
-  const int wave_len = a.split_len >> 2;
-  const int64_t wb64 = p_begin + (int64_t)wave * wave_len;
-  int64_t we64 = wb64 + wave_len;
-  we64 = we64 < p_end ? we64 : p_end;
-  const int32_t w_begin = (int32_t)wb64;   // rows < cap < 2^31
-  const int32_t w_end = (int32_t)(we64 > wb64 ? we64 : wb64);
-  const int nsteps = (w_end - w_begin + kStepRows - 1) / kStepRows;
+  // The 4 waves take turns over the split's 32-row steps (wave w: steps w, w+4, ...),
+  // so the workgroup reads K and V as two contiguous streams; a wave-per-quarter
+  // layout (8 streams per workgroup) measured ~3% slower on the million-token scan.
+  const int32_t w_begin = (int32_t)p_begin;   // rows < cap < 2^31
+  const int32_t w_end = (int32_t)(p_end > p_begin ? p_end : p_begin);
+  const int32_t first = w_begin + wave * kStepRows;
+  constexpr int kStride = kMWaves * kStepRows;
+  const int nsteps = w_end > first ? (w_end - first + kStride - 1) / kStride : 0;
 
   // Q^T fragments: head w16, dims 32q + 8grp .. +8
   bf16x8_t qf[4];
@@ -328,9 +330,8 @@ __global__ __launch_bounds__(kMThreads, 2) void scan_mfma_kernel(ScanArgs a) {
   int64_t w0 = n - a.window;
   w0 = w0 < 0 ? 0 : w0;
   const uint32_t span = (uint32_t)(w_end - w_begin);
-  uint32_t cand_span = w0 > wb64 ? (uint32_t)(w0 - wb64) : 0u;
+  uint32_t cand_span = w0 > p_begin ? (uint32_t)(w0 - p_begin) : 0u;
   cand_span = cand_span < span ? cand_span : span;
-  uint16_t* myrec = srec + wave * wave_len;
 
   for (int i = tid; i < kFastBins; i += kMThreads) shist[i] = 0u;
   if (split == 0) {   // the combine kernel sums every split's histogram into these words
@@ -348,17 +349,17 @@ __global__ __launch_bounds__(kMThreads, 2) void scan_mfma_kernel(ScanArgs a) {
   if (nsteps > 0) {
     const int32_t last = w_end - 1;
     StepBuf<kFp8> s0, s1;
-    load_step<kFp8>(s0, kb, vb, ksb, vsb, w_begin, last, grp, w16, lane);
+    load_step<kFp8>(s0, kb, vb, ksb, vsb, first, last, grp, w16, lane);
     for (int st = 0; st < nsteps; st += 2) {
       // straight-line ring: every load is issued (rows past the end re-read `last`)
-      const int32_t b0 = w_begin + st * kStepRows;
-      load_step<kFp8>(s1, kb, vb, ksb, vsb, b0 + kStepRows, last, grp, w16, lane);
-      process_step<kFp8>(s0, qf, vt, b0, w_begin, w_end, cand_span, a.scale_log2, a.G, grp, w16, lane, myrec,
+      const int32_t b0 = first + st * kStride;
+      load_step<kFp8>(s1, kb, vb, ksb, vsb, b0 + kStride, last, grp, w16, lane);
+      process_step<kFp8>(s0, qf, vt, b0, w_begin, w_end, cand_span, a.scale_log2, a.G, grp, w16, lane, srec,
                          shist, hs);
-      load_step<kFp8>(s0, kb, vb, ksb, vsb, b0 + 2 * kStepRows, last, grp, w16, lane);
+      load_step<kFp8>(s0, kb, vb, ksb, vsb, b0 + 2 * kStride, last, grp, w16, lane);
       // a step past the end (odd step count) has every row masked: no effect
-      process_step<kFp8>(s1, qf, vt, b0 + kStepRows, w_begin, w_end, cand_span, a.scale_log2, a.G, grp, w16,
-                         lane, myrec, shist, hs);
+      process_step<kFp8>(s1, qf, vt, b0 + kStride, w_begin, w_end, cand_span, a.scale_log2, a.G, grp, w16,
+                         lane, srec, shist, hs);
     }
   }
 
