@@ -160,6 +160,8 @@ def main():
     ap.add_argument("--select", default="token", choices=["token", "block"],
                     help="token selection (window 128 + top-k 1024) or the first-generation block "
                          "comparator (18 blocks of 64, no forced window)")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="fixed step shares in the context scan (bitwise reproducible, slower)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
@@ -181,11 +183,12 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": 5}), flush=True)
         return
-    from long_context_decode_full_amd import (HS2_TIMER_GATHER, HS2_TIMER_SCAN, hs2_timer_collect,
-                                              hs2_timer_enable)
+    from long_context_decode_full_amd import (HS2_TIMER_GATHER, HS2_TIMER_SCAN, hs2_set_deterministic,
+                                              hs2_timer_collect, hs2_timer_enable)
     from long_context_decode_full_amd import workloads as wl
     from long_context_decode_full_amd.runner import HybridBlockDevice
 
+    hs2_set_deterministic(args.deterministic)
     w = wl.standard_workloads()[args.workload]
     log(f"generating inputs: {w.name}")
     t0 = time.perf_counter()
@@ -264,6 +267,7 @@ def main():
                         + f", 1 full + {w.n_sparse_layers} sparse layers",
             "batch": w.batch, "ctx_tokens": ctx, "q_len": w.q_len,
             "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "kv_dtype": w.kv_dtype,
+            "deterministic": bool(args.deterministic),
         },
         "kv_gbps": achieved,
         "scan_us": scan_avg_s * 1e6,

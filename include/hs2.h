@@ -134,6 +134,15 @@ hs2_status hs2_sparse_attn(const hs2_attn_desc* desc,
 /* Static English text for a status; never NULL. */
 const char* hs2_status_string(hs2_status status);
 
+/* Reproducibility switch (process-wide, default off).  By default the waves of a
+ * context-scan workgroup share its steps through a counter, so the order in which
+ * a head's probabilities are summed into `out` varies between runs and `out` of
+ * hs2_full_attn_select can differ in the last bits of fp32 (idx never does: each
+ * position's selection score is computed on its own).  With `on` != 0, later calls
+ * give every wave a fixed share of the steps: bitwise reproducible output, ~3%
+ * slower scan.  Takes effect for calls made after it returns. */
+hs2_status hs2_set_deterministic(int on);
+
 /* Benchmark support.  `mask` selects the kernels timed from now on: HS2_TIMER_SCAN
  * (the context scan of hs2_full_attn_select), HS2_TIMER_GATHER (the gather kernel of
  * hs2_sparse_attn), both, or 0 for none.  Each timed call records two HIP events on

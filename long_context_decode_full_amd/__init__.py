@@ -20,7 +20,7 @@ __all__ = [
     "HS2_ERR_ALIGNMENT", "HS2_ERR_LAUNCH", "HS2_KV_BF16", "HS2_KV_FP8_E4M3FN",
     "HS2_SELECT_TOKEN", "HS2_SELECT_BLOCK", "Hs2AttnDesc", "Hs2Error", "make_desc",
     "hs2_validate", "hs2_workspace_size", "hs2_full_attn_select", "hs2_sparse_attn",
-    "hs2_status_string", "hs2_timer_enable", "hs2_timer_collect", "HS2_TIMER_SCAN",
+    "hs2_status_string", "hs2_set_deterministic", "hs2_timer_enable", "hs2_timer_collect", "HS2_TIMER_SCAN",
     "HS2_TIMER_GATHER", "library_path", "load_library",
     "EXPORTED_SYMBOLS",
 ]
@@ -37,8 +37,8 @@ HS2_SELECT_TOKEN = 0
 HS2_SELECT_BLOCK = 1
 
 EXPORTED_SYMBOLS = ("hs2_validate", "hs2_workspace_size", "hs2_full_attn_select",
-                    "hs2_sparse_attn", "hs2_status_string", "hs2_timer_enable",
-                    "hs2_timer_collect")
+                    "hs2_sparse_attn", "hs2_status_string", "hs2_set_deterministic",
+                    "hs2_timer_enable", "hs2_timer_collect")
 
 
 class Hs2AttnDesc(ctypes.Structure):
@@ -106,6 +106,8 @@ def load_library():
     lib.hs2_sparse_attn.restype = ctypes.c_int
     lib.hs2_status_string.argtypes = [ctypes.c_int]
     lib.hs2_status_string.restype = ctypes.c_char_p
+    lib.hs2_set_deterministic.argtypes = [ctypes.c_int]
+    lib.hs2_set_deterministic.restype = ctypes.c_int
     lib.hs2_timer_enable.argtypes = [ctypes.c_int]
     lib.hs2_timer_enable.restype = ctypes.c_int
     lib.hs2_timer_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32),
@@ -162,6 +164,11 @@ def hs2_sparse_attn(desc, q, k, v, k_scale, v_scale, ctx_len, idx, out, workspac
 
 def hs2_status_string(status: int) -> str:
     return load_library().hs2_status_string(int(status)).decode()
+
+
+def hs2_set_deterministic(on: bool) -> int:
+    """Process-wide: fixed step shares in the context scan (bitwise reproducible)."""
+    return load_library().hs2_set_deterministic(1 if on else 0)
 
 
 HS2_TIMER_SCAN = 1

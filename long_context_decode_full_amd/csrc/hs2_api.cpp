@@ -1,6 +1,7 @@
 // C-ABI host layer: descriptor validation, workspace layout, launch sequences.
 // Contract of every entry point: include/hs2.h.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -18,7 +19,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kScanTargetWorkgroups = 768;   // 3 per CU (3 waves/SIMD) on 256 CUs
-constexpr int kMfmaTargetWorkgroups = 512;   // matrix-core scan: 2 per CU
+constexpr int kMfmaTargetWorkgroups = 256;   // matrix-core scan: 1 per CU (8 waves)
 constexpr double kMaxLogitsBytes = 16.0 * (1 << 30);   // logits-path workspace budget
 constexpr int kMaxSplits = 2048;             // combine kernel keeps one weight per split in LDS
 constexpr int kSparseSplitLen = 64;          // index entries per sparse workgroup
@@ -114,7 +115,7 @@ Layout make_layout(const hs2_attn_desc* d) {
   L.n_split = (int32_t)ceil_div(d->max_ctx_len, split);
 
   // Record path: a split's records stay in LDS until it is done, which bounds the split.
-  // The matrix-core scan holds 2 workgroups per CU: one residency round of 512.  The
+  // The matrix-core scan holds 1 workgroup per CU: one residency round of 256.  The
   // chunk kernel (one workgroup per CU, 32 query tokens each) takes about 16 splits
   // of the longest context per (sequence, KV head).
   int64_t rsplit;
@@ -189,6 +190,7 @@ struct TimerRec {
   hipEvent_t a, b;
   int kind;   // 0 scan, 1 gather
 };
+std::atomic<int> g_fixed_steps{0};   // hs2_set_deterministic
 std::mutex g_timer_mu;
 int g_timer_mask = 0;   // HS2_TIMER_* bits
 std::vector<TimerRec> g_timer;
@@ -277,6 +279,7 @@ static ScanArgs scan_args(const hs2_attn_desc* d, const Layout& L, const void* q
   a.G = L.G;
   a.S = L.S;
   a.scale_log2 = d->sm_scale * 1.44269504088896340736f;
+  a.fixed_steps = g_fixed_steps.load(std::memory_order_relaxed);
   return a;
 }
 
@@ -490,6 +493,11 @@ HS2_API hs2_status hs2_sparse_attn(const hs2_attn_desc* desc, const void* q, con
   ca.Hq = desc->n_q_heads;
   ca.n_split = L.n_split_sp;
   if (launch_combine(ca, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+  return HS2_OK;
+}
+
+HS2_API hs2_status hs2_set_deterministic(int on) {
+  g_fixed_steps.store(on ? 1 : 0, std::memory_order_relaxed);
   return HS2_OK;
 }
 

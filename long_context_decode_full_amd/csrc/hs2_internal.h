@@ -73,6 +73,8 @@ struct ScanArgs {
   int32_t n_split;
   int32_t split_len;        // positions per split (dense: tokens, sparse: idx entries)
   float scale_log2;         // sm_scale * log2(e)
+  int32_t fixed_steps;      // matrix-core scan: 1 = fixed step share per wave (bitwise
+                            // reproducible), 0 = waves take steps from a shared counter
 };
 
 struct CombineArgs {

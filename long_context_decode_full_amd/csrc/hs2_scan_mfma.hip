@@ -34,7 +34,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2v_t;
 
-constexpr int kMThreads = 256;
+constexpr int kMThreads = 512;                // one workgroup per CU, 8 waves
 constexpr int kMWaves = kMThreads / 64;
 constexpr int kStepRows = 32;
 constexpr float kMSlack = 8.0f;
@@ -43,7 +43,7 @@ constexpr int kVTile = kStepRows * kVRow;     // per wave
 constexpr int kRecBytes = kMaxRecordSplit * 2;
 constexpr int kHistBytes = kFastBins * 4;
 constexpr int kMergeStride = kPartStride;     // floats per head in the wave merge area: m, z, -, -, o[128]
-constexpr int kMLds = kRecBytes + kHistBytes + 4 * kVTile;
+constexpr int kMLds = kRecBytes + kHistBytes + kMWaves * kVTile;
 static_assert(8 * kMergeStride * 4 <= kVTile, "a wave's merge record fits its V tile");
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
@@ -275,7 +275,7 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
 }
 
 template <bool kFp8>
-__global__ __launch_bounds__(kMThreads, 2) void scan_mfma_kernel(ScanArgs a) {
+__global__ __launch_bounds__(kMThreads, 1) void scan_mfma_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kMLds];
   uint16_t* srec = reinterpret_cast<uint16_t*>(lds);
   uint32_t* shist = reinterpret_cast<uint32_t*>(lds + kRecBytes);
@@ -301,14 +301,18 @@ __global__ __launch_bounds__(kMThreads, 2) void scan_mfma_kernel(ScanArgs a) {
   const int64_t p_begin = (int64_t)split * a.split_len;
   int64_t p_end = p_begin + a.split_len;
   p_end = p_end < n ? p_end : n;
-  // The 4 waves take turns over the split's 32-row steps (wave w: steps w, w+4, ...),
-  // so the workgroup reads K and V as two contiguous streams; a wave-per-quarter
-  // layout (8 streams per workgroup) measured ~3% slower on the million-token scan.
+  // The waves share the split's 32-row steps through an LDS counter: a wave takes
+  // the next step when it starts on one, so the workgroup reads K and V as two
+  // contiguous streams and every wave ends within a step of the others.  (Waves are
+  // not served equally: with a fixed share per wave, or two workgroups per CU, the
+  // younger ones took up to 1.4x longer and set the kernel's end.)  Which wave sums
+  // which step then varies from run to run, so the output can differ in the last
+  // bits; a.fixed_steps gives wave w the steps w, w+8, ... instead (reproducible,
+  // ~3% slower on the million-token scan).
   const int32_t w_begin = (int32_t)p_begin;   // rows < cap < 2^31
   const int32_t w_end = (int32_t)(p_end > p_begin ? p_end : p_begin);
-  const int32_t first = w_begin + wave * kStepRows;
-  constexpr int kStride = kMWaves * kStepRows;
-  const int nsteps = w_end > first ? (w_end - first + kStride - 1) / kStride : 0;
+  const int nsteps = (w_end - w_begin + kStepRows - 1) / kStepRows;
+  __shared__ int step_next;
 
   // Q^T fragments: head w16, dims 32q + 8grp .. +8
   bf16x8_t qf[4];
@@ -334,6 +338,7 @@ __global__ __launch_bounds__(kMThreads, 2) void scan_mfma_kernel(ScanArgs a) {
   cand_span = cand_span < span ? cand_span : span;
 
   for (int i = tid; i < kFastBins; i += kMThreads) shist[i] = 0u;
+  if (tid == 0) step_next = kMWaves;   // step w is wave w's first
   if (split == 0) {   // the combine kernel sums every split's histogram into these words
     uint32_t* hm = a.hist_merged + sel * kSelWords + kSelHist1Off;
     for (int i = tid; i < kFastBins; i += kMThreads) hm[i] = 0u;
@@ -348,22 +353,37 @@ __global__ __launch_bounds__(kMThreads, 2) void scan_mfma_kernel(ScanArgs a) {
 
   if (nsteps > 0) {
     const int32_t last = w_end - 1;
+    // next step for this wave (wave-uniform); steps taken by a wave increase, so once
+    // one is past the end every later one is too
+    const bool fixed = a.fixed_steps != 0;
+    int knext = wave + kMWaves;
+    auto take = [&]() -> int {
+      int k = knext;
+      knext += kMWaves;
+      if (!fixed && lane == 0)
+        k = __hip_atomic_fetch_add(&step_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return __builtin_amdgcn_readfirstlane(k);
+    };
     StepBuf<kFp8> s0, s1;
-    load_step<kFp8>(s0, kb, vb, ksb, vsb, first, last, grp, w16, lane);
-    for (int st = 0; st < nsteps; st += 2) {
-      // straight-line ring: every load is issued (rows past the end re-read `last`)
-      const int32_t b0 = first + st * kStride;
-      load_step<kFp8>(s1, kb, vb, ksb, vsb, b0 + kStride, last, grp, w16, lane);
-      process_step<kFp8>(s0, qf, vt, b0, w_begin, w_end, cand_span, a.scale_log2, a.G, grp, w16, lane, srec,
-                         shist, hs);
-      load_step<kFp8>(s0, kb, vb, ksb, vsb, b0 + 2 * kStride, last, grp, w16, lane);
-      // a step past the end (odd step count) has every row masked: no effect
-      process_step<kFp8>(s1, qf, vt, b0 + kStride, w_begin, w_end, cand_span, a.scale_log2, a.G, grp, w16,
-                         lane, srec, shist, hs);
+    int k0 = wave;
+    load_step<kFp8>(s0, kb, vb, ksb, vsb, w_begin + k0 * kStepRows, last, grp, w16, lane);
+    int k1 = take();
+    load_step<kFp8>(s1, kb, vb, ksb, vsb, w_begin + k1 * kStepRows, last, grp, w16, lane);
+    // two-buffer ring; every load is issued (rows past the end re-read `last`)
+    while (k0 < nsteps) {
+      process_step<kFp8>(s0, qf, vt, w_begin + k0 * kStepRows, w_begin, w_end, cand_span, a.scale_log2, a.G,
+                         grp, w16, lane, srec, shist, hs);
+      k0 = take();
+      load_step<kFp8>(s0, kb, vb, ksb, vsb, w_begin + k0 * kStepRows, last, grp, w16, lane);
+      if (k1 >= nsteps) break;
+      process_step<kFp8>(s1, qf, vt, w_begin + k1 * kStepRows, w_begin, w_end, cand_span, a.scale_log2, a.G,
+                         grp, w16, lane, srec, shist, hs);
+      k1 = take();
+      load_step<kFp8>(s1, kb, vb, ksb, vsb, w_begin + k1 * kStepRows, last, grp, w16, lane);
     }
   }
 
-  // ---- merge: the 4 row groups (shares of z), then the 4 waves through LDS
+  // ---- merge: the 4 row groups (shares of z), then the waves through LDS
   const float zt = sum_groups(hs.z);
   float* mrec = reinterpret_cast<float*>(vt);   // this wave's tile: its last reads are done
   if (w16 < 8) {
@@ -391,18 +411,18 @@ __global__ __launch_bounds__(kMThreads, 2) void scan_mfma_kernel(ScanArgs a) {
       ghist[i] = (shist[2 * i] & 0xFFFFu) | (shist[2 * i + 1] << 16);   // counts < 2^16
   }
 
-  // merge the 4 waves: thread -> (head, 4 dims)
-  {
+  // merge the waves: thread -> (head, 4 dims) for the first 256 threads
+  if (tid < 256) {
     const int h = tid >> 5;
     const int dd = (tid & 31) * 4;
     float Mw = kNegInf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < kMWaves; ++w)
       Mw = fmaxf(Mw, reinterpret_cast<const float*>(vt_all + w * kVTile)[h * kMergeStride]);
     float Z = 0.0f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kMWaves; ++w) {
       const float* mr = reinterpret_cast<const float*>(vt_all + w * kVTile) + h * kMergeStride;
       const float mw = mr[0];
       const float fw = (mw == kNegInf) ? 0.0f : fast_exp2(mw - Mw);
