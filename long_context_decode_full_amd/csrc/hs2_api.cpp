@@ -20,6 +20,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kScanTargetWorkgroups = 768;   // 3 per CU (3 waves/SIMD) on 256 CUs
 constexpr int kMfmaTargetWorkgroups = 256;   // matrix-core scan: 1 per CU (8 waves)
+constexpr int64_t kFusedSparseRows = 256;    // sparse layer: one workgroup per row from here
 constexpr double kMaxLogitsBytes = 16.0 * (1 << 30);   // logits-path workspace budget
 constexpr int kMaxSplits = 2048;             // combine kernel keeps one weight per split in LDS
 constexpr int kSparseSplitLen = 64;          // index entries per sparse workgroup
@@ -478,8 +479,21 @@ HS2_API hs2_status hs2_sparse_attn(const hs2_attn_desc* desc, const void* q, con
   sa.n_split = L.n_split_sp;
   sa.split_len = L.split_len_sp;
 
+  // With a row per CU or more (query chunks), one matrix-core workgroup per (query
+  // token, KV head) gathers the whole index row and writes the output: 2.1x faster on
+  // the 64-token chunks.  With fewer rows (decode) its 4-5 dependent steps per wave
+  // are latency-bound, and the split VALU gather + combine is faster.
+  // HS2_SPARSE_FUSED=1 / 0 forces either path.
+  const int64_t rows = (int64_t)desc->batch * desc->q_len * desc->n_kv_heads;
+  const int fused_env = env_int("HS2_SPARSE_FUSED", -1);
+  const bool fused = fused_env >= 0 ? fused_env != 0 : rows >= kFusedSparseRows;
   TimerRec rec;
   const bool timed = timer_begin(stream, 1, &rec);
+  if (fused) {
+    const hipError_t e = launch_gather_mfma(sa, out, fp8, desc->batch, stream);
+    if (timed) timer_end(stream, &rec);
+    return e == hipSuccess ? HS2_OK : HS2_ERR_LAUNCH;
+  }
   hipError_t e = launch_scan_sparse(sa, fp8, desc->batch, stream);
   if (timed) timer_end(stream, &rec);
   if (e != hipSuccess) return HS2_ERR_LAUNCH;

@@ -145,17 +145,62 @@ __device__ __forceinline__ void load_step(StepBuf<kFp8>& s, const uint8_t* __res
   }
 }
 
+// One sparse-layer step's loads: the rows named by index-row entries e0 .. e0+31
+// (srow: row per entry, -1 for a skipped entry, which loads row 0 and is masked).
+// Ordinary loads: the next sparse layer gathers the same rows.
+template <bool kFp8>
+__device__ __forceinline__ void load_step_gather(StepBuf<kFp8>& s, const uint8_t* __restrict__ kb,
+                                                 const uint8_t* __restrict__ vb, const float* __restrict__ ksb,
+                                                 const float* __restrict__ vsb, const int32_t* srow, int e0,
+                                                 int grp, int w16, int lane) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t row = (uint32_t)max(srow[e0 + 16 * t + w16], 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (kFp8)
+        s.k[t][q] = *reinterpret_cast<const uint2*>(kb + (uint64_t)row * 128 + 32 * q + 8 * grp);
+      else
+        s.k[t][q] = *reinterpret_cast<const uint4*>(kb + (uint64_t)row * 256 + 64 * q + 16 * grp);
+    }
+  }
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t row = (uint32_t)max(srow[e0 + 8 * i + (lane >> 3)], 0);
+      s.v[i] = *reinterpret_cast<const uint4*>(vb + (uint64_t)row * 128 + 16 * (lane & 7));
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t row = (uint32_t)max(srow[e0 + 16 * t + 4 * grp + v], 0);
+        s.ks[t][v] = ksb[row];
+        s.vs[t][v] = vsb[row];
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t row = (uint32_t)max(srow[e0 + 4 * i + grp], 0);
+      s.v[i] = *reinterpret_cast<const uint4*>(vb + (uint64_t)row * 256 + 16 * w16);
+    }
+  }
+}
+
 struct HeadState {
   f32x4_t o[8];   // o[b][v]: dim 16b + 4grp + v of head w16
   float m;        // running maximum of head w16 (log2 domain; equal in the 4 groups)
   float z;        // this lane's share of the softmax denominator
 };
 
-template <bool kFp8>
+// kGather: a sparse-layer step; `base` is the step's first index-row entry and srow
+// holds each entry's row (-1: skipped), so no records are formed.
+template <bool kFp8, bool kGather = false>
 __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x8_t (&qf)[4], uint8_t* vt,
                                              int32_t base, int32_t w_begin, int32_t w_end, uint32_t cand_span,
                                              float scale_log2, int G, int grp, int w16, int lane,
-                                             uint16_t* recs, uint32_t* shist, HeadState& hs) {
+                                             uint16_t* recs, uint32_t* shist, HeadState& hs,
+                                             const int32_t* srow = nullptr) {
   // V tile -> LDS (row-major, padded rows)
   if constexpr (kFp8) {
 #pragma unroll
@@ -201,11 +246,15 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
       const int32_t row = base + 16 * t + 4 * grp + v;
       float x = d[t][v] * scale_log2;
       if constexpr (kFp8) x *= s.ks[t][v];
-      l[t][v] = row < w_end ? x : kNegInf;
+      bool live;
+      if constexpr (kGather) live = srow[row] >= 0;
+      else live = row < w_end;
+      l[t][v] = live ? x : kNegInf;
       mx = fmaxf(mx, l[t][v]);
     }
 
   // bound records: e = log2 sum over the group's heads of 2^l
+  if constexpr (!kGather)
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -444,6 +493,131 @@ __global__ __launch_bounds__(kMThreads, 1) void scan_mfma_kernel(ScanArgs a) {
   }
 }
 
+// ---- Sparse Attention layer (HySparse2 article, section 02 "KV Reuse": the sparse
+// layers attend with their own queries over the rows of the shared cache that the
+// full layer's index set names; section 03: window and global rows share one
+// softmax).  One workgroup per (query token, KV head): its 8 waves gather the index
+// row's entries 32 at a time with the step code of the scan (wave w takes steps w,
+// w+8, ...: a fixed share, so the output is bitwise reproducible), merge through LDS
+// and write the normalised output, so no split combine follows.
+constexpr int kGMaxS = 4096;   // index row length bound (checked on the host)
+constexpr int kGLds = kMWaves * kVTile + kGMaxS * 4;
+
+template <bool kFp8>
+__global__ __launch_bounds__(kMThreads, 1) void gather_mfma_kernel(ScanArgs a, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kGLds];
+  uint8_t* vt_all = lds;
+  int32_t* srow = reinterpret_cast<int32_t*>(lds + kMWaves * kVTile);
+
+  const int g = blockIdx.y;
+  const int bj = blockIdx.z;
+  const int b = bj / a.Lq;
+  const int j = bj - b * a.Lq;
+  const int64_t sel = (int64_t)bj * a.Hkv + g;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int grp = lane >> 4;
+  const int w16 = lane & 15;
+  uint8_t* vt = vt_all + wave * kVTile;
+
+  int64_t ctx = a.ctx_len[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.ctx_max ? a.ctx_max : ctx);
+  int64_t n = ctx - a.Lq + j + 1;
+  n = n < 0 ? 0 : n;
+  const int nsteps = (a.S + kStepRows - 1) / kStepRows;
+
+  // the index row, with entries that name no visible row turned into -1
+  const int32_t* irow = a.idx + sel * a.S;
+  for (int e = tid; e < nsteps * kStepRows; e += kMThreads) {
+    const int32_t t = e < a.S ? irow[e] : -1;
+    srow[e] = (t >= 0 && t < n) ? t : -1;
+  }
+  bf16x8_t qf[4];
+  {
+    const uint16_t* qh = a.q + ((int64_t)bj * a.Hq + (int64_t)g * a.G + w16) * kHeadDim + 8 * grp;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      qf[q] = as_bf16x8(w16 < a.G ? *reinterpret_cast<const uint4*>(qh + 32 * q) : make_uint4(0u, 0u, 0u, 0u));
+  }
+  const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
+  const int rowbytes = kFp8 ? 128 : 256;
+  const uint8_t* kb = a.k + head_row0 * rowbytes;
+  const uint8_t* vb = a.v + head_row0 * rowbytes;
+  const float* ksb = kFp8 ? a.k_scale + head_row0 : nullptr;
+  const float* vsb = kFp8 ? a.v_scale + head_row0 : nullptr;
+  __syncthreads();
+
+  HeadState hs;
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) hs.o[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  hs.m = kNegInf;
+  hs.z = 0.0f;
+
+  if (wave < nsteps) {
+    // two-buffer ring over steps wave, wave+8, ...; loads past the last step re-read it
+    const int klast = nsteps - 1;
+    StepBuf<kFp8> s0, s1;
+    int k0 = wave, k1 = wave + kMWaves;
+    load_step_gather<kFp8>(s0, kb, vb, ksb, vsb, srow, k0 * kStepRows, grp, w16, lane);
+    load_step_gather<kFp8>(s1, kb, vb, ksb, vsb, srow, min(k1, klast) * kStepRows, grp, w16, lane);
+    while (k0 < nsteps) {
+      process_step<kFp8, true>(s0, qf, vt, k0 * kStepRows, 0, 0, 0u, a.scale_log2, a.G, grp, w16, lane, nullptr,
+                               nullptr, hs, srow);
+      k0 += 2 * kMWaves;
+      load_step_gather<kFp8>(s0, kb, vb, ksb, vsb, srow, min(k0, klast) * kStepRows, grp, w16, lane);
+      if (k1 >= nsteps) break;
+      process_step<kFp8, true>(s1, qf, vt, k1 * kStepRows, 0, 0, 0u, a.scale_log2, a.G, grp, w16, lane, nullptr,
+                               nullptr, hs, srow);
+      k1 += 2 * kMWaves;
+      load_step_gather<kFp8>(s1, kb, vb, ksb, vsb, srow, min(k1, klast) * kStepRows, grp, w16, lane);
+    }
+  }
+
+  // merge the row groups, then the waves through LDS; out = o / Z (0 when no entry is live)
+  const float zt = sum_groups(hs.z);
+  float* mrec = reinterpret_cast<float*>(vt);   // this wave's tile: its last reads are done
+  if (w16 < 8) {
+    float* mr = mrec + w16 * kMergeStride;
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb)
+      *reinterpret_cast<float4*>(mr + 4 + 16 * bb + 4 * grp) =
+          make_float4(hs.o[bb][0], hs.o[bb][1], hs.o[bb][2], hs.o[bb][3]);
+    if (grp == 0) {
+      mr[0] = hs.m;
+      mr[1] = zt;
+    }
+  }
+  __syncthreads();
+  if (tid < 256) {
+    const int h = tid >> 5;
+    const int dd = (tid & 31) * 4;
+    float Mw = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kMWaves; ++w)
+      Mw = fmaxf(Mw, reinterpret_cast<const float*>(vt_all + w * kVTile)[h * kMergeStride]);
+    float Z = 0.0f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < kMWaves; ++w) {
+      const float* mr = reinterpret_cast<const float*>(vt_all + w * kVTile) + h * kMergeStride;
+      const float mw = mr[0];
+      const float fw = (mw == kNegInf) ? 0.0f : fast_exp2(mw - Mw);
+      Z += fw * mr[1];
+      const float4 ov = *reinterpret_cast<const float4*>(mr + 4 + dd);
+      acc.x += fw * ov.x;
+      acc.y += fw * ov.y;
+      acc.z += fw * ov.z;
+      acc.w += fw * ov.w;
+    }
+    if (h < a.G) {
+      const float iz = Z > 0.0f ? 1.0f / Z : 0.0f;
+      float* op = out + ((int64_t)bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim + dd;
+      *reinterpret_cast<float4*>(op) = make_float4(acc.x * iz, acc.y * iz, acc.z * iz, acc.w * iz);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_scan_mfma(const ScanArgs& a, bool fp8, int B, hipStream_t st) {
@@ -452,6 +626,15 @@ hipError_t launch_scan_mfma(const ScanArgs& a, bool fp8, int B, hipStream_t st) 
     hipLaunchKernelGGL((scan_mfma_kernel<true>), grid, dim3(kMThreads), 0, st, a);
   else
     hipLaunchKernelGGL((scan_mfma_kernel<false>), grid, dim3(kMThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool fp8, int B, hipStream_t st) {
+  dim3 grid(1, a.Hkv, B * a.Lq);
+  if (fp8)
+    hipLaunchKernelGGL((gather_mfma_kernel<true>), grid, dim3(kMThreads), 0, st, a, out);
+  else
+    hipLaunchKernelGGL((gather_mfma_kernel<false>), grid, dim3(kMThreads), 0, st, a, out);
   return hipGetLastError();
 }
 

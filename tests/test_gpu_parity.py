@@ -121,6 +121,23 @@ def test_record_path_on_valu_scan(monkeypatch, wname):
     run_and_compare(w, f"{wname}-valu-scan")
 
 
+@pytest.mark.parametrize("wname", ["tiny", "fp8_256k", "batched"])
+def test_sparse_fused_gather_on_decode(monkeypatch, wname):
+    """HS2_SPARSE_FUSED=1: decode shapes (few rows, normally the split gather) on the
+    one-workgroup-per-row matrix-core gather; same parity bar."""
+    monkeypatch.setenv("HS2_SPARSE_FUSED", "1")
+    w = wl.standard_workloads()[wname]
+    run_and_compare(w, f"{wname}-sparse-fused")
+
+
+def test_chunk_sparse_split_path(monkeypatch):
+    """HS2_SPARSE_FUSED=0: the chunk configuration's sparse layers on the split
+    gather + combine; sampled tokens."""
+    monkeypatch.setenv("HS2_SPARSE_FUSED", "0")
+    w = wl.standard_workloads()["chunk"]
+    run_and_compare(w, "chunk-sparse-split", tokens=[(3, 0), (9, 63), (15, 17)])
+
+
 def test_million_token_decode():
     w = wl.standard_workloads()["million"]
     run_and_compare(w, "million")
@@ -178,8 +195,19 @@ def test_chunk_split_invariant(monkeypatch):
 
 
 # ------------------------------------------------------------------ edges
+@pytest.fixture(params=["auto", "fused"])
+def sparse_path(request, monkeypatch):
+    """Runs a test with the default sparse-layer routing and again with every sparse
+    layer on the one-workgroup-per-row gather."""
+    if request.param == "fused":
+        monkeypatch.setenv("HS2_SPARSE_FUSED", "1")
+    else:
+        monkeypatch.delenv("HS2_SPARSE_FUSED", raising=False)
+    return request.param
+
+
 @pytest.mark.parametrize("ctx", [1, 127, 128, 129, 1151, 1152, 1153, 5000])
-def test_short_and_boundary_contexts(ctx):
+def test_short_and_boundary_contexts(ctx, sparse_path):
     w = wl.Workload(f"ctx{ctx}", 1, 1, 16, 2, ctx_lens=[ctx], n_needles=min(4, ctx), seed=3000 + ctx)
     got, ref = run_and_compare(w, f"ctx{ctx}")
     if ctx <= 1152:   # every position selected; sparse layers equal dense attention
@@ -188,7 +216,7 @@ def test_short_and_boundary_contexts(ctx):
 
 
 @pytest.mark.parametrize("with_probs", [False, True])
-def test_ragged_batch_with_poisoned_tail(with_probs):
+def test_ragged_batch_with_poisoned_tail(with_probs, sparse_path):
     """Rows past ctx_len hold NaN; they must never be read.  Capacity > every length."""
     w = wl.Workload("ragged", 4, 1, 16, 2, ctx_lens=[3000, 1, 1300, 7777], n_needles=8,
                     capacity=8192, poison_tail=True, seed=3100)
@@ -196,7 +224,7 @@ def test_ragged_batch_with_poisoned_tail(with_probs):
 
 
 @pytest.mark.parametrize("with_probs", [False, True])
-def test_ragged_fp8_with_poisoned_tail(with_probs):
+def test_ragged_fp8_with_poisoned_tail(with_probs, sparse_path):
     w = wl.Workload("ragged fp8", 3, 1, 32, 4, ctx_lens=[4100, 200, 9000], n_needles=8,
                     kv_dtype="fp8", capacity=9216, poison_tail=True, seed=3150)
     run_and_compare(w, "ragged-fp8", with_probs=with_probs)
@@ -268,7 +296,7 @@ def test_block_baseline_chunk_kernel(lq, ctx, bs, nb):
     run_and_compare(w, f"block-chunk-lq{lq}", mode="block", block_size=bs, n_blocks=nb, tokens=toks)
 
 
-def test_rows_with_no_visible_position():
+def test_rows_with_no_visible_position(sparse_path):
     """ctx_len < Lq leaves the first query tokens with nothing visible: out = 0, idx = -1."""
     w = wl.Workload("empty rows", 2, 4, 16, 2, ctx_lens=[6, 3000], seed=3800)
     from long_context_decode_full_amd.runner import HybridBlockDevice
