@@ -21,6 +21,7 @@ constexpr size_t kAlign = 256;
 constexpr int kScanTargetWorkgroups = 768;   // 3 per CU (3 waves/SIMD) on 256 CUs
 constexpr int kMfmaTargetWorkgroups = 256;   // matrix-core scan: 1 per CU (8 waves)
 constexpr int64_t kFusedSparseRows = 256;    // sparse layer: one workgroup per row from here
+constexpr int kCandTargetWorkgroups = 4096;  // candidate stage: workgroups over all rows
 constexpr double kMaxLogitsBytes = 16.0 * (1 << 30);   // logits-path workspace budget
 constexpr int kMaxSplits = 2048;             // combine kernel keeps one weight per split in LDS
 constexpr int kSparseSplitLen = 64;          // index entries per sparse workgroup
@@ -409,6 +410,10 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
     fa.scale_log2 = sa.scale_log2;
     fa.n_chunks = L.n_cchunks;
     fa.chunk_len = L.cand_chunk_len;
+    // workgroups per row: all chunks of a row while rows are few (decode), fewer once
+    // there are many rows, so short rows do not launch mostly empty workgroups
+    const int64_t per_row = ceil_div(env_int("HS2_CAND_WGS_TOTAL", kCandTargetWorkgroups), L.n_sel);
+    fa.cand_wgs = (int32_t)std::max<int64_t>(1, std::min<int64_t>(L.n_cchunks, per_row));
     fa.n_sel = (int32_t)L.n_sel;
     fa.Lq = desc->q_len;
     fa.Hq = desc->n_q_heads;

@@ -131,7 +131,8 @@ struct FastSelArgs {
   int64_t cap;
   float scale_log2;
   int32_t n_chunks;
-  int32_t chunk_len;        // positions per candidate workgroup (power of two, 2048..16384)
+  int32_t chunk_len;        // positions per candidate chunk (power of two, 2048..16384)
+  int32_t cand_wgs;         // candidate workgroups per row (each takes every cand_wgs-th chunk)
   int32_t n_sel, Lq, Hq, Hkv, G;
   int32_t window, topk, S;
 };

@@ -125,8 +125,11 @@ __device__ __forceinline__ int32_t key_pos(uint64_t key) {
 }
 
 // ------------------------------------------------------------------ candidates + exact re-score
-// One workgroup per (row, chunk of chunk_len positions).  The threshold bin of the
-// k-th record gives two tests per position (records are bounds, see above):
+// Work unit: one (row, chunk of chunk_len positions); a workgroup takes the chunks
+// blockIdx.x, blockIdx.x + gridDim.x, ... of row blockIdx.y (the grid is sized so
+// that rows of a long context do not leave most workgroups of short rows empty).
+// The threshold bin of the k-th record gives two tests per position (records are
+// bounds, see above):
 //   candidate: its upper bound reaches the lower bound of the k-th score;
 //   certain:   its lower bound exceeds the upper bound of the k-th score (built from
 //              the bin's upper edge), so it is selected whatever the exact scores are.
@@ -134,7 +137,6 @@ __device__ __forceinline__ int32_t key_pos(uint64_t key) {
 // candidates re-read their key rows.  Keys stay in position order per chunk.
 template <bool kFp8, int R>   // R = records per thread = chunk_len / 256 (8..64)
 __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
-  const int chunk = blockIdx.x;
   const int64_t sel = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -143,15 +145,13 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   if (rg.w0 <= a.topk || a.topk == 0) return;
   constexpr int clen = R * kThreads;
   constexpr int nv = R / 8;       // 16-byte loads per thread
-  const int64_t c0 = (int64_t)chunk * clen;
-  if (c0 >= rg.w0) {
-    if (tid == 0) a.cand_count[sel * a.n_chunks + chunk] = 0;
-    return;
-  }
+  // chunks at or past the first window position hold no candidate (and are not read)
+  if ((int64_t)blockIdx.x * clen >= rg.w0) return;
 
-  __shared__ uint16_t cpos[kCandChunkLen];    // chunk-relative positions of the candidates
-  __shared__ uint16_t ulist[kCandChunkLen];   // indices into cpos of the uncertain ones
+  __shared__ uint16_t cpos[clen];    // chunk-relative positions of the candidates
+  __shared__ uint16_t ulist[clen];   // indices into cpos of the uncertain ones
   __shared__ uint32_t total_s;
+  __shared__ uint32_t wscan[kThreads / 64];
   float Mh[8], iz[8];
   load_mz(a, sel, Mh, iz);
   const int64_t bj = sel / a.Hkv;
@@ -162,27 +162,8 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   const int hown = head_of(r);
   uint32_t qp[8][4];   // issued early: its latency overlaps the threshold and the filter
   load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);
-
   const uint16_t* rrow = a.records + sel * a.rec_stride;
-  // Each thread owns R consecutive positions (one batch of 16-byte loads); a
-  // block-wide exclusive scan of the per-thread counts keeps position order.
-  const int64_t t0 = c0 + (int64_t)tid * R;
-  uint32_t words[R / 2];
-  if (t0 + R <= rg.w0) {
-#pragma unroll
-    for (int v = 0; v < nv; ++v) {
-      const uint4 x = *reinterpret_cast<const uint4*>(rrow + t0 + 8 * v);
-      words[4 * v + 0] = x.x; words[4 * v + 1] = x.y; words[4 * v + 2] = x.z; words[4 * v + 3] = x.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < R / 2; ++i) {
-      const int64_t t = t0 + 2 * i;
-      const uint32_t lo = t < rg.w0 ? (uint32_t)rrow[t] : 0u;
-      const uint32_t hi = t + 1 < rg.w0 ? (uint32_t)rrow[t + 1] : 0u;
-      words[i] = lo | (hi << 16);
-    }
-  }
+
   // threshold: bin of the k-th largest record key in the merged histogram
   uint32_t tb, above;
   block_threshold<kThreads, kFastBins / kThreads>(sel_block(a, sel) + kSelHist1Off, kFastBins,
@@ -202,84 +183,106 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   const float thr = half_bits_to_float(ebits) - half_ulp(ebits) - (lwmax - lwmin) - 2.0f * kBoundSlack;
   // certain    <=>  e - u(e) + log2 min w  >   e_hi + u(e_hi) + log2 max w  (with slack)
   const float thr_in = half_bits_to_float(ebits_hi) + half_ulp(ebits_hi) + (lwmax - lwmin) + 2.0f * kBoundSlack;
-
   // The certain test pays off where candidates are dense: rows whose candidate range
   // is short next to top-k (row-uniform); long rows have a few per workgroup.
   const bool use_cert = rg.w0 < (int64_t)a.topk * 64;
-  uint64_t hitmask = 0ull, certmask = 0ull;
-  if (use_cert) {
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-      const float e = half_bits_to_float(rb), u = half_ulp(rb);
-      const bool hit = t0 + i < rg.w0 && e + u >= thr;
-      hitmask |= (uint64_t)hit << i;
-      certmask |= (uint64_t)(hit && e - u > thr_in) << i;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-      hitmask |= (uint64_t)(t0 + i < rg.w0 && half_bits_to_float(rb) + half_ulp(rb) >= thr) << i;
-    }
-  }
-  const uint64_t uncmask = hitmask & ~certmask;
-  // block exclusive scan of (hits, uncertain hits), packed in one word (each < 2^16)
-  const uint32_t mine = (uint32_t)__builtin_popcountll(hitmask) | ((uint32_t)__builtin_popcountll(uncmask) << 16);
-  __shared__ uint32_t wscan[kThreads / 64];
-  const uint32_t x = wave_prefix_incl(mine);
-  if (lane == 63) wscan[wave] = x;
-  __syncthreads();
-  uint32_t before = x - mine;
-  for (int w = 0; w < wave; ++w) before += wscan[w];
-  if (tid == kThreads - 1) total_s = before + mine;
-  const int64_t slot0 = (sel * a.n_chunks + chunk) * (int64_t)clen;
-  uint32_t ih = before & 0xFFFFu, iu = before >> 16;
-  uint64_t hm = hitmask;
-  while (hm) {
-    const int i = __builtin_ctzll(hm);
-    hm &= hm - 1;
-    cpos[ih] = (uint16_t)(t0 + i - c0);
-    if ((uncmask >> i) & 1ull)
-      ulist[iu++] = (uint16_t)ih;
-    else
-      a.cand_keys[slot0 + ih] = cand_key(0x7F800000u, (int32_t)(t0 + i));   // certainly selected
-    ++ih;
-  }
-  __syncthreads();
-  const int cnt = (int)(total_s & 0xFFFFu);   // candidates
-  const int unc = (int)(total_s >> 16);       // of which uncertain
-  if (tid == 0) a.cand_count[sel * a.n_chunks + chunk] = cnt;
-  if (unc == 0) return;
 
-  // exact re-score: 4 rows per wave step, the scan's lane layout and arithmetic
   const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
   const uint8_t* kb = a.k + head_row0 * (kFp8 ? 128 : 256);
   const float* ksb = kFp8 ? a.k_scale + head_row0 : nullptr;
   const float Mown = Mh[hown];
   const float izown = iz[hown];
-  // Batches of kRescoreBatch wave steps: all their key loads are issued before the
-  // first row is scored, so a long candidate list does not wait on one load per step.
-  constexpr int kRescoreBatch = 4;
-  for (int i0 = wave * 4; i0 < unc; i0 += 16 * kRescoreBatch) {
-    RowData d[kRescoreBatch];
-    int32_t tpos[kRescoreBatch];
-    int tidx[kRescoreBatch];
+
+  for (int chunk = blockIdx.x; (int64_t)chunk * clen < rg.w0; chunk += gridDim.x) {
+    const int64_t c0 = (int64_t)chunk * clen;
+    // Each thread owns R consecutive positions (one batch of 16-byte loads); a
+    // block-wide exclusive scan of the per-thread counts keeps position order.
+    const int64_t t0 = c0 + (int64_t)tid * R;
+    uint32_t words[R / 2];
+    if (t0 + R <= rg.w0) {
 #pragma unroll
-    for (int u = 0; u < kRescoreBatch; ++u) {
-      const int i = i0 + 16 * u + rgrp;
-      // past the end: re-read the batch's first row (valid), the result is dropped
-      tidx[u] = ulist[i < unc ? i : i0];
-      tpos[u] = (int32_t)(c0 + cpos[tidx[u]]);
-      load_key<kFp8>(kb, ksb, (uint32_t)tpos[u], r, d[u]);
+      for (int v = 0; v < nv; ++v) {
+        const uint4 x = *reinterpret_cast<const uint4*>(rrow + t0 + 8 * v);
+        words[4 * v + 0] = x.x; words[4 * v + 1] = x.y; words[4 * v + 2] = x.z; words[4 * v + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < R / 2; ++i) {
+        const int64_t t = t0 + 2 * i;
+        const uint32_t lo = t < rg.w0 ? (uint32_t)rrow[t] : 0u;
+        const uint32_t hi = t + 1 < rg.w0 ? (uint32_t)rrow[t + 1] : 0u;
+        words[i] = lo | (hi << 16);
+      }
     }
+    uint64_t hitmask = 0ull, certmask = 0ull;
+    if (use_cert) {
 #pragma unroll
-    for (int u = 0; u < kRescoreBatch; ++u) {
-      const int i = i0 + 16 * u + rgrp;
-      const float l = row_logit<kFp8>(qp, d[u], a.scale_log2);
-      const float part = ((r & 1) == 0 && hown < a.G) ? fast_exp2(l - Mown) * izown : 0.0f;
-      const float s = rowgroup_sum16(part);
-      if (i < unc && r == 0) a.cand_keys[slot0 + tidx[u]] = cand_key(__float_as_uint(s), tpos[u]);
+      for (int i = 0; i < R; ++i) {
+        const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        const float e = half_bits_to_float(rb), u = half_ulp(rb);
+        const bool hit = t0 + i < rg.w0 && e + u >= thr;
+        hitmask |= (uint64_t)hit << i;
+        certmask |= (uint64_t)(hit && e - u > thr_in) << i;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        hitmask |= (uint64_t)(t0 + i < rg.w0 && half_bits_to_float(rb) + half_ulp(rb) >= thr) << i;
+      }
+    }
+    const uint64_t uncmask = hitmask & ~certmask;
+    // block exclusive scan of (hits, uncertain hits), packed in one word (each < 2^16)
+    const uint32_t mine = (uint32_t)__builtin_popcountll(hitmask) | ((uint32_t)__builtin_popcountll(uncmask) << 16);
+    const uint32_t x = wave_prefix_incl(mine);
+    __syncthreads();   // the previous chunk is done with wscan, cpos and ulist
+    if (lane == 63) wscan[wave] = x;
+    __syncthreads();
+    uint32_t before = x - mine;
+    for (int w = 0; w < wave; ++w) before += wscan[w];
+    if (tid == kThreads - 1) total_s = before + mine;
+    const int64_t slot0 = (sel * a.n_chunks + chunk) * (int64_t)clen;
+    uint32_t ih = before & 0xFFFFu, iu = before >> 16;
+    uint64_t hm = hitmask;
+    while (hm) {
+      const int i = __builtin_ctzll(hm);
+      hm &= hm - 1;
+      cpos[ih] = (uint16_t)(t0 + i - c0);
+      if ((uncmask >> i) & 1ull)
+        ulist[iu++] = (uint16_t)ih;
+      else
+        a.cand_keys[slot0 + ih] = cand_key(0x7F800000u, (int32_t)(t0 + i));   // certainly selected
+      ++ih;
+    }
+    __syncthreads();
+    const int cnt = (int)(total_s & 0xFFFFu);   // candidates
+    const int unc = (int)(total_s >> 16);       // of which uncertain
+    if (tid == 0) a.cand_count[sel * a.n_chunks + chunk] = cnt;
+
+    // exact re-score: 4 rows per wave step, the scan's lane layout and arithmetic.
+    // Batches of kRescoreBatch wave steps: all their key loads are issued before the
+    // first row is scored, so a long candidate list does not wait on one load per step.
+    constexpr int kRescoreBatch = 4;
+    for (int i0 = wave * 4; i0 < unc; i0 += 16 * kRescoreBatch) {
+      RowData d[kRescoreBatch];
+      int32_t tpos[kRescoreBatch];
+      int tidx[kRescoreBatch];
+#pragma unroll
+      for (int u = 0; u < kRescoreBatch; ++u) {
+        const int i = i0 + 16 * u + rgrp;
+        // past the end: re-read the batch's first row (valid), the result is dropped
+        tidx[u] = ulist[i < unc ? i : i0];
+        tpos[u] = (int32_t)(c0 + cpos[tidx[u]]);
+        load_key<kFp8>(kb, ksb, (uint32_t)tpos[u], r, d[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kRescoreBatch; ++u) {
+        const int i = i0 + 16 * u + rgrp;
+        const float l = row_logit<kFp8>(qp, d[u], a.scale_log2);
+        const float part = ((r & 1) == 0 && hown < a.G) ? fast_exp2(l - Mown) * izown : 0.0f;
+        const float s = rowgroup_sum16(part);
+        if (i < unc && r == 0) a.cand_keys[slot0 + tidx[u]] = cand_key(__float_as_uint(s), tpos[u]);
+      }
     }
   }
 }
@@ -548,7 +551,7 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
 
 template <bool kFp8>
 void launch_candidates_r(const FastSelArgs& a, hipStream_t st) {
-  const dim3 grid(a.n_chunks, a.n_sel);
+  const dim3 grid(a.cand_wgs, a.n_sel);
   switch (a.chunk_len / kThreads) {
     case 8: hipLaunchKernelGGL((candidate_kernel<kFp8, 8>), grid, dim3(kThreads), 0, st, a); break;
     case 16: hipLaunchKernelGGL((candidate_kernel<kFp8, 16>), grid, dim3(kThreads), 0, st, a); break;
