@@ -54,7 +54,7 @@ int env_int(const char* name, int dflt) {
   const char* v = std::getenv(name);
   if (v == nullptr || *v == '\0') return dflt;
   const int x = std::atoi(v);
-  return x > 0 ? x : dflt;
+  return x >= 0 ? x : dflt;   // 0 is a value (switches); sizes are clamped where used
 }
 
 hs2_status validate_desc(const hs2_attn_desc* d) {
@@ -143,7 +143,7 @@ Layout make_layout(const hs2_attn_desc* d) {
               L.rec_n_split <= kMaxSplits;
 
   int64_t sp = env_int("HS2_SPARSE_SPLIT_LEN", kSparseSplitLen);
-  sp = ceil_div(sp, 32) * 32;
+  sp = std::max<int64_t>(ceil_div(sp, 32) * 32, 32);
   while (ceil_div(L.S, sp) > kMaxSplits) sp *= 2;
   L.split_len_sp = (int32_t)sp;
   L.n_split_sp = (int32_t)ceil_div(L.S, sp);
@@ -193,6 +193,7 @@ struct TimerRec {
   int kind;   // 0 scan, 1 gather
 };
 std::atomic<int> g_fixed_steps{0};   // hs2_set_deterministic
+
 std::mutex g_timer_mu;
 int g_timer_mask = 0;   // HS2_TIMER_* bits
 std::vector<TimerRec> g_timer;

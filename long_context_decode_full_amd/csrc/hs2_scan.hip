@@ -113,6 +113,40 @@ __device__ __forceinline__ float process_row(const uint32_t (&qp)[8][4], const R
   return l;
 }
 
+// Online-softmax fold of the split partials of one (selection, head) for the 4
+// output dims 4dq .. 4dq+3: running maximum, denominator and weighted sum.
+__device__ __forceinline__ void fold_splits(const float* base, int64_t split_stride, int n_split, int dq,
+                                            float& m_loc, float& z_loc, float4& o) {
+  m_loc = kNegInf;
+  z_loc = 0.0f;
+  o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < n_split; s0 += 4) {
+    float ms[4], zs[4];
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = min(s0 + u, n_split - 1);
+      const float* ps = base + (int64_t)s * split_stride;
+      ms[u] = s0 + u < n_split ? ps[0] : kNegInf;
+      zs[u] = ps[1];
+      v[u] = *reinterpret_cast<const float4*>(ps + 4 + 4 * dq);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (ms[u] == kNegInf) continue;
+      const float mn = fmaxf(m_loc, ms[u]);
+      const float fo = fast_exp2(m_loc - mn);
+      const float fn = fast_exp2(ms[u] - mn);
+      z_loc = z_loc * fo + zs[u] * fn;
+      o.x = o.x * fo + v[u].x * fn;
+      o.y = o.y * fo + v[u].y * fn;
+      o.z = o.z * fo + v[u].z * fn;
+      o.w = o.w * fo + v[u].w * fn;
+      m_loc = mn;
+    }
+  }
+}
+
 template <int kMode, bool kFp8>
 __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
   constexpr bool kSparse = kMode == kSparseGather;
@@ -332,6 +366,7 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
       }
     }
   }
+
 }
 
 // One workgroup per (selection row, head, 32-dim chunk) merges the split partials
@@ -476,35 +511,10 @@ __global__ __launch_bounds__(256) void combine_small_kernel(CombineArgs a) {
   if (pair >= (int64_t)a.n_sel * a.G) return;
   const int sel = (int)(pair / a.G);
   const int h = (int)(pair - (int64_t)sel * a.G);
-  const int64_t split_stride = (int64_t)a.G * kPartStride;
-  const float* base = a.part + ((int64_t)sel * a.n_split * a.G + h) * kPartStride;
-  float m_loc = kNegInf, z_loc = 0.0f;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < a.n_split; s0 += 4) {
-    float ms[4], zs[4];
-    float4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = min(s0 + u, a.n_split - 1);
-      const float* ps = base + (int64_t)s * split_stride;
-      ms[u] = s0 + u < a.n_split ? ps[0] : kNegInf;
-      zs[u] = ps[1];
-      v[u] = *reinterpret_cast<const float4*>(ps + 4 + 4 * dq);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (ms[u] == kNegInf) continue;
-      const float mn = fmaxf(m_loc, ms[u]);
-      const float fo = fast_exp2(m_loc - mn);
-      const float fn = fast_exp2(ms[u] - mn);
-      z_loc = z_loc * fo + zs[u] * fn;
-      o.x = o.x * fo + v[u].x * fn;
-      o.y = o.y * fo + v[u].y * fn;
-      o.z = o.z * fo + v[u].z * fn;
-      o.w = o.w * fo + v[u].w * fn;
-      m_loc = mn;
-    }
-  }
+  float m_loc, z_loc;
+  float4 o;
+  fold_splits(a.part + ((int64_t)sel * a.n_split * a.G + h) * kPartStride, (int64_t)a.G * kPartStride,
+              a.n_split, dq, m_loc, z_loc, o);
   const float iz = z_loc > 0.0f ? 1.0f / z_loc : 0.0f;
   const int bj = sel / a.Hkv;
   const int g = sel - bj * a.Hkv;
