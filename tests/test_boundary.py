@@ -101,6 +101,15 @@ def test_workspace_monotone_in_context(lib):
     assert nbytes >= 4 * (1 << 20) * 8 * 4
 
 
+@pytest.mark.parametrize("var", ["HS2_SPLIT_LEN", "HS2_SPARSE_SPLIT_LEN", "HS2_CAND_WGS_TOTAL"])
+def test_zero_size_overrides_are_clamped(lib, monkeypatch, var):
+    """Size overrides set to 0 fall back to their minimum instead of dividing by zero."""
+    st0, n0 = hs2.hs2_workspace_size(_desc(kv_capacity=1 << 16, max_ctx_len=50000))
+    monkeypatch.setenv(var, "0")
+    st, nbytes = hs2.hs2_workspace_size(_desc(kv_capacity=1 << 16, max_ctx_len=50000))
+    assert st0 == hs2.HS2_OK and st == hs2.HS2_OK and nbytes > 0
+
+
 FAKE = 0x7F0000000000   # 16-byte aligned fake device address, never dereferenced
 
 
