@@ -310,11 +310,13 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
 
     // ---- P V, one half of the positions at a time
     float bsum[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // this block's sums
+    uint32_t tinybits = 0;   // bit 2qt + hf: this lane's record sum fell below 2^-100 (this half)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       // P of position tiles 2hf, 2hf+1 -> LDS [position][query row], high part and residual
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < 2; ++qt) {
+        float rs[2];   // this lane's 4 heads' share of the record sums of tiles 2hf, 2hf+1
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           const int pt = 2 * hf + pp;
@@ -325,26 +327,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
             z[qt][v] += p[v];
             if constexpr (want_blk) bsum[qt][v] += p[v];
           }
-          if constexpr (want_rec) {
-            // record: e = U + log2 sum_h p_h 2^(m_h - U) over the token's heads (4 here, 4 in
-            // the partner row group); the exact form when that sum is below 2^-100
-            const int32_t pos = P0 + pt * 16 + li;
-            const bool vis = pos <= pj[qt];
-            float sum = p[0] * c[qt][0] + p[1] * c[qt][1] + p[2] * c[qt][2] + p[3] * c[qt][3];
-            sum += partner(sum);
-            float e = U[qt] + __builtin_amdgcn_logf(sum);
-            const bool tiny = vis && sum < 0x1p-100f;
-            if (wave_any(tiny)) e = tiny ? exact_record(l[qt][pt], hbase, a.G) : e;
-            const int tl = tokl[qt];
-            if ((grp & 1) == 0 && tl < ntok && vis) {
-              const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)e);
-              a.records[(sel_tok0 + (int64_t)tl * a.Hkv) * a.logit_stride + pos] = rec;
-              if (pos < w0j[qt]) {
-                const uint32_t bin = half_order_key(rec) >> kFastShift;
-                atomicAdd(&shist[tl * kHistWords + (bin >> 1)], (bin & 1) ? 65536u : 1u);
-              }
-            }
-          }
+          if constexpr (want_rec) rs[pp] = p[0] * c[qt][0] + p[1] * c[qt][1] + p[2] * c[qt][2] + p[3] * c[qt][3];
           const uint32_t h01 = pack_bf16(p[0], p[1]);
           const uint32_t h23 = pack_bf16(p[2], p[3]);
           const uint32_t r01 = pack_bf16(p[0] - __uint_as_float(h01 << 16), p[1] - __uint_as_float(h01 & 0xFFFF0000u));
@@ -353,6 +336,56 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
           *reinterpret_cast<uint2*>(dst) = make_uint2(h01, h23);
           *reinterpret_cast<uint2*>(dst + kPHalf) = make_uint2(r01, r23);
         }
+        if constexpr (want_rec) {
+          // Records e = U + log2 sum_h p_h 2^(m_h - U) over the token's 8 heads (4 in this
+          // lane, 4 in the partner row group).  Even row groups finish tile 2hf, odd ones
+          // tile 2hf+1: each lane sends its partner the share of the tile the partner
+          // finishes, so one swap serves both tiles and every lane writes one record.  A
+          // sum below 2^-100 (terms lost to underflow could matter there) is not counted
+          // here and is redone exactly below.
+          const int own = grp & 1;
+          const float sum = (own ? rs[1] : rs[0]) + partner(own ? rs[0] : rs[1]);
+          const int32_t pos = P0 + (2 * hf + own) * 16 + li;
+          const int tl = tokl[qt];
+          const bool live = pos <= pj[qt] && tl < ntok;
+          const bool tiny = live && sum < 0x1p-100f;
+          tinybits |= tiny ? (1u << (2 * qt + hf)) : 0u;
+          const float e = U[qt] + __builtin_amdgcn_logf(sum);
+          if (live) {
+            const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)e);
+            a.records[(sel_tok0 + (int64_t)tl * a.Hkv) * a.logit_stride + pos] = rec;
+            if (!tiny && pos < w0j[qt]) {
+              const uint32_t bin = half_order_key(rec) >> kFastShift;
+              atomicAdd(&shist[tl * kHistWords + (bin >> 1)], (bin & 1) ? 65536u : 1u);
+            }
+          }
+        }
+      }
+      if constexpr (want_rec) {
+        // exact records of this half where the sum underflowed (rare: logits 100 log2
+        // units below the running maxima); every lane takes part in exact_record's swaps
+        if (wave_any(tinybits != 0u)) {
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) {
+            const uint32_t bit = 1u << (2 * qt + hf);
+            if (!wave_any((tinybits & bit) != 0u)) continue;
+            const float ex0 = exact_record(l[qt][2 * hf], hbase, a.G);
+            const float ex1 = exact_record(l[qt][2 * hf + 1], hbase, a.G);
+            const int own = grp & 1;
+            if (tinybits & bit) {   // implies a visible position of a present token
+              const int32_t pos = P0 + (2 * hf + own) * 16 + li;
+              const int tl = tokl[qt];
+              const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)(own ? ex1 : ex0));
+              a.records[(sel_tok0 + (int64_t)tl * a.Hkv) * a.logit_stride + pos] = rec;
+              if (pos < w0j[qt]) {
+                const uint32_t bin = half_order_key(rec) >> kFastShift;
+                atomicAdd(&shist[tl * kHistWords + (bin >> 1)], (bin & 1) ? 65536u : 1u);
+              }
+            }
+          }
+          tinybits = 0u;
+        }
+      }
       // A operands: P[query row li][positions 8grp .. 8grp+7] of this half
       bf16x8_t ph[2], pl[2];
 #pragma unroll
