@@ -257,15 +257,18 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
         sacc[qt][pt] = d;
       }
     }
-    // logits (log2 domain); the causal mask of each row's token only where some
-    // position lies beyond the first token's (wave-uniform branch)
+    // raw scores q.k; the log2-domain logit is l = scale_log2 * s (scale_log2 > 0, so
+    // maxima can be taken on s), formed inside the exp2 as fma(s, scale_log2, -m).  The
+    // causal mask of each row's token only where some position lies beyond the first
+    // token's (wave-uniform branch)
+    const float sl2 = a.scale_log2;
     float l[2][4][4];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) l[qt][pt][v] = sacc[qt][pt][v] * a.scale_log2;
+        for (int v = 0; v < 4; ++v) l[qt][pt][v] = sacc[qt][pt][v];
     if ((int64_t)P0 + kCPos - 1 > ctx - a.Lq + tok0) {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
@@ -287,7 +290,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          x[qt][v] = fmaxf(fmaxf(l[qt][0][v], l[qt][1][v]), fmaxf(l[qt][2][v], l[qt][3][v]));
+          x[qt][v] = fmaxf(fmaxf(l[qt][0][v], l[qt][1][v]), fmaxf(l[qt][2][v], l[qt][3][v])) * sl2;
           up_any |= x[qt][v] > m[qt][v] + kCSlack;
         }
       if (wave_any(up_any)) {
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
           float p[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            p[v] = fast_exp2(l[qt][pt][v] - m[qt][v]);   // m is finite: -inf logits give 0
+            p[v] = fast_exp2(__builtin_fmaf(l[qt][pt][v], sl2, -m[qt][v]));   // m finite: -inf gives 0
             z[qt][v] += p[v];
             if constexpr (want_blk) bsum[qt][v] += p[v];
           }
@@ -369,8 +372,14 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
           for (int qt = 0; qt < 2; ++qt) {
             const uint32_t bit = 1u << (2 * qt + hf);
             if (!wave_any((tinybits & bit) != 0u)) continue;
-            const float ex0 = exact_record(l[qt][2 * hf], hbase, a.G);
-            const float ex1 = exact_record(l[qt][2 * hf + 1], hbase, a.G);
+            float l0[4], l1[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              l0[v] = l[qt][2 * hf][v] * sl2;
+              l1[v] = l[qt][2 * hf + 1][v] * sl2;
+            }
+            const float ex0 = exact_record(l0, hbase, a.G);
+            const float ex1 = exact_record(l1, hbase, a.G);
             const int own = grp & 1;
             if (tinybits & bit) {   // implies a visible position of a present token
               const int32_t pos = P0 + (2 * hf + own) * 16 + li;
