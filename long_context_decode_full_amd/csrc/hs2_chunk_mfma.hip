@@ -126,10 +126,12 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   uint8_t* pst_all = lds + 2 * kKTile;
   uint32_t* shist = reinterpret_cast<uint32_t*>(lds + 2 * kKTile + kCWaves * kPWave);
 
-  // (Placing the two token halves of a split on one XCD, 8 workgroups apart, was
-  // measured slower: the pair then contends for the same L2 lines at the same time.)
-  const int half = blockIdx.x & 1;
-  const int split = blockIdx.x >> 1;
+  // blockIdx.x = split * token groups + group: the groups of 32 tokens of one split are
+  // adjacent.  (Placing the two groups of a 64-token chunk on one XCD, 8 workgroups
+  // apart, was measured slower: the pair then contends for the same L2 lines at once.)
+  const int n_tgroups = (a.Lq + kCTokens - 1) / kCTokens;
+  const int tgroup = blockIdx.x % n_tgroups;
+  const int split = blockIdx.x / n_tgroups;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
 
   int64_t ctx = a.ctx_len[b];
   ctx = ctx < 0 ? 0 : (ctx > a.ctx_max ? a.ctx_max : ctx);
-  const int tok0 = half * kCTokens;                 // first token of this workgroup
+  const int tok0 = tgroup * kCTokens;               // first token of this workgroup
   const int ntok = min(kCTokens, a.Lq - tok0);      // tokens present (may be <= 0)
   const int64_t p_begin = (int64_t)split * a.split_len;
   // the last present token sees the most positions
@@ -476,7 +478,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
 }  // namespace
 
 hipError_t launch_chunk_mfma(const ScanArgs& a, int B, hipStream_t st) {
-  dim3 grid(a.n_split * 2, a.Hkv, B);
+  dim3 grid(a.n_split * ((a.Lq + kCTokens - 1) / kCTokens), a.Hkv, B);
   if (a.blse != nullptr)
     hipLaunchKernelGGL((chunk_mfma_kernel<true>), grid, dim3(kCThreads), 0, st, a);
   else

@@ -169,11 +169,12 @@ def test_chunk_per_token_route(monkeypatch):
 
 
 @pytest.mark.parametrize("lq,ctx,hq,hkv", [(16, [3000, 700], 32, 4), (40, [4100], 16, 2),
-                                           (64, [1300, 20000], 16, 16)])
+                                           (64, [1300, 20000], 16, 16), (100, [9000, 2500], 32, 4)])
 def test_chunk_shapes(lq, ctx, hq, hkv):
-    """Partial halves (q_len 16, 40), a context shorter than window + top-k, and G = 1."""
+    """Partial token groups (q_len 16, 40, and 100 = three groups of 32 and a ragged
+    fourth), a context shorter than window + top-k, and G = 1."""
     w = wl.Workload(f"chunk lq{lq}", len(ctx), lq, hq, hkv, ctx_lens=ctx, n_needles=8, seed=2100 + lq)
-    toks = sorted({(b, j) for b in range(len(ctx)) for j in (0, lq // 2, lq - 1)})
+    toks = sorted({(b, j) for b in range(len(ctx)) for j in (0, 31, 32, lq // 2, 70, lq - 1) if j < lq})
     run_and_compare(w, f"chunk-lq{lq}", tokens=toks)
 
 
@@ -287,7 +288,7 @@ def test_block_baseline_chunk():
 
 
 @pytest.mark.parametrize("lq,ctx,bs,nb", [(64, [5000, 12000], 64, 18), (40, [4100], 128, 9),
-                                           (16, [700], 64, 18)])
+                                           (16, [700], 64, 18), (100, [6000], 64, 18)])
 def test_block_baseline_chunk_kernel(lq, ctx, bs, nb):
     """Block comparator on the chunk kernel's per-block sums (block sizes that are
     multiples of 64), including a context shorter than the block budget."""
