@@ -86,7 +86,9 @@ typedef struct hs2_attn_desc {
 /* Host only, touches no GPU: checks a descriptor.  Limits: head_dim == 128,
  * 1 <= G <= 8, window + topk <= 4096 (token mode), block_size in [1, 4096] and
  * block_size * n_blocks <= 4096 (block mode), 1 <= q_len <= max_ctx_len <= cap,
- * cap < 2^31. */
+ * cap < 2^31, batch * q_len <= 65535, n_kv_heads <= 65535 and
+ * batch * q_len * n_kv_heads (selection rows) <= 65535 * 1024; beyond these limits
+ * HS2_ERR_UNSUPPORTED. */
 hs2_status hs2_validate(const hs2_attn_desc* desc);
 
 /* Host only: bytes of device workspace that hs2_full_attn_select and

@@ -81,6 +81,8 @@ hs2_status validate_desc(const hs2_attn_desc* d) {
   if (d->kv_capacity >= (int64_t(1) << 31)) return HS2_ERR_UNSUPPORTED;
   if ((int64_t)d->batch * d->q_len > 65535) return HS2_ERR_UNSUPPORTED;
   if (d->n_kv_heads > 65535) return HS2_ERR_UNSUPPORTED;
+  // selection rows index flattened grids of (row, chunk) workgroups
+  if ((int64_t)d->batch * d->q_len * d->n_kv_heads > 65535ll * 1024) return HS2_ERR_UNSUPPORTED;
   return HS2_OK;
 }
 

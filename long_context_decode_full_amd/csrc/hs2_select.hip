@@ -117,8 +117,9 @@ __device__ void find_threshold(const uint32_t* gh, uint32_t need, uint32_t& bin,
 
 // ------------------------------------------------------------------ pass 1
 __global__ __launch_bounds__(kThreads) void groupsum_kernel(SelectArgs a) {
-  const int chunk = blockIdx.x;
-  const int64_t sel = blockIdx.y;
+  // blockIdx.x = row * n_chunks + chunk (rows can exceed the 65,535 of grid y)
+  const int chunk = (int)(blockIdx.x % (uint32_t)a.n_chunks);
+  const int64_t sel = blockIdx.x / (uint32_t)a.n_chunks;
   const int tid = threadIdx.x;
   const RowGeom rg = row_geom(a, sel);
 
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void groupsum_kernel(SelectArgs a) {
   if (!a.with_hist) return;
   __syncthreads();
   merge_hist<kHist1Bins>(lh, sel_state(a, sel) + kSelHist1Off);
-  if (!last_block(sel_state(a, sel) + kSelCounterOff + 0, gridDim.x)) return;
+  if (!last_block(sel_state(a, sel) + kSelCounterOff + 0, a.n_chunks)) return;
 
   // Last workgroup of the row: decide how the row continues.
   uint32_t* st = sel_state(a, sel);
@@ -190,8 +191,9 @@ template <int PASS>
 __global__ __launch_bounds__(kThreads) void refine_kernel(SelectArgs a) {
   constexpr int NB = PASS == 2 ? kHist2Bins : kHist3Bins;
   constexpr int DIGIT = PASS == 2 ? 12 : 8;
-  const int chunk = blockIdx.x;
-  const int64_t sel = blockIdx.y;
+  // blockIdx.x = row * n_chunks + chunk (rows can exceed the 65,535 of grid y)
+  const int chunk = (int)(blockIdx.x % (uint32_t)a.n_chunks);
+  const int64_t sel = blockIdx.x / (uint32_t)a.n_chunks;
   const int tid = threadIdx.x;
   uint32_t* st = sel_state(a, sel);
   if (st[kStResolved]) return;   // uniform across the row's workgroups
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void refine_kernel(SelectArgs a) {
   __syncthreads();
   uint32_t* gh = (PASS == 2 ? a.hist2 + sel * kHist2Bins : a.hist3 + sel * kHist3Bins);
   merge_hist<NB>(lh, gh);
-  if (!last_block(st + kSelCounterOff + (PASS - 1), gridDim.x)) return;
+  if (!last_block(st + kSelCounterOff + (PASS - 1), a.n_chunks)) return;
 
   const uint32_t above0 = st[kStAbove];
   const uint32_t need = st[kStKK] - above0;
@@ -247,8 +249,9 @@ __device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
 }
 
 __global__ __launch_bounds__(kThreads) void collect_kernel(SelectArgs a) {
-  const int chunk = blockIdx.x;
-  const int64_t sel = blockIdx.y;
+  // blockIdx.x = row * n_chunks + chunk (rows can exceed the 65,535 of grid y)
+  const int chunk = (int)(blockIdx.x % (uint32_t)a.n_chunks);
+  const int64_t sel = blockIdx.x / (uint32_t)a.n_chunks;
   const int tid = threadIdx.x;
   uint32_t* st = sel_state(a, sel);
   if (st[kStTakeAll]) return;
@@ -502,20 +505,20 @@ __global__ __launch_bounds__(kBlkThreads) void block_select_kernel(SelectArgs a)
 }  // namespace
 
 hipError_t launch_groupsum(const SelectArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(groupsum_kernel, dim3(a.n_chunks, a.n_sel), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(groupsum_kernel, dim3((uint32_t)((uint64_t)a.n_chunks * (uint64_t)a.n_sel)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_refine(const SelectArgs& a, int pass, hipStream_t st) {
   if (pass == 2)
-    hipLaunchKernelGGL(refine_kernel<2>, dim3(a.n_chunks, a.n_sel), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(refine_kernel<2>, dim3((uint32_t)((uint64_t)a.n_chunks * (uint64_t)a.n_sel)), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(refine_kernel<3>, dim3(a.n_chunks, a.n_sel), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(refine_kernel<3>, dim3((uint32_t)((uint64_t)a.n_chunks * (uint64_t)a.n_sel)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_collect(const SelectArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(collect_kernel, dim3(a.n_chunks, a.n_sel), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(collect_kernel, dim3((uint32_t)((uint64_t)a.n_chunks * (uint64_t)a.n_sel)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

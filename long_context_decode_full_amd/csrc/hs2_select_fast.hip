@@ -125,8 +125,8 @@ __device__ __forceinline__ int32_t key_pos(uint64_t key) {
 }
 
 // ------------------------------------------------------------------ candidates + exact re-score
-// Work unit: one (row, chunk of chunk_len positions); a workgroup takes the chunks
-// blockIdx.x, blockIdx.x + gridDim.x, ... of row blockIdx.y (the grid is sized so
+// Work unit: one (row, chunk of chunk_len positions); workgroup w of a row takes its
+// chunks w, w + cand_wgs, ... (blockIdx.x = row * cand_wgs + w; the grid is sized so
 // that rows of a long context do not leave most workgroups of short rows empty).
 // The threshold bin of the k-th record gives two tests per position (records are
 // bounds, see above):
@@ -137,7 +137,8 @@ __device__ __forceinline__ int32_t key_pos(uint64_t key) {
 // candidates re-read their key rows.  Keys stay in position order per chunk.
 template <bool kFp8, int R>   // R = records per thread = chunk_len / 256 (8..64)
 __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
-  const int64_t sel = blockIdx.y;
+  const int64_t sel = blockIdx.x / (uint32_t)a.cand_wgs;
+  const int wg = (int)(blockIdx.x % (uint32_t)a.cand_wgs);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   constexpr int clen = R * kThreads;
   constexpr int nv = R / 8;       // 16-byte loads per thread
   // chunks at or past the first window position hold no candidate (and are not read)
-  if ((int64_t)blockIdx.x * clen >= rg.w0) return;
+  if ((int64_t)wg * clen >= rg.w0) return;
 
   __shared__ uint16_t cpos[clen];    // chunk-relative positions of the candidates
   __shared__ uint16_t ulist[clen];   // indices into cpos of the uncertain ones
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   const float Mown = Mh[hown];
   const float izown = iz[hown];
 
-  for (int chunk = blockIdx.x; (int64_t)chunk * clen < rg.w0; chunk += gridDim.x) {
+  for (int chunk = wg; (int64_t)chunk * clen < rg.w0; chunk += a.cand_wgs) {
     const int64_t c0 = (int64_t)chunk * clen;
     // Each thread owns R consecutive positions (one batch of 16-byte loads); a
     // block-wide exclusive scan of the per-thread counts keeps position order.
@@ -551,7 +552,7 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
 
 template <bool kFp8>
 void launch_candidates_r(const FastSelArgs& a, hipStream_t st) {
-  const dim3 grid(a.cand_wgs, a.n_sel);
+  const dim3 grid((uint32_t)((uint64_t)a.cand_wgs * (uint64_t)a.n_sel));
   switch (a.chunk_len / kThreads) {
     case 8: hipLaunchKernelGGL((candidate_kernel<kFp8, 8>), grid, dim3(kThreads), 0, st, a); break;
     case 16: hipLaunchKernelGGL((candidate_kernel<kFp8, 16>), grid, dim3(kThreads), 0, st, a); break;

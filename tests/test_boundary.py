@@ -101,6 +101,14 @@ def test_workspace_monotone_in_context(lib):
     assert nbytes >= 4 * (1 << 20) * 8 * 4
 
 
+def test_selection_row_limit(lib):
+    """batch * q_len * n_kv_heads beyond 65535 * 1024 rows is reported, not launched."""
+    assert hs2.hs2_validate(_desc(batch=1000, q_len=64, n_q_heads=2048, n_kv_heads=2048,
+                                  max_ctx_len=64, kv_capacity=64)) == hs2.HS2_ERR_UNSUPPORTED
+    assert hs2.hs2_validate(_desc(batch=1000, q_len=64, n_q_heads=512, n_kv_heads=512,
+                                  max_ctx_len=64, kv_capacity=64)) == hs2.HS2_OK
+
+
 @pytest.mark.parametrize("var", ["HS2_SPLIT_LEN", "HS2_SPARSE_SPLIT_LEN", "HS2_CAND_WGS_TOTAL"])
 def test_zero_size_overrides_are_clamped(lib, monkeypatch, var):
     """Size overrides set to 0 fall back to their minimum instead of dividing by zero."""

@@ -178,6 +178,16 @@ def test_chunk_shapes(lq, ctx, hq, hkv):
     run_and_compare(w, f"chunk-lq{lq}", tokens=toks)
 
 
+@pytest.mark.parametrize("with_probs", [False, True])
+def test_more_selection_rows_than_grid_y(with_probs):
+    """64 sequences x 256 query tokens x 4 KV heads = 65,536 selection rows, past the
+    65,535 limit of a grid dimension: the selection kernels flatten (row, chunk) into
+    grid x.  Sampled tokens, first and last rows included."""
+    w = wl.Workload("many rows", 64, 256, 8, 4, ctx_lens=[600] * 64, n_needles=4, seed=2400)
+    run_and_compare(w, "many-rows", with_probs=with_probs,
+                    tokens=[(0, 0), (0, 255), (31, 100), (63, 0), (63, 255)])
+
+
 def test_chunk_split_invariant(monkeypatch):
     """Chunk kernel: several position splits and one split give the same outputs."""
     from long_context_decode_full_amd.runner import HybridBlockDevice
