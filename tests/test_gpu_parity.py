@@ -178,6 +178,15 @@ def test_chunk_shapes(lq, ctx, hq, hkv):
     run_and_compare(w, f"chunk-lq{lq}", tokens=toks)
 
 
+@pytest.mark.parametrize("mode", ["token", "block"])
+def test_fp8_query_chunk(mode):
+    """fp8 caches with several query tokens (causal inside the chunk) take the decode
+    scan once per token; every token compared."""
+    w = wl.Workload("fp8 chunk", 2, 4, 32, 4, ctx_lens=[3000, 5200], n_needles=8, kv_dtype="fp8",
+                    seed=2450)
+    run_and_compare(w, f"fp8-chunk-{mode}", mode=mode)
+
+
 @pytest.mark.parametrize("with_probs", [False, True])
 def test_more_selection_rows_than_grid_y(with_probs):
     """64 sequences x 256 query tokens x 4 KV heads = 65,536 selection rows, past the
