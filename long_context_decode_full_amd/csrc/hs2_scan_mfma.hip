@@ -101,12 +101,20 @@ struct StepBuf<false> {
 };
 template <>
 struct StepBuf<true> {
-  uint2 k[2][4];
+  uint4 k[2][2];   // 16 codes: dim chunks kchunk_fp8(2h, grp), kchunk_fp8(2h + 1, grp)
   uint4 v[4];
   float ks[2][4], vs[2][4];
 };
 
-template <bool kFp8>
+// fp8 keys: the 8-dim chunk of the row that MFMA slice q takes in row group grp.  A
+// lane loads 16 contiguous codes (two chunks, slices 2h and 2h+1) and the 4 row groups
+// cover 64 contiguous bytes per load; the queries are read in the same dim order, so
+// the dot products are unchanged.  (bf16 keys: chunk 4q + grp.)
+__device__ __forceinline__ int kchunk_fp8(int q, int grp) { return 8 * (q >> 1) + 2 * grp + (q & 1); }
+
+// kVecScale (fp8, capacity a multiple of 4, so 16-byte aligned rows of scales): the 4
+// scales of a lane's rows 4grp .. 4grp+3 of a tile in one 16-byte load.
+template <bool kFp8, bool kVecScale = false>
 __device__ __forceinline__ void load_step(StepBuf<kFp8>& s, const uint8_t* __restrict__ kb,
                                           const uint8_t* __restrict__ vb, const float* __restrict__ ksb,
                                           const float* __restrict__ vsb, int32_t base, int32_t last,
@@ -114,11 +122,13 @@ __device__ __forceinline__ void load_step(StepBuf<kFp8>& s, const uint8_t* __res
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const uint32_t row = (uint32_t)min(base + 16 * t + w16, last);
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if constexpr (kFp8)
-        s.k[t][q] = *reinterpret_cast<const uint2*>(kb + (uint64_t)row * 128 + 32 * q + 8 * grp);
-      else
+      for (int h = 0; h < 2; ++h)
+        s.k[t][h] = *reinterpret_cast<const uint4*>(kb + (uint64_t)row * 128 + 64 * h + 16 * grp);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
         s.k[t][q] = load_nt(reinterpret_cast<const uint4*>(kb + (uint64_t)row * 256 + 64 * q + 16 * grp));
     }
   }
@@ -128,14 +138,27 @@ __device__ __forceinline__ void load_step(StepBuf<kFp8>& s, const uint8_t* __res
       const uint32_t row = (uint32_t)min(base + 8 * i + (lane >> 3), last);
       s.v[i] = load_nt(reinterpret_cast<const uint4*>(vb + (uint64_t)row * 128 + 16 * (lane & 7)));
     }
+    if constexpr (kVecScale) {
+      // rows past `last` are masked; clamping the first row to a multiple of 4 at or
+      // below `last` keeps all 4 inside the capacity (a multiple of 4)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint32_t row = (uint32_t)min(base + 16 * t + 4 * grp + v, last);
-        s.ks[t][v] = ksb[row];
-        s.vs[t][v] = vsb[row];
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t row = (uint32_t)min(base + 16 * t + 4 * grp, last & ~3);
+        const float4 k4 = *reinterpret_cast<const float4*>(ksb + row);
+        const float4 v4 = *reinterpret_cast<const float4*>(vsb + row);
+        s.ks[t][0] = k4.x; s.ks[t][1] = k4.y; s.ks[t][2] = k4.z; s.ks[t][3] = k4.w;
+        s.vs[t][0] = v4.x; s.vs[t][1] = v4.y; s.vs[t][2] = v4.z; s.vs[t][3] = v4.w;
       }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t row = (uint32_t)min(base + 16 * t + 4 * grp + v, last);
+          s.ks[t][v] = ksb[row];
+          s.vs[t][v] = vsb[row];
+        }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -156,11 +179,13 @@ __device__ __forceinline__ void load_step_gather(StepBuf<kFp8>& s, const uint8_t
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const uint32_t row = (uint32_t)max(srow[e0 + 16 * t + w16], 0);
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if constexpr (kFp8)
-        s.k[t][q] = *reinterpret_cast<const uint2*>(kb + (uint64_t)row * 128 + 32 * q + 8 * grp);
-      else
+      for (int h = 0; h < 2; ++h)
+        s.k[t][h] = *reinterpret_cast<const uint4*>(kb + (uint64_t)row * 128 + 64 * h + 16 * grp);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
         s.k[t][q] = *reinterpret_cast<const uint4*>(kb + (uint64_t)row * 256 + 64 * q + 16 * grp);
     }
   }
@@ -228,9 +253,10 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
     for (int q = 0; q < 4; ++q) {
       uint4 kw;
       if constexpr (kFp8) {
-        const uint2 c = s.k[t][q];
-        kw = make_uint4(fp8x2_to_bf16x2(c.x, false), fp8x2_to_bf16x2(c.x, true), fp8x2_to_bf16x2(c.y, false),
-                        fp8x2_to_bf16x2(c.y, true));
+        const uint4 c4 = s.k[t][q >> 1];
+        const uint32_t c0 = (q & 1) ? c4.z : c4.x, c1 = (q & 1) ? c4.w : c4.y;
+        kw = make_uint4(fp8x2_to_bf16x2(c0, false), fp8x2_to_bf16x2(c0, true), fp8x2_to_bf16x2(c1, false),
+                        fp8x2_to_bf16x2(c1, true));
       } else {
         kw = s.k[t][q];
       }
@@ -291,7 +317,8 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
     for (int v = 0; v < 4; ++v) {
       p[t][v] = l[t][v] != kNegInf ? fast_exp2(l[t][v] - hs.m) : 0.0f;
       hs.z += p[t][v];
-      if constexpr (kFp8) p[t][v] *= s.vs[t][v];
+      // masked rows: the scale may come from a row past the end (4-row scale loads)
+      if constexpr (kFp8) p[t][v] = l[t][v] != kNegInf ? p[t][v] * s.vs[t][v] : 0.0f;
     }
 
   // P as bf16 high part + bf16 residual (B operand, k slot u <-> tile u/4, row 4grp + u%4)
@@ -323,7 +350,7 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
   }
 }
 
-template <bool kFp8>
+template <bool kFp8, bool kVecScale>
 __global__ __launch_bounds__(kMThreads, 1) void scan_mfma_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kMLds];
   uint16_t* srec = reinterpret_cast<uint16_t*>(lds);
@@ -366,10 +393,12 @@ __global__ __launch_bounds__(kMThreads, 1) void scan_mfma_kernel(ScanArgs a) {
   // Q^T fragments: head w16, dims 32q + 8grp .. +8
   bf16x8_t qf[4];
   {
-    const uint16_t* qh = a.q + ((int64_t)bj * a.Hq + (int64_t)g * a.G + w16) * kHeadDim + 8 * grp;
+    const uint16_t* qh = a.q + ((int64_t)bj * a.Hq + (int64_t)g * a.G + w16) * kHeadDim;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      qf[q] = as_bf16x8(w16 < a.G ? *reinterpret_cast<const uint4*>(qh + 32 * q) : make_uint4(0u, 0u, 0u, 0u));
+    for (int q = 0; q < 4; ++q) {
+      const int chunk = kFp8 ? kchunk_fp8(q, grp) : 4 * q + grp;
+      qf[q] = as_bf16x8(w16 < a.G ? *reinterpret_cast<const uint4*>(qh + 8 * chunk) : make_uint4(0u, 0u, 0u, 0u));
+    }
   }
 
   const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
@@ -415,20 +444,20 @@ __global__ __launch_bounds__(kMThreads, 1) void scan_mfma_kernel(ScanArgs a) {
     };
     StepBuf<kFp8> s0, s1;
     int k0 = wave;
-    load_step<kFp8>(s0, kb, vb, ksb, vsb, w_begin + k0 * kStepRows, last, grp, w16, lane);
+    load_step<kFp8, kVecScale>(s0, kb, vb, ksb, vsb, w_begin + k0 * kStepRows, last, grp, w16, lane);
     int k1 = take();
-    load_step<kFp8>(s1, kb, vb, ksb, vsb, w_begin + k1 * kStepRows, last, grp, w16, lane);
+    load_step<kFp8, kVecScale>(s1, kb, vb, ksb, vsb, w_begin + k1 * kStepRows, last, grp, w16, lane);
     // two-buffer ring; every load is issued (rows past the end re-read `last`)
     while (k0 < nsteps) {
       process_step<kFp8>(s0, qf, vt, w_begin + k0 * kStepRows, w_begin, w_end, cand_span, a.scale_log2, a.G,
                          grp, w16, lane, srec, shist, hs);
       k0 = take();
-      load_step<kFp8>(s0, kb, vb, ksb, vsb, w_begin + k0 * kStepRows, last, grp, w16, lane);
+      load_step<kFp8, kVecScale>(s0, kb, vb, ksb, vsb, w_begin + k0 * kStepRows, last, grp, w16, lane);
       if (k1 >= nsteps) break;
       process_step<kFp8>(s1, qf, vt, w_begin + k1 * kStepRows, w_begin, w_end, cand_span, a.scale_log2, a.G,
                          grp, w16, lane, srec, shist, hs);
       k1 = take();
-      load_step<kFp8>(s1, kb, vb, ksb, vsb, w_begin + k1 * kStepRows, last, grp, w16, lane);
+      load_step<kFp8, kVecScale>(s1, kb, vb, ksb, vsb, w_begin + k1 * kStepRows, last, grp, w16, lane);
     }
   }
 
@@ -535,10 +564,12 @@ __global__ __launch_bounds__(kMThreads, 1) void gather_mfma_kernel(ScanArgs a, f
   }
   bf16x8_t qf[4];
   {
-    const uint16_t* qh = a.q + ((int64_t)bj * a.Hq + (int64_t)g * a.G + w16) * kHeadDim + 8 * grp;
+    const uint16_t* qh = a.q + ((int64_t)bj * a.Hq + (int64_t)g * a.G + w16) * kHeadDim;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      qf[q] = as_bf16x8(w16 < a.G ? *reinterpret_cast<const uint4*>(qh + 32 * q) : make_uint4(0u, 0u, 0u, 0u));
+    for (int q = 0; q < 4; ++q) {
+      const int chunk = kFp8 ? kchunk_fp8(q, grp) : 4 * q + grp;
+      qf[q] = as_bf16x8(w16 < a.G ? *reinterpret_cast<const uint4*>(qh + 8 * chunk) : make_uint4(0u, 0u, 0u, 0u));
+    }
   }
   const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
   const int rowbytes = kFp8 ? 128 : 256;
@@ -622,10 +653,12 @@ __global__ __launch_bounds__(kMThreads, 1) void gather_mfma_kernel(ScanArgs a, f
 
 hipError_t launch_scan_mfma(const ScanArgs& a, bool fp8, int B, hipStream_t st) {
   dim3 grid(a.n_split, a.Hkv, B * a.Lq);
-  if (fp8)
-    hipLaunchKernelGGL((scan_mfma_kernel<true>), grid, dim3(kMThreads), 0, st, a);
+  if (fp8 && a.cap % 4 == 0)
+    hipLaunchKernelGGL((scan_mfma_kernel<true, true>), grid, dim3(kMThreads), 0, st, a);
+  else if (fp8)
+    hipLaunchKernelGGL((scan_mfma_kernel<true, false>), grid, dim3(kMThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((scan_mfma_kernel<false>), grid, dim3(kMThreads), 0, st, a);
+    hipLaunchKernelGGL((scan_mfma_kernel<false, false>), grid, dim3(kMThreads), 0, st, a);
   return hipGetLastError();
 }
 

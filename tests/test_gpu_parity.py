@@ -178,6 +178,16 @@ def test_chunk_shapes(lq, ctx, hq, hkv):
     run_and_compare(w, f"chunk-lq{lq}", tokens=toks)
 
 
+@pytest.mark.parametrize("cap", [5203, 5204])
+def test_fp8_scale_alignment(cap):
+    """fp8 scales are read 4 rows at a time when the capacity is a multiple of 4 (16-byte
+    aligned rows) and one by one otherwise; both against the oracle, with a context
+    ending inside a group of 4 rows."""
+    w = wl.Workload(f"fp8 cap{cap}", 2, 1, 32, 4, ctx_lens=[5001, 4099], n_needles=8, kv_dtype="fp8",
+                    capacity=cap, poison_tail=True, seed=2460)
+    run_and_compare(w, f"fp8-cap{cap}")
+
+
 @pytest.mark.parametrize("mode", ["token", "block"])
 def test_fp8_query_chunk(mode):
     """fp8 caches with several query tokens (causal inside the chunk) take the decode
