@@ -77,7 +77,10 @@ hs2_status validate_desc(const hs2_attn_desc* d) {
     return HS2_ERR_INVALID_ARG;
   }
   if (d->head_dim != kHeadDim) return HS2_ERR_UNSUPPORTED;
-  if (d->n_q_heads / d->n_kv_heads > kSlots) return HS2_ERR_UNSUPPORTED;
+  // up to 32 query heads per KV head (MQA at Hq = 32); beyond 8 only token selection
+  // on the record path (matrix-core scan and gather), see wide_group()
+  if (d->n_q_heads / d->n_kv_heads > kMaxHeads) return HS2_ERR_UNSUPPORTED;
+  if (d->n_q_heads / d->n_kv_heads > kSlots && d->select_mode != HS2_SELECT_TOKEN) return HS2_ERR_UNSUPPORTED;
   if (d->kv_capacity >= (int64_t(1) << 31)) return HS2_ERR_UNSUPPORTED;
   if ((int64_t)d->batch * d->q_len > 65535) return HS2_ERR_UNSUPPORTED;
   if (d->n_kv_heads > 65535) return HS2_ERR_UNSUPPORTED;
@@ -91,8 +94,12 @@ hs2_status validate_desc(const hs2_attn_desc* d) {
 // HS2_CHUNK_PER_TOKEN=1 runs the decode scan once per token instead (comparison).
 bool chunk_path(const hs2_attn_desc* d) {
   return d->q_len > 1 && d->kv_dtype == HS2_KV_BF16 && d->select_mode == HS2_SELECT_TOKEN &&
-         env_int("HS2_CHUNK_PER_TOKEN", 0) == 0;
+         d->n_q_heads / d->n_kv_heads <= kSlots && env_int("HS2_CHUNK_PER_TOKEN", 0) == 0;
 }
+// More than 8 query heads per KV head: the matrix-core scan with 16-head blocks, the
+// matrix-core gather and block-wise re-scoring; the logits path (probs) and the chunk
+// kernel keep 8 head slots and are not used (chunks run the scan once per token).
+bool wide_group(const hs2_attn_desc* d) { return d->n_q_heads / d->n_kv_heads > kSlots; }
 // The block comparator for a chunk (block sizes that are multiples of 64) takes its
 // block masses from the same kernel's per-block sums instead of per-position logits.
 bool chunk_block_path(const hs2_attn_desc* d) {
@@ -160,7 +167,7 @@ Layout make_layout(const hs2_attn_desc* d) {
   L.logits_ok = (double)n * (double)L.logit_stride * 36.0 <= (double)kMaxLogitsBytes;
   size_t off = 0;
   L.off_part = off;   off = align_up(off + (size_t)n * nsplit_max * L.G * kPartStride * sizeof(float));
-  L.off_mz = off;     off = align_up(off + (size_t)n * 16 * sizeof(float));
+  L.off_mz = off;     off = align_up(off + (size_t)n * kMaxHeads * 2 * sizeof(float));
   L.off_selblk = off; off = align_up(off + (size_t)n * kSelWords * sizeof(uint32_t));
   if (L.logits_ok) {
     L.off_logits = off; off = align_up(off + (size_t)n * L.logit_stride * 8 * sizeof(float));
@@ -355,9 +362,10 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   // Record path (default for token selection): compact bound records, exact
   // re-scoring of the candidates.  Logits path: every position's logits, needed
   // when the caller wants all probabilities (probs) or for the block comparator.
-  const bool fast = L.fast_ok && probs == nullptr && env_int("HS2_FORCE_LOGITS", 0) == 0;
+  const bool fast = L.fast_ok && probs == nullptr && (wide_group(desc) || env_int("HS2_FORCE_LOGITS", 0) == 0);
   const bool cblock = chunk_block_path(desc) && probs == nullptr;
   if (!fast && !cblock && !L.logits_ok) return HS2_ERR_UNSUPPORTED;
+  if (!fast && wide_group(desc)) return HS2_ERR_UNSUPPORTED;
   ScanArgs sa = scan_args(desc, L, q, k, v, k_scale, v_scale, ctx_len, ws);
   if (cblock) return chunk_block_select(desc, L, sa, ctx_len, out, idx, ws, stream);
   sa.logits = reinterpret_cast<float*>(ws + L.off_logits);
@@ -371,7 +379,7 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   TimerRec rec;
   const bool timed = timer_begin(stream, 0, &rec);
   // record path: matrix-core scan (HS2_SCAN_VALU=1 selects the VALU scan instead)
-  const bool mfma = fast && env_int("HS2_SCAN_VALU", 0) == 0;
+  const bool mfma = fast && (wide_group(desc) || env_int("HS2_SCAN_VALU", 0) == 0);
   hipError_t e = (fast && chunk_path(desc)) ? launch_chunk_mfma(sa, desc->batch, stream)
                  : mfma                     ? launch_scan_mfma(sa, fp8, desc->batch, stream)
                                             : launch_scan_dense(sa, fp8, fast, desc->batch, stream);
@@ -494,7 +502,7 @@ HS2_API hs2_status hs2_sparse_attn(const hs2_attn_desc* desc, const void* q, con
   // HS2_SPARSE_FUSED=1 / 0 forces either path.
   const int64_t rows = (int64_t)desc->batch * desc->q_len * desc->n_kv_heads;
   const int fused_env = env_int("HS2_SPARSE_FUSED", -1);
-  const bool fused = fused_env >= 0 ? fused_env != 0 : rows >= kFusedSparseRows;
+  const bool fused = wide_group(desc) || (fused_env >= 0 ? fused_env != 0 : rows >= kFusedSparseRows);
   TimerRec rec;
   const bool timed = timer_begin(stream, 1, &rec);
   if (fused) {

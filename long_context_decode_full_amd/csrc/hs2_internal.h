@@ -10,6 +10,8 @@ namespace hs2 {
 
 constexpr int kHeadDim = 128;
 constexpr int kSlots = 8;             // head slots per KV group handled by one wave
+constexpr int kMaxHeads = 32;         // query heads per KV head (G) at most; per-row (M, 1/Z)
+                                      // statistics keep kMaxHeads slots
 constexpr int kPartStride = 132;      // floats per (split, head) partial: m, z, pad, pad, o[128]
 constexpr int kHist1Bins = 2048;      // score bits 30..20
 constexpr int kHist2Bins = 4096;      // score bits 19..8
@@ -80,7 +82,7 @@ struct ScanArgs {
 struct CombineArgs {
   const float* part;        // [n_sel, n_split, G, kPartStride]
   float* out;               // [B, Lq, Hq, D]
-  float* mz;                // [n_sel, 8, 2] (M, 1/Z) or nullptr
+  float* mz;                // [n_sel, kMaxHeads, 2] (M, 1/Z) or nullptr
   uint32_t* sel_zero;       // selection words to clear per selection, or nullptr
   int32_t sel_zero_words;   // words per selection in sel_zero
   const uint16_t* hist_part;  // records mode: per-split key histograms to merge, or nullptr
@@ -92,7 +94,7 @@ struct CombineArgs {
 
 struct SelectArgs {
   const float* logits;      // [n_sel, logit_stride, 8]
-  const float* mz;          // [n_sel, 8, 2]
+  const float* mz;          // [n_sel, kMaxHeads, 2]
   float* s;                 // [n_sel, s_stride] group-summed probabilities
   int64_t s_stride;
   int64_t logit_stride;
@@ -117,7 +119,7 @@ struct SelectArgs {
 struct FastSelArgs {
   const uint16_t* records;  // [n_sel, rec_stride] binary16 bound records
   int64_t rec_stride;
-  const float* mz;          // [n_sel, 8, 2] (M, 1/Z)
+  const float* mz;          // [n_sel, kMaxHeads, 2] (M, 1/Z)
   const int32_t* ctx_len;
   int64_t ctx_max;
   uint32_t* selblk;         // [n_sel, kSelWords]

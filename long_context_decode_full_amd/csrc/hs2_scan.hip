@@ -491,8 +491,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     a.out[((int64_t)bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim + chunk * 32 + tid] =
         Z > 0.0f ? t / Z : 0.0f;
     if (a.mz != nullptr && chunk == 0 && tid == 0) {
-      a.mz[((int64_t)sel * 8 + h) * 2 + 0] = M;
-      a.mz[((int64_t)sel * 8 + h) * 2 + 1] = Z > 0.0f ? 1.0f / Z : 0.0f;
+      a.mz[((int64_t)sel * kMaxHeads + h) * 2 + 0] = M;
+      a.mz[((int64_t)sel * kMaxHeads + h) * 2 + 1] = Z > 0.0f ? 1.0f / Z : 0.0f;
     }
   }
   if (a.sel_zero != nullptr && h == 0 && chunk == 0) {
@@ -521,8 +521,8 @@ __global__ __launch_bounds__(256) void combine_small_kernel(CombineArgs a) {
   *reinterpret_cast<float4*>(a.out + ((int64_t)bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim + 4 * dq) =
       make_float4(o.x * iz, o.y * iz, o.z * iz, o.w * iz);
   if (a.mz != nullptr && dq == 0) {
-    a.mz[((int64_t)sel * 8 + h) * 2 + 0] = m_loc;
-    a.mz[((int64_t)sel * 8 + h) * 2 + 1] = iz;
+    a.mz[((int64_t)sel * kMaxHeads + h) * 2 + 0] = m_loc;
+    a.mz[((int64_t)sel * kMaxHeads + h) * 2 + 1] = iz;
   }
   if (a.sel_zero != nullptr && h == 0) {
     uint32_t* zp = a.sel_zero + (int64_t)sel * a.sel_zero_words;

@@ -34,8 +34,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2v_t;
 
-constexpr int kMThreads = 512;                // one workgroup per CU, 8 waves
-constexpr int kMWaves = kMThreads / 64;
 constexpr int kStepRows = 32;
 constexpr float kMSlack = 8.0f;
 constexpr int kVRow = 272;                    // bytes per staged V row (256 + 16 pad)
@@ -43,7 +41,6 @@ constexpr int kVTile = kStepRows * kVRow;     // per wave
 constexpr int kRecBytes = kMaxRecordSplit * 2;
 constexpr int kHistBytes = kFastBins * 4;
 constexpr int kMergeStride = kPartStride;     // floats per head in the wave merge area: m, z, -, -, o[128]
-constexpr int kMLds = kRecBytes + kHistBytes + kMWaves * kVTile;
 static_assert(8 * kMergeStride * 4 <= kVTile, "a wave's merge record fits its V tile");
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
@@ -218,13 +215,26 @@ struct HeadState {
   float z;        // this lane's share of the softmax denominator
 };
 
+// Max / sum over all 16 lanes w16 of each 16-lane row.
+__device__ __forceinline__ float max16w(float x) {
+  x = max8(x);
+  return fmaxf(x, dpp<kDppRor8>(x));
+}
+__device__ __forceinline__ float sum16w(float x) {
+  x = sum8(x);
+  return x + dpp<kDppRor8>(x);
+}
+
+// Head layout of a step.  kHB head blocks of 16 (lane w16 holds head 16 hb + w16 of
+// block hb); kWide: the bound record sums over all 16 lanes of a block (G > 8),
+// otherwise over lanes 0..7 (G <= 8: the heads 8..15 of the tile are padding).
 // kGather: a sparse-layer step; `base` is the step's first index-row entry and srow
 // holds each entry's row (-1: skipped), so no records are formed.
-template <bool kFp8, bool kGather = false>
-__device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x8_t (&qf)[4], uint8_t* vt,
+template <bool kFp8, bool kGather = false, int kHB = 1, bool kWide = false>
+__device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x8_t (&qf)[kHB][4], uint8_t* vt,
                                              int32_t base, int32_t w_begin, int32_t w_end, uint32_t cand_span,
                                              float scale_log2, int G, int grp, int w16, int lane,
-                                             uint16_t* recs, uint32_t* shist, HeadState& hs,
+                                             uint16_t* recs, uint32_t* shist, HeadState (&hs)[kHB],
                                              const int32_t* srow = nullptr) {
   // V tile -> LDS (row-major, padded rows)
   if constexpr (kFp8) {
@@ -244,11 +254,12 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
     for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(vt + (4 * i + grp) * kVRow + 16 * w16) = s.v[i];
   }
 
-  // QK
-  f32x4_t d[2];
+  // QK (the key fragment of a tile and dim slice serves every head block)
+  f32x4_t d[kHB][2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    d[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb) d[hb][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       uint4 kw;
@@ -260,23 +271,29 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
       } else {
         kw = s.k[t][q];
       }
-      d[t] = mfma16(as_bf16x8(kw), qf[q], d[t]);
+#pragma unroll
+      for (int hb = 0; hb < kHB; ++hb) d[hb][t] = mfma16(as_bf16x8(kw), qf[hb][q], d[hb][t]);
     }
   }
-  float l[2][4];
-  float mx = kNegInf;
+  float l[kHB][2][4];
+  float mx[kHB];
+#pragma unroll
+  for (int hb = 0; hb < kHB; ++hb) mx[hb] = kNegInf;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int32_t row = base + 16 * t + 4 * grp + v;
-      float x = d[t][v] * scale_log2;
-      if constexpr (kFp8) x *= s.ks[t][v];
       bool live;
       if constexpr (kGather) live = srow[row] >= 0;
       else live = row < w_end;
-      l[t][v] = live ? x : kNegInf;
-      mx = fmaxf(mx, l[t][v]);
+#pragma unroll
+      for (int hb = 0; hb < kHB; ++hb) {
+        float x = d[hb][t][v] * scale_log2;
+        if constexpr (kFp8) x *= s.ks[t][v];
+        l[hb][t][v] = live ? x : kNegInf;
+        mx[hb] = fmaxf(mx[hb], l[hb][t][v]);
+      }
     }
 
   // bound records: e = log2 sum over the group's heads of 2^l
@@ -285,10 +302,18 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float lm = w16 < G ? l[t][v] : kNegInf;
-      const float rmax = max8(lm);
-      const float ex = lm != kNegInf ? fast_exp2(lm - rmax) : 0.0f;
-      const float sum = sum8(ex);
+      float lm[kHB];
+      float rmax = kNegInf;
+#pragma unroll
+      for (int hb = 0; hb < kHB; ++hb) {
+        lm[hb] = 16 * hb + w16 < G ? l[hb][t][v] : kNegInf;
+        rmax = fmaxf(rmax, lm[hb]);
+      }
+      rmax = kWide ? max16w(rmax) : max8(rmax);
+      float ex = 0.0f;
+#pragma unroll
+      for (int hb = 0; hb < kHB; ++hb) ex += lm[hb] != kNegInf ? fast_exp2(lm[hb] - rmax) : 0.0f;
+      const float sum = kWide ? sum16w(ex) : sum8(ex);
       const float e = rmax + __builtin_amdgcn_logf(sum);
       const int32_t row = base + 16 * t + 4 * grp + v;
       const uint32_t rel = (uint32_t)(row - w_begin);
@@ -299,39 +324,51 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
       }
     }
 
-  // online softmax of head w16
-  mx = max_groups(mx);
-  const bool up = mx > hs.m + kMSlack;
-  if (wave_any(up)) {
-    const float mn = up ? mx : hs.m;
-    const float alpha = up ? fast_exp2(hs.m - mn) : 1.0f;
+  // online softmax of head 16 hb + w16
+  bool up[kHB];
+  bool up_any = false;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) hs.o[b] *= alpha;
-    hs.z *= alpha;
-    hs.m = mn;
+  for (int hb = 0; hb < kHB; ++hb) {
+    mx[hb] = max_groups(mx[hb]);
+    up[hb] = mx[hb] > hs[hb].m + kMSlack;
+    up_any |= up[hb];
   }
-  float p[2][4];
+  if (wave_any(up_any)) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+    for (int hb = 0; hb < kHB; ++hb) {
+      const float mn = up[hb] ? mx[hb] : hs[hb].m;
+      const float alpha = up[hb] ? fast_exp2(hs[hb].m - mn) : 1.0f;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      p[t][v] = l[t][v] != kNegInf ? fast_exp2(l[t][v] - hs.m) : 0.0f;
-      hs.z += p[t][v];
-      // masked rows: the scale may come from a row past the end (4-row scale loads)
-      if constexpr (kFp8) p[t][v] = l[t][v] != kNegInf ? p[t][v] * s.vs[t][v] : 0.0f;
+      for (int b = 0; b < 8; ++b) hs[hb].o[b] *= alpha;
+      hs[hb].z *= alpha;
+      hs[hb].m = mn;
     }
-
-  // P as bf16 high part + bf16 residual (B operand, k slot u <-> tile u/4, row 4grp + u%4)
-  uint32_t hw[4], lw[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const float x0 = p[u >> 1][2 * (u & 1)];
-    const float x1 = p[u >> 1][2 * (u & 1) + 1];
-    hw[u] = pack_bf16(x0, x1);
-    lw[u] = pack_bf16(x0 - __builtin_bit_cast(float, hw[u] << 16), x1 - __builtin_bit_cast(float, hw[u] & 0xFFFF0000u));
   }
-  const bf16x8_t phi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-  const bf16x8_t plo = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+  bf16x8_t phi[kHB], plo[kHB];
+#pragma unroll
+  for (int hb = 0; hb < kHB; ++hb) {
+    float p[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        p[t][v] = l[hb][t][v] != kNegInf ? fast_exp2(l[hb][t][v] - hs[hb].m) : 0.0f;
+        hs[hb].z += p[t][v];
+        // masked rows: the scale may come from a row past the end (4-row scale loads)
+        if constexpr (kFp8) p[t][v] = l[hb][t][v] != kNegInf ? p[t][v] * s.vs[t][v] : 0.0f;
+      }
+    // P as bf16 high part + bf16 residual (B operand, k slot u <-> tile u/4, row 4grp + u%4)
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float x0 = p[u >> 1][2 * (u & 1)];
+      const float x1 = p[u >> 1][2 * (u & 1) + 1];
+      hw[u] = pack_bf16(x0, x1);
+      lw[u] = pack_bf16(x0 - __builtin_bit_cast(float, hw[u] << 16), x1 - __builtin_bit_cast(float, hw[u] & 0xFFFF0000u));
+    }
+    phi[hb] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    plo[hb] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+  }
 
   // PV: A = V^T of dim block b, rows 4grp..4grp+3 of both tiles (transposed LDS reads)
   const uint8_t* tr0 = vt + (4 * grp + (w16 >> 2)) * kVRow + 8 * (w16 & 3);
@@ -345,14 +382,21 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
     const uint2 w0 = __builtin_bit_cast(uint2, x0);
     const uint2 w1 = __builtin_bit_cast(uint2, x1);
     const bf16x8_t av = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
-    hs.o[b] = mfma16(av, phi, hs.o[b]);
-    hs.o[b] = mfma16(av, plo, hs.o[b]);
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb) {
+      hs[hb].o[b] = mfma16(av, phi[hb], hs[hb].o[b]);
+      hs[hb].o[b] = mfma16(av, plo[hb], hs[hb].o[b]);
+    }
   }
 }
 
-template <bool kFp8, bool kVecScale>
-__global__ __launch_bounds__(kMThreads, 1) void scan_mfma_kernel(ScanArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kMLds];
+// kHB, kWide: head layout (see process_step); kThreads: 512 (8 waves) for up to 16
+// heads, 256 (4 waves, one per SIMD, up to 512 registers a lane) for 32 heads.
+template <bool kFp8, bool kVecScale, int kHB, bool kWide, int kThreads>
+__global__ __launch_bounds__(kThreads, 1) void scan_mfma_kernel(ScanArgs a) {
+  constexpr int kWaves = kThreads / 64;
+  constexpr int kBH = kWide ? 16 : 8;   // heads per block with state (lanes w16 < kBH)
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kRecBytes + kHistBytes + kWaves * kVTile];
   uint16_t* srec = reinterpret_cast<uint16_t*>(lds);
   uint32_t* shist = reinterpret_cast<uint32_t*>(lds + kRecBytes);
   uint8_t* vt_all = lds + kRecBytes + kHistBytes;
@@ -390,14 +434,16 @@ __global__ __launch_bounds__(kMThreads, 1) void scan_mfma_kernel(ScanArgs a) {
   const int nsteps = (w_end - w_begin + kStepRows - 1) / kStepRows;
   __shared__ int step_next;
 
-  // Q^T fragments: head w16, dims 32q + 8grp .. +8
-  bf16x8_t qf[4];
-  {
-    const uint16_t* qh = a.q + ((int64_t)bj * a.Hq + (int64_t)g * a.G + w16) * kHeadDim;
+  // Q^T fragments: head 16 hb + w16, dims of chunk (4q + grp, or kchunk_fp8)
+  bf16x8_t qf[kHB][4];
+#pragma unroll
+  for (int hb = 0; hb < kHB; ++hb) {
+    const int h = 16 * hb + w16;
+    const uint16_t* qh = a.q + ((int64_t)bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int chunk = kFp8 ? kchunk_fp8(q, grp) : 4 * q + grp;
-      qf[q] = as_bf16x8(w16 < a.G ? *reinterpret_cast<const uint4*>(qh + 8 * chunk) : make_uint4(0u, 0u, 0u, 0u));
+      qf[hb][q] = as_bf16x8(h < a.G ? *reinterpret_cast<const uint4*>(qh + 8 * chunk) : make_uint4(0u, 0u, 0u, 0u));
     }
   }
 
@@ -415,29 +461,32 @@ __global__ __launch_bounds__(kMThreads, 1) void scan_mfma_kernel(ScanArgs a) {
   uint32_t cand_span = w0 > p_begin ? (uint32_t)(w0 - p_begin) : 0u;
   cand_span = cand_span < span ? cand_span : span;
 
-  for (int i = tid; i < kFastBins; i += kMThreads) shist[i] = 0u;
-  if (tid == 0) step_next = kMWaves;   // step w is wave w's first
+  for (int i = tid; i < kFastBins; i += kThreads) shist[i] = 0u;
+  if (tid == 0) step_next = kWaves;   // step w is wave w's first
   if (split == 0) {   // the combine kernel sums every split's histogram into these words
     uint32_t* hm = a.hist_merged + sel * kSelWords + kSelHist1Off;
-    for (int i = tid; i < kFastBins; i += kMThreads) hm[i] = 0u;
+    for (int i = tid; i < kFastBins; i += kThreads) hm[i] = 0u;
   }
   __syncthreads();
 
-  HeadState hs;
+  HeadState hs[kHB];
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb) hs.o[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  hs.m = kNegInf;
-  hs.z = 0.0f;
+  for (int hb = 0; hb < kHB; ++hb) {
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) hs[hb].o[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    hs[hb].m = kNegInf;
+    hs[hb].z = 0.0f;
+  }
 
   if (nsteps > 0) {
     const int32_t last = w_end - 1;
     // next step for this wave (wave-uniform); steps taken by a wave increase, so once
     // one is past the end every later one is too
     const bool fixed = a.fixed_steps != 0;
-    int knext = wave + kMWaves;
+    int knext = wave + kWaves;
     auto take = [&]() -> int {
       int k = knext;
-      knext += kMWaves;
+      knext += kWaves;
       if (!fixed && lane == 0)
         k = __hip_atomic_fetch_add(&step_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       return __builtin_amdgcn_readfirstlane(k);
@@ -449,74 +498,79 @@ __global__ __launch_bounds__(kMThreads, 1) void scan_mfma_kernel(ScanArgs a) {
     load_step<kFp8, kVecScale>(s1, kb, vb, ksb, vsb, w_begin + k1 * kStepRows, last, grp, w16, lane);
     // two-buffer ring; every load is issued (rows past the end re-read `last`)
     while (k0 < nsteps) {
-      process_step<kFp8>(s0, qf, vt, w_begin + k0 * kStepRows, w_begin, w_end, cand_span, a.scale_log2, a.G,
-                         grp, w16, lane, srec, shist, hs);
+      process_step<kFp8, false, kHB, kWide>(s0, qf, vt, w_begin + k0 * kStepRows, w_begin, w_end, cand_span,
+                                            a.scale_log2, a.G, grp, w16, lane, srec, shist, hs);
       k0 = take();
       load_step<kFp8, kVecScale>(s0, kb, vb, ksb, vsb, w_begin + k0 * kStepRows, last, grp, w16, lane);
       if (k1 >= nsteps) break;
-      process_step<kFp8>(s1, qf, vt, w_begin + k1 * kStepRows, w_begin, w_end, cand_span, a.scale_log2, a.G,
-                         grp, w16, lane, srec, shist, hs);
+      process_step<kFp8, false, kHB, kWide>(s1, qf, vt, w_begin + k1 * kStepRows, w_begin, w_end, cand_span,
+                                            a.scale_log2, a.G, grp, w16, lane, srec, shist, hs);
       k1 = take();
       load_step<kFp8, kVecScale>(s1, kb, vb, ksb, vsb, w_begin + k1 * kStepRows, last, grp, w16, lane);
     }
   }
 
-  // ---- merge: the 4 row groups (shares of z), then the waves through LDS
-  const float zt = sum_groups(hs.z);
-  float* mrec = reinterpret_cast<float*>(vt);   // this wave's tile: its last reads are done
-  if (w16 < 8) {
-    float* mr = mrec + w16 * kMergeStride;
-#pragma unroll
-    for (int bb = 0; bb < 8; ++bb)
-      *reinterpret_cast<float4*>(mr + 4 + 16 * bb + 4 * grp) =
-          make_float4(hs.o[bb][0], hs.o[bb][1], hs.o[bb][2], hs.o[bb][3]);
-    if (grp == 0) {
-      mr[0] = hs.m;
-      mr[1] = zt;
-    }
-  }
+  // the split's records and key histogram, once every wave is done
   __syncthreads();
-
-  // the split's records and key histogram
   {
     const int cnt = p_end > p_begin ? (int)(p_end - p_begin) : 0;
     uint16_t* grec = a.records + sel * a.logit_stride + p_begin;   // 512-byte aligned
-    for (int i = tid; 2 * i + 1 < cnt; i += kMThreads)
+    for (int i = tid; 2 * i + 1 < cnt; i += kThreads)
       reinterpret_cast<uint32_t*>(grec)[i] = reinterpret_cast<const uint32_t*>(srec)[i];
     if ((cnt & 1) && tid == 0) grec[cnt - 1] = srec[cnt - 1];
     uint32_t* ghist = reinterpret_cast<uint32_t*>(a.hist_part + (sel * a.n_split + split) * kFastBins);
-    for (int i = tid; i < kFastBins / 2; i += kMThreads)
+    for (int i = tid; i < kFastBins / 2; i += kThreads)
       ghist[i] = (shist[2 * i] & 0xFFFFu) | (shist[2 * i + 1] << 16);   // counts < 2^16
   }
 
-  // merge the waves: thread -> (head, 4 dims) for the first 256 threads
-  if (tid < 256) {
-    const int h = tid >> 5;
-    const int dd = (tid & 31) * 4;
-    float Mw = kNegInf;
+  // ---- merge, one head block at a time: the 4 row groups (shares of z), then the
+  // waves through their LDS tiles (each wave's last reads of its tile are done)
+  float* mrec = reinterpret_cast<float*>(vt);
 #pragma unroll
-    for (int w = 0; w < kMWaves; ++w)
-      Mw = fmaxf(Mw, reinterpret_cast<const float*>(vt_all + w * kVTile)[h * kMergeStride]);
-    float Z = 0.0f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int hb = 0; hb < kHB; ++hb) {
+    if (hb > 0) __syncthreads();   // the previous block's merge reads are done
+    const float zt = sum_groups(hs[hb].z);
+    if (w16 < kBH) {
+      float* mr = mrec + w16 * kMergeStride;
 #pragma unroll
-    for (int w = 0; w < kMWaves; ++w) {
-      const float* mr = reinterpret_cast<const float*>(vt_all + w * kVTile) + h * kMergeStride;
-      const float mw = mr[0];
-      const float fw = (mw == kNegInf) ? 0.0f : fast_exp2(mw - Mw);
-      Z += fw * mr[1];
-      const float4 ov = *reinterpret_cast<const float4*>(mr + 4 + dd);
-      acc.x += fw * ov.x;
-      acc.y += fw * ov.y;
-      acc.z += fw * ov.z;
-      acc.w += fw * ov.w;
+      for (int bb = 0; bb < 8; ++bb)
+        *reinterpret_cast<float4*>(mr + 4 + 16 * bb + 4 * grp) =
+            make_float4(hs[hb].o[bb][0], hs[hb].o[bb][1], hs[hb].o[bb][2], hs[hb].o[bb][3]);
+      if (grp == 0) {
+        mr[0] = hs[hb].m;
+        mr[1] = zt;
+      }
     }
-    if (h < a.G) {
-      float* pp = a.part + ((sel * a.n_split + split) * a.G + h) * kPartStride;
-      *reinterpret_cast<float4*>(pp + 4 + dd) = acc;
-      if (dd == 0) {
-        pp[0] = Mw;
-        pp[1] = Z;
+    __syncthreads();
+    // thread -> (head slot, 4 dims)
+    for (int hl = tid >> 5; hl < kBH; hl += kThreads / 32) {
+      const int h = 16 * hb + hl;
+      const int dd = (tid & 31) * 4;
+      float Mw = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        Mw = fmaxf(Mw, reinterpret_cast<const float*>(vt_all + w * kVTile)[hl * kMergeStride]);
+      float Z = 0.0f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* mr = reinterpret_cast<const float*>(vt_all + w * kVTile) + hl * kMergeStride;
+        const float mw = mr[0];
+        const float fw = (mw == kNegInf) ? 0.0f : fast_exp2(mw - Mw);
+        Z += fw * mr[1];
+        const float4 ov = *reinterpret_cast<const float4*>(mr + 4 + dd);
+        acc.x += fw * ov.x;
+        acc.y += fw * ov.y;
+        acc.z += fw * ov.z;
+        acc.w += fw * ov.w;
+      }
+      if (h < a.G) {
+        float* pp = a.part + ((sel * a.n_split + split) * a.G + h) * kPartStride;
+        *reinterpret_cast<float4*>(pp + 4 + dd) = acc;
+        if (dd == 0) {
+          pp[0] = Mw;
+          pp[1] = Z;
+        }
       }
     }
   }
@@ -530,13 +584,14 @@ __global__ __launch_bounds__(kMThreads, 1) void scan_mfma_kernel(ScanArgs a) {
 // w+8, ...: a fixed share, so the output is bitwise reproducible), merge through LDS
 // and write the normalised output, so no split combine follows.
 constexpr int kGMaxS = 4096;   // index row length bound (checked on the host)
-constexpr int kGLds = kMWaves * kVTile + kGMaxS * 4;
 
-template <bool kFp8>
-__global__ __launch_bounds__(kMThreads, 1) void gather_mfma_kernel(ScanArgs a, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kGLds];
+template <bool kFp8, int kHB, bool kWide, int kThreads>
+__global__ __launch_bounds__(kThreads, 1) void gather_mfma_kernel(ScanArgs a, float* __restrict__ out) {
+  constexpr int kWaves = kThreads / 64;
+  constexpr int kBH = kWide ? 16 : 8;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kVTile + kGMaxS * 4];
   uint8_t* vt_all = lds;
-  int32_t* srow = reinterpret_cast<int32_t*>(lds + kMWaves * kVTile);
+  int32_t* srow = reinterpret_cast<int32_t*>(lds + kWaves * kVTile);
 
   const int g = blockIdx.y;
   const int bj = blockIdx.z;
@@ -558,17 +613,19 @@ __global__ __launch_bounds__(kMThreads, 1) void gather_mfma_kernel(ScanArgs a, f
 
   // the index row, with entries that name no visible row turned into -1
   const int32_t* irow = a.idx + sel * a.S;
-  for (int e = tid; e < nsteps * kStepRows; e += kMThreads) {
+  for (int e = tid; e < nsteps * kStepRows; e += kThreads) {
     const int32_t t = e < a.S ? irow[e] : -1;
     srow[e] = (t >= 0 && t < n) ? t : -1;
   }
-  bf16x8_t qf[4];
-  {
-    const uint16_t* qh = a.q + ((int64_t)bj * a.Hq + (int64_t)g * a.G + w16) * kHeadDim;
+  bf16x8_t qf[kHB][4];
+#pragma unroll
+  for (int hb = 0; hb < kHB; ++hb) {
+    const int h = 16 * hb + w16;
+    const uint16_t* qh = a.q + ((int64_t)bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int chunk = kFp8 ? kchunk_fp8(q, grp) : 4 * q + grp;
-      qf[q] = as_bf16x8(w16 < a.G ? *reinterpret_cast<const uint4*>(qh + 8 * chunk) : make_uint4(0u, 0u, 0u, 0u));
+      qf[hb][q] = as_bf16x8(h < a.G ? *reinterpret_cast<const uint4*>(qh + 8 * chunk) : make_uint4(0u, 0u, 0u, 0u));
     }
   }
   const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
@@ -579,95 +636,125 @@ __global__ __launch_bounds__(kMThreads, 1) void gather_mfma_kernel(ScanArgs a, f
   const float* vsb = kFp8 ? a.v_scale + head_row0 : nullptr;
   __syncthreads();
 
-  HeadState hs;
+  HeadState hs[kHB];
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb) hs.o[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  hs.m = kNegInf;
-  hs.z = 0.0f;
+  for (int hb = 0; hb < kHB; ++hb) {
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) hs[hb].o[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    hs[hb].m = kNegInf;
+    hs[hb].z = 0.0f;
+  }
 
   if (wave < nsteps) {
-    // two-buffer ring over steps wave, wave+8, ...; loads past the last step re-read it
+    // two-buffer ring over steps wave, wave + kWaves, ...; loads past the last step re-read it
     const int klast = nsteps - 1;
     StepBuf<kFp8> s0, s1;
-    int k0 = wave, k1 = wave + kMWaves;
+    int k0 = wave, k1 = wave + kWaves;
     load_step_gather<kFp8>(s0, kb, vb, ksb, vsb, srow, k0 * kStepRows, grp, w16, lane);
     load_step_gather<kFp8>(s1, kb, vb, ksb, vsb, srow, min(k1, klast) * kStepRows, grp, w16, lane);
     while (k0 < nsteps) {
-      process_step<kFp8, true>(s0, qf, vt, k0 * kStepRows, 0, 0, 0u, a.scale_log2, a.G, grp, w16, lane, nullptr,
-                               nullptr, hs, srow);
-      k0 += 2 * kMWaves;
+      process_step<kFp8, true, kHB, kWide>(s0, qf, vt, k0 * kStepRows, 0, 0, 0u, a.scale_log2, a.G, grp, w16, lane,
+                                           nullptr, nullptr, hs, srow);
+      k0 += 2 * kWaves;
       load_step_gather<kFp8>(s0, kb, vb, ksb, vsb, srow, min(k0, klast) * kStepRows, grp, w16, lane);
       if (k1 >= nsteps) break;
-      process_step<kFp8, true>(s1, qf, vt, k1 * kStepRows, 0, 0, 0u, a.scale_log2, a.G, grp, w16, lane, nullptr,
-                               nullptr, hs, srow);
-      k1 += 2 * kMWaves;
+      process_step<kFp8, true, kHB, kWide>(s1, qf, vt, k1 * kStepRows, 0, 0, 0u, a.scale_log2, a.G, grp, w16, lane,
+                                           nullptr, nullptr, hs, srow);
+      k1 += 2 * kWaves;
       load_step_gather<kFp8>(s1, kb, vb, ksb, vsb, srow, min(k1, klast) * kStepRows, grp, w16, lane);
     }
   }
 
-  // merge the row groups, then the waves through LDS; out = o / Z (0 when no entry is live)
-  const float zt = sum_groups(hs.z);
+  // merge, one head block at a time: the row groups, then the waves through LDS;
+  // out = o / Z (0 when no entry is live)
   float* mrec = reinterpret_cast<float*>(vt);   // this wave's tile: its last reads are done
-  if (w16 < 8) {
-    float* mr = mrec + w16 * kMergeStride;
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb)
-      *reinterpret_cast<float4*>(mr + 4 + 16 * bb + 4 * grp) =
-          make_float4(hs.o[bb][0], hs.o[bb][1], hs.o[bb][2], hs.o[bb][3]);
-    if (grp == 0) {
-      mr[0] = hs.m;
-      mr[1] = zt;
+  for (int hb = 0; hb < kHB; ++hb) {
+    if (hb > 0) __syncthreads();
+    const float zt = sum_groups(hs[hb].z);
+    if (w16 < kBH) {
+      float* mr = mrec + w16 * kMergeStride;
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb)
+        *reinterpret_cast<float4*>(mr + 4 + 16 * bb + 4 * grp) =
+            make_float4(hs[hb].o[bb][0], hs[hb].o[bb][1], hs[hb].o[bb][2], hs[hb].o[bb][3]);
+      if (grp == 0) {
+        mr[0] = hs[hb].m;
+        mr[1] = zt;
+      }
     }
-  }
-  __syncthreads();
-  if (tid < 256) {
-    const int h = tid >> 5;
-    const int dd = (tid & 31) * 4;
-    float Mw = kNegInf;
+    __syncthreads();
+    for (int hl = tid >> 5; hl < kBH; hl += kThreads / 32) {
+      const int h = 16 * hb + hl;
+      const int dd = (tid & 31) * 4;
+      float Mw = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kMWaves; ++w)
-      Mw = fmaxf(Mw, reinterpret_cast<const float*>(vt_all + w * kVTile)[h * kMergeStride]);
-    float Z = 0.0f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int w = 0; w < kWaves; ++w)
+        Mw = fmaxf(Mw, reinterpret_cast<const float*>(vt_all + w * kVTile)[hl * kMergeStride]);
+      float Z = 0.0f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int w = 0; w < kMWaves; ++w) {
-      const float* mr = reinterpret_cast<const float*>(vt_all + w * kVTile) + h * kMergeStride;
-      const float mw = mr[0];
-      const float fw = (mw == kNegInf) ? 0.0f : fast_exp2(mw - Mw);
-      Z += fw * mr[1];
-      const float4 ov = *reinterpret_cast<const float4*>(mr + 4 + dd);
-      acc.x += fw * ov.x;
-      acc.y += fw * ov.y;
-      acc.z += fw * ov.z;
-      acc.w += fw * ov.w;
-    }
-    if (h < a.G) {
-      const float iz = Z > 0.0f ? 1.0f / Z : 0.0f;
-      float* op = out + ((int64_t)bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim + dd;
-      *reinterpret_cast<float4*>(op) = make_float4(acc.x * iz, acc.y * iz, acc.z * iz, acc.w * iz);
+      for (int w = 0; w < kWaves; ++w) {
+        const float* mr = reinterpret_cast<const float*>(vt_all + w * kVTile) + hl * kMergeStride;
+        const float mw = mr[0];
+        const float fw = (mw == kNegInf) ? 0.0f : fast_exp2(mw - Mw);
+        Z += fw * mr[1];
+        const float4 ov = *reinterpret_cast<const float4*>(mr + 4 + dd);
+        acc.x += fw * ov.x;
+        acc.y += fw * ov.y;
+        acc.z += fw * ov.z;
+        acc.w += fw * ov.w;
+      }
+      if (h < a.G) {
+        const float iz = Z > 0.0f ? 1.0f / Z : 0.0f;
+        float* op = out + ((int64_t)bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim + dd;
+        *reinterpret_cast<float4*>(op) = make_float4(acc.x * iz, acc.y * iz, acc.z * iz, acc.w * iz);
+      }
     }
   }
 }
 
 }  // namespace
 
+// Head layout by group size: G <= 8 (8-lane records, 8 waves), G <= 16 (16-lane
+// records, 8 waves), G <= 32 (two head blocks, 4 waves with up to 512 registers).
+template <bool kFp8, bool kVec>
+static void launch_scan_g(const ScanArgs& a, dim3 grid, hipStream_t st) {
+  if (a.G <= 8)
+    hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 1, false, 512>), grid, dim3(512), 0, st, a);
+  else if (a.G <= 16)
+    hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 1, true, 512>), grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 2, true, 256>), grid, dim3(256), 0, st, a);
+}
+
 hipError_t launch_scan_mfma(const ScanArgs& a, bool fp8, int B, hipStream_t st) {
   dim3 grid(a.n_split, a.Hkv, B * a.Lq);
   if (fp8 && a.cap % 4 == 0)
-    hipLaunchKernelGGL((scan_mfma_kernel<true, true>), grid, dim3(kMThreads), 0, st, a);
+    launch_scan_g<true, true>(a, grid, st);
   else if (fp8)
-    hipLaunchKernelGGL((scan_mfma_kernel<true, false>), grid, dim3(kMThreads), 0, st, a);
+    launch_scan_g<true, false>(a, grid, st);
   else
-    hipLaunchKernelGGL((scan_mfma_kernel<false, false>), grid, dim3(kMThreads), 0, st, a);
+    launch_scan_g<false, false>(a, grid, st);
   return hipGetLastError();
+}
+
+template <bool kFp8>
+static void launch_gather_g(const ScanArgs& a, float* out, dim3 grid, hipStream_t st) {
+  if (a.G <= 8)
+    hipLaunchKernelGGL((gather_mfma_kernel<kFp8, 1, false, 512>), grid, dim3(512), 0, st, a, out);
+  else if (a.G <= 16)
+    hipLaunchKernelGGL((gather_mfma_kernel<kFp8, 1, true, 512>), grid, dim3(512), 0, st, a, out);
+  else
+    hipLaunchKernelGGL((gather_mfma_kernel<kFp8, 2, true, 256>), grid, dim3(256), 0, st, a, out);
 }
 
 hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool fp8, int B, hipStream_t st) {
   dim3 grid(1, a.Hkv, B * a.Lq);
   if (fp8)
-    hipLaunchKernelGGL((gather_mfma_kernel<true>), grid, dim3(kMThreads), 0, st, a, out);
+    launch_gather_g<true>(a, out, grid, st);
   else
-    hipLaunchKernelGGL((gather_mfma_kernel<false>), grid, dim3(kMThreads), 0, st, a, out);
+    launch_gather_g<false>(a, out, grid, st);
   return hipGetLastError();
 }
 

@@ -130,8 +130,8 @@ __global__ __launch_bounds__(kThreads) void groupsum_kernel(SelectArgs a) {
   float Mh[8], iz[8];
 #pragma unroll
   for (int h = 0; h < 8; ++h) {
-    Mh[h] = a.mz[(sel * 8 + h) * 2 + 0];
-    iz[h] = a.mz[(sel * 8 + h) * 2 + 1];
+    Mh[h] = a.mz[(sel * kMaxHeads + h) * 2 + 0];
+    iz[h] = a.mz[(sel * kMaxHeads + h) * 2 + 1];
   }
   __syncthreads();
 
@@ -423,8 +423,8 @@ __global__ __launch_bounds__(kBlkThreads) void block_select_kernel(SelectArgs a)
     float Mh[8], iz[8];
 #pragma unroll
     for (int h = 0; h < 8; ++h) {
-      Mh[h] = a.mz[(sel * 8 + h) * 2 + 0];
-      iz[h] = a.mz[(sel * 8 + h) * 2 + 1];
+      Mh[h] = a.mz[(sel * kMaxHeads + h) * 2 + 0];
+      iz[h] = a.mz[(sel * kMaxHeads + h) * 2 + 1];
     }
     const int sub = bs / 64;
     const int nsub = (n + 63) / 64;   // 64-blocks holding visible positions

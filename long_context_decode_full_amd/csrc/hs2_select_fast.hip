@@ -58,8 +58,8 @@ __device__ __forceinline__ uint32_t* sel_block(const FastSelArgs& a, int64_t sel
 __device__ __forceinline__ void load_mz(const FastSelArgs& a, int64_t sel, float (&Mh)[8], float (&iz)[8]) {
 #pragma unroll
   for (int h = 0; h < 8; ++h) {
-    Mh[h] = a.mz[(sel * 8 + h) * 2 + 0];
-    iz[h] = a.mz[(sel * 8 + h) * 2 + 1];
+    Mh[h] = a.mz[(sel * kMaxHeads + h) * 2 + 0];
+    iz[h] = a.mz[(sel * kMaxHeads + h) * 2 + 1];
   }
 }
 
@@ -135,7 +135,9 @@ __device__ __forceinline__ int32_t key_pos(uint64_t key) {
 //              the bin's upper edge), so it is selected whatever the exact scores are.
 // Certain positions get an infinite score key without re-scoring; only the uncertain
 // candidates re-read their key rows.  Keys stay in position order per chunk.
-template <bool kFp8, int R>   // R = records per thread = chunk_len / 256 (8..64)
+// kMB: more than 8 query heads per KV head; the exact scores are summed over blocks of
+// 8 heads (one query load per block), per candidate in LDS.
+template <bool kFp8, int R, bool kMB>   // R = records per thread = chunk_len / 256 (8..64)
 __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   const int64_t sel = blockIdx.x / (uint32_t)a.cand_wgs;
   const int wg = (int)(blockIdx.x % (uint32_t)a.cand_wgs);
@@ -172,12 +174,20 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   const uint32_t ebits = half_bits_of_key(tb << kFastShift);                  // smallest record in the bin
   const uint32_t ebits_hi = half_bits_of_key(((tb + 1) << kFastShift) - 1);   // largest
   float lwmin = __builtin_huge_valf(), lwmax = -__builtin_huge_valf();
-#pragma unroll
-  for (int h = 0; h < 8; ++h) {
-    if (h < a.G) {
-      const float lw = __builtin_amdgcn_logf(iz[h]) - Mh[h];   // log2 w_h
+  if constexpr (kMB) {
+    for (int h = 0; h < a.G; ++h) {
+      const float lw = __builtin_amdgcn_logf(a.mz[(sel * kMaxHeads + h) * 2 + 1]) - a.mz[(sel * kMaxHeads + h) * 2];
       lwmin = fminf(lwmin, lw);
       lwmax = fmaxf(lwmax, lw);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      if (h < a.G) {
+        const float lw = __builtin_amdgcn_logf(iz[h]) - Mh[h];   // log2 w_h
+        lwmin = fminf(lwmin, lw);
+        lwmax = fmaxf(lwmax, lw);
+      }
     }
   }
   // candidate  <=>  e + u(e) + log2 max w  >=  e* - u(e*) + log2 min w  (with slack)
@@ -264,26 +274,65 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
     // Batches of kRescoreBatch wave steps: all their key loads are issued before the
     // first row is scored, so a long candidate list does not wait on one load per step.
     constexpr int kRescoreBatch = 4;
-    for (int i0 = wave * 4; i0 < unc; i0 += 16 * kRescoreBatch) {
-      RowData d[kRescoreBatch];
-      int32_t tpos[kRescoreBatch];
-      int tidx[kRescoreBatch];
+    if constexpr (!kMB) {
+      for (int i0 = wave * 4; i0 < unc; i0 += 16 * kRescoreBatch) {
+        RowData d[kRescoreBatch];
+        int32_t tpos[kRescoreBatch];
+        int tidx[kRescoreBatch];
 #pragma unroll
-      for (int u = 0; u < kRescoreBatch; ++u) {
-        const int i = i0 + 16 * u + rgrp;
-        // past the end: re-read the batch's first row (valid), the result is dropped
-        tidx[u] = ulist[i < unc ? i : i0];
-        tpos[u] = (int32_t)(c0 + cpos[tidx[u]]);
-        load_key<kFp8>(kb, ksb, (uint32_t)tpos[u], r, d[u]);
-      }
+        for (int u = 0; u < kRescoreBatch; ++u) {
+          const int i = i0 + 16 * u + rgrp;
+          // past the end: re-read the batch's first row (valid), the result is dropped
+          tidx[u] = ulist[i < unc ? i : i0];
+          tpos[u] = (int32_t)(c0 + cpos[tidx[u]]);
+          load_key<kFp8>(kb, ksb, (uint32_t)tpos[u], r, d[u]);
+        }
 #pragma unroll
-      for (int u = 0; u < kRescoreBatch; ++u) {
-        const int i = i0 + 16 * u + rgrp;
-        const float l = row_logit<kFp8>(qp, d[u], a.scale_log2);
-        const float part = ((r & 1) == 0 && hown < a.G) ? fast_exp2(l - Mown) * izown : 0.0f;
-        const float s = rowgroup_sum16(part);
-        if (i < unc && r == 0) a.cand_keys[slot0 + tidx[u]] = cand_key(__float_as_uint(s), tpos[u]);
+        for (int u = 0; u < kRescoreBatch; ++u) {
+          const int i = i0 + 16 * u + rgrp;
+          const float l = row_logit<kFp8>(qp, d[u], a.scale_log2);
+          const float part = ((r & 1) == 0 && hown < a.G) ? fast_exp2(l - Mown) * izown : 0.0f;
+          const float s = rowgroup_sum16(part);
+          if (i < unc && r == 0) a.cand_keys[slot0 + tidx[u]] = cand_key(__float_as_uint(s), tpos[u]);
+        }
       }
+    } else {
+      // blocks of 8 heads; candidate i is always scored by the same lane group, so its
+      // LDS sum needs no barrier between blocks
+      __shared__ float ssum[clen];
+      const int nb = (a.G + 7) / 8;
+      for (int blk = 0; blk < nb; ++blk) {
+        const int gb = min(8, a.G - 8 * blk);
+        if (blk > 0)
+          load_query(a.q + (bj * a.Hq + (int64_t)g * a.G + 8 * blk) * kHeadDim, gb, r, qp);
+        const int hg = 8 * blk + hown;   // this lane's head
+        const float Mb = hown < gb ? a.mz[(sel * kMaxHeads + hg) * 2] : 0.0f;
+        const float izb = hown < gb ? a.mz[(sel * kMaxHeads + hg) * 2 + 1] : 0.0f;
+        for (int i0 = wave * 4; i0 < unc; i0 += 16 * kRescoreBatch) {
+          RowData d[kRescoreBatch];
+          int32_t tpos[kRescoreBatch];
+#pragma unroll
+          for (int u = 0; u < kRescoreBatch; ++u) {
+            const int i = i0 + 16 * u + rgrp;
+            tpos[u] = (int32_t)(c0 + cpos[ulist[i < unc ? i : i0]]);
+            load_key<kFp8>(kb, ksb, (uint32_t)tpos[u], r, d[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < kRescoreBatch; ++u) {
+            const int i = i0 + 16 * u + rgrp;
+            const float l = row_logit<kFp8>(qp, d[u], a.scale_log2);
+            const float part = ((r & 1) == 0 && hown < gb) ? fast_exp2(l - Mb) * izb : 0.0f;
+            const float s = rowgroup_sum16(part);
+            if (i < unc && r == 0) ssum[i] = blk == 0 ? s : ssum[i] + s;
+          }
+        }
+      }
+      __syncthreads();
+      for (int i = tid; i < unc; i += kThreads) {
+        const int ti = ulist[i];
+        a.cand_keys[slot0 + ti] = cand_key(__float_as_uint(ssum[i]), (int32_t)(c0 + cpos[ti]));
+      }
+      if (a.G > 8) load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);   // next chunk: block 0
     }
   }
 }
@@ -553,11 +602,20 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
 template <bool kFp8>
 void launch_candidates_r(const FastSelArgs& a, hipStream_t st) {
   const dim3 grid((uint32_t)((uint64_t)a.cand_wgs * (uint64_t)a.n_sel));
+  if (a.G > 8) {
+    switch (a.chunk_len / kThreads) {
+      case 8: hipLaunchKernelGGL((candidate_kernel<kFp8, 8, true>), grid, dim3(kThreads), 0, st, a); break;
+      case 16: hipLaunchKernelGGL((candidate_kernel<kFp8, 16, true>), grid, dim3(kThreads), 0, st, a); break;
+      case 32: hipLaunchKernelGGL((candidate_kernel<kFp8, 32, true>), grid, dim3(kThreads), 0, st, a); break;
+      default: hipLaunchKernelGGL((candidate_kernel<kFp8, 64, true>), grid, dim3(kThreads), 0, st, a); break;
+    }
+    return;
+  }
   switch (a.chunk_len / kThreads) {
-    case 8: hipLaunchKernelGGL((candidate_kernel<kFp8, 8>), grid, dim3(kThreads), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((candidate_kernel<kFp8, 16>), grid, dim3(kThreads), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((candidate_kernel<kFp8, 32>), grid, dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((candidate_kernel<kFp8, 64>), grid, dim3(kThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((candidate_kernel<kFp8, 8, false>), grid, dim3(kThreads), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((candidate_kernel<kFp8, 16, false>), grid, dim3(kThreads), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((candidate_kernel<kFp8, 32, false>), grid, dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((candidate_kernel<kFp8, 64, false>), grid, dim3(kThreads), 0, st, a); break;
   }
 }
 

@@ -60,7 +60,10 @@ def test_desc_struct_layout_matches_header():
     (dict(batch=0), hs2.HS2_ERR_INVALID_ARG),
     (dict(q_len=0), hs2.HS2_ERR_INVALID_ARG),
     (dict(n_q_heads=30), hs2.HS2_ERR_INVALID_ARG),          # Hq % Hkv != 0
-    (dict(n_q_heads=64, n_kv_heads=4), hs2.HS2_ERR_UNSUPPORTED),   # G = 16 > 8
+    (dict(n_q_heads=64, n_kv_heads=4), hs2.HS2_OK),              # G = 16: wide groups
+    (dict(n_q_heads=32, n_kv_heads=1), hs2.HS2_OK),              # MQA, G = 32
+    (dict(n_q_heads=64, n_kv_heads=1), hs2.HS2_ERR_UNSUPPORTED), # G = 64 > 32
+    (dict(n_q_heads=32, n_kv_heads=1, select_mode=1), hs2.HS2_ERR_UNSUPPORTED),  # G > 8: token mode only
     (dict(head_dim=64), hs2.HS2_ERR_UNSUPPORTED),
     (dict(kv_dtype=7), hs2.HS2_ERR_INVALID_ARG),
     (dict(max_ctx_len=(1 << 20) + 1), hs2.HS2_ERR_INVALID_ARG),   # beyond capacity

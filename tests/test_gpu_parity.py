@@ -178,6 +178,37 @@ def test_chunk_shapes(lq, ctx, hq, hkv):
     run_and_compare(w, f"chunk-lq{lq}", tokens=toks)
 
 
+@pytest.mark.parametrize("hq,hkv,kv,ctx", [(32, 1, "bf16", [7000, 3100]), (64, 4, "bf16", [5000]),
+                                           (12, 1, "bf16", [4500]), (32, 1, "fp8", [6200]),
+                                           (24, 2, "fp8", [3000, 9000])])
+def test_wide_groups_decode(hq, hkv, kv, ctx):
+    """More than 8 query heads per KV head (MQA at G = 32; G = 16, 12): one index set
+    per KV head from all G heads' probabilities; matrix-core scan with 16-head blocks,
+    one-launch gather, block-wise exact re-scoring."""
+    w = wl.Workload(f"G{hq // hkv} {kv}", len(ctx), 1, hq, hkv, ctx_lens=ctx, n_needles=16, kv_dtype=kv,
+                    seed=2500 + hq + hkv)
+    run_and_compare(w, f"wide-G{hq // hkv}-{kv}")
+
+
+def test_mqa_query_chunk():
+    """MQA with several query tokens: the decode scan once per token."""
+    w = wl.Workload("mqa chunk", 2, 6, 32, 1, ctx_lens=[2600, 5000], n_needles=8, seed=2520)
+    run_and_compare(w, "mqa-chunk")
+
+
+def test_wide_group_logits_path_unsupported():
+    """Requesting all probabilities needs the logits path, which keeps 8 head slots:
+    more than 8 heads per KV head is reported as unsupported, nothing is launched."""
+    from long_context_decode_full_amd import HS2_ERR_UNSUPPORTED, Hs2Error
+    from long_context_decode_full_amd.runner import HybridBlockDevice
+    w = wl.Workload("mqa probs", 1, 1, 32, 1, ctx_lens=[3000], n_needles=4, seed=2530)
+    inp = wl.make_inputs(w)
+    dev = HybridBlockDevice(inp, with_probs=True)
+    with pytest.raises(Hs2Error) as err:
+        dev.full()
+    assert err.value.status == HS2_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("cap", [5203, 5204])
 def test_fp8_scale_alignment(cap):
     """fp8 scales are read 4 rows at a time when the capacity is a multiple of 4 (16-byte
