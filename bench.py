@@ -156,7 +156,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps first: the GPU reaches its sustained clocks after a few tens of ms")
     ap.add_argument("--workload", default="million",
-                    help="tiny | batched | fp8_256k | million | chunk")
+                    help="tiny | batched | fp8_256k | million | chunk | mqa_million")
     ap.add_argument("--select", default="token", choices=["token", "block"],
                     help="token selection (window 128 + top-k 1024) or the first-generation block "
                          "comparator (18 blocks of 64, no forced window)")

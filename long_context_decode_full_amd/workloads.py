@@ -61,8 +61,9 @@ class Workload:
 
 
 def standard_workloads():
-    """The five configurations: tiny decode, batched decode, fp8 long decode,
-    million-token decode and the ragged 64-token chunk."""
+    """The five configurations (tiny decode, batched decode, fp8 long decode,
+    million-token decode, the ragged 64-token chunk) and the MQA variant of the
+    million-token decode (one KV head for all 32 query heads)."""
     return {
         "tiny": Workload("tiny decode", 1, 1, 16, 2, ctx_lens=[4096], n_needles=8, seed=1001),
         "batched": Workload("batched decode", 8, 1, 32, 4, ctx_lens=[32768] * 8, n_needles=64,
@@ -73,6 +74,8 @@ def standard_workloads():
                             n_needles=1024, drift_sigma=0.01, drift_block=4096, seed=1004),
         "chunk": Workload("ragged 64-token chunk", 16, 64, 32, 4, ctx_log_uniform=(8192, 524288),
                           n_needles=64, seed=1005),
+        "mqa_million": Workload("MQA million-token decode", 1, 1, 32, 1, ctx_lens=[1048576],
+                                n_needles=1024, drift_sigma=0.01, drift_block=4096, seed=1006),
     }
 
 

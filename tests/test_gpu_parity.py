@@ -143,6 +143,12 @@ def test_million_token_decode():
     run_and_compare(w, "million")
 
 
+def test_mqa_million_token_decode():
+    """MQA at the million-token context: one index set from all 32 heads."""
+    w = wl.standard_workloads()["mqa_million"]
+    run_and_compare(w, "mqa-million")
+
+
 @pytest.mark.parametrize("mode", ["token", "block"])
 def test_chunk_full_config(mode):
     """The ragged 64-token chunk at full size (16 sequences, contexts 8K-512K) in the
