@@ -161,7 +161,9 @@ Layout make_layout(const hs2_attn_desc* d) {
   L.n_chunks = (int32_t)ceil_div(d->max_ctx_len, kSelectChunk);
 
   const int64_t n = L.n_sel;
-  const int64_t nsplit_max = std::max({L.n_split, L.n_split_sp, L.rec_n_split});
+  // (the matrix-core split gather of wide groups takes 128-entry splits)
+  const int64_t nsplit_max = std::max({(int64_t)L.n_split, (int64_t)L.n_split_sp, (int64_t)L.rec_n_split,
+                                       ceil_div(L.S, 128)});
   // The logits path keeps 36 bytes per (selection row, position); beyond kMaxLogitsBytes
   // (chunk configurations with long contexts) it is not offered and not reserved.
   L.logits_ok = (double)n * (double)L.logit_stride * 36.0 <= (double)kMaxLogitsBytes;
@@ -500,17 +502,29 @@ HS2_API hs2_status hs2_sparse_attn(const hs2_attn_desc* desc, const void* q, con
   // the 64-token chunks.  With fewer rows (decode) its 4-5 dependent steps per wave
   // are latency-bound, and the split VALU gather + combine is faster.
   // HS2_SPARSE_FUSED=1 / 0 forces either path.
+  // More than 8 heads per KV head with few rows: the matrix-core gather over splits of
+  // one step per wave (256 entries with 8 waves, 128 with the 4-wave 32-head layout)
+  // writing partials, then the combine.
   const int64_t rows = (int64_t)desc->batch * desc->q_len * desc->n_kv_heads;
   const int fused_env = env_int("HS2_SPARSE_FUSED", -1);
-  const bool fused = wide_group(desc) || (fused_env >= 0 ? fused_env != 0 : rows >= kFusedSparseRows);
+  const bool fused = fused_env >= 0 ? fused_env != 0 : rows >= kFusedSparseRows;
   TimerRec rec;
   const bool timed = timer_begin(stream, 1, &rec);
   if (fused) {
+    sa.n_split = 1;
+    sa.split_len = L.S;
     const hipError_t e = launch_gather_mfma(sa, out, fp8, desc->batch, stream);
     if (timed) timer_end(stream, &rec);
     return e == hipSuccess ? HS2_OK : HS2_ERR_LAUNCH;
   }
-  hipError_t e = launch_scan_sparse(sa, fp8, desc->batch, stream);
+  hipError_t e;
+  if (wide_group(desc)) {
+    sa.split_len = L.G > 16 ? 128 : 256;
+    sa.n_split = (int32_t)ceil_div(L.S, sa.split_len);
+    e = launch_gather_mfma(sa, nullptr, fp8, desc->batch, stream);
+  } else {
+    e = launch_scan_sparse(sa, fp8, desc->batch, stream);
+  }
   if (timed) timer_end(stream, &rec);
   if (e != hipSuccess) return HS2_ERR_LAUNCH;
 
@@ -521,7 +535,7 @@ HS2_API hs2_status hs2_sparse_attn(const hs2_attn_desc* desc, const void* q, con
   ca.Hkv = desc->n_kv_heads;
   ca.G = L.G;
   ca.Hq = desc->n_q_heads;
-  ca.n_split = L.n_split_sp;
+  ca.n_split = sa.n_split;
   if (launch_combine(ca, stream) != hipSuccess) return HS2_ERR_LAUNCH;
   return HS2_OK;
 }

@@ -143,7 +143,9 @@ hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st
 hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t st);
 hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st);
 hipError_t launch_scan_mfma(const ScanArgs& a, bool fp8, int B, hipStream_t st);
-// sparse layer, one workgroup per (query token, KV head), normalised output (S <= 4096)
+// sparse layer on the matrix cores, one workgroup per (query token, KV head, split of
+// a.split_len index entries); out != nullptr (one split): normalised output, else
+// partials in a.part for launch_combine (S <= 4096)
 hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool fp8, int B, hipStream_t st);
 hipError_t launch_chunk_mfma(const ScanArgs& a, int B, hipStream_t st);
 hipError_t launch_scan_sparse(const ScanArgs& a, bool fp8, int B, hipStream_t st);

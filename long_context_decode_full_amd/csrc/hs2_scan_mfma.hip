@@ -579,10 +579,11 @@ __global__ __launch_bounds__(kThreads, 1) void scan_mfma_kernel(ScanArgs a) {
 // ---- Sparse Attention layer (HySparse2 article, section 02 "KV Reuse": the sparse
 // layers attend with their own queries over the rows of the shared cache that the
 // full layer's index set names; section 03: window and global rows share one
-// softmax).  One workgroup per (query token, KV head): its 8 waves gather the index
-// row's entries 32 at a time with the step code of the scan (wave w takes steps w,
-// w+8, ...: a fixed share, so the output is bitwise reproducible), merge through LDS
-// and write the normalised output, so no split combine follows.
+// softmax).  One workgroup per (query token, KV head, split of the index row): its
+// waves gather the entries 32 at a time with the step code of the scan (wave w takes
+// steps w, w + waves, ...: a fixed share, so the output is bitwise reproducible) and
+// merge through LDS.  With one split (out != nullptr) the workgroup writes the
+// normalised output and no combine follows; with several it writes partials.
 constexpr int kGMaxS = 4096;   // index row length bound (checked on the host)
 
 template <bool kFp8, int kHB, bool kWide, int kThreads>
@@ -593,6 +594,7 @@ __global__ __launch_bounds__(kThreads, 1) void gather_mfma_kernel(ScanArgs a, fl
   uint8_t* vt_all = lds;
   int32_t* srow = reinterpret_cast<int32_t*>(lds + kWaves * kVTile);
 
+  const int split = blockIdx.x;   // entries [split * split_len, +split_len) of the index row
   const int g = blockIdx.y;
   const int bj = blockIdx.z;
   const int b = bj / a.Lq;
@@ -609,12 +611,14 @@ __global__ __launch_bounds__(kThreads, 1) void gather_mfma_kernel(ScanArgs a, fl
   ctx = ctx < 0 ? 0 : (ctx > a.ctx_max ? a.ctx_max : ctx);
   int64_t n = ctx - a.Lq + j + 1;
   n = n < 0 ? 0 : n;
-  const int nsteps = (a.S + kStepRows - 1) / kStepRows;
+  const int e_begin = split * a.split_len;
+  const int e_count = max(0, min(a.split_len, a.S - e_begin));
+  const int nsteps = (e_count + kStepRows - 1) / kStepRows;
 
-  // the index row, with entries that name no visible row turned into -1
-  const int32_t* irow = a.idx + sel * a.S;
+  // this split's entries of the index row, those naming no visible row turned into -1
+  const int32_t* irow = a.idx + sel * a.S + e_begin;
   for (int e = tid; e < nsteps * kStepRows; e += kThreads) {
-    const int32_t t = e < a.S ? irow[e] : -1;
+    const int32_t t = e < e_count ? irow[e] : -1;
     srow[e] = (t >= 0 && t < n) ? t : -1;
   }
   bf16x8_t qf[kHB][4];
@@ -706,9 +710,18 @@ __global__ __launch_bounds__(kThreads, 1) void gather_mfma_kernel(ScanArgs a, fl
         acc.w += fw * ov.w;
       }
       if (h < a.G) {
-        const float iz = Z > 0.0f ? 1.0f / Z : 0.0f;
-        float* op = out + ((int64_t)bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim + dd;
-        *reinterpret_cast<float4*>(op) = make_float4(acc.x * iz, acc.y * iz, acc.z * iz, acc.w * iz);
+        if (out != nullptr) {   // the whole row in this workgroup: normalised output
+          const float iz = Z > 0.0f ? 1.0f / Z : 0.0f;
+          float* op = out + ((int64_t)bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim + dd;
+          *reinterpret_cast<float4*>(op) = make_float4(acc.x * iz, acc.y * iz, acc.z * iz, acc.w * iz);
+        } else {                // one split of the row: partials for the combine
+          float* pp = a.part + ((sel * a.n_split + split) * a.G + h) * kPartStride;
+          *reinterpret_cast<float4*>(pp + 4 + dd) = acc;
+          if (dd == 0) {
+            pp[0] = Mw;
+            pp[1] = Z;
+          }
+        }
       }
     }
   }
@@ -750,7 +763,7 @@ static void launch_gather_g(const ScanArgs& a, float* out, dim3 grid, hipStream_
 }
 
 hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool fp8, int B, hipStream_t st) {
-  dim3 grid(1, a.Hkv, B * a.Lq);
+  dim3 grid(a.n_split, a.Hkv, B * a.Lq);
   if (fp8)
     launch_gather_g<true>(a, out, grid, st);
   else

@@ -196,6 +196,15 @@ def test_wide_groups_decode(hq, hkv, kv, ctx):
     run_and_compare(w, f"wide-G{hq // hkv}-{kv}")
 
 
+@pytest.mark.parametrize("fused", ["0", "1"])
+def test_wide_group_sparse_paths(monkeypatch, fused):
+    """MQA sparse layers on the split matrix-core gather + combine (decode default) and
+    on the one-launch gather."""
+    monkeypatch.setenv("HS2_SPARSE_FUSED", fused)
+    w = wl.Workload("mqa sparse", 3, 1, 32, 1, ctx_lens=[800, 5000, 2049], n_needles=8, seed=2540)
+    run_and_compare(w, f"mqa-sparse-fused{fused}")
+
+
 def test_mqa_query_chunk():
     """MQA with several query tokens: the decode scan once per token."""
     w = wl.Workload("mqa chunk", 2, 6, 32, 1, ctx_lens=[2600, 5000], n_needles=8, seed=2520)
