@@ -57,7 +57,7 @@ extern "C" {
 typedef enum hs2_status {
   HS2_OK = 0,
   HS2_ERR_INVALID_ARG = 1,   /* null pointer, bad size or inconsistent descriptor    */
-  HS2_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head_dim != 128, G > 8 ..) */
+  HS2_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head_dim != 128, G > 32 ..)*/
   HS2_ERR_WORKSPACE = 3,     /* workspace_bytes smaller than hs2_workspace_size()      */
   HS2_ERR_ALIGNMENT = 4,     /* a device pointer is not aligned as required            */
   HS2_ERR_LAUNCH = 5         /* the HIP runtime refused a launch                        */
@@ -70,7 +70,7 @@ typedef struct hs2_attn_desc {
   int32_t batch;          /* B >= 1                                                    */
   int32_t q_len;          /* Lq >= 1: 1 at decode, e.g. 64 for an appended chunk       */
   int32_t n_q_heads;      /* Hq                                                         */
-  int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0 and G = Hq / Hkv <= 8                    */
+  int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0 and G = Hq / Hkv <= 32                   */
   int32_t head_dim;       /* must be 128                                                */
   int32_t kv_dtype;       /* HS2_KV_BF16 or HS2_KV_FP8_E4M3FN                            */
   int64_t kv_capacity;    /* cap: rows allocated per (sequence, KV head)                */
@@ -84,7 +84,9 @@ typedef struct hs2_attn_desc {
 } hs2_attn_desc;
 
 /* Host only, touches no GPU: checks a descriptor.  Limits: head_dim == 128,
- * 1 <= G <= 8, window + topk <= 4096 (token mode), block_size in [1, 4096] and
+ * 1 <= G <= 32 with G > 8 (up to MQA at 32 query heads) in token mode only and without
+ * probs (hs2_full_attn_select then returns HS2_ERR_UNSUPPORTED), window + topk <= 4096
+ * (token mode), block_size in [1, 4096] and
  * block_size * n_blocks <= 4096 (block mode), 1 <= q_len <= max_ctx_len <= cap,
  * cap < 2^31, batch * q_len <= 65535, n_kv_heads <= 65535 and
  * batch * q_len * n_kv_heads (selection rows) <= 65535 * 1024; beyond these limits
