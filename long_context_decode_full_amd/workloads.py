@@ -207,3 +207,101 @@ def make_inputs(w: Workload, threads: int = 8) -> dict:
     return dict(workload=w, q_full=q_full, q_sparse=q_sparse, k=k, v=v, k_scale=k_scale,
                 v_scale=v_scale, ctx_len=np.asarray(ctx, dtype=np.int32), capacity=cap,
                 sm_scale=1.0 / math.sqrt(D))
+
+
+# --------------------------------------------------------------------------- KV Bridging inputs
+@dataclasses.dataclass
+class BridgeWorkload:
+    """One KV Bridging call: T source hidden-state rows projected into the K/V caches
+    of n_layers target Full layers (HySparse2 article, section 02 "KV Bridging";
+    section 04: prefill ends after the Self-Decoder and these projections)."""
+    name: str
+    n_tokens: int                    # T rows of the source hidden state
+    hidden: int                      # Hd (the article gives no hidden size)
+    n_layers: int                    # target Full layers fed by this source
+    n_kv_heads: int
+    batch: int                       # sequences held by each cache
+    capacity: int                    # rows per (sequence, KV head)
+    kv_dtype: str = "fp8"            # "bf16" | "fp8"
+    head_dim: int = 128
+    placement: str = "prefill"       # "prefill" | "decode" | "ragged"
+    start: int = 0                   # prefill: position of the first token
+    outlier_channels: int = 4        # hidden channels with a larger spread
+    outlier_scale: float = 8.0
+    bad_rows: int = 0                # tokens given an out-of-range destination
+    seed: int = 0
+
+
+def bridge_workloads():
+    """KV Bridging cases.  The hidden size (2048) and the number of target layers (6)
+    are not on the pages: 6 is (49 - 25) / (1 + 3), the Cross-Decoder's 24 layers in
+    Hybrid Blocks of one Full and three Sparse layers; 2048 is a stand-in hidden size."""
+    return {
+        "bridge_prefill": BridgeWorkload("prefill chunk of a 1M-token context", 16384, 2048, 6, 4,
+                                         batch=1, capacity=1048576, start=1048576 - 16384, seed=2001),
+        "bridge_prefill_bf16": BridgeWorkload("prefill chunk, bf16 caches", 16384, 2048, 6, 4, batch=1,
+                                              capacity=1048576, kv_dtype="bf16",
+                                              start=1048576 - 16384, seed=2002),
+        "bridge_mqa": BridgeWorkload("MQA prefill chunk", 16384, 2048, 6, 1, batch=1, capacity=1048576,
+                                     start=1048576 - 16384, seed=2003),
+        "bridge_decode": BridgeWorkload("batched decode append", 16, 2048, 6, 4, batch=16,
+                                        capacity=32768, placement="decode", seed=2004),
+        "bridge_ragged": BridgeWorkload("ragged chunk append", 1000, 512, 2, 2, batch=5, capacity=4096,
+                                        placement="ragged", bad_rows=7, seed=2005),
+    }
+
+
+def make_bridge_inputs(w: BridgeWorkload) -> dict:
+    """Source hidden state, projection weights and destinations of one bridging call.
+
+      x        [T, Hd] bf16 bits: N(0, 1) entries, `outlier_channels` channels scaled up
+      weight   [L, 2, Hkv * D, Hd] bf16 bits: N(0, 1 / Hd) (W_k then W_v per layer,
+               output-feature major)
+      seq, pos [T] int32 destinations; "prefill" puts the tokens of sequence 0 at
+               start, start + 1, ...; "decode" gives sequence t one token at a random
+               position; "ragged" splits the tokens into `batch` runs of random
+               lengths at random starts; `bad_rows` tokens get an out-of-range
+               sequence or position.
+    """
+    T, Hd, L, Hkv, D = w.n_tokens, w.hidden, w.n_layers, w.n_kv_heads, w.head_dim
+    root = np.random.SeedSequence(w.seed)
+    s_x, s_w, s_o, s_d, s_b = root.spawn(5)
+    x = np.random.default_rng(s_x).standard_normal((T, Hd), dtype=np.float32)
+    if w.outlier_channels > 0:
+        ch = np.random.default_rng(s_o).choice(Hd, size=min(w.outlier_channels, Hd), replace=False)
+        x[:, ch] *= np.float32(w.outlier_scale)
+    wt = np.random.default_rng(s_w).standard_normal((L, 2, Hkv * D, Hd), dtype=np.float32)
+    wt *= np.float32(1.0 / math.sqrt(Hd))
+    rng = np.random.default_rng(s_d)
+    if w.placement == "prefill":
+        assert w.start + T <= w.capacity
+        seq = np.zeros(T, dtype=np.int32)
+        pos = (w.start + np.arange(T)).astype(np.int32)
+    elif w.placement == "decode":
+        assert T == w.batch
+        seq = np.arange(T, dtype=np.int32)
+        pos = rng.integers(0, w.capacity, size=T).astype(np.int32)
+    elif w.placement == "ragged":
+        cuts = np.sort(rng.choice(np.arange(1, T), size=w.batch - 1, replace=False))
+        lens = np.diff(np.concatenate([[0], cuts, [T]]))
+        seq = np.repeat(np.arange(w.batch), lens).astype(np.int32)
+        pos = np.concatenate([rng.integers(0, w.capacity - n + 1) + np.arange(n) for n in lens]).astype(np.int32)
+    else:
+        raise ValueError(w.placement)
+    if w.bad_rows > 0:
+        rb = np.random.default_rng(s_b)
+        bad = rb.choice(T, size=min(w.bad_rows, T), replace=False)
+        choices = [(-1, None), (w.batch, None), (None, -1), (None, w.capacity), (None, -(2 ** 31))]
+        for i, t in enumerate(bad):
+            sb, pb = choices[i % len(choices)]
+            if sb is not None:
+                seq[t] = sb
+            if pb is not None:
+                pos[t] = pb
+    return dict(workload=w, x=f32_to_bf16_bits(x), weight=f32_to_bf16_bits(wt), seq=seq, pos=pos)
+
+
+def bridge_cache_sentinel(kv_dtype: str):
+    """Initial cache contents for bridging tests: NaN codes and NaN scales, so that a
+    row written by mistake or left unwritten shows."""
+    return (E4M3FN_NAN, np.float32(np.nan)) if kv_dtype == "fp8" else (BF16_NAN, None)

@@ -1,4 +1,5 @@
-"""CPU oracle for the HySparse2 Hybrid-Block decode path -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the HySparse2 Hybrid-Block decode path and the KV Bridging
+projection that fills its caches -- TEST INFRASTRUCTURE ONLY.
 
 Plain, slow, float64 numpy.  Only tests/, __graft_entry__.smoke() and the
 cpu_baseline leg of bench.py may import anything from this package; the HIP
@@ -28,4 +29,11 @@ from .hybrid_block import (  # noqa: F401
     block_select,
     hybrid_block,
     hybrid_block_token,
+)
+from .bridge import (  # noqa: F401
+    bf16_rne,
+    e4m3fn_encode,
+    quantize_rows,
+    project,
+    kv_bridge,
 )
