@@ -28,15 +28,18 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 SCAN_SOURCES = [os.path.join(ROOT, "long_context_decode_full_amd", "csrc", f)
                 for f in ("hs2_scan_mfma.hip", "hs2_rowops.h", "hs2_device.h", "hs2_internal.h")]
+BRIDGE_SOURCES = [os.path.join(ROOT, "long_context_decode_full_amd", "csrc", f)
+                  for f in ("hs2_bridge.hip", "hs2_device.h", "hs2_internal.h")]
+BRIDGE_METRIC = "KV Bridging projection tokens/s & MFMA TFLOP/s (%bf16 dense peak)"
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def scan_source_hash():
+def scan_source_hash(files=None):
     h = hashlib.sha256()
-    for p in SCAN_SOURCES:
+    for p in files or SCAN_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -52,16 +55,16 @@ def kv_bytes(inp):
     return ctx * Hkv * 2 * D * 2
 
 
-def measured_traffic(workload):
-    """HBM bytes per scan launch from committed rocprofv3 counter runs, if they were
-    taken on the current scan kernel source; else None."""
+def measured_traffic(workload, files=None, key="scan_source_sha256"):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter
+    runs, if they were taken on the current source of that kernel; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     e = rec.get(workload)
-    if not e or e.get("scan_source_sha256") != scan_source_hash():
+    if not e or e.get(key) != scan_source_hash(files):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -149,6 +152,142 @@ def step_distribution(dev, reps, flush=None):
     return [times[len(times) // 2], times[min(len(times) - 1, int(0.9 * len(times)))]]
 
 
+def bridge_flops(w):
+    """Algorithmic FLOPs of one bridging call: one multiply-add per (token, hidden dim,
+    output feature), output features = layers x {K, V} x KV heads x 128."""
+    return 2 * w.n_tokens * w.hidden * (w.n_layers * 2 * w.n_kv_heads * w.head_dim)
+
+
+def bridge_bytes(w):
+    """Algorithmic HBM bytes of one call: X and W read once, the K/V rows (and fp8
+    scales) written once."""
+    n_feat = w.n_layers * 2 * w.n_kv_heads * w.head_dim
+    out = w.n_tokens * n_feat * (1 if w.kv_dtype == "fp8" else 2)
+    if w.kv_dtype == "fp8":
+        out += w.n_tokens * w.n_layers * 2 * w.n_kv_heads * 4
+    return 2 * w.n_tokens * w.hidden + 2 * n_feat * w.hidden + out
+
+
+def bench_bridge(args):
+    """KV Bridging projection (HySparse2 article, section 02 "KV Bridging"; section 04):
+    one hs2_kv_bridge call per step on the prefill chunk of a 1M-token context."""
+    import torch
+    import oracle
+    from long_context_decode_full_amd import workloads as wl
+    from long_context_decode_full_amd.runner import BridgeDevice
+
+    w = wl.bridge_workloads()[args.workload]
+    log(f"generating inputs: {w.name}")
+    inp = wl.make_bridge_inputs(w)
+    dev = BridgeDevice(inp, device="cuda:0")
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        dev.run()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        dev.run(stream)          # one kernel launch per call, on this stream
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_s = ev0.elapsed_time(ev1) * 1e-3 / args.steps
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    flops = bridge_flops(w)
+    nbytes = bridge_bytes(w)
+    tflops = flops / kern_s / 1e12
+    n_feat = w.n_layers * 2 * w.n_kv_heads * w.head_dim
+    result = {
+        "metric": BRIDGE_METRIC,
+        "value": w.n_tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"KV Bridging, {w.name}: T={w.n_tokens} tokens, hidden {w.hidden}, "
+                        f"{w.n_layers} target layers x (K, V) x {w.n_kv_heads} KV heads x {w.head_dim} "
+                        f"= {n_feat} features, {w.kv_dtype} caches of {w.capacity} rows",
+            "n_tokens": w.n_tokens, "hidden": w.hidden, "n_layers": w.n_layers,
+            "n_kv_heads": w.n_kv_heads, "kv_dtype": w.kv_dtype,
+        },
+        "kernel_us": kern_s * 1e6,
+        "hbm_gbps_algorithmic": nbytes / kern_s / 1e9,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": measured_traffic(args.workload, BRIDGE_SOURCES, "bridge_source_sha256"),
+            "kernel": "bridge_kernel (projection GEMM on the matrix cores + quantise + cache scatter)",
+            "algorithmic_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": nbytes,
+        },
+        "cpu_baseline": None,
+    }
+    # parity sample: the oracle's decisions for a few tokens against the cache rows
+    rng = np.random.default_rng(5)
+    sample = np.sort(rng.choice(w.n_tokens, size=min(64, w.n_tokens), replace=False))
+    got = dev.rows(sample)
+    from oracle import bridge as ob
+    Y = ob.project(inp["x"][sample], inp["weight"].reshape(n_feat, w.hidden))
+    Y32 = Y.astype(np.float32).reshape(len(sample), w.n_layers, 2, w.n_kv_heads, w.head_dim)
+    if w.kv_dtype == "fp8":
+        codes, scales = ob.quantize_rows(Y32)
+        tab = oracle.e4m3fn_table()
+        eq = float(np.mean(tab[codes] == tab[got["codes"]]))
+        rel = float(np.max(np.abs(got["scales"] / scales - 1.0)))
+        result["parity_sample"] = {"tokens": int(len(sample)), "codes_equal_frac": eq,
+                                   "scale_max_rel_diff": rel}
+    else:
+        eq = float(np.mean(ob.bf16_rne(Y32) == got["codes"]))
+        result["parity_sample"] = {"tokens": int(len(sample)), "codes_equal_frac": eq}
+
+    if not args.no_cpu_baseline:
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            cores = os.cpu_count()
+        n = min(1024, w.n_tokens)
+        xs = inp["x"][:n]
+        seq = np.zeros(n, dtype=np.int32)
+        pos = np.arange(n, dtype=np.int32)
+        shape = (w.n_layers, 1, w.n_kv_heads, n, w.head_dim)
+        if w.kv_dtype == "fp8":
+            caches = dict(k=np.zeros(shape, np.uint8), v=np.zeros(shape, np.uint8),
+                          k_scale=np.zeros(shape[:4], np.float32), v_scale=np.zeros(shape[:4], np.float32))
+        else:
+            caches = dict(k=np.zeros(shape, np.uint16), v=np.zeros(shape, np.uint16))
+        log(f"cpu oracle on {n} tokens")
+        reps = 0
+        c0 = time.perf_counter()
+        while reps < 20:
+            oracle.kv_bridge(xs, inp["weight"], seq, pos, caches)
+            reps += 1
+            if time.perf_counter() - c0 >= 10.0:
+                break
+        dt = (time.perf_counter() - c0) / reps
+        result["cpu_baseline"] = {
+            "value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 numpy oracle (projection, rounding, scatter) on the first {n} tokens "
+                      f"of the chunk into a {n}-row cache, {reps} repetition(s) of {dt:.2f}s",
+        }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,7 +295,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps first: the GPU reaches its sustained clocks after a few tens of ms")
     ap.add_argument("--workload", default="million",
-                    help="tiny | batched | fp8_256k | million | chunk | mqa_million")
+                    help="tiny | batched | fp8_256k | million | chunk | mqa_million; KV Bridging: "
+                         "bridge_prefill | bridge_prefill_bf16 | bridge_mqa | bridge_decode")
     ap.add_argument("--select", default="token", choices=["token", "block"],
                     help="token selection (window 128 + top-k 1024) or the first-generation block "
                          "comparator (18 blocks of 64, no forced window)")
@@ -182,6 +322,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": 5}), flush=True)
+        return
+    if args.workload.startswith("bridge"):
+        bench_bridge(args)
         return
     from long_context_decode_full_amd import (HS2_TIMER_GATHER, HS2_TIMER_SCAN, hs2_set_deterministic,
                                               hs2_timer_collect, hs2_timer_enable)

@@ -138,6 +138,62 @@ hs2_status hs2_sparse_attn(const hs2_attn_desc* desc,
 /* Static English text for a status; never NULL. */
 const char* hs2_status_string(hs2_status status);
 
+/* ------------------------------------------------------------------ KV Bridging
+ * HySparse2 article, section 02 "two-level KV sharing" (KV Bridging: every Full
+ * Attention layer of the Cross-Decoder builds its own KV cache from the input hidden
+ * state of the corresponding Self-Decoder Full Attention layer, with its own K and V
+ * projections) and section 04 (prefill ends once the Self-Decoder and these
+ * projections have run: they finish every cache the Cross-Decoder reads).
+ *
+ * One call projects T rows of ONE source hidden state into the caches of n_layers
+ * target layers (the Self-Decoder has a single Full Attention layer, so one source
+ * feeds every target):
+ *   K_l = X W_k,l^T and V_l = X W_v,l^T  (no bias, norm or rotary; fp32 accumulation)
+ * and writes, for every token t and KV head g, the 128 features of head g to cache
+ * row (seq[t], g, pos[t]) of layer l:
+ *   bf16 caches: rounded to nearest even;
+ *   fp8 caches:  OCP E4M3FN codes with one fp32 scale per (token, KV head) row,
+ *                scale = max|row| / 448 (1.0 for an all-zero row),
+ *                code = nearest E4M3FN value of row / scale (ties to even, at most
+ *                +-448), both fp32 operations; the row reads back as code x scale,
+ *                the format hs2_full_attn_select / hs2_sparse_attn read.
+ *
+ *   x         [T, hidden] bf16, row-major, finite values
+ *   w         [n_layers, 2, n_kv_heads * 128, hidden] bf16: W_k,l then W_v,l of each
+ *             layer, output-feature major (a linear layer's weight); rows
+ *             g*128 .. g*128+127 of a block give KV head g
+ *   seq, pos  [T] int32: destination sequence and cache position of token t; a token
+ *             with seq outside [0, batch) or pos outside [0, kv_capacity) is skipped.
+ *             Destinations must be distinct (two tokens writing one row race).
+ *   k_caches, v_caches   HOST arrays of n_layers DEVICE pointers, each to one layer's
+ *             cache [batch, n_kv_heads, kv_capacity, 128] (bf16, or E4M3FN bytes)
+ *   k_scales, v_scales   HOST arrays of n_layers device pointers to the layers'
+ *             [batch, n_kv_heads, kv_capacity] fp32 scales (fp8), or NULL (bf16)
+ * Only the destination rows (and their scales) are written; every other byte of the
+ * caches is left as it was.  x, w and the caches must be 16-byte aligned, seq, pos
+ * and the scales 4-byte aligned.  The call is asynchronous on `stream`, allocates
+ * nothing, keeps no pointer after it returns and needs no workspace.  Errors
+ * (HS2_ERR_INVALID_ARG: a NULL pointer or layer pointer, a bad size;
+ * HS2_ERR_UNSUPPORTED: head_dim != 128, hidden not a multiple of 64, more than 16
+ * layers, too large a grid; HS2_ERR_ALIGNMENT) are returned before anything is
+ * enqueued; n_tokens == 0 enqueues nothing and returns HS2_OK. */
+typedef struct hs2_bridge_desc {
+  int32_t n_tokens;       /* T >= 0 rows of the source hidden state                      */
+  int32_t hidden;         /* hidden size: a multiple of 64, at most 65536                */
+  int32_t n_layers;       /* target Full layers fed by this source: 1 .. 16              */
+  int32_t n_kv_heads;     /* KV heads per layer (1 for MQA)                              */
+  int32_t head_dim;       /* must be 128                                                 */
+  int32_t kv_dtype;       /* HS2_KV_BF16 or HS2_KV_FP8_E4M3FN                             */
+  int32_t batch;          /* sequences per cache, >= 1                                    */
+  int64_t kv_capacity;    /* rows per (sequence, KV head), 1 .. 2^31 - 1                  */
+} hs2_bridge_desc;
+
+hs2_status hs2_kv_bridge(const hs2_bridge_desc* desc, const void* x, const void* w,
+                         const int32_t* seq, const int32_t* pos,
+                         void* const* k_caches, void* const* v_caches,
+                         float* const* k_scales, float* const* v_scales,
+                         hipStream_t stream);
+
 /* Reproducibility switch (process-wide, default off).  By default the waves of a
  * context-scan workgroup share its steps through a counter, so the order in which
  * a head's probabilities are summed into `out` varies between runs and `out` of

@@ -21,7 +21,8 @@ __all__ = [
     "HS2_SELECT_TOKEN", "HS2_SELECT_BLOCK", "Hs2AttnDesc", "Hs2Error", "make_desc",
     "hs2_validate", "hs2_workspace_size", "hs2_full_attn_select", "hs2_sparse_attn",
     "hs2_status_string", "hs2_set_deterministic", "hs2_timer_enable", "hs2_timer_collect", "HS2_TIMER_SCAN",
-    "HS2_TIMER_GATHER", "library_path", "load_library",
+    "HS2_TIMER_GATHER", "library_path", "load_library", "Hs2BridgeDesc", "make_bridge_desc",
+    "hs2_kv_bridge",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -38,7 +39,7 @@ HS2_SELECT_BLOCK = 1
 
 EXPORTED_SYMBOLS = ("hs2_validate", "hs2_workspace_size", "hs2_full_attn_select",
                     "hs2_sparse_attn", "hs2_status_string", "hs2_set_deterministic",
-                    "hs2_timer_enable", "hs2_timer_collect")
+                    "hs2_timer_enable", "hs2_timer_collect", "hs2_kv_bridge")
 
 
 class Hs2AttnDesc(ctypes.Structure):
@@ -59,6 +60,26 @@ class Hs2AttnDesc(ctypes.Structure):
         ("n_blocks", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
     ]
+
+
+class Hs2BridgeDesc(ctypes.Structure):
+    """Mirror of hs2_bridge_desc (include/hs2.h)."""
+    _fields_ = [
+        ("n_tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("n_layers", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("kv_capacity", ctypes.c_int64),
+    ]
+
+
+def make_bridge_desc(n_tokens, hidden, n_layers, n_kv_heads, batch, kv_capacity, head_dim=128,
+                     kv_dtype=HS2_KV_FP8_E4M3FN) -> Hs2BridgeDesc:
+    return Hs2BridgeDesc(int(n_tokens), int(hidden), int(n_layers), int(n_kv_heads), int(head_dim),
+                         int(kv_dtype), int(batch), int(kv_capacity))
 
 
 class Hs2Error(RuntimeError):
@@ -104,6 +125,8 @@ def load_library():
     lib.hs2_full_attn_select.restype = ctypes.c_int
     lib.hs2_sparse_attn.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.hs2_sparse_attn.restype = ctypes.c_int
+    lib.hs2_kv_bridge.argtypes = [ctypes.POINTER(Hs2BridgeDesc), P, P, P, P, P, P, P, P, P]
+    lib.hs2_kv_bridge.restype = ctypes.c_int
     lib.hs2_status_string.argtypes = [ctypes.c_int]
     lib.hs2_status_string.restype = ctypes.c_char_p
     lib.hs2_set_deterministic.argtypes = [ctypes.c_int]
@@ -159,6 +182,29 @@ def hs2_sparse_attn(desc, q, k, v, k_scale, v_scale, ctx_len, idx, out, workspac
     return load_library().hs2_sparse_attn(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
         _ptr(ctx_len), _ptr(idx), _ptr(out), _ptr(workspace), int(workspace_bytes),
+        _stream(stream))
+
+
+def _ptr_array(xs):
+    """A host array of device pointers (void* const*), or None for NULL."""
+    if xs is None:
+        return None
+    arr = (ctypes.c_void_p * max(1, len(xs)))(*[_ptr(x) for x in xs])
+    return arr
+
+
+def hs2_kv_bridge(desc, x, w, seq, pos, k_caches, v_caches, k_scales=None, v_scales=None,
+                  stream=None) -> int:
+    """k_caches / v_caches (and k_scales / v_scales for fp8): one tensor or device
+    address per target layer, passed to the library as host arrays of pointers."""
+    ka, va = _ptr_array(k_caches), _ptr_array(v_caches)
+    ksa, vsa = _ptr_array(k_scales), _ptr_array(v_scales)
+    return load_library().hs2_kv_bridge(
+        ctypes.byref(desc), _ptr(x), _ptr(w), _ptr(seq), _ptr(pos),
+        ctypes.cast(ka, ctypes.c_void_p) if ka is not None else None,
+        ctypes.cast(va, ctypes.c_void_p) if va is not None else None,
+        ctypes.cast(ksa, ctypes.c_void_p) if ksa is not None else None,
+        ctypes.cast(vsa, ctypes.c_void_p) if vsa is not None else None,
         _stream(stream))
 
 

@@ -577,3 +577,57 @@ HS2_API hs2_status hs2_timer_collect(double* scan_ms, int32_t* scan_count, doubl
   *gather_count = cnt[1];
   return st;
 }
+
+HS2_API hs2_status hs2_kv_bridge(const hs2_bridge_desc* d, const void* x, const void* w,
+                                 const int32_t* seq, const int32_t* pos,
+                                 void* const* k_caches, void* const* v_caches,
+                                 float* const* k_scales, float* const* v_scales,
+                                 hipStream_t stream) {
+  if (d == nullptr) return HS2_ERR_INVALID_ARG;
+  if (d->n_tokens < 0 || d->hidden < 1 || d->n_layers < 1 || d->n_kv_heads < 1 ||
+      d->batch < 1 || d->kv_capacity < 1)
+    return HS2_ERR_INVALID_ARG;
+  if (d->kv_dtype != HS2_KV_BF16 && d->kv_dtype != HS2_KV_FP8_E4M3FN) return HS2_ERR_INVALID_ARG;
+  if (d->head_dim != kHeadDim || d->hidden % 64 != 0 || d->hidden > 65536 ||
+      d->n_layers > kMaxBridgeLayers || d->n_kv_heads > 65535 ||
+      d->kv_capacity >= (int64_t(1) << 31))
+    return HS2_ERR_UNSUPPORTED;
+  const bool fp8 = d->kv_dtype == HS2_KV_FP8_E4M3FN;
+  if (!x || !w || !seq || !pos || !k_caches || !v_caches) return HS2_ERR_INVALID_ARG;
+  if (fp8 && (!k_scales || !v_scales)) return HS2_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(seq, 4) || !aligned(pos, 4))
+    return HS2_ERR_ALIGNMENT;
+  BridgeArgs a{};
+  for (int l = 0; l < d->n_layers; ++l) {
+    if (!k_caches[l] || !v_caches[l]) return HS2_ERR_INVALID_ARG;
+    if (!aligned(k_caches[l], 16) || !aligned(v_caches[l], 16)) return HS2_ERR_ALIGNMENT;
+    a.kc[l] = k_caches[l];
+    a.vc[l] = v_caches[l];
+    if (fp8) {
+      if (!k_scales[l] || !v_scales[l]) return HS2_ERR_INVALID_ARG;
+      if (!aligned(k_scales[l], 4) || !aligned(v_scales[l], 4)) return HS2_ERR_ALIGNMENT;
+      a.ks[l] = k_scales[l];
+      a.vs[l] = v_scales[l];
+    }
+  }
+  // features: n_layers x {K, V} x n_kv_heads x 128, in tiles of 256 (two heads)
+  const int64_t n_feat = (int64_t)d->n_layers * 2 * d->n_kv_heads * kHeadDim;
+  const int64_t n_tiles = n_feat / 256;
+  const int64_t m_tiles = ceil_div(d->n_tokens, 128);
+  if (m_tiles * n_tiles > INT32_MAX) return HS2_ERR_UNSUPPORTED;
+  if (d->n_tokens == 0) return HS2_OK;
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = static_cast<const uint16_t*>(w);
+  a.seq = seq;
+  a.pos = pos;
+  a.cap = d->kv_capacity;
+  a.T = d->n_tokens;
+  a.Hd = d->hidden;
+  a.Hkv = d->n_kv_heads;
+  a.B = d->batch;
+  a.n_layers = d->n_layers;
+  a.m_tiles = (int32_t)m_tiles;
+  a.n_tiles = (int32_t)n_tiles;
+  if (launch_bridge(a, fp8, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+  return HS2_OK;
+}

@@ -139,6 +139,25 @@ struct FastSelArgs {
   int32_t window, topk, S;
 };
 
+// KV Bridging projection: Y = X W^T for one source hidden state and every target
+// layer of the call, rounded (bf16) or quantised (E4M3FN + per-row scale) and
+// written to cache row (seq[t], KV head, pos[t]) of the target layer.
+constexpr int kMaxBridgeLayers = 16;
+struct BridgeArgs {
+  const uint16_t* x;        // [T, Hd] bf16
+  const uint16_t* w;        // [L * 2 * Hkv * 128, Hd] bf16 (W_k,l then W_v,l per layer)
+  const int32_t* seq;       // [T]
+  const int32_t* pos;       // [T]
+  void* kc[kMaxBridgeLayers];   // [B, Hkv, cap, 128] per target layer
+  void* vc[kMaxBridgeLayers];
+  float* ks[kMaxBridgeLayers];  // [B, Hkv, cap] (fp8 caches)
+  float* vs[kMaxBridgeLayers];
+  int64_t cap;
+  int32_t T, Hd, Hkv, B, n_layers;
+  int32_t m_tiles, n_tiles;     // token tiles x feature tiles of the launch
+};
+hipError_t launch_bridge(const BridgeArgs& a, bool fp8, hipStream_t st);
+
 hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st);
 hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t st);
 hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st);

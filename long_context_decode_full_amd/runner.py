@@ -13,7 +13,8 @@ import numpy as np
 import torch
 
 from . import (HS2_KV_BF16, HS2_KV_FP8_E4M3FN, HS2_OK, HS2_SELECT_BLOCK, HS2_SELECT_TOKEN,
-               Hs2Error, hs2_full_attn_select, hs2_sparse_attn, hs2_workspace_size, make_desc)
+               Hs2Error, hs2_full_attn_select, hs2_kv_bridge, hs2_sparse_attn, hs2_workspace_size,
+               make_bridge_desc, make_desc)
 
 
 def _dev(a: np.ndarray, device):
@@ -84,3 +85,71 @@ class HybridBlockDevice:
         return dict(out_full=self.out_full.cpu().numpy(), idx=self.idx.cpu().numpy(),
                     probs=None if self.probs is None else self.probs.cpu().numpy(),
                     out_sparse=[o.cpu().numpy() for o in self.out_sparse])
+
+
+class BridgeDevice:
+    """Device buffers of one KV Bridging call (HySparse2 article, section 02 "KV
+    Bridging"): the source hidden state, the projection weights of every target layer,
+    the destinations, and one K and one V cache (plus scales for fp8) per target layer.
+    The caches start filled with `fill` codes (and `scale_fill` scales)."""
+
+    def __init__(self, inp: dict, device="cuda", fill=None, scale_fill=float("nan")):
+        w = inp["workload"]
+        self.device = torch.device(device)
+        self.fp8 = w.kv_dtype == "fp8"
+        self.L, self.Hkv, self.B, self.cap, self.D = w.n_layers, w.n_kv_heads, w.batch, w.capacity, w.head_dim
+        self.T, self.Hd = w.n_tokens, w.hidden
+        self.desc = make_bridge_desc(self.T, self.Hd, self.L, self.Hkv, self.B, self.cap, head_dim=self.D,
+                                     kv_dtype=HS2_KV_FP8_E4M3FN if self.fp8 else HS2_KV_BF16)
+        dv = self.device
+        self.x = _dev(inp["x"], dv)
+        self.w = _dev(inp["weight"], dv)
+        self.seq = _dev(inp["seq"].astype(np.int32), dv)
+        self.pos = _dev(inp["pos"].astype(np.int32), dv)
+        shape = (self.B, self.Hkv, self.cap, self.D)
+        if self.fp8:
+            code = 0x7F if fill is None else int(fill)
+            self.k = [torch.full(shape, code, dtype=torch.uint8, device=dv) for _ in range(self.L)]
+            self.v = [torch.full(shape, code, dtype=torch.uint8, device=dv) for _ in range(self.L)]
+            self.ks = [torch.full(shape[:3], scale_fill, dtype=torch.float32, device=dv) for _ in range(self.L)]
+            self.vs = [torch.full(shape[:3], scale_fill, dtype=torch.float32, device=dv) for _ in range(self.L)]
+        else:
+            code = 0x7FC0 if fill is None else int(fill)
+            code = code - 0x10000 if code >= 0x8000 else code
+            self.k = [torch.full(shape, code, dtype=torch.int16, device=dv) for _ in range(self.L)]
+            self.v = [torch.full(shape, code, dtype=torch.int16, device=dv) for _ in range(self.L)]
+            self.ks = self.vs = None
+
+    def run(self, stream=None):
+        st = hs2_kv_bridge(self.desc, self.x, self.w, self.seq, self.pos, self.k, self.v,
+                           self.ks, self.vs, stream)
+        if st != HS2_OK:
+            raise Hs2Error(st, "hs2_kv_bridge")
+
+    def rows(self, tokens) -> dict:
+        """Cache rows of the given tokens (which must have valid destinations):
+        codes [n, L, 2, Hkv, D] (uint8 or uint16 bits) and, for fp8, scales [n, L, 2, Hkv]."""
+        torch.cuda.synchronize(self.device)
+        t = torch.as_tensor(np.asarray(tokens, dtype=np.int64), device=self.device)
+        s = self.seq.long()[t]
+        p = self.pos.long()[t]
+        codes = torch.stack([torch.stack([c[l][s, :, p] for c in (self.k, self.v)], 1)
+                             for l in range(self.L)], 1)
+        out = dict(codes=codes.cpu().numpy())
+        if not self.fp8:
+            out["codes"] = out["codes"].view(np.uint16)
+        else:
+            out["scales"] = torch.stack([torch.stack([c[l][s, :, p] for c in (self.ks, self.vs)], 1)
+                                         for l in range(self.L)], 1).cpu().numpy()
+        return out
+
+    def caches(self) -> dict:
+        """Whole caches on the host, stacked over layers: k, v [L, B, Hkv, cap, D] (and
+        k_scale, v_scale [L, B, Hkv, cap] for fp8); for small cases only."""
+        torch.cuda.synchronize(self.device)
+        k = torch.stack(self.k).cpu().numpy()
+        v = torch.stack(self.v).cpu().numpy()
+        if not self.fp8:
+            return dict(k=k.view(np.uint16), v=v.view(np.uint16))
+        return dict(k=k, v=v, k_scale=torch.stack(self.ks).cpu().numpy(),
+                    v_scale=torch.stack(self.vs).cpu().numpy())

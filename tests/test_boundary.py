@@ -186,3 +186,84 @@ def test_product_path_has_no_fallback():
             src = open(os.path.join(pkg, name)).read()
             assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), name
             assert "hybrid_block(" not in src, name
+
+
+# ----------------------------------------------------------------------------- KV Bridging
+def test_bridge_desc_struct_layout_matches_header():
+    # int32 x7, then int64 aligned to 8 -> 28 + 4 pad + 8 = 40 bytes
+    assert ctypes.sizeof(hs2.Hs2BridgeDesc) == 40
+    assert hs2.Hs2BridgeDesc.kv_capacity.offset == 32
+
+
+_GOOD = 0x10000000          # fake 4 KiB-aligned device addresses, never dereferenced
+
+
+def _bridge(lib_unused=None, desc=None, fp8=True, n_layers=2, **over):
+    d = desc if desc is not None else hs2.make_bridge_desc(
+        300, 512, n_layers, 2, 4, 4096, kv_dtype=hs2.HS2_KV_FP8_E4M3FN if fp8 else hs2.HS2_KV_BF16)
+    args = dict(x=_GOOD, w=_GOOD + 0x1000000, seq=_GOOD + 0x2000000, pos=_GOOD + 0x3000000,
+                k_caches=[_GOOD + 0x4000000 * (i + 1) for i in range(d.n_layers)],
+                v_caches=[_GOOD + 0x4000000 * (i + 1) + 0x2000000 for i in range(d.n_layers)],
+                k_scales=[_GOOD + 0x100000 * (i + 1) for i in range(d.n_layers)] if fp8 else None,
+                v_scales=[_GOOD + 0x100000 * (i + 1) + 0x80000 for i in range(d.n_layers)] if fp8 else None)
+    args.update(over)
+    return hs2.hs2_kv_bridge(d, **args, stream=0)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_tokens", -1, hs2.HS2_ERR_INVALID_ARG),
+    ("hidden", 0, hs2.HS2_ERR_INVALID_ARG),
+    ("hidden", 100, hs2.HS2_ERR_UNSUPPORTED),
+    ("hidden", 65536 + 64, hs2.HS2_ERR_UNSUPPORTED),
+    ("head_dim", 64, hs2.HS2_ERR_UNSUPPORTED),
+    ("n_layers", 0, hs2.HS2_ERR_INVALID_ARG),
+    ("n_layers", 17, hs2.HS2_ERR_UNSUPPORTED),
+    ("n_kv_heads", 0, hs2.HS2_ERR_INVALID_ARG),
+    ("kv_dtype", 7, hs2.HS2_ERR_INVALID_ARG),
+    ("batch", 0, hs2.HS2_ERR_INVALID_ARG),
+    ("kv_capacity", 0, hs2.HS2_ERR_INVALID_ARG),
+    ("kv_capacity", 1 << 31, hs2.HS2_ERR_UNSUPPORTED),
+])
+def test_bridge_desc_checks(lib, field, value, status):
+    d = hs2.make_bridge_desc(300, 512, 2, 2, 4, 4096)
+    setattr(d, field, value)
+    over = {}
+    if field == "n_layers" and value > 0:
+        over = dict(k_caches=[_GOOD] * value, v_caches=[_GOOD] * value, k_scales=[_GOOD] * value,
+                    v_scales=[_GOOD] * value)
+    assert _bridge(desc=d, **over) == status
+
+
+def test_bridge_null_desc(lib):
+    assert lib.hs2_kv_bridge(None, None, None, None, None, None, None, None, None, None) == \
+        hs2.HS2_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field", ["x", "w", "seq", "pos", "k_caches", "v_caches", "k_scales", "v_scales"])
+def test_bridge_null_pointers_rejected(lib, field):
+    assert _bridge(**{field: None}) == hs2.HS2_ERR_INVALID_ARG
+
+
+def test_bridge_null_layer_pointer_rejected(lib):
+    assert _bridge(v_caches=[_GOOD, 0]) == hs2.HS2_ERR_INVALID_ARG
+    assert _bridge(k_scales=[_GOOD, 0]) == hs2.HS2_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field,addr", [("x", _GOOD + 8), ("w", _GOOD + 2), ("seq", _GOOD + 2),
+                                        ("pos", _GOOD + 1)])
+def test_bridge_misaligned_pointers_rejected(lib, field, addr):
+    assert _bridge(**{field: addr}) == hs2.HS2_ERR_ALIGNMENT
+
+
+def test_bridge_misaligned_layer_pointers_rejected(lib):
+    assert _bridge(k_caches=[_GOOD, _GOOD + 8]) == hs2.HS2_ERR_ALIGNMENT
+    assert _bridge(v_scales=[_GOOD, _GOOD + 2]) == hs2.HS2_ERR_ALIGNMENT
+
+
+def test_bridge_bf16_needs_no_scales_and_zero_tokens_enqueue_nothing(lib):
+    # a bf16 call with no scale arrays passes every check; with zero tokens it returns
+    # before any launch (no GPU is touched)
+    d = hs2.make_bridge_desc(0, 512, 2, 2, 4, 4096, kv_dtype=hs2.HS2_KV_BF16)
+    assert _bridge(desc=d, fp8=False) == hs2.HS2_OK
+    d8 = hs2.make_bridge_desc(0, 512, 2, 2, 4, 4096)
+    assert _bridge(desc=d8, fp8=True, k_scales=None) == hs2.HS2_ERR_INVALID_ARG
