@@ -613,7 +613,7 @@ HS2_API hs2_status hs2_kv_bridge(const hs2_bridge_desc* d, const void* x, const 
   // features: n_layers x {K, V} x n_kv_heads x 128, in tiles of 256 (two heads)
   const int64_t n_feat = (int64_t)d->n_layers * 2 * d->n_kv_heads * kHeadDim;
   const int64_t n_tiles = n_feat / 256;
-  const int64_t m_tiles = ceil_div(d->n_tokens, 128);
+  const int64_t m_tiles = ceil_div(d->n_tokens, bridge_tile_tokens(d->n_tokens));
   if (m_tiles * n_tiles > INT32_MAX) return HS2_ERR_UNSUPPORTED;
   if (d->n_tokens == 0) return HS2_OK;
   a.x = static_cast<const uint16_t*>(x);

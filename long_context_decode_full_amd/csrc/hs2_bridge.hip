@@ -11,18 +11,26 @@
 // E4M3FN with one fp32 scale (max|row| / 448; the division and the rounding in fp32),
 // and stores it at cache row (seq[t], KV head, pos[t]) of its layer.
 //
-// Tiling: a workgroup of 4 waves owns 128 tokens x 256 features (two heads); wave
-// (wm, wn) owns 64 tokens x the 128 features of one head, so the quantisation of a
-// row never leaves the wave.  Per iteration of 64 hidden dims the X and W tiles go
-// through LDS (rows padded to 144 bytes: 16-byte reads of 8 (or 16) consecutive rows
-// hit distinct banks), double-buffered, with the next tiles loaded into registers
-// while the matrix cores work on the current ones.  Products on
-// v_mfma_f32_16x16x32_bf16: A = X rows (lane: token i, dims 8grp..), B = W rows.
-// The W rows of a head are stored in LDS permuted (LDS row 16j + i holds feature
-// 8i + j), so B tile j, lane i is feature 8i + j and the accumulators of a lane for
-// one token are the 8 consecutive features 8i .. 8i + 7: each lane stores 16 bytes
-// (bf16) or 8 bytes (fp8) of a cache row directly, and a row's maximum is a max over
-// 8 registers and the 16 lanes of its DPP row.
+// Tiling: a workgroup owns kBM tokens x 256 features (two heads); wave (wm, wn) owns
+// 64 tokens x the 128 features of one head, so the quantisation of a row never
+// leaves the wave.  The hidden dims go through a ring of kStages LDS stages of kBK
+// dims, filled by direct global -> LDS loads (global_load_lds_dwordx4: a wave
+// instruction writes 64 lanes x 16 bytes into 1 KiB of LDS, no registers in
+// between), so the loads of step kb + kStages - 1 are in flight while step kb
+// computes.  Inside a staged row the 16-byte chunks are XOR-swizzled (chunk_swz) so
+// that the fragment reads run without LDS bank conflicts.  Products on
+// v_mfma_f32_16x16x32_bf16: A = X rows (lane: token i, dims 8grp..), B = W rows.  The
+// W rows of a head are staged permuted (staged row 16j + i holds feature 8i + j), so B
+// tile j, lane i is feature 8i + j and the accumulators of a lane for one token are
+// the 8 consecutive features 8i .. 8i + 7: each lane stores 16 bytes (bf16) or 8
+// bytes (fp8) of a cache row directly, and a row's maximum is a max over 8 registers
+// and the 16 lanes of its DPP row.
+//
+// Bound: with the loads removed the loop runs at ~0.8 of the bf16 matrix-core peak;
+// with them, the tile loads set the pace (each X tile is re-read by every feature
+// tile and each W tile by every token tile, ~1/5 of those reads miss the XCD's L2,
+// and a CU keeps only so many lines in flight), which is why the largest tile that
+// the registers allow (256 x 256) is used for prefill-size calls.
 #include "hs2_device.h"
 #include "hs2_internal.h"
 
@@ -32,16 +40,37 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2v_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_cvoid_t;
 
-constexpr int kBThreads = 256;                    // 4 waves
-constexpr int kBM = 128;                          // tokens per workgroup
+// Tile configuration: kBM tokens x 256 features per workgroup, kStages LDS stages of
+// kBK hidden dims.
+template <int BM, int STAGES, int BK>
+struct BridgeCfg {
+  static constexpr int kBM = BM;
+  static constexpr int kStages = STAGES;
+  static constexpr int kBK = BK;
+  static constexpr int kWavesM = BM / 64;                  // waves along the tokens
+  static constexpr int kWaves = kWavesM * 2;               // x 2 heads
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRowBytes = BK * 2;                 // staged row, unpadded
+  static constexpr int kRowChunks = kRowBytes / 16;        // 16-byte chunks per staged row
+  static constexpr int kBlockRows = 1024 / kRowBytes;      // staged rows per direct load
+  static constexpr int kStageRows = BM + 256;
+  static constexpr int kStage = kStageRows * kRowBytes;
+  static constexpr int kLds = STAGES * kStage;
+  static constexpr int kOcc = (kLds * 2 <= 160 * 1024) ? 2 : 1;   // workgroups per CU
+  static constexpr int kBlocks = kStageRows / kBlockRows;  // 1 KiB row blocks per stage
+  static constexpr int kLoads = kBlocks / kWaves;          // direct loads per wave per stage
+  static_assert(kBlocks % kWaves == 0, "row blocks must split evenly over the waves");
+};
+// Prefill-size calls: 256 x 256 tiles (8 waves, one workgroup per CU), two stages of 64
+// dims (whole 128-byte rows per load).  Small calls (decode appends, short chunks):
+// 128 x 256 tiles, two workgroups per CU, three stages of 32 dims.
+using BridgeLarge = BridgeCfg<256, 2, 64>;
+using BridgeSmall = BridgeCfg<128, 3, 32>;
+constexpr int kLargeMinTokens = 4096;
 constexpr int kBN = 256;                          // features per workgroup (two heads)
-constexpr int kBK = 64;                           // hidden dims per iteration
-constexpr int kRow = kBK * 2 + 16;                // bytes per staged row (128 + pad)
-constexpr int kStage = (kBM + kBN) * kRow;        // one X tile + one W tile
-constexpr int kBridgeLds = 2 * kStage;            // double-buffered: 110,592 bytes
-constexpr int kAChunks = kBM * kBK / 8 / kBThreads;   // 16-byte loads per thread: 4
-constexpr int kBChunks = kBN * kBK / 8 / kBThreads;   // 8
 constexpr int kGroupM = 8;                        // token tiles per tile group
 constexpr float kE4M3Max = 448.0f;
 
@@ -71,6 +100,26 @@ __device__ __forceinline__ uint32_t cvt_fp8x2(float a, float b, uint32_t old, bo
             : (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, false);
 }
 
+// Swizzle of the 16-byte chunks of a staged row (a function of the row mod 16): the
+// fragment reads (16 consecutive rows x 4 chunks per instruction) run without LDS
+// bank conflicts on gfx950 with chunk c of row r at c ^ ((r >> 1) & 3) in 64-byte
+// rows and at c ^ (r & 7) in 128-byte rows (measured with the LDS bank-conflict
+// counter; unswizzled rows, 16-byte padding and other XOR patterns conflict).
+template <int kRowChunks>
+__device__ __forceinline__ int chunk_swz(int r) {
+  if constexpr (kRowChunks == 4) return (r >> 1) & 3;
+  else return r & 7;
+}
+
+// Wait until at most N direct loads of this wave are outstanding, then meet the other
+// waves: after it, the stages those loads filled are complete for every wave, and
+// every wave has finished reading the stage about to be refilled.  One asm block so
+// that no LDS access is moved across either instruction.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // Workgroup -> (token tile, feature tile).  Workgroups are dealt to the 8 XCDs in
 // turn; each XCD takes a contiguous run of tiles in grouped order (kGroupM token
 // tiles per feature tile before the next feature tile), so the workgroups resident
@@ -88,56 +137,42 @@ __device__ __forceinline__ void tile_of(const BridgeArgs& a, int& mt, int& nt) {
   nt = in_group / gsize;
 }
 
-template <bool kFp8>
-__global__ __launch_bounds__(kBThreads, 1) void bridge_kernel(BridgeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kBridgeLds];
+template <bool kFp8, class C>
+__global__ __launch_bounds__(C::kThreads, C::kOcc) void bridge_kernel(BridgeArgs a) {
+  constexpr int kBM = C::kBM, kStages = C::kStages, kBK = C::kBK, kWavesM = C::kWavesM;
+  constexpr int kWaves = C::kWaves, kRowBytes = C::kRowBytes, kRowChunks = C::kRowChunks;
+  constexpr int kBlockRows = C::kBlockRows, kStage = C::kStage, kLoads = C::kLoads;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
+  const int wm = wave % kWavesM;
+  const int wn = wave / kWavesM;
   int mt, nt;
   tile_of(a, mt, nt);
   const int m0 = mt * kBM;
   const int n0 = nt * kBN;
   const int nk = a.Hd / kBK;
 
-  // global -> LDS assignment: 8 threads per 128-byte row slice, 32 rows per pass
-  const int lrow = tid >> 3;
-  const int lchunk = tid & 7;
-  const u32x4_t* xa[kAChunks];
-  const u32x4_t* wb[kBChunks];
-  int aoff[kAChunks], boff[kBChunks];
+  // direct loads: wave `wave` fills row blocks wave, wave + kWaves, ... of every
+  // stage; lane l writes staged row 16 * block + l / 4, physical chunk l % 4, which
+  // holds logical chunk (l % 4) ^ f(row) of the source row
+  const uint16_t* src[kLoads];
 #pragma unroll
-  for (int j = 0; j < kAChunks; ++j) {
-    const int r = lrow + 32 * j;
-    const int t = min(m0 + r, a.T - 1);          // rows past T load row T-1 (not stored)
-    xa[j] = reinterpret_cast<const u32x4_t*>(a.x + (size_t)t * a.Hd) + lchunk;
-    aoff[j] = r * kRow + lchunk * 16;
+  for (int i = 0; i < kLoads; ++i) {
+    const int r = (wave + kWaves * i) * kBlockRows + lane / kRowChunks;   // staged row
+    const int c = (lane % kRowChunks) ^ chunk_swz<kRowChunks>(r);
+    const uint16_t* row;
+    if (r < kBM) {
+      row = a.x + (size_t)min(m0 + r, a.T - 1) * a.Hd;       // rows past T: row T-1
+    } else {
+      const int rho = r - kBM;                               // 0..255
+      const int h = rho >> 7, q = rho & 127;
+      const int f = ((q & 15) << 3) + (q >> 4);              // feature held by row q
+      row = a.w + (size_t)(n0 + h * 128 + f) * a.Hd;
+    }
+    src[i] = row + c * 8;
   }
-#pragma unroll
-  for (int j = 0; j < kBChunks; ++j) {
-    const int r = lrow + 32 * j;                 // feature row of the tile, 0..255
-    wb[j] = reinterpret_cast<const u32x4_t*>(a.w + (size_t)(n0 + r) * a.Hd) + lchunk;
-    const int h = r >> 7, f = r & 127;
-    boff[j] = (kBM + h * 128 + ((f & 7) << 4) + (f >> 3)) * kRow + lchunk * 16;
-  }
-
-  u32x4_t ra[kAChunks], rb[kBChunks];
-#define HS2_BRIDGE_GLOAD(kb)                                                  \
-  do {                                                                        \
-    const int o_ = (kb) * (kBK / 8);                                          \
-    _Pragma("unroll") for (int j = 0; j < kAChunks; ++j) ra[j] = xa[j][o_];   \
-    _Pragma("unroll") for (int j = 0; j < kBChunks; ++j) rb[j] = wb[j][o_];   \
-  } while (0)
-#define HS2_BRIDGE_LSTORE(stage)                                              \
-  do {                                                                        \
-    uint8_t* s_ = lds + (stage) * kStage;                                     \
-    _Pragma("unroll") for (int j = 0; j < kAChunks; ++j)                      \
-      *reinterpret_cast<u32x4_t*>(s_ + aoff[j]) = ra[j];                        \
-    _Pragma("unroll") for (int j = 0; j < kBChunks; ++j)                      \
-      *reinterpret_cast<u32x4_t*>(s_ + boff[j]) = rb[j];                        \
-  } while (0)
 
   f32x4_t acc[4][8];
 #pragma unroll
@@ -145,36 +180,48 @@ __global__ __launch_bounds__(kBThreads, 1) void bridge_kernel(BridgeArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int a_rd = (wm * 64 + (lane & 15)) * kRow + (lane >> 4) * 16;
-  const int b_rd = (kBM + wn * 128 + (lane & 15)) * kRow + (lane >> 4) * 16;
+  const int li = lane & 15;
+  const int grp = lane >> 4;
+  const int swz = chunk_swz<kRowChunks>(li);                             // f depends on row mod 16
+  const int a_rd = (wm * 64 + li) * kRowBytes;
+  const int b_rd = (kBM + wn * 128 + li) * kRowBytes;
 
-  HS2_BRIDGE_GLOAD(0);
-  HS2_BRIDGE_LSTORE(0);
-  __syncthreads();
-  for (int kb = 0; kb < nk; ++kb) {
-    const bool more = kb + 1 < nk;
-    if (more) HS2_BRIDGE_GLOAD(kb + 1);
-    const uint8_t* s = lds + (kb & 1) * kStage;
+#define HS2_BRIDGE_ISSUE(kb, stage)                                                       \
+  do {                                                                                    \
+    uint8_t* d_ = lds + (stage) * kStage;                                                 \
+    _Pragma("unroll") for (int i = 0; i < kLoads; ++i)                                    \
+      __builtin_amdgcn_global_load_lds((global_cvoid_t*)(src[i] + (kb) * kBK),            \
+                                       (lds_void_t*)(d_ + (wave + kWaves * i) * 1024), 16, 0, 0); \
+  } while (0)
+
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < nk) HS2_BRIDGE_ISSUE(s, s);
+  for (int kb = 0; kb < nk; ++kb) {
+    const int rem = nk - 1 - kb;          // steps issued after this one
+    if (rem >= kStages - 2) wait_loads_and_barrier<kLoads * (kStages - 2)>();
+    else if (kStages > 3 && rem == 1) wait_loads_and_barrier<kLoads>();
+    else wait_loads_and_barrier<0>();
+    if (kb + kStages - 1 < nk) HS2_BRIDGE_ISSUE(kb + kStages - 1, (kb + kStages - 1) % kStages);
+    const uint8_t* s = lds + (kb % kStages) * kStage;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 32; ++ks) {
+      const int cofs = ((4 * ks + grp) ^ swz) * 16;
       bf16x8_t af[4], bfr[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(s + a_rd + i * 16 * kRow + ks * 64);
+        af[i] = *reinterpret_cast<const bf16x8_t*>(s + a_rd + cofs + i * 16 * kRowBytes);
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(s + b_rd + j * 16 * kRow + ks * 64);
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(s + b_rd + cofs + j * 16 * kRowBytes);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
     }
-    if (more) HS2_BRIDGE_LSTORE((kb + 1) & 1);
-    __syncthreads();
   }
+#undef HS2_BRIDGE_ISSUE
 
-#undef HS2_BRIDGE_GLOAD
-#undef HS2_BRIDGE_LSTORE
   // epilogue: wave's head = feature block (n0 + 128 wn) / 128 -> (layer, K|V, KV head)
   const int head = (n0 >> 7) + wn;
   const int layer = head / (2 * a.Hkv);
@@ -182,7 +229,6 @@ __global__ __launch_bounds__(kBThreads, 1) void bridge_kernel(BridgeArgs a) {
   const int g = head % a.Hkv;
   uint8_t* cache = static_cast<uint8_t*>(is_v ? a.vc[layer] : a.kc[layer]);
   float* scales = is_v ? a.vs[layer] : a.ks[layer];
-  const int li = lane & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -221,12 +267,23 @@ __global__ __launch_bounds__(kBThreads, 1) void bridge_kernel(BridgeArgs a) {
 
 }  // namespace
 
+int bridge_tile_tokens(int n_tokens) {
+  return n_tokens >= kLargeMinTokens ? BridgeLarge::kBM : BridgeSmall::kBM;
+}
+
 hipError_t launch_bridge(const BridgeArgs& a, bool fp8, hipStream_t st) {
   const dim3 grid((unsigned)(a.m_tiles * a.n_tiles));
-  if (fp8)
-    hipLaunchKernelGGL((bridge_kernel<true>), grid, dim3(kBThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((bridge_kernel<false>), grid, dim3(kBThreads), 0, st, a);
+  if (bridge_tile_tokens(a.T) == BridgeLarge::kBM) {
+    if (fp8)
+      hipLaunchKernelGGL((bridge_kernel<true, BridgeLarge>), grid, dim3(BridgeLarge::kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((bridge_kernel<false, BridgeLarge>), grid, dim3(BridgeLarge::kThreads), 0, st, a);
+  } else {
+    if (fp8)
+      hipLaunchKernelGGL((bridge_kernel<true, BridgeSmall>), grid, dim3(BridgeSmall::kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((bridge_kernel<false, BridgeSmall>), grid, dim3(BridgeSmall::kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

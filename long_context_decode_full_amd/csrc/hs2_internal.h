@@ -156,6 +156,7 @@ struct BridgeArgs {
   int32_t T, Hd, Hkv, B, n_layers;
   int32_t m_tiles, n_tiles;     // token tiles x feature tiles of the launch
 };
+int bridge_tile_tokens(int n_tokens);   // tokens per workgroup tile launch_bridge uses
 hipError_t launch_bridge(const BridgeArgs& a, bool fp8, hipStream_t st);
 
 hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st);

@@ -99,6 +99,14 @@ SMALL = {
                                                    capacity=129, seed=2103),
     "many_layers_bf16": wl.BridgeWorkload("16 layers", 200, 128, 16, 1, batch=3, capacity=300,
                                           kv_dtype="bf16", placement="ragged", seed=2104),
+    # both sides of the switch from 128- to 256-token tiles (4,096 tokens), ragged tails
+    "below_large_tiles": wl.BridgeWorkload("4095 tokens", 4095, 512, 2, 2, batch=3, capacity=8192,
+                                           placement="ragged", bad_rows=9, seed=2107),
+    "large_tiles_ragged_fp8": wl.BridgeWorkload("4097 tokens", 4097, 512, 2, 2, batch=3, capacity=8192,
+                                                placement="ragged", bad_rows=9, seed=2108),
+    "large_tiles_ragged_bf16": wl.BridgeWorkload("4097 tokens, bf16", 4097, 256, 1, 1, batch=2,
+                                                 capacity=8192, kv_dtype="bf16", placement="ragged",
+                                                 bad_rows=5, seed=2109),
 }
 
 
