@@ -31,6 +31,13 @@ SCAN_SOURCES = [os.path.join(ROOT, "long_context_decode_full_amd", "csrc", f)
 BRIDGE_SOURCES = [os.path.join(ROOT, "long_context_decode_full_amd", "csrc", f)
                   for f in ("hs2_bridge.hip", "hs2_device.h", "hs2_internal.h")]
 BRIDGE_METRIC = "KV Bridging projection tokens/s & MFMA TFLOP/s (%bf16 dense peak)"
+DECODE_METRIC = "Cross-Decoder decode tokens/s (KV Bridging append + 6 Hybrid Blocks per token)"
+DECODE_LOOPS = {
+    # name: (decode workload whose caches every block starts from, blocks, hidden)
+    "decode_loop_million": ("million", 6, 2048),
+    "decode_loop_batched": ("batched", 6, 2048),
+    "decode_loop_tiny": ("tiny", 6, 2048),
+}
 
 
 def log(msg):
@@ -288,6 +295,117 @@ def bench_bridge(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_decode_loop(args):
+    """Multi-step decode (HySparse2 article, section 02): each step appends every
+    sequence's new token to the caches of all Hybrid Blocks through KV Bridging and
+    runs every block's full and sparse layers -- one hs2_decode_step, captured once
+    into a HIP graph and replayed per token."""
+    import dataclasses
+    import torch
+    import oracle
+    from long_context_decode_full_amd import (HS2_TIMER_SCAN, hs2_timer_collect, hs2_timer_enable)
+    from long_context_decode_full_amd import workloads as wl
+    from long_context_decode_full_amd.runner import DecodeLoopDevice
+
+    base, n_blocks, hidden = DECODE_LOOPS[args.workload]
+    w0 = wl.standard_workloads()[base]
+    grow = args.warmup + 2 * args.steps + 64          # graph + eager passes each append
+    w = dataclasses.replace(w0, capacity=max(w0.ctx_lens) + grow)
+    log(f"generating inputs: {w.name}, {n_blocks} blocks, capacity {w.capacity}")
+    inp = wl.make_inputs(w, threads=16)
+    dec = wl.make_decode_steps(w, n_blocks=n_blocks, steps=1, hidden=hidden, seed=4001)
+    dev = DecodeLoopDevice(inp, n_blocks, dec["w_bits"])
+    dev.set_inputs(dec["x"][0], dec["q_full"][0], dec["q_sparse"][0])
+    g = dev.capture()
+    log(f"warmup {args.warmup} replays")
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} replays")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    graph_ms = (t1 - t0) * 1e3 / args.steps
+    # the same steps issued eagerly, the scan kernel timed by the library's events
+    hs2_timer_enable(HS2_TIMER_SCAN)
+    torch.cuda.synchronize()
+    e0 = time.perf_counter()
+    for _ in range(args.steps):
+        dev.step()
+    torch.cuda.synchronize()
+    e1 = time.perf_counter()
+    hs2_timer_enable(False)
+    st, scan_ms, scan_n, _, _ = hs2_timer_collect()
+    assert st == 0 and scan_n == args.steps * n_blocks, (st, scan_n)
+    eager_ms = (e1 - e0) * 1e3 / args.steps
+    ctx = dev.ctx_len.cpu().numpy()
+    Hkv, D = w.n_kv_heads, w.head_dim
+    row_bytes = 2 * D * (1 if w.kv_dtype == "fp8" else 2) + (8 if w.kv_dtype == "fp8" else 0)
+    scan_bytes = int(ctx.sum()) * Hkv * row_bytes
+    scan_s = scan_ms * 1e-3 / scan_n
+    achieved = scan_bytes / scan_s / 1e9
+    result = {
+        "metric": DECODE_METRIC,
+        "value": w.batch / (graph_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": graph_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3fn" if w.kv_dtype == "fp8" else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"decode loop over {n_blocks} Hybrid Blocks ({w.name} caches: B={w.batch}, "
+                        f"ctx {w0.ctx_lens[0]}+, Hq={w.n_q_heads}/Hkv={Hkv}), KV Bridging from hidden "
+                        f"{hidden}, 1 full + {w.n_sparse_layers} sparse layers per block, one HIP graph per step",
+            "batch": w.batch, "n_blocks": n_blocks, "hidden": hidden, "ctx_end": ctx.tolist(),
+        },
+        "eager_ms_per_step": eager_ms,
+        "graph_speedup": eager_ms / graph_ms,
+        "scan_us": scan_s * 1e6,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "kernel": "scan_mfma_kernel (each block's full-attention scan; eager pass, library events)",
+            "algorithmic_bytes_per_launch": scan_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            cores = os.cpu_count()
+        # the oracle for one block of one sequence, and the bridge oracle for its token
+        one = dict(inp, q_full=dec["q_full"][0][0], q_sparse=dec["q_sparse"][0][:w.n_sparse_layers])
+        one["ctx_len"] = inp["ctx_len"].copy()
+        c0 = time.perf_counter()
+        oracle.hybrid_block_token(one, 0, 0)
+        t_block = time.perf_counter() - c0
+        shape = (n_blocks, 1, Hkv, 1, D)
+        caches = dict(k=np.zeros(shape, np.uint16), v=np.zeros(shape, np.uint16))
+        c0 = time.perf_counter()
+        oracle.kv_bridge(dec["x"][0][:1], dec["w_bits"], np.zeros(1, np.int32), np.zeros(1, np.int32), caches)
+        t_bridge = time.perf_counter() - c0
+        per_seq = t_bridge + n_blocks * t_block
+        result["cpu_baseline"] = {
+            "value": 1.0 / per_seq, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 oracle: one Hybrid Block for sequence 0 ({t_block:.2f}s) x {n_blocks} "
+                      f"blocks + the bridge for its token ({t_bridge:.2f}s), per sequence",
+        }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -296,7 +414,8 @@ def main():
                     help="untimed steps first: the GPU reaches its sustained clocks after a few tens of ms")
     ap.add_argument("--workload", default="million",
                     help="tiny | batched | fp8_256k | million | chunk | mqa_million; KV Bridging: "
-                         "bridge_prefill | bridge_prefill_bf16 | bridge_mqa | bridge_decode")
+                         "bridge_prefill | bridge_prefill_bf16 | bridge_mqa | bridge_decode; decode loop: "
+                         "decode_loop_million | decode_loop_batched | decode_loop_tiny")
     ap.add_argument("--select", default="token", choices=["token", "block"],
                     help="token selection (window 128 + top-k 1024) or the first-generation block "
                          "comparator (18 blocks of 64, no forced window)")
@@ -325,6 +444,9 @@ def main():
         return
     if args.workload.startswith("bridge"):
         bench_bridge(args)
+        return
+    if args.workload in DECODE_LOOPS:
+        bench_decode_loop(args)
         return
     from long_context_decode_full_amd import (HS2_TIMER_GATHER, HS2_TIMER_SCAN, hs2_set_deterministic,
                                               hs2_timer_collect, hs2_timer_enable)

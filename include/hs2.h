@@ -194,6 +194,47 @@ hs2_status hs2_kv_bridge(const hs2_bridge_desc* desc, const void* x, const void*
                          float* const* k_scales, float* const* v_scales,
                          hipStream_t stream);
 
+/* ------------------------------------------------------------------ decode step
+ * One generated token for each of `batch` sequences through the Cross-Decoder's
+ * attention: HySparse2 article, section 02 (KV Bridging builds each target Full
+ * layer's cache from the Self-Decoder hidden state; KV Reuse: in every Hybrid Block the
+ * Full layer selects positions from its own attention scores and the Sparse layers
+ * reuse its cache and selection) and section 04 (generation keeps the full network).
+ * In stream order:
+ *   1. pos[b] = ctx_len[b] and ctx_len[b] += 1 (a sequence whose cache is full keeps
+ *      its length and appends nothing);
+ *   2. hs2_kv_bridge of the batch's new source rows x [batch, hidden] into the caches
+ *      of every block (block l = target layer l of w), at (b, pos[b]);
+ *   3. for each block l: hs2_full_attn_select(q_full[l]) into out_full[l], idx[l],
+ *      then hs2_sparse_attn(q_sparse[l * n_sparse + j], idx[l]) into
+ *      out_sparse[l * n_sparse + j] for j < n_sparse.
+ * `attn` describes every block's attention: q_len must be 1 and max_ctx_len bounds
+ * the lengths the step may reach (grids are sized for it, so the step can be
+ * captured once into a HIP graph and replayed while the contexts grow).  q_full,
+ * q_sparse, k/v_caches, k/v_scales, out_full, idx and out_sparse are HOST arrays of
+ * device pointers (n_blocks, or n_blocks * n_sparse, entries); layouts and
+ * alignment as in the calls above.  The step allocates nothing, never synchronises,
+ * and enqueues only kernels (no memset or copy nodes), so it can be captured.  Every
+ * check of every call it makes is done before anything is enqueued; the workspace
+ * (hs2_decode_workspace_size) holds the attention workspace plus the new tokens'
+ * positions. */
+typedef struct hs2_decode_plan {
+  hs2_attn_desc attn;     /* per-block attention; q_len == 1                           */
+  int32_t n_blocks;       /* Hybrid Blocks = bridge target layers: 1 .. 16              */
+  int32_t n_sparse;       /* Sparse layers per block: 0 .. 8 (3 in the article)         */
+  int32_t hidden;         /* hidden size of the bridge source rows                      */
+  int32_t reserved;       /* 0                                                          */
+} hs2_decode_plan;
+
+hs2_status hs2_decode_workspace_size(const hs2_decode_plan* plan, size_t* bytes);
+hs2_status hs2_decode_step(const hs2_decode_plan* plan, const void* x, const void* w,
+                           const void* const* q_full, const void* const* q_sparse,
+                           void* const* k_caches, void* const* v_caches,
+                           float* const* k_scales, float* const* v_scales,
+                           int32_t* ctx_len, float* const* out_full, int32_t* const* idx,
+                           float* const* out_sparse, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 /* Reproducibility switch (process-wide, default off).  By default the waves of a
  * context-scan workgroup share its steps through a counter, so the order in which
  * a head's probabilities are summed into `out` varies between runs and `out` of

@@ -22,7 +22,8 @@ __all__ = [
     "hs2_validate", "hs2_workspace_size", "hs2_full_attn_select", "hs2_sparse_attn",
     "hs2_status_string", "hs2_set_deterministic", "hs2_timer_enable", "hs2_timer_collect", "HS2_TIMER_SCAN",
     "HS2_TIMER_GATHER", "library_path", "load_library", "Hs2BridgeDesc", "make_bridge_desc",
-    "hs2_kv_bridge",
+    "hs2_kv_bridge", "Hs2DecodePlan", "make_decode_plan", "hs2_decode_workspace_size",
+    "hs2_decode_step",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -39,7 +40,8 @@ HS2_SELECT_BLOCK = 1
 
 EXPORTED_SYMBOLS = ("hs2_validate", "hs2_workspace_size", "hs2_full_attn_select",
                     "hs2_sparse_attn", "hs2_status_string", "hs2_set_deterministic",
-                    "hs2_timer_enable", "hs2_timer_collect", "hs2_kv_bridge")
+                    "hs2_timer_enable", "hs2_timer_collect", "hs2_kv_bridge",
+                    "hs2_decode_workspace_size", "hs2_decode_step")
 
 
 class Hs2AttnDesc(ctypes.Structure):
@@ -80,6 +82,21 @@ def make_bridge_desc(n_tokens, hidden, n_layers, n_kv_heads, batch, kv_capacity,
                      kv_dtype=HS2_KV_FP8_E4M3FN) -> Hs2BridgeDesc:
     return Hs2BridgeDesc(int(n_tokens), int(hidden), int(n_layers), int(n_kv_heads), int(head_dim),
                          int(kv_dtype), int(batch), int(kv_capacity))
+
+
+class Hs2DecodePlan(ctypes.Structure):
+    """Mirror of hs2_decode_plan (include/hs2.h)."""
+    _fields_ = [
+        ("attn", Hs2AttnDesc),
+        ("n_blocks", ctypes.c_int32),
+        ("n_sparse", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+def make_decode_plan(attn: Hs2AttnDesc, n_blocks, n_sparse, hidden) -> Hs2DecodePlan:
+    return Hs2DecodePlan(attn, int(n_blocks), int(n_sparse), int(hidden), 0)
 
 
 class Hs2Error(RuntimeError):
@@ -127,6 +144,11 @@ def load_library():
     lib.hs2_sparse_attn.restype = ctypes.c_int
     lib.hs2_kv_bridge.argtypes = [ctypes.POINTER(Hs2BridgeDesc), P, P, P, P, P, P, P, P, P]
     lib.hs2_kv_bridge.restype = ctypes.c_int
+    lib.hs2_decode_workspace_size.argtypes = [ctypes.POINTER(Hs2DecodePlan), ctypes.POINTER(ctypes.c_size_t)]
+    lib.hs2_decode_workspace_size.restype = ctypes.c_int
+    lib.hs2_decode_step.argtypes = [ctypes.POINTER(Hs2DecodePlan), P, P, P, P, P, P, P, P, P, P, P, P,
+                                    P, ctypes.c_size_t, P]
+    lib.hs2_decode_step.restype = ctypes.c_int
     lib.hs2_status_string.argtypes = [ctypes.c_int]
     lib.hs2_status_string.restype = ctypes.c_char_p
     lib.hs2_set_deterministic.argtypes = [ctypes.c_int]
@@ -205,6 +227,27 @@ def hs2_kv_bridge(desc, x, w, seq, pos, k_caches, v_caches, k_scales=None, v_sca
         ctypes.cast(va, ctypes.c_void_p) if va is not None else None,
         ctypes.cast(ksa, ctypes.c_void_p) if ksa is not None else None,
         ctypes.cast(vsa, ctypes.c_void_p) if vsa is not None else None,
+        _stream(stream))
+
+
+def hs2_decode_workspace_size(plan):
+    """Returns (status, bytes)."""
+    n = ctypes.c_size_t(0)
+    st = load_library().hs2_decode_workspace_size(ctypes.byref(plan), ctypes.byref(n))
+    return st, n.value
+
+
+def hs2_decode_step(plan, x, w, q_full, q_sparse, k_caches, v_caches, k_scales, v_scales,
+                    ctx_len, out_full, idx, out_sparse, workspace, workspace_bytes,
+                    stream=None) -> int:
+    """Lists of tensors (or device addresses) are passed as host arrays of pointers.
+    The arrays are built here and live only for the call (the library keeps none)."""
+    arrays = [_ptr_array(v) for v in (q_full, q_sparse, k_caches, v_caches, k_scales, v_scales,
+                                      out_full, idx, out_sparse)]
+    ptrs = [ctypes.cast(a, ctypes.c_void_p) if a is not None else None for a in arrays]
+    return load_library().hs2_decode_step(
+        ctypes.byref(plan), _ptr(x), _ptr(w), ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4],
+        ptrs[5], _ptr(ctx_len), ptrs[6], ptrs[7], ptrs[8], _ptr(workspace), int(workspace_bytes),
         _stream(stream))
 
 

@@ -273,6 +273,18 @@ static hs2_status check_common(const hs2_attn_desc* d, const void* q, const void
   return HS2_OK;
 }
 
+// Which selection path hs2_full_attn_select takes, and whether it has one for this call.
+static bool use_record_path(const hs2_attn_desc* d, const Layout& L, const float* probs) {
+  return L.fast_ok && probs == nullptr && (wide_group(d) || env_int("HS2_FORCE_LOGITS", 0) == 0);
+}
+static hs2_status full_path_supported(const hs2_attn_desc* d, const Layout& L, const float* probs) {
+  const bool fast = use_record_path(d, L, probs);
+  const bool cblock = chunk_block_path(d) && probs == nullptr;
+  if (!fast && !cblock && !L.logits_ok) return HS2_ERR_UNSUPPORTED;
+  if (!fast && wide_group(d)) return HS2_ERR_UNSUPPORTED;
+  return HS2_OK;
+}
+
 static ScanArgs scan_args(const hs2_attn_desc* d, const Layout& L, const void* q, const void* k,
                           const void* v, const float* ks, const float* vs, const int32_t* ctx_len,
                           uint8_t* ws) {
@@ -364,10 +376,10 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   // Record path (default for token selection): compact bound records, exact
   // re-scoring of the candidates.  Logits path: every position's logits, needed
   // when the caller wants all probabilities (probs) or for the block comparator.
-  const bool fast = L.fast_ok && probs == nullptr && (wide_group(desc) || env_int("HS2_FORCE_LOGITS", 0) == 0);
+  const bool fast = use_record_path(desc, L, probs);
   const bool cblock = chunk_block_path(desc) && probs == nullptr;
-  if (!fast && !cblock && !L.logits_ok) return HS2_ERR_UNSUPPORTED;
-  if (!fast && wide_group(desc)) return HS2_ERR_UNSUPPORTED;
+  s = full_path_supported(desc, L, probs);
+  if (s != HS2_OK) return s;
   ScanArgs sa = scan_args(desc, L, q, k, v, k_scale, v_scale, ctx_len, ws);
   if (cblock) return chunk_block_select(desc, L, sa, ctx_len, out, idx, ws, stream);
   sa.logits = reinterpret_cast<float*>(ws + L.off_logits);
@@ -578,11 +590,11 @@ HS2_API hs2_status hs2_timer_collect(double* scan_ms, int32_t* scan_count, doubl
   return st;
 }
 
-HS2_API hs2_status hs2_kv_bridge(const hs2_bridge_desc* d, const void* x, const void* w,
-                                 const int32_t* seq, const int32_t* pos,
-                                 void* const* k_caches, void* const* v_caches,
-                                 float* const* k_scales, float* const* v_scales,
-                                 hipStream_t stream) {
+// Every check of hs2_kv_bridge; fills the launch arguments.  *empty: nothing to launch.
+static hs2_status bridge_prepare(const hs2_bridge_desc* d, const void* x, const void* w,
+                                 const int32_t* seq, const int32_t* pos, void* const* k_caches,
+                                 void* const* v_caches, float* const* k_scales,
+                                 float* const* v_scales, BridgeArgs* out, bool* empty) {
   if (d == nullptr) return HS2_ERR_INVALID_ARG;
   if (d->n_tokens < 0 || d->hidden < 1 || d->n_layers < 1 || d->n_kv_heads < 1 ||
       d->batch < 1 || d->kv_capacity < 1)
@@ -615,7 +627,6 @@ HS2_API hs2_status hs2_kv_bridge(const hs2_bridge_desc* d, const void* x, const 
   const int64_t n_tiles = n_feat / 256;
   const int64_t m_tiles = ceil_div(d->n_tokens, bridge_tile_tokens(d->n_tokens));
   if (m_tiles * n_tiles > INT32_MAX) return HS2_ERR_UNSUPPORTED;
-  if (d->n_tokens == 0) return HS2_OK;
   a.x = static_cast<const uint16_t*>(x);
   a.w = static_cast<const uint16_t*>(w);
   a.seq = seq;
@@ -628,6 +639,128 @@ HS2_API hs2_status hs2_kv_bridge(const hs2_bridge_desc* d, const void* x, const 
   a.n_layers = d->n_layers;
   a.m_tiles = (int32_t)m_tiles;
   a.n_tiles = (int32_t)n_tiles;
+  *out = a;
+  *empty = d->n_tokens == 0;
+  return HS2_OK;
+}
+
+HS2_API hs2_status hs2_kv_bridge(const hs2_bridge_desc* d, const void* x, const void* w,
+                                 const int32_t* seq, const int32_t* pos,
+                                 void* const* k_caches, void* const* v_caches,
+                                 float* const* k_scales, float* const* v_scales,
+                                 hipStream_t stream) {
+  BridgeArgs a{};
+  bool empty = false;
+  const hs2_status s = bridge_prepare(d, x, w, seq, pos, k_caches, v_caches, k_scales, v_scales,
+                                      &a, &empty);
+  if (s != HS2_OK || empty) return s;
+  const bool fp8 = d->kv_dtype == HS2_KV_FP8_E4M3FN;
   if (launch_bridge(a, fp8, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+  return HS2_OK;
+}
+
+// ---------------------------------------------------------------- decode step
+namespace {
+
+struct DecodeWs {
+  size_t attn = 0, off_seq = 0, off_pos = 0, total = 0;
+};
+
+hs2_status decode_layout(const hs2_decode_plan* p, DecodeWs* w) {
+  if (p == nullptr) return HS2_ERR_INVALID_ARG;
+  const hs2_status s = validate_desc(&p->attn);
+  if (s != HS2_OK) return s;
+  if (p->attn.q_len != 1) return HS2_ERR_INVALID_ARG;
+  if (p->n_blocks < 1 || p->n_sparse < 0 || p->hidden < 1) return HS2_ERR_INVALID_ARG;
+  if (p->n_blocks > kMaxBridgeLayers || p->n_sparse > kMaxDecodeSparse) return HS2_ERR_UNSUPPORTED;
+  w->attn = make_layout(&p->attn).total;
+  w->off_seq = align_up(w->attn);
+  w->off_pos = align_up(w->off_seq + (size_t)p->attn.batch * sizeof(int32_t));
+  w->total = align_up(w->off_pos + (size_t)p->attn.batch * sizeof(int32_t));
+  return HS2_OK;
+}
+
+}  // namespace
+
+HS2_API hs2_status hs2_decode_workspace_size(const hs2_decode_plan* plan, size_t* bytes) {
+  DecodeWs w;
+  const hs2_status s = decode_layout(plan, &w);
+  if (s != HS2_OK) return s;
+  if (bytes == nullptr) return HS2_ERR_INVALID_ARG;
+  *bytes = w.total;
+  return HS2_OK;
+}
+
+HS2_API hs2_status hs2_decode_step(const hs2_decode_plan* plan, const void* x, const void* w,
+                                   const void* const* q_full, const void* const* q_sparse,
+                                   void* const* k_caches, void* const* v_caches,
+                                   float* const* k_scales, float* const* v_scales,
+                                   int32_t* ctx_len, float* const* out_full,
+                                   int32_t* const* idx, float* const* out_sparse,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  DecodeWs wl;
+  hs2_status s = decode_layout(plan, &wl);
+  if (s != HS2_OK) return s;
+  const hs2_attn_desc* d = &plan->attn;
+  const int nb = plan->n_blocks, ns = plan->n_sparse;
+  const bool fp8 = d->kv_dtype == HS2_KV_FP8_E4M3FN;
+  if (!q_full || !k_caches || !v_caches || !ctx_len || !out_full || !idx || !workspace)
+    return HS2_ERR_INVALID_ARG;
+  if (ns > 0 && (!q_sparse || !out_sparse)) return HS2_ERR_INVALID_ARG;
+  if (fp8 && (!k_scales || !v_scales)) return HS2_ERR_INVALID_ARG;
+  if (!aligned(workspace, 16)) return HS2_ERR_ALIGNMENT;
+  if (workspace_bytes < wl.total) return HS2_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* seq = reinterpret_cast<int32_t*>(ws + wl.off_seq);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + wl.off_pos);
+
+  // every check of every call below, before anything is enqueued
+  hs2_bridge_desc bd{};
+  bd.n_tokens = d->batch;
+  bd.hidden = plan->hidden;
+  bd.n_layers = nb;
+  bd.n_kv_heads = d->n_kv_heads;
+  bd.head_dim = d->head_dim;
+  bd.kv_dtype = d->kv_dtype;
+  bd.batch = d->batch;
+  bd.kv_capacity = d->kv_capacity;
+  BridgeArgs ba{};
+  bool empty = false;
+  s = bridge_prepare(&bd, x, w, seq, pos, k_caches, v_caches, k_scales, v_scales, &ba, &empty);
+  if (s != HS2_OK) return s;
+  for (int l = 0; l < nb; ++l) {
+    const float* ks = fp8 ? k_scales[l] : nullptr;
+    const float* vs = fp8 ? v_scales[l] : nullptr;
+    Layout L;
+    s = check_common(d, q_full[l], k_caches[l], v_caches[l], ks, vs, ctx_len, out_full[l], idx[l],
+                     workspace, wl.attn, &L);
+    if (s != HS2_OK) return s;
+    s = full_path_supported(d, L, nullptr);
+    if (s != HS2_OK) return s;
+    for (int j = 0; j < ns; ++j) {
+      s = check_common(d, q_sparse[l * ns + j], k_caches[l], v_caches[l], ks, vs, ctx_len,
+                       out_sparse[l * ns + j], idx[l], workspace, wl.attn, &L);
+      if (s != HS2_OK) return s;
+    }
+  }
+
+  // 1. positions of the new tokens; contexts grow by one
+  if (launch_advance(ctx_len, seq, pos, d->batch, d->kv_capacity, stream) != hipSuccess)
+    return HS2_ERR_LAUNCH;
+  // 2. KV Bridging: the new tokens' K/V rows into every block's cache
+  if (launch_bridge(ba, fp8, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+  // 3. every Hybrid Block: the full layer selects, its sparse layers reuse the selection
+  for (int l = 0; l < nb; ++l) {
+    const float* ks = fp8 ? k_scales[l] : nullptr;
+    const float* vs = fp8 ? v_scales[l] : nullptr;
+    s = hs2_full_attn_select(d, q_full[l], k_caches[l], v_caches[l], ks, vs, ctx_len, out_full[l],
+                             idx[l], nullptr, workspace, wl.attn, stream);
+    if (s != HS2_OK) return s;
+    for (int j = 0; j < ns; ++j) {
+      s = hs2_sparse_attn(d, q_sparse[l * ns + j], k_caches[l], v_caches[l], ks, vs, ctx_len,
+                          idx[l], out_sparse[l * ns + j], workspace, wl.attn, stream);
+      if (s != HS2_OK) return s;
+    }
+  }
   return HS2_OK;
 }

@@ -288,3 +288,35 @@ hipError_t launch_bridge(const BridgeArgs& a, bool fp8, hipStream_t st) {
 }
 
 }  // namespace hs2
+
+// ---------------------------------------------------------------- decode step helper
+namespace hs2 {
+namespace {
+
+// One new token per sequence: its cache position is the current context length, after
+// which the context grows by one (HySparse2 article, section 02: the Cross-Decoder's
+// caches grow by the bridged K/V of each generated token).  A sequence whose cache is
+// full (or whose length is invalid) gets position -1, which the bridge skips, and
+// keeps its length.
+__global__ void advance_kernel(int32_t* ctx_len, int32_t* seq, int32_t* pos, int B, int64_t cap) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int32_t c = ctx_len[b];
+  seq[b] = b;
+  if (c >= 0 && (int64_t)c < cap) {
+    pos[b] = c;
+    ctx_len[b] = c + 1;
+  } else {
+    pos[b] = -1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_advance(int32_t* ctx_len, int32_t* seq, int32_t* pos, int B, int64_t cap,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(advance_kernel, dim3((B + 255) / 256), dim3(256), 0, st, ctx_len, seq, pos, B, cap);
+  return hipGetLastError();
+}
+
+}  // namespace hs2

@@ -143,6 +143,7 @@ struct FastSelArgs {
 // layer of the call, rounded (bf16) or quantised (E4M3FN + per-row scale) and
 // written to cache row (seq[t], KV head, pos[t]) of the target layer.
 constexpr int kMaxBridgeLayers = 16;
+constexpr int kMaxDecodeSparse = 8;     // sparse layers per Hybrid Block in one decode step
 struct BridgeArgs {
   const uint16_t* x;        // [T, Hd] bf16
   const uint16_t* w;        // [L * 2 * Hkv * 128, Hd] bf16 (W_k,l then W_v,l per layer)
@@ -158,6 +159,9 @@ struct BridgeArgs {
 };
 int bridge_tile_tokens(int n_tokens);   // tokens per workgroup tile launch_bridge uses
 hipError_t launch_bridge(const BridgeArgs& a, bool fp8, hipStream_t st);
+// decode step: pos[b] = ctx_len[b] and ctx_len[b] += 1 (pos -1 and no change when full)
+hipError_t launch_advance(int32_t* ctx_len, int32_t* seq, int32_t* pos, int B, int64_t cap,
+                          hipStream_t st);
 
 hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st);
 hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t st);

@@ -13,8 +13,9 @@ import numpy as np
 import torch
 
 from . import (HS2_KV_BF16, HS2_KV_FP8_E4M3FN, HS2_OK, HS2_SELECT_BLOCK, HS2_SELECT_TOKEN,
-               Hs2Error, hs2_full_attn_select, hs2_kv_bridge, hs2_sparse_attn, hs2_workspace_size,
-               make_bridge_desc, make_desc)
+               Hs2Error, hs2_decode_step, hs2_decode_workspace_size, hs2_full_attn_select,
+               hs2_kv_bridge, hs2_sparse_attn, hs2_workspace_size, make_bridge_desc,
+               make_decode_plan, make_desc)
 
 
 def _dev(a: np.ndarray, device):
@@ -153,3 +154,103 @@ class BridgeDevice:
             return dict(k=k.view(np.uint16), v=v.view(np.uint16))
         return dict(k=k, v=v, k_scale=torch.stack(self.ks).cpu().numpy(),
                     v_scale=torch.stack(self.vs).cpu().numpy())
+
+
+class DecodeLoopDevice:
+    """Device state of a multi-step decode through the Cross-Decoder's attention
+    (HySparse2 article, section 02: KV Bridging appends each new token's K/V to every
+    Full layer's cache; each Hybrid Block's full layer selects, its sparse layers
+    reuse the selection).  n_blocks Hybrid Blocks, each with its own cache, all
+    starting from the caches of `inp` (as built by workloads.make_inputs); the bridge
+    weights `w_bits` [n_blocks, 2, Hkv*128, hidden]; per step the new tokens' source
+    rows and every layer's queries are copied into fixed input slots, so one step can
+    be captured in a HIP graph and replayed (hs2_decode_step enqueues only kernels)."""
+
+    def __init__(self, inp: dict, n_blocks: int, w_bits: np.ndarray, device="cuda",
+                 max_ctx_len=None, window=128, topk=1024):
+        self.device = dv = torch.device(device)
+        B, Lq, Hq, D = inp["q_full"].shape
+        assert Lq == 1, "decode: one query token per sequence"
+        Hkv, cap = inp["k"].shape[1], inp["k"].shape[2]
+        self.fp8 = inp["k"].dtype == np.uint8
+        self.B, self.Hq, self.Hkv, self.cap, self.D = B, Hq, Hkv, cap, D
+        self.nb, self.ns = n_blocks, len(inp["q_sparse"])
+        self.hidden = w_bits.shape[-1]
+        mctx = int(max_ctx_len if max_ctx_len is not None else cap)
+        self.desc = make_desc(B, 1, Hq, Hkv, cap, mctx, head_dim=D,
+                              kv_dtype=HS2_KV_FP8_E4M3FN if self.fp8 else HS2_KV_BF16,
+                              window=window, topk=topk, sm_scale=inp["sm_scale"])
+        self.plan = make_decode_plan(self.desc, n_blocks, self.ns, self.hidden)
+        k0, v0 = _dev(inp["k"], dv), _dev(inp["v"], dv)
+        self.k = [k0.clone() for _ in range(n_blocks)]
+        self.v = [v0.clone() for _ in range(n_blocks)]
+        if self.fp8:
+            ks0, vs0 = _dev(inp["k_scale"], dv), _dev(inp["v_scale"], dv)
+            self.ks = [ks0.clone() for _ in range(n_blocks)]
+            self.vs = [vs0.clone() for _ in range(n_blocks)]
+        else:
+            self.ks = self.vs = None
+        del k0, v0
+        self.ctx_len = _dev(inp["ctx_len"].astype(np.int32), dv)
+        self.w = _dev(w_bits, dv)
+        self.x = torch.zeros((B, self.hidden), dtype=torch.int16, device=dv)
+        self.q_full = [torch.zeros((B, 1, Hq, D), dtype=torch.int16, device=dv) for _ in range(n_blocks)]
+        self.q_sparse = [torch.zeros((B, 1, Hq, D), dtype=torch.int16, device=dv)
+                         for _ in range(n_blocks * self.ns)]
+        self.out_full = [torch.zeros((B, 1, Hq, D), dtype=torch.float32, device=dv) for _ in range(n_blocks)]
+        self.idx = [torch.full((B, 1, Hkv, window + topk), -7, dtype=torch.int32, device=dv)
+                    for _ in range(n_blocks)]
+        self.out_sparse = [torch.zeros((B, 1, Hq, D), dtype=torch.float32, device=dv)
+                           for _ in range(n_blocks * self.ns)]
+        st, nbytes = hs2_decode_workspace_size(self.plan)
+        if st != HS2_OK:
+            raise Hs2Error(st, "hs2_decode_workspace_size")
+        self.ws_bytes = nbytes
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dv)
+
+    def set_inputs(self, x_bits, q_full_bits, q_sparse_bits):
+        """x_bits [B, hidden]; q_full_bits: n_blocks arrays [B, 1, Hq, D]; q_sparse_bits:
+        n_blocks * n_sparse arrays (block-major) -- copied into the input slots."""
+        self.x.copy_(torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)))
+        for dst, src in zip(self.q_full, q_full_bits):
+            dst.copy_(torch.from_numpy(np.ascontiguousarray(src).view(np.int16)))
+        for dst, src in zip(self.q_sparse, q_sparse_bits):
+            dst.copy_(torch.from_numpy(np.ascontiguousarray(src).view(np.int16)))
+
+    def step(self, stream=None):
+        st = hs2_decode_step(self.plan, self.x, self.w, self.q_full, self.q_sparse, self.k, self.v,
+                             self.ks, self.vs, self.ctx_len, self.out_full, self.idx, self.out_sparse,
+                             self.workspace, self.ws_bytes, stream)
+        if st != HS2_OK:
+            raise Hs2Error(st, "hs2_decode_step")
+
+    def capture(self):
+        """One step captured into a HIP graph (torch.cuda.CUDAGraph); nothing runs until
+        replay().  The graph reads the input slots and the device-side ctx_len."""
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize(self.device)
+        with torch.cuda.graph(g):
+            self.step()
+        torch.cuda.synchronize(self.device)
+        return g
+
+    def state(self) -> dict:
+        torch.cuda.synchronize(self.device)
+        out = dict(ctx_len=self.ctx_len.cpu().numpy(),
+                   out_full=[o.cpu().numpy() for o in self.out_full],
+                   idx=[i.cpu().numpy() for i in self.idx],
+                   out_sparse=[o.cpu().numpy() for o in self.out_sparse])
+        return out
+
+    def block_inputs(self, l: int, q_full_bits, q_sparse_bits) -> dict:
+        """Block l's caches as they are now, with the given queries, in the layout of
+        workloads.make_inputs (for the oracle)."""
+        torch.cuda.synchronize(self.device)
+        kt = np.uint8 if self.fp8 else np.uint16
+        d = dict(q_full=np.asarray(q_full_bits), q_sparse=[np.asarray(q) for q in q_sparse_bits],
+                 k=self.k[l].cpu().numpy().view(kt), v=self.v[l].cpu().numpy().view(kt),
+                 k_scale=self.ks[l].cpu().numpy() if self.fp8 else None,
+                 v_scale=self.vs[l].cpu().numpy() if self.fp8 else None,
+                 ctx_len=self.ctx_len.cpu().numpy(), capacity=self.cap,
+                 sm_scale=float(self.desc.sm_scale))
+        return d

@@ -305,3 +305,35 @@ def bridge_cache_sentinel(kv_dtype: str):
     """Initial cache contents for bridging tests: NaN codes and NaN scales, so that a
     row written by mistake or left unwritten shows."""
     return (E4M3FN_NAN, np.float32(np.nan)) if kv_dtype == "fp8" else (BF16_NAN, None)
+
+
+def make_decode_steps(w: Workload, n_blocks: int, steps: int, hidden: int, seed: int,
+                      outlier_channels: int = 4, outlier_scale: float = 8.0) -> dict:
+    """Per-step inputs of a multi-step decode over n_blocks Hybrid Blocks that all start
+    from the caches of make_inputs(w): the bridge weights of every block and, for each
+    step, the new tokens' source rows and every layer's queries.
+
+      w_bits     [n_blocks, 2, Hkv * 128, hidden] bf16 bits, N(0, 1 / hidden)
+      x[t]       [B, hidden] bf16 bits, N(0, 1) with `outlier_channels` channels scaled
+      q_full[t]  n_blocks arrays [B, 1, Hq, 128] bf16 bits, N(0, 1)
+      q_sparse[t] n_blocks * n_sparse arrays (block-major), N(0, 1)
+    """
+    B, Hq, Hkv, D = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    ns = w.n_sparse_layers
+    root = np.random.SeedSequence(seed)
+    s_w, s_x, s_q, s_o = root.spawn(4)
+    wt = np.random.default_rng(s_w).standard_normal((n_blocks, 2, Hkv * D, hidden), dtype=np.float32)
+    wt *= np.float32(1.0 / math.sqrt(hidden))
+    ch = np.random.default_rng(s_o).choice(hidden, size=min(outlier_channels, hidden), replace=False)
+    rx = np.random.default_rng(s_x)
+    rq = np.random.default_rng(s_q)
+    xs, qf, qs = [], [], []
+    for _ in range(steps):
+        x = rx.standard_normal((B, hidden), dtype=np.float32)
+        x[:, ch] *= np.float32(outlier_scale)
+        xs.append(f32_to_bf16_bits(x))
+        qf.append([f32_to_bf16_bits(rq.standard_normal((B, 1, Hq, D), dtype=np.float32))
+                   for _ in range(n_blocks)])
+        qs.append([f32_to_bf16_bits(rq.standard_normal((B, 1, Hq, D), dtype=np.float32))
+                   for _ in range(n_blocks * ns)])
+    return dict(w_bits=f32_to_bf16_bits(wt), x=xs, q_full=qf, q_sparse=qs)

@@ -267,3 +267,75 @@ def test_bridge_bf16_needs_no_scales_and_zero_tokens_enqueue_nothing(lib):
     assert _bridge(desc=d, fp8=False) == hs2.HS2_OK
     d8 = hs2.make_bridge_desc(0, 512, 2, 2, 4, 4096)
     assert _bridge(desc=d8, fp8=True, k_scales=None) == hs2.HS2_ERR_INVALID_ARG
+
+
+# ----------------------------------------------------------------------------- decode step
+def test_decode_plan_struct_layout_matches_header():
+    # hs2_attn_desc (64 bytes) then four int32
+    assert ctypes.sizeof(hs2.Hs2DecodePlan) == 80
+    assert hs2.Hs2DecodePlan.n_blocks.offset == 64
+    assert hs2.Hs2DecodePlan.hidden.offset == 72
+
+
+def _plan(**kw):
+    attn = _desc(kv_capacity=8192, max_ctx_len=8192)
+    p = dict(n_blocks=2, n_sparse=3, hidden=512)
+    p.update(kw)
+    return hs2.make_decode_plan(attn, p["n_blocks"], p["n_sparse"], p["hidden"])
+
+
+def _step(plan, **over):
+    nb, ns = plan.n_blocks, plan.n_sparse
+    st, need = hs2.hs2_decode_workspace_size(plan)
+    need = need if st == hs2.HS2_OK else 1 << 20
+    args = dict(x=_GOOD, w=_GOOD + 0x1000000, q_full=[_GOOD + 0x10000 * (i + 1) for i in range(nb)],
+                q_sparse=[_GOOD + 0x20000 * (i + 1) for i in range(nb * ns)],
+                k_caches=[_GOOD + 0x4000000 * (i + 1) for i in range(nb)],
+                v_caches=[_GOOD + 0x4000000 * (i + 1) + 0x2000000 for i in range(nb)],
+                k_scales=None, v_scales=None, ctx_len=_GOOD + 0x3000000,
+                out_full=[_GOOD + 0x40000 * (i + 1) for i in range(nb)],
+                idx=[_GOOD + 0x80000 * (i + 1) for i in range(nb)],
+                out_sparse=[_GOOD + 0x100000 * (i + 1) for i in range(nb * ns)],
+                workspace=_GOOD + 0x8000000, workspace_bytes=need)
+    args.update(over)
+    return hs2.hs2_decode_step(plan, stream=0, **args)
+
+
+def test_decode_workspace_size_covers_attention(lib):
+    st, n = hs2.hs2_decode_workspace_size(_plan())
+    st2, n_attn = hs2.hs2_workspace_size(_desc(kv_capacity=8192, max_ctx_len=8192))
+    assert st == st2 == hs2.HS2_OK and n >= n_attn + 2 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_blocks=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(n_blocks=17), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(n_sparse=-1), hs2.HS2_ERR_INVALID_ARG),
+    (dict(n_sparse=9), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(hidden=0), hs2.HS2_ERR_INVALID_ARG),
+])
+def test_decode_plan_checks(lib, kw, status):
+    p = _plan(**kw)
+    assert hs2.hs2_decode_workspace_size(p)[0] == status
+    assert _step(p) == status
+
+
+def test_decode_step_needs_single_query_token(lib):
+    p = _plan()
+    p.attn.q_len = 2
+    assert _step(p) == hs2.HS2_ERR_INVALID_ARG
+
+
+def test_decode_step_argument_checks_before_any_launch(lib):
+    p = _plan()
+    assert _step(p, workspace_bytes=100) == hs2.HS2_ERR_WORKSPACE
+    assert _step(p, ctx_len=None) == hs2.HS2_ERR_INVALID_ARG
+    assert _step(p, q_sparse=None) == hs2.HS2_ERR_INVALID_ARG
+    assert _step(p, idx=[_GOOD, 0]) == hs2.HS2_ERR_INVALID_ARG
+    assert _step(p, out_sparse=[_GOOD] * 5 + [0]) == hs2.HS2_ERR_INVALID_ARG
+    assert _step(p, x=_GOOD + 8) == hs2.HS2_ERR_ALIGNMENT           # bridge source row
+    assert _step(_plan(hidden=100)) == hs2.HS2_ERR_UNSUPPORTED                # bridge hidden size
+    assert _step(p, k_caches=[_GOOD, _GOOD + 8]) == hs2.HS2_ERR_ALIGNMENT
+    p8 = _plan()
+    p8.attn.kv_dtype = hs2.HS2_KV_FP8_E4M3FN
+    assert _step(p8) == hs2.HS2_ERR_INVALID_ARG                      # fp8 without scales
