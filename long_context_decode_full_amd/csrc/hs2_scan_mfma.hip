@@ -296,34 +296,6 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
       }
     }
 
-  // bound records: e = log2 sum over the group's heads of 2^l
-  if constexpr (!kGather)
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float lm[kHB];
-      float rmax = kNegInf;
-#pragma unroll
-      for (int hb = 0; hb < kHB; ++hb) {
-        lm[hb] = 16 * hb + w16 < G ? l[hb][t][v] : kNegInf;
-        rmax = fmaxf(rmax, lm[hb]);
-      }
-      rmax = kWide ? max16w(rmax) : max8(rmax);
-      float ex = 0.0f;
-#pragma unroll
-      for (int hb = 0; hb < kHB; ++hb) ex += lm[hb] != kNegInf ? fast_exp2(lm[hb] - rmax) : 0.0f;
-      const float sum = kWide ? sum16w(ex) : sum8(ex);
-      const float e = rmax + __builtin_amdgcn_logf(sum);
-      const int32_t row = base + 16 * t + 4 * grp + v;
-      const uint32_t rel = (uint32_t)(row - w_begin);
-      if (w16 == 0 && row < w_end) {
-        const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)e);
-        recs[rel] = rec;
-        if (rel < cand_span) atomicAdd(&shist[half_order_key(rec) >> kFastShift], 1u);
-      }
-    }
-
   // online softmax of head 16 hb + w16
   bool up[kHB];
   bool up_any = false;
@@ -345,6 +317,20 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
     }
   }
   bf16x8_t phi[kHB], plo[kHB];
+  float rsum[2][4];                     // records: sum over this lane's head blocks of p 2^(m - U)
+  float U = kNegInf, c[kHB];
+  if constexpr (!kGather) {
+    // U: the largest running maximum of the group's heads (equal in every lane)
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb) U = fmaxf(U, 16 * hb + w16 < G ? hs[hb].m : kNegInf);
+    U = kWide ? max16w(U) : max8(U);
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb) c[hb] = 16 * hb + w16 < G ? fast_exp2(hs[hb].m - U) : 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) rsum[t][v] = 0.0f;
+  }
 #pragma unroll
   for (int hb = 0; hb < kHB; ++hb) {
     float p[2][4];
@@ -354,6 +340,7 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
       for (int v = 0; v < 4; ++v) {
         p[t][v] = l[hb][t][v] != kNegInf ? fast_exp2(l[hb][t][v] - hs[hb].m) : 0.0f;
         hs[hb].z += p[t][v];
+        if constexpr (!kGather) rsum[t][v] = fmaf(p[t][v], c[hb], rsum[t][v]);
         // masked rows: the scale may come from a row past the end (4-row scale loads)
         if constexpr (kFp8) p[t][v] = l[hb][t][v] != kNegInf ? p[t][v] * s.vs[t][v] : 0.0f;
       }
@@ -368,6 +355,56 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
     }
     phi[hb] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
     plo[hb] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+  }
+
+  // bound records: e = log2 sum over the group's heads of 2^l.  With p = 2^(l - m) of
+  // each head (formed above for P.V), sum_h 2^l_h = 2^U sum_h p_h 2^(m_h - U); a live
+  // row whose sum is below 2^-100 (terms lost to underflow could matter there) makes
+  // the wave take the direct form, max then sum of 2^(l - max), for the step.
+  if constexpr (!kGather) {
+    float e[2][4];
+    bool tiny = false;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float sm = kWide ? sum16w(rsum[t][v]) : sum8(rsum[t][v]);
+        const int32_t row = base + 16 * t + 4 * grp + v;
+        tiny |= row < w_end && !(sm >= 0x1p-100f);
+        e[t][v] = U + __builtin_amdgcn_logf(sm);
+      }
+    if (wave_any(tiny)) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float lm[kHB];
+          float rmax = kNegInf;
+#pragma unroll
+          for (int hb = 0; hb < kHB; ++hb) {
+            lm[hb] = 16 * hb + w16 < G ? l[hb][t][v] : kNegInf;
+            rmax = fmaxf(rmax, lm[hb]);
+          }
+          rmax = kWide ? max16w(rmax) : max8(rmax);
+          float ex = 0.0f;
+#pragma unroll
+          for (int hb = 0; hb < kHB; ++hb) ex += lm[hb] != kNegInf ? fast_exp2(lm[hb] - rmax) : 0.0f;
+          const float sum = kWide ? sum16w(ex) : sum8(ex);
+          e[t][v] = rmax + __builtin_amdgcn_logf(sum);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int32_t row = base + 16 * t + 4 * grp + v;
+        const uint32_t rel = (uint32_t)(row - w_begin);
+        if (w16 == 0 && row < w_end) {
+          const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)e[t][v]);
+          recs[rel] = rec;
+          if (rel < cand_span) atomicAdd(&shist[half_order_key(rec) >> kFastShift], 1u);
+        }
+      }
   }
 
   // PV: A = V^T of dim block b, rows 4grp..4grp+3 of both tiles (transposed LDS reads)
