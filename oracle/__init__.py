@@ -30,6 +30,12 @@ from .hybrid_block import (  # noqa: F401
     hybrid_block,
     hybrid_block_token,
 )
+from .gen1 import (  # noqa: F401
+    local_rows,
+    local_kv,
+    swa_branch,
+    gen1_sparse_layer,
+)
 from .bridge import (  # noqa: F401
     bf16_rne,
     e4m3fn_encode,

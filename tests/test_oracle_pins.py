@@ -341,3 +341,56 @@ def test_fp8_path_uses_dequantised_values():
     assert K[17, 3] == tab[inp["k"][0, 1, 17, 3]] * float(inp["k_scale"][0, 1, 17])
     # the per-row scale maps the largest magnitude to 448 (up to fp32 rounding of the scale)
     assert np.all(np.abs(np.abs(K).max(axis=1) / inp["k_scale"][0, 1] - 448) <= 448 * 2 ** -3)
+
+
+# ----------------------------------------------------------------------------- gen-1 comparator
+def test_gen1_ring_rows_match_a_linear_cache():
+    """The ring layout (position p at row p % R) gives the same branch output as the
+    window's rows taken from a linear cache of every position."""
+    rng = np.random.default_rng(41)
+    n_total, R, W, D = 300, 140, 128, 128
+    lin_k = rng.standard_normal((n_total, D))
+    lin_v = rng.standard_normal((n_total, D))
+    ring_k = np.zeros((R, D))
+    ring_v = np.zeros((R, D))
+    for p in range(n_total):                      # the ring keeps the last R positions
+        ring_k[p % R] = lin_k[p]
+        ring_v[p % R] = lin_v[p]
+    q = rng.standard_normal((4, D))
+    for n in (n_total, n_total - 5, n_total - 12):   # query tokens of a 13-token chunk
+        got = oracle.swa_branch(q, ring_k, ring_v, n, W, 0.1)
+        ref, _ = oracle.full_attention(q, lin_k[n - W:n], lin_v[n - W:n], 0.1)
+        assert np.allclose(got, ref, rtol=0, atol=1e-13)
+    # fewer than W visible positions: all of them
+    got = oracle.swa_branch(q, ring_k, ring_v, 50, W, 0.1)
+    assert list(oracle.local_rows(50, W, R)) == list(range(50))
+    assert list(oracle.local_rows(300, 128, 140)) == [p % 140 for p in range(172, 300)]
+
+
+def test_gen1_branch_against_torch_sdpa():
+    rng = np.random.default_rng(42)
+    R, W, D, G = 200, 128, 128, 8
+    K = rng.standard_normal((R, D))
+    V = rng.standard_normal((R, D))
+    q = rng.standard_normal((G, D))
+    n = 333
+    rows = [(p % R) for p in range(n - W, n)]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(K[rows])[None], torch.from_numpy(V[rows])[None],
+        scale=1 / math.sqrt(D))[0].numpy()
+    assert np.allclose(oracle.swa_branch(q, K, V, n, W, 1 / math.sqrt(D)), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_gen1_layer_is_the_sum_of_its_branches():
+    rng = np.random.default_rng(43)
+    n, R, W, D, G = 900, 130, 128, 128, 4
+    K, V = rng.standard_normal((n, D)), rng.standard_normal((n, D))
+    Kl, Vl = rng.standard_normal((R, D)), rng.standard_normal((R, D))
+    q = rng.standard_normal((G, D))
+    idx = np.concatenate([np.arange(64, 128), np.arange(640, 704), -np.ones(10, int)])
+    both = oracle.gen1_sparse_layer(q, K, V, idx, Kl, Vl, n, W, 0.09)
+    shared = oracle.sparse_attention(q, K, V, idx, 0.09)
+    local = oracle.gen1_sparse_layer(q, K, V, np.full(5, -1), Kl, Vl, n, W, 0.09)   # empty selection
+    assert np.allclose(both, shared + local, rtol=0, atol=1e-13)
+    zero_v = oracle.gen1_sparse_layer(q, K, V, idx, Kl, np.zeros_like(Vl), n, W, 0.09)
+    assert np.allclose(zero_v, shared, rtol=0, atol=1e-13)
