@@ -416,9 +416,11 @@ def main():
                     help="tiny | batched | fp8_256k | million | chunk | mqa_million; KV Bridging: "
                          "bridge_prefill | bridge_prefill_bf16 | bridge_mqa | bridge_decode; decode loop: "
                          "decode_loop_million | decode_loop_batched | decode_loop_tiny")
-    ap.add_argument("--select", default="token", choices=["token", "block"],
-                    help="token selection (window 128 + top-k 1024) or the first-generation block "
-                         "comparator (18 blocks of 64, no forced window)")
+    ap.add_argument("--select", default="token", choices=["token", "block", "gen1"],
+                    help="token selection (window 128 + top-k 1024), the first-generation block "
+                         "comparator (18 blocks of 64, no forced window), or the full first-generation "
+                         "comparator (block selection + a separate 128-token sliding-window branch "
+                         "over each sparse layer's own local ring)")
     ap.add_argument("--deterministic", action="store_true",
                     help="fixed step shares in the context scan (bitwise reproducible, slower)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -459,7 +461,11 @@ def main():
     t0 = time.perf_counter()
     inp = wl.make_inputs(w, threads=16)
     log(f"inputs ready in {time.perf_counter() - t0:.1f}s; uploading")
-    dev = HybridBlockDevice(inp, device="cuda:0", mode=args.select)
+    rings = None
+    if args.select == "gen1":
+        # each sparse layer's own local ring: the 128-token window of every query token
+        rings = wl.make_local_rings(w, 128 + w.q_len - 1, seed=w.seed + 100)
+    dev = HybridBlockDevice(inp, device="cuda:0", mode=args.select, local_rings=rings)
     torch.cuda.synchronize()
 
     log(f"warmup {args.warmup}")
@@ -527,8 +533,10 @@ def main():
             "workload": f"{w.name}: B={w.batch}, ctx_len={w.ctx_lens}, q_len={w.q_len}, "
                         f"Hq={w.n_q_heads}/Hkv={w.n_kv_heads}, head_dim={w.head_dim}, "
                         f"{w.kv_dtype} KV, "
-                        + ("window 128 + top-k 1024" if args.select == "token" else
-                           "block comparator: 18 blocks of 64")
+                        + {"token": "window 128 + top-k 1024",
+                           "block": "block comparator: 18 blocks of 64",
+                           "gen1": "first-generation comparator: 18 blocks of 64 + a separate "
+                                   "128-token sliding-window branch per sparse layer"}[args.select]
                         + f", 1 full + {w.n_sparse_layers} sparse layers",
             "batch": w.batch, "ctx_tokens": ctx, "q_len": w.q_len,
             "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "kv_dtype": w.kv_dtype,
@@ -566,6 +574,11 @@ def main():
         }
         result["config"]["ctx_lens"] = [int(c) for c in inp["ctx_len"]]
 
+    if args.select == "gen1":
+        # the oracle's comparator path is checked by tests/test_gpu_gen1.py; its timing
+        # sample would be the block path's plus a 128-row attention per layer
+        args.no_cpu_baseline = True
+        result["sparse_layer_us_note"] = "per branch: each gen-1 sparse layer runs two gathers"
     if not args.no_cpu_baseline:
         Hkv = inp["k"].shape[1]
         groups = list(range(Hkv))

@@ -138,6 +138,30 @@ hs2_status hs2_sparse_attn(const hs2_attn_desc* desc,
 /* Static English text for a status; never NULL. */
 const char* hs2_status_string(hs2_status status);
 
+/* ------------------------------------------------------------ first-generation sparse layer
+ * Comparator, not part of HySparse2: the sparse layer of the first-generation HySparse
+ * (HySparse2 article, section 01: block-level selection by a few Full layers; section
+ * 03: the recent tokens came from an independent sliding-window branch with its own
+ * local KV cache built from the sparse layer's own hidden state, which HySparse2 folds
+ * into the one sparse computation).  out = attention of q over the shared-cache rows
+ * named by idx (as hs2_sparse_attn; normally a block-mode selection), PLUS attention of
+ * q over the layer's own local K/V of the token's window: the positions
+ * [max(0, n - local_window), n) of a query token that sees n positions, held in a ring
+ * k_local / v_local [batch, n_kv_heads, local_rows, 128] at row p % local_rows (with
+ * kl_scale / vl_scale [batch, n_kv_heads, local_rows] for fp8).  Two softmaxes; the
+ * outputs are added (the article gives no gate).  local_rows >= local_window + q_len - 1
+ * (so every query token of a chunk finds its whole window), local_window <= 4096.  The
+ * workspace (hs2_sparse_attn_swa_workspace_size) holds the branches' scratch.  Errors
+ * as hs2_sparse_attn, all returned before anything is enqueued. */
+hs2_status hs2_sparse_attn_swa_workspace_size(const hs2_attn_desc* desc, int32_t local_window,
+                                              int32_t local_rows, size_t* bytes);
+hs2_status hs2_sparse_attn_swa(const hs2_attn_desc* desc, const void* q, const void* k,
+                               const void* v, const float* k_scale, const float* v_scale,
+                               const int32_t* ctx_len, const int32_t* idx, const void* k_local,
+                               const void* v_local, const float* kl_scale, const float* vl_scale,
+                               int32_t local_window, int32_t local_rows, float* out,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ KV Bridging
  * HySparse2 article, section 02 "two-level KV sharing" (KV Bridging: every Full
  * Attention layer of the Cross-Decoder builds its own KV cache from the input hidden

@@ -23,7 +23,7 @@ __all__ = [
     "hs2_status_string", "hs2_set_deterministic", "hs2_timer_enable", "hs2_timer_collect", "HS2_TIMER_SCAN",
     "HS2_TIMER_GATHER", "library_path", "load_library", "Hs2BridgeDesc", "make_bridge_desc",
     "hs2_kv_bridge", "Hs2DecodePlan", "make_decode_plan", "hs2_decode_workspace_size",
-    "hs2_decode_step",
+    "hs2_decode_step", "hs2_sparse_attn_swa_workspace_size", "hs2_sparse_attn_swa",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -41,7 +41,8 @@ HS2_SELECT_BLOCK = 1
 EXPORTED_SYMBOLS = ("hs2_validate", "hs2_workspace_size", "hs2_full_attn_select",
                     "hs2_sparse_attn", "hs2_status_string", "hs2_set_deterministic",
                     "hs2_timer_enable", "hs2_timer_collect", "hs2_kv_bridge",
-                    "hs2_decode_workspace_size", "hs2_decode_step")
+                    "hs2_decode_workspace_size", "hs2_decode_step",
+                    "hs2_sparse_attn_swa_workspace_size", "hs2_sparse_attn_swa")
 
 
 class Hs2AttnDesc(ctypes.Structure):
@@ -149,6 +150,12 @@ def load_library():
     lib.hs2_decode_step.argtypes = [ctypes.POINTER(Hs2DecodePlan), P, P, P, P, P, P, P, P, P, P, P, P,
                                     P, ctypes.c_size_t, P]
     lib.hs2_decode_step.restype = ctypes.c_int
+    lib.hs2_sparse_attn_swa_workspace_size.argtypes = [D, ctypes.c_int32, ctypes.c_int32,
+                                                       ctypes.POINTER(ctypes.c_size_t)]
+    lib.hs2_sparse_attn_swa_workspace_size.restype = ctypes.c_int
+    lib.hs2_sparse_attn_swa.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32,
+                                        P, P, ctypes.c_size_t, P]
+    lib.hs2_sparse_attn_swa.restype = ctypes.c_int
     lib.hs2_status_string.argtypes = [ctypes.c_int]
     lib.hs2_status_string.restype = ctypes.c_char_p
     lib.hs2_set_deterministic.argtypes = [ctypes.c_int]
@@ -249,6 +256,23 @@ def hs2_decode_step(plan, x, w, q_full, q_sparse, k_caches, v_caches, k_scales, 
         ctypes.byref(plan), _ptr(x), _ptr(w), ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4],
         ptrs[5], _ptr(ctx_len), ptrs[6], ptrs[7], ptrs[8], _ptr(workspace), int(workspace_bytes),
         _stream(stream))
+
+
+def hs2_sparse_attn_swa_workspace_size(desc, local_window, local_rows):
+    """Returns (status, bytes)."""
+    n = ctypes.c_size_t(0)
+    st = load_library().hs2_sparse_attn_swa_workspace_size(ctypes.byref(desc), int(local_window),
+                                                           int(local_rows), ctypes.byref(n))
+    return st, n.value
+
+
+def hs2_sparse_attn_swa(desc, q, k, v, k_scale, v_scale, ctx_len, idx, k_local, v_local, kl_scale,
+                        vl_scale, local_window, local_rows, out, workspace, workspace_bytes,
+                        stream=None) -> int:
+    return load_library().hs2_sparse_attn_swa(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), _ptr(ctx_len),
+        _ptr(idx), _ptr(k_local), _ptr(v_local), _ptr(kl_scale), _ptr(vl_scale), int(local_window),
+        int(local_rows), _ptr(out), _ptr(workspace), int(workspace_bytes), _stream(stream))
 
 
 def hs2_status_string(status: int) -> str:

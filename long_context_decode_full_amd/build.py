@@ -7,7 +7,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libhs2.so")
-SOURCES = ["hs2_scan.hip", "hs2_scan_mfma.hip", "hs2_chunk_mfma.hip", "hs2_select.hip", "hs2_select_fast.hip", "hs2_bridge.hip", "hs2_api.cpp"]
+SOURCES = ["hs2_scan.hip", "hs2_scan_mfma.hip", "hs2_chunk_mfma.hip", "hs2_select.hip", "hs2_select_fast.hip", "hs2_bridge.hip", "hs2_swa.hip", "hs2_api.cpp"]
 
 
 def hipcc() -> str:

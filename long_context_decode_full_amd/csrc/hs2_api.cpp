@@ -493,10 +493,11 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   return HS2_OK;
 }
 
-HS2_API hs2_status hs2_sparse_attn(const hs2_attn_desc* desc, const void* q, const void* k,
-                                   const void* v, const float* k_scale, const float* v_scale,
-                                   const int32_t* ctx_len, const int32_t* idx, float* out,
-                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// slot_rows: index entries are rows of a local cache (any row < cap), not positions.
+static hs2_status sparse_impl(const hs2_attn_desc* desc, const void* q, const void* k, const void* v,
+                              const float* k_scale, const float* v_scale, const int32_t* ctx_len,
+                              const int32_t* idx, float* out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, int slot_rows) {
   Layout L;
   hs2_status s = check_common(desc, q, k, v, k_scale, v_scale, ctx_len, out, idx, workspace,
                               workspace_bytes, &L);
@@ -506,6 +507,7 @@ HS2_API hs2_status hs2_sparse_attn(const hs2_attn_desc* desc, const void* q, con
 
   ScanArgs sa = scan_args(desc, L, q, k, v, k_scale, v_scale, ctx_len, ws);
   sa.idx = idx;
+  sa.slot_rows = slot_rows;
   sa.n_split = L.n_split_sp;
   sa.split_len = L.split_len_sp;
 
@@ -550,6 +552,14 @@ HS2_API hs2_status hs2_sparse_attn(const hs2_attn_desc* desc, const void* q, con
   ca.n_split = sa.n_split;
   if (launch_combine(ca, stream) != hipSuccess) return HS2_ERR_LAUNCH;
   return HS2_OK;
+}
+
+HS2_API hs2_status hs2_sparse_attn(const hs2_attn_desc* desc, const void* q, const void* k,
+                                   const void* v, const float* k_scale, const float* v_scale,
+                                   const int32_t* ctx_len, const int32_t* idx, float* out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return sparse_impl(desc, q, k, v, k_scale, v_scale, ctx_len, idx, out, workspace, workspace_bytes,
+                     stream, 0);
 }
 
 HS2_API hs2_status hs2_set_deterministic(int on) {
@@ -762,5 +772,89 @@ HS2_API hs2_status hs2_decode_step(const hs2_decode_plan* plan, const void* x, c
       if (s != HS2_OK) return s;
     }
   }
+  return HS2_OK;
+}
+
+// ---------------------------------------------------------------- first-generation sparse layer
+namespace {
+
+struct SwaWs {
+  hs2_attn_desc local{};
+  size_t attn = 0, off_idx = 0, off_out = 0, total = 0;
+};
+
+hs2_status swa_layout(const hs2_attn_desc* d, int32_t W, int32_t R, SwaWs* w) {
+  const hs2_status s = validate_desc(d);
+  if (s != HS2_OK) return s;
+  if (W < 1 || R < 1) return HS2_ERR_INVALID_ARG;
+  if (W > 4096 || (int64_t)R < (int64_t)W + d->q_len - 1) return HS2_ERR_UNSUPPORTED;
+  // the local branch: the same heads and queries over a cache of R rows, index rows of W
+  w->local = *d;
+  w->local.kv_capacity = R;
+  w->local.max_ctx_len = R;
+  w->local.window = W;
+  w->local.topk = 0;
+  w->local.select_mode = HS2_SELECT_TOKEN;
+  const hs2_status sl = validate_desc(&w->local);
+  if (sl != HS2_OK) return sl;
+  const size_t a = make_layout(d).total, b = make_layout(&w->local).total;
+  const int64_t n_sel = (int64_t)d->batch * d->q_len * d->n_kv_heads;
+  w->attn = std::max(a, b);
+  w->off_idx = align_up(w->attn);
+  w->off_out = align_up(w->off_idx + (size_t)n_sel * W * sizeof(int32_t));
+  w->total = align_up(w->off_out + (size_t)d->batch * d->q_len * d->n_q_heads * kHeadDim * sizeof(float));
+  return HS2_OK;
+}
+
+}  // namespace
+
+HS2_API hs2_status hs2_sparse_attn_swa_workspace_size(const hs2_attn_desc* desc, int32_t local_window,
+                                                      int32_t local_rows, size_t* bytes) {
+  SwaWs w;
+  const hs2_status s = swa_layout(desc, local_window, local_rows, &w);
+  if (s != HS2_OK) return s;
+  if (bytes == nullptr) return HS2_ERR_INVALID_ARG;
+  *bytes = w.total;
+  return HS2_OK;
+}
+
+HS2_API hs2_status hs2_sparse_attn_swa(const hs2_attn_desc* desc, const void* q, const void* k,
+                                       const void* v, const float* k_scale, const float* v_scale,
+                                       const int32_t* ctx_len, const int32_t* idx, const void* k_local,
+                                       const void* v_local, const float* kl_scale, const float* vl_scale,
+                                       int32_t local_window, int32_t local_rows, float* out,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  SwaWs w;
+  hs2_status s = swa_layout(desc, local_window, local_rows, &w);
+  if (s != HS2_OK) return s;
+  if (!workspace) return HS2_ERR_INVALID_ARG;
+  if (!aligned(workspace, 16)) return HS2_ERR_ALIGNMENT;
+  if (workspace_bytes < w.total) return HS2_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* idx_local = reinterpret_cast<int32_t*>(ws + w.off_idx);
+  float* out_local = reinterpret_cast<float*>(ws + w.off_out);
+  // every check of both branches before anything is enqueued
+  Layout L;
+  s = check_common(desc, q, k, v, k_scale, v_scale, ctx_len, out, idx, workspace, w.attn, &L);
+  if (s != HS2_OK) return s;
+  s = check_common(&w.local, q, k_local, v_local, kl_scale, vl_scale, ctx_len, out_local, idx_local,
+                   workspace, w.attn, &L);
+  if (s != HS2_OK) return s;
+
+  const int64_t n_sel = (int64_t)desc->batch * desc->q_len * desc->n_kv_heads;
+  // 1. the block-selected rows of the shared cache
+  s = sparse_impl(desc, q, k, v, k_scale, v_scale, ctx_len, idx, out, workspace, w.attn, stream, 0);
+  if (s != HS2_OK) return s;
+  // 2. the separate sliding-window branch over the layer's own local cache
+  if (launch_swa_rows(ctx_len, idx_local, n_sel, desc->q_len, desc->n_kv_heads, local_window, local_rows,
+                      desc->max_ctx_len, stream) != hipSuccess)
+    return HS2_ERR_LAUNCH;
+  s = sparse_impl(&w.local, q, k_local, v_local, kl_scale, vl_scale, ctx_len, idx_local, out_local,
+                  workspace, w.attn, stream, 1);
+  if (s != HS2_OK) return s;
+  // 3. the two branches' outputs summed
+  if (launch_add(out, out_local, (int64_t)desc->batch * desc->q_len * desc->n_q_heads * kHeadDim,
+                 stream) != hipSuccess)
+    return HS2_ERR_LAUNCH;
   return HS2_OK;
 }

@@ -77,6 +77,8 @@ struct ScanArgs {
   float scale_log2;         // sm_scale * log2(e)
   int32_t fixed_steps;      // matrix-core scan: 1 = fixed step share per wave (bitwise
                             // reproducible), 0 = waves take steps from a shared counter
+  int32_t slot_rows;        // sparse mode: 1 = index entries are rows of a local cache, taken
+                            // when 0 <= entry < cap (no visibility limit); 0 = positions < n
 };
 
 struct CombineArgs {
@@ -162,6 +164,12 @@ hipError_t launch_bridge(const BridgeArgs& a, bool fp8, hipStream_t st);
 // decode step: pos[b] = ctx_len[b] and ctx_len[b] += 1 (pos -1 and no change when full)
 hipError_t launch_advance(int32_t* ctx_len, int32_t* seq, int32_t* pos, int B, int64_t cap,
                           hipStream_t st);
+
+// first-generation sparse layer: local-cache rows of every selection row's window, and
+// out += add (n floats, a multiple of 4)
+hipError_t launch_swa_rows(const int32_t* ctx_len, int32_t* idx, int64_t n_sel, int Lq, int Hkv, int W,
+                           int R, int64_t ctx_max, hipStream_t st);
+hipError_t launch_add(float* out, const float* add, int64_t n, hipStream_t st);
 
 hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st);
 hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t st);

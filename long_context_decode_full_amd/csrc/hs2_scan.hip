@@ -201,7 +201,8 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
   // Rows are < cap < 2^31, so 32-bit row numbers suffice.
   const int32_t wb = (int32_t)w_begin;
   const int32_t we = (int32_t)w_end;
-  const int32_t n32 = (int32_t)n;
+  // sparse mode: entries name visible positions (< n), or local-cache rows (< cap)
+  const int32_t n32 = (kSparse && a.slot_rows) ? (int32_t)a.cap : (int32_t)n;
 
   // The step loops are straight-line per step: every prefetch load is issued (steps
   // past the end re-read a valid row and are masked) and no load or store sits under

@@ -652,11 +652,13 @@ __global__ __launch_bounds__(kThreads, 1) void gather_mfma_kernel(ScanArgs a, fl
   const int e_count = max(0, min(a.split_len, a.S - e_begin));
   const int nsteps = (e_count + kStepRows - 1) / kStepRows;
 
-  // this split's entries of the index row, those naming no visible row turned into -1
+  // this split's entries of the index row, those naming no visible row (or, for a
+  // local cache, no row of it) turned into -1
+  const int64_t lim = a.slot_rows ? a.cap : n;
   const int32_t* irow = a.idx + sel * a.S + e_begin;
   for (int e = tid; e < nsteps * kStepRows; e += kThreads) {
     const int32_t t = e < e_count ? irow[e] : -1;
-    srow[e] = (t >= 0 && t < n) ? t : -1;
+    srow[e] = (t >= 0 && t < lim) ? t : -1;
   }
   bf16x8_t qf[kHB][4];
 #pragma unroll

@@ -14,8 +14,8 @@ import torch
 
 from . import (HS2_KV_BF16, HS2_KV_FP8_E4M3FN, HS2_OK, HS2_SELECT_BLOCK, HS2_SELECT_TOKEN,
                Hs2Error, hs2_decode_step, hs2_decode_workspace_size, hs2_full_attn_select,
-               hs2_kv_bridge, hs2_sparse_attn, hs2_workspace_size, make_bridge_desc,
-               make_decode_plan, make_desc)
+               hs2_kv_bridge, hs2_sparse_attn, hs2_sparse_attn_swa, hs2_sparse_attn_swa_workspace_size,
+               hs2_workspace_size, make_bridge_desc, make_decode_plan, make_desc)
 
 
 def _dev(a: np.ndarray, device):
@@ -26,7 +26,8 @@ def _dev(a: np.ndarray, device):
 
 class HybridBlockDevice:
     def __init__(self, inp: dict, device="cuda", window=128, topk=1024, mode="token",
-                 block_size=64, n_blocks=18, with_probs=False, max_ctx_len=None):
+                 block_size=64, n_blocks=18, with_probs=False, max_ctx_len=None, local_rings=None,
+                 local_window=128):
         self.device = torch.device(device)
         q = inp["q_full"]
         B, Lq, Hq, D = q.shape
@@ -34,12 +35,17 @@ class HybridBlockDevice:
         cap = inp["k"].shape[2]
         fp8 = inp["k"].dtype == np.uint8
         mctx = int(max_ctx_len if max_ctx_len is not None else max(int(inp["ctx_len"].max()), Lq))
+        # "gen1": the first-generation comparator -- block selection, and sparse layers
+        # with a separate sliding-window branch over their own local rings
+        blockish = mode in ("block", "gen1")
         self.desc = make_desc(B, Lq, Hq, Hkv, cap, mctx, head_dim=D,
                               kv_dtype=HS2_KV_FP8_E4M3FN if fp8 else HS2_KV_BF16,
                               window=window, topk=topk,
-                              select_mode=HS2_SELECT_BLOCK if mode == "block" else HS2_SELECT_TOKEN,
+                              select_mode=HS2_SELECT_BLOCK if blockish else HS2_SELECT_TOKEN,
                               block_size=block_size, n_blocks=n_blocks, sm_scale=inp["sm_scale"])
-        self.S = block_size * n_blocks if mode == "block" else window + topk
+        self.S = block_size * n_blocks if blockish else window + topk
+        self.gen1 = mode == "gen1"
+        self.local_window = local_window
         dv = self.device
         self.q_full = _dev(q, dv)
         self.q_sparse = [_dev(x, dv) for x in inp["q_sparse"]]
@@ -53,12 +59,23 @@ class HybridBlockDevice:
         self.probs = (torch.full((B, Lq, Hkv, cap), -1.0, dtype=torch.float32, device=dv)
                       if with_probs else None)
         self.out_sparse = [torch.zeros_like(self.out_full) for _ in self.q_sparse]
+        if self.gen1:
+            assert local_rings is not None and len(local_rings) == len(self.q_sparse)
+            self.local = [dict(k=_dev(r["k"], dv), v=_dev(r["v"], dv),
+                               k_scale=_dev(r["k_scale"], dv) if fp8 else None,
+                               v_scale=_dev(r["v_scale"], dv) if fp8 else None) for r in local_rings]
+            self.local_rows = int(local_rings[0]["k"].shape[2])
         self.alloc_workspace()
 
     def alloc_workspace(self):
         st, nbytes = hs2_workspace_size(self.desc)
         if st != HS2_OK:
             raise Hs2Error(st, "hs2_workspace_size")
+        if self.gen1:
+            st, n2 = hs2_sparse_attn_swa_workspace_size(self.desc, self.local_window, self.local_rows)
+            if st != HS2_OK:
+                raise Hs2Error(st, "hs2_sparse_attn_swa_workspace_size")
+            nbytes = max(nbytes, n2)
         self.ws_bytes = nbytes
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
 
@@ -70,6 +87,16 @@ class HybridBlockDevice:
             raise Hs2Error(st, "hs2_full_attn_select")
 
     def sparse(self, layer: int, idx=None, stream=None):
+        if self.gen1:
+            lr = self.local[layer]
+            st = hs2_sparse_attn_swa(self.desc, self.q_sparse[layer], self.k, self.v, self.k_scale,
+                                     self.v_scale, self.ctx_len, self.idx if idx is None else idx,
+                                     lr["k"], lr["v"], lr["k_scale"], lr["v_scale"], self.local_window,
+                                     self.local_rows, self.out_sparse[layer], self.workspace,
+                                     self.ws_bytes, stream)
+            if st != HS2_OK:
+                raise Hs2Error(st, "hs2_sparse_attn_swa")
+            return
         st = hs2_sparse_attn(self.desc, self.q_sparse[layer], self.k, self.v, self.k_scale,
                              self.v_scale, self.ctx_len, self.idx if idx is None else idx,
                              self.out_sparse[layer], self.workspace, self.ws_bytes, stream)

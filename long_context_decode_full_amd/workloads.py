@@ -337,3 +337,25 @@ def make_decode_steps(w: Workload, n_blocks: int, steps: int, hidden: int, seed:
         qs.append([f32_to_bf16_bits(rq.standard_normal((B, 1, Hq, D), dtype=np.float32))
                    for _ in range(n_blocks * ns)])
     return dict(w_bits=f32_to_bf16_bits(wt), x=xs, q_full=qf, q_sparse=qs)
+
+
+def make_local_rings(w: Workload, rows: int, seed: int) -> list:
+    """The first-generation comparator's local caches: for each sparse layer a ring of
+    `rows` K/V rows per (sequence, KV head) standing for the layer's own K/V of its
+    most recent positions (position p at row p % rows).  N(0, 1) rows, stored like the
+    shared cache (bf16 bits, or e4m3fn codes with per-row scales).  Returns a list of
+    dicts with k, v (and k_scale, v_scale for fp8)."""
+    B, Hkv, D = w.batch, w.n_kv_heads, w.head_dim
+    out = []
+    for s in np.random.SeedSequence(seed).spawn(w.n_sparse_layers):
+        rk, rv = (np.random.default_rng(x) for x in s.spawn(2))
+        xk = rk.standard_normal((B, Hkv, rows, D), dtype=np.float32)
+        xv = rv.standard_normal((B, Hkv, rows, D), dtype=np.float32)
+        if w.kv_dtype == "fp8":
+            ck, sk = quantize_e4m3fn_rows(xk.reshape(-1, D))
+            cv, sv = quantize_e4m3fn_rows(xv.reshape(-1, D))
+            out.append(dict(k=ck.reshape(B, Hkv, rows, D), v=cv.reshape(B, Hkv, rows, D),
+                            k_scale=sk.reshape(B, Hkv, rows), v_scale=sv.reshape(B, Hkv, rows)))
+        else:
+            out.append(dict(k=f32_to_bf16_bits(xk), v=f32_to_bf16_bits(xv), k_scale=None, v_scale=None))
+    return out

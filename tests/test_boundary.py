@@ -339,3 +339,36 @@ def test_decode_step_argument_checks_before_any_launch(lib):
     p8 = _plan()
     p8.attn.kv_dtype = hs2.HS2_KV_FP8_E4M3FN
     assert _step(p8) == hs2.HS2_ERR_INVALID_ARG                      # fp8 without scales
+
+
+# ----------------------------------------------------------------------------- first-generation comparator
+def _swa(d, **over):
+    st, need = hs2.hs2_sparse_attn_swa_workspace_size(d, over.pop("W", 128), over.get("R", 140))
+    args = dict(q=_GOOD, k=_GOOD + 0x1000000, v=_GOOD + 0x2000000, k_scale=None, v_scale=None,
+                ctx_len=_GOOD + 0x3000000, idx=_GOOD + 0x4000000, k_local=_GOOD + 0x5000000,
+                v_local=_GOOD + 0x6000000, kl_scale=None, vl_scale=None, local_window=128,
+                local_rows=140, out=_GOOD + 0x7000000, workspace=_GOOD + 0x8000000,
+                workspace_bytes=need if st == hs2.HS2_OK else 1 << 20)
+    args.update(over)
+    args.pop("R", None)
+    return hs2.hs2_sparse_attn_swa(d, stream=0, **args)
+
+
+def test_swa_workspace_and_ring_limits(lib):
+    d = _desc(q_len=16, kv_capacity=8192, max_ctx_len=8192, select_mode=hs2.HS2_SELECT_BLOCK)
+    assert hs2.hs2_sparse_attn_swa_workspace_size(d, 128, 143)[0] == hs2.HS2_OK
+    assert hs2.hs2_sparse_attn_swa_workspace_size(d, 128, 142)[0] == hs2.HS2_ERR_UNSUPPORTED  # < W + Lq - 1
+    assert hs2.hs2_sparse_attn_swa_workspace_size(d, 0, 143)[0] == hs2.HS2_ERR_INVALID_ARG
+    assert hs2.hs2_sparse_attn_swa_workspace_size(d, 4097, 5000)[0] == hs2.HS2_ERR_UNSUPPORTED
+
+
+def test_swa_argument_checks_before_any_launch(lib):
+    d = _desc(kv_capacity=8192, max_ctx_len=8192, select_mode=hs2.HS2_SELECT_BLOCK)
+    assert _swa(d, k_local=None) == hs2.HS2_ERR_INVALID_ARG
+    assert _swa(d, v_local=_GOOD + 8) == hs2.HS2_ERR_ALIGNMENT
+    assert _swa(d, idx=None) == hs2.HS2_ERR_INVALID_ARG
+    assert _swa(d, workspace_bytes=64) == hs2.HS2_ERR_WORKSPACE
+    assert _swa(d, local_rows=100) == hs2.HS2_ERR_UNSUPPORTED
+    d8 = _desc(kv_capacity=8192, max_ctx_len=8192, kv_dtype=hs2.HS2_KV_FP8_E4M3FN,
+               select_mode=hs2.HS2_SELECT_BLOCK)
+    assert _swa(d8, k_scale=_GOOD, v_scale=_GOOD) == hs2.HS2_ERR_INVALID_ARG   # local scales missing
