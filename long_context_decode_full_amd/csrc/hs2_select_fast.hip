@@ -340,10 +340,11 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
 // ------------------------------------------------------------------ exact top-k + output
 constexpr int kFinThreads = 1024;
 constexpr int kFinWaves = kFinThreads / 64;
-constexpr int kFinStage = 6144;   // candidates staged in LDS (larger sets read global memory)
+constexpr int kFinStage = 12288;  // candidates staged in LDS (larger sets read global memory)
 constexpr int kFinRun = kFinStage / kFinThreads;   // consecutive candidates per thread
 constexpr int kFinBnd = 1024;     // threshold-bin entries ranked pairwise
 constexpr int kDigitBins = 4096;  // first radix digit: score bits 30..19
+constexpr int kFinChunkLds = kDigitBins / 2;   // chunks whose counts the general path keeps in lh
 
 
 // One workgroup per selection.  Stages the candidates (position order) in LDS,
@@ -534,7 +535,11 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
       kk = (int)(total < need0 ? total : need0);
     } else {
       // general path: two more digits give the exact k-th score value vk; equal
-      // scores are taken in position order by the ordered pass
+      // scores are taken in position order by the ordered pass.  A candidate set
+      // beyond the LDS stage is read straight from the per-chunk lists (wave w takes
+      // chunks w, w + kFinWaves, ...: coalesced loads, no flat-index lookups) when its
+      // chunk counts fit the histogram's LDS.
+      const bool bychunk = !staged && nch <= kFinChunkLds;
       uint32_t prefix = b1, need = need1;
       const int shifts[2] = {7, 0};
       const int widths[2] = {12, 7};
@@ -542,11 +547,23 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
         const int sh = shifts[d];
         const uint32_t nb = 1u << widths[d];
         const int shp = d == 0 ? 19 : 7;
+        __syncthreads();   // the previous digit's threshold has read lh
         for (uint32_t i = tid; i < nb; i += kFinThreads) lh[i] = 0u;
         __syncthreads();
-        for (uint32_t fi = tid; fi < m; fi += kFinThreads) {
-          const uint32_t u = score_bits(fi);
-          if ((u >> shp) == prefix) atomicAdd(&lh[(u >> sh) & (nb - 1)], 1u);
+        if (bychunk) {
+          for (int c = wave; c < nch; c += kFinWaves) {
+            const uint32_t cn = pref[c + 1] - pref[c];
+            const uint64_t* src = a.cand_keys + lbase + (int64_t)c * clen;
+            for (uint32_t j = lane; j < cn; j += 64) {
+              const uint32_t u = (uint32_t)(src[j] >> 32);
+              if ((u >> shp) == prefix) atomicAdd(&lh[(u >> sh) & (nb - 1)], 1u);
+            }
+          }
+        } else {
+          for (uint32_t fi = tid; fi < m; fi += kFinThreads) {
+            const uint32_t u = score_bits(fi);
+            if ((u >> shp) == prefix) atomicAdd(&lh[(u >> sh) & (nb - 1)], 1u);
+          }
         }
         __syncthreads();
         uint32_t bd, ab;
@@ -555,6 +572,96 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
         prefix = (prefix << widths[d]) | bd;
       }
       const uint32_t vk = prefix;   // bits of the k-th largest score
+      if (bychunk) {
+        // per chunk: keys above vk (cgt) and equal to vk (ctie), in the histogram's LDS
+        uint32_t* cgt = lh;
+        uint32_t* ctie = lh + kFinChunkLds;
+        __syncthreads();
+        for (int c = wave; c < nch; c += kFinWaves) {
+          const uint32_t cn = pref[c + 1] - pref[c];
+          const uint64_t* src = a.cand_keys + lbase + (int64_t)c * clen;
+          uint32_t gt = 0, tie = 0;
+          for (uint32_t j = lane; j < cn; j += 64) {
+            const uint32_t u = (uint32_t)(src[j] >> 32);
+            gt += u > vk ? 1u : 0u;
+            tie += u == vk ? 1u : 0u;
+          }
+          gt = (uint32_t)__builtin_amdgcn_readlane((int)wave_prefix_incl(gt), 63);
+          tie = (uint32_t)__builtin_amdgcn_readlane((int)wave_prefix_incl(tie), 63);
+          if (lane == 0) {
+            cgt[c] = gt;
+            ctie[c] = tie;
+          }
+        }
+        __syncthreads();
+        // ties before each chunk (exclusive prefix, in place), then each chunk's chosen
+        // count = its keys above vk + the ties it supplies before `need` is reached, and
+        // the output offset of each chunk (exclusive prefix of the chosen counts)
+        {
+          const uint32_t a0 = 2 * tid < nch ? ctie[2 * tid] : 0u;
+          const uint32_t a1 = 2 * tid + 1 < nch ? ctie[2 * tid + 1] : 0u;
+          const uint32_t incl = wave_prefix_incl(a0 + a1);
+          if (lane == 63) wsum[wave][0] = incl;
+          __syncthreads();
+          uint32_t off = 0;
+          for (int w = 0; w < wave; ++w) off += wsum[w][0];
+          const uint32_t ex = off + incl - (a0 + a1);
+          if (2 * tid < nch) {
+            const uint32_t t0 = ex;
+            const uint32_t take0 = need > t0 ? min(need - t0, a0) : 0u;
+            cgt[2 * tid] += take0;
+            ctie[2 * tid] = t0;
+          }
+          if (2 * tid + 1 < nch) {
+            const uint32_t t1 = ex + a0;
+            const uint32_t take1 = need > t1 ? min(need - t1, a1) : 0u;
+            cgt[2 * tid + 1] += take1;
+            ctie[2 * tid + 1] = t1;
+          }
+        }
+        __syncthreads();
+        uint32_t chosen_total;
+        {
+          const uint32_t a0 = 2 * tid < nch ? cgt[2 * tid] : 0u;
+          const uint32_t a1 = 2 * tid + 1 < nch ? cgt[2 * tid + 1] : 0u;
+          const uint32_t incl = wave_prefix_incl(a0 + a1);
+          if (lane == 63) wsum[wave][1] = incl;
+          __syncthreads();
+          uint32_t off = 0, all = 0;
+          for (int w = 0; w < kFinWaves; ++w) {
+            all += wsum[w][1];
+            off += w < wave ? wsum[w][1] : 0u;
+          }
+          chosen_total = all;
+          const uint32_t ex = off + incl - (a0 + a1);
+          __syncthreads();   // every thread has read its counts
+          if (2 * tid < nch) cgt[2 * tid] = ex;
+          if (2 * tid + 1 < nch) cgt[2 * tid + 1] = ex + a0;
+        }
+        __syncthreads();
+        // ordered write: keys above vk, and ties while their rank (in position order) is
+        // below `need`, at the chunk's output offset
+        for (int c = wave; c < nch; c += kFinWaves) {
+          const uint32_t cn = pref[c + 1] - pref[c];
+          const uint64_t* src = a.cand_keys + lbase + (int64_t)c * clen;
+          uint32_t opos = cgt[c], trank = ctie[c];
+          for (uint32_t j0 = 0; j0 < cn; j0 += 64) {
+            const uint32_t j = j0 + lane;
+            const bool in = j < cn;
+            const uint64_t key = in ? src[j] : 0ull;
+            const uint32_t u = (uint32_t)(key >> 32);
+            const bool tie = in && u == vk;
+            const uint64_t tmask = __builtin_amdgcn_ballot_w64(tie);
+            const bool chosen = in && (u > vk || (tie && trank + lanes_below(tmask) < need));
+            const uint64_t cmask = __builtin_amdgcn_ballot_w64(chosen);
+            const uint32_t o = opos + lanes_below(cmask);
+            if (chosen && o < need0) out[o] = key_pos(key);
+            opos += (uint32_t)__builtin_popcountll(cmask);
+            trank += (uint32_t)__builtin_popcountll(tmask);
+          }
+        }
+        kk = (int)min(need0, chosen_total);
+      } else {
       if (tid == 0) {
         carry[0] = 0u;   // chosen so far
         carry[1] = 0u;   // ties so far
@@ -590,6 +697,7 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
         __syncthreads();
       }
       kk = (int)min(need0, carry[0]);
+      }
     }
   }
   const int nwin = n - w0;

@@ -53,6 +53,7 @@ class Workload:
     poison_tail: bool = False                # fill rows >= ctx_len with NaN
     identical_keys: bool = False             # every key row of a (b, g) equal
     zero_q: bool = False                     # all query vectors zero
+    unaligned_queries: bool = False          # full-layer queries drawn after the needles, unrelated to them
     seed: int = 0
 
     @property
@@ -204,6 +205,11 @@ def make_inputs(w: Workload, threads: int = 8) -> dict:
     with ThreadPoolExecutor(max(1, threads)) as ex:
         list(ex.map(fill, tasks))
 
+    if w.unaligned_queries:
+        # the keys (and needles) stay as built; the full layer's queries are fresh draws,
+        # so no planted key stands out and the selection boundary falls among many
+        # similar scores
+        q_full = qgen(np.random.SeedSequence([w.seed, 7919]))
     return dict(workload=w, q_full=q_full, q_sparse=q_sparse, k=k, v=v, k_scale=k_scale,
                 v_scale=v_scale, ctx_len=np.asarray(ctx, dtype=np.int32), capacity=cap,
                 sm_scale=1.0 / math.sqrt(D))

@@ -143,6 +143,16 @@ def test_million_token_decode():
     run_and_compare(w, "million")
 
 
+@pytest.mark.parametrize("name", ["million", "fp8_256k"])
+def test_unaligned_queries_many_candidates(name):
+    """Queries unrelated to the planted keys: the selection boundary falls among many
+    similar scores, so each row keeps thousands of candidates (beyond the final stage's
+    LDS at 1M positions) and the exact top-k is resolved from the per-chunk lists."""
+    import dataclasses
+    w = dataclasses.replace(wl.standard_workloads()[name], unaligned_queries=True)
+    run_and_compare(w, name + " unaligned queries")
+
+
 def test_mqa_million_token_decode():
     """MQA at the million-token context: one index set from all 32 heads."""
     w = wl.standard_workloads()["mqa_million"]
