@@ -96,6 +96,8 @@ def _same_state(a, b, dev_a, dev_b):
 
 CASES = {
     "bf16": dict(kv="bf16", ctx=[3000, 5000], cap=5008, steps=4),
+    # MQA: 32 query heads on one KV head (wide-group scan and gather)
+    "mqa": dict(kv="bf16", ctx=[4000, 2500], cap=4010, steps=3, hq=32, hkv=1),
     "fp8": dict(kv="fp8", ctx=[2500, 4100], cap=4110, steps=3),
     # sequence 1 starts with a full cache: it keeps its length, appends nothing
     "full_cache": dict(kv="bf16", ctx=[1200, 1500], cap=1500, steps=3),
@@ -105,9 +107,10 @@ CASES = {
 @pytest.mark.parametrize("name", list(CASES))
 def test_decode_loop_graph_eager_and_oracle(name, deterministic):
     c = CASES[name]
-    w = wl.Workload(f"decode loop {name}", 2, 1, 16, 2, ctx_lens=c["ctx"], capacity=c["cap"],
+    hq, hkv = c.get("hq", 16), c.get("hkv", 2)
+    w = wl.Workload(f"decode loop {name}", 2, 1, hq, hkv, ctx_lens=c["ctx"], capacity=c["cap"],
                     kv_dtype=c["kv"], n_needles=8, seed=3001)
-    print(f"\n[decode loop] {name}: B=2 Hq16/Hkv2 ctx={c['ctx']} cap={c['cap']} {c['kv']} "
+    print(f"\n[decode loop] {name}: B=2 Hq{hq}/Hkv{hkv} ctx={c['ctx']} cap={c['cap']} {c['kv']} "
           f"blocks=2 hidden=256 steps={c['steps']}", flush=True)
     inp = wl.make_inputs(w)
     dec = wl.make_decode_steps(w, n_blocks=2, steps=c["steps"], hidden=256, seed=3002)
