@@ -88,24 +88,70 @@ def scan_flops(inp):
     return total * Hq * 4 * D
 
 
-def cpu_baseline(inp, groups, min_s=10.0, max_reps=20, mode="token"):
+def host_description():
+    """The host the CPU oracle is timed on: processor model and the threads this process
+    may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_threads": usable}
+
+
+def measured_copy_peak(torch, nbytes=1 << 30, reps=10):
+    """A second bandwidth denominator measured on this device: a plain 1 GiB
+    device-to-device copy (read + write bytes over its event-timed duration)."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbps
+
+
+def cpu_baseline(inp, groups, min_s=10.0, max_reps=20, mode="token", threads=None):
     """The float64 oracle, as it is, on KV groups `groups` of sequence 0 / token 0,
-    repeated until about `min_s` seconds of CPU work; returns seconds per repetition."""
+    repeated until about `min_s` seconds of CPU work; returns seconds per repetition.
+    `threads` limits the BLAS/OpenMP pools (None: as configured)."""
+    import contextlib
     import oracle
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limit = threadpool_limits(threads) if threads else contextlib.nullcontext()
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
-    reps = 0
-    ref = None
-    t0 = time.perf_counter()
-    while reps < max_reps:
-        ref = oracle.hybrid_block_token(inp, 0, 0, groups=groups, mode=mode)
-        reps += 1
-        if time.perf_counter() - t0 >= min_s:
-            break
-    return (time.perf_counter() - t0) / reps, cores, reps, ref
+        threadpool_info = None
+        limit = contextlib.nullcontext()
+    with limit:
+        if threadpool_info is not None:
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        else:  # pragma: no cover
+            cores = threads or os.cpu_count()
+        reps = 0
+        ref = None
+        t0 = time.perf_counter()
+        while reps < max_reps:
+            ref = oracle.hybrid_block_token(inp, 0, 0, groups=groups, mode=mode)
+            reps += 1
+            if time.perf_counter() - t0 >= min_s:
+                break
+        dt = time.perf_counter() - t0
+    return dt / reps, cores, reps, ref
 
 
 def check_sample(got, ref, mode, topk=1024):
@@ -289,6 +335,7 @@ def bench_bridge(args):
         dt = (time.perf_counter() - c0) / reps
         result["cpu_baseline"] = {
             "value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "host": host_description(),
             "sample": f"float64 numpy oracle (projection, rounding, scatter) on the first {n} tokens "
                       f"of the chunk into a {n}-row cache, {reps} repetition(s) of {dt:.2f}s",
         }
@@ -400,6 +447,7 @@ def bench_decode_loop(args):
         per_seq = t_bridge + n_blocks * t_block
         result["cpu_baseline"] = {
             "value": 1.0 / per_seq, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "host": host_description(),
             "sample": f"float64 oracle: one Hybrid Block for sequence 0 ({t_block:.2f}s) x {n_blocks} "
                       f"blocks + the bridge for its token ({t_bridge:.2f}s), per sequence",
         }
@@ -503,6 +551,7 @@ def main():
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
     cold_dist = step_distribution(dev, nrep, flush)
     del flush
+    copy_gbps = measured_copy_peak(torch)
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     ctx = int(np.sum(inp["ctx_len"]))
@@ -556,6 +605,8 @@ def main():
             "traffic": measured_traffic(args.workload),
             "kernel": "scan_mfma_kernel (split-K full-attention scan on the matrix cores)",
             "algorithmic_bytes_per_launch": algo,
+            "measured_copy_gbps": copy_gbps,
+            "frac_of_measured_copy": achieved / copy_gbps,
         },
         "cpu_baseline": None,
     }
@@ -600,7 +651,14 @@ def main():
                        f"layers for {len(groups)} of {Hkv} KV groups of sequence 0 / token 0, "
                        f"{reps} repetition(s) of {dt:.2f}s, scaled by {rows_scale:.1f} (the step's "
                        f"visible positions over all (sequence, query token) rows / this row's)"),
+            "host": host_description(),
         }
+        if args.workload in ("tiny", "batched"):
+            # the short-context configurations also report the oracle on one thread
+            dt1, cores1, reps1, _ = cpu_baseline(inp, groups, min_s=5.0, mode=args.select, threads=1)
+            result["cpu_baseline"]["one_thread"] = {
+                "value": (w.batch * w.q_len if chunk else ctx) / (dt1 * Hkv / len(groups) * rows_scale),
+                "cores": cores1, "sample": f"{reps1} repetition(s) of {dt1:.3f}s, same scaling"}
     print(json.dumps(result), flush=True)
 
 

@@ -649,6 +649,9 @@ static hs2_status bridge_prepare(const hs2_bridge_desc* d, const void* x, const 
   a.n_layers = d->n_layers;
   a.m_tiles = (int32_t)m_tiles;
   a.n_tiles = (int32_t)n_tiles;
+  // few tokens (decode): the W-streaming path; HS2_BRIDGE_GEMV_MAX moves the switch (0..1024)
+  const int gemv_max = std::min(std::max(env_int("HS2_BRIDGE_GEMV_MAX", kBridgeGemvMaxTokens), 0), 1024);
+  a.gemv = d->n_tokens <= gemv_max ? 1 : 0;
   *out = a;
   *empty = d->n_tokens == 0;
   return HS2_OK;

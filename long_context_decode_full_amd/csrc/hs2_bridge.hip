@@ -265,6 +265,118 @@ __global__ __launch_bounds__(C::kThreads, C::kOcc) void bridge_kernel(BridgeArgs
   }
 }
 
+// Decode-size projection (a few tokens): the tile kernel would stream W through LDS
+// for 128-token tiles that are almost all padding.  Here a workgroup owns kSlices
+// slices of 16 features and 16 tokens; its waves are (slice, part of the hidden dims)
+// pairs, each reading its W rows straight into registers (kGemvUnroll steps of 16
+// bytes per lane in flight).  The parts meet in LDS (summed in part order).  bf16
+// rows need nothing across features, so a workgroup takes one slice (4 waves, 8
+// workgroups per 128-feature row: enough workgroups to keep the W stream going);
+// an fp8 row's scale is the maximum over its 128 features, so a workgroup takes a
+// whole row (8 slices x 2 parts), the slice maxima meeting in LDS.  W is read once
+// per 16 tokens.
+constexpr int kGemvTokens = 16;
+constexpr int kGemvUnroll = 8;
+
+template <bool kFp8>
+struct GemvShape {
+  static constexpr int kSlices = kFp8 ? 8 : 1;
+  static constexpr int kParts = kFp8 ? 2 : 4;
+  static constexpr int kThreads = 64 * kSlices * kParts;
+};
+
+template <bool kFp8>
+__global__ __launch_bounds__(GemvShape<kFp8>::kThreads) void bridge_gemv_kernel(BridgeArgs a) {
+  constexpr int kSlices = GemvShape<kFp8>::kSlices;
+  constexpr int kParts = GemvShape<kFp8>::kParts;
+  const int m0 = blockIdx.y * kGemvTokens;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int fs = wave % kSlices;   // feature slice
+  const int kp = wave / kSlices;   // part of the hidden dims
+  const int li = lane & 15;
+  const int grp = lane >> 4;
+  const int feat0 = (blockIdx.x * kSlices + fs) * 16;   // first feature of the slice
+  // part kp takes 32-dim steps [s0, s1) of the Hd / 32
+  const int n_steps = a.Hd / 32;
+  const int s0 = kp * n_steps / kParts;
+  const int s1 = (kp + 1) * n_steps / kParts;
+  // A = X rows (lane: token m0 + li, clamped; rows past T are dropped at the store),
+  // B = W rows (lane: feature feat0 + li); both take dims 8 grp .. 8 grp + 7 of a step
+  const int tok = min(m0 + li, a.T - 1);
+  const uint16_t* xr = a.x + (size_t)tok * a.Hd + 8 * grp;
+  const uint16_t* wr = a.w + ((size_t)feat0 + li) * a.Hd + 8 * grp;
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  int st = s0;
+  for (; st + kGemvUnroll <= s1; st += kGemvUnroll) {
+    bf16x8_t xa[kGemvUnroll], wb[kGemvUnroll];
+#pragma unroll
+    for (int u = 0; u < kGemvUnroll; ++u) {
+      wb[u] = *reinterpret_cast<const bf16x8_t*>(wr + (size_t)(st + u) * 32);
+      xa[u] = *reinterpret_cast<const bf16x8_t*>(xr + (size_t)(st + u) * 32);
+    }
+#pragma unroll
+    for (int u = 0; u < kGemvUnroll; ++u) acc = mfma16(xa[u], wb[u], acc);
+  }
+  for (; st < s1; ++st) {
+    const bf16x8_t wb = *reinterpret_cast<const bf16x8_t*>(wr + (size_t)st * 32);
+    const bf16x8_t xa = *reinterpret_cast<const bf16x8_t*>(xr + (size_t)st * 32);
+    acc = mfma16(xa, wb, acc);
+  }
+
+  // lane (li, grp) holds y[token m0 + 4 grp + r][feature feat0 + li], r = 0..3
+  __shared__ float red[kParts - 1][kSlices][4][64];
+  __shared__ float rmax[kSlices][kGemvTokens];
+  if (kp > 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[kp - 1][fs][r][lane] = acc[r];
+  }
+  __syncthreads();
+  if (kp == 0) {
+#pragma unroll
+    for (int q = 0; q < kParts - 1; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] += red[q][fs][r][lane];
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float m = max16(fabsf(acc[r]));
+        if (li == 0) rmax[fs][4 * grp + r] = m;
+      }
+    }
+  }
+  if constexpr (kFp8) __syncthreads();
+  if (kp != 0) return;
+  const int head = feat0 >> 7;   // (layer, K|V, KV head) feature block
+  const int layer = head / (2 * a.Hkv);
+  const int is_v = (head / a.Hkv) & 1;
+  const int g = head % a.Hkv;
+  uint8_t* cache = static_cast<uint8_t*>(is_v ? a.vc[layer] : a.kc[layer]);
+  float* scales = is_v ? a.vs[layer] : a.ks[layer];
+  const int f = (feat0 & 127) + li;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = m0 + 4 * grp + r;
+    const int t = row < a.T ? row : 0;
+    const int sq = a.seq[t];
+    const int ps = a.pos[t];
+    const bool ok = row < a.T && sq >= 0 && sq < a.B && ps >= 0 && (int64_t)ps < a.cap;
+    if (!ok) continue;
+    const size_t crow = ((size_t)sq * a.Hkv + g) * (size_t)a.cap + (size_t)ps;
+    if constexpr (kFp8) {
+      float m = rmax[0][4 * grp + r];
+#pragma unroll
+      for (int k = 1; k < kSlices; ++k) m = fmaxf(m, rmax[k][4 * grp + r]);
+      const float sc = m > 0.f ? m / kE4M3Max : 1.0f;
+      cache[crow * 128 + f] = (uint8_t)(cvt_fp8x2(acc[r] / sc, 0.0f, 0u, false) & 0xFFu);
+      if (f == 0) scales[crow] = sc;
+    } else {
+      reinterpret_cast<uint16_t*>(cache)[crow * 128 + f] = (uint16_t)(pack_bf16(acc[r], 0.0f) & 0xFFFFu);
+    }
+  }
+}
+
 }  // namespace
 
 int bridge_tile_tokens(int n_tokens) {
@@ -272,6 +384,17 @@ int bridge_tile_tokens(int n_tokens) {
 }
 
 hipError_t launch_bridge(const BridgeArgs& a, bool fp8, hipStream_t st) {
+  if (a.gemv) {
+    const unsigned n_slices = (unsigned)(2 * a.n_layers * a.Hkv * (128 / 16));
+    const unsigned m_blocks = (unsigned)((a.T + kGemvTokens - 1) / kGemvTokens);
+    if (fp8)
+      hipLaunchKernelGGL((bridge_gemv_kernel<true>), dim3(n_slices / GemvShape<true>::kSlices, m_blocks),
+                         dim3(GemvShape<true>::kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((bridge_gemv_kernel<false>), dim3(n_slices / GemvShape<false>::kSlices, m_blocks),
+                         dim3(GemvShape<false>::kThreads), 0, st, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)(a.m_tiles * a.n_tiles));
   if (bridge_tile_tokens(a.T) == BridgeLarge::kBM) {
     if (fp8)

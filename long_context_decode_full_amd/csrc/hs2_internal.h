@@ -158,7 +158,9 @@ struct BridgeArgs {
   int64_t cap;
   int32_t T, Hd, Hkv, B, n_layers;
   int32_t m_tiles, n_tiles;     // token tiles x feature tiles of the launch
+  int32_t gemv;                 // 1: decode-size path (one workgroup per 128 features x 16 tokens)
 };
+constexpr int kBridgeGemvMaxTokens = 16;   // default largest T of the decode-size path
 int bridge_tile_tokens(int n_tokens);   // tokens per workgroup tile launch_bridge uses
 hipError_t launch_bridge(const BridgeArgs& a, bool fp8, hipStream_t st);
 // decode step: pos[b] = ctx_len[b] and ctx_len[b] += 1 (pos -1 and no change when full)

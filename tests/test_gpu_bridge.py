@@ -118,6 +118,41 @@ def test_bridge_small_whole_caches(name):
     assert _full_compare(inp, dev) == int(_valid(inp).sum())
 
 
+# The decode-size path (one workgroup per 128 features x 16 tokens, W read straight
+# into registers) takes calls of at most 16 tokens; HS2_BRIDGE_GEMV_MAX moves the
+# switch, so each path is also run on the other's sizes.
+GEMV = {
+    # hidden 64: one 32-dim step per half (remainder loop only)
+    "gemv_hidden_64_bf16": (wl.BridgeWorkload("5 tokens, hidden 64", 5, 64, 2, 1, batch=2, capacity=16,
+                                              kv_dtype="bf16", placement="ragged", seed=2110), None),
+    # hidden 576: 9 steps per half (one unrolled batch of 8 + one)
+    "gemv_hidden_576_fp8": (wl.BridgeWorkload("9 tokens, hidden 576", 9, 576, 3, 2, batch=4, capacity=64,
+                                              placement="ragged", bad_rows=2, seed=2111), None),
+    "gemv_mqa_fp8": (wl.BridgeWorkload("16 tokens, one KV head", 16, 2048, 4, 1, batch=16, capacity=40,
+                                       placement="decode", seed=2112), None),
+    # three token blocks, the last one ragged
+    "gemv_forced_40_tokens_fp8": (wl.BridgeWorkload("40 tokens on the decode-size path", 40, 1024, 2, 4,
+                                                    batch=3, capacity=128, placement="ragged", bad_rows=3,
+                                                    seed=2113), "64"),
+    "gemv_forced_40_tokens_bf16": (wl.BridgeWorkload("40 tokens on the decode-size path, bf16", 40, 512, 2, 2,
+                                                     batch=3, capacity=128, kv_dtype="bf16",
+                                                     placement="ragged", bad_rows=3, seed=2114), "64"),
+    # the tile path on a decode-size call
+    "tile_forced_16_tokens_fp8": (wl.BridgeWorkload("16 tokens on the tile path", 16, 2048, 2, 4, batch=16,
+                                                    capacity=40, placement="decode", seed=2115), "0"),
+}
+
+
+@pytest.mark.parametrize("name", list(GEMV))
+def test_bridge_decode_size_paths(name, monkeypatch):
+    w, switch = GEMV[name]
+    if switch is not None:
+        monkeypatch.setenv("HS2_BRIDGE_GEMV_MAX", switch)
+    _announce(name, w)
+    inp, dev = _run(w)
+    assert _full_compare(inp, dev) == int(_valid(inp).sum())
+
+
 def test_bridge_every_destination_invalid_writes_nothing():
     w = wl.BridgeWorkload("all invalid", 50, 128, 2, 2, batch=2, capacity=64, placement="ragged",
                           bad_rows=50, seed=2105)
@@ -127,25 +162,28 @@ def test_bridge_every_destination_invalid_writes_nothing():
     assert _full_compare(inp, dev) == 0
 
 
-def test_bridge_zero_and_large_rows():
+@pytest.mark.parametrize("n_tokens", [256, 12])
+def test_bridge_zero_and_large_rows(n_tokens):
     """All-zero hidden rows give all-zero K/V rows (scale 1, codes 0); rows scaled by
-    2^12 keep the same codes with scales 2^12 larger (the maximum still maps to 448)."""
-    w = wl.BridgeWorkload("zero and large", 256, 512, 2, 2, batch=1, capacity=256, seed=2106)
-    _announce("zero_and_large", w)
+    2^12 keep the same codes with scales 2^12 larger (the maximum still maps to 448).
+    256 tokens take the tile kernel, 12 the decode-size kernel."""
+    w = wl.BridgeWorkload("zero and large", n_tokens, 512, 2, 2, batch=1, capacity=256, seed=2106)
+    _announce(f"zero_and_large_{n_tokens}", w)
+    k = min(16, n_tokens // 3)
     base = wl.make_bridge_inputs(w)
     x = base["x"].copy()
-    x[:16] = 0                                          # zero rows
-    big = x[16:32].view(np.uint16).astype(np.uint32) + (12 << 7)   # exponent + 12
-    x[16:32] = big.astype(np.uint16)
+    x[:k] = 0                                           # zero rows
+    big = x[k:2 * k].view(np.uint16).astype(np.uint32) + (12 << 7)   # exponent + 12
+    x[k:2 * k] = big.astype(np.uint16)
     inp, dev = _run(w, x=x)
     _full_compare(inp, dev)
-    rows = dev.rows(np.arange(32))
-    assert np.all(rows["scales"][:16] == 1.0) and not rows["codes"][:16].any()
+    rows = dev.rows(np.arange(2 * k))
+    assert np.all(rows["scales"][:k] == 1.0) and not rows["codes"][:k].any()
     # the same tokens unscaled, in a second call
     inp2, dev2 = _run(w)
-    r2 = dev2.rows(np.arange(16, 32))
-    assert np.array_equal(rows["codes"][16:32], r2["codes"])
-    assert np.array_equal(rows["scales"][16:32], r2["scales"] * np.float32(4096.0))
+    r2 = dev2.rows(np.arange(k, 2 * k))
+    assert np.array_equal(rows["codes"][k:2 * k], r2["codes"])
+    assert np.array_equal(rows["scales"][k:2 * k], r2["scales"] * np.float32(4096.0))
 
 
 def test_bridge_decode_append():
