@@ -125,7 +125,7 @@ def measured_copy_peak(torch, nbytes=1 << 30, reps=10):
     return gbps
 
 
-def cpu_baseline(inp, groups, min_s=10.0, max_reps=20, mode="token", threads=None):
+def cpu_baseline(inp, groups, min_s=10.0, max_reps=100000, mode="token", threads=None):
     """The float64 oracle, as it is, on KV groups `groups` of sequence 0 / token 0,
     repeated until about `min_s` seconds of CPU work; returns seconds per repetition.
     `threads` limits the BLAS/OpenMP pools (None: as configured)."""

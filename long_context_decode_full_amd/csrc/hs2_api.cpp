@@ -24,7 +24,8 @@ constexpr int64_t kFusedSparseRows = 256;    // sparse layer: one workgroup per 
 constexpr int kCandTargetWorkgroups = 4096;  // candidate stage: workgroups over all rows
 constexpr double kMaxLogitsBytes = 16.0 * (1 << 30);   // logits-path workspace budget
 constexpr int kMaxSplits = 2048;             // combine kernel keeps one weight per split in LDS
-constexpr int kSparseSplitLen = 64;          // index entries per sparse workgroup
+constexpr int kSparseSplitLen = 64;          // index entries per sparse workgroup (fewest)
+constexpr int kSparseTargetWorkgroups = 320;  // ... unless the rows would launch more than this
 constexpr int kSelectChunk = kSelectChunkLen;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -151,7 +152,11 @@ Layout make_layout(const hs2_attn_desc* d) {
   L.fast_ok = d->select_mode == HS2_SELECT_TOKEN && L.n_cchunks <= kMaxFastChunks &&
               L.rec_n_split <= kMaxSplits;
 
-  int64_t sp = env_int("HS2_SPARSE_SPLIT_LEN", kSparseSplitLen);
+  // index entries per sparse workgroup: 64, doubled (up to 256) while the rows would
+  // launch more than ~320 workgroups (many rows: fewer, longer chains measured faster)
+  int64_t sp = kSparseSplitLen;
+  while (sp < 256 && L.n_sel * ceil_div(L.S, sp) > kSparseTargetWorkgroups) sp *= 2;
+  sp = env_int("HS2_SPARSE_SPLIT_LEN", (int)sp);
   sp = std::max<int64_t>(ceil_div(sp, 32) * 32, 32);
   while (ceil_div(L.S, sp) > kMaxSplits) sp *= 2;
   L.split_len_sp = (int32_t)sp;
