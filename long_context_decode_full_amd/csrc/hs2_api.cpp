@@ -24,6 +24,7 @@ constexpr int64_t kFusedSparseRows = 256;    // sparse layer: one workgroup per 
 constexpr int kCandTargetWorkgroups = 4096;  // candidate stage: workgroups over all rows
 constexpr double kMaxLogitsBytes = 16.0 * (1 << 30);   // logits-path workspace budget
 constexpr int kMaxSplits = 2048;             // combine kernel keeps one weight per split in LDS
+constexpr int kChunkMaxSplit = 4096;         // positions per chunk-kernel split (at most)
 constexpr int kSparseSplitLen = 64;          // index entries per sparse workgroup (fewest)
 constexpr int kSparseTargetWorkgroups = 320;  // ... unless the rows would launch more than this
 constexpr int kSelectChunk = kSelectChunkLen;
@@ -128,12 +129,15 @@ Layout make_layout(const hs2_attn_desc* d) {
 
   // Record path: a split's records stay in LDS until it is done, which bounds the split.
   // The matrix-core scan holds 1 workgroup per CU: one residency round of 256.  The
-  // chunk kernel (one workgroup per CU, 32 query tokens each) takes about 16 splits
-  // of the longest context per (sequence, KV head).
+  // chunk kernel (one workgroup per CU, 32 query tokens each) takes 1/16 of the
+  // longest context per split, between 1,024 and 4,096 positions: ragged batches
+  // then spread over many rounds of workgroups (16,384-position splits left a third
+  // of the CUs idle in the last round; splits past a sequence's end cost nothing).
   int64_t rsplit;
   if (chunk_path(d) || chunk_block_path(d)) {
     rsplit = ceil_div(ceil_div(d->max_ctx_len, 16), 256) * 256;
-    rsplit = std::max<int64_t>(rsplit, 1024);
+    rsplit = std::min<int64_t>(std::max<int64_t>(rsplit, 1024), kChunkMaxSplit);
+    while (ceil_div(d->max_ctx_len, rsplit) > kMaxSplits && rsplit < kMaxRecordSplit) rsplit *= 2;
   } else {
     const int64_t rec_target = env_int("HS2_SCAN_VALU", 0) ? kScanTargetWorkgroups : kMfmaTargetWorkgroups;
     rsplit = ceil_div(ceil_div(rows, rec_target), 256) * 256;
@@ -343,6 +347,10 @@ hs2_status chunk_block_select(const hs2_attn_desc* desc, const Layout& L, ScanAr
   ca.G = L.G;
   ca.Hq = desc->n_q_heads;
   ca.n_split = sa.n_split;
+  ca.ctx_len = sa.ctx_len;   // fold only the splits below each row's visible length
+  ca.ctx_max = sa.ctx_max;
+  ca.Lq = sa.Lq;
+  ca.split_len = sa.split_len;
   if (launch_combine(ca, stream) != hipSuccess) return HS2_ERR_LAUNCH;
 
   SelectArgs sl{};
@@ -420,6 +428,10 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   ca.G = L.G;
   ca.Hq = desc->n_q_heads;
   ca.n_split = sa.n_split;
+  ca.ctx_len = sa.ctx_len;   // fold only the splits below each row's visible length
+  ca.ctx_max = sa.ctx_max;
+  ca.Lq = sa.Lq;
+  ca.split_len = sa.split_len;
   if (launch_combine(ca, stream) != hipSuccess) return HS2_ERR_LAUNCH;
 
   if (fast) {

@@ -152,6 +152,10 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   int64_t p_end = p_begin + a.split_len;
   p_end = p_end < n_last ? p_end : n_last;
   if (ntok <= 0) return;
+  // a split past every visible position of this group's tokens has nothing to write:
+  // the combine folds, per token, only the splits below its visible length (split 0
+  // always runs: it also clears the merged histograms)
+  if (split > 0 && p_begin >= n_last) return;
   const int64_t sel_tok0 = ((int64_t)b * a.Lq + tok0) * a.Hkv + g;   // sel of token tok0; +Hkv per token
 
   constexpr bool want_rec = !kBlockMode;   // token selection: records + histograms

@@ -92,6 +92,11 @@ struct CombineArgs {
                             // + kSelHist1Off (atomic sums into words the scan cleared)
   int32_t hist_only;        // launch-internal: blockIdx.y indexes histogram groups only
   int32_t n_sel, Hkv, G, Hq, n_split;
+  // context scans: a row folds only the splits that hold its visible positions
+  // (ceil(n / split_len)); the others may be unwritten.  nullptr: every split.
+  const int32_t* ctx_len;
+  int64_t ctx_max;
+  int32_t Lq, split_len;
 };
 
 struct SelectArgs {

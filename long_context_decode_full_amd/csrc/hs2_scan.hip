@@ -370,6 +370,21 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
 
 }
 
+// Splits of selection row `sel` that hold visible positions (all of them for the
+// sparse gather, whose splits run over index entries).
+__device__ __forceinline__ int live_splits(const CombineArgs& a, int64_t sel) {
+  if (a.ctx_len == nullptr) return a.n_split;
+  const int64_t bj = sel / a.Hkv;
+  const int64_t b = bj / a.Lq;
+  const int64_t j = bj - b * a.Lq;
+  int64_t ctx = a.ctx_len[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.ctx_max ? a.ctx_max : ctx);
+  int64_t n = ctx - a.Lq + j + 1;
+  n = n < 0 ? 0 : n;
+  const int64_t live = (n + a.split_len - 1) / a.split_len;
+  return (int)(live < a.n_split ? live : a.n_split);
+}
+
 // One workgroup per (selection row, head, 32-dim chunk) merges the split partials
 // into the normalised output and records the row's softmax statistics (M, 1/Z),
 // which the selection kernels need to turn logits into probabilities.  It merges the
@@ -390,7 +405,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     if (a.hist_part == nullptr) return;
     const int mg = (chunk - kHeadDim / 32) * a.G + h;
     const int s0 = mg * kHistMergeSplits;
-    if (s0 >= a.n_split) return;
+    const int live = live_splits(a, sel);
+    if (s0 >= live) return;
     __shared__ __attribute__((aligned(16))) uint32_t hred[4][kFastBins];
     // wave w: splits s0 + 4w .. s0 + 4w + 3; lane l: bins [16 l, 16 l + 16)
     const uint16_t* hp = a.hist_part + (int64_t)sel * a.n_split * kFastBins + lane * 16;
@@ -398,7 +414,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int s = s0 + wave * 4 + u;
-      if (s < a.n_split) {
+      if (s < live) {
         wv[u][0] = *reinterpret_cast<const uint4*>(hp + (int64_t)s * kFastBins);
         wv[u][1] = *reinterpret_cast<const uint4*>(hp + (int64_t)s * kFastBins + 8);
       } else {
@@ -440,7 +456,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   float o[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) o[i] = 0.0f;
-  for (int s = tid; s < a.n_split; s += 256) {
+  const int live = live_splits(a, sel);
+  for (int s = tid; s < live; s += 256) {
     const float* ps = base + (int64_t)s * split_stride;
     const float ms = ps[0];
     const float zs = ps[1];
@@ -502,9 +519,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
 }
 
-// Few splits (sparse layers, chunk rows): one thread per (row, head, 4 dims) folds
-// every split itself, four splits of loads in flight; no cross-thread reduction.
+// Few splits (sparse layers), or many rows (query chunks: a row folds only its live
+// splits, ~30 on average there): one thread per (row, head, 4 dims) folds every split
+// itself, four splits of loads in flight; no cross-thread reduction.
 constexpr int kSmallSplits = 32;
+constexpr int64_t kSmallPairs = 8192;   // (row, head) pairs from which rows give the parallelism
 __global__ __launch_bounds__(256) void combine_small_kernel(CombineArgs a) {
   const int tid = threadIdx.x;
   const int64_t pair = (int64_t)blockIdx.x * 8 + (tid >> 5);   // sel * G + h
@@ -515,7 +534,7 @@ __global__ __launch_bounds__(256) void combine_small_kernel(CombineArgs a) {
   float m_loc, z_loc;
   float4 o;
   fold_splits(a.part + ((int64_t)sel * a.n_split * a.G + h) * kPartStride, (int64_t)a.G * kPartStride,
-              a.n_split, dq, m_loc, z_loc, o);
+              live_splits(a, sel), dq, m_loc, z_loc, o);
   const float iz = z_loc > 0.0f ? 1.0f / z_loc : 0.0f;
   const int bj = sel / a.Hkv;
   const int g = sel - bj * a.Hkv;
@@ -561,7 +580,7 @@ hipError_t launch_scan_sparse(const ScanArgs& a, bool fp8, int B, hipStream_t st
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   const int n_groups = (a.n_split + kHistMergeSplits - 1) / kHistMergeSplits;
   const int extra = a.hist_part != nullptr ? (n_groups + a.G - 1) / a.G : 0;
-  if (a.n_split <= kSmallSplits) {
+  if (a.n_split <= kSmallSplits || (int64_t)a.n_sel * a.G >= kSmallPairs) {
     const int64_t pairs = (int64_t)a.n_sel * a.G;
     hipLaunchKernelGGL(combine_small_kernel, dim3((unsigned)((pairs + 7) / 8)), dim3(256), 0, st, a);
     if (extra > 0) {   // histogram merge only
