@@ -280,6 +280,47 @@ def test_chunk_split_invariant(monkeypatch):
     assert np.max(np.abs(a["out_full"] - b["out_full"])) <= 2e-6 * max(1.0, np.max(np.abs(b["out_full"])))
 
 
+POISON_CASES = {
+    # query chunks of very different lengths: most position splits of the short
+    # sequences lie past their ends (their workgroups exit without writing)
+    "chunk_token": (wl.Workload("ragged chunk", 3, 64, 32, 4, ctx_lens=[40000, 3000, 9000], n_needles=16,
+                                seed=2210), "token"),
+    "chunk_block": (wl.Workload("ragged chunk", 3, 64, 32, 4, ctx_lens=[40000, 3000, 9000], n_needles=16,
+                                seed=2211), "block"),
+    # ragged decode: splits past a short row's end are written but never folded
+    "decode_token": (wl.Workload("ragged decode", 3, 1, 32, 4, ctx_lens=[200000, 5000, 70], n_needles=16,
+                                 seed=2212), "token"),
+}
+
+
+@pytest.mark.parametrize("name", list(POISON_CASES))
+def test_workspace_contents_do_not_matter(name):
+    """The workspace filled with 0xFF bytes (NaN floats, maximal counts) before the
+    call gives bitwise the outputs of a zeroed one (deterministic scan): no kernel reads
+    workspace memory that the same call did not write (the combine folds only the
+    splits below each row's visible length)."""
+    from long_context_decode_full_amd import hs2_set_deterministic
+    from long_context_decode_full_amd.runner import HybridBlockDevice
+    w, mode = POISON_CASES[name]
+    _announce(f"poisoned-workspace-{name}", w)
+    inp = wl.make_inputs(w)
+    hs2_set_deterministic(True)
+    try:
+        outs = []
+        for fill in (0, 255):
+            dev = HybridBlockDevice(inp, mode=mode)
+            dev.workspace.fill_(fill)
+            dev.step()
+            outs.append(dev.results())
+    finally:
+        hs2_set_deterministic(False)
+    a, b = outs
+    assert np.array_equal(a["idx"], b["idx"])
+    for x, y in zip([a["out_full"]] + list(a["out_sparse"]), [b["out_full"]] + list(b["out_sparse"])):
+        assert not np.isnan(y).any()
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
 # ------------------------------------------------------------------ edges
 @pytest.fixture(params=["auto", "fused"])
 def sparse_path(request, monkeypatch):
