@@ -124,6 +124,27 @@ __device__ __forceinline__ int32_t key_pos(uint64_t key) {
   return 0x7FFFFFFF - (int32_t)(uint32_t)key;
 }
 
+// Records t0 .. t0 + R - 1 of a row (zero past w0) as R/2 packed words.
+template <int R>
+__device__ __forceinline__ void load_records(uint32_t (&words)[R / 2], const uint16_t* __restrict__ rrow,
+                                             int64_t t0, int64_t w0) {
+  if (t0 + R <= w0) {
+#pragma unroll
+    for (int v = 0; v < R / 8; ++v) {
+      const uint4 x = *reinterpret_cast<const uint4*>(rrow + t0 + 8 * v);
+      words[4 * v + 0] = x.x; words[4 * v + 1] = x.y; words[4 * v + 2] = x.z; words[4 * v + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < R / 2; ++i) {
+      const int64_t t = t0 + 2 * i;
+      const uint32_t lo = t < w0 ? (uint32_t)rrow[t] : 0u;
+      const uint32_t hi = t + 1 < w0 ? (uint32_t)rrow[t + 1] : 0u;
+      words[i] = lo | (hi << 16);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ candidates + exact re-score
 // Work unit: one (row, chunk of chunk_len positions); workgroup w of a row takes its
 // chunks w, w + cand_wgs, ... (blockIdx.x = row * cand_wgs + w; the grid is sized so
@@ -147,7 +168,6 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   const RowGeom rg = row_geom(a, sel);
   if (rg.w0 <= a.topk || a.topk == 0) return;
   constexpr int clen = R * kThreads;
-  constexpr int nv = R / 8;       // 16-byte loads per thread
   // chunks at or past the first window position hold no candidate (and are not read)
   if ((int64_t)wg * clen >= rg.w0) return;
 
@@ -166,6 +186,12 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   uint32_t qp[8][4];   // issued early: its latency overlaps the threshold and the filter
   load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);
   const uint16_t* rrow = a.records + sel * a.rec_stride;
+  // The first chunk's records are loaded before the threshold is found (their latency
+  // overlaps it); with R <= 32 the next chunk's records are loaded while the current
+  // chunk re-scores (a row's workgroup takes its chunks in turn in the chunk config).
+  constexpr bool kPrefetch = R <= 32;
+  uint32_t words[R / 2];
+  load_records<R>(words, rrow, (int64_t)wg * clen + (int64_t)tid * R, rg.w0);
 
   // threshold: bin of the k-th largest record key in the merged histogram
   uint32_t tb, above;
@@ -209,22 +235,7 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
     // Each thread owns R consecutive positions (one batch of 16-byte loads); a
     // block-wide exclusive scan of the per-thread counts keeps position order.
     const int64_t t0 = c0 + (int64_t)tid * R;
-    uint32_t words[R / 2];
-    if (t0 + R <= rg.w0) {
-#pragma unroll
-      for (int v = 0; v < nv; ++v) {
-        const uint4 x = *reinterpret_cast<const uint4*>(rrow + t0 + 8 * v);
-        words[4 * v + 0] = x.x; words[4 * v + 1] = x.y; words[4 * v + 2] = x.z; words[4 * v + 3] = x.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < R / 2; ++i) {
-        const int64_t t = t0 + 2 * i;
-        const uint32_t lo = t < rg.w0 ? (uint32_t)rrow[t] : 0u;
-        const uint32_t hi = t + 1 < rg.w0 ? (uint32_t)rrow[t + 1] : 0u;
-        words[i] = lo | (hi << 16);
-      }
-    }
+    if (!kPrefetch && chunk != wg) load_records<R>(words, rrow, t0, rg.w0);
     uint64_t hitmask = 0ull, certmask = 0ull;
     if (use_cert) {
 #pragma unroll
@@ -243,6 +254,10 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
       }
     }
     const uint64_t uncmask = hitmask & ~certmask;
+    if constexpr (kPrefetch) {   // this chunk's records are consumed: load the next chunk's
+      const int64_t cn = c0 + (int64_t)a.cand_wgs * clen;
+      if (cn < rg.w0) load_records<R>(words, rrow, cn + (int64_t)tid * R, rg.w0);
+    }
     // block exclusive scan of (hits, uncertain hits), packed in one word (each < 2^16)
     const uint32_t mine = (uint32_t)__builtin_popcountll(hitmask) | ((uint32_t)__builtin_popcountll(uncmask) << 16);
     const uint32_t x = wave_prefix_incl(mine);
