@@ -157,10 +157,15 @@ def block_select(s, block: int, n_blocks: int):
 
 # --------------------------------------------------------------------------- one Hybrid Block
 def hybrid_block_token(inp: dict, b: int, j: int, window=128, topk=1024, mode="token",
-                       block=64, n_blocks=18, want_scores=True, groups=None):
+                       block=64, n_blocks=18, want_scores=True, groups=None, ctx_max=None,
+                       kv_cache=None):
     """Everything the Hybrid Block computes for query token j of sequence b, per KV group g:
     full-layer output, group scores, index set, and each sparse layer's output.
-    `groups` restricts the work to some KV groups (others are left zero / -1)."""
+    `groups` restricts the work to some KV groups (others are left zero / -1).
+    `ctx_max`: the caller's bound on the context length (default: the capacity); a
+    larger ctx_len counts as ctx_max.  `kv_cache`: optional dict g -> (K, V) of float64
+    rows [0, m) of sequence b (as kv_rows returns them, m >= the visible count), so that
+    several tokens of one sequence share one conversion."""
     q_full = bf16_to_f64(inp["q_full"][b, j])            # [Hq, D]
     qs = [bf16_to_f64(q[b, j]) for q in inp["q_sparse"]]
     Hq = q_full.shape[0]
@@ -168,8 +173,9 @@ def hybrid_block_token(inp: dict, b: int, j: int, window=128, topk=1024, mode="t
     G = Hq // Hkv
     Lq = inp["q_full"].shape[1]
     sm = inp["sm_scale"]
-    n = int(inp["ctx_len"][b]) - Lq + j + 1                # R8
-    n = max(0, min(n, inp["k"].shape[2]))
+    cap = inp["k"].shape[2]
+    ctx = min(max(int(inp["ctx_len"][b]), 0), cap if ctx_max is None else min(int(ctx_max), cap))
+    n = max(0, ctx - Lq + j + 1)                           # R8
     S = block * n_blocks if mode == "block" else window + topk
     out_full = np.zeros((Hq, q_full.shape[1]))
     out_sp = [np.zeros_like(out_full) for _ in qs]
@@ -177,7 +183,10 @@ def hybrid_block_token(inp: dict, b: int, j: int, window=128, topk=1024, mode="t
     s_all = []
     for g in (range(Hkv) if groups is None else groups):
         heads = slice(g * G, (g + 1) * G)                  # R5
-        K, V = kv_rows(inp, b, g, n)
+        if kv_cache is not None:
+            K, V = kv_cache[g][0][:n], kv_cache[g][1][:n]
+        else:
+            K, V = kv_rows(inp, b, g, n)
         o, P = full_attention(q_full[heads], K, V, sm)
         out_full[heads] = o
         s = group_scores(P)

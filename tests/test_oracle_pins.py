@@ -333,6 +333,29 @@ def test_chunk_positions_are_causal():
                 assert r["idx"][g].max() == r["n"] - 1
 
 
+def test_context_clamp_and_shared_conversion():
+    """A ctx_len above the caller's bound counts as the bound (every token of the chunk
+    shifts with it; the library clamps ctx_len to [0, max_ctx_len] the same way), a
+    negative one as 0; rows converted once per sequence give the per-token result."""
+    w = wl.Workload("t", 1, 4, 8, 2, ctx_lens=[300], seed=5)
+    inp = wl.make_inputs(w)
+    for j in range(4):
+        r = oracle.hybrid_block_token(inp, 0, j, window=16, topk=32, ctx_max=250)
+        assert r["n"] == 250 - 4 + j + 1
+        low = dict(inp, ctx_len=np.array([250], dtype=np.int32))
+        ref = oracle.hybrid_block_token(low, 0, j, window=16, topk=32)
+        assert np.array_equal(r["idx"], ref["idx"]) and np.array_equal(r["out_full"], ref["out_full"])
+        neg = oracle.hybrid_block_token(dict(inp, ctx_len=np.array([-9], dtype=np.int32)), 0, j)
+        assert neg["n"] == 0 and np.all(neg["idx"] == -1) and not neg["out_full"].any()
+        cache = {g: oracle.kv_rows(inp, 0, g, 300) for g in range(2)}
+        shared = oracle.hybrid_block_token(inp, 0, j, window=16, topk=32, kv_cache=cache)
+        plain = oracle.hybrid_block_token(inp, 0, j, window=16, topk=32)
+        assert np.array_equal(shared["idx"], plain["idx"])
+        assert np.array_equal(shared["out_full"], plain["out_full"])
+        for a, c in zip(shared["out_sparse"], plain["out_sparse"]):
+            assert np.array_equal(a, c)
+
+
 def test_fp8_path_uses_dequantised_values():
     w = wl.Workload("t", 1, 1, 8, 2, ctx_lens=[500], kv_dtype="fp8", n_needles=4, seed=12)
     inp = wl.make_inputs(w)
