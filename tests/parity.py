@@ -17,7 +17,15 @@ rounded to float32 and values below the smallest normal float32 are flushed to
 zero (the kernel's exp2 does not produce subnormals) before the k-th value and
 the band are evaluated.  Probabilities that small (e.g. 1e-72 next to a
 dominant key) are all zero in float32, and then the lower-position tie rule
-decides on both sides.
+decides on both sides -- and is checked: when the rows differ, the GPU's choice
+must be the top-k by (score desc, position asc) for SOME scores within the band
+of the kernel-precision ones.  Each candidate gets the interval
+[s32 (1 - band), s32 (1 + band)] (lower end 0 for scores at the edge of the
+float32 range, which the kernel may flush), and no unselected candidate may
+beat a selected one for every choice in the intervals: an unselected u beats a
+selected t if lo(u) > hi(t), or lo(u) == hi(t) (a degenerate interval, i.e. an
+exact zero on both sides) and u < t.  So among candidates whose score is 0 in
+float32, the GPU must pick the lowest positions.
 """
 import numpy as np
 
@@ -53,6 +61,32 @@ def assert_out_close(gpu, ref, tol=OUT_TOL, what="out"):
     return worst
 
 
+def order_violation(sel_mask, s32, band=TIE_BAND):
+    """First (t, u) with candidate t selected, u not, and u ahead of t in (score desc,
+    position asc) order for every score within the band of s32 (see the module
+    docstring), or None.  sel_mask: boolean per candidate position; s32:
+    kernel-precision scores of the candidates."""
+    sel = np.nonzero(sel_mask)[0]
+    unsel = np.nonzero(~sel_mask)[0]
+    if len(sel) == 0 or len(unsel) == 0:
+        return None
+    edge = F32_TINY * (1.0 + 4.0 * band)
+    h = s32[sel] * (1.0 + band)
+    su = s32[unsel]
+    l = np.where(su <= edge, 0.0, su * (1.0 - band))
+    a, b = h.min(), l.max()
+    if a > b:
+        return None
+    if a < b:
+        return int(sel[np.argmin(h)]), int(unsel[np.argmax(l)])
+    # a == b: only exact equalities (zeros) remain; positions decide
+    t_last = sel[h == a].max()
+    u_first = unsel[l == b].min()
+    if u_first < t_last:
+        return int(t_last), int(u_first)
+    return None
+
+
 def check_idx_row(gpu_row, ref_row, s, n, window, topk, band=TIE_BAND):
     """Returns the number of positions swapped inside the tie band (asserts otherwise)."""
     gpu_row = np.asarray(gpu_row)
@@ -66,16 +100,25 @@ def check_idx_row(gpu_row, ref_row, s, n, window, topk, band=TIE_BAND):
     w0 = max(0, n - window)
     assert set(range(w0, n)) <= set(gv.tolist()), "forced window missing"
     diff = set(gv.tolist()) ^ set(rv.tolist())
-    if not diff:
-        return 0
-    cand = np.arange(w0)
     kk = min(topk, w0)
-    assert kk < w0, "all candidates are selected, no swap is allowed"
-    s32 = kernel_precision(s)
-    vk = np.sort(s32[cand])[::-1][kk - 1]
+    if kk == w0:
+        assert not diff, "all candidates are selected, no swap is allowed"
+        return 0
+    s32 = kernel_precision(np.asarray(s)[:w0])
+    if not diff and np.count_nonzero(s32 > 0) >= kk:
+        # same set as the oracle, whose float64 order is consistent with every band
+        return 0
+    vk = np.sort(s32)[::-1][kk - 1]
+    edge = F32_TINY * (1.0 + 4.0 * band)
     for t in diff:
         assert t < w0, f"window position {t} differs"
-        assert abs(s32[t] - vk) <= band * vk, f"swap at {t}: score {s[t]!r} vs k-th {vk!r}"
+        near = abs(s32[t] - vk) <= band * vk or (vk == 0.0 and s32[t] <= edge)
+        assert near, f"swap at {t}: score {s[t]!r} vs k-th {vk!r}"
+    sel_mask = np.zeros(w0, dtype=bool)
+    sel_mask[gv[gv < w0]] = True
+    bad = order_violation(sel_mask, s32, band)
+    assert bad is None, (f"tie order: position {bad[0]} selected over {bad[1]} "
+                         f"(scores {s32[bad[0]]!r}, {s32[bad[1]]!r}, k-th {vk!r})")
     return len(diff) // 2
 
 
