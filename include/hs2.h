@@ -25,9 +25,10 @@
  *   - Every argument is checked on the host before anything is enqueued.  A
  *     failed check returns its status and enqueues nothing.  A launch failure
  *     returns HS2_ERR_LAUNCH.  Nothing is printed and nothing aborts.
- *   - The library is stateless apart from the optional kernel timer below;
- *     concurrent calls on different streams need distinct workspaces and
- *     outputs.
+ *   - The library keeps no state between calls (no globals, no environment
+ *     reads): everything a call does follows from its arguments, so it is
+ *     reentrant; concurrent calls on different streams need distinct
+ *     workspaces and outputs.
  *
  * Layouts (row-major; B batch, Lq query tokens per sequence, Hq query heads,
  * Hkv KV heads, G = Hq / Hkv, D = head_dim = 128, cap = kv_capacity,
@@ -38,7 +39,8 @@
  *   ctx_len  [B] int32: visible positions of sequence b, INCLUDING its Lq query
  *            tokens, which occupy positions ctx_len[b]-Lq .. ctx_len[b]-1.  Query
  *            token j sees positions [0, ctx_len[b]-Lq+j] (causal inside the chunk).
- *            Values are clamped to [0, cap] on the device.
+ *            Values are clamped to [0, max_ctx_len] on the device (max_ctx_len is
+ *            the descriptor's host-side bound; values above it are a caller error).
  *   out      [B, Lq, Hq, D]    float32                                16-B aligned
  *   idx      [B, Lq, Hkv, S]   int32, ascending positions, -1 padding at the end
  *   probs    [B, Lq, Hkv, cap] float32 group-summed probabilities (optional)
@@ -81,17 +83,56 @@ typedef struct hs2_attn_desc {
   int32_t block_size;     /* block mode only: positions per block (64)                   */
   int32_t n_blocks;       /* block mode only: blocks kept (18)                           */
   float sm_scale;         /* softmax scale, normally 1/sqrt(head_dim); must be > 0       */
+  /* Options.  A zero-initialised tail gives the defaults; every value below changes
+   * only how the work is split or which kernels run, never what is computed (up to
+   * fp32 summation order in `out`; idx is the same).  All are part of the descriptor,
+   * so hs2_workspace_size and the calls always agree on the workspace layout. */
+  uint32_t flags;         /* HS2_FLAG_* bits                                             */
+  int32_t split_len;      /* positions per context-scan workgroup: 0 = automatic, else
+                             rounded up to a multiple of 256 (kernel limits applied)      */
+  int32_t sparse_split_len; /* index entries per sparse-gather workgroup: 0 = automatic,
+                             else rounded up to a multiple of 32                          */
+  int32_t cand_workgroups;  /* candidate-stage workgroups over all selection rows:
+                             0 = automatic (4096), else at least one per row              */
 } hs2_attn_desc;
 
-/* Host only, touches no GPU: checks a descriptor.  Limits: head_dim == 128,
+/* hs2_attn_desc.flags */
+enum {
+  /* Fixed step shares in the context scan.  By default the waves of a scan workgroup
+   * take steps from a shared counter, so the order in which a head's probabilities are
+   * summed into `out` varies between runs and `out` of hs2_full_attn_select can differ
+   * in the last fp32 bits (idx never does).  With this flag `out` is bitwise
+   * reproducible; the scan is ~3% slower. */
+  HS2_FLAG_DETERMINISTIC = 1u << 0,
+  /* Token selection on the logits path (every logit kept, exact radix select) even
+   * when probs is NULL.  For comparing the two selection paths. */
+  HS2_FLAG_FORCE_LOGITS = 1u << 1,
+  /* The record path's context scan on the VALU kernel (dot2 + DPP) instead of the
+   * matrix cores.  For comparing the two scans. */
+  HS2_FLAG_SCAN_VALU = 1u << 2,
+  /* Query chunks (q_len > 1) run the decode scan once per query token instead of the
+   * matrix-core chunk kernel. */
+  HS2_FLAG_CHUNK_PER_TOKEN = 1u << 3,
+  /* Sparse layers: one workgroup per (token, KV head) gathering the whole index row
+   * (the default from 256 rows), or the split gather + combine (the default below).
+   * Setting both is HS2_ERR_INVALID_ARG. */
+  HS2_FLAG_SPARSE_FUSED = 1u << 4,
+  HS2_FLAG_SPARSE_SPLIT = 1u << 5
+};
+#define HS2_FLAGS_ALL 0x3Fu
+
+/* Host only, touches no GPU: checks a descriptor and that `workspace_bytes` covers
+ * hs2_workspace_size(desc) (HS2_ERR_WORKSPACE otherwise; pass SIZE_MAX to check the
+ * descriptor alone).  Limits: head_dim == 128,
  * 1 <= G <= 32 with G > 8 (up to MQA at 32 query heads) in token mode only and without
  * probs (hs2_full_attn_select then returns HS2_ERR_UNSUPPORTED), window + topk <= 4096
  * (token mode), block_size in [1, 4096] and
  * block_size * n_blocks <= 4096 (block mode), 1 <= q_len <= max_ctx_len <= cap,
  * cap < 2^31, batch * q_len <= 65535, n_kv_heads <= 65535 and
  * batch * q_len * n_kv_heads (selection rows) <= 65535 * 1024; beyond these limits
- * HS2_ERR_UNSUPPORTED. */
-hs2_status hs2_validate(const hs2_attn_desc* desc);
+ * HS2_ERR_UNSUPPORTED; unknown flag bits or negative tuning values are
+ * HS2_ERR_INVALID_ARG. */
+hs2_status hs2_validate(const hs2_attn_desc* desc, size_t workspace_bytes);
 
 /* Host only: bytes of device workspace that hs2_full_attn_select and
  * hs2_sparse_attn need for this descriptor (the larger of the two).  Requesting probs,
@@ -199,7 +240,8 @@ hs2_status hs2_sparse_attn_swa(const hs2_attn_desc* desc, const void* q, const v
  * nothing, keeps no pointer after it returns and needs no workspace.  Errors
  * (HS2_ERR_INVALID_ARG: a NULL pointer or layer pointer, a bad size;
  * HS2_ERR_UNSUPPORTED: head_dim != 128, hidden not a multiple of 64, more than 16
- * layers, too large a grid; HS2_ERR_ALIGNMENT) are returned before anything is
+ * layers, too large a grid; HS2_ERR_ALIGNMENT; HS2_ERR_INVALID_ARG for a
+ * gemv_max_tokens outside -1 .. 1024 or reserved != 0) are returned before anything is
  * enqueued; n_tokens == 0 enqueues nothing and returns HS2_OK. */
 typedef struct hs2_bridge_desc {
   int32_t n_tokens;       /* T >= 0 rows of the source hidden state                      */
@@ -210,6 +252,12 @@ typedef struct hs2_bridge_desc {
   int32_t kv_dtype;       /* HS2_KV_BF16 or HS2_KV_FP8_E4M3FN                             */
   int32_t batch;          /* sequences per cache, >= 1                                    */
   int64_t kv_capacity;    /* rows per (sequence, KV head), 1 .. 2^31 - 1                  */
+  /* Option (zero = default): calls of at most this many tokens take the decode-size
+   * kernel (W rows streamed into registers) instead of the tile GEMM.  0 = 16 tokens,
+   * -1 = never, else 1 .. 1024.  Same results either way (fp32 sums of the same
+   * products in another order). */
+  int32_t gemv_max_tokens;
+  int32_t reserved;       /* 0                                                           */
 } hs2_bridge_desc;
 
 hs2_status hs2_kv_bridge(const hs2_bridge_desc* desc, const void* x, const void* w,
@@ -225,8 +273,10 @@ hs2_status hs2_kv_bridge(const hs2_bridge_desc* desc, const void* x, const void*
  * Full layer selects positions from its own attention scores and the Sparse layers
  * reuse its cache and selection) and section 04 (generation keeps the full network).
  * In stream order:
- *   1. pos[b] = ctx_len[b] and ctx_len[b] += 1 (a sequence whose cache is full keeps
- *      its length and appends nothing);
+ *   1. pos[b] = ctx_len[b] and ctx_len[b] += 1, except that a sequence whose length
+ *      has reached attn.max_ctx_len (the bound every attention call reads up to; at
+ *      most the capacity) keeps its length and appends nothing -- its attention then
+ *      runs over the same max_ctx_len positions again;
  *   2. hs2_kv_bridge of the batch's new source rows x [batch, hidden] into the caches
  *      of every block (block l = target layer l of w), at (b, pos[b]);
  *   3. for each block l: hs2_full_attn_select(q_full[l]) into out_full[l], idx[l],
@@ -259,27 +309,36 @@ hs2_status hs2_decode_step(const hs2_decode_plan* plan, const void* x, const voi
                            float* const* out_sparse, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
-/* Reproducibility switch (process-wide, default off).  By default the waves of a
- * context-scan workgroup share its steps through a counter, so the order in which
- * a head's probabilities are summed into `out` varies between runs and `out` of
- * hs2_full_attn_select can differ in the last bits of fp32 (idx never does: each
- * position's selection score is computed on its own).  With `on` != 0, later calls
- * give every wave a fixed share of the steps: bitwise reproducible output, ~3%
- * slower scan.  Takes effect for calls made after it returns. */
-hs2_status hs2_set_deterministic(int on);
+/* ------------------------------------------------------------------ kernel timing
+ * Benchmark support without library state: the caller creates two HIP events
+ * (hipEventCreate) and passes them; the call records `begin` on `stream` just before
+ * its dominant kernel -- the context scan of hs2_full_attn_select, the gather of
+ * hs2_sparse_attn -- and `end` just after it, so hipEventElapsedTime(begin, end) is
+ * that kernel's duration.  Otherwise identical to the untimed calls (which are these
+ * with events == NULL).  The caller owns and destroys the events. */
+typedef struct hs2_kernel_events {
+  hipEvent_t begin;
+  hipEvent_t end;
+} hs2_kernel_events;
 
-/* Benchmark support.  `mask` selects the kernels timed from now on: HS2_TIMER_SCAN
- * (the context scan of hs2_full_attn_select), HS2_TIMER_GATHER (the gather kernel of
- * hs2_sparse_attn), both, or 0 for none.  Each timed call records two HIP events on
- * its stream around that kernel.  The events are created by the library (host-side
- * bookkeeping, no device memory) and kept until hs2_timer_collect, which waits for
- * them and returns the summed milliseconds and the number of launches timed for
- * each kind, then forgets them.  Not thread-safe; meant for single-threaded
- * benchmark drivers. */
-enum { HS2_TIMER_SCAN = 1, HS2_TIMER_GATHER = 2 };
-hs2_status hs2_timer_enable(int mask);
-hs2_status hs2_timer_collect(double* scan_ms, int32_t* scan_count,
-                             double* gather_ms, int32_t* gather_count);
+hs2_status hs2_full_attn_select_timed(const hs2_attn_desc* desc,
+                                      const void* q, const void* k, const void* v,
+                                      const float* k_scale, const float* v_scale,
+                                      const int32_t* ctx_len,
+                                      float* out, int32_t* idx, float* probs,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream, const hs2_kernel_events* events);
+hs2_status hs2_sparse_attn_timed(const hs2_attn_desc* desc,
+                                 const void* q, const void* k, const void* v,
+                                 const float* k_scale, const float* v_scale,
+                                 const int32_t* ctx_len, const int32_t* idx,
+                                 float* out,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream, const hs2_kernel_events* events);
+
+/* Static text naming the sources the library was built from (a hash of the kernel,
+ * host and header files); never NULL.  Lets a caller detect a stale binary. */
+const char* hs2_build_id(void);
 
 #ifdef __cplusplus
 }

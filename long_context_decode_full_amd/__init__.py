@@ -20,11 +20,13 @@ __all__ = [
     "HS2_ERR_ALIGNMENT", "HS2_ERR_LAUNCH", "HS2_KV_BF16", "HS2_KV_FP8_E4M3FN",
     "HS2_SELECT_TOKEN", "HS2_SELECT_BLOCK", "Hs2AttnDesc", "Hs2Error", "make_desc",
     "hs2_validate", "hs2_workspace_size", "hs2_full_attn_select", "hs2_sparse_attn",
-    "hs2_status_string", "hs2_set_deterministic", "hs2_timer_enable", "hs2_timer_collect", "HS2_TIMER_SCAN",
-    "HS2_TIMER_GATHER", "library_path", "load_library", "Hs2BridgeDesc", "make_bridge_desc",
+    "hs2_status_string", "hs2_full_attn_select_timed", "hs2_sparse_attn_timed", "Hs2KernelEvents",
+    "hs2_build_id", "HS2_FLAG_DETERMINISTIC", "HS2_FLAG_FORCE_LOGITS", "HS2_FLAG_SCAN_VALU",
+    "HS2_FLAG_CHUNK_PER_TOKEN", "HS2_FLAG_SPARSE_FUSED", "HS2_FLAG_SPARSE_SPLIT", "HS2_FLAGS_ALL",
+    "library_path", "load_library", "Hs2BridgeDesc", "make_bridge_desc",
     "hs2_kv_bridge", "Hs2DecodePlan", "make_decode_plan", "hs2_decode_workspace_size",
     "hs2_decode_step", "hs2_sparse_attn_swa_workspace_size", "hs2_sparse_attn_swa",
-    "EXPORTED_SYMBOLS",
+    "EXPORTED_SYMBOLS", "SIZE_MAX",
 ]
 
 HS2_OK = 0
@@ -37,10 +39,19 @@ HS2_KV_BF16 = 0
 HS2_KV_FP8_E4M3FN = 1
 HS2_SELECT_TOKEN = 0
 HS2_SELECT_BLOCK = 1
+# hs2_attn_desc.flags
+HS2_FLAG_DETERMINISTIC = 1 << 0
+HS2_FLAG_FORCE_LOGITS = 1 << 1
+HS2_FLAG_SCAN_VALU = 1 << 2
+HS2_FLAG_CHUNK_PER_TOKEN = 1 << 3
+HS2_FLAG_SPARSE_FUSED = 1 << 4
+HS2_FLAG_SPARSE_SPLIT = 1 << 5
+HS2_FLAGS_ALL = 0x3F
+SIZE_MAX = (1 << 64) - 1
 
 EXPORTED_SYMBOLS = ("hs2_validate", "hs2_workspace_size", "hs2_full_attn_select",
-                    "hs2_sparse_attn", "hs2_status_string", "hs2_set_deterministic",
-                    "hs2_timer_enable", "hs2_timer_collect", "hs2_kv_bridge",
+                    "hs2_sparse_attn", "hs2_status_string", "hs2_full_attn_select_timed",
+                    "hs2_sparse_attn_timed", "hs2_build_id", "hs2_kv_bridge",
                     "hs2_decode_workspace_size", "hs2_decode_step",
                     "hs2_sparse_attn_swa_workspace_size", "hs2_sparse_attn_swa")
 
@@ -62,6 +73,10 @@ class Hs2AttnDesc(ctypes.Structure):
         ("block_size", ctypes.c_int32),
         ("n_blocks", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+        ("split_len", ctypes.c_int32),
+        ("sparse_split_len", ctypes.c_int32),
+        ("cand_workgroups", ctypes.c_int32),
     ]
 
 
@@ -76,13 +91,20 @@ class Hs2BridgeDesc(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("batch", ctypes.c_int32),
         ("kv_capacity", ctypes.c_int64),
+        ("gemv_max_tokens", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
 def make_bridge_desc(n_tokens, hidden, n_layers, n_kv_heads, batch, kv_capacity, head_dim=128,
-                     kv_dtype=HS2_KV_FP8_E4M3FN) -> Hs2BridgeDesc:
+                     kv_dtype=HS2_KV_FP8_E4M3FN, gemv_max_tokens=0) -> Hs2BridgeDesc:
     return Hs2BridgeDesc(int(n_tokens), int(hidden), int(n_layers), int(n_kv_heads), int(head_dim),
-                         int(kv_dtype), int(batch), int(kv_capacity))
+                         int(kv_dtype), int(batch), int(kv_capacity), int(gemv_max_tokens), 0)
+
+
+class Hs2KernelEvents(ctypes.Structure):
+    """Mirror of hs2_kernel_events (include/hs2.h): two caller-owned hipEvent_t."""
+    _fields_ = [("begin", ctypes.c_void_p), ("end", ctypes.c_void_p)]
 
 
 class Hs2DecodePlan(ctypes.Structure):
@@ -108,11 +130,13 @@ class Hs2Error(RuntimeError):
 
 def make_desc(batch, q_len, n_q_heads, n_kv_heads, kv_capacity, max_ctx_len, head_dim=128,
               kv_dtype=HS2_KV_BF16, window=128, topk=1024, select_mode=HS2_SELECT_TOKEN,
-              block_size=64, n_blocks=18, sm_scale=None) -> Hs2AttnDesc:
+              block_size=64, n_blocks=18, sm_scale=None, flags=0, split_len=0, sparse_split_len=0,
+              cand_workgroups=0) -> Hs2AttnDesc:
     return Hs2AttnDesc(int(batch), int(q_len), int(n_q_heads), int(n_kv_heads), int(head_dim),
                        int(kv_dtype), int(kv_capacity), int(max_ctx_len), int(window), int(topk),
                        int(select_mode), int(block_size), int(n_blocks),
-                       float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(head_dim)))
+                       float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(head_dim)),
+                       int(flags), int(split_len), int(sparse_split_len), int(cand_workgroups))
 
 
 # --------------------------------------------------------------------------- loading
@@ -123,19 +147,21 @@ def library_path() -> str:
     return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhs2.so")
 
 
-def load_library():
-    """Load libhs2.so (built in-tree by build.py).  Raises if it is absent."""
+def load_library(path=None):
+    """Load libhs2.so (built in-tree by build.py), or the library at `path` (a host-only
+    build for sanitizer tests) if none is loaded yet.  Raises if it is absent."""
     global _LIB
     if _LIB is not None:
         return _LIB
-    path = library_path()
+    path = path or library_path()
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run __graft_entry__.build() "
                            "(hipcc --offload-arch=gfx950) first")
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     D = ctypes.POINTER(Hs2AttnDesc)
-    lib.hs2_validate.argtypes = [D]
+    E = ctypes.POINTER(Hs2KernelEvents)
+    lib.hs2_validate.argtypes = [D, ctypes.c_size_t]
     lib.hs2_validate.restype = ctypes.c_int
     lib.hs2_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
     lib.hs2_workspace_size.restype = ctypes.c_int
@@ -143,6 +169,12 @@ def load_library():
     lib.hs2_full_attn_select.restype = ctypes.c_int
     lib.hs2_sparse_attn.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.hs2_sparse_attn.restype = ctypes.c_int
+    lib.hs2_full_attn_select_timed.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, E]
+    lib.hs2_full_attn_select_timed.restype = ctypes.c_int
+    lib.hs2_sparse_attn_timed.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, E]
+    lib.hs2_sparse_attn_timed.restype = ctypes.c_int
+    lib.hs2_build_id.argtypes = []
+    lib.hs2_build_id.restype = ctypes.c_char_p
     lib.hs2_kv_bridge.argtypes = [ctypes.POINTER(Hs2BridgeDesc), P, P, P, P, P, P, P, P, P]
     lib.hs2_kv_bridge.restype = ctypes.c_int
     lib.hs2_decode_workspace_size.argtypes = [ctypes.POINTER(Hs2DecodePlan), ctypes.POINTER(ctypes.c_size_t)]
@@ -158,13 +190,6 @@ def load_library():
     lib.hs2_sparse_attn_swa.restype = ctypes.c_int
     lib.hs2_status_string.argtypes = [ctypes.c_int]
     lib.hs2_status_string.restype = ctypes.c_char_p
-    lib.hs2_set_deterministic.argtypes = [ctypes.c_int]
-    lib.hs2_set_deterministic.restype = ctypes.c_int
-    lib.hs2_timer_enable.argtypes = [ctypes.c_int]
-    lib.hs2_timer_enable.restype = ctypes.c_int
-    lib.hs2_timer_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32),
-                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
-    lib.hs2_timer_collect.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -187,8 +212,10 @@ def _stream(s):
 
 
 # --------------------------------------------------------------------------- C ABI
-def hs2_validate(desc: Hs2AttnDesc) -> int:
-    return load_library().hs2_validate(ctypes.byref(desc))
+def hs2_validate(desc: Hs2AttnDesc, workspace_bytes: int = SIZE_MAX) -> int:
+    """Checks the descriptor and that workspace_bytes covers its workspace (the default
+    SIZE_MAX checks the descriptor alone)."""
+    return load_library().hs2_validate(ctypes.byref(desc), int(workspace_bytes))
 
 
 def hs2_workspace_size(desc: Hs2AttnDesc):
@@ -212,6 +239,35 @@ def hs2_sparse_attn(desc, q, k, v, k_scale, v_scale, ctx_len, idx, out, workspac
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
         _ptr(ctx_len), _ptr(idx), _ptr(out), _ptr(workspace), int(workspace_bytes),
         _stream(stream))
+
+
+def _events(events):
+    """(begin, end) hipEvent_t handles (ints, or objects with a `cuda_event` handle such
+    as a recorded torch.cuda.Event) -> Hs2KernelEvents, or None."""
+    if events is None:
+        return None
+    b, e = (x if isinstance(x, int) else x.cuda_event for x in events)
+    return Hs2KernelEvents(b, e)
+
+
+def hs2_full_attn_select_timed(desc, q, k, v, k_scale, v_scale, ctx_len, out, idx, probs,
+                               workspace, workspace_bytes, stream=None, events=None) -> int:
+    """hs2_full_attn_select recording events = (begin, end) around its context scan."""
+    ev = _events(events)
+    return load_library().hs2_full_attn_select_timed(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
+        _ptr(ctx_len), _ptr(out), _ptr(idx), _ptr(probs), _ptr(workspace),
+        int(workspace_bytes), _stream(stream), ctypes.byref(ev) if ev is not None else None)
+
+
+def hs2_sparse_attn_timed(desc, q, k, v, k_scale, v_scale, ctx_len, idx, out, workspace,
+                          workspace_bytes, stream=None, events=None) -> int:
+    """hs2_sparse_attn recording events = (begin, end) around its gather kernel."""
+    ev = _events(events)
+    return load_library().hs2_sparse_attn_timed(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
+        _ptr(ctx_len), _ptr(idx), _ptr(out), _ptr(workspace), int(workspace_bytes),
+        _stream(stream), ctypes.byref(ev) if ev is not None else None)
 
 
 def _ptr_array(xs):
@@ -279,26 +335,6 @@ def hs2_status_string(status: int) -> str:
     return load_library().hs2_status_string(int(status)).decode()
 
 
-def hs2_set_deterministic(on: bool) -> int:
-    """Process-wide: fixed step shares in the context scan (bitwise reproducible)."""
-    return load_library().hs2_set_deterministic(1 if on else 0)
-
-
-HS2_TIMER_SCAN = 1
-HS2_TIMER_GATHER = 2
-
-
-def hs2_timer_enable(mask) -> int:
-    """mask: HS2_TIMER_* bits; True times both kernels, False none."""
-    if mask is True:
-        mask = HS2_TIMER_SCAN | HS2_TIMER_GATHER
-    return load_library().hs2_timer_enable(int(mask))
-
-
-def hs2_timer_collect():
-    """Returns (status, scan_ms, scan_count, gather_ms, gather_count)."""
-    a, c = ctypes.c_double(0), ctypes.c_int32(0)
-    b, d = ctypes.c_double(0), ctypes.c_int32(0)
-    st = load_library().hs2_timer_collect(ctypes.byref(a), ctypes.byref(c), ctypes.byref(b),
-                                          ctypes.byref(d))
-    return st, a.value, c.value, b.value, d.value
+def hs2_build_id() -> str:
+    """Hash of the sources libhs2.so was built from."""
+    return load_library().hs2_build_id().decode()

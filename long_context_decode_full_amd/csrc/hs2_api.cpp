@@ -1,13 +1,10 @@
 // C-ABI host layer: descriptor validation, workspace layout, launch sequences.
 // Contract of every entry point: include/hs2.h.
 #include <algorithm>
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
-#include <mutex>
-#include <vector>
 
 #include "hs2.h"
 #include "hs2_internal.h"
@@ -52,13 +49,6 @@ struct Layout {
          off_hist3 = 0, off_winners = 0, off_boundary = 0, total = 0;
 };
 
-int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  if (v == nullptr || *v == '\0') return dflt;
-  const int x = std::atoi(v);
-  return x >= 0 ? x : dflt;   // 0 is a value (switches); sizes are clamped where used
-}
-
 hs2_status validate_desc(const hs2_attn_desc* d) {
   if (d == nullptr) return HS2_ERR_INVALID_ARG;
   if (d->batch < 1 || d->q_len < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1)
@@ -68,6 +58,10 @@ hs2_status validate_desc(const hs2_attn_desc* d) {
   if (d->kv_capacity < 1 || d->max_ctx_len < d->q_len || d->max_ctx_len > d->kv_capacity)
     return HS2_ERR_INVALID_ARG;
   if (!(d->sm_scale > 0.0f) || !std::isfinite(d->sm_scale)) return HS2_ERR_INVALID_ARG;
+  // options: known flag bits, not both sparse routes, non-negative sizes
+  if ((d->flags & ~HS2_FLAGS_ALL) != 0u) return HS2_ERR_INVALID_ARG;
+  if ((d->flags & HS2_FLAG_SPARSE_FUSED) && (d->flags & HS2_FLAG_SPARSE_SPLIT)) return HS2_ERR_INVALID_ARG;
+  if (d->split_len < 0 || d->sparse_split_len < 0 || d->cand_workgroups < 0) return HS2_ERR_INVALID_ARG;
   if (d->select_mode == HS2_SELECT_TOKEN) {
     if (d->window < 0 || d->topk < 0 || (int64_t)d->window + d->topk < 1) return HS2_ERR_INVALID_ARG;
     if ((int64_t)d->window + d->topk > 4096) return HS2_ERR_UNSUPPORTED;
@@ -91,12 +85,14 @@ hs2_status validate_desc(const hs2_attn_desc* d) {
   return HS2_OK;
 }
 
+bool has_flag(const hs2_attn_desc* d, uint32_t f) { return (d->flags & f) != 0u; }
+
 // Token selection for a chunk of query tokens (q_len > 1, bf16 cache) runs the
 // matrix-core chunk kernel, which reads each KV row once for 32 tokens.
-// HS2_CHUNK_PER_TOKEN=1 runs the decode scan once per token instead (comparison).
+// HS2_FLAG_CHUNK_PER_TOKEN runs the decode scan once per token instead (comparison).
 bool chunk_path(const hs2_attn_desc* d) {
   return d->q_len > 1 && d->kv_dtype == HS2_KV_BF16 && d->select_mode == HS2_SELECT_TOKEN &&
-         d->n_q_heads / d->n_kv_heads <= kSlots && env_int("HS2_CHUNK_PER_TOKEN", 0) == 0;
+         d->n_q_heads / d->n_kv_heads <= kSlots && !has_flag(d, HS2_FLAG_CHUNK_PER_TOKEN);
 }
 // More than 8 query heads per KV head: the matrix-core scan with 16-head blocks, the
 // matrix-core gather and block-wise re-scoring; the logits path (probs) and the chunk
@@ -106,7 +102,7 @@ bool wide_group(const hs2_attn_desc* d) { return d->n_q_heads / d->n_kv_heads > 
 // block masses from the same kernel's per-block sums instead of per-position logits.
 bool chunk_block_path(const hs2_attn_desc* d) {
   return d->q_len > 1 && d->kv_dtype == HS2_KV_BF16 && d->select_mode == HS2_SELECT_BLOCK &&
-         d->block_size % 64 == 0 && env_int("HS2_CHUNK_PER_TOKEN", 0) == 0;
+         d->block_size % 64 == 0 && !has_flag(d, HS2_FLAG_CHUNK_PER_TOKEN);
 }
 
 Layout make_layout(const hs2_attn_desc* d) {
@@ -120,7 +116,7 @@ Layout make_layout(const hs2_attn_desc* d) {
   // Dense scan: enough splits to give ~2 workgroups per CU in one residency round.
   const int64_t rows = L.n_sel * d->max_ctx_len;
   int64_t split = ceil_div(ceil_div(rows, kScanTargetWorkgroups), 256) * 256;
-  split = env_int("HS2_SPLIT_LEN", (int)std::min<int64_t>(split, 1 << 30));
+  split = d->split_len > 0 ? (int64_t)d->split_len : std::min<int64_t>(split, 1 << 30);
   split = ceil_div(split, 256) * 256;
   if (split < 256) split = 256;
   while (ceil_div(d->max_ctx_len, split) > kMaxSplits) split *= 2;
@@ -139,10 +135,10 @@ Layout make_layout(const hs2_attn_desc* d) {
     rsplit = std::min<int64_t>(std::max<int64_t>(rsplit, 1024), kChunkMaxSplit);
     while (ceil_div(d->max_ctx_len, rsplit) > kMaxSplits && rsplit < kMaxRecordSplit) rsplit *= 2;
   } else {
-    const int64_t rec_target = env_int("HS2_SCAN_VALU", 0) ? kScanTargetWorkgroups : kMfmaTargetWorkgroups;
+    const int64_t rec_target = has_flag(d, HS2_FLAG_SCAN_VALU) ? kScanTargetWorkgroups : kMfmaTargetWorkgroups;
     rsplit = ceil_div(ceil_div(rows, rec_target), 256) * 256;
   }
-  rsplit = env_int("HS2_SPLIT_LEN", (int)std::min<int64_t>(rsplit, 1 << 30));
+  rsplit = d->split_len > 0 ? (int64_t)d->split_len : std::min<int64_t>(rsplit, 1 << 30);
   rsplit = ceil_div(rsplit, 256) * 256;
   if (rsplit < 256) rsplit = 256;
   if (rsplit > kMaxRecordSplit) rsplit = kMaxRecordSplit;
@@ -160,7 +156,7 @@ Layout make_layout(const hs2_attn_desc* d) {
   // launch more than ~320 workgroups (many rows: fewer, longer chains measured faster)
   int64_t sp = kSparseSplitLen;
   while (sp < 256 && L.n_sel * ceil_div(L.S, sp) > kSparseTargetWorkgroups) sp *= 2;
-  sp = env_int("HS2_SPARSE_SPLIT_LEN", (int)sp);
+  if (d->sparse_split_len > 0) sp = d->sparse_split_len;
   sp = std::max<int64_t>(ceil_div(sp, 32) * 32, 32);
   while (ceil_div(L.S, sp) > kMaxSplits) sp *= 2;
   L.split_len_sp = (int32_t)sp;
@@ -207,34 +203,11 @@ Layout make_layout(const hs2_attn_desc* d) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// ---------------------------------------------------------------- kernel timer
-struct TimerRec {
-  hipEvent_t a, b;
-  int kind;   // 0 scan, 1 gather
-};
-std::atomic<int> g_fixed_steps{0};   // hs2_set_deterministic
-
-std::mutex g_timer_mu;
-int g_timer_mask = 0;   // HS2_TIMER_* bits
-std::vector<TimerRec> g_timer;
-
-bool timer_begin(hipStream_t st, int kind, TimerRec* rec) {
-  std::lock_guard<std::mutex> lk(g_timer_mu);
-  if ((g_timer_mask & (1 << kind)) == 0) return false;
-  if (hipEventCreate(&rec->a) != hipSuccess) return false;
-  if (hipEventCreate(&rec->b) != hipSuccess) {
-    (void)hipEventDestroy(rec->a);
-    return false;
-  }
-  rec->kind = kind;
-  (void)hipEventRecord(rec->a, st);
-  return true;
-}
-
-void timer_end(hipStream_t st, TimerRec* rec) {
-  std::lock_guard<std::mutex> lk(g_timer_mu);
-  (void)hipEventRecord(rec->b, st);
-  g_timer.push_back(*rec);
+// HIP events around the dominant kernel of a call (hs2_*_timed), or none.
+void event_record(const hs2_kernel_events* ev, bool begin, hipStream_t st) {
+  if (ev == nullptr) return;
+  const hipEvent_t e = begin ? ev->begin : ev->end;
+  if (e != nullptr) (void)hipEventRecord(e, st);
 }
 
 }  // namespace
@@ -242,7 +215,16 @@ void timer_end(hipStream_t st, TimerRec* rec) {
 
 using namespace hs2;
 
-HS2_API hs2_status hs2_validate(const hs2_attn_desc* desc) { return validate_desc(desc); }
+HS2_API hs2_status hs2_validate(const hs2_attn_desc* desc, size_t workspace_bytes) {
+  const hs2_status s = validate_desc(desc);
+  if (s != HS2_OK) return s;
+  return workspace_bytes < make_layout(desc).total ? HS2_ERR_WORKSPACE : HS2_OK;
+}
+
+#ifndef HS2_BUILD_ID
+#define HS2_BUILD_ID "unknown"
+#endif
+HS2_API const char* hs2_build_id(void) { return HS2_BUILD_ID; }
 
 HS2_API hs2_status hs2_workspace_size(const hs2_attn_desc* desc, size_t* bytes) {
   const hs2_status s = validate_desc(desc);
@@ -284,7 +266,7 @@ static hs2_status check_common(const hs2_attn_desc* d, const void* q, const void
 
 // Which selection path hs2_full_attn_select takes, and whether it has one for this call.
 static bool use_record_path(const hs2_attn_desc* d, const Layout& L, const float* probs) {
-  return L.fast_ok && probs == nullptr && (wide_group(d) || env_int("HS2_FORCE_LOGITS", 0) == 0);
+  return L.fast_ok && probs == nullptr && (wide_group(d) || !has_flag(d, HS2_FLAG_FORCE_LOGITS));
 }
 static hs2_status full_path_supported(const hs2_attn_desc* d, const Layout& L, const float* probs) {
   const bool fast = use_record_path(d, L, probs);
@@ -314,7 +296,7 @@ static ScanArgs scan_args(const hs2_attn_desc* d, const Layout& L, const void* q
   a.G = L.G;
   a.S = L.S;
   a.scale_log2 = d->sm_scale * 1.44269504088896340736f;
-  a.fixed_steps = g_fixed_steps.load(std::memory_order_relaxed);
+  a.fixed_steps = has_flag(d, HS2_FLAG_DETERMINISTIC) ? 1 : 0;
   return a;
 }
 
@@ -322,7 +304,7 @@ static ScanArgs scan_args(const hs2_attn_desc* d, const Layout& L, const void* q
 // then the block selection on those sums.
 hs2_status chunk_block_select(const hs2_attn_desc* desc, const Layout& L, ScanArgs sa,
                               const int32_t* ctx_len, float* out, int32_t* idx, uint8_t* ws,
-                              hipStream_t stream) {
+                              hipStream_t stream, const hs2_kernel_events* ev) {
   sa.records = nullptr;
   sa.hist_part = nullptr;
   sa.hist_merged = nullptr;
@@ -331,10 +313,9 @@ hs2_status chunk_block_select(const hs2_attn_desc* desc, const Layout& L, ScanAr
   sa.window = 0;
   sa.n_split = L.rec_n_split;
   sa.split_len = L.rec_split_len;
-  TimerRec rec;
-  const bool timed = timer_begin(stream, 0, &rec);
+  event_record(ev, true, stream);
   const hipError_t e = launch_chunk_mfma(sa, desc->batch, stream);
-  if (timed) timer_end(stream, &rec);
+  event_record(ev, false, stream);
   if (e != hipSuccess) return HS2_ERR_LAUNCH;
 
   CombineArgs ca{};
@@ -373,11 +354,11 @@ hs2_status chunk_block_select(const hs2_attn_desc* desc, const Layout& L, ScanAr
   return HS2_OK;
 }
 
-HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q, const void* k,
-                                        const void* v, const float* k_scale, const float* v_scale,
-                                        const int32_t* ctx_len, float* out, int32_t* idx,
-                                        float* probs, void* workspace, size_t workspace_bytes,
-                                        hipStream_t stream) {
+HS2_API hs2_status hs2_full_attn_select_timed(const hs2_attn_desc* desc, const void* q, const void* k,
+                                              const void* v, const float* k_scale, const float* v_scale,
+                                              const int32_t* ctx_len, float* out, int32_t* idx,
+                                              float* probs, void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream, const hs2_kernel_events* ev) {
   Layout L;
   hs2_status s = check_common(desc, q, k, v, k_scale, v_scale, ctx_len, out, idx, workspace,
                               workspace_bytes, &L);
@@ -394,7 +375,7 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   s = full_path_supported(desc, L, probs);
   if (s != HS2_OK) return s;
   ScanArgs sa = scan_args(desc, L, q, k, v, k_scale, v_scale, ctx_len, ws);
-  if (cblock) return chunk_block_select(desc, L, sa, ctx_len, out, idx, ws, stream);
+  if (cblock) return chunk_block_select(desc, L, sa, ctx_len, out, idx, ws, stream, ev);
   sa.logits = reinterpret_cast<float*>(ws + L.off_logits);
   sa.records = reinterpret_cast<uint16_t*>(ws + L.off_records);
   sa.hist_part = reinterpret_cast<uint16_t*>(ws + L.off_hist_part);
@@ -403,14 +384,13 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   sa.n_split = fast ? L.rec_n_split : L.n_split;
   sa.split_len = fast ? L.rec_split_len : L.split_len;
 
-  TimerRec rec;
-  const bool timed = timer_begin(stream, 0, &rec);
-  // record path: matrix-core scan (HS2_SCAN_VALU=1 selects the VALU scan instead)
-  const bool mfma = fast && (wide_group(desc) || env_int("HS2_SCAN_VALU", 0) == 0);
+  event_record(ev, true, stream);
+  // record path: matrix-core scan (HS2_FLAG_SCAN_VALU selects the VALU scan instead)
+  const bool mfma = fast && (wide_group(desc) || !has_flag(desc, HS2_FLAG_SCAN_VALU));
   hipError_t e = (fast && chunk_path(desc)) ? launch_chunk_mfma(sa, desc->batch, stream)
                  : mfma                     ? launch_scan_mfma(sa, fp8, desc->batch, stream)
                                             : launch_scan_dense(sa, fp8, fast, desc->batch, stream);
-  if (timed) timer_end(stream, &rec);
+  event_record(ev, false, stream);
   if (e != hipSuccess) return HS2_ERR_LAUNCH;
 
   CombineArgs ca{};
@@ -454,7 +434,8 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
     fa.chunk_len = L.cand_chunk_len;
     // workgroups per row: all chunks of a row while rows are few (decode), fewer once
     // there are many rows, so short rows do not launch mostly empty workgroups
-    const int64_t per_row = ceil_div(env_int("HS2_CAND_WGS_TOTAL", kCandTargetWorkgroups), L.n_sel);
+    const int64_t per_row =
+        ceil_div(desc->cand_workgroups > 0 ? desc->cand_workgroups : kCandTargetWorkgroups, L.n_sel);
     fa.cand_wgs = (int32_t)std::max<int64_t>(1, std::min<int64_t>(L.n_cchunks, per_row));
     fa.n_sel = (int32_t)L.n_sel;
     fa.Lq = desc->q_len;
@@ -510,11 +491,20 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
   return HS2_OK;
 }
 
+HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q, const void* k,
+                                        const void* v, const float* k_scale, const float* v_scale,
+                                        const int32_t* ctx_len, float* out, int32_t* idx,
+                                        float* probs, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  return hs2_full_attn_select_timed(desc, q, k, v, k_scale, v_scale, ctx_len, out, idx, probs,
+                                    workspace, workspace_bytes, stream, nullptr);
+}
+
 // slot_rows: index entries are rows of a local cache (any row < cap), not positions.
 static hs2_status sparse_impl(const hs2_attn_desc* desc, const void* q, const void* k, const void* v,
                               const float* k_scale, const float* v_scale, const int32_t* ctx_len,
                               const int32_t* idx, float* out, void* workspace, size_t workspace_bytes,
-                              hipStream_t stream, int slot_rows) {
+                              hipStream_t stream, int slot_rows, const hs2_kernel_events* ev) {
   Layout L;
   hs2_status s = check_common(desc, q, k, v, k_scale, v_scale, ctx_len, out, idx, workspace,
                               workspace_bytes, &L);
@@ -532,20 +522,20 @@ static hs2_status sparse_impl(const hs2_attn_desc* desc, const void* q, const vo
   // token, KV head) gathers the whole index row and writes the output: 2.1x faster on
   // the 64-token chunks.  With fewer rows (decode) its 4-5 dependent steps per wave
   // are latency-bound, and the split VALU gather + combine is faster.
-  // HS2_SPARSE_FUSED=1 / 0 forces either path.
+  // HS2_FLAG_SPARSE_FUSED / HS2_FLAG_SPARSE_SPLIT force either path.
   // More than 8 heads per KV head with few rows: the matrix-core gather over splits of
   // one step per wave (256 entries with 8 waves, 128 with the 4-wave 32-head layout)
   // writing partials, then the combine.
   const int64_t rows = (int64_t)desc->batch * desc->q_len * desc->n_kv_heads;
-  const int fused_env = env_int("HS2_SPARSE_FUSED", -1);
-  const bool fused = fused_env >= 0 ? fused_env != 0 : rows >= kFusedSparseRows;
-  TimerRec rec;
-  const bool timed = timer_begin(stream, 1, &rec);
+  const bool fused = has_flag(desc, HS2_FLAG_SPARSE_FUSED)   ? true
+                    : has_flag(desc, HS2_FLAG_SPARSE_SPLIT) ? false
+                                                            : rows >= kFusedSparseRows;
+  event_record(ev, true, stream);
   if (fused) {
     sa.n_split = 1;
     sa.split_len = L.S;
     const hipError_t e = launch_gather_mfma(sa, out, fp8, desc->batch, stream);
-    if (timed) timer_end(stream, &rec);
+    event_record(ev, false, stream);
     return e == hipSuccess ? HS2_OK : HS2_ERR_LAUNCH;
   }
   hipError_t e;
@@ -556,7 +546,7 @@ static hs2_status sparse_impl(const hs2_attn_desc* desc, const void* q, const vo
   } else {
     e = launch_scan_sparse(sa, fp8, desc->batch, stream);
   }
-  if (timed) timer_end(stream, &rec);
+  event_record(ev, false, stream);
   if (e != hipSuccess) return HS2_ERR_LAUNCH;
 
   CombineArgs ca{};
@@ -571,50 +561,21 @@ static hs2_status sparse_impl(const hs2_attn_desc* desc, const void* q, const vo
   return HS2_OK;
 }
 
+HS2_API hs2_status hs2_sparse_attn_timed(const hs2_attn_desc* desc, const void* q, const void* k,
+                                         const void* v, const float* k_scale, const float* v_scale,
+                                         const int32_t* ctx_len, const int32_t* idx, float* out,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                         const hs2_kernel_events* ev) {
+  return sparse_impl(desc, q, k, v, k_scale, v_scale, ctx_len, idx, out, workspace, workspace_bytes,
+                     stream, 0, ev);
+}
+
 HS2_API hs2_status hs2_sparse_attn(const hs2_attn_desc* desc, const void* q, const void* k,
                                    const void* v, const float* k_scale, const float* v_scale,
                                    const int32_t* ctx_len, const int32_t* idx, float* out,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return sparse_impl(desc, q, k, v, k_scale, v_scale, ctx_len, idx, out, workspace, workspace_bytes,
-                     stream, 0);
-}
-
-HS2_API hs2_status hs2_set_deterministic(int on) {
-  g_fixed_steps.store(on ? 1 : 0, std::memory_order_relaxed);
-  return HS2_OK;
-}
-
-HS2_API hs2_status hs2_timer_enable(int mask) {
-  std::lock_guard<std::mutex> lk(g_timer_mu);
-  g_timer_mask = mask & (HS2_TIMER_SCAN | HS2_TIMER_GATHER);
-  return HS2_OK;
-}
-
-HS2_API hs2_status hs2_timer_collect(double* scan_ms, int32_t* scan_count, double* gather_ms,
-                                     int32_t* gather_count) {
-  if (!scan_ms || !scan_count || !gather_ms || !gather_count) return HS2_ERR_INVALID_ARG;
-  std::vector<TimerRec> recs;
-  {
-    std::lock_guard<std::mutex> lk(g_timer_mu);
-    recs.swap(g_timer);
-  }
-  double ms[2] = {0.0, 0.0};
-  int32_t cnt[2] = {0, 0};
-  hs2_status st = HS2_OK;
-  for (const TimerRec& r : recs) {
-    float t = 0.0f;
-    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
-      st = HS2_ERR_LAUNCH;
-    ms[r.kind] += t;
-    cnt[r.kind] += 1;
-    (void)hipEventDestroy(r.a);
-    (void)hipEventDestroy(r.b);
-  }
-  *scan_ms = ms[0];
-  *scan_count = cnt[0];
-  *gather_ms = ms[1];
-  *gather_count = cnt[1];
-  return st;
+                     stream, 0, nullptr);
 }
 
 // Every check of hs2_kv_bridge; fills the launch arguments.  *empty: nothing to launch.
@@ -626,6 +587,7 @@ static hs2_status bridge_prepare(const hs2_bridge_desc* d, const void* x, const 
   if (d->n_tokens < 0 || d->hidden < 1 || d->n_layers < 1 || d->n_kv_heads < 1 ||
       d->batch < 1 || d->kv_capacity < 1)
     return HS2_ERR_INVALID_ARG;
+  if (d->gemv_max_tokens < -1 || d->gemv_max_tokens > 1024 || d->reserved != 0) return HS2_ERR_INVALID_ARG;
   if (d->kv_dtype != HS2_KV_BF16 && d->kv_dtype != HS2_KV_FP8_E4M3FN) return HS2_ERR_INVALID_ARG;
   if (d->head_dim != kHeadDim || d->hidden % 64 != 0 || d->hidden > 65536 ||
       d->n_layers > kMaxBridgeLayers || d->n_kv_heads > 65535 ||
@@ -666,8 +628,8 @@ static hs2_status bridge_prepare(const hs2_bridge_desc* d, const void* x, const 
   a.n_layers = d->n_layers;
   a.m_tiles = (int32_t)m_tiles;
   a.n_tiles = (int32_t)n_tiles;
-  // few tokens (decode): the W-streaming path; HS2_BRIDGE_GEMV_MAX moves the switch (0..1024)
-  const int gemv_max = std::min(std::max(env_int("HS2_BRIDGE_GEMV_MAX", kBridgeGemvMaxTokens), 0), 1024);
+  // few tokens (decode): the W-streaming path; gemv_max_tokens moves the switch
+  const int gemv_max = d->gemv_max_tokens == 0 ? kBridgeGemvMaxTokens : d->gemv_max_tokens;   // -1: never
   a.gemv = d->n_tokens <= gemv_max ? 1 : 0;
   *out = a;
   *empty = d->n_tokens == 0;
@@ -775,7 +737,7 @@ HS2_API hs2_status hs2_decode_step(const hs2_decode_plan* plan, const void* x, c
   }
 
   // 1. positions of the new tokens; contexts grow by one
-  if (launch_advance(ctx_len, seq, pos, d->batch, d->kv_capacity, stream) != hipSuccess)
+  if (launch_advance(ctx_len, seq, pos, d->batch, d->max_ctx_len, stream) != hipSuccess)
     return HS2_ERR_LAUNCH;
   // 2. KV Bridging: the new tokens' K/V rows into every block's cache
   if (launch_bridge(ba, fp8, stream) != hipSuccess) return HS2_ERR_LAUNCH;
@@ -863,14 +825,14 @@ HS2_API hs2_status hs2_sparse_attn_swa(const hs2_attn_desc* desc, const void* q,
 
   const int64_t n_sel = (int64_t)desc->batch * desc->q_len * desc->n_kv_heads;
   // 1. the block-selected rows of the shared cache
-  s = sparse_impl(desc, q, k, v, k_scale, v_scale, ctx_len, idx, out, workspace, w.attn, stream, 0);
+  s = sparse_impl(desc, q, k, v, k_scale, v_scale, ctx_len, idx, out, workspace, w.attn, stream, 0, nullptr);
   if (s != HS2_OK) return s;
   // 2. the separate sliding-window branch over the layer's own local cache
   if (launch_swa_rows(ctx_len, idx_local, n_sel, desc->q_len, desc->n_kv_heads, local_window, local_rows,
                       desc->max_ctx_len, stream) != hipSuccess)
     return HS2_ERR_LAUNCH;
   s = sparse_impl(&w.local, q, k_local, v_local, kl_scale, vl_scale, ctx_len, idx_local, out_local,
-                  workspace, w.attn, stream, 1);
+                  workspace, w.attn, stream, 1, nullptr);
   if (s != HS2_OK) return s;
   // 3. the two branches' outputs summed
   if (launch_add(out, out_local, (int64_t)desc->batch * desc->q_len * desc->n_q_heads * kHeadDim,

@@ -421,12 +421,13 @@ namespace {
 // caches grow by the bridged K/V of each generated token).  A sequence whose cache is
 // full (or whose length is invalid) gets position -1, which the bridge skips, and
 // keeps its length.
-__global__ void advance_kernel(int32_t* ctx_len, int32_t* seq, int32_t* pos, int B, int64_t cap) {
+// limit: the largest length a sequence may reach (the attention calls' max_ctx_len)
+__global__ void advance_kernel(int32_t* ctx_len, int32_t* seq, int32_t* pos, int B, int64_t limit) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
   const int32_t c = ctx_len[b];
   seq[b] = b;
-  if (c >= 0 && (int64_t)c < cap) {
+  if (c >= 0 && (int64_t)c < limit) {
     pos[b] = c;
     ctx_len[b] = c + 1;
   } else {
@@ -436,9 +437,9 @@ __global__ void advance_kernel(int32_t* ctx_len, int32_t* seq, int32_t* pos, int
 
 }  // namespace
 
-hipError_t launch_advance(int32_t* ctx_len, int32_t* seq, int32_t* pos, int B, int64_t cap,
+hipError_t launch_advance(int32_t* ctx_len, int32_t* seq, int32_t* pos, int B, int64_t limit,
                           hipStream_t st) {
-  hipLaunchKernelGGL(advance_kernel, dim3((B + 255) / 256), dim3(256), 0, st, ctx_len, seq, pos, B, cap);
+  hipLaunchKernelGGL(advance_kernel, dim3((B + 255) / 256), dim3(256), 0, st, ctx_len, seq, pos, B, limit);
   return hipGetLastError();
 }
 

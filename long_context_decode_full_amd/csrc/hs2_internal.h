@@ -168,8 +168,9 @@ struct BridgeArgs {
 constexpr int kBridgeGemvMaxTokens = 16;   // default largest T of the decode-size path
 int bridge_tile_tokens(int n_tokens);   // tokens per workgroup tile launch_bridge uses
 hipError_t launch_bridge(const BridgeArgs& a, bool fp8, hipStream_t st);
-// decode step: pos[b] = ctx_len[b] and ctx_len[b] += 1 (pos -1 and no change when full)
-hipError_t launch_advance(int32_t* ctx_len, int32_t* seq, int32_t* pos, int B, int64_t cap,
+// decode step: pos[b] = ctx_len[b] and ctx_len[b] += 1 (pos -1 and no change once the
+// length has reached `limit`, the attention calls' max_ctx_len)
+hipError_t launch_advance(int32_t* ctx_len, int32_t* seq, int32_t* pos, int B, int64_t limit,
                           hipStream_t st);
 
 // first-generation sparse layer: local-cache rows of every selection row's window, and

@@ -13,9 +13,10 @@ import numpy as np
 import torch
 
 from . import (HS2_KV_BF16, HS2_KV_FP8_E4M3FN, HS2_OK, HS2_SELECT_BLOCK, HS2_SELECT_TOKEN,
-               Hs2Error, hs2_decode_step, hs2_decode_workspace_size, hs2_full_attn_select,
-               hs2_kv_bridge, hs2_sparse_attn, hs2_sparse_attn_swa, hs2_sparse_attn_swa_workspace_size,
-               hs2_workspace_size, make_bridge_desc, make_decode_plan, make_desc)
+               Hs2Error, hs2_decode_step, hs2_decode_workspace_size, hs2_full_attn_select_timed,
+               hs2_kv_bridge, hs2_sparse_attn_timed, hs2_sparse_attn_swa,
+               hs2_sparse_attn_swa_workspace_size, hs2_workspace_size, make_bridge_desc,
+               make_decode_plan, make_desc)
 
 
 def _dev(a: np.ndarray, device):
@@ -27,7 +28,7 @@ def _dev(a: np.ndarray, device):
 class HybridBlockDevice:
     def __init__(self, inp: dict, device="cuda", window=128, topk=1024, mode="token",
                  block_size=64, n_blocks=18, with_probs=False, max_ctx_len=None, local_rings=None,
-                 local_window=128):
+                 local_window=128, flags=0, split_len=0, sparse_split_len=0):
         self.device = torch.device(device)
         q = inp["q_full"]
         B, Lq, Hq, D = q.shape
@@ -42,7 +43,8 @@ class HybridBlockDevice:
                               kv_dtype=HS2_KV_FP8_E4M3FN if fp8 else HS2_KV_BF16,
                               window=window, topk=topk,
                               select_mode=HS2_SELECT_BLOCK if blockish else HS2_SELECT_TOKEN,
-                              block_size=block_size, n_blocks=n_blocks, sm_scale=inp["sm_scale"])
+                              block_size=block_size, n_blocks=n_blocks, sm_scale=inp["sm_scale"],
+                              flags=flags, split_len=split_len, sparse_split_len=sparse_split_len)
         self.S = block_size * n_blocks if blockish else window + topk
         self.gen1 = mode == "gen1"
         self.local_window = local_window
@@ -79,14 +81,15 @@ class HybridBlockDevice:
         self.ws_bytes = nbytes
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
 
-    def full(self, stream=None):
-        st = hs2_full_attn_select(self.desc, self.q_full, self.k, self.v, self.k_scale,
-                                  self.v_scale, self.ctx_len, self.out_full, self.idx, self.probs,
-                                  self.workspace, self.ws_bytes, stream)
+    def full(self, stream=None, events=None):
+        """events: optional (begin, end) HIP events recorded around the context scan."""
+        st = hs2_full_attn_select_timed(self.desc, self.q_full, self.k, self.v, self.k_scale,
+                                        self.v_scale, self.ctx_len, self.out_full, self.idx, self.probs,
+                                        self.workspace, self.ws_bytes, stream, events)
         if st != HS2_OK:
             raise Hs2Error(st, "hs2_full_attn_select")
 
-    def sparse(self, layer: int, idx=None, stream=None):
+    def sparse(self, layer: int, idx=None, stream=None, events=None):
         if self.gen1:
             lr = self.local[layer]
             st = hs2_sparse_attn_swa(self.desc, self.q_sparse[layer], self.k, self.v, self.k_scale,
@@ -97,16 +100,19 @@ class HybridBlockDevice:
             if st != HS2_OK:
                 raise Hs2Error(st, "hs2_sparse_attn_swa")
             return
-        st = hs2_sparse_attn(self.desc, self.q_sparse[layer], self.k, self.v, self.k_scale,
-                             self.v_scale, self.ctx_len, self.idx if idx is None else idx,
-                             self.out_sparse[layer], self.workspace, self.ws_bytes, stream)
+        st = hs2_sparse_attn_timed(self.desc, self.q_sparse[layer], self.k, self.v, self.k_scale,
+                                   self.v_scale, self.ctx_len, self.idx if idx is None else idx,
+                                   self.out_sparse[layer], self.workspace, self.ws_bytes, stream, events)
         if st != HS2_OK:
             raise Hs2Error(st, "hs2_sparse_attn")
 
-    def step(self, stream=None):
-        self.full(stream)
+    def step(self, stream=None, scan_events=None, gather_events=None):
+        """One Hybrid Block: the full layer, then every sparse layer.  scan_events /
+        gather_events: optional (begin, end) HIP events around the context scan / the
+        first sparse layer's gather."""
+        self.full(stream, scan_events)
         for layer in range(len(self.q_sparse)):
-            self.sparse(layer, stream=stream)
+            self.sparse(layer, stream=stream, events=gather_events if layer == 0 else None)
 
     def results(self) -> dict:
         torch.cuda.synchronize(self.device)
@@ -121,14 +127,15 @@ class BridgeDevice:
     the destinations, and one K and one V cache (plus scales for fp8) per target layer.
     The caches start filled with `fill` codes (and `scale_fill` scales)."""
 
-    def __init__(self, inp: dict, device="cuda", fill=None, scale_fill=float("nan")):
+    def __init__(self, inp: dict, device="cuda", fill=None, scale_fill=float("nan"), gemv_max_tokens=0):
         w = inp["workload"]
         self.device = torch.device(device)
         self.fp8 = w.kv_dtype == "fp8"
         self.L, self.Hkv, self.B, self.cap, self.D = w.n_layers, w.n_kv_heads, w.batch, w.capacity, w.head_dim
         self.T, self.Hd = w.n_tokens, w.hidden
         self.desc = make_bridge_desc(self.T, self.Hd, self.L, self.Hkv, self.B, self.cap, head_dim=self.D,
-                                     kv_dtype=HS2_KV_FP8_E4M3FN if self.fp8 else HS2_KV_BF16)
+                                     kv_dtype=HS2_KV_FP8_E4M3FN if self.fp8 else HS2_KV_BF16,
+                                     gemv_max_tokens=gemv_max_tokens)
         dv = self.device
         self.x = _dev(inp["x"], dv)
         self.w = _dev(inp["weight"], dv)
@@ -194,7 +201,7 @@ class DecodeLoopDevice:
     be captured in a HIP graph and replayed (hs2_decode_step enqueues only kernels)."""
 
     def __init__(self, inp: dict, n_blocks: int, w_bits: np.ndarray, device="cuda",
-                 max_ctx_len=None, window=128, topk=1024):
+                 max_ctx_len=None, window=128, topk=1024, flags=0):
         self.device = dv = torch.device(device)
         B, Lq, Hq, D = inp["q_full"].shape
         assert Lq == 1, "decode: one query token per sequence"
@@ -206,7 +213,7 @@ class DecodeLoopDevice:
         mctx = int(max_ctx_len if max_ctx_len is not None else cap)
         self.desc = make_desc(B, 1, Hq, Hkv, cap, mctx, head_dim=D,
                               kv_dtype=HS2_KV_FP8_E4M3FN if self.fp8 else HS2_KV_BF16,
-                              window=window, topk=topk, sm_scale=inp["sm_scale"])
+                              window=window, topk=topk, sm_scale=inp["sm_scale"], flags=flags)
         self.plan = make_decode_plan(self.desc, n_blocks, self.ns, self.hidden)
         k0, v0 = _dev(inp["k"], dv), _dev(inp["v"], dv)
         self.k = [k0.clone() for _ in range(n_blocks)]
@@ -250,6 +257,18 @@ class DecodeLoopDevice:
                              self.workspace, self.ws_bytes, stream)
         if st != HS2_OK:
             raise Hs2Error(st, "hs2_decode_step")
+
+    def full_layer(self, l: int, events=None, stream=None):
+        """Block l's full layer alone (hs2_full_attn_select on the block's cache, query
+        slot, outputs and the step's workspace), with optional (begin, end) events around
+        its context scan -- for timing the scan outside a captured step."""
+        ks = self.ks[l] if self.fp8 else None
+        vs = self.vs[l] if self.fp8 else None
+        st = hs2_full_attn_select_timed(self.desc, self.q_full[l], self.k[l], self.v[l], ks, vs,
+                                        self.ctx_len, self.out_full[l], self.idx[l], None,
+                                        self.workspace, self.ws_bytes, stream, events)
+        if st != HS2_OK:
+            raise Hs2Error(st, "hs2_full_attn_select")
 
     def capture(self):
         """One step captured into a HIP graph (torch.cuda.CUDAGraph); nothing runs until

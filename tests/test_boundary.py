@@ -18,6 +18,9 @@ HEADER = os.path.join(ROOT, "include", "hs2.h")
 
 @pytest.fixture(scope="module")
 def lib():
+    host = os.environ.get("HS2_HOST_LIB")   # the sanitizer run loads a host-only build
+    if host:
+        return hs2.load_library(host)
     if not os.path.exists(hs2.library_path()):
         import __graft_entry__
         __graft_entry__.build()
@@ -49,10 +52,23 @@ def test_status_strings(lib):
 
 
 def test_desc_struct_layout_matches_header():
-    # int32 x6, int64 x2, int32 x5, float -> 24 + 16 + 20 + 4 = 64 bytes with alignment
-    assert ctypes.sizeof(hs2.Hs2AttnDesc) == 64
+    # int32 x6, int64 x2, int32 x5, float, then the options: uint32 flags, int32 x3
+    # -> 24 + 16 + 20 + 4 + 16 = 80 bytes
+    assert ctypes.sizeof(hs2.Hs2AttnDesc) == 80
     assert hs2.Hs2AttnDesc.kv_capacity.offset == 24
     assert hs2.Hs2AttnDesc.sm_scale.offset == 60
+    assert hs2.Hs2AttnDesc.flags.offset == 64
+    assert hs2.Hs2AttnDesc.cand_workgroups.offset == 76
+
+
+def test_build_id_names_the_current_sources(lib):
+    """The library embeds a hash of the sources it was built from; a stale libhs2.so
+    (sources edited after the build) shows here instead of running old kernels."""
+    from long_context_decode_full_amd import build
+    if os.environ.get("HS2_HOST_LIB"):
+        assert hs2.hs2_build_id() == "host-sanitizer-build"
+        return
+    assert hs2.hs2_build_id() == build.source_hash()
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -80,13 +96,36 @@ def test_desc_struct_layout_matches_header():
     (dict(sm_scale=float("nan")), hs2.HS2_ERR_INVALID_ARG),
     (dict(kv_capacity=1 << 31, max_ctx_len=1 << 20), hs2.HS2_ERR_UNSUPPORTED),
     (dict(batch=1100, q_len=64, kv_capacity=4096, max_ctx_len=4096), hs2.HS2_ERR_UNSUPPORTED),
+    # options
+    (dict(flags=hs2.HS2_FLAGS_ALL & ~(hs2.HS2_FLAG_SPARSE_FUSED)), hs2.HS2_OK),
+    (dict(flags=0x40), hs2.HS2_ERR_INVALID_ARG),                  # unknown flag bit
+    (dict(flags=1 << 31), hs2.HS2_ERR_INVALID_ARG),
+    (dict(flags=hs2.HS2_FLAG_SPARSE_FUSED | hs2.HS2_FLAG_SPARSE_SPLIT), hs2.HS2_ERR_INVALID_ARG),
+    (dict(split_len=-1), hs2.HS2_ERR_INVALID_ARG),
+    (dict(sparse_split_len=-32), hs2.HS2_ERR_INVALID_ARG),
+    (dict(cand_workgroups=-1), hs2.HS2_ERR_INVALID_ARG),
+    (dict(split_len=1, sparse_split_len=1, cand_workgroups=1), hs2.HS2_OK),   # clamped upwards
 ])
 def test_validate(lib, kw, status):
     assert hs2.hs2_validate(_desc(**kw)) == status
 
 
+def test_validate_checks_the_workspace_size(lib):
+    """hs2_validate(desc, bytes) is the descriptor check plus the workspace check that
+    every call makes."""
+    for kw in (dict(), dict(q_len=64, max_ctx_len=300000, kv_capacity=300000),
+               dict(select_mode=hs2.HS2_SELECT_BLOCK, max_ctx_len=5000, kv_capacity=5000)):
+        d = _desc(**kw)
+        st, need = hs2.hs2_workspace_size(d)
+        assert st == hs2.HS2_OK
+        assert hs2.hs2_validate(d, need) == hs2.HS2_OK
+        assert hs2.hs2_validate(d, need - 1) == hs2.HS2_ERR_WORKSPACE
+        assert _full(d, workspace_bytes=need - 1) == hs2.HS2_ERR_WORKSPACE
+    assert hs2.hs2_validate(_desc(head_dim=64), 0) == hs2.HS2_ERR_UNSUPPORTED   # descriptor first
+
+
 def test_validate_null_desc(lib):
-    assert lib.hs2_validate(None) == hs2.HS2_ERR_INVALID_ARG
+    assert lib.hs2_validate(None, 0) == hs2.HS2_ERR_INVALID_ARG
     n = ctypes.c_size_t(0)
     assert lib.hs2_workspace_size(None, ctypes.byref(n)) == hs2.HS2_ERR_INVALID_ARG
     assert lib.hs2_workspace_size(ctypes.byref(_desc()), None) == hs2.HS2_ERR_INVALID_ARG
@@ -112,13 +151,28 @@ def test_selection_row_limit(lib):
                                   max_ctx_len=64, kv_capacity=64)) == hs2.HS2_OK
 
 
-@pytest.mark.parametrize("var", ["HS2_SPLIT_LEN", "HS2_SPARSE_SPLIT_LEN", "HS2_CAND_WGS_TOTAL"])
-def test_zero_size_overrides_are_clamped(lib, monkeypatch, var):
-    """Size overrides set to 0 fall back to their minimum instead of dividing by zero."""
-    st0, n0 = hs2.hs2_workspace_size(_desc(kv_capacity=1 << 16, max_ctx_len=50000))
-    monkeypatch.setenv(var, "0")
-    st, nbytes = hs2.hs2_workspace_size(_desc(kv_capacity=1 << 16, max_ctx_len=50000))
-    assert st0 == hs2.HS2_OK and st == hs2.HS2_OK and nbytes > 0
+@pytest.mark.parametrize("field", ["split_len", "sparse_split_len", "cand_workgroups"])
+def test_size_options_follow_the_descriptor(lib, field, monkeypatch):
+    """Split sizes come from the descriptor only: 0 means automatic, tiny values are
+    clamped to the kernels' minimum, and the environment is never read (a variable set
+    between hs2_workspace_size and a call cannot change the layout)."""
+    base = _desc(kv_capacity=1 << 16, max_ctx_len=50000)
+    st0, n0 = hs2.hs2_workspace_size(base)
+    for v in (0, 1, 7, 256, 4096):
+        st, nbytes = hs2.hs2_workspace_size(_desc(kv_capacity=1 << 16, max_ctx_len=50000, **{field: v}))
+        assert st == hs2.HS2_OK and nbytes > 0
+        if v == 0:
+            assert nbytes == n0
+    for var in ("HS2_SPLIT_LEN", "HS2_SPARSE_SPLIT_LEN", "HS2_CAND_WGS_TOTAL", "HS2_SCAN_VALU",
+                "HS2_FORCE_LOGITS", "HS2_CHUNK_PER_TOKEN", "HS2_SPARSE_FUSED"):
+        monkeypatch.setenv(var, "1")
+    assert hs2.hs2_workspace_size(base) == (st0, n0)
+
+
+def test_library_reads_no_environment():
+    """No getenv in the host layer: every option travels in the descriptor."""
+    src = open(os.path.join(ROOT, "long_context_decode_full_amd", "csrc", "hs2_api.cpp")).read()
+    assert "getenv" not in src
 
 
 FAKE = 0x7F0000000000   # 16-byte aligned fake device address, never dereferenced
@@ -171,11 +225,17 @@ def test_invalid_desc_checked_before_pointers(lib):
     assert _full(_desc(head_dim=96), q=None) == hs2.HS2_ERR_UNSUPPORTED
 
 
-def test_timer_collect_empty(lib):
-    assert hs2.hs2_timer_enable(False) == 0
-    st, a, c, b, d = hs2.hs2_timer_collect()
-    assert st == 0 and c == 0 and d == 0 and a == 0.0 and b == 0.0
-    assert lib.hs2_timer_collect(None, None, None, None) == hs2.HS2_ERR_INVALID_ARG
+def test_timed_calls_check_like_the_plain_ones(lib):
+    """The _timed variants take caller-owned events; argument checks come first and
+    return before any event is recorded (fake handles here are never touched)."""
+    ev = (0x1234, 0x5678)
+    d = _desc()
+    assert hs2.hs2_full_attn_select_timed(d, *([FAKE] * 3), None, None, FAKE, FAKE, FAKE, None, FAKE, 16,
+                                          stream=0, events=ev) == hs2.HS2_ERR_WORKSPACE
+    assert hs2.hs2_sparse_attn_timed(d, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, 1 << 40,
+                                     stream=0, events=ev) == hs2.HS2_ERR_INVALID_ARG
+    assert hs2.hs2_full_attn_select_timed(_desc(head_dim=64), *([FAKE] * 3), None, None, FAKE, FAKE,
+                                          FAKE, None, FAKE, 1 << 40, stream=0, events=ev) == hs2.HS2_ERR_UNSUPPORTED
 
 
 def test_product_path_has_no_fallback():
@@ -190,9 +250,10 @@ def test_product_path_has_no_fallback():
 
 # ----------------------------------------------------------------------------- KV Bridging
 def test_bridge_desc_struct_layout_matches_header():
-    # int32 x7, then int64 aligned to 8 -> 28 + 4 pad + 8 = 40 bytes
-    assert ctypes.sizeof(hs2.Hs2BridgeDesc) == 40
+    # int32 x7, then int64 aligned to 8 -> 28 + 4 pad + 8 = 40 bytes, then two int32
+    assert ctypes.sizeof(hs2.Hs2BridgeDesc) == 48
     assert hs2.Hs2BridgeDesc.kv_capacity.offset == 32
+    assert hs2.Hs2BridgeDesc.gemv_max_tokens.offset == 40
 
 
 _GOOD = 0x10000000          # fake 4 KiB-aligned device addresses, never dereferenced
@@ -223,6 +284,9 @@ def _bridge(lib_unused=None, desc=None, fp8=True, n_layers=2, **over):
     ("batch", 0, hs2.HS2_ERR_INVALID_ARG),
     ("kv_capacity", 0, hs2.HS2_ERR_INVALID_ARG),
     ("kv_capacity", 1 << 31, hs2.HS2_ERR_UNSUPPORTED),
+    ("gemv_max_tokens", -2, hs2.HS2_ERR_INVALID_ARG),
+    ("gemv_max_tokens", 1025, hs2.HS2_ERR_INVALID_ARG),
+    ("reserved", 1, hs2.HS2_ERR_INVALID_ARG),
 ])
 def test_bridge_desc_checks(lib, field, value, status):
     d = hs2.make_bridge_desc(300, 512, 2, 2, 4, 4096)
@@ -271,10 +335,10 @@ def test_bridge_bf16_needs_no_scales_and_zero_tokens_enqueue_nothing(lib):
 
 # ----------------------------------------------------------------------------- decode step
 def test_decode_plan_struct_layout_matches_header():
-    # hs2_attn_desc (64 bytes) then four int32
-    assert ctypes.sizeof(hs2.Hs2DecodePlan) == 80
-    assert hs2.Hs2DecodePlan.n_blocks.offset == 64
-    assert hs2.Hs2DecodePlan.hidden.offset == 72
+    # hs2_attn_desc (80 bytes) then four int32
+    assert ctypes.sizeof(hs2.Hs2DecodePlan) == 96
+    assert hs2.Hs2DecodePlan.n_blocks.offset == 80
+    assert hs2.Hs2DecodePlan.hidden.offset == 88
 
 
 def _plan(**kw):

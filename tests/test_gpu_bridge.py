@@ -119,8 +119,8 @@ def test_bridge_small_whole_caches(name):
 
 
 # The decode-size path (one workgroup per 128 features x 16 tokens, W read straight
-# into registers) takes calls of at most 16 tokens; HS2_BRIDGE_GEMV_MAX moves the
-# switch, so each path is also run on the other's sizes.
+# into registers) takes calls of at most 16 tokens; the descriptor's gemv_max_tokens
+# moves the switch, so each path is also run on the other's sizes.
 GEMV = {
     # hidden 64: one 32-dim step per half (remainder loop only)
     "gemv_hidden_64_bf16": (wl.BridgeWorkload("5 tokens, hidden 64", 5, 64, 2, 1, batch=2, capacity=16,
@@ -133,23 +133,21 @@ GEMV = {
     # three token blocks, the last one ragged
     "gemv_forced_40_tokens_fp8": (wl.BridgeWorkload("40 tokens on the decode-size path", 40, 1024, 2, 4,
                                                     batch=3, capacity=128, placement="ragged", bad_rows=3,
-                                                    seed=2113), "64"),
+                                                    seed=2113), 64),
     "gemv_forced_40_tokens_bf16": (wl.BridgeWorkload("40 tokens on the decode-size path, bf16", 40, 512, 2, 2,
                                                      batch=3, capacity=128, kv_dtype="bf16",
-                                                     placement="ragged", bad_rows=3, seed=2114), "64"),
+                                                     placement="ragged", bad_rows=3, seed=2114), 64),
     # the tile path on a decode-size call
     "tile_forced_16_tokens_fp8": (wl.BridgeWorkload("16 tokens on the tile path", 16, 2048, 2, 4, batch=16,
-                                                    capacity=40, placement="decode", seed=2115), "0"),
+                                                    capacity=40, placement="decode", seed=2115), -1),
 }
 
 
 @pytest.mark.parametrize("name", list(GEMV))
-def test_bridge_decode_size_paths(name, monkeypatch):
+def test_bridge_decode_size_paths(name):
     w, switch = GEMV[name]
-    if switch is not None:
-        monkeypatch.setenv("HS2_BRIDGE_GEMV_MAX", switch)
     _announce(name, w)
-    inp, dev = _run(w)
+    inp, dev = _run(w, gemv_max_tokens=switch or 0)
     assert _full_compare(inp, dev) == int(_valid(inp).sum())
 
 

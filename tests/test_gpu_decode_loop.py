@@ -9,27 +9,21 @@ then runs every block's full layer and sparse layers (HySparse2 article, section
 - Every appended K/V row matches the KV Bridging oracle (interval rule of
   tests/bridge_check.py); the last step's outputs and index sets match the
   Hybrid-Block oracle on the caches as they then are (rules of tests/parity.py).
-- A sequence whose cache is full keeps its length and its rows.
+- A sequence whose cache is full keeps its length and its rows; so does one that has
+  reached the plan's max_ctx_len below the capacity (the rows past it stay untouched).
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from long_context_decode_full_amd import hs2_set_deterministic
+from long_context_decode_full_amd import HS2_FLAG_DETERMINISTIC
 from long_context_decode_full_amd import workloads as wl
 from long_context_decode_full_amd.runner import DecodeLoopDevice
 from tests import bridge_check as bc
 from tests.parity import assert_out_close, check_idx_row
 
 pytestmark = pytest.mark.gpu
-
-
-@pytest.fixture
-def deterministic():
-    hs2_set_deterministic(True)
-    yield
-    hs2_set_deterministic(False)
 
 
 def _appended_rows(dev, ctx_before, ctx_after):
@@ -101,21 +95,24 @@ CASES = {
     "fp8": dict(kv="fp8", ctx=[2500, 4100], cap=4110, steps=3),
     # sequence 1 starts with a full cache: it keeps its length, appends nothing
     "full_cache": dict(kv="bf16", ctx=[1200, 1500], cap=1500, steps=3),
+    # the plan bounds lengths at 1502 < capacity 1600: sequence 1 grows twice, then stays
+    "length_bound": dict(kv="bf16", ctx=[1200, 1500], cap=1600, steps=4, max_ctx=1502),
 }
 
 
 @pytest.mark.parametrize("name", list(CASES))
-def test_decode_loop_graph_eager_and_oracle(name, deterministic):
+def test_decode_loop_graph_eager_and_oracle(name):
     c = CASES[name]
     hq, hkv = c.get("hq", 16), c.get("hkv", 2)
+    limit = c.get("max_ctx", c["cap"])
     w = wl.Workload(f"decode loop {name}", 2, 1, hq, hkv, ctx_lens=c["ctx"], capacity=c["cap"],
-                    kv_dtype=c["kv"], n_needles=8, seed=3001)
+                    kv_dtype=c["kv"], n_needles=8, poison_tail=limit < c["cap"], seed=3001)
     print(f"\n[decode loop] {name}: B=2 Hq{hq}/Hkv{hkv} ctx={c['ctx']} cap={c['cap']} {c['kv']} "
           f"blocks=2 hidden=256 steps={c['steps']}", flush=True)
     inp = wl.make_inputs(w)
     dec = wl.make_decode_steps(w, n_blocks=2, steps=c["steps"], hidden=256, seed=3002)
-    eager = DecodeLoopDevice(inp, 2, dec["w_bits"])
-    graph = DecodeLoopDevice(inp, 2, dec["w_bits"])
+    eager = DecodeLoopDevice(inp, 2, dec["w_bits"], max_ctx_len=limit, flags=HS2_FLAG_DETERMINISTIC)
+    graph = DecodeLoopDevice(inp, 2, dec["w_bits"], max_ctx_len=limit, flags=HS2_FLAG_DETERMINISTIC)
     g = None
     ctx = inp["ctx_len"].copy()
     for t in range(c["steps"]):
@@ -128,7 +125,7 @@ def test_decode_loop_graph_eager_and_oracle(name, deterministic):
         torch.cuda.synchronize()
         se, sg = eager.state(), graph.state()
         _same_state(se, sg, eager, graph)
-        expect = np.where(ctx < c["cap"], ctx + 1, ctx)
+        expect = np.where(ctx < limit, ctx + 1, ctx)
         assert np.array_equal(sg["ctx_len"], expect), (sg["ctx_len"], expect)
         bs, rows = _appended_rows(graph, ctx, sg["ctx_len"])
         _check_bridge_rows(graph, dec, t, bs, rows)
@@ -140,3 +137,36 @@ def test_decode_loop_graph_eager_and_oracle(name, deterministic):
         # the full sequence's rows are the initial ones
         k0 = inp["k"][1]
         assert np.array_equal(graph.k[0][1].cpu().numpy().view(np.uint16), k0)
+    if name == "length_bound":
+        assert int(ctx[1]) == limit
+        # rows at and past the bound are never written (they still hold the NaN poison)
+        for l in range(2):
+            for cache in (graph.k[l], graph.v[l]):
+                tail = cache[1, :, limit:].cpu().numpy().view(np.uint16)
+                assert np.all(tail == inp["k"][1, :, limit:]) and np.all(tail == wl.BF16_NAN)
+
+
+def test_decode_step_at_the_million_token_context():
+    """One hs2_decode_step at full size: a million-token context (32 query heads on 4 KV
+    heads, bf16) grows by one token through KV Bridging (hidden 2048), then the block's
+    full layer selects over 1,048,577 positions and its 3 sparse layers reuse the
+    selection; the appended rows against the bridge oracle and every output and index
+    set against the Hybrid-Block oracle, as in the small cases."""
+    import dataclasses
+    base = wl.standard_workloads()["million"]
+    w = dataclasses.replace(base, capacity=base.ctx_lens[0] + 8)
+    print(f"\n[decode loop] million: B=1 Hq32/Hkv4 ctx={w.ctx_lens} cap={w.capacity} bf16 blocks=1 "
+          f"hidden=2048 steps=1", flush=True)
+    inp = wl.make_inputs(w, threads=16)
+    dec = wl.make_decode_steps(w, n_blocks=1, steps=1, hidden=2048, seed=3010)
+    dev = DecodeLoopDevice(inp, 1, dec["w_bits"])
+    del inp
+    ctx = dev.ctx_len.cpu().numpy().copy()
+    dev.set_inputs(dec["x"][0], dec["q_full"][0], dec["q_sparse"][0])
+    dev.step()
+    st = dev.state()
+    assert np.array_equal(st["ctx_len"], ctx + 1)
+    bs, rows = _appended_rows(dev, ctx, st["ctx_len"])
+    _check_bridge_rows(dev, dec, 0, bs, rows)
+    _check_attention(dev, dec, 0)
+    print("[decode loop]   million step: bridge rows and attention match the oracles", flush=True)

@@ -9,8 +9,11 @@ import pytest
 import torch
 
 import oracle
+from long_context_decode_full_amd import (HS2_FLAG_CHUNK_PER_TOKEN, HS2_FLAG_DETERMINISTIC,
+                                          HS2_FLAG_SCAN_VALU, HS2_FLAG_SPARSE_FUSED,
+                                          HS2_FLAG_SPARSE_SPLIT)
 from long_context_decode_full_amd import workloads as wl
-from parity import assert_out_close, check_block_row, check_idx_row
+from parity import assert_out_close, check_block_row, check_idx_row, out_row_errors
 
 pytestmark = pytest.mark.gpu
 
@@ -27,22 +30,44 @@ def _announce(tag, w):
           flush=True)
 
 
+def oracle_tokens(inp, tokens, **kw):
+    """oracle.hybrid_block_token for every (b, j) of `tokens`, converting each sequence's
+    K/V rows to float64 once for all of its tokens (the oracle's kv_cache argument)."""
+    ref = {}
+    by_seq = {}
+    for b, j in tokens:
+        by_seq.setdefault(b, []).append(j)
+    Hkv = inp["k"].shape[1]
+    Lq = inp["q_full"].shape[1]
+    for b, js in by_seq.items():
+        m = max(0, min(int(inp["ctx_len"][b]), inp["k"].shape[2]))
+        cache = {g: oracle.kv_rows(inp, b, g, m) for g in range(Hkv)} if m > 0 and Lq > 1 else None
+        for j in js:
+            ref[(b, j)] = oracle.hybrid_block_token(inp, b, j, kv_cache=cache, **kw)
+        del cache
+    return ref
+
+
 def run_and_compare(w, tag, tokens=None, window=128, topk=1024, mode="token", block_size=64,
-                    n_blocks=18, with_probs=False, max_ctx_len=None, max_swaps=None):
+                    n_blocks=18, with_probs=False, max_ctx_len=None, max_swaps=None, flags=0,
+                    inp=None, groups=None):
     """with_probs=False runs the default record-based selection; with_probs=True makes the
-    library keep every logit and also returns all group-summed probabilities."""
+    library keep every logit and also returns all group-summed probabilities.  `flags`
+    are the descriptor's HS2_FLAG_* options; `inp` replaces the generated inputs;
+    `groups` restricts the oracle to some KV heads."""
     from long_context_decode_full_amd.runner import HybridBlockDevice
-    _announce(tag + (" [logits path]" if with_probs else " [record path]"), w)
-    inp = wl.make_inputs(w)
+    _announce(tag + (" [logits path]" if with_probs else " [record path]") + (f" flags={flags:#x}" if flags else ""), w)
+    if inp is None:
+        inp = wl.make_inputs(w)
     dev = HybridBlockDevice(inp, window=window, topk=topk, mode=mode, block_size=block_size,
-                            n_blocks=n_blocks, with_probs=with_probs, max_ctx_len=max_ctx_len)
+                            n_blocks=n_blocks, with_probs=with_probs, max_ctx_len=max_ctx_len, flags=flags)
     dev.step()
     got = dev.results()
     B, Lq = inp["q_full"].shape[:2]
     if tokens is None:
         tokens = [(b, j) for b in range(B) for j in range(Lq)]
-    ref = oracle.hybrid_block(inp, tokens=tokens, window=window, topk=topk, mode=mode,
-                              block=block_size, n_blocks=n_blocks)
+    ref = oracle_tokens(inp, tokens, window=window, topk=topk, mode=mode, block=block_size,
+                        n_blocks=n_blocks)
     # sparse layers again, fed the oracle's index sets (independent of the GPU selection)
     ref_idx = np.full(got["idx"].shape, -1, dtype=np.int32)
     for (b, j), r in ref.items():
@@ -113,29 +138,26 @@ def test_fp8_256k_decode(with_probs):
 
 
 @pytest.mark.parametrize("wname", ["tiny", "fp8_256k"])
-def test_record_path_on_valu_scan(monkeypatch, wname):
-    """HS2_SCAN_VALU=1: the record path's scan on the VALU kernel (dot2 + DPP butterfly)
+def test_record_path_on_valu_scan(wname):
+    """HS2_FLAG_SCAN_VALU: the record path's scan on the VALU kernel (dot2 + DPP butterfly)
     instead of the matrix cores; same parity bar."""
-    monkeypatch.setenv("HS2_SCAN_VALU", "1")
     w = wl.standard_workloads()[wname]
-    run_and_compare(w, f"{wname}-valu-scan")
+    run_and_compare(w, f"{wname}-valu-scan", flags=HS2_FLAG_SCAN_VALU)
 
 
 @pytest.mark.parametrize("wname", ["tiny", "fp8_256k", "batched"])
-def test_sparse_fused_gather_on_decode(monkeypatch, wname):
-    """HS2_SPARSE_FUSED=1: decode shapes (few rows, normally the split gather) on the
+def test_sparse_fused_gather_on_decode(wname):
+    """HS2_FLAG_SPARSE_FUSED: decode shapes (few rows, normally the split gather) on the
     one-workgroup-per-row matrix-core gather; same parity bar."""
-    monkeypatch.setenv("HS2_SPARSE_FUSED", "1")
     w = wl.standard_workloads()[wname]
-    run_and_compare(w, f"{wname}-sparse-fused")
+    run_and_compare(w, f"{wname}-sparse-fused", flags=HS2_FLAG_SPARSE_FUSED)
 
 
-def test_chunk_sparse_split_path(monkeypatch):
-    """HS2_SPARSE_FUSED=0: the chunk configuration's sparse layers on the split
+def test_chunk_sparse_split_path():
+    """HS2_FLAG_SPARSE_SPLIT: the chunk configuration's sparse layers on the split
     gather + combine; sampled tokens."""
-    monkeypatch.setenv("HS2_SPARSE_FUSED", "0")
     w = wl.standard_workloads()["chunk"]
-    run_and_compare(w, "chunk-sparse-split", tokens=[(3, 0), (9, 63), (15, 17)])
+    run_and_compare(w, "chunk-sparse-split", tokens=[(3, 0), (9, 63), (15, 17)], flags=HS2_FLAG_SPARSE_SPLIT)
 
 
 def test_million_token_decode():
@@ -159,14 +181,50 @@ def test_mqa_million_token_decode():
     run_and_compare(w, "mqa-million")
 
 
-@pytest.mark.parametrize("mode", ["token", "block"])
-def test_chunk_full_config(mode):
-    """The ragged 64-token chunk at full size (16 sequences, contexts 8K-512K) in the
-    benchmark's launch configuration; tokens sampled from the longest and a short
-    sequence and from both halves of the chunk."""
+@pytest.fixture(scope="module")
+def chunk_full_inputs():
+    """The ragged 64-token chunk configuration's inputs, built once for the module."""
     w = wl.standard_workloads()["chunk"]
-    run_and_compare(w, f"chunk-full-{mode}", mode=mode,
-                    tokens=[(6, 0), (6, 63), (0, 31), (12, 32), (13, 5)])
+    return w, wl.make_inputs(w, threads=16)
+
+
+@pytest.mark.parametrize("mode", ["token", "block"])
+@pytest.mark.parametrize("part", ["longest", "shortest_and_edges"])
+def test_chunk_full_config(chunk_full_inputs, mode, part):
+    """The ragged 64-token chunk at full size (16 sequences, contexts 8K-512K) in the
+    benchmark's launch configuration.  "longest": all 64 tokens of the longest sequence
+    (both 32-token workgroups of every split, all 256 selection rows).  "shortest_and_
+    edges": all 64 tokens of the three shortest sequences, plus the first and last
+    token of every other sequence."""
+    w, inp = chunk_full_inputs
+    order = np.argsort(inp["ctx_len"])
+    if part == "longest":
+        tokens = [(int(order[-1]), j) for j in range(64)]
+    else:
+        short = [int(b) for b in order[:3]]
+        tokens = [(b, j) for b in short for j in range(64)]
+        tokens += [(b, j) for b in range(w.batch) if b not in short for j in (0, 63)]
+    run_and_compare(w, f"chunk-full-{mode}-{part}", mode=mode, tokens=tokens, inp=inp)
+
+
+@pytest.mark.parametrize("ctx", [64, 65, 40, 100])
+def test_chunk_context_within_the_chunk(ctx):
+    """A 64-token chunk whose context is (nearly) the chunk itself: with ctx_len = 64
+    every token of both 32-token workgroups sees only part of its own chunk; 65 adds
+    one earlier position; 40 < 64 leaves the first 24 tokens with nothing visible
+    (out = 0, idx = -1).  Every token compared; a second sequence of 3,000 keeps the
+    launch ragged."""
+    w = wl.Workload(f"chunk ctx{ctx}", 2, 64, 32, 4, ctx_lens=[max(ctx, 64), 3000], n_needles=8,
+                    seed=2300 + ctx)
+    inp = wl.make_inputs(w)
+    inp["ctx_len"][0] = ctx
+    got, ref = run_and_compare(w, f"chunk-ctx{ctx}", inp=inp, max_ctx_len=3000)
+    dead = max(0, 64 - ctx)
+    assert np.all(got["out_full"][0, :dead] == 0) and np.all(got["idx"][0, :dead] == -1)
+    for j in range(dead, 64):   # n <= 1152: every visible position, ascending
+        n = ctx - 64 + j + 1
+        for g in range(4):
+            assert got["idx"][0, j, g, :n].tolist() == list(range(n))
 
 
 def test_chunk_small_mfma_path():
@@ -177,11 +235,11 @@ def test_chunk_small_mfma_path():
                                               (1, 0), (1, 33), (1, 63)])
 
 
-def test_chunk_per_token_route(monkeypatch):
-    """The same chunk with HS2_CHUNK_PER_TOKEN=1: the decode scan once per token."""
-    monkeypatch.setenv("HS2_CHUNK_PER_TOKEN", "1")
+def test_chunk_per_token_route():
+    """The same chunk with HS2_FLAG_CHUNK_PER_TOKEN: the decode scan once per token."""
     w = wl.Workload("chunk per token", 1, 64, 32, 4, ctx_lens=[6000], n_needles=16, seed=2006)
-    run_and_compare(w, "chunk-per-token", tokens=[(0, 0), (0, 31), (0, 32), (0, 63)])
+    run_and_compare(w, "chunk-per-token", tokens=[(0, 0), (0, 31), (0, 32), (0, 63)],
+                    flags=HS2_FLAG_CHUNK_PER_TOKEN)
 
 
 @pytest.mark.parametrize("lq,ctx,hq,hkv", [(16, [3000, 700], 32, 4), (40, [4100], 16, 2),
@@ -207,12 +265,12 @@ def test_wide_groups_decode(hq, hkv, kv, ctx):
 
 
 @pytest.mark.parametrize("fused", ["0", "1"])
-def test_wide_group_sparse_paths(monkeypatch, fused):
+def test_wide_group_sparse_paths(fused):
     """MQA sparse layers on the split matrix-core gather + combine (decode default) and
     on the one-launch gather."""
-    monkeypatch.setenv("HS2_SPARSE_FUSED", fused)
     w = wl.Workload("mqa sparse", 3, 1, 32, 1, ctx_lens=[800, 5000, 2049], n_needles=8, seed=2540)
-    run_and_compare(w, f"mqa-sparse-fused{fused}")
+    run_and_compare(w, f"mqa-sparse-fused{fused}",
+                    flags=HS2_FLAG_SPARSE_FUSED if fused == "1" else HS2_FLAG_SPARSE_SPLIT)
 
 
 def test_mqa_query_chunk():
@@ -263,21 +321,23 @@ def test_more_selection_rows_than_grid_y(with_probs):
                     tokens=[(0, 0), (0, 255), (31, 100), (63, 0), (63, 255)])
 
 
-def test_chunk_split_invariant(monkeypatch):
-    """Chunk kernel: several position splits and one split give the same outputs."""
+def test_chunk_split_invariant():
+    """Chunk kernel: several position splits and one split give the same index sets and,
+    per output row, the same values to SPLIT_TOL of the row's largest entry."""
     from long_context_decode_full_amd.runner import HybridBlockDevice
     w = wl.Workload("chunk splits", 1, 64, 32, 4, ctx_lens=[9000], n_needles=16, seed=2200)
     _announce("chunk-split-invariance", w)
     inp = wl.make_inputs(w)
     outs = []
-    for sl in ("1024", "16384"):
-        monkeypatch.setenv("HS2_SPLIT_LEN", sl)
-        dev = HybridBlockDevice(inp)
+    for sl in (1024, 16384):
+        dev = HybridBlockDevice(inp, split_len=sl)
         dev.step()
         outs.append(dev.results())
     a, b = outs
     assert np.array_equal(a["idx"], b["idx"])
-    assert np.max(np.abs(a["out_full"] - b["out_full"])) <= 2e-6 * max(1.0, np.max(np.abs(b["out_full"])))
+    worst = float(out_row_errors(a["out_full"], b["out_full"]).max())
+    print(f"[gpu case] chunk split invariance: worst row difference {worst:.2e}", flush=True)
+    assert worst <= SPLIT_TOL
 
 
 POISON_CASES = {
@@ -299,21 +359,16 @@ def test_workspace_contents_do_not_matter(name):
     call gives bitwise the outputs of a zeroed one (deterministic scan): no kernel reads
     workspace memory that the same call did not write (the combine folds only the
     splits below each row's visible length)."""
-    from long_context_decode_full_amd import hs2_set_deterministic
     from long_context_decode_full_amd.runner import HybridBlockDevice
     w, mode = POISON_CASES[name]
     _announce(f"poisoned-workspace-{name}", w)
     inp = wl.make_inputs(w)
-    hs2_set_deterministic(True)
-    try:
-        outs = []
-        for fill in (0, 255):
-            dev = HybridBlockDevice(inp, mode=mode)
-            dev.workspace.fill_(fill)
-            dev.step()
-            outs.append(dev.results())
-    finally:
-        hs2_set_deterministic(False)
+    outs = []
+    for fill in (0, 255):
+        dev = HybridBlockDevice(inp, mode=mode, flags=HS2_FLAG_DETERMINISTIC)
+        dev.workspace.fill_(fill)
+        dev.step()
+        outs.append(dev.results())
     a, b = outs
     assert np.array_equal(a["idx"], b["idx"])
     for x, y in zip([a["out_full"]] + list(a["out_sparse"]), [b["out_full"]] + list(b["out_sparse"])):
@@ -323,20 +378,16 @@ def test_workspace_contents_do_not_matter(name):
 
 # ------------------------------------------------------------------ edges
 @pytest.fixture(params=["auto", "fused"])
-def sparse_path(request, monkeypatch):
+def sparse_path(request):
     """Runs a test with the default sparse-layer routing and again with every sparse
-    layer on the one-workgroup-per-row gather."""
-    if request.param == "fused":
-        monkeypatch.setenv("HS2_SPARSE_FUSED", "1")
-    else:
-        monkeypatch.delenv("HS2_SPARSE_FUSED", raising=False)
-    return request.param
+    layer on the one-workgroup-per-row gather; returns the descriptor flags."""
+    return HS2_FLAG_SPARSE_FUSED if request.param == "fused" else 0
 
 
 @pytest.mark.parametrize("ctx", [1, 127, 128, 129, 1151, 1152, 1153, 5000])
 def test_short_and_boundary_contexts(ctx, sparse_path):
     w = wl.Workload(f"ctx{ctx}", 1, 1, 16, 2, ctx_lens=[ctx], n_needles=min(4, ctx), seed=3000 + ctx)
-    got, ref = run_and_compare(w, f"ctx{ctx}")
+    got, ref = run_and_compare(w, f"ctx{ctx}", flags=sparse_path)
     if ctx <= 1152:   # every position selected; sparse layers equal dense attention
         for g in range(2):
             assert got["idx"][0, 0, g, :ctx].tolist() == list(range(ctx))
@@ -347,14 +398,14 @@ def test_ragged_batch_with_poisoned_tail(with_probs, sparse_path):
     """Rows past ctx_len hold NaN; they must never be read.  Capacity > every length."""
     w = wl.Workload("ragged", 4, 1, 16, 2, ctx_lens=[3000, 1, 1300, 7777], n_needles=8,
                     capacity=8192, poison_tail=True, seed=3100)
-    run_and_compare(w, "ragged-poison", with_probs=with_probs)
+    run_and_compare(w, "ragged-poison", with_probs=with_probs, flags=sparse_path)
 
 
 @pytest.mark.parametrize("with_probs", [False, True])
 def test_ragged_fp8_with_poisoned_tail(with_probs, sparse_path):
     w = wl.Workload("ragged fp8", 3, 1, 32, 4, ctx_lens=[4100, 200, 9000], n_needles=8,
                     kv_dtype="fp8", capacity=9216, poison_tail=True, seed=3150)
-    run_and_compare(w, "ragged-fp8", with_probs=with_probs)
+    run_and_compare(w, "ragged-fp8", with_probs=with_probs, flags=sparse_path)
 
 
 @pytest.mark.parametrize("with_probs", [False, True])
@@ -430,7 +481,7 @@ def test_rows_with_no_visible_position(sparse_path):
     _announce("empty-rows", w)
     inp = wl.make_inputs(w)
     inp["ctx_len"][0] = 2          # rows j = 0, 1 of sequence 0 see nothing
-    dev = HybridBlockDevice(inp, max_ctx_len=3000)
+    dev = HybridBlockDevice(inp, max_ctx_len=3000, flags=sparse_path)
     dev.step()
     got = dev.results()
     assert np.all(got["out_full"][0, :2] == 0) and np.all(got["idx"][0, :2] == -1)
@@ -444,39 +495,36 @@ def test_rows_with_no_visible_position(sparse_path):
 
 
 # ------------------------------------------------------------------ properties
-@pytest.fixture
-def deterministic_mode():
-    """Switches the context scan's fixed step shares on for one test."""
-    from long_context_decode_full_amd import hs2_set_deterministic
-    assert hs2_set_deterministic(True) == 0
-    yield
-    assert hs2_set_deterministic(False) == 0
+# Split invariance: two runs of the same inputs that sum the same terms in different
+# orders (other split lengths, or the scan's dynamic step sharing) must agree per output
+# row to SPLIT_TOL of the row's largest |entry|.  Each run is within ~4e-6 of the
+# float64 oracle per row in every parity case (the fp32 sums and the bf16 two-part
+# split of the probabilities), so two runs differ by at most about twice that; 1e-5
+# leaves a margin and is 200x tighter than the parity bar.
+SPLIT_TOL = 1e-5
 
 
 @pytest.mark.parametrize("fixed", [False, True])
-def test_deterministic_and_split_invariant(monkeypatch, request, fixed):
+def test_deterministic_and_split_invariant(fixed):
     """Index sets never depend on the run or the split length.  The full layer's output
-    is bitwise reproducible with hs2_set_deterministic(1); by default the scan's waves
+    is bitwise reproducible with HS2_FLAG_DETERMINISTIC; by default the scan's waves
     share steps dynamically and it may differ in the last fp32 bits between runs.  The
-    sparse layers are always bitwise reproducible for one index set."""
+    sparse layers are always bitwise reproducible for one index set.  Across split
+    lengths every output row agrees to SPLIT_TOL of its largest entry."""
     from long_context_decode_full_amd.runner import HybridBlockDevice
-    if fixed:
-        request.getfixturevalue("deterministic_mode")
+    flags = HS2_FLAG_DETERMINISTIC if fixed else 0
     w = wl.Workload("split invariance", 1, 1, 32, 4, ctx_lens=[70000], n_needles=32, seed=3900)
     _announce(f"split-invariance fixed={fixed}", w)
     inp = wl.make_inputs(w)
     outs = []
-    for split in ("", "256", "4096", "20480"):
-        if split:
-            monkeypatch.setenv("HS2_SPLIT_LEN", split)
-        else:
-            monkeypatch.delenv("HS2_SPLIT_LEN", raising=False)
-        print(f"[gpu case] split-invariance HS2_SPLIT_LEN={split or 'default'}", flush=True)
-        dev = HybridBlockDevice(inp)
+    for split in (0, 256, 4096, 20480):
+        print(f"[gpu case] split-invariance split_len={split or 'default'}", flush=True)
+        dev = HybridBlockDevice(inp, flags=flags, split_len=split)
         for rep in range(3):
             dev.step()
             outs.append((split, rep, dev.results()))
     base = outs[0][2]
+    worst = 0.0
     for split, rep, r in outs[1:]:
         assert np.array_equal(r["idx"], base["idx"]), f"idx changed (split {split}, rep {rep})"
         if split == outs[0][0]:
@@ -484,15 +532,17 @@ def test_deterministic_and_split_invariant(monkeypatch, request, fixed):
                 assert np.array_equal(r["out_full"], base["out_full"]), "not bitwise deterministic"
             for layer in range(3):
                 assert np.array_equal(r["out_sparse"][layer], base["out_sparse"][layer])
-        assert np.max(np.abs(r["out_full"] - base["out_full"])) <= 1e-5
+        worst = max(worst, float(out_row_errors(r["out_full"], base["out_full"]).max()))
         for layer in range(3):
-            assert np.max(np.abs(r["out_sparse"][layer] - base["out_sparse"][layer])) <= 1e-5
+            worst = max(worst, float(out_row_errors(r["out_sparse"][layer], base["out_sparse"][layer]).max()))
+    print(f"[gpu case] split invariance: worst row difference {worst:.2e} (bound {SPLIT_TOL:.0e})", flush=True)
+    assert worst <= SPLIT_TOL
 
 
-def test_deterministic_mode_parity(deterministic_mode):
+def test_deterministic_mode_parity():
     """The fixed-share scan against the oracle (batched decode)."""
     w = wl.standard_workloads()["batched"]
-    run_and_compare(w, "batched-fixed-steps")
+    run_and_compare(w, "batched-fixed-steps", flags=HS2_FLAG_DETERMINISTIC)
 
 
 def test_sparse_over_all_positions_equals_dense():
