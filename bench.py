@@ -30,6 +30,8 @@ SCAN_SOURCES = [os.path.join(ROOT, "long_context_decode_full_amd", "csrc", f)
                 for f in ("hs2_scan_mfma.hip", "hs2_rowops.h", "hs2_device.h", "hs2_internal.h")]
 BRIDGE_SOURCES = [os.path.join(ROOT, "long_context_decode_full_amd", "csrc", f)
                   for f in ("hs2_bridge.hip", "hs2_device.h", "hs2_internal.h")]
+CHUNK_SOURCES = [os.path.join(ROOT, "long_context_decode_full_amd", "csrc", f)
+                 for f in ("hs2_chunk_mfma.hip", "hs2_rowops.h", "hs2_device.h", "hs2_internal.h")]
 BRIDGE_METRIC = "KV Bridging projection tokens/s & MFMA TFLOP/s (%bf16 dense peak)"
 DECODE_METRIC = "Cross-Decoder decode tokens/s (KV Bridging append + 6 Hybrid Blocks per token)"
 DECODE_LOOPS = {
@@ -607,7 +609,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(args.workload),
+            # counters were taken for token selection (the record path's scan)
+            "traffic": measured_traffic(args.workload) if args.select == "token" else None,
             "kernel": "scan_mfma_kernel (split-K full-attention scan on the matrix cores)",
             "algorithmic_bytes_per_launch": algo,
             "measured_copy_gbps": copy_gbps,
@@ -623,7 +626,8 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": (measured_traffic(args.workload, CHUNK_SOURCES, "chunk_source_sha256")
+                        if args.select == "token" else None),
             "kernel": "chunk_mfma_kernel (64-token chunk full-attention scan on the matrix cores)",
             "algorithmic_flops_per_launch": flops,
             "kv_gbps": achieved,
