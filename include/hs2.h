@@ -62,7 +62,9 @@ typedef enum hs2_status {
   HS2_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head_dim != 128, G > 32 ..)*/
   HS2_ERR_WORKSPACE = 3,     /* workspace_bytes smaller than hs2_workspace_size()      */
   HS2_ERR_ALIGNMENT = 4,     /* a device pointer is not aligned as required            */
-  HS2_ERR_LAUNCH = 5         /* the HIP runtime refused a launch                        */
+  HS2_ERR_LAUNCH = 5,        /* the HIP runtime refused a launch                        */
+  HS2_ERR_SCRATCH_LIMIT = 6  /* hs2_full_attn_select_noalloc: the call needs more scratch
+                                than HS2_NOALLOC_SCRATCH_BYTES                          */
 } hs2_status;
 
 enum { HS2_KV_BF16 = 0, HS2_KV_FP8_E4M3FN = 1 };
@@ -308,6 +310,28 @@ hs2_status hs2_decode_step(const hs2_decode_plan* plan, const void* x, const voi
                            int32_t* ctx_len, float* const* out_full, int32_t* const* idx,
                            float* const* out_sparse, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/* ------------------------------------------------------------------ no allocation
+ * For callers that cannot allocate device memory or pass a workspace: code under HIP
+ * graph capture, serving loops and harnesses that forbid allocation.  Computes exactly
+ * what hs2_full_attn_select computes, with the same kernels, but its scratch is one
+ * static device array of HS2_NOALLOC_SCRATCH_BYTES held by the library on each GPU it
+ * runs on (until the process ends); the caller passes only inputs and outputs.  The
+ * scratch needed is the call's own path only (no logits area on the record path):
+ * the million-token decode needs ~47 MiB; a call needing more returns
+ * HS2_ERR_SCRATCH_LIMIT before anything is enqueued (as does every argument check of
+ * hs2_full_attn_select).  The device is the calling thread's current HIP device, which
+ * must own `stream`.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (concurrent streams, several host threads) race.  The array
+ * keeps the last call's contents, which no later call reads before writing.  Calls
+ * no hipMalloc, hipFree or allocating library routine. */
+#define HS2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hs2_status hs2_full_attn_select_noalloc(const hs2_attn_desc* desc,
+                                        const void* q, const void* k, const void* v,
+                                        const float* k_scale, const float* v_scale,
+                                        const int32_t* ctx_len,
+                                        float* out, int32_t* idx, float* probs,
+                                        hipStream_t stream);
 
 /* ------------------------------------------------------------------ kernel timing
  * Benchmark support without library state: the caller creates two HIP events

@@ -26,7 +26,8 @@ __all__ = [
     "library_path", "load_library", "Hs2BridgeDesc", "make_bridge_desc",
     "hs2_kv_bridge", "Hs2DecodePlan", "make_decode_plan", "hs2_decode_workspace_size",
     "hs2_decode_step", "hs2_sparse_attn_swa_workspace_size", "hs2_sparse_attn_swa",
-    "EXPORTED_SYMBOLS", "SIZE_MAX",
+    "EXPORTED_SYMBOLS", "SIZE_MAX", "hs2_full_attn_select_noalloc", "HS2_ERR_SCRATCH_LIMIT",
+    "HS2_NOALLOC_SCRATCH_BYTES",
 ]
 
 HS2_OK = 0
@@ -35,6 +36,8 @@ HS2_ERR_UNSUPPORTED = 2
 HS2_ERR_WORKSPACE = 3
 HS2_ERR_ALIGNMENT = 4
 HS2_ERR_LAUNCH = 5
+HS2_ERR_SCRATCH_LIMIT = 6
+HS2_NOALLOC_SCRATCH_BYTES = 64 << 20
 HS2_KV_BF16 = 0
 HS2_KV_FP8_E4M3FN = 1
 HS2_SELECT_TOKEN = 0
@@ -53,7 +56,8 @@ EXPORTED_SYMBOLS = ("hs2_validate", "hs2_workspace_size", "hs2_full_attn_select"
                     "hs2_sparse_attn", "hs2_status_string", "hs2_full_attn_select_timed",
                     "hs2_sparse_attn_timed", "hs2_build_id", "hs2_kv_bridge",
                     "hs2_decode_workspace_size", "hs2_decode_step",
-                    "hs2_sparse_attn_swa_workspace_size", "hs2_sparse_attn_swa")
+                    "hs2_sparse_attn_swa_workspace_size", "hs2_sparse_attn_swa",
+                    "hs2_full_attn_select_noalloc")
 
 
 class Hs2AttnDesc(ctypes.Structure):
@@ -173,6 +177,8 @@ def load_library(path=None):
     lib.hs2_full_attn_select_timed.restype = ctypes.c_int
     lib.hs2_sparse_attn_timed.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, E]
     lib.hs2_sparse_attn_timed.restype = ctypes.c_int
+    lib.hs2_full_attn_select_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
+    lib.hs2_full_attn_select_noalloc.restype = ctypes.c_int
     lib.hs2_build_id.argtypes = []
     lib.hs2_build_id.restype = ctypes.c_char_p
     lib.hs2_kv_bridge.argtypes = [ctypes.POINTER(Hs2BridgeDesc), P, P, P, P, P, P, P, P, P]
@@ -239,6 +245,14 @@ def hs2_sparse_attn(desc, q, k, v, k_scale, v_scale, ctx_len, idx, out, workspac
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
         _ptr(ctx_len), _ptr(idx), _ptr(out), _ptr(workspace), int(workspace_bytes),
         _stream(stream))
+
+
+def hs2_full_attn_select_noalloc(desc, q, k, v, k_scale, v_scale, ctx_len, out, idx, probs,
+                                 stream=None) -> int:
+    """hs2_full_attn_select over the library's own scratch: no workspace argument."""
+    return load_library().hs2_full_attn_select_noalloc(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
+        _ptr(ctx_len), _ptr(out), _ptr(idx), _ptr(probs), _stream(stream))
 
 
 def _events(events):

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhs2.so")
 SOURCES = ["hs2_scan.hip", "hs2_scan_mfma.hip", "hs2_chunk_mfma.hip", "hs2_select.hip", "hs2_select_fast.hip",
-           "hs2_bridge.hip", "hs2_swa.hip", "hs2_api.cpp"]
+           "hs2_bridge.hip", "hs2_swa.hip", "hs2_scratch.hip", "hs2_api.cpp"]
 
 
 def hipcc() -> str:

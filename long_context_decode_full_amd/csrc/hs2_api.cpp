@@ -105,7 +105,10 @@ bool chunk_block_path(const hs2_attn_desc* d) {
          d->block_size % 64 == 0 && !has_flag(d, HS2_FLAG_CHUNK_PER_TOKEN);
 }
 
-Layout make_layout(const hs2_attn_desc* d) {
+// logits_area: reserve the logits path's per-position scores whenever that path fits
+// its budget (the workspace callers size with hs2_workspace_size), or only when this
+// call takes that path (the no-allocation entry point, which knows its call).
+Layout make_layout(const hs2_attn_desc* d, bool logits_area = true) {
   Layout L;
   L.n_sel = (int64_t)d->batch * d->q_len * d->n_kv_heads;
   L.G = d->n_q_heads / d->n_kv_heads;
@@ -176,7 +179,7 @@ Layout make_layout(const hs2_attn_desc* d) {
   L.off_part = off;   off = align_up(off + (size_t)n * nsplit_max * L.G * kPartStride * sizeof(float));
   L.off_mz = off;     off = align_up(off + (size_t)n * kMaxHeads * 2 * sizeof(float));
   L.off_selblk = off; off = align_up(off + (size_t)n * kSelWords * sizeof(uint32_t));
-  if (L.logits_ok) {
+  if (L.logits_ok && logits_area) {
     L.off_logits = off; off = align_up(off + (size_t)n * L.logit_stride * 8 * sizeof(float));
     L.off_records = L.off_logits;   // the record path's 2-byte records share that area
     L.off_s = off;      off = align_up(off + (size_t)n * L.logit_stride * sizeof(float));
@@ -242,6 +245,7 @@ HS2_API const char* hs2_status_string(hs2_status status) {
     case HS2_ERR_WORKSPACE: return "workspace too small";
     case HS2_ERR_ALIGNMENT: return "misaligned pointer";
     case HS2_ERR_LAUNCH: return "kernel launch failed";
+    case HS2_ERR_SCRATCH_LIMIT: return "call needs more than the library's no-allocation scratch";
   }
   return "unknown status";
 }
@@ -354,6 +358,13 @@ hs2_status chunk_block_select(const hs2_attn_desc* desc, const Layout& L, ScanAr
   return HS2_OK;
 }
 
+// The launches of hs2_full_attn_select for a checked call, in workspace layout L.
+static hs2_status full_select_launch(const hs2_attn_desc* desc, const Layout& L, const void* q,
+                                     const void* k, const void* v, const float* k_scale,
+                                     const float* v_scale, const int32_t* ctx_len, float* out,
+                                     int32_t* idx, float* probs, uint8_t* ws, hipStream_t stream,
+                                     const hs2_kernel_events* ev);
+
 HS2_API hs2_status hs2_full_attn_select_timed(const hs2_attn_desc* desc, const void* q, const void* k,
                                               const void* v, const float* k_scale, const float* v_scale,
                                               const int32_t* ctx_len, float* out, int32_t* idx,
@@ -364,16 +375,23 @@ HS2_API hs2_status hs2_full_attn_select_timed(const hs2_attn_desc* desc, const v
                               workspace_bytes, &L);
   if (s != HS2_OK) return s;
   if (probs != nullptr && !aligned(probs, 4)) return HS2_ERR_ALIGNMENT;
-  const bool fp8 = desc->kv_dtype == HS2_KV_FP8_E4M3FN;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  s = full_path_supported(desc, L, probs);
+  if (s != HS2_OK) return s;
+  return full_select_launch(desc, L, q, k, v, k_scale, v_scale, ctx_len, out, idx, probs,
+                            static_cast<uint8_t*>(workspace), stream, ev);
+}
 
+static hs2_status full_select_launch(const hs2_attn_desc* desc, const Layout& L, const void* q,
+                                     const void* k, const void* v, const float* k_scale,
+                                     const float* v_scale, const int32_t* ctx_len, float* out,
+                                     int32_t* idx, float* probs, uint8_t* ws, hipStream_t stream,
+                                     const hs2_kernel_events* ev) {
+  const bool fp8 = desc->kv_dtype == HS2_KV_FP8_E4M3FN;
   // Record path (default for token selection): compact bound records, exact
   // re-scoring of the candidates.  Logits path: every position's logits, needed
   // when the caller wants all probabilities (probs) or for the block comparator.
   const bool fast = use_record_path(desc, L, probs);
   const bool cblock = chunk_block_path(desc) && probs == nullptr;
-  s = full_path_supported(desc, L, probs);
-  if (s != HS2_OK) return s;
   ScanArgs sa = scan_args(desc, L, q, k, v, k_scale, v_scale, ctx_len, ws);
   if (cblock) return chunk_block_select(desc, L, sa, ctx_len, out, idx, ws, stream, ev);
   sa.logits = reinterpret_cast<float*>(ws + L.off_logits);
@@ -387,7 +405,7 @@ HS2_API hs2_status hs2_full_attn_select_timed(const hs2_attn_desc* desc, const v
   event_record(ev, true, stream);
   // record path: matrix-core scan (HS2_FLAG_SCAN_VALU selects the VALU scan instead)
   const bool mfma = fast && (wide_group(desc) || !has_flag(desc, HS2_FLAG_SCAN_VALU));
-  hipError_t e = (fast && chunk_path(desc)) ? launch_chunk_mfma(sa, desc->batch, stream)
+  const hipError_t e = (fast && chunk_path(desc)) ? launch_chunk_mfma(sa, desc->batch, stream)
                  : mfma                     ? launch_scan_mfma(sa, fp8, desc->batch, stream)
                                             : launch_scan_dense(sa, fp8, fast, desc->batch, stream);
   event_record(ev, false, stream);
@@ -498,6 +516,33 @@ HS2_API hs2_status hs2_full_attn_select(const hs2_attn_desc* desc, const void* q
                                         hipStream_t stream) {
   return hs2_full_attn_select_timed(desc, q, k, v, k_scale, v_scale, ctx_len, out, idx, probs,
                                     workspace, workspace_bytes, stream, nullptr);
+}
+
+// Same launches over the library's own scratch (one static device array per GPU): no
+// workspace argument, nothing allocated.  The layout reserves only what this call's
+// path uses, so the record path at a million positions fits the array.
+HS2_API hs2_status hs2_full_attn_select_noalloc(const hs2_attn_desc* desc, const void* q, const void* k,
+                                                const void* v, const float* k_scale, const float* v_scale,
+                                                const int32_t* ctx_len, float* out, int32_t* idx,
+                                                float* probs, hipStream_t stream) {
+  hs2_status s = validate_desc(desc);
+  if (s != HS2_OK) return s;
+  Layout L;
+  // every pointer check of the workspace entry point (the workspace itself aside)
+  static uint8_t stand_in[16] __attribute__((aligned(16)));
+  s = check_common(desc, q, k, v, k_scale, v_scale, ctx_len, out, idx, stand_in, SIZE_MAX, &L);
+  if (s != HS2_OK) return s;
+  if (probs != nullptr && !aligned(probs, 4)) return HS2_ERR_ALIGNMENT;
+  L = make_layout(desc, false);
+  if (!use_record_path(desc, L, probs) && !(chunk_block_path(desc) && probs == nullptr))
+    L = make_layout(desc, true);   // the logits path's scores are needed
+  s = full_path_supported(desc, L, probs);
+  if (s != HS2_OK) return s;
+  if (L.total > kNoallocScratchBytes) return HS2_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess || ws == nullptr) return HS2_ERR_LAUNCH;
+  return full_select_launch(desc, L, q, k, v, k_scale, v_scale, ctx_len, out, idx, probs,
+                            static_cast<uint8_t*>(ws), stream, nullptr);
 }
 
 // slot_rows: index entries are rows of a local cache (any row < cap), not positions.

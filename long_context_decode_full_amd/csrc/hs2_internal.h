@@ -179,6 +179,11 @@ hipError_t launch_swa_rows(const int32_t* ctx_len, int32_t* idx, int64_t n_sel, 
                            int R, int64_t ctx_max, hipStream_t st);
 hipError_t launch_add(float* out, const float* add, int64_t n, hipStream_t st);
 
+// hs2_full_attn_select_noalloc: the device address of the calling thread's current
+// GPU's copy of the library's scratch array (taken once per device, then cached)
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st);
 hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t st);
 hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st);

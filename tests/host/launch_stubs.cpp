@@ -58,6 +58,14 @@ static void check_scan(const ScanArgs& a, int B, bool records) {
 
 int bridge_tile_tokens(int n_tokens) { return n_tokens >= 4096 ? 256 : 128; }
 
+// the no-allocation entry point's scratch: a fake device address; the test announces
+// [kStubScratch, kStubScratch + kNoallocScratchBytes) as the workspace
+constexpr uintptr_t kStubScratch = uintptr_t(0x7D0000000000);
+hipError_t noalloc_scratch(void** ptr) {
+  *ptr = reinterpret_cast<void*>(kStubScratch);
+  return hipSuccess;
+}
+
 hipError_t launch_bridge(const BridgeArgs& a, bool, hipStream_t) {
   if (a.T < 1) fail("bridge: launched with no token");
   for (int l = 0; l < a.n_layers; ++l)

@@ -45,7 +45,7 @@ def test_header_symbols_are_exported(lib):
 
 
 def test_status_strings(lib):
-    for st in range(6):
+    for st in range(7):
         assert hs2.hs2_status_string(st)
     assert hs2.hs2_status_string(0) == "ok"
     assert hs2.hs2_status_string(99) == "unknown status"
@@ -219,6 +219,26 @@ def test_workspace_too_small(lib):
     assert st == 0
     assert _full(d, workspace_bytes=nbytes - 1) == hs2.HS2_ERR_WORKSPACE
     assert _sparse(d, workspace_bytes=16) == hs2.HS2_ERR_WORKSPACE
+
+
+def test_noalloc_checks_before_touching_a_device(lib):
+    """The no-allocation entry point checks its arguments like hs2_full_attn_select and
+    refuses calls beyond its fixed scratch before any HIP call (no GPU needed here)."""
+    def noalloc(d, **over):
+        args = dict(q=FAKE, k=FAKE, v=FAKE, k_scale=None, v_scale=None, ctx_len=FAKE, out=FAKE, idx=FAKE,
+                    probs=None)
+        args.update(over)
+        return hs2.hs2_full_attn_select_noalloc(d, stream=0, **args)
+    assert noalloc(_desc(head_dim=64)) == hs2.HS2_ERR_UNSUPPORTED
+    assert noalloc(_desc(), q=None) == hs2.HS2_ERR_INVALID_ARG
+    assert noalloc(_desc(), out=FAKE + 4) == hs2.HS2_ERR_ALIGNMENT
+    assert noalloc(_desc(), probs=FAKE + 2) == hs2.HS2_ERR_ALIGNMENT
+    assert noalloc(_desc(kv_dtype=hs2.HS2_KV_FP8_E4M3FN)) == hs2.HS2_ERR_INVALID_ARG
+    # the 64-token chunk at 500K positions, or every logit of a million positions
+    assert noalloc(_desc(batch=16, q_len=64, kv_capacity=502710, max_ctx_len=502710)) == \
+        hs2.HS2_ERR_SCRATCH_LIMIT
+    assert noalloc(_desc(), probs=FAKE) == hs2.HS2_ERR_SCRATCH_LIMIT
+    assert "scratch" in hs2.hs2_status_string(hs2.HS2_ERR_SCRATCH_LIMIT)
 
 
 def test_invalid_desc_checked_before_pointers(lib):

@@ -87,6 +87,32 @@ def test_full_and_sparse_launch_sequences(lib, name, probs):
                   f"{name} sparse layer")
 
 
+SCRATCH = 0x7D0000000000     # the stand-ins' scratch address
+
+
+@pytest.mark.parametrize("name", ["million", "fp8_256k", "batched", "tiny", "mqa", "decode_block", "short",
+                                  "force_logits", "splits"])
+@pytest.mark.parametrize("probs", [False, True])
+def test_noalloc_launch_sequence_fits_the_scratch(lib, name, probs):
+    """hs2_full_attn_select_noalloc: every array its kernels index lies inside the
+    library's fixed scratch, or the call is refused with HS2_ERR_SCRATCH_LIMIT."""
+    d = hs2.make_desc(**DESCS[name])
+    fp8 = d.kv_dtype == hs2.HS2_KV_FP8_E4M3FN
+    sc = BUF + 0x10000000 if fp8 else None
+    lib.hs2_stub_set_workspace(SCRATCH, hs2.HS2_NOALLOC_SCRATCH_BYTES)
+    st = hs2.hs2_full_attn_select_noalloc(d, BUF, BUF, BUF, sc, sc, BUF, BUF, BUF, BUF if probs else None,
+                                          stream=0)
+    if st == hs2.HS2_ERR_SCRATCH_LIMIT:
+        assert probs or d.select_mode == hs2.HS2_SELECT_BLOCK or d.flags & hs2.HS2_FLAG_FORCE_LOGITS, name
+        assert lib.hs2_stub_launches() == 0
+    elif st == hs2.HS2_ERR_UNSUPPORTED:
+        assert probs and d.n_q_heads // d.n_kv_heads > 8
+    else:
+        _expect_clean(lib, st, f"{name} no-allocation full layer")
+    if name == "million" and not probs:
+        assert st == hs2.HS2_OK   # the benchmark's decode fits
+
+
 def test_decode_step_launch_sequence(lib):
     attn = hs2.make_desc(2, 1, 32, 4, 40000, 39000)
     plan = hs2.make_decode_plan(attn, 3, 3, 2048)
