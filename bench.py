@@ -474,7 +474,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps first: the GPU reaches its sustained clocks after a few tens of ms")
     ap.add_argument("--workload", default="million",
-                    help="tiny | batched | fp8_256k | million | chunk | mqa_million; KV Bridging: "
+                    help="tiny | batched | fp8_256k | million | chunk | mqa_million | mqa_chunk; KV Bridging: "
                          "bridge_prefill | bridge_prefill_bf16 | bridge_mqa | bridge_decode; decode loop: "
                          "decode_loop_million | decode_loop_batched | decode_loop_tiny")
     ap.add_argument("--select", default="token", choices=["token", "block", "gen1"],

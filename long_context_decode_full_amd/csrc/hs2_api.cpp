@@ -88,15 +88,16 @@ hs2_status validate_desc(const hs2_attn_desc* d) {
 bool has_flag(const hs2_attn_desc* d, uint32_t f) { return (d->flags & f) != 0u; }
 
 // Token selection for a chunk of query tokens (q_len > 1, bf16 cache) runs the
-// matrix-core chunk kernel, which reads each KV row once for 32 tokens.
+// matrix-core chunk kernel, which reads each KV row once for 256 query rows (32 tokens
+// of up to 8 heads, 16 of up to 16, 8 of up to 32).
 // HS2_FLAG_CHUNK_PER_TOKEN runs the decode scan once per token instead (comparison).
 bool chunk_path(const hs2_attn_desc* d) {
   return d->q_len > 1 && d->kv_dtype == HS2_KV_BF16 && d->select_mode == HS2_SELECT_TOKEN &&
-         d->n_q_heads / d->n_kv_heads <= kSlots && !has_flag(d, HS2_FLAG_CHUNK_PER_TOKEN);
+         !has_flag(d, HS2_FLAG_CHUNK_PER_TOKEN);
 }
-// More than 8 query heads per KV head: the matrix-core scan with 16-head blocks, the
-// matrix-core gather and block-wise re-scoring; the logits path (probs) and the chunk
-// kernel keep 8 head slots and are not used (chunks run the scan once per token).
+// More than 8 query heads per KV head: the matrix-core scans with 16-head blocks, the
+// matrix-core gather and block-wise re-scoring; the logits path (probs) keeps 8 head
+// slots and is not used.
 bool wide_group(const hs2_attn_desc* d) { return d->n_q_heads / d->n_kv_heads > kSlots; }
 // The block comparator for a chunk (block sizes that are multiples of 64) takes its
 // block masses from the same kernel's per-block sums instead of per-position logits.

@@ -2,32 +2,35 @@
 // of a Hybrid Block for every token of an appended chunk, causal inside the chunk,
 // with the record-path outputs of the decode scan (online-softmax partials per
 // (token, head, split), a 2-byte bound record per (token, position) and a key
-// histogram per (token, split)).
+// histogram per (token, split)), or, in block mode, log2 of the sum of 2^logit over
+// each aligned 64-position block per (token, head).
 //
 // HySparse2 article, section 02 "KV Reuse" (the full layer's own attention scores
 // decide what the sparse layers reuse) and section 03 (selection per token: every
 // query token of the chunk gets its own window and top-k).
 //
-// A workgroup owns one position split of one (sequence, KV head) and 32 query tokens
-// (16 tiles of 16 query rows = 2 tokens x 8 head slots; slots >= G are zero), so it
-// reads every K/V row of its split once for 256 query rows.  Per iteration of 64
-// positions the K and V tiles go through LDS (shared by the 8 waves); wave w owns
-// query tiles 2w, 2w+1.  With lane = 16*grp + i:
-//   S = Q K^T on v_mfma_f32_16x16x32_bf16: A = Q (lane: query row i, dims 32s + 8grp),
-//     B = K^T (lane: position i, the same dims) read from the K tile; the
-//     accumulator lane holds query rows 4grp+v (v = 0..3) at position i, so the 4
-//     rows of a lane are 4 heads of one token.
-//   softmax per query row: maxima over the 16 lanes of a row group (DPP), lazy
-//     raise by 8 (log2 units) as in the decode scan.
-//   record per (token, position): log2 of the sum over the token's heads of
-//     2^logit, from the probabilities already formed for P.V: with U the largest
-//     running maximum of the token's heads, e = U + log2 sum_h p_h 2^(m_h - U)
-//     (4 heads in the lane, 4 in the partner row group via a permlane16 swap);
-//     sums below 2^-100 (terms lost to underflow could matter there) take the
-//     exact form on a wave-uniform branch.
-//   O = P V: P (bf16 high part + bf16 residual) is staged per wave in LDS position-
-//     major and read back as the A operand with ds_read_b64_tr_b16; B = V read from
-//     the V tile with the same transposed read.
+// A workgroup owns one position split of one (sequence, KV head) and 256 query rows:
+// 256 / kGp tokens of kGp head slots each (kGp = 8, 16 or 32: the group size rounded
+// up; slots >= G are zero), so it reads every K/V row of its split once for all of
+// them.  Per iteration of 64 positions the K and V tiles go through LDS (two stages:
+// the next tiles are stored while the current ones are read, one barrier per
+// iteration); wave w owns query rows 32w .. 32w+31 (two tiles of 16).  The scores are
+// formed transposed, S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K rows from the K
+// tile, lane: position i, dims 32s + 8grp; B = Q^T from registers, lane: query row
+// i, the same dims), so a lane's accumulators are 4 positions (4grp + v) of one query
+// row (i) and the probabilities are already in the B-operand layout of the second
+// product: O^T = V^T P^T with A = V^T read transposed from the V tile
+// (ds_read_b64_tr_b16, rows 4grp..4grp+3 of two position tiles per lane) and B = the
+// lane's own 8 probabilities of a 32-position block, as a bf16 high part and a bf16
+// residual (P never goes through LDS).
+//   softmax per query row: the lane's 16 values per iteration, the running maximum
+//     raised lazily by 8 (log2 units) with a max over the 4 row groups.
+//   record per (token, position): log2 of the sum over the token's heads of 2^logit,
+//     from the probabilities already formed: with U the largest running maximum of
+//     the token's heads, e = U + log2 sum_h p_h 2^(m_h - U), a DPP sum over the
+//     token's head lanes (and the second tile for 32 heads); sums below 2^-100 (terms
+//     lost to underflow could matter there) take the exact form on a wave-uniform
+//     branch.
 #include "hs2_rowops.h"
 
 namespace hs2 {
@@ -40,18 +43,24 @@ typedef __attribute__((ext_vector_type(2))) float f32x2v_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kCThreads = 512;                 // 8 waves
-constexpr int kCWaves = kCThreads / 64;
-constexpr int kCTokens = 32;                   // query tokens per workgroup
+constexpr int kCRows = 256;                    // query rows per workgroup
 constexpr int kCPos = 64;                      // positions per iteration
 constexpr float kCSlack = 8.0f;
 constexpr float kMFloor = -1.0e30f;            // initial running maximum (below any logit)
-constexpr int kKRow = 272;                     // bytes per staged K/V row (256 + 16 pad)
+// Staged rows are padded so that the fragment reads spread over the LDS banks: the K
+// rows (16-byte reads, lane = row) by 16 bytes, the V rows (8-byte transposed reads,
+// four lanes per row over four consecutive rows) by 32 bytes.
+constexpr int kKRow = 272;                     // bytes per staged K row (256 + 16 pad)
+constexpr int kVRow = 288;                     // bytes per staged V row (256 + 32 pad)
 constexpr int kKTile = kCPos * kKRow;
-constexpr int kPRow = 72;                      // bytes per staged P row: 32 query rows bf16 + pad
-constexpr int kPHalf = 32 * kPRow;             // 32 positions
-constexpr int kPWave = 2 * kPHalf;             // high part + residual
+constexpr int kVTile = kCPos * kVRow;
+constexpr int kStage = kKTile + kVTile;        // K and V tiles of one iteration
 constexpr int kHistWords = kFastBins / 2;      // two u16 counters per word
-constexpr int kCLds = 2 * kKTile + kCWaves * kPWave + kCTokens * kHistWords * 4;
+
+template <int kGp>
+constexpr int tokens_per_wg() { return kCRows / kGp; }
+template <int kGp, bool kBlockMode>
+constexpr int chunk_lds_bytes() { return 2 * kStage + (kBlockMode ? 0 : tokens_per_wg<kGp>() * kHistWords * 4); }
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -61,75 +70,145 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   const f32x2v_t x = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
 }
-__device__ __forceinline__ bf16x8_t tr_pair(const uint8_t* p0, const uint8_t* p1) {
-  const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0);
-  const s16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p1);
-  const uint2 w0 = __builtin_bit_cast(uint2, x0);
-  const uint2 w1 = __builtin_bit_cast(uint2, x1);
-  return as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+
+// Reductions over the lanes of one token's heads inside a 16-lane row: 8 lanes
+// (lanes 0-7 and 8-15 separately) or all 16.
+template <int kLanes>
+__device__ __forceinline__ float head_sum(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppMirror8>(x);
+  if constexpr (kLanes == 16) x += dpp<kDppRor8>(x);
+  return x;
 }
-// Max / sum over the 16 lanes of a row group.
-__device__ __forceinline__ float max16(float x) {
+template <int kLanes>
+__device__ __forceinline__ float head_max(float x) {
   x = fmaxf(x, dpp<kDppXor1>(x));
   x = fmaxf(x, dpp<kDppXor2>(x));
   x = fmaxf(x, dpp<kDppMirror8>(x));
-  x = fmaxf(x, dpp<kDppRor8>(x));
+  if constexpr (kLanes == 16) x = fmaxf(x, dpp<kDppRor8>(x));
   return x;
 }
-// Partner row group (grp ^ 1): permlane16 swap.  Results are copied to scalars
-// before any bit cast (a bit cast of a vector element reads element 0 here).
-__device__ __forceinline__ float partner(float x) {
+
+// Combine the 4 lanes i, i+16, i+32, i+48 (the four row groups, which hold other
+// positions of the same query row) with the permlane swaps.  The swap results are
+// copied to scalars before any bit cast (a bit cast of a vector element reads
+// element 0 here).
+template <bool kMax>
+__device__ __forceinline__ float across_groups(float x) {
   const uint32_t u = __float_as_uint(x);
-  const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const uint32_t a0 = s[0], a1 = s[1];
-  // lanes of even row groups receive the odd group's value in a1, odd ones in a0
-  return __uint_as_float((__lane_id() & 16) ? a0 : a1);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t a0 = s32[0], a1 = s32[1];
+  x = kMax ? fmaxf(__uint_as_float(a0), __uint_as_float(a1)) : __uint_as_float(a0) + __uint_as_float(a1);
+  const uint32_t w = __float_as_uint(x);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  const uint32_t c0 = s16[0], c1 = s16[1];
+  return kMax ? fmaxf(__uint_as_float(c0), __uint_as_float(c1)) : __uint_as_float(c0) + __uint_as_float(c1);
 }
 
-// U per query tile and c per accumulator row, after the running maxima m changed.
-__device__ __forceinline__ void update_record_scale(const float (&m)[2][4], int hbase, int G,
-                                                    float (&U)[2], float (&c)[2][4]) {
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    float u = kMFloor;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) u = hbase + v < G ? fmaxf(u, m[qt][v]) : u;
-    u = fmaxf(u, partner(u));
-    U[qt] = u;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) c[qt][v] = hbase + v < G ? fast_exp2(m[qt][v] - u) : 0.0f;
+// Sum over one token's heads of a per-lane value: the head lanes of the row (8 or
+// 16) and, for 32 heads, the two query tiles of the wave.
+template <int kGp>
+__device__ __forceinline__ void token_sums(const float (&x)[2], float (&out)[2]) {
+  if constexpr (kGp == 8) {
+    out[0] = head_sum<8>(x[0]);
+    out[1] = head_sum<8>(x[1]);
+  } else if constexpr (kGp == 16) {
+    out[0] = head_sum<16>(x[0]);
+    out[1] = head_sum<16>(x[1]);
+  } else {
+    const float s = head_sum<16>(x[0]) + head_sum<16>(x[1]);
+    out[0] = s;
+    out[1] = s;
   }
 }
-// log2 of the sum over the token's valid heads of 2^l (this lane's 4 + the partner's 4),
-// with the per-position maximum as reference.
-__device__ __forceinline__ float exact_record(const float (&lv)[4], int hbase, int G) {
-  float lm[4];
-  float r = kNegInf;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    lm[v] = hbase + v < G ? lv[v] : kNegInf;
-    r = fmaxf(r, lm[v]);
+template <int kGp>
+__device__ __forceinline__ void token_maxes(const float (&x)[2], float (&out)[2]) {
+  if constexpr (kGp == 8) {
+    out[0] = head_max<8>(x[0]);
+    out[1] = head_max<8>(x[1]);
+  } else if constexpr (kGp == 16) {
+    out[0] = head_max<16>(x[0]);
+    out[1] = head_max<16>(x[1]);
+  } else {
+    const float s = fmaxf(head_max<16>(x[0]), head_max<16>(x[1]));
+    out[0] = s;
+    out[1] = s;
   }
-  r = fmaxf(fmaxf(r, partner(r)), kMFloor);   // finite: exp2 of -inf is 0
-  float sum = 0.0f;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) sum += fast_exp2(lm[v] - r);
-  sum += partner(sum);
-  return r + __builtin_amdgcn_logf(sum);
 }
 
-template <bool kBlockMode>   // false: records + key histograms; true: per-block sums
+// Records of a 32-position block: the values a lane contributes, one per (query tile,
+// position tile of the block, position v), are reduce-scattered over the lanes that hold
+// the token's heads (each DPP step halves the values a lane keeps and adds its
+// partner's other half), so every lane ends with the full head sum of one record:
+//   8 head slots:  8 values (4 qt + v) of one position tile over the 8 lanes of a
+//                 half-row, lane index w16 & 7 (two passes, one per position tile);
+//   16 slots:     16 values (8 tt + 4 qt + v) over the 16 lanes of a row, index w16;
+//   32 slots:      8 values (4 tt + v), the two query tiles (one token) added first, over
+//                 the 16 lanes of a row: index (w16 >> 1), lanes w16 and w16 ^ 1 alike.
+struct RecSlot {
+  int qt, tt, v;
+};
+template <int kGp>
+constexpr int kRecValsOf = kGp == 16 ? 16 : 8;
+template <int kGp>
+constexpr int kRecPassesOf = kGp == 8 ? 2 : 1;
+template <int kGp>
+__device__ __forceinline__ RecSlot rec_slot(int i, int pass) {
+  if constexpr (kGp == 8) return {i >> 2, pass, i & 3};
+  else if constexpr (kGp == 16) return {(i >> 2) & 1, i >> 3, i & 3};
+  else return {0, i >> 2, i & 3};
+}
+template <int kGp>
+__device__ __forceinline__ int own_index(int w16) {
+  return kGp == 8 ? (w16 & 7) : kGp == 16 ? w16 : (w16 >> 1);
+}
+template <int kGp>
+__device__ __forceinline__ bool rec_writer(int w16) {
+  return kGp == 32 ? (w16 & 1) == 0 : true;
+}
+// keep x[j] or x[j + N] (by `upper`) plus the partner lane's other one
+template <int CTRL, int N>
+__device__ __forceinline__ void rs_step(const float* x, float* y, bool upper) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const float keep = upper ? x[j + N] : x[j];
+    const float send = upper ? x[j] : x[j + N];
+    y[j] = keep + dpp<CTRL>(send);
+  }
+}
+template <int kGp>
+__device__ __forceinline__ float reduce_scatter(const float (&x)[kRecValsOf<kGp>], int w16) {
+  const bool b3 = (w16 & 8) != 0, b2 = (w16 & 4) != 0, b1 = (w16 & 2) != 0, b0 = (w16 & 1) != 0;
+  float a8[8], a4[4], a2[2], a1[1];
+  if constexpr (kGp == 8) {
+    rs_step<kDppMirror8, 4>(x, a4, b2);   // partner 7 - i: bit 2 differs
+    rs_step<kDppXor2, 2>(a4, a2, b1);
+    rs_step<kDppXor1, 1>(a2, a1, b0);
+    return a1[0];
+  } else if constexpr (kGp == 16) {
+    rs_step<kDppRor8, 8>(x, a8, b3);
+    rs_step<kDppMirror8, 4>(a8, a4, b2);
+    rs_step<kDppXor2, 2>(a4, a2, b1);
+    rs_step<kDppXor1, 1>(a2, a1, b0);
+    return a1[0];
+  } else {
+    rs_step<kDppRor8, 4>(x, a4, b3);
+    rs_step<kDppMirror8, 2>(a4, a2, b2);
+    rs_step<kDppXor2, 1>(a2, a1, b1);
+    return a1[0] + dpp<kDppXor1>(a1[0]);
+  }
+}
+
+template <int kGp, bool kBlockMode>   // false: records + key histograms; true: per-block sums
 __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kCLds];
-  uint8_t* ktile = lds;
-  uint8_t* vtile = lds + kKTile;
-  uint8_t* pst_all = lds + 2 * kKTile;
-  uint32_t* shist = reinterpret_cast<uint32_t*>(lds + 2 * kKTile + kCWaves * kPWave);
+  constexpr int kTPW = tokens_per_wg<kGp>();
+  constexpr int kRecVals = kRecValsOf<kGp>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[chunk_lds_bytes<kGp, kBlockMode>()];
+  uint32_t* shist = reinterpret_cast<uint32_t*>(lds + 2 * kStage);
 
-  // blockIdx.x = split * token groups + group: the groups of 32 tokens of one split are
-  // adjacent.  (Placing the two groups of a 64-token chunk on one XCD, 8 workgroups
-  // apart, was measured slower: the pair then contends for the same L2 lines at once.)
-  const int n_tgroups = (a.Lq + kCTokens - 1) / kCTokens;
+  // blockIdx.x = split * token groups + group: the groups of one split are adjacent
+  const int n_tgroups = (a.Lq + kTPW - 1) / kTPW;
   const int tgroup = blockIdx.x % n_tgroups;
   const int split = blockIdx.x / n_tgroups;
   const int g = blockIdx.y;
@@ -138,13 +217,12 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int grp = lane >> 4;
-  const int li = lane & 15;
-  uint8_t* pst = pst_all + wave * kPWave;
+  const int w16 = lane & 15;
 
   int64_t ctx = a.ctx_len[b];
   ctx = ctx < 0 ? 0 : (ctx > a.ctx_max ? a.ctx_max : ctx);
-  const int tok0 = tgroup * kCTokens;               // first token of this workgroup
-  const int ntok = min(kCTokens, a.Lq - tok0);      // tokens present (may be <= 0)
+  const int tok0 = tgroup * kTPW;                   // first token of this workgroup
+  const int ntok = min(kTPW, a.Lq - tok0);          // tokens present (may be <= 0)
   const int64_t p_begin = (int64_t)split * a.split_len;
   // the last present token sees the most positions
   int64_t n_last = ctx - a.Lq + (tok0 + ntok - 1) + 1;
@@ -158,70 +236,67 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   if (split > 0 && p_begin >= n_last) return;
   const int64_t sel_tok0 = ((int64_t)b * a.Lq + tok0) * a.Hkv + g;   // sel of token tok0; +Hkv per token
 
-  constexpr bool want_rec = !kBlockMode;   // token selection: records + histograms
-  constexpr bool want_blk = kBlockMode;    // block comparator: per-block sums
-  // histograms of this workgroup's tokens; split 0 also clears the merged ones
-  for (int i = tid; i < kCTokens * kHistWords; i += kCThreads) shist[i] = 0u;
-  if (want_rec && split == 0) {
-    for (int i = tid; i < ntok * kFastBins; i += kCThreads) {
-      const int t = i / kFastBins;
-      a.hist_merged[(sel_tok0 + (int64_t)t * a.Hkv) * kSelWords + kSelHist1Off + (i - t * kFastBins)] = 0u;
+  constexpr bool want_rec = !kBlockMode;
+  if constexpr (want_rec) {
+    for (int i = tid; i < kTPW * kHistWords; i += kCThreads) shist[i] = 0u;
+    if (split == 0) {
+      for (int i = tid; i < ntok * kFastBins; i += kCThreads) {
+        const int t = i / kFastBins;
+        a.hist_merged[(sel_tok0 + (int64_t)t * a.Hkv) * kSelWords + kSelHist1Off + (i - t * kFastBins)] = 0u;
+      }
     }
   }
 
-  // Q fragments (A operand): query tile Qt = 2*wave + qt, row li -> token 2Qt + li/8,
-  // head li%8; dims 32s + 8grp
-  bf16x8_t qf[2][4];
+  // this lane's query row in tile qt: r = 32 wave + 16 qt + w16 = (token, head slot)
+  int tokl[2], head[2];
+  bool valid[2];       // a present token and a real head
+  int32_t pj[2];       // last visible position of the token (positions < cap < 2^31)
+  int32_t w0j[2];      // first window position (candidates are < w0j)
+  bf16x8_t qf[2][4];   // Q^T fragments (B operand): dims 32s + 8grp of the lane's query row
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    const int tl = 2 * (2 * wave + qt) + (li >> 3);   // token within the workgroup
-    const int h = li & 7;
-    const bool ok = tl < ntok && h < a.G;
-    const uint16_t* qh = a.q + (((int64_t)b * a.Lq + tok0 + tl) * a.Hq + (int64_t)g * a.G + h) * kHeadDim + 8 * grp;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      qf[qt][s] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(qh + 32 * s) : make_uint4(0u, 0u, 0u, 0u));
-  }
-  // per accumulator row (qt, v): token, head, visibility limits
-  int tokl[2];        // token of the lane's rows in tile qt (within the workgroup)
-  int32_t pj[2];      // last visible position of that token (positions < cap < 2^31)
-  int32_t w0j[2];     // first window position (candidates are < w0j)
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    tokl[qt] = 2 * (2 * wave + qt) + (grp >> 1);
+    const int r = 32 * wave + 16 * qt + w16;
+    tokl[qt] = r / kGp;
+    head[qt] = r % kGp;
+    valid[qt] = tokl[qt] < ntok && head[qt] < a.G;
     const int64_t pp = ctx - a.Lq + tok0 + tokl[qt];
     pj[qt] = (int32_t)pp;
-    int64_t w0 = pp + 1 - a.window;
+    const int64_t w0 = pp + 1 - a.window;
     w0j[qt] = (int32_t)(w0 < 0 ? 0 : w0);
+    const uint16_t* qh = a.q + (((int64_t)b * a.Lq + tok0 + tokl[qt]) * a.Hq + (int64_t)g * a.G + head[qt]) * kHeadDim +
+                         8 * grp;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qf[qt][s] = as_bf16x8(valid[qt] ? *reinterpret_cast<const uint4*>(qh + 32 * s) : make_uint4(0u, 0u, 0u, 0u));
   }
-
-  // record scale: U = the largest running maximum over the token's heads, c_v =
-  // 2^(m_v - U) for this lane's 4 heads (0 for head slots >= G)
-  const int hbase = 4 * (grp & 1);   // heads of this lane's accumulator rows: hbase .. hbase+3
-  float U[2], c[2][4];
 
   const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
   const uint8_t* kb = a.k + head_row0 * 256;
   const uint8_t* vb = a.v + head_row0 * 256;
 
-  f32x4_t o[2][8];
-  float m[2][4], z[2][4];
+  f32x4_t o[2][8];     // O^T: dims 16 bb + 4 grp + v of the lane's query row
+  float m[2], z[2];    // running maximum (log2 units, equal in the 4 row groups), this lane's share of Z
+  float U[2], c[2];    // record scale: U = the token's largest running maximum, c = 2^(m - U) (0: no head)
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
 #pragma unroll
     for (int d = 0; d < 8; ++d) o[qt][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      m[qt][v] = kMFloor;   // finite, so exp2(l - m) needs no -inf test
-      z[qt][v] = 0.0f;
-    }
+    m[qt] = kMFloor;   // finite, so exp2(l - m) needs no -inf test
+    z[qt] = 0.0f;
   }
-  update_record_scale(m, hbase, a.G, U, c);
-  __syncthreads();
+  auto record_scale = [&]() {
+    float mv[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) mv[qt] = valid[qt] ? m[qt] : kMFloor;
+    token_maxes<kGp>(mv, U);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) c[qt] = valid[qt] ? fast_exp2(m[qt] - U[qt]) : 0.0f;
+  };
+  if constexpr (want_rec) record_scale();
 
   const int nit = p_end > p_begin ? (int)((p_end - p_begin + kCPos - 1) / kCPos) : 0;
   const int32_t last = (int32_t)(p_end - 1);
-  // this thread's share of a tile load: rows (tid >> 4) + 32r, 16 bytes at (tid & 15)
+  // this thread's share of a tile load: rows (tid >> 4) + 32 r, 16 bytes at (tid & 15)
   const int lrow = tid >> 4, lcol = (tid & 15) * 16;
   // (named registers, not arrays: small arrays live across the loop got placed in
   // LDS / scratch by the compiler)
@@ -234,259 +309,263 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
     vr0 = *reinterpret_cast<const uint4*>(vb + (uint64_t)row0 * 256 + lcol);
     vr1 = *reinterpret_cast<const uint4*>(vb + (uint64_t)row1 * 256 + lcol);
   };
-  if (nit > 0) load_tiles((int32_t)p_begin);
+  auto store_tiles = [&](uint8_t* st) {
+    *reinterpret_cast<uint4*>(st + lrow * kKRow + lcol) = kr0;
+    *reinterpret_cast<uint4*>(st + (lrow + 32) * kKRow + lcol) = kr1;
+    *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + lcol) = vr0;
+    *reinterpret_cast<uint4*>(st + kKTile + (lrow + 32) * kVRow + lcol) = vr1;
+  };
+  if (nit > 0) {
+    load_tiles((int32_t)p_begin);
+    store_tiles(lds);
+    load_tiles((int32_t)p_begin + kCPos);
+  }
+  __syncthreads();   // stage 0 and the cleared histograms are ready
+  const float sl2 = a.scale_log2;
+  const int32_t first_pj = (int32_t)(ctx - a.Lq + tok0);   // the workgroup's first token sees least
+
   for (int it = 0; it < nit; ++it) {
     const int32_t P0 = (int32_t)p_begin + it * kCPos;
-    __syncthreads();   // every wave is done with the previous tiles
-    *reinterpret_cast<uint4*>(ktile + lrow * kKRow + lcol) = kr0;
-    *reinterpret_cast<uint4*>(ktile + (lrow + 32) * kKRow + lcol) = kr1;
-    *reinterpret_cast<uint4*>(vtile + lrow * kKRow + lcol) = vr0;
-    *reinterpret_cast<uint4*>(vtile + (lrow + 32) * kKRow + lcol) = vr1;
-    __syncthreads();
-    // next tiles: in flight during this iteration's compute (the last iteration
-    // re-reads clamped rows; no branch, so the loads are not sunk into one)
-    load_tiles(P0 + kCPos);
+    const uint8_t* ks = lds + (it & 1) * kStage;
+    const uint8_t* vs = ks + kKTile;
+    // the next iteration's tiles into the other stage (its last readers finished the
+    // previous iteration before the barrier that ended it), then the loads after them
+    store_tiles(lds + ((it + 1) & 1) * kStage);
+    load_tiles(P0 + 2 * kCPos);
 
-    // ---- S = Q K^T for 2 query tiles x 4 position tiles
-    f32x4_t sacc[2][4];
+    // ---- S^T = K Q^T for 4 position tiles x 2 query tiles
+    f32x4_t sacc[4][2];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       bf16x8_t kf[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(ktile + (pt * 16 + li) * kKRow + 64 * s + 16 * grp));
+        kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(ks + (pt * 16 + w16) * kKRow + 64 * s + 16 * grp));
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
         f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) d = mfma16(qf[qt][s], kf[s], d);
-        sacc[qt][pt] = d;
+        for (int s = 0; s < 4; ++s) d = mfma16(kf[s], qf[qt][s], d);
+        sacc[pt][qt] = d;
       }
     }
-    // raw scores q.k; the log2-domain logit is l = scale_log2 * s (scale_log2 > 0, so
-    // maxima can be taken on s), formed inside the exp2 as fma(s, scale_log2, -m).  The
-    // causal mask of each row's token only where some position lies beyond the first
-    // token's (wave-uniform branch)
-    const float sl2 = a.scale_log2;
+    // raw scores; the log2-domain logit is scale_log2 * s (scale_log2 > 0), formed
+    // inside the exp2 as fma(s, scale_log2, -m).  The causal mask only where some
+    // position lies beyond the first token's last visible one (wave-uniform branch).
     float l[2][4][4];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) l[qt][pt][v] = sacc[qt][pt][v];
-    if ((int64_t)P0 + kCPos - 1 > ctx - a.Lq + tok0) {
+        for (int v = 0; v < 4; ++v) l[qt][pt][v] = sacc[pt][qt][v];
+    if (P0 + kCPos - 1 > first_pj) {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          const bool vis = P0 + pt * 16 + li <= pj[qt];
+        for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) l[qt][pt][v] = vis ? l[qt][pt][v] : kNegInf;
-        }
+          for (int v = 0; v < 4; ++v)
+            l[qt][pt][v] = P0 + pt * 16 + 4 * grp + v <= pj[qt] ? l[qt][pt][v] : kNegInf;
     }
 
-    // ---- online softmax per query row.  The running maximum m only needs raising
-    // when some logit exceeds m + 8: a per-lane test and one ballot per step; the
-    // exact row maximum (DPP over the row group) only on that rare path.
+    // ---- online softmax per query row: a lane test and one ballot per iteration; the
+    // exact row maximum (over the 4 row groups) only on the rare raise
     {
-      float x[2][4];
+      float x[2];
       bool up_any = false;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < 2; ++qt) {
+        float mx = kNegInf;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          x[qt][v] = fmaxf(fmaxf(l[qt][0][v], l[qt][1][v]), fmaxf(l[qt][2][v], l[qt][3][v])) * sl2;
-          up_any |= x[qt][v] > m[qt][v] + kCSlack;
-        }
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) mx = fmaxf(mx, l[qt][pt][v]);
+        x[qt] = mx * sl2;
+        up_any |= x[qt] > m[qt] + kCSlack;
+      }
       if (wave_any(up_any)) {
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+        for (int qt = 0; qt < 2; ++qt) {
+          const float mx = across_groups<true>(x[qt]);
+          const bool up = mx > m[qt] + kCSlack;
+          const float mn = up ? mx : m[qt];
+          const float alpha = up ? fast_exp2(m[qt] - mn) : 1.0f;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float mx = max16(x[qt][v]);
-            const bool up = mx > m[qt][v] + kCSlack;
-            const float mn = up ? mx : m[qt][v];
-            const float alpha = up ? fast_exp2(m[qt][v] - mn) : 1.0f;
-#pragma unroll
-            for (int d = 0; d < 8; ++d) o[qt][d][v] *= alpha;
-            z[qt][v] *= alpha;
-            m[qt][v] = mn;
-          }
-        update_record_scale(m, hbase, a.G, U, c);
+          for (int d = 0; d < 8; ++d) o[qt][d] *= alpha;
+          z[qt] *= alpha;
+          m[qt] = mn;
+        }
+        if constexpr (want_rec) record_scale();
       }
     }
 
-    // ---- P V, one half of the positions at a time
-    float bsum[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // this block's sums
-    uint32_t tinybits = 0;   // bit 2qt + hf: this lane's record sum fell below 2^-100 (this half)
+    // ---- probabilities, records / block sums, P^T V^T per 32-position block
+    float bsum[2] = {0.f, 0.f};
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      // P of position tiles 2hf, 2hf+1 -> LDS [position][query row], high part and residual
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      float p[2][2][4];   // [qt][tile of the block][v]
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        float rs[2];   // this lane's 4 heads' share of the record sums of tiles 2hf, 2hf+1
+      for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const int pt = 2 * hf + pp;
-          float p[4];
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            p[v] = fast_exp2(__builtin_fmaf(l[qt][pt][v], sl2, -m[qt][v]));   // m finite: -inf gives 0
-            z[qt][v] += p[v];
-            if constexpr (want_blk) bsum[qt][v] += p[v];
+            const float x = fast_exp2(__builtin_fmaf(l[qt][2 * kb2 + tt][v], sl2, -m[qt]));   // -inf -> 0
+            p[qt][tt][v] = x;
+            z[qt] += x;
+            if constexpr (kBlockMode) bsum[qt] += x;
           }
-          if constexpr (want_rec) rs[pp] = p[0] * c[qt][0] + p[1] * c[qt][1] + p[2] * c[qt][2] + p[3] * c[qt][3];
-          const uint32_t h01 = pack_bf16(p[0], p[1]);
-          const uint32_t h23 = pack_bf16(p[2], p[3]);
-          const uint32_t r01 = pack_bf16(p[0] - __uint_as_float(h01 << 16), p[1] - __uint_as_float(h01 & 0xFFFF0000u));
-          const uint32_t r23 = pack_bf16(p[2] - __uint_as_float(h23 << 16), p[3] - __uint_as_float(h23 & 0xFFFF0000u));
-          uint8_t* dst = pst + (pp * 16 + li) * kPRow + 2 * (qt * 16 + 4 * grp);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(h01, h23);
-          *reinterpret_cast<uint2*>(dst + kPHalf) = make_uint2(r01, r23);
-        }
-        if constexpr (want_rec) {
-          // Records e = U + log2 sum_h p_h 2^(m_h - U) over the token's 8 heads (4 in this
-          // lane, 4 in the partner row group).  Even row groups finish tile 2hf, odd ones
-          // tile 2hf+1: each lane sends its partner the share of the tile the partner
-          // finishes, so one swap serves both tiles and every lane writes one record.  A
-          // sum below 2^-100 (terms lost to underflow could matter there) is not counted
-          // here and is redone exactly below.
-          const int own = grp & 1;
-          const float sum = (own ? rs[1] : rs[0]) + partner(own ? rs[0] : rs[1]);
-          const int32_t pos = P0 + (2 * hf + own) * 16 + li;
-          const int tl = tokl[qt];
-          const bool live = pos <= pj[qt] && tl < ntok;
-          const bool tiny = live && sum < 0x1p-100f;
-          tinybits |= tiny ? (1u << (2 * qt + hf)) : 0u;
-          const float e = U[qt] + __builtin_amdgcn_logf(sum);
-          if (live) {
-            const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)e);
-            a.records[(sel_tok0 + (int64_t)tl * a.Hkv) * a.logit_stride + pos] = rec;
-            if (!tiny && pos < w0j[qt]) {
-              const uint32_t bin = half_order_key(rec) >> kFastShift;
-              atomicAdd(&shist[tl * kHistWords + (bin >> 1)], (bin & 1) ? 65536u : 1u);
-            }
-          }
-        }
-      }
       if constexpr (want_rec) {
-        // exact records of this half where the sum underflowed (rare: logits 100 log2
-        // units below the running maxima); every lane takes part in exact_record's swaps
-        if (wave_any(tinybits != 0u)) {
+        // records of the block's 32 positions: per (token, position) the sum over the
+        // token's heads of c p, reduce-scattered over the head lanes so that every lane
+        // ends with one record (rec_slot), then the exact form where a sum underflowed
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt) {
-            const uint32_t bit = 1u << (2 * qt + hf);
-            if (!wave_any((tinybits & bit) != 0u)) continue;
-            float l0[4], l1[4];
+        for (int pass = 0; pass < kRecPassesOf<kGp>; ++pass) {
+        float x[kRecVals];
+#pragma unroll
+        for (int i = 0; i < kRecVals; ++i) {
+          const RecSlot rs = rec_slot<kGp>(i, pass);
+          x[i] = kGp == 32 ? p[0][rs.tt][rs.v] * c[0] + p[1][rs.tt][rs.v] * c[1] : p[rs.qt][rs.tt][rs.v] * c[rs.qt];
+        }
+        const float sum = reduce_scatter<kGp>(x, w16);
+        const RecSlot own = rec_slot<kGp>(own_index<kGp>(w16), pass);
+        const int32_t pos = P0 + (2 * kb2 + own.tt) * 16 + 4 * grp + own.v;
+        const int tl = own.qt ? tokl[1] : tokl[0];
+        const bool live = rec_writer<kGp>(w16) && pos <= (own.qt ? pj[1] : pj[0]) && tl < ntok;
+        const bool tiny = live && !(sum >= 0x1p-100f);
+        float e = (own.qt ? U[1] : U[0]) + __builtin_amdgcn_logf(sum);
+        if (wave_any(tiny)) {
+          // exact: max and sum of 2^(l - max) over the token's heads, for every value of
+          // the lane (all-reduce: every lane takes part in the DPP reductions)
+          float ex_own = 0.0f;
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              l0[v] = l[qt][2 * hf][v] * sl2;
-              l1[v] = l[qt][2 * hf + 1][v] * sl2;
-            }
-            const float ex0 = exact_record(l0, hbase, a.G);
-            const float ex1 = exact_record(l1, hbase, a.G);
-            const int own = grp & 1;
-            if (tinybits & bit) {   // implies a visible position of a present token
-              const int32_t pos = P0 + (2 * hf + own) * 16 + li;
-              const int tl = tokl[qt];
-              const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)(own ? ex1 : ex0));
-              a.records[(sel_tok0 + (int64_t)tl * a.Hkv) * a.logit_stride + pos] = rec;
-              if (pos < w0j[qt]) {
-                const uint32_t bin = half_order_key(rec) >> kFastShift;
-                atomicAdd(&shist[tl * kHistWords + (bin >> 1)], (bin & 1) ? 65536u : 1u);
+              float lv[2], rmax[2], ex[2], sums[2];
+#pragma unroll
+              for (int qt = 0; qt < 2; ++qt) lv[qt] = valid[qt] ? l[qt][2 * kb2 + tt][v] * sl2 : kNegInf;
+              token_maxes<kGp>(lv, rmax);
+#pragma unroll
+              for (int qt = 0; qt < 2; ++qt) {
+                rmax[qt] = fmaxf(rmax[qt], kMFloor);   // finite: exp2 of -inf is 0
+                ex[qt] = fast_exp2(lv[qt] - rmax[qt]);
+              }
+              token_sums<kGp>(ex, sums);
+#pragma unroll
+              for (int qt = 0; qt < 2; ++qt) {
+                const bool mine = own.tt == tt && own.v == v && (kGp == 32 || own.qt == qt);
+                ex_own = mine ? rmax[qt] + __builtin_amdgcn_logf(sums[qt]) : ex_own;
               }
             }
+          e = tiny ? ex_own : e;
+        }
+        if (live) {
+          const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)e);
+          a.records[(sel_tok0 + (int64_t)tl * a.Hkv) * a.logit_stride + pos] = rec;
+          if (pos < (own.qt ? w0j[1] : w0j[0])) {
+            const uint32_t bin = half_order_key(rec) >> kFastShift;
+            atomicAdd(&shist[tl * kHistWords + (bin >> 1)], (bin & 1) ? 65536u : 1u);
           }
-          tinybits = 0u;
+        }
         }
       }
-      // A operands: P[query row li][positions 8grp .. 8grp+7] of this half
+      // B operands: P^T of the block, k slot 8 grp + u <-> tile u / 4, position 4 grp + u % 4
       bf16x8_t ph[2], pl[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        const uint8_t* p0 = pst + (8 * grp + (li >> 2)) * kPRow + 2 * (qt * 16 + 4 * (li & 3));
-        const uint8_t* p1 = p0 + 4 * kPRow;
-        ph[qt] = tr_pair(p0, p1);
-        pl[qt] = tr_pair(p0 + kPHalf, p1 + kPHalf);
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float x0 = p[qt][u >> 1][2 * (u & 1)];
+          const float x1 = p[qt][u >> 1][2 * (u & 1) + 1];
+          hw[u] = pack_bf16(x0, x1);
+          lw[u] = pack_bf16(x0 - __uint_as_float(hw[u] << 16), x1 - __uint_as_float(hw[u] & 0xFFFF0000u));
+        }
+        ph[qt] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        pl[qt] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
-      // B operands: V[positions 32hf + 8grp .. +7][dims 16d + li]
+      // A operands: V^T of dim block d, rows 4grp..4grp+3 of the block's two tiles
+      const uint8_t* tr0 = vs + (32 * kb2 + 4 * grp + (w16 >> 2)) * kVRow + 8 * (w16 & 3);
+      const uint8_t* tr1 = tr0 + 16 * kVRow;
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        const uint8_t* v0 = vtile + (32 * hf + 8 * grp + (li >> 2)) * kKRow + 2 * (16 * d + 4 * (li & 3));
-        const bf16x8_t vf = tr_pair(v0, v0 + 4 * kKRow);
+        const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tr0 + 32 * d));
+        const s16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tr1 + 32 * d));
+        const uint2 w0 = __builtin_bit_cast(uint2, x0);
+        const uint2 w1 = __builtin_bit_cast(uint2, x1);
+        const bf16x8_t av = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-          o[qt][d] = mfma16(ph[qt], vf, o[qt][d]);
-          o[qt][d] = mfma16(pl[qt], vf, o[qt][d]);
+          o[qt][d] = mfma16(av, ph[qt], o[qt][d]);
+          o[qt][d] = mfma16(av, pl[qt], o[qt][d]);
         }
       }
     }
-    if constexpr (want_blk) {
+    if constexpr (kBlockMode) {
       // log2 of the sum of 2^logit over this 64-position block, per (token, head)
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        float lse[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float x = bsum[qt][v];
-          x += dpp<kDppXor1>(x);
-          x += dpp<kDppXor2>(x);
-          x += dpp<kDppMirror8>(x);
-          x += dpp<kDppRor8>(x);
-          lse[v] = m[qt][v] + __builtin_amdgcn_logf(x);   // -inf for an empty block
-        }
-        const int tl = tokl[qt];
-        if (li == 0 && tl < ntok) {
-          float* dst = a.blse + ((sel_tok0 + (int64_t)tl * a.Hkv) * a.blse_stride + P0 / kCPos) * 8 + 4 * (grp & 1);
-          *reinterpret_cast<float4*>(dst) = make_float4(lse[0], lse[1], lse[2], lse[3]);
-        }
+        const float sum = across_groups<false>(bsum[qt]);
+        const float lse = m[qt] + __builtin_amdgcn_logf(sum);   // -inf for an empty block
+        if (grp == 0 && valid[qt])
+          a.blse[((sel_tok0 + (int64_t)tokl[qt] * a.Hkv) * a.blse_stride + P0 / kCPos) * 8 + head[qt]] = lse;
       }
     }
+    __syncthreads();   // every wave is done with this stage; the next one is stored
   }
 
-  // ---- partials per (token, head): rows 4grp+v of tile qt
+  // ---- partials per (token, head): O^T dims 16 d + 4 grp .. +3 of the lane's query row
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    const int tl = tokl[qt];
+    const float zz = across_groups<false>(z[qt]);
+    if (valid[qt]) {
+      float* pp = a.part + (((sel_tok0 + (int64_t)tokl[qt] * a.Hkv) * a.n_split + split) * a.G + head[qt]) *
+                               kPartStride;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float zz = z[qt][v];
-      zz += dpp<kDppXor1>(zz);
-      zz += dpp<kDppXor2>(zz);
-      zz += dpp<kDppMirror8>(zz);
-      zz += dpp<kDppRor8>(zz);
-      const int h = 4 * (grp & 1) + v;
-      if (tl < ntok && h < a.G) {
-        float* pp = a.part + (((sel_tok0 + (int64_t)tl * a.Hkv) * a.n_split + split) * a.G + h) * kPartStride;
-#pragma unroll
-        for (int d = 0; d < 8; ++d) pp[4 + 16 * d + li] = o[qt][d][v];
-        if (li == 0) {
-          pp[0] = m[qt][v] == kMFloor ? kNegInf : m[qt][v];   // no visible position: -inf
-          pp[1] = zz;
-        }
+      for (int d = 0; d < 8; ++d)
+        *reinterpret_cast<float4*>(pp + 4 + 16 * d + 4 * grp) =
+            make_float4(o[qt][d][0], o[qt][d][1], o[qt][d][2], o[qt][d][3]);
+      if (grp == 0) {
+        pp[0] = m[qt] == kMFloor ? kNegInf : m[qt];   // no visible position: -inf
+        pp[1] = zz;
       }
     }
   }
   // ---- per-token key histograms of this split
-  if (!want_rec) return;
-  __syncthreads();
-  for (int i = tid; i < ntok * kHistWords; i += kCThreads) {
-    const int t = i / kHistWords;
-    const int w = i - t * kHistWords;
-    reinterpret_cast<uint32_t*>(a.hist_part + ((sel_tok0 + (int64_t)t * a.Hkv) * a.n_split + split) * kFastBins)[w] =
-        shist[i];
+  if constexpr (want_rec) {
+    __syncthreads();
+    for (int i = tid; i < ntok * kHistWords; i += kCThreads) {
+      const int t = i / kHistWords;
+      const int w = i - t * kHistWords;
+      reinterpret_cast<uint32_t*>(a.hist_part + ((sel_tok0 + (int64_t)t * a.Hkv) * a.n_split + split) * kFastBins)[w] =
+          shist[i];
+    }
   }
+}
+
+template <int kGp>
+dim3 chunk_grid(const ScanArgs& a, int B) {
+  return dim3(a.n_split * ((a.Lq + tokens_per_wg<kGp>() - 1) / tokens_per_wg<kGp>()), a.Hkv, B);
 }
 
 }  // namespace
 
+// Block mode (per-block sums, 8 head slots) for G <= 8 only; token mode for G <= 32.
 hipError_t launch_chunk_mfma(const ScanArgs& a, int B, hipStream_t st) {
-  dim3 grid(a.n_split * ((a.Lq + kCTokens - 1) / kCTokens), a.Hkv, B);
-  if (a.blse != nullptr)
-    hipLaunchKernelGGL((chunk_mfma_kernel<true>), grid, dim3(kCThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((chunk_mfma_kernel<false>), grid, dim3(kCThreads), 0, st, a);
+  if (a.blse != nullptr) {
+    if (a.G > 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((chunk_mfma_kernel<8, true>), chunk_grid<8>(a, B), dim3(kCThreads), 0, st, a);
+  } else if (a.G <= 8) {
+    hipLaunchKernelGGL((chunk_mfma_kernel<8, false>), chunk_grid<8>(a, B), dim3(kCThreads), 0, st, a);
+  } else if (a.G <= 16) {
+    hipLaunchKernelGGL((chunk_mfma_kernel<16, false>), chunk_grid<16>(a, B), dim3(kCThreads), 0, st, a);
+  } else if (a.G <= 32) {
+    hipLaunchKernelGGL((chunk_mfma_kernel<32, false>), chunk_grid<32>(a, B), dim3(kCThreads), 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -24,15 +24,18 @@ constexpr int kDppXor3 = 0x1B;   // quad_perm [3,2,1,0]
 constexpr int kDppMirror8 = 0x141;  // row_half_mirror: lane i <-> 7-i inside each 8
 constexpr int kDppRor8 = 0x128;  // row_ror:8: lane i <-> i^8 inside each 16
 
+// Every lane has a source lane under these permutations, so bound_ctrl (read 0 from a
+// missing source) changes nothing; it lets the compiler fold the move into the VALU
+// instruction that consumes it (v_add_f32_dpp, v_max_f32_dpp, ...).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
 }
 
 // Streaming loads with the non-temporal hint (global_load ... nt): data read once is
@@ -76,12 +79,13 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool high) {
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts inside each row
+// (a lane without a source lane adds 0)
 // of 16 lanes, then the row totals (lanes 15, 31, 47) are added to the later rows.
 __device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);   // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);   // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);   // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
   const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
   const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
   const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);

@@ -129,7 +129,7 @@ hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool, int B, hipStr
   return hipSuccess;
 }
 hipError_t launch_chunk_mfma(const ScanArgs& a, int B, hipStream_t) {
-  if (a.G > kSlots) fail("chunk kernel: more than 8 heads per KV head");
+  if (a.G > kMaxHeads || (a.blse != nullptr && a.G > kSlots)) fail("chunk kernel: head slots");
   check_scan(a, B, a.blse == nullptr);
   return hipSuccess;
 }

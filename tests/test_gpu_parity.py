@@ -274,9 +274,36 @@ def test_wide_group_sparse_paths(fused):
 
 
 def test_mqa_query_chunk():
-    """MQA with several query tokens: the decode scan once per token."""
+    """MQA with several query tokens (6 of the chunk kernel's 8 token slots for 32
+    heads); every token compared."""
     w = wl.Workload("mqa chunk", 2, 6, 32, 1, ctx_lens=[2600, 5000], n_needles=8, seed=2520)
     run_and_compare(w, "mqa-chunk")
+
+
+@pytest.mark.parametrize("hq,hkv,lq,ctx", [(32, 1, 64, [7000, 3000]), (64, 4, 64, [5000]), (12, 1, 40, [4100]),
+                                           (24, 2, 17, [3000, 9000]), (32, 1, 64, [64, 6000])])
+def test_wide_group_chunks(hq, hkv, lq, ctx):
+    """More than 8 query heads per KV head on the chunk kernel: 16 tokens of 16 head slots
+    (G = 16, and G = 12 with 4 empty slots) or 8 tokens of 32 (MQA, G = 24) per workgroup;
+    64-token chunks (several token groups per split), partial groups, and a chunk whose
+    context is the chunk itself.  Every token compared."""
+    w = wl.Workload(f"wide chunk G{hq // hkv}", len(ctx), lq, hq, hkv, ctx_lens=ctx, n_needles=8,
+                    seed=2600 + hq + lq)
+    got, _ = run_and_compare(w, f"wide-chunk-G{hq // hkv}-lq{lq}")
+    if min(ctx) == lq:   # the chunk is the whole context: every visible position, ascending
+        for j in range(lq):
+            assert got["idx"][0, j, 0, :j + 1].tolist() == list(range(j + 1))
+
+
+def test_mqa_chunk_full_config_sample():
+    """The MQA variant of the ragged 64-token chunk at full size (16 sequences, contexts
+    8K-512K, 32 query heads on one KV head) in the benchmark's launch configuration:
+    all 64 tokens of the shortest sequence and both edge tokens of the longest."""
+    w = wl.standard_workloads()["mqa_chunk"]
+    inp = wl.make_inputs(w, threads=16)
+    order = np.argsort(inp["ctx_len"])
+    tokens = [(int(order[0]), j) for j in range(64)] + [(int(order[-1]), 0), (int(order[-1]), 63)]
+    run_and_compare(w, "mqa-chunk-full", tokens=tokens, inp=inp)
 
 
 def test_wide_group_logits_path_unsupported():
