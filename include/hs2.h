@@ -95,7 +95,8 @@ typedef struct hs2_attn_desc {
   int32_t sparse_split_len; /* index entries per sparse-gather workgroup: 0 = automatic,
                              else rounded up to a multiple of 32                          */
   int32_t cand_workgroups;  /* candidate-stage workgroups over all selection rows:
-                             0 = automatic (4096), else at least one per row              */
+                             0 = automatic (4096; from 256 rows on, 2 per row), else at
+                             least one per row                                            */
 } hs2_attn_desc;
 
 /* hs2_attn_desc.flags */

@@ -19,6 +19,7 @@ constexpr int kScanTargetWorkgroups = 768;   // 3 per CU (3 waves/SIMD) on 256 C
 constexpr int kMfmaTargetWorkgroups = 256;   // matrix-core scan: 1 per CU (8 waves)
 constexpr int64_t kFusedSparseRows = 256;    // sparse layer: one workgroup per row from here
 constexpr int kCandTargetWorkgroups = 4096;  // candidate stage: workgroups over all rows
+constexpr int kCandTwoStepPerRow = 2;         // the two-kernel form (many rows): workgroups per row
 constexpr double kMaxLogitsBytes = 16.0 * (1 << 30);   // logits-path workspace budget
 constexpr int kMaxSplits = 2048;             // combine kernel keeps one weight per split in LDS
 constexpr int kChunkMaxSplit = 4096;         // positions per chunk-kernel split (at most)
@@ -453,8 +454,9 @@ static hs2_status full_select_launch(const hs2_attn_desc* desc, const Layout& L,
     fa.chunk_len = L.cand_chunk_len;
     // workgroups per row: all chunks of a row while rows are few (decode), fewer once
     // there are many rows, so short rows do not launch mostly empty workgroups
-    const int64_t per_row =
-        ceil_div(desc->cand_workgroups > 0 ? desc->cand_workgroups : kCandTargetWorkgroups, L.n_sel);
+    const int64_t per_row = desc->cand_workgroups > 0 ? ceil_div(desc->cand_workgroups, L.n_sel)
+                            : L.n_sel >= kTwoStepMinRows ? kCandTwoStepPerRow
+                                                         : ceil_div(kCandTargetWorkgroups, L.n_sel);
     fa.cand_wgs = (int32_t)std::max<int64_t>(1, std::min<int64_t>(L.n_cchunks, per_row));
     fa.n_sel = (int32_t)L.n_sel;
     fa.Lq = desc->q_len;

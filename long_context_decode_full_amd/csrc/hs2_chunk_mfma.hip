@@ -240,9 +240,9 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   if constexpr (want_rec) {
     for (int i = tid; i < kTPW * kHistWords; i += kCThreads) shist[i] = 0u;
     if (split == 0) {
-      for (int i = tid; i < ntok * kFastBins; i += kCThreads) {
-        const int t = i / kFastBins;
-        a.hist_merged[(sel_tok0 + (int64_t)t * a.Hkv) * kSelWords + kSelHist1Off + (i - t * kFastBins)] = 0u;
+      for (int i = tid; i < ntok * kMergedWords; i += kCThreads) {
+        const int t = i / kMergedWords;
+        a.hist_merged[(sel_tok0 + (int64_t)t * a.Hkv) * kSelWords + kSelHist1Off + (i - t * kMergedWords)] = 0u;
       }
     }
   }

@@ -25,13 +25,20 @@ constexpr int kFastShift = 6;
 constexpr int kHistMergeSplits = 16;  // per-split histograms summed by one combine workgroup
 constexpr int kCandChunkLen = 16384;  // record path: most positions per candidate workgroup
 constexpr int kMinCandChunkLen = 2048;  // fewest (a power of two in between is chosen per call)
+constexpr int kTwoStepMinRows = 256;  // record path: rows from which candidates take two kernels
 constexpr int kMaxFastChunks = 8192;  // positions per row <= kMaxFastChunks * kCandChunkLen
 // Per-selection control block (u32 words): [0,16) state, [16,20) pass tickets,
-// [32, 32+2048) first histogram.  The logits path clears it in the combine kernel;
-// the record path's scan clears the kFastBins words of the merged key histogram.
+// [32, 32+2048) first histogram.  The logits path clears it in the combine kernel.
+// The record path keeps the merged key histogram at [32, 32+kFastBins) and, after it,
+// the kFastSubBins-way histogram of the keys inside the threshold bin; its scan clears
+// those kMergedWords words.
 constexpr int kSelCounterOff = 16;
 constexpr int kSelHist1Off = 32;
 constexpr int kSelWords = kSelHist1Off + (kFastBins > kHist1Bins ? kFastBins : kHist1Bins);
+constexpr int kFastSubBins = 1 << kFastShift;  // key values per histogram bin
+constexpr int kSelSubOff = kSelHist1Off + kFastBins;
+constexpr int kMergedWords = kFastBins + kFastSubBins;
+static_assert(kSelSubOff + kFastSubBins <= kSelWords, "control block too small");
 constexpr int kMaxBlocksLds = 16384;  // block mode: blocks per row held in LDS
 constexpr int kMaxRecordSplit = 16384; // records mode: positions per scan workgroup (LDS bound)
 
@@ -46,7 +53,8 @@ enum StateWord {
   kStWinCount = 6,   // collect: winners appended
   kStBndCount = 7,   // collect: boundary entries appended (may exceed the cap)
   kStKK = 8,         // number of global positions to select
-  kStLambda = 9,     // record path: fp32 bits of the candidate threshold
+  kStFastBin = 10,   // record path: histogram bin of the k-th largest record key
+  kStFastAbove = 11, // record path: records in the bins above it
 };
 
 struct ScanArgs {

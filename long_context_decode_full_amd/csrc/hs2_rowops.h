@@ -113,13 +113,11 @@ __device__ __forceinline__ void load_query(const uint16_t* qgroup, int G, int r,
   const int hown = head_of(r);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
+    // branch-free: a slot past the group reads head 0 (in bounds) and keeps zeros
     const int head = i ^ hown;
-    if (head < G) {
-      const uint4 x = *reinterpret_cast<const uint4*>(qgroup + head * kHeadDim + 8 * r);
-      qp[i][0] = x.x; qp[i][1] = x.y; qp[i][2] = x.z; qp[i][3] = x.w;
-    } else {
-      qp[i][0] = qp[i][1] = qp[i][2] = qp[i][3] = 0u;
-    }
+    const bool in = head < G;
+    const uint4 x = *reinterpret_cast<const uint4*>(qgroup + (in ? head : 0) * kHeadDim + 8 * r);
+    qp[i][0] = in ? x.x : 0u; qp[i][1] = in ? x.y : 0u; qp[i][2] = in ? x.z : 0u; qp[i][3] = in ? x.w : 0u;
   }
 }
 

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 3) void scan_kernel(ScanArgs a) {
       for (int i = tid; i < kFastBins; i += kThreads) shist[i] = 0u;
       if (split == 0) {   // the combine kernel sums every split's histogram into these words
         uint32_t* hm = a.hist_merged + sel * kSelWords + kSelHist1Off;
-        for (int i = tid; i < kFastBins; i += kThreads) hm[i] = 0u;
+        for (int i = tid; i < kMergedWords; i += kThreads) hm[i] = 0u;
       }
       __syncthreads();
     }

@@ -502,7 +502,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_mfma_kernel(ScanArgs a) {
   if (tid == 0) step_next = kWaves;   // step w is wave w's first
   if (split == 0) {   // the combine kernel sums every split's histogram into these words
     uint32_t* hm = a.hist_merged + sel * kSelWords + kSelHist1Off;
-    for (int i = tid; i < kFastBins; i += kThreads) hm[i] = 0u;
+    for (int i = tid; i < kMergedWords; i += kThreads) hm[i] = 0u;
   }
   __syncthreads();
 

@@ -18,6 +18,9 @@
 //                     chunk) and re-scores them exactly by re-reading their keys
 //                     with the scan's own arithmetic (row_logit), so s is
 //                     bit-identical to the value the scan's logits would give.
+//                     From 256 rows on (chunks of query tokens) the stage runs as two
+//                     kernels instead, cand_filter_kernel and cand_rescore_kernel, that
+//                     take the exact k-th largest record in place of its bin's edges.
 //   final_kernel:     exact top-k of the candidates by (s desc, position asc): a
 //                     radix digit on the fp32 bit pattern of s (s >= 0 orders like
 //                     its bits) finds the bin of the k-th score, the entries of that
@@ -349,6 +352,285 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
       }
       if (a.G > 8) load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);   // next chunk: block 0
     }
+  }
+}
+
+// ------------------------------------------------------------------ two-step candidates
+// The same tests with the exact k-th largest record E_k in place of its histogram bin's
+// edges: the k-th largest score lies between 2^(E_k - u) min w and 2^(E_k + u) max w
+// (u = u(E_k)), so
+//   candidate:  e + u(e) + log2 max w  >=  E_k - u + log2 min w
+//   certain:    e - u(e) + log2 min w  >   E_k + u + log2 max w.
+// E_k is known only once every record of the row has been seen, hence two kernels
+// over the same (row, chunk) work units:
+//   cand_filter_kernel:  keeps the positions that reach the bin-edge test (a superset,
+//                        since x - u(x) does not decrease with x), writes them with their
+//                        records, and counts the records inside the threshold bin by
+//                        their low key bits (kFastSubBins counters per row);
+//   cand_rescore_kernel: finds E_k from those counts, applies the two tests to the list
+//                        and re-scores the uncertain candidates.
+// The filter's list sits in the upper half of each chunk's key slots (32-bit entries:
+// record bits << 16 | chunk-relative position); keys are written from the bottom, and
+// a block of kRsBlk entries is read in full before its keys are written, so a key never
+// lands on an entry that is still to be read (key j < base + kRsBlk ends at byte
+// 8 (base + kRsBlk) <= 4 clen + 4 (base + kRsBlk), the start of the next block).
+constexpr int kRsBlk = 1024;   // list entries per re-score block
+constexpr int kRsPer = kRsBlk / kThreads;
+constexpr int kRsBatch = 8;    // wave steps (4 rows each) whose key loads are issued together
+constexpr int kRsBatchMB = 4;  // the same with more than 8 heads (per-row sums stay in registers)
+static_assert(kFastSubBins == 64, "one lane per sub-bin");
+static_assert(kMinCandChunkLen % kRsBlk == 0, "blocks tile a chunk");
+
+__device__ __forceinline__ void log_weight_range(const FastSelArgs& a, int64_t sel, float& lwmin, float& lwmax) {
+  lwmin = __builtin_huge_valf();
+  lwmax = -__builtin_huge_valf();
+  for (int h = 0; h < a.G; ++h) {
+    const float lw = __builtin_amdgcn_logf(a.mz[(sel * kMaxHeads + h) * 2 + 1]) - a.mz[(sel * kMaxHeads + h) * 2];
+    lwmin = fminf(lwmin, lw);
+    lwmax = fmaxf(lwmax, lw);
+  }
+}
+
+template <int R>   // records per thread: chunk_len / 256
+__global__ __launch_bounds__(kThreads) void cand_filter_kernel(FastSelArgs a) {
+  const int64_t sel = blockIdx.x / (uint32_t)a.cand_wgs;
+  const int wg = (int)(blockIdx.x % (uint32_t)a.cand_wgs);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const RowGeom rg = row_geom(a, sel);
+  if (rg.w0 <= a.topk || a.topk == 0) return;
+  constexpr int clen = R * kThreads;
+  if ((int64_t)wg * clen >= rg.w0) return;
+
+  __shared__ uint32_t sub[kFastSubBins];
+  __shared__ uint32_t wscan[kThreads / 64];
+  __shared__ uint32_t srec[kThreads][R / 2 + 1];   // this thread's records, for its hits
+  const uint16_t* rrow = a.records + sel * a.rec_stride;
+  uint32_t words[R / 2];
+  load_records<R>(words, rrow, (int64_t)wg * clen + (int64_t)tid * R, rg.w0);
+  if (tid < kFastSubBins) sub[tid] = 0u;
+  uint32_t* blk = sel_block(a, sel);
+  uint32_t tb, above;
+  block_threshold<kThreads, kFastBins / kThreads>(blk + kSelHist1Off, kFastBins, (uint32_t)a.topk, tb, above);
+  if (wg == 0 && tid == 0) {
+    blk[kStFastBin] = tb;
+    blk[kStFastAbove] = above;
+  }
+  float lwmin, lwmax;
+  log_weight_range(a, sel, lwmin, lwmax);
+  const uint32_t ebits = half_bits_of_key(tb << kFastShift);   // smallest record in the bin
+  const float thr = half_bits_to_float(ebits) - half_ulp(ebits) - (lwmax - lwmin) - 2.0f * kBoundSlack;
+
+  for (int chunk = wg; (int64_t)chunk * clen < rg.w0; chunk += a.cand_wgs) {
+    const int64_t c0 = (int64_t)chunk * clen;
+    const int64_t t0 = c0 + (int64_t)tid * R;
+    uint64_t hitmask = 0ull;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      hitmask |= (uint64_t)(t0 + i < rg.w0 && half_bits_to_float(rb) + half_ulp(rb) >= thr) << i;
+    }
+    if (hitmask != 0ull) {
+#pragma unroll
+      for (int i = 0; i < R / 2; ++i) srec[tid][i] = words[i];
+    }
+    const int64_t cn = c0 + (int64_t)a.cand_wgs * clen;   // this workgroup's next chunk
+    if (cn < rg.w0) load_records<R>(words, rrow, cn + (int64_t)tid * R, rg.w0);
+    const uint32_t mine = (uint32_t)__builtin_popcountll(hitmask);
+    const uint32_t x = wave_prefix_incl(mine);
+    __syncthreads();   // the previous chunk is done with wscan
+    if (lane == 63) wscan[wave] = x;
+    __syncthreads();
+    uint32_t ih = x - mine, total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      total += wscan[w];
+      ih += w < wave ? wscan[w] : 0u;
+    }
+    uint32_t* ent = reinterpret_cast<uint32_t*>(a.cand_keys + (sel * a.n_chunks + chunk) * (int64_t)clen) + clen;
+    uint64_t hm = hitmask;
+    while (hm) {
+      const int i = __builtin_ctzll(hm);
+      hm &= hm - 1;
+      const uint32_t rb = (srec[tid][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      ent[ih++] = (rb << 16) | (uint32_t)(tid * R + i);
+      const uint32_t key = half_order_key(rb);
+      if ((key >> kFastShift) == tb) atomicAdd(&sub[key & (kFastSubBins - 1)], 1u);
+    }
+    if (tid == 0) a.cand_count[sel * a.n_chunks + chunk] = (int32_t)total;
+  }
+  __syncthreads();
+  if (tid < kFastSubBins) {
+    const uint32_t c = sub[tid];
+    if (c != 0u) atomicAdd(blk + kSelSubOff + tid, c);
+  }
+}
+
+template <bool kFp8, bool kMB>
+__global__ __launch_bounds__(kThreads) void cand_rescore_kernel(FastSelArgs a) {
+  const int64_t sel = blockIdx.x / (uint32_t)a.cand_wgs;
+  const int wg = (int)(blockIdx.x % (uint32_t)a.cand_wgs);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const RowGeom rg = row_geom(a, sel);
+  if (rg.w0 <= a.topk || a.topk == 0) return;
+  const int clen = a.chunk_len;
+  if ((int64_t)wg * clen >= rg.w0) return;
+
+  __shared__ uint32_t ulist[kRsBlk];   // uncertain: key slot << 16 | chunk-relative position
+  __shared__ uint32_t wscan[kThreads / 64];
+  const int64_t bj = sel / a.Hkv;
+  const int g = (int)(sel - bj * a.Hkv);
+  const int b = (int)(bj / a.Lq);
+  const int r = lane & 15;
+  const int rgrp = lane >> 4;
+  const int hown = head_of(r);
+  uint32_t qp[8][4];
+  load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);
+  const float Mown = hown < a.G ? a.mz[(sel * kMaxHeads + hown) * 2] : 0.0f;
+  const float izown = hown < a.G ? a.mz[(sel * kMaxHeads + hown) * 2 + 1] : 0.0f;
+
+  // E_k: the sub-bins of the threshold bin from the top, one per lane
+  const uint32_t* blk = sel_block(a, sel);
+  const uint32_t tb = blk[kStFastBin];
+  const uint32_t need = (uint32_t)a.topk - blk[kStFastAbove];   // >= 1: the bin holds the k-th
+  const uint32_t cum = wave_prefix_incl(blk[kSelSubOff + (kFastSubBins - 1 - lane)]);
+  const uint64_t reach = __builtin_amdgcn_ballot_w64(cum >= need);
+  uint32_t e_lo, e_hi;   // binary16 bits bracketing E_k (equal once the counts are known)
+  if (reach != 0ull) {
+    e_lo = e_hi = half_bits_of_key((tb << kFastShift) | (uint32_t)(kFastSubBins - 1 - __builtin_ctzll(reach)));
+  } else {   // counts short of `need` cannot happen; the bin's edges remain valid bounds
+    e_lo = half_bits_of_key(tb << kFastShift);
+    e_hi = half_bits_of_key(((tb + 1) << kFastShift) - 1);
+  }
+  float lwmin, lwmax;
+  log_weight_range(a, sel, lwmin, lwmax);
+  const float thr = half_bits_to_float(e_lo) - half_ulp(e_lo) - (lwmax - lwmin) - 2.0f * kBoundSlack;
+  const float thr_in = half_bits_to_float(e_hi) + half_ulp(e_hi) + (lwmax - lwmin) + 2.0f * kBoundSlack;
+
+  const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
+  const uint8_t* kb = a.k + head_row0 * (kFp8 ? 128 : 256);
+  const float* ksb = kFp8 ? a.k_scale + head_row0 : nullptr;
+
+  for (int chunk = wg; (int64_t)chunk * clen < rg.w0; chunk += a.cand_wgs) {
+    const int64_t c0 = (int64_t)chunk * clen;
+    const int64_t slot0 = (sel * a.n_chunks + chunk) * (int64_t)clen;
+    const uint32_t* ent = reinterpret_cast<const uint32_t*>(a.cand_keys + slot0) + clen;
+    const uint32_t cnt = (uint32_t)a.cand_count[sel * a.n_chunks + chunk];
+    uint32_t outn = 0;
+    for (uint32_t base = 0; base < cnt; base += kRsBlk) {
+      // thread t classifies entries base + kRsPer t + i (position order is kept)
+      const uint32_t f0 = base + kRsPer * tid;
+      uint32_t ev[kRsPer];
+      if (f0 + kRsPer <= cnt) {
+        const uint4 v4 = *reinterpret_cast<const uint4*>(ent + f0);
+        ev[0] = v4.x; ev[1] = v4.y; ev[2] = v4.z; ev[3] = v4.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < kRsPer; ++i) ev[i] = f0 + i < cnt ? ent[f0 + i] : 0u;
+      }
+      uint32_t cm = 0u, um = 0u;
+#pragma unroll
+      for (int i = 0; i < kRsPer; ++i) {
+        const uint32_t rb = ev[i] >> 16;
+        const float e = half_bits_to_float(rb), u = half_ulp(rb);
+        const bool c = f0 + i < cnt && e + u >= thr;
+        cm |= (uint32_t)c << i;
+        um |= (uint32_t)(c && !(e - u > thr_in)) << i;
+      }
+      const uint32_t mine = (uint32_t)__builtin_popcount(cm) | ((uint32_t)__builtin_popcount(um) << 16);
+      const uint32_t x = wave_prefix_incl(mine);
+      __syncthreads();   // the previous block is done with ulist and wscan
+      if (lane == 63) wscan[wave] = x;
+      __syncthreads();   // every entry of this block has been read
+      uint32_t before = x - mine, total = 0;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) {
+        total += wscan[w];
+        before += w < wave ? wscan[w] : 0u;
+      }
+      uint32_t ic = outn + (before & 0xFFFFu), iu = before >> 16;
+#pragma unroll
+      for (int i = 0; i < kRsPer; ++i) {
+        if ((cm >> i) & 1u) {
+          const uint32_t pos = ev[i] & 0xFFFFu;
+          if ((um >> i) & 1u)
+            ulist[iu++] = (ic << 16) | pos;
+          else
+            a.cand_keys[slot0 + ic] = cand_key(0x7F800000u, (int32_t)(c0 + pos));   // certainly selected
+          ++ic;
+        }
+      }
+      __syncthreads();
+      const int nu = (int)(total >> 16);
+      // exact re-score: 4 rows per wave step, the scan's lane layout and arithmetic;
+      // the key loads of kRsBatch steps are issued before the first row is scored
+      if constexpr (!kMB) {
+        for (int i0 = wave * 4; i0 < nu; i0 += 16 * kRsBatch) {
+          RowData d[kRsBatch];
+          uint32_t ue[kRsBatch];
+#pragma unroll
+          for (int u = 0; u < kRsBatch; ++u) {
+            const int i = i0 + 16 * u + rgrp;
+            ue[u] = ulist[i < nu ? i : i0];   // past the end: a valid row, result dropped
+            load_key<kFp8>(kb, ksb, (uint32_t)(c0 + (ue[u] & 0xFFFFu)), r, d[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < kRsBatch; ++u) {
+            if (i0 + 16 * u < nu) {
+              const int i = i0 + 16 * u + rgrp;
+              const float l = row_logit<kFp8>(qp, d[u], a.scale_log2);
+              const float part = ((r & 1) == 0 && hown < a.G) ? fast_exp2(l - Mown) * izown : 0.0f;
+              const float s = rowgroup_sum16(part);
+              if (i < nu && r == 0)
+                a.cand_keys[slot0 + (ue[u] >> 16)] = cand_key(__float_as_uint(s), (int32_t)(c0 + (ue[u] & 0xFFFFu)));
+            }
+          }
+        }
+      } else {
+        // more than 8 heads: the batch's key rows stay in registers while the query
+        // blocks of 8 heads take turns; the group sum adds the blocks in order
+        const int nb = (a.G + 7) / 8;
+        for (int i0 = wave * 4; i0 < nu; i0 += 16 * kRsBatchMB) {
+          RowData d[kRsBatchMB];
+          uint32_t ue[kRsBatchMB];
+          float ssum[kRsBatchMB];
+#pragma unroll
+          for (int u = 0; u < kRsBatchMB; ++u) {
+            const int i = i0 + 16 * u + rgrp;
+            ue[u] = ulist[i < nu ? i : i0];
+            load_key<kFp8>(kb, ksb, (uint32_t)(c0 + (ue[u] & 0xFFFFu)), r, d[u]);
+            ssum[u] = 0.0f;
+          }
+          for (int hb = 0; hb < nb; ++hb) {
+            const int gb = min(8, a.G - 8 * hb);
+            load_query(a.q + (bj * a.Hq + (int64_t)g * a.G + 8 * hb) * kHeadDim, gb, r, qp);
+            const int hg = 8 * hb + hown;
+            const float Mb = hown < gb ? a.mz[(sel * kMaxHeads + hg) * 2] : 0.0f;
+            const float izb = hown < gb ? a.mz[(sel * kMaxHeads + hg) * 2 + 1] : 0.0f;
+#pragma unroll
+            for (int u = 0; u < kRsBatchMB; ++u) {
+              if (i0 + 16 * u < nu) {   // wave-uniform
+                const float l = row_logit<kFp8>(qp, d[u], a.scale_log2);
+                const float part = ((r & 1) == 0 && hown < gb) ? fast_exp2(l - Mb) * izb : 0.0f;
+                const float sb = rowgroup_sum16(part);
+                ssum[u] = hb == 0 ? sb : ssum[u] + sb;
+              }
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kRsBatchMB; ++u) {
+            const int i = i0 + 16 * u + rgrp;
+            if (i0 + 16 * u < nu && i < nu && r == 0)
+              a.cand_keys[slot0 + (ue[u] >> 16)] = cand_key(__float_as_uint(ssum[u]), (int32_t)(c0 + (ue[u] & 0xFFFFu)));
+          }
+        }
+      }
+      outn += total & 0xFFFFu;
+    }
+    if (tid == 0) a.cand_count[sel * a.n_chunks + chunk] = (int32_t)outn;
   }
 }
 
@@ -723,6 +1005,21 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
 }  // namespace
 
 template <bool kFp8>
+void launch_two_step(const FastSelArgs& a, hipStream_t st) {
+  const dim3 grid((uint32_t)((uint64_t)a.cand_wgs * (uint64_t)a.n_sel));
+  switch (a.chunk_len / kThreads) {
+    case 8: hipLaunchKernelGGL((cand_filter_kernel<8>), grid, dim3(kThreads), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((cand_filter_kernel<16>), grid, dim3(kThreads), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((cand_filter_kernel<32>), grid, dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((cand_filter_kernel<64>), grid, dim3(kThreads), 0, st, a); break;
+  }
+  if (a.G > 8)
+    hipLaunchKernelGGL((cand_rescore_kernel<kFp8, true>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((cand_rescore_kernel<kFp8, false>), grid, dim3(kThreads), 0, st, a);
+}
+
+template <bool kFp8>
 void launch_candidates_r(const FastSelArgs& a, hipStream_t st) {
   const dim3 grid((uint32_t)((uint64_t)a.cand_wgs * (uint64_t)a.n_sel));
   if (a.G > 8) {
@@ -743,10 +1040,16 @@ void launch_candidates_r(const FastSelArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st) {
-  if (fp8)
+  if (a.n_sel >= kTwoStepMinRows) {
+    if (fp8)
+      launch_two_step<true>(a, st);
+    else
+      launch_two_step<false>(a, st);
+  } else if (fp8) {
     launch_candidates_r<true>(a, st);
-  else
+  } else {
     launch_candidates_r<false>(a, st);
+  }
   return hipGetLastError();
 }
 
