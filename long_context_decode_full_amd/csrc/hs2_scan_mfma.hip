@@ -213,7 +213,22 @@ struct HeadState {
   f32x4_t o[8];   // o[b][v]: dim 16b + 4grp + v of head w16
   float m;        // running maximum of head w16 (log2 domain; equal in the 4 groups)
   float z;        // this lane's share of the softmax denominator
+  float c;        // records: 2^(m - U) for a head of the group, else 0
 };
+
+// Reduce-scatter of 8 values over the 8 lanes w16 & 7 of a half-row: lane i ends with
+// the sum over the 8 lanes of value i.  Each step keeps the half of the values named by
+// one lane bit and adds the partner's copy of it (partners i^7, i^2, i^1: the bit
+// differs, so the two keep complementary halves).
+__device__ __forceinline__ float reduce_scatter8(const float (&x)[8], int w16) {
+  const bool b2 = (w16 & 4) != 0, b1 = (w16 & 2) != 0, b0 = (w16 & 1) != 0;
+  float y[4], z[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) y[j] = (b2 ? x[j + 4] : x[j]) + dpp<kDppMirror8>(b2 ? x[j] : x[j + 4]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) z[j] = (b1 ? y[j + 2] : y[j]) + dpp<kDppXor2>(b1 ? y[j] : y[j + 2]);
+  return (b0 ? z[1] : z[0]) + dpp<kDppXor1>(b0 ? z[0] : z[1]);
+}
 
 // Max / sum over all 16 lanes w16 of each 16-lane row.
 __device__ __forceinline__ float max16w(float x) {
@@ -234,7 +249,7 @@ template <bool kFp8, bool kGather = false, int kHB = 1, bool kWide = false>
 __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x8_t (&qf)[kHB][4], uint8_t* vt,
                                              int32_t base, int32_t w_begin, int32_t w_end, uint32_t cand_span,
                                              float scale_log2, int G, int grp, int w16, int lane,
-                                             uint16_t* recs, uint32_t* shist, HeadState (&hs)[kHB],
+                                             uint16_t* recs, uint32_t* shist, HeadState (&hs)[kHB], float& U,
                                              const int32_t* srow = nullptr) {
   // V tile -> LDS (row-major, padded rows)
   if constexpr (kFp8) {
@@ -315,17 +330,20 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
       hs[hb].z *= alpha;
       hs[hb].m = mn;
     }
+    if constexpr (!kGather) {
+      // U: the largest running maximum of the group's heads (equal in every lane), and
+      // the record scale of each head; they change only with a running maximum
+      U = kNegInf;
+#pragma unroll
+      for (int hb = 0; hb < kHB; ++hb) U = fmaxf(U, 16 * hb + w16 < G ? hs[hb].m : kNegInf);
+      U = kWide ? max16w(U) : max8(U);
+#pragma unroll
+      for (int hb = 0; hb < kHB; ++hb) hs[hb].c = 16 * hb + w16 < G ? fast_exp2(hs[hb].m - U) : 0.0f;
+    }
   }
   bf16x8_t phi[kHB], plo[kHB];
   float rsum[2][4];                     // records: sum over this lane's head blocks of p 2^(m - U)
-  float U = kNegInf, c[kHB];
   if constexpr (!kGather) {
-    // U: the largest running maximum of the group's heads (equal in every lane)
-#pragma unroll
-    for (int hb = 0; hb < kHB; ++hb) U = fmaxf(U, 16 * hb + w16 < G ? hs[hb].m : kNegInf);
-    U = kWide ? max16w(U) : max8(U);
-#pragma unroll
-    for (int hb = 0; hb < kHB; ++hb) c[hb] = 16 * hb + w16 < G ? fast_exp2(hs[hb].m - U) : 0.0f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -340,7 +358,7 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
       for (int v = 0; v < 4; ++v) {
         p[t][v] = l[hb][t][v] != kNegInf ? fast_exp2(l[hb][t][v] - hs[hb].m) : 0.0f;
         hs[hb].z += p[t][v];
-        if constexpr (!kGather) rsum[t][v] = fmaf(p[t][v], c[hb], rsum[t][v]);
+        if constexpr (!kGather) rsum[t][v] = fmaf(p[t][v], hs[hb].c, rsum[t][v]);
         // masked rows: the scale may come from a row past the end (4-row scale loads)
         if constexpr (kFp8) p[t][v] = l[hb][t][v] != kNegInf ? p[t][v] * s.vs[t][v] : 0.0f;
       }
@@ -358,22 +376,26 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
   }
 
   // bound records: e = log2 sum over the group's heads of 2^l.  With p = 2^(l - m) of
-  // each head (formed above for P.V), sum_h 2^l_h = 2^U sum_h p_h 2^(m_h - U); a live
-  // row whose sum is below 2^-100 (terms lost to underflow could matter there) makes
-  // the wave take the direct form, max then sum of 2^(l - max), for the step.
+  // each head (formed above for P.V), sum_h 2^l_h = 2^U sum_h p_h 2^(m_h - U).  The 8
+  // row sums of a lane are reduce-scattered over the head lanes (the two half-rows
+  // added first when the group spans 16 lanes), so lane w16 < 8 owns row w16 of its
+  // row group: one logarithm, one record store and one histogram count per lane.  A
+  // live row whose sum is below 2^-100 (terms lost to underflow could matter there)
+  // makes the wave take the direct form, max then sum of 2^(l - max), for the step.
   if constexpr (!kGather) {
-    float e[2][4];
-    bool tiny = false;
+    float x[8];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float sm = kWide ? sum16w(rsum[t][v]) : sum8(rsum[t][v]);
-        const int32_t row = base + 16 * t + 4 * grp + v;
-        tiny |= row < w_end && !(sm >= 0x1p-100f);
-        e[t][v] = U + __builtin_amdgcn_logf(sm);
-      }
-    if (wave_any(tiny)) {
+    for (int i = 0; i < 8; ++i) {
+      x[i] = rsum[i >> 2][i & 3];
+      if constexpr (kWide) x[i] += dpp<kDppRor8>(x[i]);
+    }
+    const float sm = reduce_scatter8(x, w16);
+    const int io = w16 & 7;   // own row: tile io >> 2, v = io & 3
+    const int32_t row_o = base + 16 * (io >> 2) + 4 * grp + (io & 3);
+    const bool writer = w16 < 8 && row_o < w_end;
+    float e = U + __builtin_amdgcn_logf(sm);
+    if (wave_any(writer && !(sm >= 0x1p-100f))) {
+      // every lane takes part in the reductions; each keeps its own row's value
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -390,21 +412,16 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
 #pragma unroll
           for (int hb = 0; hb < kHB; ++hb) ex += lm[hb] != kNegInf ? fast_exp2(lm[hb] - rmax) : 0.0f;
           const float sum = kWide ? sum16w(ex) : sum8(ex);
-          e[t][v] = rmax + __builtin_amdgcn_logf(sum);
+          const float ed = rmax + __builtin_amdgcn_logf(sum);
+          e = io == 4 * t + v ? ed : e;
         }
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int32_t row = base + 16 * t + 4 * grp + v;
-        const uint32_t rel = (uint32_t)(row - w_begin);
-        if (w16 == 0 && row < w_end) {
-          const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)e[t][v]);
-          recs[rel] = rec;
-          if (rel < cand_span) atomicAdd(&shist[half_order_key(rec) >> kFastShift], 1u);
-        }
-      }
+    if (writer) {
+      const uint32_t rel = (uint32_t)(row_o - w_begin);
+      const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)e);
+      recs[rel] = rec;
+      if (rel < cand_span) atomicAdd(&shist[half_order_key(rec) >> kFastShift], 1u);
+    }
   }
 
   // PV: A = V^T of dim block b, rows 4grp..4grp+3 of both tiles (transposed LDS reads)
@@ -513,7 +530,9 @@ __global__ __launch_bounds__(kThreads, 1) void scan_mfma_kernel(ScanArgs a) {
     for (int bb = 0; bb < 8; ++bb) hs[hb].o[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     hs[hb].m = kNegInf;
     hs[hb].z = 0.0f;
+    hs[hb].c = 0.0f;
   }
+  float U = kNegInf;
 
   if (nsteps > 0) {
     const int32_t last = w_end - 1;
@@ -536,12 +555,12 @@ __global__ __launch_bounds__(kThreads, 1) void scan_mfma_kernel(ScanArgs a) {
     // two-buffer ring; every load is issued (rows past the end re-read `last`)
     while (k0 < nsteps) {
       process_step<kFp8, false, kHB, kWide>(s0, qf, vt, w_begin + k0 * kStepRows, w_begin, w_end, cand_span,
-                                            a.scale_log2, a.G, grp, w16, lane, srec, shist, hs);
+                                            a.scale_log2, a.G, grp, w16, lane, srec, shist, hs, U);
       k0 = take();
       load_step<kFp8, kVecScale>(s0, kb, vb, ksb, vsb, w_begin + k0 * kStepRows, last, grp, w16, lane);
       if (k1 >= nsteps) break;
       process_step<kFp8, false, kHB, kWide>(s1, qf, vt, w_begin + k1 * kStepRows, w_begin, w_end, cand_span,
-                                            a.scale_log2, a.G, grp, w16, lane, srec, shist, hs);
+                                            a.scale_log2, a.G, grp, w16, lane, srec, shist, hs, U);
       k1 = take();
       load_step<kFp8, kVecScale>(s1, kb, vb, ksb, vsb, w_begin + k1 * kStepRows, last, grp, w16, lane);
     }
@@ -686,7 +705,9 @@ __global__ __launch_bounds__(kThreads, 1) void gather_mfma_kernel(ScanArgs a, fl
     for (int bb = 0; bb < 8; ++bb) hs[hb].o[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     hs[hb].m = kNegInf;
     hs[hb].z = 0.0f;
+    hs[hb].c = 0.0f;
   }
+  float U = kNegInf;   // unused here: gather steps form no records
 
   if (wave < nsteps) {
     // two-buffer ring over steps wave, wave + kWaves, ...; loads past the last step re-read it
@@ -697,12 +718,12 @@ __global__ __launch_bounds__(kThreads, 1) void gather_mfma_kernel(ScanArgs a, fl
     load_step_gather<kFp8>(s1, kb, vb, ksb, vsb, srow, min(k1, klast) * kStepRows, grp, w16, lane);
     while (k0 < nsteps) {
       process_step<kFp8, true, kHB, kWide>(s0, qf, vt, k0 * kStepRows, 0, 0, 0u, a.scale_log2, a.G, grp, w16, lane,
-                                           nullptr, nullptr, hs, srow);
+                                           nullptr, nullptr, hs, U, srow);
       k0 += 2 * kWaves;
       load_step_gather<kFp8>(s0, kb, vb, ksb, vsb, srow, min(k0, klast) * kStepRows, grp, w16, lane);
       if (k1 >= nsteps) break;
       process_step<kFp8, true, kHB, kWide>(s1, qf, vt, k1 * kStepRows, 0, 0, 0u, a.scale_log2, a.G, grp, w16, lane,
-                                           nullptr, nullptr, hs, srow);
+                                           nullptr, nullptr, hs, U, srow);
       k1 += 2 * kWaves;
       load_step_gather<kFp8>(s1, kb, vb, ksb, vsb, srow, min(k1, klast) * kStepRows, grp, w16, lane);
     }
