@@ -30,6 +30,8 @@
 //                     two more digits with ties taken in position order.
 #include "hs2_rowops.h"
 
+#include <type_traits>
+
 namespace hs2 {
 namespace {
 
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
     if (tid == kThreads - 1) total_s = before + mine;
     const int64_t slot0 = (sel * a.n_chunks + chunk) * (int64_t)clen;
     uint32_t ih = before & 0xFFFFu, iu = before >> 16;
-    uint64_t hm = hitmask;
+    uint64_t hm = (uint64_t)hitmask;
     while (hm) {
       const int i = __builtin_ctzll(hm);
       hm &= hm - 1;
@@ -421,23 +423,56 @@ __global__ __launch_bounds__(kThreads) void cand_filter_kernel(FastSelArgs a) {
   log_weight_range(a, sel, lwmin, lwmax);
   const uint32_t ebits = half_bits_of_key(tb << kFastShift);   // smallest record in the bin
   const float thr = half_bits_to_float(ebits) - half_ulp(ebits) - (lwmax - lwmin) - 2.0f * kBoundSlack;
+  // e + u(e) does not decrease with the record's order key, so the test e + u(e) >= thr
+  // holds exactly on the keys [kmin, key(+inf)] (binary search on that same expression);
+  // as binary16 bits that is one interval of non-negative codes [plo, phi] and, when
+  // kmin falls below +0, one of negative codes [0x8000, nhi]
+  uint32_t kmin;
+  {
+    uint32_t lo = 0u, hi = 0x10000u;   // the first key that passes lies in [lo, hi]
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      const uint32_t bm = half_bits_of_key(mid);
+      if (half_bits_to_float(bm) + half_ulp(bm) >= thr) hi = mid; else lo = mid + 1;
+    }
+    kmin = lo;   // 0x10000: none passes
+  }
+  constexpr uint32_t kPInf = 0x7C00u;   // binary16 +inf (NaN codes above it never pass)
+  const uint32_t plo = kmin >= 0x8000u ? kmin - 0x8000u : 0u;
+  const uint32_t pspan = plo <= kPInf ? kPInf - plo : 0xFFFFFFFFu;   // (code - plo) <= pspan
+  const bool pnone = kmin > 0xFC00u;                                 // not even +inf passes
+  const uint32_t nspan = kmin < 0x8000u ? 0x7FFFu - kmin : 0u;       // (code - 0x8000) <= nspan
+  const bool neg = kmin < 0x8000u;
+  typedef typename std::conditional<(R > 32), uint64_t, uint32_t>::type mask_t;
 
   for (int chunk = wg; (int64_t)chunk * clen < rg.w0; chunk += a.cand_wgs) {
     const int64_t c0 = (int64_t)chunk * clen;
     const int64_t t0 = c0 + (int64_t)tid * R;
-    uint64_t hitmask = 0ull;
+    mask_t hitmask = 0;
+    if (!pnone) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-      hitmask |= (uint64_t)(t0 + i < rg.w0 && half_bits_to_float(rb) + half_ulp(rb) >= thr) << i;
+      for (int i = 0; i < R; ++i) {
+        const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        hitmask |= rb - plo <= pspan ? ((mask_t)1 << i) : (mask_t)0;
+      }
+      if (neg) {   // workgroup-uniform: thresholds below +0 also take negative codes
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+          hitmask |= rb - 0x8000u <= nspan ? ((mask_t)1 << i) : (mask_t)0;
+        }
+      }
     }
+    // positions at or past w0 (their records read as zero) are not candidates
+    const int64_t nv = rg.w0 - t0;
+    if (nv < R) hitmask &= nv <= 0 ? (mask_t)0 : (mask_t)((((mask_t)1) << nv) - 1);
     if (hitmask != 0ull) {
 #pragma unroll
       for (int i = 0; i < R / 2; ++i) srec[tid][i] = words[i];
     }
     const int64_t cn = c0 + (int64_t)a.cand_wgs * clen;   // this workgroup's next chunk
     if (cn < rg.w0) load_records<R>(words, rrow, cn + (int64_t)tid * R, rg.w0);
-    const uint32_t mine = (uint32_t)__builtin_popcountll(hitmask);
+    const uint32_t mine = (uint32_t)__builtin_popcountll((uint64_t)hitmask);
     const uint32_t x = wave_prefix_incl(mine);
     __syncthreads();   // the previous chunk is done with wscan
     if (lane == 63) wscan[wave] = x;
@@ -449,7 +484,7 @@ __global__ __launch_bounds__(kThreads) void cand_filter_kernel(FastSelArgs a) {
       ih += w < wave ? wscan[w] : 0u;
     }
     uint32_t* ent = reinterpret_cast<uint32_t*>(a.cand_keys + (sel * a.n_chunks + chunk) * (int64_t)clen) + clen;
-    uint64_t hm = hitmask;
+    uint64_t hm = (uint64_t)hitmask;
     while (hm) {
       const int i = __builtin_ctzll(hm);
       hm &= hm - 1;
@@ -636,9 +671,7 @@ __global__ __launch_bounds__(kThreads) void cand_rescore_kernel(FastSelArgs a) {
 
 // ------------------------------------------------------------------ exact top-k + output
 constexpr int kFinThreads = 1024;
-constexpr int kFinWaves = kFinThreads / 64;
 constexpr int kFinStage = 12288;  // candidates staged in LDS (larger sets read global memory)
-constexpr int kFinRun = kFinStage / kFinThreads;   // consecutive candidates per thread
 constexpr int kFinBnd = 1024;     // threshold-bin entries ranked pairwise
 constexpr int kDigitBins = 4096;  // first radix digit: score bits 30..19
 constexpr int kFinChunkLds = kDigitBins / 2;   // chunks whose counts the general path keeps in lh
@@ -650,7 +683,11 @@ constexpr int kFinChunkLds = kDigitBins / 2;   // chunks whose counts the genera
 // and writes the chosen positions ascending with one block-wide scan, then the
 // window.  Candidate sets beyond the LDS stage or threshold bins beyond kFinBnd
 // entries take two more radix digits and resolve equal scores in position order.
+template <int kFinThreads, int kFinStage, int kFinBnd, int kMaxCh>
 __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
+  constexpr int kFinWaves = kFinThreads / 64;
+  // the per-chunk tie pass takes two chunks per thread, for up to kFinChunkLds chunks
+  static_assert((kMaxCh < kFinChunkLds ? kMaxCh : kFinChunkLds) <= 2 * kFinThreads, "tie pass covers the chunks");
   const int64_t sel = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -660,7 +697,7 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
   const int w0 = (int)rg.w0;
   int32_t* out = a.idx + sel * a.S;
 
-  __shared__ uint32_t pref[kMaxFastChunks + 1];
+  __shared__ uint32_t pref[kMaxCh + 1];
   __shared__ uint32_t lh[kDigitBins];
   __shared__ uint64_t st_key[kFinStage];
   __shared__ uint64_t bkey[kFinBnd];
@@ -683,7 +720,7 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
     const int nch = (w0 + clen - 1) / clen;
     const int32_t* cc = a.cand_count + sel * a.n_chunks;
     const int64_t lbase = sel * a.n_chunks * (int64_t)clen;
-    constexpr int kU = 4;   // chunks per wave in the single-round copy (64 = 16 waves x 4)
+    constexpr int kU = 64 / kFinWaves;   // chunks per wave in the single-round copy (64 in all)
     uint32_t m = 0;
     bool staged;
     if (nch <= kFinWaves * kU) {
@@ -1054,7 +1091,8 @@ hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st
 }
 
 hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(final_kernel, dim3(a.n_sel), dim3(kFinThreads), 0, st, a);
+  hipLaunchKernelGGL((final_kernel<kFinThreads, kFinStage, kFinBnd, kMaxFastChunks>), dim3(a.n_sel),
+                     dim3(kFinThreads), 0, st, a);
   return hipGetLastError();
 }
 
