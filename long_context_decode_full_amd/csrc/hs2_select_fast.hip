@@ -150,6 +150,58 @@ __device__ __forceinline__ void load_records(uint32_t (&words)[R / 2], const uin
   }
 }
 
+// Records that pass a test which does not decrease with the record's value (e + u(e)
+// >= thr, e - u(e) > thr: both hold from some order key on): the first passing key by a
+// binary search on the test itself, then, as binary16 codes, one interval of
+// non-negative codes [plo, +inf] and, when that key falls below +0, one interval of
+// negative codes [0x8000, 0xFFFF - kmin].  NaN codes (above +inf) never pass.
+struct CodeRange {
+  uint32_t plo, pspan, nspan;
+  bool none, neg;
+};
+template <class Pass>
+__device__ __forceinline__ CodeRange code_range(Pass pass) {
+  uint32_t lo = 0u, hi = 0x10000u;   // the first passing key lies in [lo, hi] (0x10000: none)
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (pass(half_bits_of_key(mid))) hi = mid; else lo = mid + 1;
+  }
+  constexpr uint32_t kPInf = 0x7C00u;
+  CodeRange c;
+  c.plo = lo >= 0x8000u ? lo - 0x8000u : 0u;
+  c.none = lo > 0xFC00u;   // not even +inf passes
+  c.pspan = c.plo <= kPInf ? kPInf - c.plo : 0u;
+  c.neg = lo < 0x8000u;
+  c.nspan = c.neg ? 0x7FFFu - lo : 0u;
+  return c;
+}
+// Bit i set where record i of the R (packed two per word) lies in the range.
+template <int R, typename mask_t>
+__device__ __forceinline__ mask_t range_mask(const uint32_t (&words)[R / 2], const CodeRange& c) {
+  mask_t m = 0;
+  if (!c.none) {   // workgroup-uniform
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      m |= rb - c.plo <= c.pspan ? ((mask_t)1 << i) : (mask_t)0;
+    }
+    if (c.neg) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        m |= rb - 0x8000u <= c.nspan ? ((mask_t)1 << i) : (mask_t)0;
+      }
+    }
+  }
+  return m;
+}
+// The first `nv` of R bits (positions before w0).
+template <int R, typename mask_t>
+__device__ __forceinline__ mask_t valid_mask(int64_t nv) {
+  if (nv >= R) return ~(mask_t)0 >> (8 * sizeof(mask_t) - R);
+  return nv <= 0 ? (mask_t)0 : (mask_t)((((mask_t)1) << nv) - 1);
+}
+
 // ------------------------------------------------------------------ candidates + exact re-score
 // Work unit: one (row, chunk of chunk_len positions); workgroup w of a row takes its
 // chunks w, w + cand_wgs, ... (blockIdx.x = row * cand_wgs + w; the grid is sized so
@@ -228,6 +280,8 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   // The certain test pays off where candidates are dense: rows whose candidate range
   // is short next to top-k (row-uniform); long rows have a few per workgroup.
   const bool use_cert = rg.w0 < (int64_t)a.topk * 64;
+  const CodeRange cand_r = code_range([&](uint32_t h) { return half_bits_to_float(h) + half_ulp(h) >= thr; });
+  const CodeRange cert_r = code_range([&](uint32_t h) { return half_bits_to_float(h) - half_ulp(h) > thr_in; });
 
   const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
   const uint8_t* kb = a.k + head_row0 * (kFp8 ? 128 : 256);
@@ -241,23 +295,9 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
     // block-wide exclusive scan of the per-thread counts keeps position order.
     const int64_t t0 = c0 + (int64_t)tid * R;
     if (!kPrefetch && chunk != wg) load_records<R>(words, rrow, t0, rg.w0);
-    uint64_t hitmask = 0ull, certmask = 0ull;
-    if (use_cert) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-        const float e = half_bits_to_float(rb), u = half_ulp(rb);
-        const bool hit = t0 + i < rg.w0 && e + u >= thr;
-        hitmask |= (uint64_t)hit << i;
-        certmask |= (uint64_t)(hit && e - u > thr_in) << i;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-        hitmask |= (uint64_t)(t0 + i < rg.w0 && half_bits_to_float(rb) + half_ulp(rb) >= thr) << i;
-      }
-    }
+    // positions at or past w0 (their records read as zero) are not candidates
+    const uint64_t hitmask = range_mask<R, uint64_t>(words, cand_r) & valid_mask<R, uint64_t>(rg.w0 - t0);
+    const uint64_t certmask = use_cert ? hitmask & range_mask<R, uint64_t>(words, cert_r) : 0ull;
     const uint64_t uncmask = hitmask & ~certmask;
     if constexpr (kPrefetch) {   // this chunk's records are consumed: load the next chunk's
       const int64_t cn = c0 + (int64_t)a.cand_wgs * clen;
@@ -423,50 +463,15 @@ __global__ __launch_bounds__(kThreads) void cand_filter_kernel(FastSelArgs a) {
   log_weight_range(a, sel, lwmin, lwmax);
   const uint32_t ebits = half_bits_of_key(tb << kFastShift);   // smallest record in the bin
   const float thr = half_bits_to_float(ebits) - half_ulp(ebits) - (lwmax - lwmin) - 2.0f * kBoundSlack;
-  // e + u(e) does not decrease with the record's order key, so the test e + u(e) >= thr
-  // holds exactly on the keys [kmin, key(+inf)] (binary search on that same expression);
-  // as binary16 bits that is one interval of non-negative codes [plo, phi] and, when
-  // kmin falls below +0, one of negative codes [0x8000, nhi]
-  uint32_t kmin;
-  {
-    uint32_t lo = 0u, hi = 0x10000u;   // the first key that passes lies in [lo, hi]
-    while (lo < hi) {
-      const uint32_t mid = (lo + hi) >> 1;
-      const uint32_t bm = half_bits_of_key(mid);
-      if (half_bits_to_float(bm) + half_ulp(bm) >= thr) hi = mid; else lo = mid + 1;
-    }
-    kmin = lo;   // 0x10000: none passes
-  }
-  constexpr uint32_t kPInf = 0x7C00u;   // binary16 +inf (NaN codes above it never pass)
-  const uint32_t plo = kmin >= 0x8000u ? kmin - 0x8000u : 0u;
-  const uint32_t pspan = plo <= kPInf ? kPInf - plo : 0xFFFFFFFFu;   // (code - plo) <= pspan
-  const bool pnone = kmin > 0xFC00u;                                 // not even +inf passes
-  const uint32_t nspan = kmin < 0x8000u ? 0x7FFFu - kmin : 0u;       // (code - 0x8000) <= nspan
-  const bool neg = kmin < 0x8000u;
+  const CodeRange cr = code_range([&](uint32_t h) { return half_bits_to_float(h) + half_ulp(h) >= thr; });
   typedef typename std::conditional<(R > 32), uint64_t, uint32_t>::type mask_t;
 
   for (int chunk = wg; (int64_t)chunk * clen < rg.w0; chunk += a.cand_wgs) {
     const int64_t c0 = (int64_t)chunk * clen;
     const int64_t t0 = c0 + (int64_t)tid * R;
-    mask_t hitmask = 0;
-    if (!pnone) {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-        hitmask |= rb - plo <= pspan ? ((mask_t)1 << i) : (mask_t)0;
-      }
-      if (neg) {   // workgroup-uniform: thresholds below +0 also take negative codes
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const uint32_t rb = (words[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-          hitmask |= rb - 0x8000u <= nspan ? ((mask_t)1 << i) : (mask_t)0;
-        }
-      }
-    }
     // positions at or past w0 (their records read as zero) are not candidates
-    const int64_t nv = rg.w0 - t0;
-    if (nv < R) hitmask &= nv <= 0 ? (mask_t)0 : (mask_t)((((mask_t)1) << nv) - 1);
-    if (hitmask != 0ull) {
+    const mask_t hitmask = range_mask<R, mask_t>(words, cr) & valid_mask<R, mask_t>(rg.w0 - t0);
+    if (hitmask != 0) {
 #pragma unroll
       for (int i = 0; i < R / 2; ++i) srec[tid][i] = words[i];
     }
