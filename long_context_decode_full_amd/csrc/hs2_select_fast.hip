@@ -129,7 +129,9 @@ __device__ __forceinline__ int32_t key_pos(uint64_t key) {
   return 0x7FFFFFFF - (int32_t)(uint32_t)key;
 }
 
-// Records t0 .. t0 + R - 1 of a row (zero past w0) as R/2 packed words.
+// Records t0 .. t0 + R - 1 of a row as R/2 packed words; slots at or past `limit` (the
+// row's record slots, or the candidate range) read as zero.  Records past w0 are stale
+// (a row's scan writes only its visible positions); the tests mask them off.
 template <int R>
 __device__ __forceinline__ void load_records(uint32_t (&words)[R / 2], const uint16_t* __restrict__ rrow,
                                              int64_t t0, int64_t w0) {
@@ -222,10 +224,15 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  constexpr int clen = R * kThreads;
+  const uint16_t* rrow = a.records + sel * a.rec_stride;
+  // The first chunk's records do not wait for the row's length: the loads cover the
+  // row's record slots and the tests below mask the positions at or past w0.
+  uint32_t words[R / 2];
+  load_records<R>(words, rrow, (int64_t)wg * clen + (int64_t)tid * R, a.rec_stride);
   const RowGeom rg = row_geom(a, sel);
   if (rg.w0 <= a.topk || a.topk == 0) return;
-  constexpr int clen = R * kThreads;
-  // chunks at or past the first window position hold no candidate (and are not read)
+  // chunks at or past the first window position hold no candidate
   if ((int64_t)wg * clen >= rg.w0) return;
 
   __shared__ uint16_t cpos[clen];    // chunk-relative positions of the candidates
@@ -242,13 +249,9 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   const int hown = head_of(r);
   uint32_t qp[8][4];   // issued early: its latency overlaps the threshold and the filter
   load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);
-  const uint16_t* rrow = a.records + sel * a.rec_stride;
-  // The first chunk's records are loaded before the threshold is found (their latency
-  // overlaps it); with R <= 32 the next chunk's records are loaded while the current
-  // chunk re-scores (a row's workgroup takes its chunks in turn in the chunk config).
+  // With R <= 32 the next chunk's records are loaded while the current chunk re-scores
+  // (a row's workgroup takes its chunks in turn when rows are many).
   constexpr bool kPrefetch = R <= 32;
-  uint32_t words[R / 2];
-  load_records<R>(words, rrow, (int64_t)wg * clen + (int64_t)tid * R, rg.w0);
 
   // threshold: bin of the k-th largest record key in the merged histogram
   uint32_t tb, above;
@@ -294,14 +297,14 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
     // Each thread owns R consecutive positions (one batch of 16-byte loads); a
     // block-wide exclusive scan of the per-thread counts keeps position order.
     const int64_t t0 = c0 + (int64_t)tid * R;
-    if (!kPrefetch && chunk != wg) load_records<R>(words, rrow, t0, rg.w0);
+    if (!kPrefetch && chunk != wg) load_records<R>(words, rrow, t0, a.rec_stride);
     // positions at or past w0 (their records read as zero) are not candidates
     const uint64_t hitmask = range_mask<R, uint64_t>(words, cand_r) & valid_mask<R, uint64_t>(rg.w0 - t0);
     const uint64_t certmask = use_cert ? hitmask & range_mask<R, uint64_t>(words, cert_r) : 0ull;
     const uint64_t uncmask = hitmask & ~certmask;
     if constexpr (kPrefetch) {   // this chunk's records are consumed: load the next chunk's
       const int64_t cn = c0 + (int64_t)a.cand_wgs * clen;
-      if (cn < rg.w0) load_records<R>(words, rrow, cn + (int64_t)tid * R, rg.w0);
+      if (cn < rg.w0) load_records<R>(words, rrow, cn + (int64_t)tid * R, a.rec_stride);
     }
     // block exclusive scan of (hits, uncertain hits), packed in one word (each < 2^16)
     const uint32_t mine = (uint32_t)__builtin_popcountll(hitmask) | ((uint32_t)__builtin_popcountll(uncmask) << 16);
@@ -440,17 +443,17 @@ __global__ __launch_bounds__(kThreads) void cand_filter_kernel(FastSelArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  constexpr int clen = R * kThreads;
+  const uint16_t* rrow = a.records + sel * a.rec_stride;
+  uint32_t words[R / 2];   // issued before the row's length is known (see candidate_kernel)
+  load_records<R>(words, rrow, (int64_t)wg * clen + (int64_t)tid * R, a.rec_stride);
   const RowGeom rg = row_geom(a, sel);
   if (rg.w0 <= a.topk || a.topk == 0) return;
-  constexpr int clen = R * kThreads;
   if ((int64_t)wg * clen >= rg.w0) return;
 
   __shared__ uint32_t sub[kFastSubBins];
   __shared__ uint32_t wscan[kThreads / 64];
   __shared__ uint32_t srec[kThreads][R / 2 + 1];   // this thread's records, for its hits
-  const uint16_t* rrow = a.records + sel * a.rec_stride;
-  uint32_t words[R / 2];
-  load_records<R>(words, rrow, (int64_t)wg * clen + (int64_t)tid * R, rg.w0);
   if (tid < kFastSubBins) sub[tid] = 0u;
   uint32_t* blk = sel_block(a, sel);
   uint32_t tb, above;
@@ -476,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void cand_filter_kernel(FastSelArgs a) {
       for (int i = 0; i < R / 2; ++i) srec[tid][i] = words[i];
     }
     const int64_t cn = c0 + (int64_t)a.cand_wgs * clen;   // this workgroup's next chunk
-    if (cn < rg.w0) load_records<R>(words, rrow, cn + (int64_t)tid * R, rg.w0);
+    if (cn < rg.w0) load_records<R>(words, rrow, cn + (int64_t)tid * R, a.rec_stride);
     const uint32_t mine = (uint32_t)__builtin_popcountll((uint64_t)hitmask);
     const uint32_t x = wave_prefix_incl(mine);
     __syncthreads();   // the previous chunk is done with wscan
@@ -697,6 +700,25 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int clen = a.chunk_len;
+  const int32_t* cc = a.cand_count + sel * a.n_chunks;
+  const int64_t lbase = sel * a.n_chunks * (int64_t)clen;
+  // Up to 64 chunks a row: every wave reads the 64 counts and, speculatively, the first
+  // 64 keys of its chunks wave, wave + kFinWaves, ... (the slots exist whether or not
+  // they hold candidates), before the row's length is known; what lies past the row's
+  // candidate chunks is dropped below.
+  constexpr int kU = 64 / kFinWaves;
+  const bool one_round = a.n_chunks <= kFinWaves * kU;
+  uint32_t cnt_s = 0u;
+  uint64_t kv[kU];
+  if (one_round) {
+    cnt_s = lane < a.n_chunks ? (uint32_t)cc[lane] : 0u;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = wave + u * kFinWaves;
+      kv[u] = c < a.n_chunks ? a.cand_keys[lbase + (int64_t)c * clen + lane] : 0ull;
+    }
+  }
   const RowGeom rg = row_geom(a, sel);
   const int n = (int)rg.n;
   const int w0 = (int)rg.w0;
@@ -721,24 +743,11 @@ __global__ __launch_bounds__(kFinThreads) void final_kernel(FastSelArgs a) {
       nbnd = 0u;
       kth = ~0ull;
     }
-    const int clen = a.chunk_len;
     const int nch = (w0 + clen - 1) / clen;
-    const int32_t* cc = a.cand_count + sel * a.n_chunks;
-    const int64_t lbase = sel * a.n_chunks * (int64_t)clen;
-    constexpr int kU = 64 / kFinWaves;   // chunks per wave in the single-round copy (64 in all)
     uint32_t m = 0;
     bool staged;
-    if (nch <= kFinWaves * kU) {
-      // one round of loads: every wave reads the 64 counts and, speculatively, the
-      // first 64 keys of its chunks wave, wave + 16, ... (slots exist whether or
-      // not they hold candidates)
-      const uint32_t cnt = lane < nch ? (uint32_t)cc[lane] : 0u;
-      uint64_t kv[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int c = wave + u * kFinWaves;
-        kv[u] = c < nch ? a.cand_keys[lbase + (int64_t)c * clen + lane] : 0ull;
-      }
+    if (one_round) {   // nch <= n_chunks <= 64
+      const uint32_t cnt = lane < nch ? cnt_s : 0u;
       const uint32_t incl = wave_prefix_incl(cnt);
       m = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
       if (wave == 0) {
