@@ -107,11 +107,13 @@ enum {
    * in the last fp32 bits (idx never does).  With this flag `out` is bitwise
    * reproducible; the scan is ~3% slower. */
   HS2_FLAG_DETERMINISTIC = 1u << 0,
-  /* Token selection on the logits path (every logit kept, exact radix select) even
-   * when probs is NULL.  For comparing the two selection paths. */
+  /* Selection on the logits path (every logit kept; token mode: exact radix select,
+   * block mode: block sums of the per-position s) even when probs is NULL.  For
+   * comparing the selection paths.  Without it, block mode at up to 8 query heads per
+   * KV head sums the blocks inside the context scan. */
   HS2_FLAG_FORCE_LOGITS = 1u << 1,
   /* The record path's context scan on the VALU kernel (dot2 + DPP) instead of the
-   * matrix cores.  For comparing the two scans. */
+   * matrix cores (block mode: the logits path).  For comparing the two scans. */
   HS2_FLAG_SCAN_VALU = 1u << 2,
   /* Query chunks (q_len > 1) run the decode scan once per query token instead of the
    * matrix-core chunk kernel. */

@@ -43,8 +43,11 @@ struct Layout {
   bool fast_ok = false;                         // record path usable for this descriptor
   bool logits_ok = false;                       // logits path (probs, block mode) fits its budget
   size_t off_records = 0;
-  size_t off_blse = 0;                          // chunk block mode: per-block sums
+  size_t off_blse = 0;                          // block mode: per-block sums
   int64_t blse_stride = 0;
+  int32_t blse_gran = 0;                        // positions per block sum
+  size_t off_bcand = 0;                         // block mode: mass workgroups' candidate keys
+  int32_t bm_wgs = 0;                           // ... workgroups a row (0: one-kernel selection)
   size_t off_cand_keys = 0, off_cand_count = 0, off_hist_part = 0;
   size_t off_logits = 0, off_part = 0, off_mz = 0, off_s = 0, off_selblk = 0, off_hist2 = 0,
          off_hist3 = 0, off_winners = 0, off_boundary = 0, total = 0;
@@ -105,6 +108,13 @@ bool wide_group(const hs2_attn_desc* d) { return d->n_q_heads / d->n_kv_heads > 
 bool chunk_block_path(const hs2_attn_desc* d) {
   return d->q_len > 1 && d->kv_dtype == HS2_KV_BF16 && d->select_mode == HS2_SELECT_BLOCK &&
          d->block_size % 64 == 0 && !has_flag(d, HS2_FLAG_CHUNK_PER_TOKEN);
+}
+// The block comparator otherwise (decode, per-token and fp8 chunks): per-32-position
+// block sums from the decode scan, for up to 8 query heads per KV head.
+// HS2_FLAG_FORCE_LOGITS or HS2_FLAG_SCAN_VALU keep it on the logits path.
+bool scan_block_path(const hs2_attn_desc* d) {
+  return d->select_mode == HS2_SELECT_BLOCK && !chunk_block_path(d) && !wide_group(d) &&
+         d->block_size % 32 == 0 && !has_flag(d, HS2_FLAG_FORCE_LOGITS) && !has_flag(d, HS2_FLAG_SCAN_VALU);
 }
 
 // logits_area: reserve the logits path's per-position scores whenever that path fits
@@ -192,9 +202,16 @@ Layout make_layout(const hs2_attn_desc* d, bool logits_area = true) {
   } else {
     L.off_records = off; off = align_up(off + (size_t)n * L.logit_stride * sizeof(uint16_t));
   }
-  if (chunk_block_path(d)) {
-    L.blse_stride = ceil_div(d->max_ctx_len, 64);
+  if (chunk_block_path(d) || scan_block_path(d)) {
+    L.blse_gran = chunk_block_path(d) ? 64 : 32;
+    L.blse_stride = ceil_div(d->max_ctx_len, L.blse_gran);
     L.off_blse = off; off = align_up(off + (size_t)n * L.blse_stride * 8 * sizeof(float));
+    // block selection over many workgroups a row (up to 64 blocks kept)
+    const int64_t wgs = ceil_div(ceil_div(d->max_ctx_len, d->block_size), kBlockMassBlocks);
+    if (d->n_blocks <= 64 && wgs * d->n_blocks <= kMaxBlockPick) {
+      L.bm_wgs = (int32_t)wgs;
+      L.off_bcand = off; off = align_up(off + (size_t)n * wgs * d->n_blocks * sizeof(uint64_t));
+    }
   }
   if (L.fast_ok) {
     const size_t slots = (size_t)n * L.n_cchunks * L.cand_chunk_len;
@@ -274,10 +291,14 @@ static hs2_status check_common(const hs2_attn_desc* d, const void* q, const void
 static bool use_record_path(const hs2_attn_desc* d, const Layout& L, const float* probs) {
   return L.fast_ok && probs == nullptr && (wide_group(d) || !has_flag(d, HS2_FLAG_FORCE_LOGITS));
 }
+// Block comparator on the scans' block sums (needs no per-position scores).
+static bool block_sums_path(const hs2_attn_desc* d, const float* probs) {
+  return probs == nullptr && (chunk_block_path(d) || scan_block_path(d));
+}
 static hs2_status full_path_supported(const hs2_attn_desc* d, const Layout& L, const float* probs) {
   const bool fast = use_record_path(d, L, probs);
-  const bool cblock = chunk_block_path(d) && probs == nullptr;
-  if (!fast && !cblock && !L.logits_ok) return HS2_ERR_UNSUPPORTED;
+  const bool bsums = block_sums_path(d, probs);
+  if (!fast && !bsums && !L.logits_ok) return HS2_ERR_UNSUPPORTED;
   if (!fast && wide_group(d)) return HS2_ERR_UNSUPPORTED;
   return HS2_OK;
 }
@@ -306,11 +327,12 @@ static ScanArgs scan_args(const hs2_attn_desc* d, const Layout& L, const void* q
   return a;
 }
 
-// Block comparator for a chunk: the chunk kernel's per-block sums, the split combine,
-// then the block selection on those sums.
-hs2_status chunk_block_select(const hs2_attn_desc* desc, const Layout& L, ScanArgs sa,
-                              const int32_t* ctx_len, float* out, int32_t* idx, uint8_t* ws,
-                              hipStream_t stream, const hs2_kernel_events* ev) {
+// Block comparator on block sums: the chunk kernel's (64 positions) or the decode
+// scan's (32 positions) per-block log-sum-exp per head, the split combine, then the
+// block selection on those sums.  No per-position score is written or re-read.
+hs2_status block_sums_select(const hs2_attn_desc* desc, const Layout& L, ScanArgs sa,
+                             const int32_t* ctx_len, float* out, int32_t* idx, uint8_t* ws,
+                             hipStream_t stream, const hs2_kernel_events* ev) {
   sa.records = nullptr;
   sa.hist_part = nullptr;
   sa.hist_merged = nullptr;
@@ -320,7 +342,9 @@ hs2_status chunk_block_select(const hs2_attn_desc* desc, const Layout& L, ScanAr
   sa.n_split = L.rec_n_split;
   sa.split_len = L.rec_split_len;
   event_record(ev, true, stream);
-  const hipError_t e = launch_chunk_mfma(sa, desc->batch, stream);
+  const hipError_t e = chunk_block_path(desc)
+                           ? launch_chunk_mfma(sa, desc->batch, stream)
+                           : launch_scan_mfma_blocks(sa, desc->kv_dtype == HS2_KV_FP8_E4M3FN, desc->batch, stream);
   event_record(ev, false, stream);
   if (e != hipSuccess) return HS2_ERR_LAUNCH;
 
@@ -356,6 +380,9 @@ hs2_status chunk_block_select(const hs2_attn_desc* desc, const Layout& L, ScanAr
   sl.n_blocks = desc->n_blocks;
   sl.blse = sa.blse;
   sl.blse_stride = L.blse_stride;
+  sl.blse_gran = L.blse_gran;
+  sl.bcand = L.bm_wgs > 0 ? reinterpret_cast<uint64_t*>(ws + L.off_bcand) : nullptr;
+  sl.bm_wgs = L.bm_wgs;
   if (launch_block_select(sl, stream) != hipSuccess) return HS2_ERR_LAUNCH;
   return HS2_OK;
 }
@@ -393,9 +420,8 @@ static hs2_status full_select_launch(const hs2_attn_desc* desc, const Layout& L,
   // re-scoring of the candidates.  Logits path: every position's logits, needed
   // when the caller wants all probabilities (probs) or for the block comparator.
   const bool fast = use_record_path(desc, L, probs);
-  const bool cblock = chunk_block_path(desc) && probs == nullptr;
   ScanArgs sa = scan_args(desc, L, q, k, v, k_scale, v_scale, ctx_len, ws);
-  if (cblock) return chunk_block_select(desc, L, sa, ctx_len, out, idx, ws, stream, ev);
+  if (block_sums_path(desc, probs)) return block_sums_select(desc, L, sa, ctx_len, out, idx, ws, stream, ev);
   sa.logits = reinterpret_cast<float*>(ws + L.off_logits);
   sa.records = reinterpret_cast<uint16_t*>(ws + L.off_records);
   sa.hist_part = reinterpret_cast<uint16_t*>(ws + L.off_hist_part);
@@ -537,7 +563,7 @@ HS2_API hs2_status hs2_full_attn_select_noalloc(const hs2_attn_desc* desc, const
   if (s != HS2_OK) return s;
   if (probs != nullptr && !aligned(probs, 4)) return HS2_ERR_ALIGNMENT;
   L = make_layout(desc, false);
-  if (!use_record_path(desc, L, probs) && !(chunk_block_path(desc) && probs == nullptr))
+  if (!use_record_path(desc, L, probs) && !block_sums_path(desc, probs))
     L = make_layout(desc, true);   // the logits path's scores are needed
   s = full_path_supported(desc, L, probs);
   if (s != HS2_OK) return s;

@@ -40,6 +40,8 @@ constexpr int kSelSubOff = kSelHist1Off + kFastBins;
 constexpr int kMergedWords = kFastBins + kFastSubBins;
 static_assert(kSelSubOff + kFastSubBins <= kSelWords, "control block too small");
 constexpr int kMaxBlocksLds = 16384;  // block mode: blocks per row held in LDS
+constexpr int kBlockMassBlocks = 256; // block mode on block sums: blocks per mass workgroup
+constexpr int kMaxBlockPick = 4096;   // ... and candidate keys per row (64 per lane of one wave)
 constexpr int kMaxRecordSplit = 16384; // records mode: positions per scan workgroup (LDS bound)
 
 // Per-selection state words (u32).
@@ -70,8 +72,9 @@ struct ScanArgs {
   uint16_t* hist_part;      // records mode: [n_sel, n_split, kFastBins] key histograms
   uint32_t* hist_merged;    // records mode: merged histograms at + sel*kSelWords + kSelHist1Off,
                             // cleared by split 0 of each selection
-  float* blse;              // chunk block mode: [n_sel, blse_stride, 8] log2 of the sum of
-                            // 2^logit over each aligned 64-position block, per head
+  float* blse;              // block mode: [n_sel, blse_stride, 8] log2 of the sum of 2^logit
+                            // over each aligned block of positions, per head (64 positions
+                            // from the chunk kernel, 32 from the decode scan)
   int64_t blse_stride;
   int32_t window;           // records mode: positions >= ctx - window are not candidates
   float* part;              // [n_sel, n_split, G, kPartStride]
@@ -127,8 +130,12 @@ struct SelectArgs {
   int32_t chunk_len;        // positions per workgroup in the streaming passes
   int32_t n_chunks;
   int32_t with_hist;        // token mode: build the first histogram
-  const float* blse;        // block mode from the chunk kernel's block sums, else nullptr
+  const float* blse;        // block mode from the scans' block sums, else nullptr
   int64_t blse_stride;
+  int32_t blse_gran;        // positions per block sum (32 or 64; divides block_size)
+  uint64_t* bcand;          // block sums, many blocks: [n_sel, bm_wgs, n_blocks] candidate
+                            // keys of the mass workgroups (see block_mass_kernel), or nullptr
+  int32_t bm_wgs;           // mass workgroups per row (kBlockMassBlocks blocks each)
 };
 
 struct FastSelArgs {
@@ -196,6 +203,8 @@ hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st
 hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t st);
 hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st);
 hipError_t launch_scan_mfma(const ScanArgs& a, bool fp8, int B, hipStream_t st);
+// The decode scan in block-comparator mode: per-32-position block sums into a.blse (G <= 8).
+hipError_t launch_scan_mfma_blocks(const ScanArgs& a, bool fp8, int B, hipStream_t st);
 // sparse layer on the matrix cores, one workgroup per (query token, KV head, split of
 // a.split_len index entries); out != nullptr (one split): normalised output, else
 // partials in a.part for launch_combine (S <= 4096)

@@ -245,12 +245,15 @@ __device__ __forceinline__ float sum16w(float x) {
 // otherwise over lanes 0..7 (G <= 8: the heads 8..15 of the tile are padding).
 // kGather: a sparse-layer step; `base` is the step's first index-row entry and srow
 // holds each entry's row (-1: skipped), so no records are formed.
-template <bool kFp8, bool kGather = false, int kHB = 1, bool kWide = false>
+// kBlk: a block-comparator step: instead of records, log2 of the sum of 2^logit over
+// the step's 32 positions per head goes to blrow[(base / 32) * 8 + head].
+template <bool kFp8, bool kGather = false, int kHB = 1, bool kWide = false, bool kBlk = false>
 __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x8_t (&qf)[kHB][4], uint8_t* vt,
                                              int32_t base, int32_t w_begin, int32_t w_end, uint32_t cand_span,
                                              float scale_log2, int G, int grp, int w16, int lane,
                                              uint16_t* recs, uint32_t* shist, HeadState (&hs)[kHB], float& U,
-                                             const int32_t* srow = nullptr) {
+                                             const int32_t* srow = nullptr, float* blrow = nullptr) {
+  constexpr bool kRec = !kGather && !kBlk;   // bound records and their histogram
   // V tile -> LDS (row-major, padded rows)
   if constexpr (kFp8) {
 #pragma unroll
@@ -330,7 +333,7 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
       hs[hb].z *= alpha;
       hs[hb].m = mn;
     }
-    if constexpr (!kGather) {
+    if constexpr (kRec) {
       // U: the largest running maximum of the group's heads (equal in every lane), and
       // the record scale of each head; they change only with a running maximum
       U = kNegInf;
@@ -343,7 +346,8 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
   }
   bf16x8_t phi[kHB], plo[kHB];
   float rsum[2][4];                     // records: sum over this lane's head blocks of p 2^(m - U)
-  if constexpr (!kGather) {
+  float bsum[kHB];                      // block steps: this lane's sum of p per head block
+  if constexpr (kRec) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -358,7 +362,8 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
       for (int v = 0; v < 4; ++v) {
         p[t][v] = l[hb][t][v] != kNegInf ? fast_exp2(l[hb][t][v] - hs[hb].m) : 0.0f;
         hs[hb].z += p[t][v];
-        if constexpr (!kGather) rsum[t][v] = fmaf(p[t][v], hs[hb].c, rsum[t][v]);
+        if constexpr (kRec) rsum[t][v] = fmaf(p[t][v], hs[hb].c, rsum[t][v]);
+        if constexpr (kBlk) bsum[hb] = (t == 0 && v == 0) ? p[t][v] : bsum[hb] + p[t][v];
         // masked rows: the scale may come from a row past the end (4-row scale loads)
         if constexpr (kFp8) p[t][v] = l[hb][t][v] != kNegInf ? p[t][v] * s.vs[t][v] : 0.0f;
       }
@@ -382,7 +387,16 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
   // row group: one logarithm, one record store and one histogram count per lane.  A
   // live row whose sum is below 2^-100 (terms lost to underflow could matter there)
   // makes the wave take the direct form, max then sum of 2^(l - max), for the step.
-  if constexpr (!kGather) {
+  if constexpr (kBlk) {
+    // the step's share of each head's softmax sum, relative to the running maximum
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb) {
+      const float tot = sum_groups(bsum[hb]);
+      const float lse = hs[hb].m + __builtin_amdgcn_logf(tot);   // -inf for an empty step
+      if (grp == 0 && 16 * hb + w16 < G) blrow[(int64_t)(base / kStepRows) * 8 + 16 * hb + w16] = lse;
+    }
+  }
+  if constexpr (kRec) {
     float x[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -446,7 +460,8 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
 
 // kHB, kWide: head layout (see process_step); kThreads: 512 (8 waves) for up to 16
 // heads, 256 (4 waves, one per SIMD, up to 512 registers a lane) for 32 heads.
-template <bool kFp8, bool kVecScale, int kHB, bool kWide, int kThreads>
+// kBlk: the block comparator's scan (per-32-position block sums, no records).
+template <bool kFp8, bool kVecScale, int kHB, bool kWide, int kThreads, bool kBlk = false>
 __global__ __launch_bounds__(kThreads, 1) void scan_mfma_kernel(ScanArgs a) {
   constexpr int kWaves = kThreads / 64;
   constexpr int kBH = kWide ? 16 : 8;   // heads per block with state (lanes w16 < kBH)
@@ -515,12 +530,15 @@ __global__ __launch_bounds__(kThreads, 1) void scan_mfma_kernel(ScanArgs a) {
   uint32_t cand_span = w0 > p_begin ? (uint32_t)(w0 - p_begin) : 0u;
   cand_span = cand_span < span ? cand_span : span;
 
-  for (int i = tid; i < kFastBins; i += kThreads) shist[i] = 0u;
-  if (tid == 0) step_next = kWaves;   // step w is wave w's first
-  if (split == 0) {   // the combine kernel sums every split's histogram into these words
-    uint32_t* hm = a.hist_merged + sel * kSelWords + kSelHist1Off;
-    for (int i = tid; i < kMergedWords; i += kThreads) hm[i] = 0u;
+  if constexpr (!kBlk) {
+    for (int i = tid; i < kFastBins; i += kThreads) shist[i] = 0u;
+    if (split == 0) {   // the combine kernel sums every split's histogram into these words
+      uint32_t* hm = a.hist_merged + sel * kSelWords + kSelHist1Off;
+      for (int i = tid; i < kMergedWords; i += kThreads) hm[i] = 0u;
+    }
   }
+  if (tid == 0) step_next = kWaves;   // step w is wave w's first
+  float* blrow = kBlk ? a.blse + sel * a.blse_stride * 8 : nullptr;
   __syncthreads();
 
   HeadState hs[kHB];
@@ -554,13 +572,15 @@ __global__ __launch_bounds__(kThreads, 1) void scan_mfma_kernel(ScanArgs a) {
     load_step<kFp8, kVecScale>(s1, kb, vb, ksb, vsb, w_begin + k1 * kStepRows, last, grp, w16, lane);
     // two-buffer ring; every load is issued (rows past the end re-read `last`)
     while (k0 < nsteps) {
-      process_step<kFp8, false, kHB, kWide>(s0, qf, vt, w_begin + k0 * kStepRows, w_begin, w_end, cand_span,
-                                            a.scale_log2, a.G, grp, w16, lane, srec, shist, hs, U);
+      process_step<kFp8, false, kHB, kWide, kBlk>(s0, qf, vt, w_begin + k0 * kStepRows, w_begin, w_end, cand_span,
+                                                  a.scale_log2, a.G, grp, w16, lane, srec, shist, hs, U, nullptr,
+                                                  blrow);
       k0 = take();
       load_step<kFp8, kVecScale>(s0, kb, vb, ksb, vsb, w_begin + k0 * kStepRows, last, grp, w16, lane);
       if (k1 >= nsteps) break;
-      process_step<kFp8, false, kHB, kWide>(s1, qf, vt, w_begin + k1 * kStepRows, w_begin, w_end, cand_span,
-                                            a.scale_log2, a.G, grp, w16, lane, srec, shist, hs, U);
+      process_step<kFp8, false, kHB, kWide, kBlk>(s1, qf, vt, w_begin + k1 * kStepRows, w_begin, w_end, cand_span,
+                                                  a.scale_log2, a.G, grp, w16, lane, srec, shist, hs, U, nullptr,
+                                                  blrow);
       k1 = take();
       load_step<kFp8, kVecScale>(s1, kb, vb, ksb, vsb, w_begin + k1 * kStepRows, last, grp, w16, lane);
     }
@@ -568,7 +588,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_mfma_kernel(ScanArgs a) {
 
   // the split's records and key histogram, once every wave is done
   __syncthreads();
-  {
+  if constexpr (!kBlk) {
     const int cnt = p_end > p_begin ? (int)(p_end - p_begin) : 0;
     uint16_t* grec = a.records + sel * a.logit_stride + p_begin;   // 512-byte aligned
     for (int i = tid; 2 * i + 1 < cnt; i += kThreads)
@@ -799,6 +819,18 @@ static void launch_scan_g(const ScanArgs& a, dim3 grid, hipStream_t st) {
     hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 1, true, 512>), grid, dim3(512), 0, st, a);
   else
     hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 2, true, 256>), grid, dim3(256), 0, st, a);
+}
+
+hipError_t launch_scan_mfma_blocks(const ScanArgs& a, bool fp8, int B, hipStream_t st) {
+  if (a.G > 8 || a.blse == nullptr) return hipErrorInvalidValue;
+  dim3 grid(a.n_split, a.Hkv, B * a.Lq);
+  if (fp8 && a.cap % 4 == 0)
+    hipLaunchKernelGGL((scan_mfma_kernel<true, true, 1, false, 512, true>), grid, dim3(512), 0, st, a);
+  else if (fp8)
+    hipLaunchKernelGGL((scan_mfma_kernel<true, false, 1, false, 512, true>), grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((scan_mfma_kernel<false, false, 1, false, 512, true>), grid, dim3(512), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_scan_mfma(const ScanArgs& a, bool fp8, int B, hipStream_t st) {

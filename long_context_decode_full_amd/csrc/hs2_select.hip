@@ -418,16 +418,18 @@ __global__ __launch_bounds__(kBlkThreads) void block_select_kernel(SelectArgs a)
   __shared__ int32_t cnt[4097];
 
   if (a.blse != nullptr) {
-    // chunk kernel: per 64-position block and head h, L_h = log2 sum 2^logit, so the
-    // block's share of head h's softmax is 2^(L_h - M_h) / Z_h (bs is a multiple of 64)
+    // the scans' block sums: per aligned block of blse_gran positions and head h,
+    // L_h = log2 sum 2^logit, so its share of head h's softmax is 2^(L_h - M_h) / Z_h
+    // (bs is a multiple of blse_gran)
     float Mh[8], iz[8];
 #pragma unroll
     for (int h = 0; h < 8; ++h) {
       Mh[h] = a.mz[(sel * kMaxHeads + h) * 2 + 0];
       iz[h] = a.mz[(sel * kMaxHeads + h) * 2 + 1];
     }
-    const int sub = bs / 64;
-    const int nsub = (n + 63) / 64;   // 64-blocks holding visible positions
+    const int gran = a.blse_gran;
+    const int sub = bs / gran;
+    const int nsub = (n + gran - 1) / gran;   // block sums holding visible positions
     const float* brow = a.blse + sel * a.blse_stride * 8;
     for (int blk = tid; blk < nb; blk += kBlkThreads) {
       float acc = 0.0f;
@@ -527,8 +529,162 @@ hipError_t launch_finalize(const SelectArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+namespace {
+
+// ------------------------------------------------------------------ block comparator on block sums
+// The same selection from the scans' block sums in two launches that spread a long row
+// over many workgroups:
+//   block_mass_kernel: workgroup w of a row takes blocks [kBmBlocks w, kBmBlocks (w+1)),
+//                      forms their masses (the sum above, same order) and keeps its
+//                      n_blocks best (mass desc, block asc) as candidates;
+//   block_pick_kernel: one wave per row: the n_blocks best of the row's candidates
+//                      (register-resident rounds of a wave argmax on a unique key), then
+//                      the chosen blocks ascending, expanded to their visible positions.
+// The row's best n_blocks are among the union of every workgroup's best n_blocks.
+constexpr int kBmThreads = 256;
+constexpr int kBmBlocks = kBlockMassBlocks;        // blocks per mass workgroup
+constexpr int kPickPerLane = kMaxBlockPick / 64;   // candidates a lane of the pick wave holds
+
+// Unique order key of a candidate: larger mass first (masses are >= 0, so their bits
+// order like the values), then the lower block; 0 marks no candidate.
+__device__ __forceinline__ uint64_t block_key(float mass, int32_t blk) {
+  return ((uint64_t)__float_as_uint(mass) << 32) | (uint32_t)(0x7FFFFFFF - blk);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, off, 64);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), off, 64);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    x = o > x ? o : x;
+  }
+  return x;
+}
+
+__global__ __launch_bounds__(kBmThreads) void block_mass_kernel(SelectArgs a) {
+  const int64_t sel = blockIdx.x / (uint32_t)a.bm_wgs;
+  const int wg = (int)(blockIdx.x % (uint32_t)a.bm_wgs);
+  const int tid = threadIdx.x;
+  const RowGeom rg = row_geom(a, sel);
+  const int n = (int)rg.n;
+  const int bs = a.block_size;
+  const int nb = (n + bs - 1) / bs;
+  const int b0 = wg * kBmBlocks;
+  uint64_t* outc = a.bcand + (sel * a.bm_wgs + wg) * a.n_blocks;
+  __shared__ float mass[kBmBlocks];
+  if (b0 < nb) {
+    float Mh[8], iz[8];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      Mh[h] = a.mz[(sel * kMaxHeads + h) * 2 + 0];
+      iz[h] = a.mz[(sel * kMaxHeads + h) * 2 + 1];
+    }
+    const int gran = a.blse_gran;
+    const int sub = bs / gran;
+    const int nsub = (n + gran - 1) / gran;
+    const float* brow = a.blse + sel * a.blse_stride * 8;
+    for (int i = tid; i < kBmBlocks; i += kBmThreads) {
+      const int blk = b0 + i;
+      float acc = -1.0f;   // no block
+      if (blk < nb) {
+        acc = 0.0f;
+        for (int u = 0; u < sub; ++u) {
+          const int sb = blk * sub + u;
+          if (sb >= nsub) break;
+          const float4 l0 = *reinterpret_cast<const float4*>(brow + (int64_t)sb * 8);
+          const float4 l1 = *reinterpret_cast<const float4*>(brow + (int64_t)sb * 8 + 4);
+          const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+          for (int h = 0; h < 8; ++h)
+            if (h < a.G) acc += fast_exp2(lv[h] - Mh[h]) * iz[h];
+        }
+      }
+      mass[i] = acc;
+    }
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  // wave 0: the workgroup's n_blocks best, 4 blocks a lane
+  const int lane = tid;
+  uint64_t key[kBmBlocks / 64];
+#pragma unroll
+  for (int j = 0; j < kBmBlocks / 64; ++j) {
+    const int i = lane + 64 * j;
+    key[j] = (b0 < nb && mass[i] >= 0.0f) ? block_key(mass[i], b0 + i) : 0ull;
+  }
+  for (int r = 0; r < a.n_blocks; ++r) {
+    uint64_t best = 0ull;
+#pragma unroll
+    for (int j = 0; j < kBmBlocks / 64; ++j) best = key[j] > best ? key[j] : best;
+    best = wave_max_u64(best);
+    if (lane == 0) outc[r] = best;
+#pragma unroll
+    for (int j = 0; j < kBmBlocks / 64; ++j) key[j] = key[j] == best ? 0ull : key[j];
+  }
+}
+
+__global__ __launch_bounds__(64) void block_pick_kernel(SelectArgs a) {
+  const int64_t sel = blockIdx.x;
+  const int lane = threadIdx.x;
+  const RowGeom rg = row_geom(a, sel);
+  const int n = (int)rg.n;
+  const int bs = a.block_size;
+  const int nb = (n + bs - 1) / bs;
+  const int take = a.n_blocks < nb ? a.n_blocks : nb;
+  int32_t* out = a.idx + sel * a.S;
+  const int ncand = a.bm_wgs * a.n_blocks;
+  const uint64_t* cand = a.bcand + sel * (int64_t)ncand;
+  uint64_t key[kPickPerLane];
+#pragma unroll
+  for (int j = 0; j < kPickPerLane; ++j) {
+    const int i = lane + 64 * j;
+    key[j] = i < ncand ? cand[i] : 0ull;
+  }
+  __shared__ int32_t chosen[64];
+  for (int r = 0; r < take; ++r) {
+    uint64_t best = 0ull;
+#pragma unroll
+    for (int j = 0; j < kPickPerLane; ++j) best = key[j] > best ? key[j] : best;
+    best = wave_max_u64(best);
+    if (lane == 0) chosen[r] = 0x7FFFFFFF - (int32_t)(uint32_t)best;
+#pragma unroll
+    for (int j = 0; j < kPickPerLane; ++j) key[j] = key[j] == best ? 0ull : key[j];
+  }
+  __syncthreads();
+  // ascending block order: lane r < take holds chosen block r and its rank
+  int myblk = lane < take ? chosen[lane] : 0x7FFFFFFF;
+  int rank = 0;
+  for (int i = 0; i < take; ++i) rank += chosen[i] < myblk ? 1 : 0;
+  int len = 0;
+  if (lane < take) {
+    const int t0 = myblk * bs;
+    len = ((t0 + bs < n) ? t0 + bs : n) - t0;
+  }
+  __shared__ int32_t sorted_blk[64], sorted_len[64];
+  if (lane < take) {
+    sorted_blk[rank] = myblk;
+    sorted_len[rank] = len;
+  }
+  __syncthreads();
+  int off = 0;
+  for (int i = 0; i < take; ++i) {
+    const int blk = sorted_blk[i], ln = sorted_len[i];
+    for (int t = lane; t < ln; t += 64) out[off + t] = blk * bs + t;
+    off += ln;
+  }
+  for (int i = off + lane; i < a.S; i += 64) out[i] = -1;
+}
+
+}  // namespace
+
 hipError_t launch_block_select(const SelectArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(block_select_kernel, dim3(a.n_sel), dim3(kBlkThreads), 0, st, a);
+  if (a.blse != nullptr && a.bcand != nullptr) {
+    hipLaunchKernelGGL(block_mass_kernel, dim3((uint32_t)((uint64_t)a.n_sel * a.bm_wgs)), dim3(kBmThreads), 0, st, a);
+    hipLaunchKernelGGL(block_pick_kernel, dim3(a.n_sel), dim3(64), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(block_select_kernel, dim3(a.n_sel), dim3(kBlkThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

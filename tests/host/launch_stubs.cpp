@@ -122,6 +122,13 @@ hipError_t launch_scan_mfma(const ScanArgs& a, bool, int B, hipStream_t) {
   check_scan(a, B, true);
   return hipSuccess;
 }
+hipError_t launch_scan_mfma_blocks(const ScanArgs& a, bool, int B, hipStream_t) {
+  if (a.split_len > kMaxRecordSplit) fail("block scan: split beyond the scan's LDS");
+  if (a.G > kSlots || a.blse == nullptr) fail("block scan: head slots or no block sums");
+  if (a.blse != nullptr && (int64_t)a.blse_stride * 32 < a.ctx_max) fail("block scan: block sums do not cover the context");
+  check_scan(a, B, false);
+  return hipSuccess;
+}
 hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool, int B, hipStream_t) {
   if (out == nullptr) in_ws(a.part, sel_rows(a, B) * a.n_split * a.G * kPartStride * 4ull, "gather: partials");
   if ((int64_t)a.n_split * a.split_len < a.S) fail("gather: splits do not cover the index row");
@@ -170,6 +177,15 @@ hipError_t launch_groupsum(const SelectArgs& a, hipStream_t) {
 hipError_t launch_refine(const SelectArgs& a, int, hipStream_t) { check_select(a); return hipSuccess; }
 hipError_t launch_collect(const SelectArgs& a, hipStream_t) { check_select(a); return hipSuccess; }
 hipError_t launch_finalize(const SelectArgs& a, hipStream_t) { check_select(a); return hipSuccess; }
-hipError_t launch_block_select(const SelectArgs& a, hipStream_t) { check_select(a); return hipSuccess; }
+hipError_t launch_block_select(const SelectArgs& a, hipStream_t) {
+  if (a.blse != nullptr && (a.blse_gran < 1 || a.block_size % a.blse_gran != 0)) fail("block select: block-sum granularity");
+  if (a.bcand != nullptr) {
+    in_ws(a.bcand, (uint64_t)a.n_sel * a.bm_wgs * a.n_blocks * 8ull, "block select: candidate keys");
+    if (a.n_blocks > 64 || (int64_t)a.bm_wgs * a.n_blocks > kMaxBlockPick) fail("block select: pick wave capacity");
+    if ((int64_t)a.bm_wgs * kBlockMassBlocks * a.block_size < a.ctx_max) fail("block select: mass workgroups do not cover the row");
+  }
+  check_select(a);
+  return hipSuccess;
+}
 
 }  // namespace hs2
