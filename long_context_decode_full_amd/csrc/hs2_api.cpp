@@ -208,7 +208,7 @@ Layout make_layout(const hs2_attn_desc* d, bool logits_area = true) {
     L.off_blse = off; off = align_up(off + (size_t)n * L.blse_stride * 8 * sizeof(float));
     // block selection over many workgroups a row (up to 64 blocks kept)
     const int64_t wgs = ceil_div(ceil_div(d->max_ctx_len, d->block_size), kBlockMassBlocks);
-    if (d->n_blocks <= 64 && wgs * d->n_blocks <= kMaxBlockPick) {
+    if (d->n_blocks <= 64 && wgs <= kMaxBlockMassWgs && wgs * d->n_blocks <= kMaxBlockPick) {
       L.bm_wgs = (int32_t)wgs;
       L.off_bcand = off; off = align_up(off + (size_t)n * wgs * d->n_blocks * sizeof(uint64_t));
     }

@@ -41,7 +41,8 @@ constexpr int kMergedWords = kFastBins + kFastSubBins;
 static_assert(kSelSubOff + kFastSubBins <= kSelWords, "control block too small");
 constexpr int kMaxBlocksLds = 16384;  // block mode: blocks per row held in LDS
 constexpr int kBlockMassBlocks = 256; // block mode on block sums: blocks per mass workgroup
-constexpr int kMaxBlockPick = 4096;   // ... and candidate keys per row (64 per lane of one wave)
+constexpr int kMaxBlockPick = 4096;   // ... candidate keys per row held by the pick wave
+constexpr int kMaxBlockMassWgs = 256; // ... and mass workgroups per row (4 lists a lane)
 constexpr int kMaxRecordSplit = 16384; // records mode: positions per scan workgroup (LDS bound)
 
 // Per-selection state words (u32).

@@ -537,13 +537,13 @@ namespace {
 //   block_mass_kernel: workgroup w of a row takes blocks [kBmBlocks w, kBmBlocks (w+1)),
 //                      forms their masses (the sum above, same order) and keeps its
 //                      n_blocks best (mass desc, block asc) as candidates;
-//   block_pick_kernel: one wave per row: the n_blocks best of the row's candidates
-//                      (register-resident rounds of a wave argmax on a unique key), then
-//                      the chosen blocks ascending, expanded to their visible positions.
+//   block_pick_kernel: one wave per row: the n_blocks best of the row's candidates (a
+//                      merge of the workgroups' sorted lists on a unique key), then the
+//                      chosen blocks ascending, expanded to their visible positions.
 // The row's best n_blocks are among the union of every workgroup's best n_blocks.
 constexpr int kBmThreads = 256;
 constexpr int kBmBlocks = kBlockMassBlocks;        // blocks per mass workgroup
-constexpr int kPickPerLane = kMaxBlockPick / 64;   // candidates a lane of the pick wave holds
+constexpr int kPickLists = kMaxBlockMassWgs / 64;   // mass workgroups' lists a lane merges
 
 // Unique order key of a candidate: larger mass first (masses are >= 0, so their bits
 // order like the values), then the lower block; 0 marks no candidate.
@@ -633,23 +633,37 @@ __global__ __launch_bounds__(64) void block_pick_kernel(SelectArgs a) {
   const int nb = (n + bs - 1) / bs;
   const int take = a.n_blocks < nb ? a.n_blocks : nb;
   int32_t* out = a.idx + sel * a.S;
-  const int ncand = a.bm_wgs * a.n_blocks;
-  const uint64_t* cand = a.bcand + sel * (int64_t)ncand;
-  uint64_t key[kPickPerLane];
+  // Each mass workgroup's list is in descending key order: a k-way merge.  Lane l keeps
+  // the heads of lists l, l + 64, ... (at most kPickLists) and each round the wave takes
+  // the largest head; keys are unique, so exactly one list advances.
+  const int nl = a.bm_wgs, ll = a.n_blocks;
+  const uint64_t* cand = a.bcand + sel * (int64_t)nl * ll;
+  __shared__ uint64_t lists[kMaxBlockPick];
+  for (int i = lane; i < nl * ll; i += 64) lists[i] = cand[i];
+  __syncthreads();
+  int ptr[kPickLists];
+  uint64_t head[kPickLists];
 #pragma unroll
-  for (int j = 0; j < kPickPerLane; ++j) {
-    const int i = lane + 64 * j;
-    key[j] = i < ncand ? cand[i] : 0ull;
+  for (int u = 0; u < kPickLists; ++u) {
+    const int li = lane + 64 * u;
+    ptr[u] = 0;
+    head[u] = li < nl ? lists[li * ll] : 0ull;
   }
   __shared__ int32_t chosen[64];
   for (int r = 0; r < take; ++r) {
     uint64_t best = 0ull;
 #pragma unroll
-    for (int j = 0; j < kPickPerLane; ++j) best = key[j] > best ? key[j] : best;
+    for (int u = 0; u < kPickLists; ++u) best = head[u] > best ? head[u] : best;
     best = wave_max_u64(best);
     if (lane == 0) chosen[r] = 0x7FFFFFFF - (int32_t)(uint32_t)best;
 #pragma unroll
-    for (int j = 0; j < kPickPerLane; ++j) key[j] = key[j] == best ? 0ull : key[j];
+    for (int u = 0; u < kPickLists; ++u) {
+      if (head[u] == best) {   // the list the round took from (best > 0)
+        const int li = lane + 64 * u;
+        ++ptr[u];
+        head[u] = ptr[u] < ll ? lists[li * ll + ptr[u]] : 0ull;
+      }
+    }
   }
   __syncthreads();
   // ascending block order: lane r < take holds chosen block r and its rank

@@ -181,7 +181,8 @@ hipError_t launch_block_select(const SelectArgs& a, hipStream_t) {
   if (a.blse != nullptr && (a.blse_gran < 1 || a.block_size % a.blse_gran != 0)) fail("block select: block-sum granularity");
   if (a.bcand != nullptr) {
     in_ws(a.bcand, (uint64_t)a.n_sel * a.bm_wgs * a.n_blocks * 8ull, "block select: candidate keys");
-    if (a.n_blocks > 64 || (int64_t)a.bm_wgs * a.n_blocks > kMaxBlockPick) fail("block select: pick wave capacity");
+    if (a.n_blocks > 64 || a.bm_wgs > kMaxBlockMassWgs || (int64_t)a.bm_wgs * a.n_blocks > kMaxBlockPick)
+      fail("block select: pick wave capacity");
     if ((int64_t)a.bm_wgs * kBlockMassBlocks * a.block_size < a.ctx_max) fail("block select: mass workgroups do not cover the row");
   }
   check_select(a);
