@@ -35,6 +35,9 @@
 namespace hs2 {
 namespace {
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
 constexpr int kThreads = 256;
 constexpr float kBoundSlack = 2e-3f;   // log2 units: fp32 rounding of e and of the exact s
 
@@ -422,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
 constexpr int kRsBlk = 1024;   // list entries per re-score block
 constexpr int kRsPer = kRsBlk / kThreads;
 constexpr int kRsBatch = 8;    // wave steps (4 rows each) whose key loads are issued together
-constexpr int kRsBatchMB = 4;  // the same with more than 8 heads (per-row sums stay in registers)
+constexpr int kRsTiles = 4;    // more than 8 heads: 16-candidate tiles a wave loads together
 static_assert(kFastSubBins == 64, "one lane per sub-bin");
 static_assert(kMinCandChunkLen % kRsBlk == 0, "blocks tile a chunk");
 
@@ -530,10 +533,29 @@ __global__ __launch_bounds__(kThreads) void cand_rescore_kernel(FastSelArgs a) {
   const int r = lane & 15;
   const int rgrp = lane >> 4;
   const int hown = head_of(r);
-  uint32_t qp[8][4];
-  load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);
-  const float Mown = hown < a.G ? a.mz[(sel * kMaxHeads + hown) * 2] : 0.0f;
-  const float izown = hown < a.G ? a.mz[(sel * kMaxHeads + hown) * 2 + 1] : 0.0f;
+  uint32_t qp[8][4];   // VALU re-score (up to 8 heads): the scan's row layout
+  float Mown = 0.0f, izown = 0.0f;
+  bf16x8_t qf[2][4];   // matrix-core re-score (more heads): Q^T of heads 16 hb + w16, dims 32 s + 8 grp
+  float Mq[2], izq[2];
+  if constexpr (!kMB) {
+    load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);
+    Mown = hown < a.G ? a.mz[(sel * kMaxHeads + hown) * 2] : 0.0f;
+    izown = hown < a.G ? a.mz[(sel * kMaxHeads + hown) * 2 + 1] : 0.0f;
+  } else {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int h = 16 * hb + r;
+      const bool in = h < a.G;
+      const uint16_t* qh = a.q + (bj * a.Hq + (int64_t)g * a.G + (in ? h : 0)) * kHeadDim;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const uint4 x = *reinterpret_cast<const uint4*>(qh + 32 * sl + 8 * rgrp);
+        qf[hb][sl] = __builtin_bit_cast(bf16x8_t, in ? x : make_uint4(0u, 0u, 0u, 0u));
+      }
+      Mq[hb] = in ? a.mz[(sel * kMaxHeads + h) * 2] : 0.0f;
+      izq[hb] = in ? a.mz[(sel * kMaxHeads + h) * 2 + 1] : 0.0f;
+    }
+  }
 
   // E_k: the sub-bins of the threshold bin from the top, one per lane
   const uint32_t* blk = sel_block(a, sel);
@@ -633,41 +655,69 @@ __global__ __launch_bounds__(kThreads) void cand_rescore_kernel(FastSelArgs a) {
           }
         }
       } else {
-        // more than 8 heads: the batch's key rows stay in registers while the query
-        // blocks of 8 heads take turns; the group sum adds the blocks in order
-        const int nb = (a.G + 7) / 8;
-        for (int i0 = wave * 4; i0 < nu; i0 += 16 * kRsBatchMB) {
-          RowData d[kRsBatchMB];
-          uint32_t ue[kRsBatchMB];
-          float ssum[kRsBatchMB];
+        // more than 8 heads: tiles of 16 candidates on the matrix cores.  S = K Q^T with
+        // A = the candidates' key rows (lane: candidate w16 of the tile, dims 32 s + 8 grp)
+        // and B = Q^T of each 16-head block, so lane (head w16, grp) gets the logits of
+        // candidates 4 grp + v; the group sum adds the two blocks, then the 16 head lanes.
+        // Wave w takes tiles w, w + 4, ...; kRsTiles tiles' loads are issued together.
+        const int ntiles = (nu + 15) >> 4;
+        for (int t0 = wave; t0 < ntiles; t0 += 4 * kRsTiles) {
+          bf16x8_t kf[kRsTiles][4];
+          float ks4[kRsTiles][4];
 #pragma unroll
-          for (int u = 0; u < kRsBatchMB; ++u) {
-            const int i = i0 + 16 * u + rgrp;
-            ue[u] = ulist[i < nu ? i : i0];
-            load_key<kFp8>(kb, ksb, (uint32_t)(c0 + (ue[u] & 0xFFFFu)), r, d[u]);
-            ssum[u] = 0.0f;
-          }
-          for (int hb = 0; hb < nb; ++hb) {
-            const int gb = min(8, a.G - 8 * hb);
-            load_query(a.q + (bj * a.Hq + (int64_t)g * a.G + 8 * hb) * kHeadDim, gb, r, qp);
-            const int hg = 8 * hb + hown;
-            const float Mb = hown < gb ? a.mz[(sel * kMaxHeads + hg) * 2] : 0.0f;
-            const float izb = hown < gb ? a.mz[(sel * kMaxHeads + hg) * 2 + 1] : 0.0f;
+          for (int u = 0; u < kRsTiles; ++u) {
+            const int t = min(t0 + 4 * u, ntiles - 1);   // past the end: a valid tile, dropped
+            const int i = 16 * t + r;
+            const uint32_t pos = (uint32_t)(c0 + (ulist[i < nu ? i : 16 * t] & 0xFFFFu));
 #pragma unroll
-            for (int u = 0; u < kRsBatchMB; ++u) {
-              if (i0 + 16 * u < nu) {   // wave-uniform
-                const float l = row_logit<kFp8>(qp, d[u], a.scale_log2);
-                const float part = ((r & 1) == 0 && hown < gb) ? fast_exp2(l - Mb) * izb : 0.0f;
-                const float sb = rowgroup_sum16(part);
-                ssum[u] = hb == 0 ? sb : ssum[u] + sb;
+            for (int sl = 0; sl < 4; ++sl) {
+              if constexpr (kFp8) {
+                const uint2 c = *reinterpret_cast<const uint2*>(kb + (uint64_t)pos * 128 + 32 * sl + 8 * rgrp);
+                kf[u][sl] = __builtin_bit_cast(bf16x8_t, make_uint4(fp8x2_to_bf16x2(c.x, false), fp8x2_to_bf16x2(c.x, true),
+                                                                    fp8x2_to_bf16x2(c.y, false), fp8x2_to_bf16x2(c.y, true)));
+              } else {
+                kf[u][sl] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kb + (uint64_t)pos * 256 + 64 * sl + 16 * rgrp));
+              }
+            }
+            if constexpr (kFp8) {
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const int iv = 16 * t + 4 * rgrp + v;
+                ks4[u][v] = ksb[c0 + (ulist[iv < nu ? iv : 16 * t] & 0xFFFFu)];
               }
             }
           }
 #pragma unroll
-          for (int u = 0; u < kRsBatchMB; ++u) {
-            const int i = i0 + 16 * u + rgrp;
-            if (i0 + 16 * u < nu && i < nu && r == 0)
-              a.cand_keys[slot0 + (ue[u] >> 16)] = cand_key(__float_as_uint(ssum[u]), (int32_t)(c0 + (ue[u] & 0xFFFFu)));
+          for (int u = 0; u < kRsTiles; ++u) {
+            const int t = t0 + 4 * u;
+            if (t < ntiles) {   // wave-uniform
+              float x[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int hb = 0; hb < 2; ++hb) {
+                f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sl = 0; sl < 4; ++sl) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][sl], qf[hb][sl], d, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                  float l = d[v] * a.scale_log2;
+                  if constexpr (kFp8) l *= ks4[u][v];
+                  x[v] += 16 * hb + r < a.G ? fast_exp2(l - Mq[hb]) * izq[hb] : 0.0f;
+                }
+              }
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                x[v] += dpp<kDppXor1>(x[v]);
+                x[v] += dpp<kDppXor2>(x[v]);
+                x[v] += dpp<kDppMirror8>(x[v]);
+                x[v] += dpp<kDppRor8>(x[v]);
+              }
+              const int iv = 16 * t + 4 * rgrp + r;   // lanes r < 4 write candidate 4 grp + r
+              if (r < 4 && iv < nu) {
+                const float sv = r == 0 ? x[0] : r == 1 ? x[1] : r == 2 ? x[2] : x[3];
+                const uint32_t e = ulist[iv];
+                a.cand_keys[slot0 + (e >> 16)] = cand_key(__float_as_uint(sv), (int32_t)(c0 + (e & 0xFFFFu)));
+              }
+            }
           }
         }
       }
