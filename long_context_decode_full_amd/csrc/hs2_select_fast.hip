@@ -207,6 +207,96 @@ __device__ __forceinline__ mask_t valid_mask(int64_t nv) {
   return nv <= 0 ? (mask_t)0 : (mask_t)((((mask_t)1) << nv) - 1);
 }
 
+// Exact re-score with more than 8 query heads per KV head (up to 32), on the matrix
+// cores: tiles of 16 list entries, S = K Q^T with A = the entries' key rows (lane:
+// entry w16 of the tile, dims 32 s + 8 grp) and B = Q^T of each 16-head block, so lane
+// (head w16, grp) gets the logits of entries 4 grp + v; the group sum adds the two
+// blocks, then the 16 head lanes (DPP).  Wave w of 4 takes tiles w, w + 4, ...; the key
+// loads of kRsTiles tiles are issued together.  pos_of(i): entry i's position;
+// write(i, s): store its score.
+constexpr int kRsTiles = 4;
+struct WideQuery {
+  bf16x8_t qf[2][4];   // Q^T of heads 16 hb + w16 (zero past G), dims 32 s + 8 grp
+  float M[2], iz[2];   // their (M, 1/Z)
+};
+__device__ __forceinline__ void load_wide_query(const FastSelArgs& a, int64_t sel, int64_t bj, int g, int r,
+                                                int rgrp, WideQuery& wq) {
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int h = 16 * hb + r;
+    const bool in = h < a.G;
+    const uint16_t* qh = a.q + (bj * a.Hq + (int64_t)g * a.G + (in ? h : 0)) * kHeadDim;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const uint4 x = *reinterpret_cast<const uint4*>(qh + 32 * sl + 8 * rgrp);
+      wq.qf[hb][sl] = __builtin_bit_cast(bf16x8_t, in ? x : make_uint4(0u, 0u, 0u, 0u));
+    }
+    wq.M[hb] = in ? a.mz[(sel * kMaxHeads + h) * 2] : 0.0f;
+    wq.iz[hb] = in ? a.mz[(sel * kMaxHeads + h) * 2 + 1] : 0.0f;
+  }
+}
+template <bool kFp8, class PosOf, class Write>
+__device__ __forceinline__ void rescore_wide(int nu, int wave, int r, int rgrp, const WideQuery& wq,
+                                             const uint8_t* __restrict__ kb, const float* __restrict__ ksb,
+                                             float scale_log2, int G, PosOf pos_of, Write write) {
+  const int ntiles = (nu + 15) >> 4;
+  for (int t0 = wave; t0 < ntiles; t0 += 4 * kRsTiles) {
+    bf16x8_t kf[kRsTiles][4];
+    float ks4[kRsTiles][4];
+#pragma unroll
+    for (int u = 0; u < kRsTiles; ++u) {
+      const int t = min(t0 + 4 * u, ntiles - 1);   // past the end: a valid tile, dropped
+      const int i = 16 * t + r;
+      const uint32_t pos = pos_of(i < nu ? i : 16 * t);
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        if constexpr (kFp8) {
+          const uint2 c = *reinterpret_cast<const uint2*>(kb + (uint64_t)pos * 128 + 32 * sl + 8 * rgrp);
+          kf[u][sl] = __builtin_bit_cast(bf16x8_t, make_uint4(fp8x2_to_bf16x2(c.x, false), fp8x2_to_bf16x2(c.x, true),
+                                                              fp8x2_to_bf16x2(c.y, false), fp8x2_to_bf16x2(c.y, true)));
+        } else {
+          kf[u][sl] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kb + (uint64_t)pos * 256 + 64 * sl + 16 * rgrp));
+        }
+      }
+      if constexpr (kFp8) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int iv = 16 * t + 4 * rgrp + v;
+          ks4[u][v] = ksb[pos_of(iv < nu ? iv : 16 * t)];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRsTiles; ++u) {
+      const int t = t0 + 4 * u;
+      if (t < ntiles) {   // wave-uniform
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][sl], wq.qf[hb][sl], d, 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float l = d[v] * scale_log2;
+            if constexpr (kFp8) l *= ks4[u][v];
+            x[v] += 16 * hb + r < G ? fast_exp2(l - wq.M[hb]) * wq.iz[hb] : 0.0f;
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          x[v] += dpp<kDppXor1>(x[v]);
+          x[v] += dpp<kDppXor2>(x[v]);
+          x[v] += dpp<kDppMirror8>(x[v]);
+          x[v] += dpp<kDppRor8>(x[v]);
+        }
+        const int iv = 16 * t + 4 * rgrp + r;   // lanes r < 4 write entry 4 grp + r
+        if (r < 4 && iv < nu) write(iv, r == 0 ? x[0] : r == 1 ? x[1] : r == 2 ? x[2] : x[3]);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ candidates + exact re-score
 // Work unit: one (row, chunk of chunk_len positions); workgroup w of a row takes its
 // chunks w, w + cand_wgs, ... (blockIdx.x = row * cand_wgs + w; the grid is sized so
@@ -250,8 +340,13 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
   const int r = lane & 15;
   const int rgrp = lane >> 4;
   const int hown = head_of(r);
-  uint32_t qp[8][4];   // issued early: its latency overlaps the threshold and the filter
-  load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);
+  // the queries are loaded early: their latency overlaps the threshold and the filter
+  uint32_t qp[8][4];   // up to 8 heads: the scan's row layout (VALU re-score)
+  WideQuery wq;        // more heads: the matrix-core re-score's fragments
+  if constexpr (!kMB)
+    load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);
+  else
+    load_wide_query(a, sel, bj, g, r, rgrp, wq);
   // With R <= 32 the next chunk's records are loaded while the current chunk re-scores
   // (a row's workgroup takes its chunks in turn when rows are many).
   constexpr bool kPrefetch = R <= 32;
@@ -363,42 +458,12 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
         }
       }
     } else {
-      // blocks of 8 heads; candidate i is always scored by the same lane group, so its
-      // LDS sum needs no barrier between blocks
-      __shared__ float ssum[clen];
-      const int nb = (a.G + 7) / 8;
-      for (int blk = 0; blk < nb; ++blk) {
-        const int gb = min(8, a.G - 8 * blk);
-        if (blk > 0)
-          load_query(a.q + (bj * a.Hq + (int64_t)g * a.G + 8 * blk) * kHeadDim, gb, r, qp);
-        const int hg = 8 * blk + hown;   // this lane's head
-        const float Mb = hown < gb ? a.mz[(sel * kMaxHeads + hg) * 2] : 0.0f;
-        const float izb = hown < gb ? a.mz[(sel * kMaxHeads + hg) * 2 + 1] : 0.0f;
-        for (int i0 = wave * 4; i0 < unc; i0 += 16 * kRescoreBatch) {
-          RowData d[kRescoreBatch];
-          int32_t tpos[kRescoreBatch];
-#pragma unroll
-          for (int u = 0; u < kRescoreBatch; ++u) {
-            const int i = i0 + 16 * u + rgrp;
-            tpos[u] = (int32_t)(c0 + cpos[ulist[i < unc ? i : i0]]);
-            load_key<kFp8>(kb, ksb, (uint32_t)tpos[u], r, d[u]);
-          }
-#pragma unroll
-          for (int u = 0; u < kRescoreBatch; ++u) {
-            const int i = i0 + 16 * u + rgrp;
-            const float l = row_logit<kFp8>(qp, d[u], a.scale_log2);
-            const float part = ((r & 1) == 0 && hown < gb) ? fast_exp2(l - Mb) * izb : 0.0f;
-            const float s = rowgroup_sum16(part);
-            if (i < unc && r == 0) ssum[i] = blk == 0 ? s : ssum[i] + s;
-          }
-        }
-      }
-      __syncthreads();
-      for (int i = tid; i < unc; i += kThreads) {
-        const int ti = ulist[i];
-        a.cand_keys[slot0 + ti] = cand_key(__float_as_uint(ssum[i]), (int32_t)(c0 + cpos[ti]));
-      }
-      if (a.G > 8) load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);   // next chunk: block 0
+      rescore_wide<kFp8>(unc, wave, r, rgrp, wq, kb, ksb, a.scale_log2, a.G,
+                         [&](int i) { return (uint32_t)(c0 + cpos[ulist[i]]); },
+                         [&](int i, float sv) {
+                           const int ti = ulist[i];
+                           a.cand_keys[slot0 + ti] = cand_key(__float_as_uint(sv), (int32_t)(c0 + cpos[ti]));
+                         });
     }
   }
 }
@@ -425,7 +490,6 @@ __global__ __launch_bounds__(kThreads) void candidate_kernel(FastSelArgs a) {
 constexpr int kRsBlk = 1024;   // list entries per re-score block
 constexpr int kRsPer = kRsBlk / kThreads;
 constexpr int kRsBatch = 8;    // wave steps (4 rows each) whose key loads are issued together
-constexpr int kRsTiles = 4;    // more than 8 heads: 16-candidate tiles a wave loads together
 static_assert(kFastSubBins == 64, "one lane per sub-bin");
 static_assert(kMinCandChunkLen % kRsBlk == 0, "blocks tile a chunk");
 
@@ -535,26 +599,13 @@ __global__ __launch_bounds__(kThreads) void cand_rescore_kernel(FastSelArgs a) {
   const int hown = head_of(r);
   uint32_t qp[8][4];   // VALU re-score (up to 8 heads): the scan's row layout
   float Mown = 0.0f, izown = 0.0f;
-  bf16x8_t qf[2][4];   // matrix-core re-score (more heads): Q^T of heads 16 hb + w16, dims 32 s + 8 grp
-  float Mq[2], izq[2];
+  WideQuery wq;        // matrix-core re-score (more heads)
   if constexpr (!kMB) {
     load_query(a.q + (bj * a.Hq + (int64_t)g * a.G) * kHeadDim, a.G, r, qp);
     Mown = hown < a.G ? a.mz[(sel * kMaxHeads + hown) * 2] : 0.0f;
     izown = hown < a.G ? a.mz[(sel * kMaxHeads + hown) * 2 + 1] : 0.0f;
   } else {
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int h = 16 * hb + r;
-      const bool in = h < a.G;
-      const uint16_t* qh = a.q + (bj * a.Hq + (int64_t)g * a.G + (in ? h : 0)) * kHeadDim;
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        const uint4 x = *reinterpret_cast<const uint4*>(qh + 32 * sl + 8 * rgrp);
-        qf[hb][sl] = __builtin_bit_cast(bf16x8_t, in ? x : make_uint4(0u, 0u, 0u, 0u));
-      }
-      Mq[hb] = in ? a.mz[(sel * kMaxHeads + h) * 2] : 0.0f;
-      izq[hb] = in ? a.mz[(sel * kMaxHeads + h) * 2 + 1] : 0.0f;
-    }
+    load_wide_query(a, sel, bj, g, r, rgrp, wq);
   }
 
   // E_k: the sub-bins of the threshold bin from the top, one per lane
@@ -655,71 +706,12 @@ __global__ __launch_bounds__(kThreads) void cand_rescore_kernel(FastSelArgs a) {
           }
         }
       } else {
-        // more than 8 heads: tiles of 16 candidates on the matrix cores.  S = K Q^T with
-        // A = the candidates' key rows (lane: candidate w16 of the tile, dims 32 s + 8 grp)
-        // and B = Q^T of each 16-head block, so lane (head w16, grp) gets the logits of
-        // candidates 4 grp + v; the group sum adds the two blocks, then the 16 head lanes.
-        // Wave w takes tiles w, w + 4, ...; kRsTiles tiles' loads are issued together.
-        const int ntiles = (nu + 15) >> 4;
-        for (int t0 = wave; t0 < ntiles; t0 += 4 * kRsTiles) {
-          bf16x8_t kf[kRsTiles][4];
-          float ks4[kRsTiles][4];
-#pragma unroll
-          for (int u = 0; u < kRsTiles; ++u) {
-            const int t = min(t0 + 4 * u, ntiles - 1);   // past the end: a valid tile, dropped
-            const int i = 16 * t + r;
-            const uint32_t pos = (uint32_t)(c0 + (ulist[i < nu ? i : 16 * t] & 0xFFFFu));
-#pragma unroll
-            for (int sl = 0; sl < 4; ++sl) {
-              if constexpr (kFp8) {
-                const uint2 c = *reinterpret_cast<const uint2*>(kb + (uint64_t)pos * 128 + 32 * sl + 8 * rgrp);
-                kf[u][sl] = __builtin_bit_cast(bf16x8_t, make_uint4(fp8x2_to_bf16x2(c.x, false), fp8x2_to_bf16x2(c.x, true),
-                                                                    fp8x2_to_bf16x2(c.y, false), fp8x2_to_bf16x2(c.y, true)));
-              } else {
-                kf[u][sl] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kb + (uint64_t)pos * 256 + 64 * sl + 16 * rgrp));
-              }
-            }
-            if constexpr (kFp8) {
-#pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                const int iv = 16 * t + 4 * rgrp + v;
-                ks4[u][v] = ksb[c0 + (ulist[iv < nu ? iv : 16 * t] & 0xFFFFu)];
-              }
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < kRsTiles; ++u) {
-            const int t = t0 + 4 * u;
-            if (t < ntiles) {   // wave-uniform
-              float x[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int hb = 0; hb < 2; ++hb) {
-                f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int sl = 0; sl < 4; ++sl) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][sl], qf[hb][sl], d, 0, 0, 0);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                  float l = d[v] * a.scale_log2;
-                  if constexpr (kFp8) l *= ks4[u][v];
-                  x[v] += 16 * hb + r < a.G ? fast_exp2(l - Mq[hb]) * izq[hb] : 0.0f;
-                }
-              }
-#pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                x[v] += dpp<kDppXor1>(x[v]);
-                x[v] += dpp<kDppXor2>(x[v]);
-                x[v] += dpp<kDppMirror8>(x[v]);
-                x[v] += dpp<kDppRor8>(x[v]);
-              }
-              const int iv = 16 * t + 4 * rgrp + r;   // lanes r < 4 write candidate 4 grp + r
-              if (r < 4 && iv < nu) {
-                const float sv = r == 0 ? x[0] : r == 1 ? x[1] : r == 2 ? x[2] : x[3];
-                const uint32_t e = ulist[iv];
-                a.cand_keys[slot0 + (e >> 16)] = cand_key(__float_as_uint(sv), (int32_t)(c0 + (e & 0xFFFFu)));
-              }
-            }
-          }
-        }
+        rescore_wide<kFp8>(nu, wave, r, rgrp, wq, kb, ksb, a.scale_log2, a.G,
+                           [&](int i) { return (uint32_t)(c0 + (ulist[i] & 0xFFFFu)); },
+                           [&](int i, float sv) {
+                             const uint32_t e = ulist[i];
+                             a.cand_keys[slot0 + (e >> 16)] = cand_key(__float_as_uint(sv), (int32_t)(c0 + (e & 0xFFFFu)));
+                           });
       }
       outn += total & 0xFFFFu;
     }
