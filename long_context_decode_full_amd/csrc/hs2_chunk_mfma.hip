@@ -335,6 +335,10 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
 
     // ---- S^T = K Q^T for 4 position tiles x 2 query tiles
     f32x4_t sacc[4][2];
+    // the MFMA groups run at raised wave priority: when the two waves of a SIMD are
+    // in different phases, the matrix core starts as soon as it is free and the
+    // other wave's vector work fills the issue slots in between
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       bf16x8_t kf[4];
@@ -349,6 +353,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
         sacc[pt][qt] = d;
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // raw scores; the log2-domain logit is scale_log2 * s (scale_log2 > 0), formed
     // inside the exp2 as fma(s, scale_log2, -m).  The causal mask only where some
     // position lies beyond the first token's last visible one (wave-uniform branch).
@@ -489,6 +494,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
       // A operands: V^T of dim block d, rows 4grp..4grp+3 of the block's two tiles
       const uint8_t* tr0 = vs + (32 * kb2 + 4 * grp + (w16 >> 2)) * kVRow + 8 * (w16 & 3);
       const uint8_t* tr1 = tr0 + 16 * kVRow;
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tr0 + 32 * d));
@@ -502,6 +508,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
           o[qt][d] = mfma16(av, pl[qt], o[qt][d]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     if constexpr (kBlockMode) {
       // log2 of the sum of 2^logit over this 64-position block, per (token, head)
