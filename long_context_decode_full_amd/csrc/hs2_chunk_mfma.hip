@@ -13,8 +13,10 @@
 // 256 / kGp tokens of kGp head slots each (kGp = 8, 16 or 32: the group size rounded
 // up; slots >= G are zero), so it reads every K/V row of its split once for all of
 // them.  Per iteration of 64 positions the K and V tiles go through LDS (two stages:
-// the next tiles are stored while the current ones are read, one barrier per
-// iteration); wave w owns query rows 32w .. 32w+31 (two tiles of 16).  The scores are
+// the next tiles are stored while the current ones are read; one barrier after those
+// stores, so that the first K fragments of the next tile can be read during the
+// current one, and one at the end of the iteration); wave w owns 32 / kGp tokens as two query tiles of 16 rows, a token's
+// heads spread over both tiles (head = (kGp / 2) tile + lane % (kGp / 2)).  The scores are
 // formed transposed, S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K rows from the K
 // tile, lane: position i, dims 32s + 8grp; B = Q^T from registers, lane: query row
 // i, the same dims), so a lane's accumulators are 4 positions (4grp + v) of one query
@@ -27,10 +29,10 @@
 //     raised lazily by 8 (log2 units) with a max over the 4 row groups.
 //   record per (token, position): log2 of the sum over the token's heads of 2^logit,
 //     from the probabilities already formed: with U the largest running maximum of
-//     the token's heads, e = U + log2 sum_h p_h 2^(m_h - U), a DPP sum over the
-//     token's head lanes (and the second tile for 32 heads); sums below 2^-100 (terms
-//     lost to underflow could matter there) take the exact form on a wave-uniform
-//     branch.
+//     the token's heads, e = U + log2 sum_h p_h 2^(m_h - U), the two tiles added
+//     in-lane, then a DPP reduce-scatter over the token's kGp / 2 head lanes; sums
+//     below 2^-100 (terms lost to underflow could matter there) take the exact form on
+//     a wave-uniform branch.
 #include "hs2_rowops.h"
 
 namespace hs2 {
@@ -46,6 +48,7 @@ constexpr int kCThreads = 512;                 // 8 waves
 constexpr int kCRows = 256;                    // query rows per workgroup
 constexpr int kCPos = 64;                      // positions per iteration
 constexpr float kCSlack = 8.0f;
+constexpr int kVPre = 4;                       // V^T operands read ahead of the records (of 8)
 constexpr float kMFloor = -1.0e30f;            // initial running maximum (below any logit)
 // Staged rows are padded so that the fragment reads spread over the LDS banks: the K
 // rows (16-byte reads, lane = row) by 16 bytes, the V rows (8-byte transposed reads,
@@ -71,13 +74,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
 }
 
-// Reductions over the lanes of one token's heads inside a 16-lane row: 8 lanes
-// (lanes 0-7 and 8-15 separately) or all 16.
+// Reductions over the lanes of one token's heads inside a 16-lane row: 4 lanes (each
+// quad separately), 8 (lanes 0-7 and 8-15 separately) or all 16.
 template <int kLanes>
 __device__ __forceinline__ float head_sum(float x) {
   x += dpp<kDppXor1>(x);
   x += dpp<kDppXor2>(x);
-  x += dpp<kDppMirror8>(x);
+  if constexpr (kLanes >= 8) x += dpp<kDppMirror8>(x);
   if constexpr (kLanes == 16) x += dpp<kDppRor8>(x);
   return x;
 }
@@ -85,7 +88,7 @@ template <int kLanes>
 __device__ __forceinline__ float head_max(float x) {
   x = fmaxf(x, dpp<kDppXor1>(x));
   x = fmaxf(x, dpp<kDppXor2>(x));
-  x = fmaxf(x, dpp<kDppMirror8>(x));
+  if constexpr (kLanes >= 8) x = fmaxf(x, dpp<kDppMirror8>(x));
   if constexpr (kLanes == 16) x = fmaxf(x, dpp<kDppRor8>(x));
   return x;
 }
@@ -106,62 +109,36 @@ __device__ __forceinline__ float across_groups(float x) {
   return kMax ? fmaxf(__uint_as_float(c0), __uint_as_float(c1)) : __uint_as_float(c0) + __uint_as_float(c1);
 }
 
-// Sum over one token's heads of a per-lane value: the head lanes of the row (8 or
-// 16) and, for 32 heads, the two query tiles of the wave.
+// A token's kGp head slots are kGp / 2 lanes of the row (w16 % (kGp / 2)) in both query
+// tiles of the wave: head = (kGp / 2) qt + w16 % (kGp / 2).  Sums and maxima over the
+// token's heads therefore combine the two tiles in-lane and kGp / 2 lanes by DPP.
 template <int kGp>
 __device__ __forceinline__ void token_sums(const float (&x)[2], float (&out)[2]) {
-  if constexpr (kGp == 8) {
-    out[0] = head_sum<8>(x[0]);
-    out[1] = head_sum<8>(x[1]);
-  } else if constexpr (kGp == 16) {
-    out[0] = head_sum<16>(x[0]);
-    out[1] = head_sum<16>(x[1]);
-  } else {
-    const float s = head_sum<16>(x[0]) + head_sum<16>(x[1]);
-    out[0] = s;
-    out[1] = s;
-  }
+  const float s = head_sum<kGp / 2>(x[0]) + head_sum<kGp / 2>(x[1]);
+  out[0] = s;
+  out[1] = s;
 }
 template <int kGp>
 __device__ __forceinline__ void token_maxes(const float (&x)[2], float (&out)[2]) {
-  if constexpr (kGp == 8) {
-    out[0] = head_max<8>(x[0]);
-    out[1] = head_max<8>(x[1]);
-  } else if constexpr (kGp == 16) {
-    out[0] = head_max<16>(x[0]);
-    out[1] = head_max<16>(x[1]);
-  } else {
-    const float s = fmaxf(head_max<16>(x[0]), head_max<16>(x[1]));
-    out[0] = s;
-    out[1] = s;
-  }
+  const float s = fmaxf(head_max<kGp / 2>(x[0]), head_max<kGp / 2>(x[1]));
+  out[0] = s;
+  out[1] = s;
 }
 
-// Records of a 32-position block: the values a lane contributes, one per (query tile,
-// position tile of the block, position v), are reduce-scattered over the lanes that hold
-// the token's heads (each DPP step halves the values a lane keeps and adds its
-// partner's other half), so every lane ends with the full head sum of one record:
-//   8 head slots:  8 values (4 qt + v) of one position tile over the 8 lanes of a
-//                 half-row, lane index w16 & 7 (two passes, one per position tile);
-//   16 slots:     16 values (8 tt + 4 qt + v) over the 16 lanes of a row, index w16;
-//   32 slots:      8 values (4 tt + v), the two query tiles (one token) added first, over
-//                 the 16 lanes of a row: index (w16 >> 1), lanes w16 and w16 ^ 1 alike.
-struct RecSlot {
-  int qt, tt, v;
-};
+// Records of a 32-position block: every lane forms, for each of the block's 8
+// positions it holds (index 4 tt + v: position tile tt of the block, position
+// 4 grp + v of the tile), its two tiles' c p summed; these 8 values are then
+// reduce-scattered over the token's kGp / 2 head lanes (each DPP step halves the
+// values a lane keeps and adds its partner's other half), so that every lane ends with
+// whole records:
+//   8 head slots:  4 lanes, 2 records a lane: indices 2 (w16 & 3) + j (adjacent positions);
+//   16 slots:      8 lanes, 1 record a lane: index w16 & 7;
+//   32 slots:     16 lanes, 1 record per lane pair: index w16 >> 1 (lanes w16, w16 ^ 1 alike).
 template <int kGp>
-constexpr int kRecValsOf = kGp == 16 ? 16 : 8;
+constexpr int kRecOut = kGp == 8 ? 2 : 1;
 template <int kGp>
-constexpr int kRecPassesOf = kGp == 8 ? 2 : 1;
-template <int kGp>
-__device__ __forceinline__ RecSlot rec_slot(int i, int pass) {
-  if constexpr (kGp == 8) return {i >> 2, pass, i & 3};
-  else if constexpr (kGp == 16) return {(i >> 2) & 1, i >> 3, i & 3};
-  else return {0, i >> 2, i & 3};
-}
-template <int kGp>
-__device__ __forceinline__ int own_index(int w16) {
-  return kGp == 8 ? (w16 & 7) : kGp == 16 ? w16 : (w16 >> 1);
+__device__ __forceinline__ int rec_index(int w16, int j) {
+  return kGp == 8 ? 2 * (w16 & 3) + j : kGp == 16 ? (w16 & 7) : (w16 >> 1);
 }
 template <int kGp>
 __device__ __forceinline__ bool rec_writer(int w16) {
@@ -178,32 +155,30 @@ __device__ __forceinline__ void rs_step(const float* x, float* y, bool upper) {
   }
 }
 template <int kGp>
-__device__ __forceinline__ float reduce_scatter(const float (&x)[kRecValsOf<kGp>], int w16) {
+__device__ __forceinline__ void reduce_scatter(const float (&x)[8], int w16, float (&out)[kRecOut<kGp>]) {
   const bool b3 = (w16 & 8) != 0, b2 = (w16 & 4) != 0, b1 = (w16 & 2) != 0, b0 = (w16 & 1) != 0;
-  float a8[8], a4[4], a2[2], a1[1];
+  float a4[4], a2[2], a1[1];
   if constexpr (kGp == 8) {
+    rs_step<kDppXor2, 4>(x, a4, b1);
+    rs_step<kDppXor1, 2>(a4, a2, b0);
+    out[0] = a2[0];
+    out[1] = a2[1];
+  } else if constexpr (kGp == 16) {
     rs_step<kDppMirror8, 4>(x, a4, b2);   // partner 7 - i: bit 2 differs
     rs_step<kDppXor2, 2>(a4, a2, b1);
     rs_step<kDppXor1, 1>(a2, a1, b0);
-    return a1[0];
-  } else if constexpr (kGp == 16) {
-    rs_step<kDppRor8, 8>(x, a8, b3);
-    rs_step<kDppMirror8, 4>(a8, a4, b2);
-    rs_step<kDppXor2, 2>(a4, a2, b1);
-    rs_step<kDppXor1, 1>(a2, a1, b0);
-    return a1[0];
+    out[0] = a1[0];
   } else {
     rs_step<kDppRor8, 4>(x, a4, b3);
     rs_step<kDppMirror8, 2>(a4, a2, b2);
     rs_step<kDppXor2, 1>(a2, a1, b1);
-    return a1[0] + dpp<kDppXor1>(a1[0]);
+    out[0] = a1[0] + dpp<kDppXor1>(a1[0]);
   }
 }
 
 template <int kGp, bool kBlockMode>   // false: records + key histograms; true: per-block sums
 __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   constexpr int kTPW = tokens_per_wg<kGp>();
-  constexpr int kRecVals = kRecValsOf<kGp>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[chunk_lds_bytes<kGp, kBlockMode>()];
   uint32_t* shist = reinterpret_cast<uint32_t*>(lds + 2 * kStage);
 
@@ -255,9 +230,8 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   bf16x8_t qf[2][4];   // Q^T fragments (B operand): dims 32s + 8grp of the lane's query row
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    const int r = 32 * wave + 16 * qt + w16;
-    tokl[qt] = r / kGp;
-    head[qt] = r % kGp;
+    tokl[qt] = (32 / kGp) * wave + w16 / (kGp / 2);   // the same in both tiles
+    head[qt] = (kGp / 2) * qt + w16 % (kGp / 2);
     valid[qt] = tokl[qt] < ntok && head[qt] < a.G;
     const int64_t pp = ctx - a.Lq + tok0 + tokl[qt];
     pj[qt] = (int32_t)pp;
@@ -324,6 +298,15 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   const float sl2 = a.scale_log2;
   const int32_t first_pj = (int32_t)(ctx - a.Lq + tok0);   // the workgroup's first token sees least
 
+  // K fragments of the first position tile, read one iteration ahead (the next stage
+  // is visible once the barrier after its stores has passed)
+  auto read_kf = [&](const uint8_t* ks, int pt, bf16x8_t (&kf)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(ks + (pt * 16 + w16) * kKRow + 64 * s + 16 * grp));
+  };
+  bf16x8_t kpre[4];
+  if (nit > 0) read_kf(lds, 0, kpre);
   for (int it = 0; it < nit; ++it) {
     const int32_t P0 = (int32_t)p_begin + it * kCPos;
     const uint8_t* ks = lds + (it & 1) * kStage;
@@ -332,6 +315,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
     // previous iteration before the barrier that ended it), then the loads after them
     store_tiles(lds + ((it + 1) & 1) * kStage);
     load_tiles(P0 + 2 * kCPos);
+    __syncthreads();   // the next stage is complete
 
     // ---- S^T = K Q^T for 4 position tiles x 2 query tiles
     f32x4_t sacc[4][2];
@@ -342,9 +326,12 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       bf16x8_t kf[4];
+      if (pt == 0) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(ks + (pt * 16 + w16) * kKRow + 64 * s + 16 * grp));
+        for (int s = 0; s < 4; ++s) kf[s] = kpre[s];
+      } else {
+        read_kf(ks, pt, kf);
+      }
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
         f32x4_t d = {0.f, 0.f, 0.f, 0.f};
@@ -409,6 +396,21 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
     float bsum[2] = {0.f, 0.f};
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
+      // A operands of the block's P V: V^T of dim block d, rows 4grp..4grp+3 of the
+      // block's two tiles; the first kVPre of them are read here, so that their LDS
+      // latency passes under the probabilities and records
+      const uint8_t* tr0 = vs + (32 * kb2 + 4 * grp + (w16 >> 2)) * kVRow + 8 * (w16 & 3);
+      const uint8_t* tr1 = tr0 + 16 * kVRow;
+      auto read_vt = [&](int d) {
+        const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tr0 + 32 * d));
+        const s16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tr1 + 32 * d));
+        const uint2 w0 = __builtin_bit_cast(uint2, x0);
+        const uint2 w1 = __builtin_bit_cast(uint2, x1);
+        return as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+      };
+      bf16x8_t avp[kVPre];
+#pragma unroll
+      for (int d = 0; d < kVPre; ++d) avp[d] = read_vt(d);
       float p[2][2][4];   // [qt][tile of the block][v]
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
@@ -423,27 +425,34 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
           }
       if constexpr (want_rec) {
         // records of the block's 32 positions: per (token, position) the sum over the
-        // token's heads of c p, reduce-scattered over the head lanes so that every lane
-        // ends with one record (rec_slot), then the exact form where a sum underflowed
+        // token's heads of c p (both tiles in-lane, then the head lanes), then the exact
+        // form where a sum underflowed; a token's rows share tokl, pj and w0j
+        constexpr int kOut = kRecOut<kGp>;
+        float x[8];
 #pragma unroll
-        for (int pass = 0; pass < kRecPassesOf<kGp>; ++pass) {
-        float x[kRecVals];
+        for (int i = 0; i < 8; ++i) x[i] = p[0][i >> 2][i & 3] * c[0] + p[1][i >> 2][i & 3] * c[1];
+        float sum[kOut];
+        reduce_scatter<kGp>(x, w16, sum);
+        const int tl = tokl[0];
+        int32_t pos[kOut];
+        bool live[kOut], tiny[kOut];
+        float e[kOut];
+        bool any_tiny = false;
 #pragma unroll
-        for (int i = 0; i < kRecVals; ++i) {
-          const RecSlot rs = rec_slot<kGp>(i, pass);
-          x[i] = kGp == 32 ? p[0][rs.tt][rs.v] * c[0] + p[1][rs.tt][rs.v] * c[1] : p[rs.qt][rs.tt][rs.v] * c[rs.qt];
+        for (int j = 0; j < kOut; ++j) {
+          const int idx = rec_index<kGp>(w16, j);
+          pos[j] = P0 + (2 * kb2 + (idx >> 2)) * 16 + 4 * grp + (idx & 3);
+          live[j] = rec_writer<kGp>(w16) && pos[j] <= pj[0] && tl < ntok;
+          tiny[j] = live[j] && !(sum[j] >= 0x1p-100f);
+          any_tiny |= tiny[j];
+          e[j] = U[0] + __builtin_amdgcn_logf(sum[j]);
         }
-        const float sum = reduce_scatter<kGp>(x, w16);
-        const RecSlot own = rec_slot<kGp>(own_index<kGp>(w16), pass);
-        const int32_t pos = P0 + (2 * kb2 + own.tt) * 16 + 4 * grp + own.v;
-        const int tl = own.qt ? tokl[1] : tokl[0];
-        const bool live = rec_writer<kGp>(w16) && pos <= (own.qt ? pj[1] : pj[0]) && tl < ntok;
-        const bool tiny = live && !(sum >= 0x1p-100f);
-        float e = (own.qt ? U[1] : U[0]) + __builtin_amdgcn_logf(sum);
-        if (wave_any(tiny)) {
+        if (wave_any(any_tiny)) {
           // exact: max and sum of 2^(l - max) over the token's heads, for every value of
           // the lane (all-reduce: every lane takes part in the DPP reductions)
-          float ex_own = 0.0f;
+          float ex_own[kOut];
+#pragma unroll
+          for (int j = 0; j < kOut; ++j) ex_own[j] = 0.0f;
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -458,22 +467,33 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
                 ex[qt] = fast_exp2(lv[qt] - rmax[qt]);
               }
               token_sums<kGp>(ex, sums);
+              const float val = rmax[0] + __builtin_amdgcn_logf(sums[0]);
 #pragma unroll
-              for (int qt = 0; qt < 2; ++qt) {
-                const bool mine = own.tt == tt && own.v == v && (kGp == 32 || own.qt == qt);
-                ex_own = mine ? rmax[qt] + __builtin_amdgcn_logf(sums[qt]) : ex_own;
-              }
+              for (int j = 0; j < kOut; ++j) ex_own[j] = rec_index<kGp>(w16, j) == 4 * tt + v ? val : ex_own[j];
             }
-          e = tiny ? ex_own : e;
+#pragma unroll
+          for (int j = 0; j < kOut; ++j) e[j] = tiny[j] ? ex_own[j] : e[j];
         }
-        if (live) {
-          const uint16_t rec = __builtin_bit_cast(uint16_t, (_Float16)e);
-          a.records[(sel_tok0 + (int64_t)tl * a.Hkv) * a.logit_stride + pos] = rec;
-          if (pos < (own.qt ? w0j[1] : w0j[0])) {
-            const uint32_t bin = half_order_key(rec) >> kFastShift;
+        uint16_t rec[kOut];
+#pragma unroll
+        for (int j = 0; j < kOut; ++j) rec[j] = __builtin_bit_cast(uint16_t, (_Float16)e[j]);
+        uint16_t* rrow = a.records + (sel_tok0 + (int64_t)tl * a.Hkv) * a.logit_stride;
+        if constexpr (kOut == 2) {
+          // adjacent positions (pos[0] is even): one 4-byte store where both are visible
+          // (live[1] implies live[0])
+          if (live[1])
+            *reinterpret_cast<uint32_t*>(rrow + pos[0]) = (uint32_t)rec[0] | ((uint32_t)rec[1] << 16);
+          else if (live[0])
+            rrow[pos[0]] = rec[0];
+        } else {
+          if (live[0]) rrow[pos[0]] = rec[0];
+        }
+#pragma unroll
+        for (int j = 0; j < kOut; ++j) {
+          if (live[j] && pos[j] < w0j[0]) {
+            const uint32_t bin = half_order_key(rec[j]) >> kFastShift;
             atomicAdd(&shist[tl * kHistWords + (bin >> 1)], (bin & 1) ? 65536u : 1u);
           }
-        }
         }
       }
       // B operands: P^T of the block, k slot 8 grp + u <-> tile u / 4, position 4 grp + u % 4
@@ -491,17 +511,11 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
         ph[qt] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
         pl[qt] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
-      // A operands: V^T of dim block d, rows 4grp..4grp+3 of the block's two tiles
-      const uint8_t* tr0 = vs + (32 * kb2 + 4 * grp + (w16 >> 2)) * kVRow + 8 * (w16 & 3);
-      const uint8_t* tr1 = tr0 + 16 * kVRow;
+      if (kb2 == 1 && it + 1 < nit) read_kf(lds + ((it + 1) & 1) * kStage, 0, kpre);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tr0 + 32 * d));
-        const s16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tr1 + 32 * d));
-        const uint2 w0 = __builtin_bit_cast(uint2, x0);
-        const uint2 w1 = __builtin_bit_cast(uint2, x1);
-        const bf16x8_t av = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+        const bf16x8_t av = d < kVPre ? avp[d < kVPre ? d : 0] : read_vt(d);
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           o[qt][d] = mfma16(av, ph[qt], o[qt][d]);
