@@ -474,7 +474,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps first: the GPU reaches its sustained clocks after a few tens of ms")
     ap.add_argument("--workload", default="million",
-                    help="tiny | batched | fp8_256k | million | chunk | mqa_million | mqa_chunk; KV Bridging: "
+                    help="tiny | batched | fp8_256k | million | chunk | mqa_million | mqa_chunk | fp8_chunk; KV Bridging: "
                          "bridge_prefill | bridge_prefill_bf16 | bridge_mqa | bridge_decode; decode loop: "
                          "decode_loop_million | decode_loop_batched | decode_loop_tiny")
     ap.add_argument("--select", default="token", choices=["token", "block", "gen1"],
@@ -484,6 +484,9 @@ def main():
                          "over each sparse layer's own local ring)")
     ap.add_argument("--deterministic", action="store_true",
                     help="fixed step shares in the context scan (bitwise reproducible, slower)")
+    ap.add_argument("--chunk-per-token", action="store_true",
+                    help="query chunks: the decode scan once per token (HS2_FLAG_CHUNK_PER_TOKEN) "
+                         "instead of the chunk kernel, for comparison")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
@@ -511,7 +514,7 @@ def main():
     if args.workload in DECODE_LOOPS:
         bench_decode_loop(args)
         return
-    from long_context_decode_full_amd import HS2_FLAG_DETERMINISTIC
+    from long_context_decode_full_amd import HS2_FLAG_CHUNK_PER_TOKEN, HS2_FLAG_DETERMINISTIC
     from long_context_decode_full_amd import workloads as wl
     from long_context_decode_full_amd.runner import HybridBlockDevice
 
@@ -524,8 +527,9 @@ def main():
     if args.select == "gen1":
         # each sparse layer's own local ring: the 128-token window of every query token
         rings = wl.make_local_rings(w, 128 + w.q_len - 1, seed=w.seed + 100)
-    dev = HybridBlockDevice(inp, device="cuda:0", mode=args.select, local_rings=rings,
-                            flags=HS2_FLAG_DETERMINISTIC if args.deterministic else 0)
+    flags = (HS2_FLAG_DETERMINISTIC if args.deterministic else 0) | \
+            (HS2_FLAG_CHUNK_PER_TOKEN if args.chunk_per_token else 0)
+    dev = HybridBlockDevice(inp, device="cuda:0", mode=args.select, local_rings=rings, flags=flags)
     torch.cuda.synchronize()
 
     # Auxiliary measurements first (they are reported, not part of the timed steps):
@@ -597,6 +601,7 @@ def main():
             "batch": w.batch, "ctx_tokens": ctx, "q_len": w.q_len,
             "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "kv_dtype": w.kv_dtype,
             "deterministic": bool(args.deterministic),
+            "chunk_per_token": bool(args.chunk_per_token),
         },
         "kv_gbps": achieved,
         "scan_us": scan_avg_s * 1e6,

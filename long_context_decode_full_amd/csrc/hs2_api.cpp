@@ -91,13 +91,12 @@ hs2_status validate_desc(const hs2_attn_desc* d) {
 
 bool has_flag(const hs2_attn_desc* d, uint32_t f) { return (d->flags & f) != 0u; }
 
-// Token selection for a chunk of query tokens (q_len > 1, bf16 cache) runs the
+// Token selection for a chunk of query tokens (q_len > 1, bf16 or fp8 cache) runs the
 // matrix-core chunk kernel, which reads each KV row once for 256 query rows (32 tokens
 // of up to 8 heads, 16 of up to 16, 8 of up to 32).
 // HS2_FLAG_CHUNK_PER_TOKEN runs the decode scan once per token instead (comparison).
 bool chunk_path(const hs2_attn_desc* d) {
-  return d->q_len > 1 && d->kv_dtype == HS2_KV_BF16 && d->select_mode == HS2_SELECT_TOKEN &&
-         !has_flag(d, HS2_FLAG_CHUNK_PER_TOKEN);
+  return d->q_len > 1 && d->select_mode == HS2_SELECT_TOKEN && !has_flag(d, HS2_FLAG_CHUNK_PER_TOKEN);
 }
 // More than 8 query heads per KV head: the matrix-core scans with 16-head blocks, the
 // matrix-core gather and block-wise re-scoring; the logits path (probs) keeps 8 head
@@ -106,10 +105,10 @@ bool wide_group(const hs2_attn_desc* d) { return d->n_q_heads / d->n_kv_heads > 
 // The block comparator for a chunk (block sizes that are multiples of 64) takes its
 // block masses from the same kernel's per-block sums instead of per-position logits.
 bool chunk_block_path(const hs2_attn_desc* d) {
-  return d->q_len > 1 && d->kv_dtype == HS2_KV_BF16 && d->select_mode == HS2_SELECT_BLOCK &&
-         d->block_size % 64 == 0 && !has_flag(d, HS2_FLAG_CHUNK_PER_TOKEN);
+  return d->q_len > 1 && d->select_mode == HS2_SELECT_BLOCK && d->block_size % 64 == 0 &&
+         !has_flag(d, HS2_FLAG_CHUNK_PER_TOKEN);
 }
-// The block comparator otherwise (decode, per-token and fp8 chunks): per-32-position
+// The block comparator otherwise (decode, per-token chunks): per-32-position
 // block sums from the decode scan, for up to 8 query heads per KV head.
 // HS2_FLAG_FORCE_LOGITS or HS2_FLAG_SCAN_VALU keep it on the logits path.
 bool scan_block_path(const hs2_attn_desc* d) {
@@ -343,7 +342,7 @@ hs2_status block_sums_select(const hs2_attn_desc* desc, const Layout& L, ScanArg
   sa.split_len = L.rec_split_len;
   event_record(ev, true, stream);
   const hipError_t e = chunk_block_path(desc)
-                           ? launch_chunk_mfma(sa, desc->batch, stream)
+                           ? launch_chunk_mfma(sa, desc->batch, desc->kv_dtype == HS2_KV_FP8_E4M3FN, stream)
                            : launch_scan_mfma_blocks(sa, desc->kv_dtype == HS2_KV_FP8_E4M3FN, desc->batch, stream);
   event_record(ev, false, stream);
   if (e != hipSuccess) return HS2_ERR_LAUNCH;
@@ -433,7 +432,7 @@ static hs2_status full_select_launch(const hs2_attn_desc* desc, const Layout& L,
   event_record(ev, true, stream);
   // record path: matrix-core scan (HS2_FLAG_SCAN_VALU selects the VALU scan instead)
   const bool mfma = fast && (wide_group(desc) || !has_flag(desc, HS2_FLAG_SCAN_VALU));
-  const hipError_t e = (fast && chunk_path(desc)) ? launch_chunk_mfma(sa, desc->batch, stream)
+  const hipError_t e = (fast && chunk_path(desc)) ? launch_chunk_mfma(sa, desc->batch, fp8, stream)
                  : mfma                     ? launch_scan_mfma(sa, fp8, desc->batch, stream)
                                             : launch_scan_dense(sa, fp8, fast, desc->batch, stream);
   event_record(ev, false, stream);

@@ -59,11 +59,15 @@ constexpr int kKTile = kCPos * kKRow;
 constexpr int kVTile = kCPos * kVRow;
 constexpr int kStage = kKTile + kVTile;        // K and V tiles of one iteration
 constexpr int kHistWords = kFastBins / 2;      // two u16 counters per word
+// fp8 caches: the per-position K and V scales of both stages, after the tiles
+constexpr int kScaleBytes = 2 * 2 * kCPos * 4;
 
 template <int kGp>
 constexpr int tokens_per_wg() { return kCRows / kGp; }
-template <int kGp, bool kBlockMode>
-constexpr int chunk_lds_bytes() { return 2 * kStage + (kBlockMode ? 0 : tokens_per_wg<kGp>() * kHistWords * 4); }
+template <int kGp, bool kBlockMode, bool kFp8>
+constexpr int chunk_lds_bytes() {
+  return 2 * kStage + (kFp8 ? kScaleBytes : 0) + (kBlockMode ? 0 : tokens_per_wg<kGp>() * kHistWords * 4);
+}
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -176,11 +180,17 @@ __device__ __forceinline__ void reduce_scatter(const float (&x)[8], int w16, flo
   }
 }
 
-template <int kGp, bool kBlockMode>   // false: records + key histograms; true: per-block sums
+// kBlockMode: false: records + key histograms; true: per-block sums.  kFp8: the cache
+// holds E4M3FN codes with one fp32 scale per (position, KV head): the tiles are
+// converted to bf16 (exactly) as they are staged, the scores take the K scale of their
+// position, and the P^T operands of P V the V scale.
+template <int kGp, bool kBlockMode, bool kFp8>
 __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   constexpr int kTPW = tokens_per_wg<kGp>();
-  __shared__ __attribute__((aligned(16))) uint8_t lds[chunk_lds_bytes<kGp, kBlockMode>()];
-  uint32_t* shist = reinterpret_cast<uint32_t*>(lds + 2 * kStage);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[chunk_lds_bytes<kGp, kBlockMode, kFp8>()];
+  uint32_t* shist = reinterpret_cast<uint32_t*>(lds + 2 * kStage + (kFp8 ? kScaleBytes : 0));
+  // per-position scales of stage st: K (kv = 0) or V (kv = 1)
+  auto stage_scales = [&](int st, int kv) { return reinterpret_cast<float*>(lds + 2 * kStage) + (2 * st + kv) * kCPos; };
 
   // blockIdx.x = split * token groups + group: the groups of one split are adjacent
   const int n_tgroups = (a.Lq + kTPW - 1) / kTPW;
@@ -245,8 +255,11 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   }
 
   const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
-  const uint8_t* kb = a.k + head_row0 * 256;
-  const uint8_t* vb = a.v + head_row0 * 256;
+  constexpr int kRowBytes = kFp8 ? 128 : 256;   // bytes of one cache row
+  const uint8_t* kb = a.k + head_row0 * kRowBytes;
+  const uint8_t* vb = a.v + head_row0 * kRowBytes;
+  const float* ksb = kFp8 ? a.k_scale + head_row0 : nullptr;
+  const float* vsb = kFp8 ? a.v_scale + head_row0 : nullptr;
 
   f32x4_t o[2][8];     // O^T: dims 16 bb + 4 grp + v of the lane's query row
   float m[2], z[2];    // running maximum (log2 units, equal in the 4 row groups), this lane's share of Z
@@ -270,28 +283,61 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
 
   const int nit = p_end > p_begin ? (int)((p_end - p_begin + kCPos - 1) / kCPos) : 0;
   const int32_t last = (int32_t)(p_end - 1);
-  // this thread's share of a tile load: rows (tid >> 4) + 32 r, 16 bytes at (tid & 15)
-  const int lrow = tid >> 4, lcol = (tid & 15) * 16;
-  // (named registers, not arrays: small arrays live across the loop got placed in
-  // LDS / scratch by the compiler)
+  // this thread's share of a tile load: bf16 rows (tid >> 4) + 32 r, 16 bytes at
+  // (tid & 15); fp8 row (tid >> 3), 16 codes at (tid & 7), and with tid < 64 the K and V
+  // scales of position tid.  (Named registers, not arrays: small arrays live across the
+  // loop got placed in LDS / scratch by the compiler.)
+  const int lrow = kFp8 ? (tid >> 3) : (tid >> 4);
+  const int lcol = kFp8 ? (tid & 7) * 16 : (tid & 15) * 16;
   uint4 kr0, kr1, vr0, vr1;
+  float ksr = 0.0f, vsr = 0.0f;
   auto load_tiles = [&](int32_t base) {
     const uint32_t row0 = (uint32_t)min(base + lrow, last);
-    const uint32_t row1 = (uint32_t)min(base + lrow + 32, last);
-    kr0 = *reinterpret_cast<const uint4*>(kb + (uint64_t)row0 * 256 + lcol);
-    kr1 = *reinterpret_cast<const uint4*>(kb + (uint64_t)row1 * 256 + lcol);
-    vr0 = *reinterpret_cast<const uint4*>(vb + (uint64_t)row0 * 256 + lcol);
-    vr1 = *reinterpret_cast<const uint4*>(vb + (uint64_t)row1 * 256 + lcol);
+    kr0 = *reinterpret_cast<const uint4*>(kb + (uint64_t)row0 * kRowBytes + lcol);
+    vr0 = *reinterpret_cast<const uint4*>(vb + (uint64_t)row0 * kRowBytes + lcol);
+    if constexpr (kFp8) {
+      if (tid < kCPos) {
+        const uint32_t srow = (uint32_t)min(base + tid, last);
+        ksr = ksb[srow];
+        vsr = vsb[srow];
+      }
+    } else {
+      const uint32_t row1 = (uint32_t)min(base + lrow + 32, last);
+      kr1 = *reinterpret_cast<const uint4*>(kb + (uint64_t)row1 * 256 + lcol);
+      vr1 = *reinterpret_cast<const uint4*>(vb + (uint64_t)row1 * 256 + lcol);
+    }
   };
-  auto store_tiles = [&](uint8_t* st) {
-    *reinterpret_cast<uint4*>(st + lrow * kKRow + lcol) = kr0;
-    *reinterpret_cast<uint4*>(st + (lrow + 32) * kKRow + lcol) = kr1;
-    *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + lcol) = vr0;
-    *reinterpret_cast<uint4*>(st + kKTile + (lrow + 32) * kVRow + lcol) = vr1;
+  auto store_tiles = [&](int stg) {
+    uint8_t* st = lds + stg * kStage;
+    if constexpr (kFp8) {
+      // 16 codes -> 16 bf16 (exact), bytes 2 lcol .. 2 lcol + 31 of the staged row
+      auto widen = [](uint4 c, uint4& lo, uint4& hi) {
+        lo = make_uint4(fp8x2_to_bf16x2(c.x, false), fp8x2_to_bf16x2(c.x, true), fp8x2_to_bf16x2(c.y, false),
+                        fp8x2_to_bf16x2(c.y, true));
+        hi = make_uint4(fp8x2_to_bf16x2(c.z, false), fp8x2_to_bf16x2(c.z, true), fp8x2_to_bf16x2(c.w, false),
+                        fp8x2_to_bf16x2(c.w, true));
+      };
+      uint4 lo, hi;
+      widen(kr0, lo, hi);
+      *reinterpret_cast<uint4*>(st + lrow * kKRow + 2 * lcol) = lo;
+      *reinterpret_cast<uint4*>(st + lrow * kKRow + 2 * lcol + 16) = hi;
+      widen(vr0, lo, hi);
+      *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + 2 * lcol) = lo;
+      *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + 2 * lcol + 16) = hi;
+      if (tid < kCPos) {
+        stage_scales(stg, 0)[tid] = ksr;
+        stage_scales(stg, 1)[tid] = vsr;
+      }
+    } else {
+      *reinterpret_cast<uint4*>(st + lrow * kKRow + lcol) = kr0;
+      *reinterpret_cast<uint4*>(st + (lrow + 32) * kKRow + lcol) = kr1;
+      *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + lcol) = vr0;
+      *reinterpret_cast<uint4*>(st + kKTile + (lrow + 32) * kVRow + lcol) = vr1;
+    }
   };
   if (nit > 0) {
     load_tiles((int32_t)p_begin);
-    store_tiles(lds);
+    store_tiles(0);
     load_tiles((int32_t)p_begin + kCPos);
   }
   __syncthreads();   // stage 0 and the cleared histograms are ready
@@ -313,7 +359,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
     const uint8_t* vs = ks + kKTile;
     // the next iteration's tiles into the other stage (its last readers finished the
     // previous iteration before the barrier that ended it), then the loads after them
-    store_tiles(lds + ((it + 1) & 1) * kStage);
+    store_tiles((it + 1) & 1);
     load_tiles(P0 + 2 * kCPos);
     __syncthreads();   // the next stage is complete
 
@@ -344,13 +390,18 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
     // raw scores; the log2-domain logit is scale_log2 * s (scale_log2 > 0), formed
     // inside the exp2 as fma(s, scale_log2, -m).  The causal mask only where some
     // position lies beyond the first token's last visible one (wave-uniform branch).
+    // (fp8: the score of position i is scale_i * q.k_i, k_i the stored codes)
     float l[2][4][4];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int pt = 0; pt < 4; ++pt) {
+      float4 ksc = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+      if constexpr (kFp8) ksc = *reinterpret_cast<const float4*>(stage_scales(it & 1, 0) + pt * 16 + 4 * grp);
+      const float kv4[4] = {ksc.x, ksc.y, ksc.z, ksc.w};
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
+      for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) l[qt][pt][v] = sacc[pt][qt][v];
+        for (int v = 0; v < 4; ++v) l[qt][pt][v] = kFp8 ? sacc[pt][qt][v] * kv4[v] : sacc[pt][qt][v];
+    }
     if (P0 + kCPos - 1 > first_pj) {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
@@ -497,14 +548,26 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
         }
       }
       // B operands: P^T of the block, k slot 8 grp + u <-> tile u / 4, position 4 grp + u % 4
+      // (fp8: times the V scale of the position)
+      float vsc[2][4] = {{1.0f, 1.0f, 1.0f, 1.0f}, {1.0f, 1.0f, 1.0f, 1.0f}};
+      if constexpr (kFp8) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const float4 s4 = *reinterpret_cast<const float4*>(stage_scales(it & 1, 1) + (2 * kb2 + tt) * 16 + 4 * grp);
+          vsc[tt][0] = s4.x;
+          vsc[tt][1] = s4.y;
+          vsc[tt][2] = s4.z;
+          vsc[tt][3] = s4.w;
+        }
+      }
       bf16x8_t ph[2], pl[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float x0 = p[qt][u >> 1][2 * (u & 1)];
-          const float x1 = p[qt][u >> 1][2 * (u & 1) + 1];
+          const float x0 = p[qt][u >> 1][2 * (u & 1)] * (kFp8 ? vsc[u >> 1][2 * (u & 1)] : 1.0f);
+          const float x1 = p[qt][u >> 1][2 * (u & 1) + 1] * (kFp8 ? vsc[u >> 1][2 * (u & 1) + 1] : 1.0f);
           hw[u] = pack_bf16(x0, x1);
           lw[u] = pack_bf16(x0 - __uint_as_float(hw[u] << 16), x1 - __uint_as_float(hw[u] & 0xFFFF0000u));
         }
@@ -570,24 +633,28 @@ template <int kGp>
 dim3 chunk_grid(const ScanArgs& a, int B) {
   return dim3(a.n_split * ((a.Lq + tokens_per_wg<kGp>() - 1) / tokens_per_wg<kGp>()), a.Hkv, B);
 }
-
-}  // namespace
-
-// Block mode (per-block sums, 8 head slots) for G <= 8 only; token mode for G <= 32.
-hipError_t launch_chunk_mfma(const ScanArgs& a, int B, hipStream_t st) {
+template <bool kFp8>
+hipError_t launch_chunk_t(const ScanArgs& a, int B, hipStream_t st) {
   if (a.blse != nullptr) {
     if (a.G > 8) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((chunk_mfma_kernel<8, true>), chunk_grid<8>(a, B), dim3(kCThreads), 0, st, a);
+    hipLaunchKernelGGL((chunk_mfma_kernel<8, true, kFp8>), chunk_grid<8>(a, B), dim3(kCThreads), 0, st, a);
   } else if (a.G <= 8) {
-    hipLaunchKernelGGL((chunk_mfma_kernel<8, false>), chunk_grid<8>(a, B), dim3(kCThreads), 0, st, a);
+    hipLaunchKernelGGL((chunk_mfma_kernel<8, false, kFp8>), chunk_grid<8>(a, B), dim3(kCThreads), 0, st, a);
   } else if (a.G <= 16) {
-    hipLaunchKernelGGL((chunk_mfma_kernel<16, false>), chunk_grid<16>(a, B), dim3(kCThreads), 0, st, a);
+    hipLaunchKernelGGL((chunk_mfma_kernel<16, false, kFp8>), chunk_grid<16>(a, B), dim3(kCThreads), 0, st, a);
   } else if (a.G <= 32) {
-    hipLaunchKernelGGL((chunk_mfma_kernel<32, false>), chunk_grid<32>(a, B), dim3(kCThreads), 0, st, a);
+    hipLaunchKernelGGL((chunk_mfma_kernel<32, false, kFp8>), chunk_grid<32>(a, B), dim3(kCThreads), 0, st, a);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+// Block mode (per-block sums, 8 head slots) for G <= 8 only; token mode for G <= 32.
+hipError_t launch_chunk_mfma(const ScanArgs& a, int B, bool fp8, hipStream_t st) {
+  return fp8 ? launch_chunk_t<true>(a, B, st) : launch_chunk_t<false>(a, B, st);
 }
 
 }  // namespace hs2

@@ -210,7 +210,8 @@ hipError_t launch_scan_mfma_blocks(const ScanArgs& a, bool fp8, int B, hipStream
 // a.split_len index entries); out != nullptr (one split): normalised output, else
 // partials in a.part for launch_combine (S <= 4096)
 hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool fp8, int B, hipStream_t st);
-hipError_t launch_chunk_mfma(const ScanArgs& a, int B, hipStream_t st);
+// query chunks (q_len > 1) on the matrix cores, bf16 or fp8 caches (chunk_mfma_kernel)
+hipError_t launch_chunk_mfma(const ScanArgs& a, int B, bool fp8, hipStream_t st);
 hipError_t launch_scan_sparse(const ScanArgs& a, bool fp8, int B, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_groupsum(const SelectArgs& a, hipStream_t st);

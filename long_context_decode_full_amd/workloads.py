@@ -63,9 +63,10 @@ class Workload:
 
 def standard_workloads():
     """The five configurations (tiny decode, batched decode, fp8 long decode,
-    million-token decode, the ragged 64-token chunk) and the MQA variants of the
+    million-token decode, the ragged 64-token chunk), the MQA variants of the
     million-token decode and of the chunk (one KV head for all 32 query heads; the
-    chunk variant draws the same context lengths as the chunk configuration)."""
+    chunk variant draws the same context lengths as the chunk configuration) and the
+    chunk with fp8 caches (same lengths)."""
     return {
         "tiny": Workload("tiny decode", 1, 1, 16, 2, ctx_lens=[4096], n_needles=8, seed=1001),
         "batched": Workload("batched decode", 8, 1, 32, 4, ctx_lens=[32768] * 8, n_needles=64,
@@ -80,6 +81,8 @@ def standard_workloads():
                                 n_needles=1024, drift_sigma=0.01, drift_block=4096, seed=1006),
         "mqa_chunk": Workload("MQA ragged 64-token chunk", 16, 64, 32, 1, ctx_log_uniform=(8192, 524288),
                               n_needles=64, seed=1005),
+        "fp8_chunk": Workload("ragged 64-token chunk, fp8 caches", 16, 64, 32, 4,
+                              ctx_log_uniform=(8192, 524288), kv_dtype="fp8", n_needles=64, seed=1005),
     }
 
 

@@ -135,8 +135,9 @@ hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool, int B, hipStr
   ++g_launches;
   return hipSuccess;
 }
-hipError_t launch_chunk_mfma(const ScanArgs& a, int B, hipStream_t) {
+hipError_t launch_chunk_mfma(const ScanArgs& a, int B, bool fp8, hipStream_t) {
   if (a.G > kMaxHeads || (a.blse != nullptr && a.G > kSlots)) fail("chunk kernel: head slots");
+  if (fp8 && (a.k_scale == nullptr || a.v_scale == nullptr)) fail("chunk kernel: fp8 scales");
   check_scan(a, B, a.blse == nullptr);
   return hipSuccess;
 }

@@ -330,12 +330,39 @@ def test_fp8_scale_alignment(cap):
 
 
 @pytest.mark.parametrize("mode", ["token", "block"])
-def test_fp8_query_chunk(mode):
-    """fp8 caches with several query tokens (causal inside the chunk) take the decode
-    scan once per token; every token compared."""
+@pytest.mark.parametrize("route", ["chunk_kernel", "per_token"])
+def test_fp8_query_chunk(mode, route):
+    """fp8 caches with several query tokens (causal inside the chunk): the chunk kernel
+    (tiles widened to bf16 as they are staged, K scale on the scores, V scale on P^T),
+    and with HS2_FLAG_CHUNK_PER_TOKEN the decode scan once per token; every token
+    compared."""
     w = wl.Workload("fp8 chunk", 2, 4, 32, 4, ctx_lens=[3000, 5200], n_needles=8, kv_dtype="fp8",
                     seed=2450)
-    run_and_compare(w, f"fp8-chunk-{mode}", mode=mode)
+    run_and_compare(w, f"fp8-chunk-{mode}-{route}", mode=mode,
+                    flags=HS2_FLAG_CHUNK_PER_TOKEN if route == "per_token" else 0)
+
+
+@pytest.mark.parametrize("mode", ["token", "block"])
+@pytest.mark.parametrize("ctx", [[9000, 2500, 64], [40000, 700]])
+def test_fp8_chunk64(mode, ctx):
+    """64-token fp8 chunks on the chunk kernel: both 32-token workgroups of every split,
+    a context equal to the chunk, ragged lengths, NaN codes and scales past each
+    sequence's end (never read); every token compared."""
+    w = wl.Workload("fp8 chunk64", len(ctx), 64, 32, 4, ctx_lens=ctx, n_needles=16, kv_dtype="fp8",
+                    poison_tail=True, seed=2470 + len(ctx))
+    got, _ = run_and_compare(w, f"fp8-chunk64-{mode}-{len(ctx)}", mode=mode)
+    if mode == "token" and 64 in ctx:   # the chunk is the whole context
+        b = ctx.index(64)
+        for j in range(64):
+            assert got["idx"][b, j, 0, :j + 1].tolist() == list(range(j + 1))
+
+
+@pytest.mark.parametrize("hq,hkv,lq,ctx", [(32, 1, 64, [5000, 900]), (32, 2, 40, [4100])])
+def test_fp8_wide_group_chunks(hq, hkv, lq, ctx):
+    """fp8 chunks with 32 (MQA) and 16 query heads per KV head on the chunk kernel."""
+    w = wl.Workload(f"fp8 wide chunk G{hq // hkv}", len(ctx), lq, hq, hkv, ctx_lens=ctx, n_needles=8,
+                    kv_dtype="fp8", seed=2480 + hq + lq)
+    run_and_compare(w, f"fp8-wide-chunk-G{hq // hkv}-lq{lq}")
 
 
 @pytest.mark.parametrize("with_probs", [False, True])
