@@ -551,15 +551,28 @@ __device__ __forceinline__ uint64_t block_key(float mass, int32_t blk) {
   return ((uint64_t)__float_as_uint(mass) << 32) | (uint32_t)(0x7FFFFFFF - blk);
 }
 
+// Maximum over the 64 lanes (all active): DPP steps inside each 16-lane row, then the
+// permlane swaps across the four rows (VALU only, no LDS round trip).  The swap
+// results are copied to scalars before use.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u<kDppXor1>(x));
+  x = max(x, dpp_u<kDppXor2>(x));
+  x = max(x, dpp_u<kDppMirror8>(x));
+  x = max(x, dpp_u<kDppRor8>(x));
+  const auto s32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  const uint32_t a0 = s32[0], a1 = s32[1];
+  x = max(a0, a1);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const uint32_t c0 = s16[0], c1 = s16[1];
+  return max(c0, c1);
+}
+// 64-bit maximum as two 32-bit ones: the high words, then the low words of the lanes
+// that hold the largest high word.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, off, 64);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), off, 64);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    x = o > x ? o : x;
-  }
-  return x;
+  const uint32_t hi = (uint32_t)(x >> 32), lo = (uint32_t)x;
+  const uint32_t mh = wave_max_u32(hi);
+  const uint32_t ml = wave_max_u32(hi == mh ? lo : 0u);
+  return ((uint64_t)mh << 32) | ml;
 }
 
 __global__ __launch_bounds__(kBmThreads) void block_mass_kernel(SelectArgs a) {
@@ -589,11 +602,28 @@ __global__ __launch_bounds__(kBmThreads) void block_mass_kernel(SelectArgs a) {
       float acc = -1.0f;   // no block
       if (blk < nb) {
         acc = 0.0f;
+        // up to kSubPre sums of the block loaded together, then added in order
+        constexpr int kSubPre = 4;
+        float4 pre[kSubPre][2];
+#pragma unroll
+        for (int u = 0; u < kSubPre; ++u) {
+          const int sb = blk * sub + u;
+          if (u < sub && sb < nsub) {
+            pre[u][0] = *reinterpret_cast<const float4*>(brow + (int64_t)sb * 8);
+            pre[u][1] = *reinterpret_cast<const float4*>(brow + (int64_t)sb * 8 + 4);
+          }
+        }
         for (int u = 0; u < sub; ++u) {
           const int sb = blk * sub + u;
           if (sb >= nsub) break;
-          const float4 l0 = *reinterpret_cast<const float4*>(brow + (int64_t)sb * 8);
-          const float4 l1 = *reinterpret_cast<const float4*>(brow + (int64_t)sb * 8 + 4);
+          float4 l0, l1;
+          if (u < kSubPre) {
+            l0 = pre[u < kSubPre ? u : 0][0];
+            l1 = pre[u < kSubPre ? u : 0][1];
+          } else {
+            l0 = *reinterpret_cast<const float4*>(brow + (int64_t)sb * 8);
+            l1 = *reinterpret_cast<const float4*>(brow + (int64_t)sb * 8 + 4);
+          }
           const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
           for (int h = 0; h < 8; ++h)
@@ -639,7 +669,23 @@ __global__ __launch_bounds__(64) void block_pick_kernel(SelectArgs a) {
   const int nl = a.bm_wgs, ll = a.n_blocks;
   const uint64_t* cand = a.bcand + sel * (int64_t)nl * ll;
   __shared__ uint64_t lists[kMaxBlockPick];
-  for (int i = lane; i < nl * ll; i += 64) lists[i] = cand[i];
+  // the lists into LDS, 16 loads a lane in flight per batch (one memory latency each
+  // batch instead of one per key)
+  constexpr int kBatch = 16;
+  const int nk = nl * ll;
+  for (int base = 0; base < nk; base += 64 * kBatch) {
+    uint64_t t[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = base + 64 * u + lane;
+      t[u] = i < nk ? cand[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = base + 64 * u + lane;
+      if (i < nk) lists[i] = t[u];
+    }
+  }
   __syncthreads();
   int ptr[kPickLists];
   uint64_t head[kPickLists];
