@@ -15,9 +15,11 @@
 // them.  Per iteration of 64 positions the K and V tiles go through LDS (two stages:
 // the next tiles are stored while the current ones are read; one barrier after those
 // stores, so that the first K fragments of the next tile can be read during the
-// current one, and one at the end of the iteration); wave w owns 32 / kGp tokens as two query tiles of 16 rows, a token's
-// heads spread over both tiles (head = (kGp / 2) tile + lane % (kGp / 2)).  The scores are
-// formed transposed, S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K rows from the K
+// current one, and one at the end of the iteration); fp8 caches are widened to bf16 as
+// they are staged.  Wave w owns 32 / kGp tokens as two query tiles of 16 rows, a
+// token's heads spread over both tiles (head = (kGp / 2) tile + lane % (kGp / 2)).
+// The scores are formed transposed, S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K
+// rows from the K
 // tile, lane: position i, dims 32s + 8grp; B = Q^T from registers, lane: query row
 // i, the same dims), so a lane's accumulators are 4 positions (4grp + v) of one query
 // row (i) and the probabilities are already in the B-operand layout of the second
