@@ -10,8 +10,9 @@ Every function states the passage of the HySparse2 article (Xiaomi MiMo,
 "HySparse2" for MiMo-V3, as reprinted by IT Home and translated by AIHOT.vn
 with sections 01-05) that it follows, or the reading adopted where the article
 is silent.  Parity status: every function here is pinned by tests in
-tests/test_oracle_pins.py against closed forms, brute force, hand-worked cases
-or library routines; none is "parity unpinned".  What is unpinned is whether
+tests/test_oracle_pins.py (the KV Bridging functions of oracle/bridge.py in
+tests/test_oracle_bridge_pins.py) against closed forms, brute force, hand-worked
+cases or library routines; none is "parity unpinned".  What is unpinned is whether
 the score-to-selection rule is the one the article's model uses: the article
 gives no formula for it, so the rule is the specified one (group-summed
 softmax probabilities, ties to the lower index).

@@ -31,7 +31,7 @@ Readings where the article is silent (each is listed in the design doc):
      scale and the division are fp32 operations (correctly rounded), as a fused
      kernel evaluates them.
 
-Parity status: every function here is pinned in tests/test_oracle_pins.py
+Parity status: every function here is pinned in tests/test_oracle_bridge_pins.py
 (format definitions against torch's independent casts and hand-made tie and
 saturation cases, the projection against brute-force loops, the scatter against
 a per-element brute force); none is "parity unpinned".
