@@ -109,8 +109,8 @@ enum {
   HS2_FLAG_DETERMINISTIC = 1u << 0,
   /* Selection on the logits path (every logit kept; token mode: exact radix select,
    * block mode: block sums of the per-position s) even when probs is NULL.  For
-   * comparing the selection paths.  Without it, block mode at up to 8 query heads per
-   * KV head sums the blocks inside the context scan. */
+   * comparing the selection paths (up to 8 query heads per KV head).  Without it, block
+   * mode sums the blocks inside the context scan. */
   HS2_FLAG_FORCE_LOGITS = 1u << 1,
   /* The record path's context scan on the VALU kernel (dot2 + DPP) instead of the
    * matrix cores (block mode: the logits path).  For comparing the two scans. */
@@ -129,8 +129,10 @@ enum {
 /* Host only, touches no GPU: checks a descriptor and that `workspace_bytes` covers
  * hs2_workspace_size(desc) (HS2_ERR_WORKSPACE otherwise; pass SIZE_MAX to check the
  * descriptor alone).  Limits: head_dim == 128,
- * 1 <= G <= 32 with G > 8 (up to MQA at 32 query heads) in token mode only and without
- * probs (hs2_full_attn_select then returns HS2_ERR_UNSUPPORTED), window + topk <= 4096
+ * 1 <= G <= 32; with G > 8 (up to MQA at 32 query heads) hs2_full_attn_select returns
+ * HS2_ERR_UNSUPPORTED where only the logits path would serve the call (probs requested,
+ * HS2_FLAG_FORCE_LOGITS, or HS2_FLAG_SCAN_VALU or a block_size that is not a multiple
+ * of 32 in block mode), window + topk <= 4096
  * (token mode), block_size in [1, 4096] and
  * block_size * n_blocks <= 4096 (block mode), 1 <= q_len <= max_ctx_len <= cap,
  * cap < 2^31, batch * q_len <= 65535, n_kv_heads <= 65535 and

@@ -77,10 +77,9 @@ hs2_status validate_desc(const hs2_attn_desc* d) {
     return HS2_ERR_INVALID_ARG;
   }
   if (d->head_dim != kHeadDim) return HS2_ERR_UNSUPPORTED;
-  // up to 32 query heads per KV head (MQA at Hq = 32); beyond 8 only token selection
-  // on the record path (matrix-core scan and gather), see wide_group()
+  // up to 32 query heads per KV head (MQA at Hq = 32); beyond 8 the record path and the
+  // block sums only (no logits path), see wide_group() and full_path_supported()
   if (d->n_q_heads / d->n_kv_heads > kMaxHeads) return HS2_ERR_UNSUPPORTED;
-  if (d->n_q_heads / d->n_kv_heads > kSlots && d->select_mode != HS2_SELECT_TOKEN) return HS2_ERR_UNSUPPORTED;
   if (d->kv_capacity >= (int64_t(1) << 31)) return HS2_ERR_UNSUPPORTED;
   if ((int64_t)d->batch * d->q_len > 65535) return HS2_ERR_UNSUPPORTED;
   if (d->n_kv_heads > 65535) return HS2_ERR_UNSUPPORTED;
@@ -109,11 +108,11 @@ bool chunk_block_path(const hs2_attn_desc* d) {
          !has_flag(d, HS2_FLAG_CHUNK_PER_TOKEN);
 }
 // The block comparator otherwise (decode, per-token chunks): per-32-position
-// block sums from the decode scan, for up to 8 query heads per KV head.
-// HS2_FLAG_FORCE_LOGITS or HS2_FLAG_SCAN_VALU keep it on the logits path.
+// block sums from the decode scan, in the scan's head layout (up to 32 query heads per
+// KV head).  HS2_FLAG_FORCE_LOGITS or HS2_FLAG_SCAN_VALU keep it on the logits path.
 bool scan_block_path(const hs2_attn_desc* d) {
-  return d->select_mode == HS2_SELECT_BLOCK && !chunk_block_path(d) && !wide_group(d) &&
-         d->block_size % 32 == 0 && !has_flag(d, HS2_FLAG_FORCE_LOGITS) && !has_flag(d, HS2_FLAG_SCAN_VALU);
+  return d->select_mode == HS2_SELECT_BLOCK && !chunk_block_path(d) && d->block_size % 32 == 0 &&
+         !has_flag(d, HS2_FLAG_FORCE_LOGITS) && !has_flag(d, HS2_FLAG_SCAN_VALU);
 }
 
 // logits_area: reserve the logits path's per-position scores whenever that path fits
@@ -204,7 +203,7 @@ Layout make_layout(const hs2_attn_desc* d, bool logits_area = true) {
   if (chunk_block_path(d) || scan_block_path(d)) {
     L.blse_gran = chunk_block_path(d) ? 64 : 32;
     L.blse_stride = ceil_div(d->max_ctx_len, L.blse_gran);
-    L.off_blse = off; off = align_up(off + (size_t)n * L.blse_stride * 8 * sizeof(float));
+    L.off_blse = off; off = align_up(off + (size_t)n * L.blse_stride * blse_heads_of(L.G) * sizeof(float));
     // block selection over many workgroups a row (up to 64 blocks kept)
     const int64_t wgs = ceil_div(ceil_div(d->max_ctx_len, d->block_size), kBlockMassBlocks);
     if (d->n_blocks <= 64 && wgs <= kMaxBlockMassWgs && wgs * d->n_blocks <= kMaxBlockPick) {
@@ -298,7 +297,7 @@ static hs2_status full_path_supported(const hs2_attn_desc* d, const Layout& L, c
   const bool fast = use_record_path(d, L, probs);
   const bool bsums = block_sums_path(d, probs);
   if (!fast && !bsums && !L.logits_ok) return HS2_ERR_UNSUPPORTED;
-  if (!fast && wide_group(d)) return HS2_ERR_UNSUPPORTED;
+  if (!fast && !bsums && wide_group(d)) return HS2_ERR_UNSUPPORTED;   // the logits path has 8 head slots
   return HS2_OK;
 }
 

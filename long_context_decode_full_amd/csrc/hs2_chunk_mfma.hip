@@ -596,7 +596,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
         const float sum = across_groups<false>(bsum[qt]);
         const float lse = m[qt] + __builtin_amdgcn_logf(sum);   // -inf for an empty block
         if (grp == 0 && valid[qt])
-          a.blse[((sel_tok0 + (int64_t)tokl[qt] * a.Hkv) * a.blse_stride + P0 / kCPos) * 8 + head[qt]] = lse;
+          a.blse[((sel_tok0 + (int64_t)tokl[qt] * a.Hkv) * a.blse_stride + P0 / kCPos) * kGp + head[qt]] = lse;
       }
     }
     __syncthreads();   // every wave is done with this stage; the next one is stored
@@ -637,9 +637,15 @@ dim3 chunk_grid(const ScanArgs& a, int B) {
 }
 template <bool kFp8>
 hipError_t launch_chunk_t(const ScanArgs& a, int B, hipStream_t st) {
-  if (a.blse != nullptr) {
-    if (a.G > 8) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((chunk_mfma_kernel<8, true, kFp8>), chunk_grid<8>(a, B), dim3(kCThreads), 0, st, a);
+  if (a.blse != nullptr) {   // block mode: per-block sums in kGp head slots
+    if (a.G <= 8)
+      hipLaunchKernelGGL((chunk_mfma_kernel<8, true, kFp8>), chunk_grid<8>(a, B), dim3(kCThreads), 0, st, a);
+    else if (a.G <= 16)
+      hipLaunchKernelGGL((chunk_mfma_kernel<16, true, kFp8>), chunk_grid<16>(a, B), dim3(kCThreads), 0, st, a);
+    else if (a.G <= 32)
+      hipLaunchKernelGGL((chunk_mfma_kernel<32, true, kFp8>), chunk_grid<32>(a, B), dim3(kCThreads), 0, st, a);
+    else
+      return hipErrorInvalidValue;
   } else if (a.G <= 8) {
     hipLaunchKernelGGL((chunk_mfma_kernel<8, false, kFp8>), chunk_grid<8>(a, B), dim3(kCThreads), 0, st, a);
   } else if (a.G <= 16) {
@@ -654,7 +660,7 @@ hipError_t launch_chunk_t(const ScanArgs& a, int B, hipStream_t st) {
 
 }  // namespace
 
-// Block mode (per-block sums, 8 head slots) for G <= 8 only; token mode for G <= 32.
+// Token and block mode for G <= 32.
 hipError_t launch_chunk_mfma(const ScanArgs& a, int B, bool fp8, hipStream_t st) {
   return fp8 ? launch_chunk_t<true>(a, B, st) : launch_chunk_t<false>(a, B, st);
 }

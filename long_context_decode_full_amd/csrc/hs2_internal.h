@@ -12,6 +12,9 @@ constexpr int kHeadDim = 128;
 constexpr int kSlots = 8;             // head slots per KV group handled by one wave
 constexpr int kMaxHeads = 32;         // query heads per KV head (G) at most; per-row (M, 1/Z)
                                       // statistics keep kMaxHeads slots
+// Head slots of the block comparator's per-block sums: the group size rounded up to 8,
+// 16 or 32 (the head layouts of the scans and of the chunk kernel).
+constexpr int blse_heads_of(int G) { return G <= 8 ? 8 : G <= 16 ? 16 : 32; }
 constexpr int kPartStride = 132;      // floats per (split, head) partial: m, z, pad, pad, o[128]
 constexpr int kHist1Bins = 2048;      // score bits 30..20
 constexpr int kHist2Bins = 4096;      // score bits 19..8

@@ -246,7 +246,8 @@ __device__ __forceinline__ float sum16w(float x) {
 // kGather: a sparse-layer step; `base` is the step's first index-row entry and srow
 // holds each entry's row (-1: skipped), so no records are formed.
 // kBlk: a block-comparator step: instead of records, log2 of the sum of 2^logit over
-// the step's 32 positions per head goes to blrow[(base / 32) * 8 + head].
+// the step's 32 positions per head goes to blrow[(base / 32) * H + head], H the head
+// slots of the layout (8, 16 or 32).
 template <bool kFp8, bool kGather = false, int kHB = 1, bool kWide = false, bool kBlk = false>
 __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x8_t (&qf)[kHB][4], uint8_t* vt,
                                              int32_t base, int32_t w_begin, int32_t w_end, uint32_t cand_span,
@@ -393,7 +394,8 @@ __device__ __forceinline__ void process_step(const StepBuf<kFp8>& s, const bf16x
     for (int hb = 0; hb < kHB; ++hb) {
       const float tot = sum_groups(bsum[hb]);
       const float lse = hs[hb].m + __builtin_amdgcn_logf(tot);   // -inf for an empty step
-      if (grp == 0 && 16 * hb + w16 < G) blrow[(int64_t)(base / kStepRows) * 8 + 16 * hb + w16] = lse;
+      if (grp == 0 && 16 * hb + w16 < G)
+        blrow[(int64_t)(base / kStepRows) * ((kWide ? 16 : 8) * kHB) + 16 * hb + w16] = lse;
     }
   }
   if constexpr (kRec) {
@@ -538,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_mfma_kernel(ScanArgs a) {
     }
   }
   if (tid == 0) step_next = kWaves;   // step w is wave w's first
-  float* blrow = kBlk ? a.blse + sel * a.blse_stride * 8 : nullptr;
+  float* blrow = kBlk ? a.blse + sel * a.blse_stride * (kBH * kHB) : nullptr;
   __syncthreads();
 
   HeadState hs[kHB];
@@ -821,15 +823,26 @@ static void launch_scan_g(const ScanArgs& a, dim3 grid, hipStream_t st) {
     hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 2, true, 256>), grid, dim3(256), 0, st, a);
 }
 
+// the block comparator's scan, same head layouts (per-block sums in blse_heads_of(G) slots)
+template <bool kFp8, bool kVec>
+static void launch_scan_blocks_g(const ScanArgs& a, dim3 grid, hipStream_t st) {
+  if (a.G <= 8)
+    hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 1, false, 512, true>), grid, dim3(512), 0, st, a);
+  else if (a.G <= 16)
+    hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 1, true, 512, true>), grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 2, true, 256, true>), grid, dim3(256), 0, st, a);
+}
+
 hipError_t launch_scan_mfma_blocks(const ScanArgs& a, bool fp8, int B, hipStream_t st) {
-  if (a.G > 8 || a.blse == nullptr) return hipErrorInvalidValue;
+  if (a.G > kMaxHeads || a.blse == nullptr) return hipErrorInvalidValue;
   dim3 grid(a.n_split, a.Hkv, B * a.Lq);
   if (fp8 && a.cap % 4 == 0)
-    hipLaunchKernelGGL((scan_mfma_kernel<true, true, 1, false, 512, true>), grid, dim3(512), 0, st, a);
+    launch_scan_blocks_g<true, true>(a, grid, st);
   else if (fp8)
-    hipLaunchKernelGGL((scan_mfma_kernel<true, false, 1, false, 512, true>), grid, dim3(512), 0, st, a);
+    launch_scan_blocks_g<true, false>(a, grid, st);
   else
-    hipLaunchKernelGGL((scan_mfma_kernel<false, false, 1, false, 512, true>), grid, dim3(512), 0, st, a);
+    launch_scan_blocks_g<false, false>(a, grid, st);
   return hipGetLastError();
 }
 

@@ -401,6 +401,37 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(SelectArgs a) {
 // blocks (ties to the lower block) are expanded to their visible positions.
 constexpr int kBlkThreads = 1024;
 
+// Block masses from the scans' block sums: per aligned block of blse_gran positions and
+// head h, L_h = log2 sum 2^logit, so the block's share of head h's softmax is
+// 2^(L_h - M_h) / Z_h; a block's mass adds those of its block sums and heads h < G in
+// that order (sums ascending, heads ascending).  H = blse_heads_of(G) head slots.
+template <int H>
+__device__ __forceinline__ void load_head_stats(const SelectArgs& a, int64_t sel, float (&Mh)[H], float (&iz)[H]) {
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    Mh[h] = a.mz[(sel * kMaxHeads + h) * 2 + 0];
+    iz[h] = a.mz[(sel * kMaxHeads + h) * 2 + 1];
+  }
+}
+template <int H>
+__device__ __forceinline__ void load_block_sum(const float* brow, int sb, float4 (&l)[H / 4]) {
+#pragma unroll
+  for (int j = 0; j < H / 4; ++j) l[j] = *reinterpret_cast<const float4*>(brow + (int64_t)sb * H + 4 * j);
+}
+template <int H>
+__device__ __forceinline__ float add_block_sum(float acc, const float4 (&l)[H / 4], const float (&Mh)[H],
+                                               const float (&iz)[H], int G) {
+#pragma unroll
+  for (int j = 0; j < H / 4; ++j) {
+    const float lv[4] = {l[j].x, l[j].y, l[j].z, l[j].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (4 * j + c < G) acc += fast_exp2(lv[c] - Mh[4 * j + c]) * iz[4 * j + c];
+  }
+  return acc;
+}
+
+template <int H>   // block-sum head slots (blse_heads_of(G))
 __global__ __launch_bounds__(kBlkThreads) void block_select_kernel(SelectArgs a) {
   const int64_t sel = blockIdx.x;
   const int tid = threadIdx.x;
@@ -418,27 +449,21 @@ __global__ __launch_bounds__(kBlkThreads) void block_select_kernel(SelectArgs a)
   __shared__ int32_t cnt[4097];
 
   if (a.blse != nullptr) {
-    // the scans' block sums: per aligned block of blse_gran positions and head h,
-    // L_h = log2 sum 2^logit, so its share of head h's softmax is 2^(L_h - M_h) / Z_h
-    // (bs is a multiple of blse_gran)
-    float Mh[8], iz[8];
-#pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      Mh[h] = a.mz[(sel * kMaxHeads + h) * 2 + 0];
-      iz[h] = a.mz[(sel * kMaxHeads + h) * 2 + 1];
-    }
+    // the scans' block sums (bs is a multiple of blse_gran)
+    float Mh[H], iz[H];
+    load_head_stats<H>(a, sel, Mh, iz);
     const int gran = a.blse_gran;
     const int sub = bs / gran;
     const int nsub = (n + gran - 1) / gran;   // block sums holding visible positions
-    const float* brow = a.blse + sel * a.blse_stride * 8;
+    const float* brow = a.blse + sel * a.blse_stride * H;
     for (int blk = tid; blk < nb; blk += kBlkThreads) {
       float acc = 0.0f;
       for (int u = 0; u < sub; ++u) {
         const int sb = blk * sub + u;
         if (sb >= nsub) break;
-#pragma unroll
-        for (int h = 0; h < 8; ++h)
-          if (h < a.G) acc += fast_exp2(brow[(int64_t)sb * 8 + h] - Mh[h]) * iz[h];
+        float4 l[H / 4];
+        load_block_sum<H>(brow, sb, l);
+        acc = add_block_sum<H>(acc, l, Mh, iz, a.G);
       }
       mass[blk] = acc;
     }
@@ -575,6 +600,7 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
   return ((uint64_t)mh << 32) | ml;
 }
 
+template <int H>   // block-sum head slots (blse_heads_of(G))
 __global__ __launch_bounds__(kBmThreads) void block_mass_kernel(SelectArgs a) {
   const int64_t sel = blockIdx.x / (uint32_t)a.bm_wgs;
   const int wg = (int)(blockIdx.x % (uint32_t)a.bm_wgs);
@@ -587,47 +613,37 @@ __global__ __launch_bounds__(kBmThreads) void block_mass_kernel(SelectArgs a) {
   uint64_t* outc = a.bcand + (sel * a.bm_wgs + wg) * a.n_blocks;
   __shared__ float mass[kBmBlocks];
   if (b0 < nb) {
-    float Mh[8], iz[8];
-#pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      Mh[h] = a.mz[(sel * kMaxHeads + h) * 2 + 0];
-      iz[h] = a.mz[(sel * kMaxHeads + h) * 2 + 1];
-    }
+    float Mh[H], iz[H];
+    load_head_stats<H>(a, sel, Mh, iz);
     const int gran = a.blse_gran;
     const int sub = bs / gran;
     const int nsub = (n + gran - 1) / gran;
-    const float* brow = a.blse + sel * a.blse_stride * 8;
+    const float* brow = a.blse + sel * a.blse_stride * H;
     for (int i = tid; i < kBmBlocks; i += kBmThreads) {
       const int blk = b0 + i;
       float acc = -1.0f;   // no block
       if (blk < nb) {
         acc = 0.0f;
-        // up to kSubPre sums of the block loaded together, then added in order
-        constexpr int kSubPre = 4;
-        float4 pre[kSubPre][2];
+        // the first kSubPre sums of the block (8 float4 loads) issued together, then
+        // every sum added in order
+        constexpr int kSubPre = 32 / H;
+        float4 pre[kSubPre][H / 4];
 #pragma unroll
         for (int u = 0; u < kSubPre; ++u) {
           const int sb = blk * sub + u;
-          if (u < sub && sb < nsub) {
-            pre[u][0] = *reinterpret_cast<const float4*>(brow + (int64_t)sb * 8);
-            pre[u][1] = *reinterpret_cast<const float4*>(brow + (int64_t)sb * 8 + 4);
-          }
+          if (u < sub && sb < nsub) load_block_sum<H>(brow, sb, pre[u]);
         }
         for (int u = 0; u < sub; ++u) {
           const int sb = blk * sub + u;
           if (sb >= nsub) break;
-          float4 l0, l1;
+          float4 l[H / 4];
           if (u < kSubPre) {
-            l0 = pre[u < kSubPre ? u : 0][0];
-            l1 = pre[u < kSubPre ? u : 0][1];
-          } else {
-            l0 = *reinterpret_cast<const float4*>(brow + (int64_t)sb * 8);
-            l1 = *reinterpret_cast<const float4*>(brow + (int64_t)sb * 8 + 4);
-          }
-          const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
-          for (int h = 0; h < 8; ++h)
-            if (h < a.G) acc += fast_exp2(lv[h] - Mh[h]) * iz[h];
+            for (int j = 0; j < H / 4; ++j) l[j] = pre[u < kSubPre ? u : 0][j];
+          } else {
+            load_block_sum<H>(brow, sb, l);
+          }
+          acc = add_block_sum<H>(acc, l, Mh, iz, a.G);
         }
       }
       mass[i] = acc;
@@ -738,13 +754,25 @@ __global__ __launch_bounds__(64) void block_pick_kernel(SelectArgs a) {
 
 }  // namespace
 
-hipError_t launch_block_select(const SelectArgs& a, hipStream_t st) {
+template <int H>
+static void launch_block_select_h(const SelectArgs& a, hipStream_t st) {
   if (a.blse != nullptr && a.bcand != nullptr) {
-    hipLaunchKernelGGL(block_mass_kernel, dim3((uint32_t)((uint64_t)a.n_sel * a.bm_wgs)), dim3(kBmThreads), 0, st, a);
+    hipLaunchKernelGGL(block_mass_kernel<H>, dim3((uint32_t)((uint64_t)a.n_sel * a.bm_wgs)), dim3(kBmThreads), 0, st, a);
     hipLaunchKernelGGL(block_pick_kernel, dim3(a.n_sel), dim3(64), 0, st, a);
   } else {
-    hipLaunchKernelGGL(block_select_kernel, dim3(a.n_sel), dim3(kBlkThreads), 0, st, a);
+    hipLaunchKernelGGL(block_select_kernel<H>, dim3(a.n_sel), dim3(kBlkThreads), 0, st, a);
   }
+}
+
+hipError_t launch_block_select(const SelectArgs& a, hipStream_t st) {
+  // per-position scores (logits path) or block sums in blse_heads_of(G) head slots
+  const int H = a.blse != nullptr ? blse_heads_of(a.G) : 8;
+  if (H == 8)
+    launch_block_select_h<8>(a, st);
+  else if (H == 16)
+    launch_block_select_h<16>(a, st);
+  else
+    launch_block_select_h<32>(a, st);
   return hipGetLastError();
 }
 

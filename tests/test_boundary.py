@@ -79,7 +79,7 @@ def test_build_id_names_the_current_sources(lib):
     (dict(n_q_heads=64, n_kv_heads=4), hs2.HS2_OK),              # G = 16: wide groups
     (dict(n_q_heads=32, n_kv_heads=1), hs2.HS2_OK),              # MQA, G = 32
     (dict(n_q_heads=64, n_kv_heads=1), hs2.HS2_ERR_UNSUPPORTED), # G = 64 > 32
-    (dict(n_q_heads=32, n_kv_heads=1, select_mode=1), hs2.HS2_ERR_UNSUPPORTED),  # G > 8: token mode only
+    (dict(n_q_heads=32, n_kv_heads=1, select_mode=1), hs2.HS2_OK),  # G > 8 block mode: the scans' block sums
     (dict(head_dim=64), hs2.HS2_ERR_UNSUPPORTED),
     (dict(kv_dtype=7), hs2.HS2_ERR_INVALID_ARG),
     (dict(max_ctx_len=(1 << 20) + 1), hs2.HS2_ERR_INVALID_ARG),   # beyond capacity
@@ -243,6 +243,22 @@ def test_noalloc_checks_before_touching_a_device(lib):
 
 def test_invalid_desc_checked_before_pointers(lib):
     assert _full(_desc(head_dim=96), q=None) == hs2.HS2_ERR_UNSUPPORTED
+
+
+def test_wide_groups_have_no_logits_path(lib):
+    """More than 8 query heads per KV head: block mode runs on the scans' block sums, and
+    every call that only the logits path (8 head slots) could serve is refused before
+    anything is enqueued (fake device pointers, never touched)."""
+    mqa = dict(n_q_heads=32, n_kv_heads=1, kv_capacity=65536, max_ctx_len=65536)
+    assert _full(_desc(**mqa), probs=FAKE) == hs2.HS2_ERR_UNSUPPORTED
+    assert _full(_desc(select_mode=1, **mqa), probs=FAKE) == hs2.HS2_ERR_UNSUPPORTED
+    assert _full(_desc(select_mode=1, flags=hs2.HS2_FLAG_FORCE_LOGITS, **mqa)) == hs2.HS2_ERR_UNSUPPORTED
+    assert _full(_desc(select_mode=1, flags=hs2.HS2_FLAG_SCAN_VALU, **mqa)) == hs2.HS2_ERR_UNSUPPORTED
+    assert _full(_desc(select_mode=1, block_size=48, n_blocks=18, **mqa)) == hs2.HS2_ERR_UNSUPPORTED
+    # a chunk: 96-position blocks take the per-token scan's block sums (a multiple of
+    # 32), 48-position blocks would need the logits path
+    g16 = dict(n_q_heads=64, n_kv_heads=4, q_len=64, kv_capacity=65536, max_ctx_len=65536)
+    assert _full(_desc(select_mode=1, block_size=48, n_blocks=18, **g16)) == hs2.HS2_ERR_UNSUPPORTED
 
 
 def test_timed_calls_check_like_the_plain_ones(lib):

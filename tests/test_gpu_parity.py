@@ -531,6 +531,33 @@ def test_block_baseline_chunk_kernel(lq, ctx, bs, nb, kv):
     run_and_compare(w, f"block-chunk-lq{lq}-{kv}", mode="block", block_size=bs, n_blocks=nb, tokens=toks)
 
 
+@pytest.mark.parametrize("hq,hkv,lq,ctx,bs,nb,kv", [
+    (64, 4, 1, [20000, 3001], 64, 18, "bf16"),     # G = 16, decode scan block sums
+    (32, 1, 1, [50000, 900], 64, 18, "bf16"),      # MQA, two head blocks
+    (32, 1, 1, [30000], 128, 9, "fp8"),
+    (64, 4, 64, [7000, 2100], 64, 18, "bf16"),     # chunk kernel, 16 head slots
+    (32, 1, 64, [9000, 64], 64, 18, "bf16"),       # chunk kernel, 32 head slots
+    (32, 2, 40, [6000], 128, 9, "fp8"),
+    (32, 1, 16, [5000], 96, 12, "bf16"),           # per-token scan route (96 % 64 != 0)
+])
+def test_block_baseline_wide_groups(hq, hkv, lq, ctx, bs, nb, kv):
+    """Block comparator with more than 8 query heads per KV head (up to MQA): per-block
+    sums in 16 or 32 head slots from the decode scan and from the chunk kernel, block
+    masses over all G heads.  Sampled tokens (every token at q_len 1)."""
+    w = wl.Workload(f"block G{hq // hkv} lq{lq} {kv}", len(ctx), lq, hq, hkv, ctx_lens=ctx, n_needles=8,
+                    kv_dtype=kv, seed=3900 + hq + lq)
+    toks = sorted({(b, j) for b in range(len(ctx)) for j in (0, lq // 2, lq - 1)})
+    run_and_compare(w, f"block-wide-G{hq // hkv}-lq{lq}-{kv}", mode="block", block_size=bs, n_blocks=nb,
+                    tokens=toks)
+
+
+def test_block_baseline_wide_one_kernel_selection():
+    """MQA block mode with 128 blocks of 32 (more than the 64 best that a mass workgroup
+    keeps): the one-kernel selection over the 32-head block sums."""
+    w = wl.Workload("block MQA one kernel", 1, 1, 32, 1, ctx_lens=[300000], n_needles=16, seed=3950)
+    run_and_compare(w, "block-wide-one-kernel", mode="block", block_size=32, n_blocks=128)
+
+
 def test_rows_with_no_visible_position(sparse_path):
     """ctx_len < Lq leaves the first query tokens with nothing visible: out = 0, idx = -1."""
     w = wl.Workload("empty rows", 2, 4, 16, 2, ctx_lens=[6, 3000], seed=3800)
