@@ -129,10 +129,11 @@ enum {
 /* Host only, touches no GPU: checks a descriptor and that `workspace_bytes` covers
  * hs2_workspace_size(desc) (HS2_ERR_WORKSPACE otherwise; pass SIZE_MAX to check the
  * descriptor alone).  Limits: head_dim == 128,
- * 1 <= G <= 32; with G > 8 (up to MQA at 32 query heads) hs2_full_attn_select returns
- * HS2_ERR_UNSUPPORTED where only the logits path would serve the call (probs requested,
- * HS2_FLAG_FORCE_LOGITS, or HS2_FLAG_SCAN_VALU or a block_size that is not a multiple
- * of 32 in block mode), window + topk <= 4096
+ * 1 <= G <= 32; with G > 8 (up to MQA at 32 query heads) probs come from an exact
+ * re-score of every visible position after the selection, and hs2_full_attn_select
+ * returns HS2_ERR_UNSUPPORTED where only the logits path (8 head slots) would serve the
+ * call (block mode with HS2_FLAG_FORCE_LOGITS, HS2_FLAG_SCAN_VALU or a block_size that
+ * is not a multiple of 32), window + topk <= 4096
  * (token mode), block_size in [1, 4096] and
  * block_size * n_blocks <= 4096 (block mode), 1 <= q_len <= max_ctx_len <= cap,
  * cap < 2^31, batch * q_len <= 65535, n_kv_heads <= 65535 and

@@ -286,12 +286,36 @@ static hs2_status check_common(const hs2_attn_desc* d, const void* q, const void
 }
 
 // Which selection path hs2_full_attn_select takes, and whether it has one for this call.
+// More than 8 query heads per KV head: no logits path; probs, when asked for, come from
+// an exact re-score of every visible position after the selection (launch_probs_wide).
 static bool use_record_path(const hs2_attn_desc* d, const Layout& L, const float* probs) {
-  return L.fast_ok && probs == nullptr && (wide_group(d) || !has_flag(d, HS2_FLAG_FORCE_LOGITS));
+  return L.fast_ok && (probs == nullptr || wide_group(d)) && (wide_group(d) || !has_flag(d, HS2_FLAG_FORCE_LOGITS));
 }
 // Block comparator on the scans' block sums (needs no per-position scores).
 static bool block_sums_path(const hs2_attn_desc* d, const float* probs) {
-  return probs == nullptr && (chunk_block_path(d) || scan_block_path(d));
+  return (probs == nullptr || wide_group(d)) && (chunk_block_path(d) || scan_block_path(d));
+}
+// probs for G > 8: s of every visible position from the row's (M, 1/Z), after the selection
+static hipError_t probs_pass(const hs2_attn_desc* d, const Layout& L, const ScanArgs& sa, const float* mz,
+                             float* probs, hipStream_t stream) {
+  FastSelArgs fa{};
+  fa.mz = mz;
+  fa.ctx_len = sa.ctx_len;
+  fa.ctx_max = d->max_ctx_len;
+  fa.q = sa.q;
+  fa.k = sa.k;
+  fa.k_scale = sa.k_scale;
+  fa.cap = d->kv_capacity;
+  fa.scale_log2 = sa.scale_log2;
+  fa.n_sel = (int32_t)L.n_sel;
+  fa.Lq = d->q_len;
+  fa.Hq = d->n_q_heads;
+  fa.Hkv = d->n_kv_heads;
+  fa.G = L.G;
+  fa.window = d->window;
+  fa.topk = d->topk;
+  fa.S = L.S;
+  return launch_probs_wide(fa, probs, d->kv_capacity, d->kv_dtype == HS2_KV_FP8_E4M3FN, stream);
 }
 static hs2_status full_path_supported(const hs2_attn_desc* d, const Layout& L, const float* probs) {
   const bool fast = use_record_path(d, L, probs);
@@ -329,7 +353,7 @@ static ScanArgs scan_args(const hs2_attn_desc* d, const Layout& L, const void* q
 // scan's (32 positions) per-block log-sum-exp per head, the split combine, then the
 // block selection on those sums.  No per-position score is written or re-read.
 hs2_status block_sums_select(const hs2_attn_desc* desc, const Layout& L, ScanArgs sa,
-                             const int32_t* ctx_len, float* out, int32_t* idx, uint8_t* ws,
+                             const int32_t* ctx_len, float* out, int32_t* idx, float* probs, uint8_t* ws,
                              hipStream_t stream, const hs2_kernel_events* ev) {
   sa.records = nullptr;
   sa.hist_part = nullptr;
@@ -382,6 +406,7 @@ hs2_status block_sums_select(const hs2_attn_desc* desc, const Layout& L, ScanArg
   sl.bcand = L.bm_wgs > 0 ? reinterpret_cast<uint64_t*>(ws + L.off_bcand) : nullptr;
   sl.bm_wgs = L.bm_wgs;
   if (launch_block_select(sl, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+  if (probs != nullptr && probs_pass(desc, L, sa, ca.mz, probs, stream) != hipSuccess) return HS2_ERR_LAUNCH;
   return HS2_OK;
 }
 
@@ -419,7 +444,7 @@ static hs2_status full_select_launch(const hs2_attn_desc* desc, const Layout& L,
   // when the caller wants all probabilities (probs) or for the block comparator.
   const bool fast = use_record_path(desc, L, probs);
   ScanArgs sa = scan_args(desc, L, q, k, v, k_scale, v_scale, ctx_len, ws);
-  if (block_sums_path(desc, probs)) return block_sums_select(desc, L, sa, ctx_len, out, idx, ws, stream, ev);
+  if (block_sums_path(desc, probs)) return block_sums_select(desc, L, sa, ctx_len, out, idx, probs, ws, stream, ev);
   sa.logits = reinterpret_cast<float*>(ws + L.off_logits);
   sa.records = reinterpret_cast<uint16_t*>(ws + L.off_records);
   sa.hist_part = reinterpret_cast<uint16_t*>(ws + L.off_hist_part);
@@ -492,6 +517,7 @@ static hs2_status full_select_launch(const hs2_attn_desc* desc, const Layout& L,
     fa.S = L.S;
     if (launch_fast_candidates(fa, fp8, stream) != hipSuccess) return HS2_ERR_LAUNCH;
     if (launch_fast_final(fa, stream) != hipSuccess) return HS2_ERR_LAUNCH;
+    if (probs != nullptr && probs_pass(desc, L, sa, ca.mz, probs, stream) != hipSuccess) return HS2_ERR_LAUNCH;
     return HS2_OK;
   }
 

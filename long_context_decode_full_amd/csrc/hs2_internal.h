@@ -205,6 +205,9 @@ hipError_t noalloc_scratch(void** ptr);
 
 hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st);
 hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t st);
+// probs (s of every visible position) for G > 8: the exact re-score of every position
+// (uses q, k, k_scale, mz, ctx_len, ctx_max, cap, scale_log2, n_sel, Lq, Hq, Hkv, G)
+hipError_t launch_probs_wide(const FastSelArgs& a, float* probs, int64_t probs_stride, bool fp8, hipStream_t st);
 hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st);
 hipError_t launch_scan_mfma(const ScanArgs& a, bool fp8, int B, hipStream_t st);
 // The decode scan in block-comparator mode: per-32-position block sums into a.blse (G <= 8).

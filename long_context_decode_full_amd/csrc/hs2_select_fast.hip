@@ -1152,4 +1152,47 @@ hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+namespace {
+// Group-summed probabilities s of every visible position of a row for more than 8
+// query heads per KV head (the logits path holds 8 head slots): the candidate stage's
+// matrix-core re-score applied to each position once the row's (M, 1/Z) are known.
+// Work unit: kProbsChunk positions of one row (blockIdx.x = row * chunks + chunk).
+constexpr int kProbsChunk = 2048;
+template <bool kFp8>
+__global__ __launch_bounds__(kThreads) void probs_wide_kernel(FastSelArgs a, float* probs, int64_t probs_stride,
+                                                                int chunks) {
+  const int64_t sel = blockIdx.x / (uint32_t)chunks;
+  const int64_t p0 = (int64_t)(blockIdx.x % (uint32_t)chunks) * kProbsChunk;
+  const RowGeom rg = row_geom(a, sel);
+  if (p0 >= rg.n) return;
+  const int nu = (int)min((int64_t)kProbsChunk, rg.n - p0);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t bj = sel / a.Hkv;
+  const int g = (int)(sel - bj * a.Hkv);
+  const int b = (int)(bj / a.Lq);
+  const int r = lane & 15;
+  const int rgrp = lane >> 4;
+  WideQuery wq;
+  load_wide_query(a, sel, bj, g, r, rgrp, wq);
+  const int64_t head_row0 = (int64_t)(b * a.Hkv + g) * a.cap;
+  const uint8_t* kb = a.k + head_row0 * (kFp8 ? 128 : 256);
+  const float* ksb = kFp8 ? a.k_scale + head_row0 : nullptr;
+  float* prow = probs + sel * probs_stride + p0;
+  rescore_wide<kFp8>(nu, wave, r, rgrp, wq, kb, ksb, a.scale_log2, a.G,
+                     [&](int i) { return (uint32_t)(p0 + i); }, [&](int i, float sv) { prow[i] = sv; });
+}
+}  // namespace
+
+hipError_t launch_probs_wide(const FastSelArgs& a, float* probs, int64_t probs_stride, bool fp8, hipStream_t st) {
+  if (a.G <= kSlots || a.G > kMaxHeads) return hipErrorInvalidValue;
+  const int chunks = (int)((a.ctx_max + kProbsChunk - 1) / kProbsChunk);
+  const dim3 grid((uint32_t)((uint64_t)a.n_sel * chunks));
+  if (fp8)
+    hipLaunchKernelGGL(probs_wide_kernel<true>, grid, dim3(kThreads), 0, st, a, probs, probs_stride, chunks);
+  else
+    hipLaunchKernelGGL(probs_wide_kernel<false>, grid, dim3(kThreads), 0, st, a, probs, probs_stride, chunks);
+  return hipGetLastError();
+}
+
 }  // namespace hs2

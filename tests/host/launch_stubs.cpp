@@ -106,6 +106,13 @@ hipError_t launch_fast_candidates(const FastSelArgs& a, bool, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_probs_wide(const FastSelArgs& a, float* probs, int64_t probs_stride, bool, hipStream_t) {
+  in_ws(a.mz, (uint64_t)a.n_sel * kMaxHeads * 2ull * 4ull, "probs: (M, 1/Z)");
+  if (probs == nullptr || probs_stride < a.ctx_max) fail("probs: rows");
+  if (a.G <= kSlots || a.G > kMaxHeads) fail("probs: group size");
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t) {
   in_ws(a.cand_keys, (uint64_t)a.n_sel * a.n_chunks * (uint64_t)a.chunk_len * 8ull, "final: keys");
   if (a.n_chunks > kMaxFastChunks) fail("final: chunk count beyond its LDS");

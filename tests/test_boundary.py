@@ -246,12 +246,11 @@ def test_invalid_desc_checked_before_pointers(lib):
 
 
 def test_wide_groups_have_no_logits_path(lib):
-    """More than 8 query heads per KV head: block mode runs on the scans' block sums, and
-    every call that only the logits path (8 head slots) could serve is refused before
-    anything is enqueued (fake device pointers, never touched)."""
+    """More than 8 query heads per KV head: token mode on the record path, block mode on
+    the scans' block sums (probs from a re-score pass), and every call that only the
+    logits path (8 head slots) could serve is refused before anything is enqueued (fake
+    device pointers, never touched)."""
     mqa = dict(n_q_heads=32, n_kv_heads=1, kv_capacity=65536, max_ctx_len=65536)
-    assert _full(_desc(**mqa), probs=FAKE) == hs2.HS2_ERR_UNSUPPORTED
-    assert _full(_desc(select_mode=1, **mqa), probs=FAKE) == hs2.HS2_ERR_UNSUPPORTED
     assert _full(_desc(select_mode=1, flags=hs2.HS2_FLAG_FORCE_LOGITS, **mqa)) == hs2.HS2_ERR_UNSUPPORTED
     assert _full(_desc(select_mode=1, flags=hs2.HS2_FLAG_SCAN_VALU, **mqa)) == hs2.HS2_ERR_UNSUPPORTED
     assert _full(_desc(select_mode=1, block_size=48, n_blocks=18, **mqa)) == hs2.HS2_ERR_UNSUPPORTED

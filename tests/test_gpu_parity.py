@@ -264,6 +264,22 @@ def test_wide_groups_decode(hq, hkv, kv, ctx):
     run_and_compare(w, f"wide-G{hq // hkv}-{kv}")
 
 
+@pytest.mark.parametrize("hq,hkv,lq,ctx,kv,mode", [(32, 1, 1, [7000, 3100], "bf16", "token"),
+                                                (32, 1, 1, [6200], "fp8", "token"),
+                                                (64, 4, 1, [5000, 900], "bf16", "block"),
+                                                (32, 1, 16, [3000], "bf16", "token")])
+def test_wide_group_probs(hq, hkv, lq, ctx, kv, mode):
+    """probs with more than 8 query heads per KV head: the selection on the record path
+    or the block sums, then s of every visible position from an exact re-score pass;
+    every position against the oracle's float64 s (rel err <= 1e-5)."""
+    w = wl.Workload(f"G{hq // hkv} probs {kv}", len(ctx), lq, hq, hkv, ctx_lens=ctx, n_needles=8, kv_dtype=kv,
+                    seed=2560 + hq + lq)
+    toks = sorted({(b, j) for b in range(len(ctx)) for j in (0, lq - 1)})
+    got, _ = run_and_compare(w, f"wide-probs-G{hq // hkv}-{kv}-{mode}-lq{lq}", mode=mode, with_probs=True,
+                             tokens=toks)
+    assert got["probs"] is not None
+
+
 @pytest.mark.parametrize("fused", ["0", "1"])
 def test_wide_group_sparse_paths(fused):
     """MQA sparse layers on the split matrix-core gather + combine (decode default) and
@@ -307,13 +323,15 @@ def test_mqa_chunk_full_config_sample():
 
 
 def test_wide_group_logits_path_unsupported():
-    """Requesting all probabilities needs the logits path, which keeps 8 head slots:
-    more than 8 heads per KV head is reported as unsupported, nothing is launched."""
-    from long_context_decode_full_amd import HS2_ERR_UNSUPPORTED, Hs2Error
+    """The logits path keeps 8 head slots: a call that only it could serve (block mode
+    with HS2_FLAG_FORCE_LOGITS) at more than 8 heads per KV head is reported as
+    unsupported and nothing is launched (probs themselves come from the re-score pass,
+    test_wide_group_probs)."""
+    from long_context_decode_full_amd import HS2_ERR_UNSUPPORTED, HS2_FLAG_FORCE_LOGITS, Hs2Error
     from long_context_decode_full_amd.runner import HybridBlockDevice
-    w = wl.Workload("mqa probs", 1, 1, 32, 1, ctx_lens=[3000], n_needles=4, seed=2530)
+    w = wl.Workload("mqa logits", 1, 1, 32, 1, ctx_lens=[3000], n_needles=4, seed=2530)
     inp = wl.make_inputs(w)
-    dev = HybridBlockDevice(inp, with_probs=True)
+    dev = HybridBlockDevice(inp, mode="block", flags=HS2_FLAG_FORCE_LOGITS)
     with pytest.raises(Hs2Error) as err:
         dev.full()
     assert err.value.status == HS2_ERR_UNSUPPORTED
