@@ -1186,12 +1186,13 @@ __global__ __launch_bounds__(kThreads) void probs_wide_kernel(FastSelArgs a, flo
 
 hipError_t launch_probs_wide(const FastSelArgs& a, float* probs, int64_t probs_stride, bool fp8, hipStream_t st) {
   if (a.G <= kSlots || a.G > kMaxHeads) return hipErrorInvalidValue;
-  const int chunks = (int)((a.ctx_max + kProbsChunk - 1) / kProbsChunk);
-  const dim3 grid((uint32_t)((uint64_t)a.n_sel * chunks));
+  const int64_t chunks = (a.ctx_max + kProbsChunk - 1) / kProbsChunk;
+  if ((uint64_t)a.n_sel * (uint64_t)chunks > 0x7FFFFFFFull) return hipErrorInvalidValue;   // grid x
+  const dim3 grid((uint32_t)((uint64_t)a.n_sel * (uint64_t)chunks));
   if (fp8)
-    hipLaunchKernelGGL(probs_wide_kernel<true>, grid, dim3(kThreads), 0, st, a, probs, probs_stride, chunks);
+    hipLaunchKernelGGL(probs_wide_kernel<true>, grid, dim3(kThreads), 0, st, a, probs, probs_stride, (int)chunks);
   else
-    hipLaunchKernelGGL(probs_wide_kernel<false>, grid, dim3(kThreads), 0, st, a, probs, probs_stride, chunks);
+    hipLaunchKernelGGL(probs_wide_kernel<false>, grid, dim3(kThreads), 0, st, a, probs, probs_stride, (int)chunks);
   return hipGetLastError();
 }
 
