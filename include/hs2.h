@@ -341,11 +341,13 @@ hs2_status hs2_full_attn_select_noalloc(const hs2_attn_desc* desc,
 
 /* ------------------------------------------------------------------ kernel timing
  * Benchmark support without library state: the caller creates two HIP events
- * (hipEventCreate) and passes them; the call records `begin` on `stream` just before
- * its dominant kernel -- the context scan of hs2_full_attn_select, the gather of
- * hs2_sparse_attn -- and `end` just after it, so hipEventElapsedTime(begin, end) is
- * that kernel's duration.  Otherwise identical to the untimed calls (which are these
- * with events == NULL).  The caller owns and destroys the events. */
+ * (hipEventCreate) and passes them; the call launches its dominant kernel -- the
+ * context scan of hs2_full_attn_select, the gather of hs2_sparse_attn -- with
+ * hipExtLaunchKernel, which sets `begin` to that kernel's start and `end` to its end,
+ * so hipEventElapsedTime(begin, end) is the kernel's own duration (the dispatch and
+ * completion latency around it excluded).  Either event may be NULL.  Otherwise
+ * identical to the untimed calls (which are these with events == NULL).  The caller
+ * owns and destroys the events. */
 typedef struct hs2_kernel_events {
   hipEvent_t begin;
   hipEvent_t end;

@@ -223,12 +223,17 @@ Layout make_layout(const hs2_attn_desc* d, bool logits_area = true) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// HIP events around the dominant kernel of a call (hs2_*_timed), or none.
-void event_record(const hs2_kernel_events* ev, bool begin, hipStream_t st) {
-  if (ev == nullptr) return;
-  const hipEvent_t e = begin ? ev->begin : ev->end;
-  if (e != nullptr) (void)hipEventRecord(e, st);
-}
+// The events of a timed call (hs2_*_timed), bound to its dominant kernel's launch.
+struct TimedLaunch {
+  KernelEvents kev{};
+  const KernelEvents* ptr = nullptr;
+  explicit TimedLaunch(const hs2_kernel_events* ev) {
+    if (ev != nullptr) {
+      kev = KernelEvents{ev->begin, ev->end};
+      ptr = &kev;
+    }
+  }
+};
 
 }  // namespace
 }  // namespace hs2
@@ -363,11 +368,11 @@ hs2_status block_sums_select(const hs2_attn_desc* desc, const Layout& L, ScanArg
   sa.window = 0;
   sa.n_split = L.rec_n_split;
   sa.split_len = L.rec_split_len;
-  event_record(ev, true, stream);
+  const TimedLaunch tl(ev);
   const hipError_t e = chunk_block_path(desc)
-                           ? launch_chunk_mfma(sa, desc->batch, desc->kv_dtype == HS2_KV_FP8_E4M3FN, stream)
-                           : launch_scan_mfma_blocks(sa, desc->kv_dtype == HS2_KV_FP8_E4M3FN, desc->batch, stream);
-  event_record(ev, false, stream);
+                           ? launch_chunk_mfma(sa, desc->batch, desc->kv_dtype == HS2_KV_FP8_E4M3FN, stream, tl.ptr)
+                           : launch_scan_mfma_blocks(sa, desc->kv_dtype == HS2_KV_FP8_E4M3FN, desc->batch, stream,
+                                                     tl.ptr);
   if (e != hipSuccess) return HS2_ERR_LAUNCH;
 
   CombineArgs ca{};
@@ -453,13 +458,12 @@ static hs2_status full_select_launch(const hs2_attn_desc* desc, const Layout& L,
   sa.n_split = fast ? L.rec_n_split : L.n_split;
   sa.split_len = fast ? L.rec_split_len : L.split_len;
 
-  event_record(ev, true, stream);
   // record path: matrix-core scan (HS2_FLAG_SCAN_VALU selects the VALU scan instead)
   const bool mfma = fast && (wide_group(desc) || !has_flag(desc, HS2_FLAG_SCAN_VALU));
-  const hipError_t e = (fast && chunk_path(desc)) ? launch_chunk_mfma(sa, desc->batch, fp8, stream)
-                 : mfma                     ? launch_scan_mfma(sa, fp8, desc->batch, stream)
-                                            : launch_scan_dense(sa, fp8, fast, desc->batch, stream);
-  event_record(ev, false, stream);
+  const TimedLaunch tl(ev);
+  const hipError_t e = (fast && chunk_path(desc)) ? launch_chunk_mfma(sa, desc->batch, fp8, stream, tl.ptr)
+                 : mfma                     ? launch_scan_mfma(sa, fp8, desc->batch, stream, tl.ptr)
+                                            : launch_scan_dense(sa, fp8, fast, desc->batch, stream, tl.ptr);
   if (e != hipSuccess) return HS2_ERR_LAUNCH;
 
   CombineArgs ca{};
@@ -628,23 +632,21 @@ static hs2_status sparse_impl(const hs2_attn_desc* desc, const void* q, const vo
   const bool fused = has_flag(desc, HS2_FLAG_SPARSE_FUSED)   ? true
                     : has_flag(desc, HS2_FLAG_SPARSE_SPLIT) ? false
                                                             : rows >= kFusedSparseRows;
-  event_record(ev, true, stream);
+  const TimedLaunch tl(ev);
   if (fused) {
     sa.n_split = 1;
     sa.split_len = L.S;
-    const hipError_t e = launch_gather_mfma(sa, out, fp8, desc->batch, stream);
-    event_record(ev, false, stream);
+    const hipError_t e = launch_gather_mfma(sa, out, fp8, desc->batch, stream, tl.ptr);
     return e == hipSuccess ? HS2_OK : HS2_ERR_LAUNCH;
   }
   hipError_t e;
   if (wide_group(desc)) {
     sa.split_len = L.G > 16 ? 128 : 256;
     sa.n_split = (int32_t)ceil_div(L.S, sa.split_len);
-    e = launch_gather_mfma(sa, nullptr, fp8, desc->batch, stream);
+    e = launch_gather_mfma(sa, nullptr, fp8, desc->batch, stream, tl.ptr);
   } else {
-    e = launch_scan_sparse(sa, fp8, desc->batch, stream);
+    e = launch_scan_sparse(sa, fp8, desc->batch, stream, tl.ptr);
   }
-  event_record(ev, false, stream);
   if (e != hipSuccess) return HS2_ERR_LAUNCH;
 
   CombineArgs ca{};

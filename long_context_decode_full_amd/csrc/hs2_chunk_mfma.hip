@@ -636,22 +636,22 @@ dim3 chunk_grid(const ScanArgs& a, int B) {
   return dim3(a.n_split * ((a.Lq + tokens_per_wg<kGp>() - 1) / tokens_per_wg<kGp>()), a.Hkv, B);
 }
 template <bool kFp8>
-hipError_t launch_chunk_t(const ScanArgs& a, int B, hipStream_t st) {
+hipError_t launch_chunk_t(const ScanArgs& a, int B, hipStream_t st, const KernelEvents* ev) {
   if (a.blse != nullptr) {   // block mode: per-block sums in kGp head slots
     if (a.G <= 8)
-      hipLaunchKernelGGL((chunk_mfma_kernel<8, true, kFp8>), chunk_grid<8>(a, B), dim3(kCThreads), 0, st, a);
+      launch_on(ev, chunk_mfma_kernel<8, true, kFp8>, chunk_grid<8>(a, B), dim3(kCThreads), 0, st, a);
     else if (a.G <= 16)
-      hipLaunchKernelGGL((chunk_mfma_kernel<16, true, kFp8>), chunk_grid<16>(a, B), dim3(kCThreads), 0, st, a);
+      launch_on(ev, chunk_mfma_kernel<16, true, kFp8>, chunk_grid<16>(a, B), dim3(kCThreads), 0, st, a);
     else if (a.G <= 32)
-      hipLaunchKernelGGL((chunk_mfma_kernel<32, true, kFp8>), chunk_grid<32>(a, B), dim3(kCThreads), 0, st, a);
+      launch_on(ev, chunk_mfma_kernel<32, true, kFp8>, chunk_grid<32>(a, B), dim3(kCThreads), 0, st, a);
     else
       return hipErrorInvalidValue;
   } else if (a.G <= 8) {
-    hipLaunchKernelGGL((chunk_mfma_kernel<8, false, kFp8>), chunk_grid<8>(a, B), dim3(kCThreads), 0, st, a);
+    launch_on(ev, chunk_mfma_kernel<8, false, kFp8>, chunk_grid<8>(a, B), dim3(kCThreads), 0, st, a);
   } else if (a.G <= 16) {
-    hipLaunchKernelGGL((chunk_mfma_kernel<16, false, kFp8>), chunk_grid<16>(a, B), dim3(kCThreads), 0, st, a);
+    launch_on(ev, chunk_mfma_kernel<16, false, kFp8>, chunk_grid<16>(a, B), dim3(kCThreads), 0, st, a);
   } else if (a.G <= 32) {
-    hipLaunchKernelGGL((chunk_mfma_kernel<32, false, kFp8>), chunk_grid<32>(a, B), dim3(kCThreads), 0, st, a);
+    launch_on(ev, chunk_mfma_kernel<32, false, kFp8>, chunk_grid<32>(a, B), dim3(kCThreads), 0, st, a);
   } else {
     return hipErrorInvalidValue;
   }
@@ -661,8 +661,8 @@ hipError_t launch_chunk_t(const ScanArgs& a, int B, hipStream_t st) {
 }  // namespace
 
 // Token and block mode for G <= 32.
-hipError_t launch_chunk_mfma(const ScanArgs& a, int B, bool fp8, hipStream_t st) {
-  return fp8 ? launch_chunk_t<true>(a, B, st) : launch_chunk_t<false>(a, B, st);
+hipError_t launch_chunk_mfma(const ScanArgs& a, int B, bool fp8, hipStream_t st, const KernelEvents* ev) {
+  return fp8 ? launch_chunk_t<true>(a, B, st, ev) : launch_chunk_t<false>(a, B, st, ev);
 }
 
 }  // namespace hs2

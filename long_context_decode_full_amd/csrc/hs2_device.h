@@ -1,10 +1,21 @@
 // Device helpers shared by the HIP kernels (gfx950 / CDNA4, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace hs2 {
+
+// Enqueue `kernel` on `st`; with events (the timed entry points) hipExtLaunchKernelGGL
+// sets them to the kernel's own start and end times.
+template <typename Ev, typename K, typename... Args>
+inline void launch_on(const Ev* ev, K kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t st, Args... args) {
+  if (ev != nullptr)
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, st, ev->begin, ev->end, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shm, st, args...);
+}
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;

@@ -203,22 +203,33 @@ hipError_t launch_add(float* out, const float* add, int64_t n, hipStream_t st);
 constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
 hipError_t noalloc_scratch(void** ptr);
 
+// Events bound to one kernel launch (the timed entry points): the launch takes them
+// through hipExtLaunchKernelGGL, so they carry that kernel's own start and end times
+// (no dispatch or completion latency in between).  Either may be null.
+struct KernelEvents {
+  hipEvent_t begin;
+  hipEvent_t end;
+};
+
 hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st);
 hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t st);
 // probs (s of every visible position) for G > 8: the exact re-score of every position
 // (uses q, k, k_scale, mz, ctx_len, ctx_max, cap, scale_log2, n_sel, Lq, Hq, Hkv, G)
 hipError_t launch_probs_wide(const FastSelArgs& a, float* probs, int64_t probs_stride, bool fp8, hipStream_t st);
-hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st);
-hipError_t launch_scan_mfma(const ScanArgs& a, bool fp8, int B, hipStream_t st);
+hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st,
+                             const KernelEvents* ev = nullptr);
+hipError_t launch_scan_mfma(const ScanArgs& a, bool fp8, int B, hipStream_t st, const KernelEvents* ev = nullptr);
 // The decode scan in block-comparator mode: per-32-position block sums into a.blse (G <= 8).
-hipError_t launch_scan_mfma_blocks(const ScanArgs& a, bool fp8, int B, hipStream_t st);
+hipError_t launch_scan_mfma_blocks(const ScanArgs& a, bool fp8, int B, hipStream_t st,
+                                   const KernelEvents* ev = nullptr);
 // sparse layer on the matrix cores, one workgroup per (query token, KV head, split of
 // a.split_len index entries); out != nullptr (one split): normalised output, else
 // partials in a.part for launch_combine (S <= 4096)
-hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool fp8, int B, hipStream_t st);
+hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool fp8, int B, hipStream_t st,
+                              const KernelEvents* ev = nullptr);
 // query chunks (q_len > 1) on the matrix cores, bf16 or fp8 caches (chunk_mfma_kernel)
-hipError_t launch_chunk_mfma(const ScanArgs& a, int B, bool fp8, hipStream_t st);
-hipError_t launch_scan_sparse(const ScanArgs& a, bool fp8, int B, hipStream_t st);
+hipError_t launch_chunk_mfma(const ScanArgs& a, int B, bool fp8, hipStream_t st, const KernelEvents* ev = nullptr);
+hipError_t launch_scan_sparse(const ScanArgs& a, bool fp8, int B, hipStream_t st, const KernelEvents* ev = nullptr);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_groupsum(const SelectArgs& a, hipStream_t st);
 hipError_t launch_refine(const SelectArgs& a, int pass, hipStream_t st);

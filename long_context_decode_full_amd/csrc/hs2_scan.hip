@@ -552,28 +552,29 @@ __global__ __launch_bounds__(256) void combine_small_kernel(CombineArgs a) {
 
 }  // namespace
 
-hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st) {
+hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st,
+                             const KernelEvents* ev) {
   dim3 grid(a.n_split, a.Hkv, B * a.Lq);
   if (records) {
     if (fp8)
-      hipLaunchKernelGGL((scan_kernel<kDenseRecords, true>), grid, dim3(kThreads), 0, st, a);
+      launch_on(ev, scan_kernel<kDenseRecords, true>, grid, dim3(kThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((scan_kernel<kDenseRecords, false>), grid, dim3(kThreads), 0, st, a);
+      launch_on(ev, scan_kernel<kDenseRecords, false>, grid, dim3(kThreads), 0, st, a);
   } else {
     if (fp8)
-      hipLaunchKernelGGL((scan_kernel<kDenseLogits, true>), grid, dim3(kThreads), 0, st, a);
+      launch_on(ev, scan_kernel<kDenseLogits, true>, grid, dim3(kThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((scan_kernel<kDenseLogits, false>), grid, dim3(kThreads), 0, st, a);
+      launch_on(ev, scan_kernel<kDenseLogits, false>, grid, dim3(kThreads), 0, st, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_scan_sparse(const ScanArgs& a, bool fp8, int B, hipStream_t st) {
+hipError_t launch_scan_sparse(const ScanArgs& a, bool fp8, int B, hipStream_t st, const KernelEvents* ev) {
   dim3 grid(a.n_split, a.Hkv, B * a.Lq);
   if (fp8)
-    hipLaunchKernelGGL((scan_kernel<kSparseGather, true>), grid, dim3(kThreads), 0, st, a);
+    launch_on(ev, scan_kernel<kSparseGather, true>, grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((scan_kernel<kSparseGather, false>), grid, dim3(kThreads), 0, st, a);
+    launch_on(ev, scan_kernel<kSparseGather, false>, grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -814,65 +814,66 @@ __global__ __launch_bounds__(kThreads, 1) void gather_mfma_kernel(ScanArgs a, fl
 // Head layout by group size: G <= 8 (8-lane records, 8 waves), G <= 16 (16-lane
 // records, 8 waves), G <= 32 (two head blocks, 4 waves with up to 512 registers).
 template <bool kFp8, bool kVec>
-static void launch_scan_g(const ScanArgs& a, dim3 grid, hipStream_t st) {
+static void launch_scan_g(const ScanArgs& a, dim3 grid, hipStream_t st, const KernelEvents* ev) {
   if (a.G <= 8)
-    hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 1, false, 512>), grid, dim3(512), 0, st, a);
+    launch_on(ev, scan_mfma_kernel<kFp8, kVec, 1, false, 512>, grid, dim3(512), 0, st, a);
   else if (a.G <= 16)
-    hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 1, true, 512>), grid, dim3(512), 0, st, a);
+    launch_on(ev, scan_mfma_kernel<kFp8, kVec, 1, true, 512>, grid, dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 2, true, 256>), grid, dim3(256), 0, st, a);
+    launch_on(ev, scan_mfma_kernel<kFp8, kVec, 2, true, 256>, grid, dim3(256), 0, st, a);
 }
 
 // the block comparator's scan, same head layouts (per-block sums in blse_heads_of(G) slots)
 template <bool kFp8, bool kVec>
-static void launch_scan_blocks_g(const ScanArgs& a, dim3 grid, hipStream_t st) {
+static void launch_scan_blocks_g(const ScanArgs& a, dim3 grid, hipStream_t st, const KernelEvents* ev) {
   if (a.G <= 8)
-    hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 1, false, 512, true>), grid, dim3(512), 0, st, a);
+    launch_on(ev, scan_mfma_kernel<kFp8, kVec, 1, false, 512, true>, grid, dim3(512), 0, st, a);
   else if (a.G <= 16)
-    hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 1, true, 512, true>), grid, dim3(512), 0, st, a);
+    launch_on(ev, scan_mfma_kernel<kFp8, kVec, 1, true, 512, true>, grid, dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL((scan_mfma_kernel<kFp8, kVec, 2, true, 256, true>), grid, dim3(256), 0, st, a);
+    launch_on(ev, scan_mfma_kernel<kFp8, kVec, 2, true, 256, true>, grid, dim3(256), 0, st, a);
 }
 
-hipError_t launch_scan_mfma_blocks(const ScanArgs& a, bool fp8, int B, hipStream_t st) {
+hipError_t launch_scan_mfma_blocks(const ScanArgs& a, bool fp8, int B, hipStream_t st, const KernelEvents* ev) {
   if (a.G > kMaxHeads || a.blse == nullptr) return hipErrorInvalidValue;
   dim3 grid(a.n_split, a.Hkv, B * a.Lq);
   if (fp8 && a.cap % 4 == 0)
-    launch_scan_blocks_g<true, true>(a, grid, st);
+    launch_scan_blocks_g<true, true>(a, grid, st, ev);
   else if (fp8)
-    launch_scan_blocks_g<true, false>(a, grid, st);
+    launch_scan_blocks_g<true, false>(a, grid, st, ev);
   else
-    launch_scan_blocks_g<false, false>(a, grid, st);
+    launch_scan_blocks_g<false, false>(a, grid, st, ev);
   return hipGetLastError();
 }
 
-hipError_t launch_scan_mfma(const ScanArgs& a, bool fp8, int B, hipStream_t st) {
+hipError_t launch_scan_mfma(const ScanArgs& a, bool fp8, int B, hipStream_t st, const KernelEvents* ev) {
   dim3 grid(a.n_split, a.Hkv, B * a.Lq);
   if (fp8 && a.cap % 4 == 0)
-    launch_scan_g<true, true>(a, grid, st);
+    launch_scan_g<true, true>(a, grid, st, ev);
   else if (fp8)
-    launch_scan_g<true, false>(a, grid, st);
+    launch_scan_g<true, false>(a, grid, st, ev);
   else
-    launch_scan_g<false, false>(a, grid, st);
+    launch_scan_g<false, false>(a, grid, st, ev);
   return hipGetLastError();
 }
 
 template <bool kFp8>
-static void launch_gather_g(const ScanArgs& a, float* out, dim3 grid, hipStream_t st) {
+static void launch_gather_g(const ScanArgs& a, float* out, dim3 grid, hipStream_t st, const KernelEvents* ev) {
   if (a.G <= 8)
-    hipLaunchKernelGGL((gather_mfma_kernel<kFp8, 1, false, 512>), grid, dim3(512), 0, st, a, out);
+    launch_on(ev, gather_mfma_kernel<kFp8, 1, false, 512>, grid, dim3(512), 0, st, a, out);
   else if (a.G <= 16)
-    hipLaunchKernelGGL((gather_mfma_kernel<kFp8, 1, true, 512>), grid, dim3(512), 0, st, a, out);
+    launch_on(ev, gather_mfma_kernel<kFp8, 1, true, 512>, grid, dim3(512), 0, st, a, out);
   else
-    hipLaunchKernelGGL((gather_mfma_kernel<kFp8, 2, true, 256>), grid, dim3(256), 0, st, a, out);
+    launch_on(ev, gather_mfma_kernel<kFp8, 2, true, 256>, grid, dim3(256), 0, st, a, out);
 }
 
-hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool fp8, int B, hipStream_t st) {
+hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool fp8, int B, hipStream_t st,
+                              const KernelEvents* ev) {
   dim3 grid(a.n_split, a.Hkv, B * a.Lq);
   if (fp8)
-    launch_gather_g<true>(a, out, grid, st);
+    launch_gather_g<true>(a, out, grid, st, ev);
   else
-    launch_gather_g<false>(a, out, grid, st);
+    launch_gather_g<false>(a, out, grid, st, ev);
   return hipGetLastError();
 }
 

@@ -119,36 +119,36 @@ hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
-hipError_t launch_scan_dense(const ScanArgs& a, bool, bool records, int B, hipStream_t) {
+hipError_t launch_scan_dense(const ScanArgs& a, bool, bool records, int B, hipStream_t, const KernelEvents*) {
   check_scan(a, B, records);
   if (!records) in_ws(a.logits, sel_rows(a, B) * (uint64_t)a.logit_stride * 8ull * 4ull, "scan: logits");
   return hipSuccess;
 }
-hipError_t launch_scan_mfma(const ScanArgs& a, bool, int B, hipStream_t) {
+hipError_t launch_scan_mfma(const ScanArgs& a, bool, int B, hipStream_t, const KernelEvents*) {
   if (a.split_len > kMaxRecordSplit) fail("mfma scan: split beyond its LDS records");
   check_scan(a, B, true);
   return hipSuccess;
 }
-hipError_t launch_scan_mfma_blocks(const ScanArgs& a, bool, int B, hipStream_t) {
+hipError_t launch_scan_mfma_blocks(const ScanArgs& a, bool, int B, hipStream_t, const KernelEvents*) {
   if (a.split_len > kMaxRecordSplit) fail("block scan: split beyond the scan's LDS");
   if (a.G > kSlots || a.blse == nullptr) fail("block scan: head slots or no block sums");
   if (a.blse != nullptr && (int64_t)a.blse_stride * 32 < a.ctx_max) fail("block scan: block sums do not cover the context");
   check_scan(a, B, false);
   return hipSuccess;
 }
-hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool, int B, hipStream_t) {
+hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool, int B, hipStream_t, const KernelEvents*) {
   if (out == nullptr) in_ws(a.part, sel_rows(a, B) * a.n_split * a.G * kPartStride * 4ull, "gather: partials");
   if ((int64_t)a.n_split * a.split_len < a.S) fail("gather: splits do not cover the index row");
   ++g_launches;
   return hipSuccess;
 }
-hipError_t launch_chunk_mfma(const ScanArgs& a, int B, bool fp8, hipStream_t) {
+hipError_t launch_chunk_mfma(const ScanArgs& a, int B, bool fp8, hipStream_t, const KernelEvents*) {
   if (a.G > kMaxHeads || (a.blse != nullptr && a.G > kSlots)) fail("chunk kernel: head slots");
   if (fp8 && (a.k_scale == nullptr || a.v_scale == nullptr)) fail("chunk kernel: fp8 scales");
   check_scan(a, B, a.blse == nullptr);
   return hipSuccess;
 }
-hipError_t launch_scan_sparse(const ScanArgs& a, bool, int B, hipStream_t) {
+hipError_t launch_scan_sparse(const ScanArgs& a, bool, int B, hipStream_t, const KernelEvents*) {
   in_ws(a.part, sel_rows(a, B) * a.n_split * a.G * kPartStride * 4ull, "sparse: partials");
   if ((int64_t)a.n_split * a.split_len < a.S) fail("sparse: splits do not cover the index row");
   ++g_launches;
