@@ -118,13 +118,17 @@ enum {
   /* Query chunks (q_len > 1) run the decode scan once per query token instead of the
    * matrix-core chunk kernel. */
   HS2_FLAG_CHUNK_PER_TOKEN = 1u << 3,
-  /* Sparse layers: one workgroup per (token, KV head) gathering the whole index row
-   * (the default from 256 rows), or the split gather + combine (the default below).
-   * Setting both is HS2_ERR_INVALID_ARG. */
+  /* Sparse layers (rows = batch * q_len * n_kv_heads): one workgroup per (token, KV
+   * head) gathering the whole index row (SPARSE_FUSED, the default from 256 rows); the
+   * split gather + combine (SPARSE_SPLIT, the default from 64 rows); one workgroup per
+   * (token, query head) gathering its KV head's whole index row, no combine launch
+   * (SPARSE_HEAD, the default below 64 rows).  Setting more than one is
+   * HS2_ERR_INVALID_ARG. */
   HS2_FLAG_SPARSE_FUSED = 1u << 4,
-  HS2_FLAG_SPARSE_SPLIT = 1u << 5
+  HS2_FLAG_SPARSE_SPLIT = 1u << 5,
+  HS2_FLAG_SPARSE_HEAD = 1u << 6
 };
-#define HS2_FLAGS_ALL 0x3Fu
+#define HS2_FLAGS_ALL 0x7Fu
 
 /* Host only, touches no GPU: checks a descriptor and that `workspace_bytes` covers
  * hs2_workspace_size(desc) (HS2_ERR_WORKSPACE otherwise; pass SIZE_MAX to check the

@@ -18,6 +18,7 @@ constexpr size_t kAlign = 256;
 constexpr int kScanTargetWorkgroups = 768;   // 3 per CU (3 waves/SIMD) on 256 CUs
 constexpr int kMfmaTargetWorkgroups = 256;   // matrix-core scan: 1 per CU (8 waves)
 constexpr int64_t kFusedSparseRows = 256;    // sparse layer: one workgroup per row from here
+constexpr int64_t kHeadPathRows = 64;        // ... and one workgroup per query head below this
 constexpr int kCandTargetWorkgroups = 4096;  // candidate stage: workgroups over all rows
 constexpr int kCandTwoStepPerRow = 2;         // the two-kernel form (many rows): workgroups per row
 constexpr double kMaxLogitsBytes = 16.0 * (1 << 30);   // logits-path workspace budget
@@ -64,7 +65,8 @@ hs2_status validate_desc(const hs2_attn_desc* d) {
   if (!(d->sm_scale > 0.0f) || !std::isfinite(d->sm_scale)) return HS2_ERR_INVALID_ARG;
   // options: known flag bits, not both sparse routes, non-negative sizes
   if ((d->flags & ~HS2_FLAGS_ALL) != 0u) return HS2_ERR_INVALID_ARG;
-  if ((d->flags & HS2_FLAG_SPARSE_FUSED) && (d->flags & HS2_FLAG_SPARSE_SPLIT)) return HS2_ERR_INVALID_ARG;
+  const uint32_t sparse_paths = d->flags & (HS2_FLAG_SPARSE_FUSED | HS2_FLAG_SPARSE_SPLIT | HS2_FLAG_SPARSE_HEAD);
+  if ((sparse_paths & (sparse_paths - 1u)) != 0u) return HS2_ERR_INVALID_ARG;   // at most one
   if (d->split_len < 0 || d->sparse_split_len < 0 || d->cand_workgroups < 0) return HS2_ERR_INVALID_ARG;
   if (d->select_mode == HS2_SELECT_TOKEN) {
     if (d->window < 0 || d->topk < 0 || (int64_t)d->window + d->topk < 1) return HS2_ERR_INVALID_ARG;
@@ -623,16 +625,24 @@ static hs2_status sparse_impl(const hs2_attn_desc* desc, const void* q, const vo
   // With a row per CU or more (query chunks), one matrix-core workgroup per (query
   // token, KV head) gathers the whole index row and writes the output: 2.1x faster on
   // the 64-token chunks.  With fewer rows (decode) its 4-5 dependent steps per wave
-  // are latency-bound, and the split VALU gather + combine is faster.
-  // HS2_FLAG_SPARSE_FUSED / HS2_FLAG_SPARSE_SPLIT force either path.
-  // More than 8 heads per KV head with few rows: the matrix-core gather over splits of
-  // one step per wave (256 entries with 8 waves, 128 with the 4-wave 32-head layout)
-  // writing partials, then the combine.
+  // are latency-bound.  Below kHeadPathRows rows one workgroup per (query token,
+  // query head) gathers its KV head's whole index row and writes the output in one
+  // launch; in between, the split VALU gather + combine.
+  // HS2_FLAG_SPARSE_FUSED / _SPLIT / _HEAD force a path.
+  // More than 8 heads per KV head on the split path: the matrix-core gather over
+  // splits of one step per wave (256 entries with 8 waves, 128 with the 4-wave 32-head
+  // layout) writing partials, then the combine.
   const int64_t rows = (int64_t)desc->batch * desc->q_len * desc->n_kv_heads;
-  const bool fused = has_flag(desc, HS2_FLAG_SPARSE_FUSED)   ? true
-                    : has_flag(desc, HS2_FLAG_SPARSE_SPLIT) ? false
-                                                            : rows >= kFusedSparseRows;
+  static_assert(kMaxHeadPathS >= 4096, "validate_desc admits index rows of up to 4,096 entries");
+  const bool forced = has_flag(desc, HS2_FLAG_SPARSE_FUSED) || has_flag(desc, HS2_FLAG_SPARSE_SPLIT) ||
+                      has_flag(desc, HS2_FLAG_SPARSE_HEAD);
+  const bool fused = has_flag(desc, HS2_FLAG_SPARSE_FUSED) || (!forced && rows >= kFusedSparseRows);
+  const bool head = has_flag(desc, HS2_FLAG_SPARSE_HEAD) || (!forced && rows < kHeadPathRows);
   const TimedLaunch tl(ev);
+  if (head) {
+    const hipError_t e = launch_sparse_head(sa, rows, out, fp8, stream, tl.ptr);
+    return e == hipSuccess ? HS2_OK : HS2_ERR_LAUNCH;
+  }
   if (fused) {
     sa.n_split = 1;
     sa.split_len = L.S;

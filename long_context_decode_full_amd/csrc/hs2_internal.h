@@ -230,6 +230,12 @@ hipError_t launch_gather_mfma(const ScanArgs& a, float* out, bool fp8, int B, hi
 // query chunks (q_len > 1) on the matrix cores, bf16 or fp8 caches (chunk_mfma_kernel)
 hipError_t launch_chunk_mfma(const ScanArgs& a, int B, bool fp8, hipStream_t st, const KernelEvents* ev = nullptr);
 hipError_t launch_scan_sparse(const ScanArgs& a, bool fp8, int B, hipStream_t st, const KernelEvents* ev = nullptr);
+// sparse layer, one 1024-thread workgroup per (query token, query head) over the
+// whole index row (a.S <= kMaxHeadPathS), normalised output straight to `out`
+// (n_sel = B * Lq * Hkv rows; no workspace)
+constexpr int kMaxHeadPathS = 4096;
+hipError_t launch_sparse_head(const ScanArgs& a, int64_t n_sel, float* out, bool fp8, hipStream_t st,
+                              const KernelEvents* ev = nullptr);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 hipError_t launch_groupsum(const SelectArgs& a, hipStream_t st);
 hipError_t launch_refine(const SelectArgs& a, int pass, hipStream_t st);

@@ -550,7 +550,169 @@ __global__ __launch_bounds__(256) void combine_small_kernel(CombineArgs a) {
   }
 }
 
+// ---- Sparse Attention layer at decode sizes (HySparse2 article, section 02 "KV
+// Reuse": each sparse layer attends with its own queries over the rows the full
+// layer's index set names; section 03: window and global rows share one softmax).
+// One workgroup of 16 waves per (query token, query head) gathers every index entry
+// of its KV head and writes the normalised output: no partials, no combine launch.
+// Its 64 row groups of 16 lanes take entries gi, gi + 64, ... (lane r holds dims
+// [8r, 8r+8) of the row and of the query, as in the scan); each group runs its own
+// online softmax and the groups merge through LDS in a fixed order, so the output is
+// bitwise reproducible.  blockIdx.x = row + rows * head (workgroups go to the XCDs
+// round-robin) keeps the workgroups of one (token, KV head) on 8 / gcd(rows, 8) XCDs,
+// one from 8 rows on, whose L2 then serves the repeated row reads.  A workgroup reads
+// S rows of 512 bytes (bf16) itself, at ~80 GB/s per workgroup, so this form suits
+// calls with few rows: the host takes it for fewer than 64 rows.
+constexpr int kHeadThreads = 1024;
+constexpr int kHeadGroups = kHeadThreads / 16;
+// rows per group in flight: 2 (1,024 threads) measured fastest; 4 or 8 rows, 512 or 256
+// threads, or a second batch in flight were 2-50% slower on the million-token decode
+constexpr int kHeadBatch = 2;
+
+template <bool kFp8>
+__global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, int64_t n_sel, float* __restrict__ out) {
+  __shared__ int32_t sidx[kMaxHeadPathS];
+  __shared__ float smz[kHeadGroups][2];
+  __shared__ __attribute__((aligned(16))) float so[kHeadGroups][kHeadDim];
+
+  const int64_t wg = blockIdx.x;
+  const int64_t sel = wg % n_sel;
+  const int h = (int)(wg / n_sel);   // head of the KV group, < G
+  const int64_t bj = sel / a.Hkv;
+  const int g = (int)(sel - bj * a.Hkv);
+  const int64_t b = bj / a.Lq;
+  const int j = (int)(bj - b * a.Lq);
+  const int tid = threadIdx.x;
+  const int r = tid & 15;
+  const int gi = tid >> 4;
+
+  int64_t ctx = a.ctx_len[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.ctx_max ? a.ctx_max : ctx);
+  int64_t n = ctx - a.Lq + j + 1;
+  n = n < 0 ? 0 : n;
+  // entries name visible positions (< n), or local-cache rows (< cap)
+  const int64_t lim = a.slot_rows ? a.cap : n;
+  const int32_t* irow = a.idx + sel * a.S;
+  for (int e = tid; e < a.S; e += kHeadThreads) {
+    const int32_t t = irow[e];
+    sidx[e] = (t >= 0 && t < lim) ? t : -1;
+  }
+  const uint4 qv = *reinterpret_cast<const uint4*>(a.q + (bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim + 8 * r);
+  const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+
+  const int64_t head_row0 = (b * a.Hkv + g) * a.cap;
+  const int rowbytes = kFp8 ? 128 : 256;
+  const uint8_t* kb = a.k + head_row0 * rowbytes;
+  const uint8_t* vb = a.v + head_row0 * rowbytes;
+  const float* ksb = kFp8 ? a.k_scale + head_row0 : nullptr;
+  const float* vsb = kFp8 ? a.v_scale + head_row0 : nullptr;
+  __syncthreads();
+
+  float m = kNegInf, z = 0.0f;
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.0f;
+  auto load_batch = [&](int e0, int32_t (&t)[kHeadBatch], RowData (&d)[kHeadBatch]) {
+#pragma unroll
+    for (int u = 0; u < kHeadBatch; ++u) {
+      const int e = e0 + u * kHeadGroups;
+      t[u] = e < a.S ? sidx[e] : -1;
+      load_row<kFp8>(kb, vb, ksb, vsb, t[u] >= 0 ? (uint32_t)t[u] : 0u, r, d[u]);
+    }
+  };
+  auto use_batch = [&](const int32_t (&t)[kHeadBatch], const RowData (&d)[kHeadBatch]) {
+#pragma unroll
+    for (int u = 0; u < kHeadBatch; ++u) {
+      if (t[u] < 0) continue;   // the 16 lanes of a group agree
+      uint32_t kw[4];
+      if (kFp8) {
+        kw[0] = fp8x2_to_bf16x2(d[u].k[0], false);
+        kw[1] = fp8x2_to_bf16x2(d[u].k[0], true);
+        kw[2] = fp8x2_to_bf16x2(d[u].k[1], false);
+        kw[3] = fp8x2_to_bf16x2(d[u].k[1], true);
+      } else {
+        kw[0] = d[u].k[0]; kw[1] = d[u].k[1]; kw[2] = d[u].k[2]; kw[3] = d[u].k[3];
+      }
+      float s = dot2_bf16(qw[0], kw[0], 0.0f);
+      s = dot2_bf16(qw[1], kw[1], s);
+      s = dot2_bf16(qw[2], kw[2], s);
+      s = dot2_bf16(qw[3], kw[3], s);
+      s = rowgroup_sum16(s);
+      float l = s * a.scale_log2;
+      if (kFp8) l *= d[u].ks;
+      if (l > m + kSlack) {   // raise the running maximum (rare)
+        const float alpha = fast_exp2(m - l);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] *= alpha;
+        z *= alpha;
+        m = l;
+      }
+      const float p = fast_exp2(l - m);
+      z += p;
+      const float pv = kFp8 ? p * d[u].vs : p;
+      float vf[8];
+      if (kFp8) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x2_t x = fp8x2_to_f32(d[u].v[c >> 1], (c & 1) != 0);
+          vf[2 * c] = x[0];
+          vf[2 * c + 1] = x[1];
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          vf[2 * c] = bf16_lo(d[u].v[c]);
+          vf[2 * c + 1] = bf16_hi(d[u].v[c]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = __builtin_fmaf(pv, vf[i], o[i]);
+    }
+  };
+  for (int e0 = gi; e0 < a.S; e0 += kHeadGroups * kHeadBatch) {
+    int32_t t[kHeadBatch];
+    RowData d[kHeadBatch];
+    load_batch(e0, t, d);
+    use_batch(t, d);
+  }
+
+  // merge the 64 groups (fixed order)
+  if (r == 0) {
+    smz[gi][0] = m;
+    smz[gi][1] = z;
+  }
+  *reinterpret_cast<float4*>(&so[gi][8 * r]) = make_float4(o[0], o[1], o[2], o[3]);
+  *reinterpret_cast<float4*>(&so[gi][8 * r + 4]) = make_float4(o[4], o[5], o[6], o[7]);
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float M = kNegInf;
+    for (int q = 0; q < kHeadGroups; ++q) M = fmaxf(M, smz[q][0]);
+    float Z = 0.0f, acc = 0.0f;
+    if (M != kNegInf) {
+      for (int q = 0; q < kHeadGroups; ++q) {
+        const float mq = smz[q][0];
+        const float f = mq == kNegInf ? 0.0f : fast_exp2(mq - M);
+        Z = __builtin_fmaf(f, smz[q][1], Z);
+        acc = __builtin_fmaf(f, so[q][tid], acc);
+      }
+    }
+    out[(bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim + tid] = Z > 0.0f ? acc / Z : 0.0f;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_sparse_head(const ScanArgs& a, int64_t n_sel, float* out, bool fp8, hipStream_t st,
+                              const KernelEvents* ev) {
+  if (a.S > kMaxHeadPathS || n_sel < 1 || a.G < 1 || a.G > kMaxHeads) return hipErrorInvalidValue;
+  const int64_t wgs = n_sel * a.G;
+  if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (fp8)
+    launch_on(ev, sparse_head_kernel<true>, dim3((unsigned)wgs), dim3(kHeadThreads), 0, st, a, n_sel, out);
+  else
+    launch_on(ev, sparse_head_kernel<false>, dim3((unsigned)wgs), dim3(kHeadThreads), 0, st, a, n_sel, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st,
                              const KernelEvents* ev) {

@@ -154,6 +154,12 @@ hipError_t launch_scan_sparse(const ScanArgs& a, bool, int B, hipStream_t, const
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_sparse_head(const ScanArgs& a, int64_t n_sel, float* out, bool, hipStream_t, const KernelEvents*) {
+  if (a.S > kMaxHeadPathS) fail("sparse head: index row beyond its LDS");
+  if (n_sel < 1 || out == nullptr) fail("sparse head: rows or output");
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_combine(const CombineArgs& a, hipStream_t) {
   const uint64_t n = (uint64_t)a.n_sel;
   in_ws(a.part, n * a.n_split * a.G * kPartStride * 4ull, "combine: partials");

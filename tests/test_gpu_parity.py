@@ -11,7 +11,7 @@ import torch
 import oracle
 from long_context_decode_full_amd import (HS2_FLAG_CHUNK_PER_TOKEN, HS2_FLAG_DETERMINISTIC,
                                           HS2_FLAG_SCAN_VALU, HS2_FLAG_SPARSE_FUSED,
-                                          HS2_FLAG_SPARSE_SPLIT)
+                                          HS2_FLAG_SPARSE_HEAD, HS2_FLAG_SPARSE_SPLIT)
 from long_context_decode_full_amd import workloads as wl
 from parity import assert_out_close, check_block_row, check_idx_row, out_row_errors
 
@@ -145,12 +145,27 @@ def test_record_path_on_valu_scan(wname):
     run_and_compare(w, f"{wname}-valu-scan", flags=HS2_FLAG_SCAN_VALU)
 
 
+@pytest.mark.parametrize("route", ["fused", "split"])
 @pytest.mark.parametrize("wname", ["tiny", "fp8_256k", "batched"])
-def test_sparse_fused_gather_on_decode(wname):
-    """HS2_FLAG_SPARSE_FUSED: decode shapes (few rows, normally the split gather) on the
-    one-workgroup-per-row matrix-core gather; same parity bar."""
+def test_sparse_routes_on_decode(wname, route):
+    """Decode shapes (few rows: by default one workgroup per query head) with every
+    sparse layer on the one-workgroup-per-row matrix-core gather (HS2_FLAG_SPARSE_FUSED)
+    or on the split VALU gather + combine (HS2_FLAG_SPARSE_SPLIT); same parity bar."""
     w = wl.standard_workloads()[wname]
-    run_and_compare(w, f"{wname}-sparse-fused", flags=HS2_FLAG_SPARSE_FUSED)
+    flags = HS2_FLAG_SPARSE_FUSED if route == "fused" else HS2_FLAG_SPARSE_SPLIT
+    run_and_compare(w, f"{wname}-sparse-{route}", flags=flags)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_sparse_head_path_on_chunks(kv):
+    """HS2_FLAG_SPARSE_HEAD on query chunks (rows past the default threshold), ragged
+    contexts shorter than the chunk included, poisoned tails."""
+    w = wl.Workload("head chunk", 3, 64, 32, 4, ctx_lens=[64, 3000, 9000], n_needles=8, kv_dtype=kv,
+                    capacity=9216, poison_tail=True, seed=3170)
+    inp = wl.make_inputs(w)
+    inp["ctx_len"][0] = 40   # its first 24 tokens see nothing
+    run_and_compare(w, f"chunk-sparse-head-{kv}", tokens=[(0, 0), (0, 23), (0, 24), (0, 63), (1, 0), (1, 63),
+                                                          (2, 31)], flags=HS2_FLAG_SPARSE_HEAD, inp=inp)
 
 
 def test_chunk_sparse_split_path():
@@ -280,13 +295,13 @@ def test_wide_group_probs(hq, hkv, lq, ctx, kv, mode):
     assert got["probs"] is not None
 
 
-@pytest.mark.parametrize("fused", ["0", "1"])
-def test_wide_group_sparse_paths(fused):
-    """MQA sparse layers on the split matrix-core gather + combine (decode default) and
-    on the one-launch gather."""
+@pytest.mark.parametrize("route", ["split", "fused", "head"])
+def test_wide_group_sparse_paths(route):
+    """MQA sparse layers on the split matrix-core gather + combine, on the one-launch
+    gather per (token, KV head) and on one workgroup per query head (decode default)."""
     w = wl.Workload("mqa sparse", 3, 1, 32, 1, ctx_lens=[800, 5000, 2049], n_needles=8, seed=2540)
-    run_and_compare(w, f"mqa-sparse-fused{fused}",
-                    flags=HS2_FLAG_SPARSE_FUSED if fused == "1" else HS2_FLAG_SPARSE_SPLIT)
+    flags = {"split": HS2_FLAG_SPARSE_SPLIT, "fused": HS2_FLAG_SPARSE_FUSED, "head": HS2_FLAG_SPARSE_HEAD}[route]
+    run_and_compare(w, f"mqa-sparse-{route}", flags=flags)
 
 
 def test_mqa_query_chunk():
@@ -449,11 +464,12 @@ def test_workspace_contents_do_not_matter(name):
 
 
 # ------------------------------------------------------------------ edges
-@pytest.fixture(params=["auto", "fused"])
+@pytest.fixture(params=["auto", "fused", "split"])
 def sparse_path(request):
-    """Runs a test with the default sparse-layer routing and again with every sparse
-    layer on the one-workgroup-per-row gather; returns the descriptor flags."""
-    return HS2_FLAG_SPARSE_FUSED if request.param == "fused" else 0
+    """Runs a test with the default sparse-layer routing (one workgroup per query head
+    at these sizes) and again with every sparse layer on the one-workgroup-per-row
+    gather and on the split gather + combine; returns the descriptor flags."""
+    return {"auto": 0, "fused": HS2_FLAG_SPARSE_FUSED, "split": HS2_FLAG_SPARSE_SPLIT}[request.param]
 
 
 @pytest.mark.parametrize("ctx", [1, 127, 128, 129, 1151, 1152, 1153, 5000])

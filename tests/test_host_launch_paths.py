@@ -61,6 +61,8 @@ DESCS = {
                    flags=hs2.HS2_FLAG_DETERMINISTIC | hs2.HS2_FLAG_SPARSE_FUSED),
     "sparse_split": dict(batch=16, q_len=64, n_q_heads=32, n_kv_heads=4, kv_capacity=20000, max_ctx_len=20000,
                          flags=hs2.HS2_FLAG_SPARSE_SPLIT),
+    "sparse_head": dict(batch=4, q_len=64, n_q_heads=32, n_kv_heads=4, kv_capacity=20000, max_ctx_len=20000,
+                        flags=hs2.HS2_FLAG_SPARSE_HEAD),
 }
 
 
@@ -123,7 +125,7 @@ def test_decode_step_launch_sequence(lib):
     st = hs2.hs2_decode_step(plan, BUF, BUF, ptrs(3, BUF), ptrs(9, BUF), ptrs(3, BUF), ptrs(3, BUF), None, None,
                              BUF, ptrs(3, BUF), ptrs(3, BUF), ptrs(9, BUF), WS, need, stream=0)
     _expect_clean(lib, st, "decode step")
-    assert lib.hs2_stub_launches() == 2 + 3 * (1 + 1 + 2 + 3 * 2)   # advance, bridge, blocks
+    assert lib.hs2_stub_launches() == 2 + 3 * (1 + 1 + 2 + 3 * 1)   # advance, bridge, blocks
 
 
 def test_bridge_and_first_generation_launch_sequences(lib):
