@@ -553,31 +553,58 @@ __global__ __launch_bounds__(256) void combine_small_kernel(CombineArgs a) {
 // ---- Sparse Attention layer at decode sizes (HySparse2 article, section 02 "KV
 // Reuse": each sparse layer attends with its own queries over the rows the full
 // layer's index set names; section 03: window and global rows share one softmax).
-// One workgroup of 16 waves per (query token, query head) gathers every index entry
-// of its KV head and writes the normalised output: no partials, no combine launch.
-// Its 64 row groups of 16 lanes take entries gi, gi + 64, ... (lane r holds dims
-// [8r, 8r+8) of the row and of the query, as in the scan); each group runs its own
-// online softmax and the groups merge through LDS in a fixed order, so the output is
-// bitwise reproducible.  blockIdx.x = row + rows * head (workgroups go to the XCDs
-// round-robin) keeps the workgroups of one (token, KV head) on 8 / gcd(rows, 8) XCDs,
-// one from 8 rows on, whose L2 then serves the repeated row reads.  A workgroup reads
-// S rows of 512 bytes (bf16) itself, at ~80 GB/s per workgroup, so this form suits
-// calls with few rows: the host takes it for fewer than 64 rows.
+// One workgroup of 16 waves per (query token, query head, 128/kDs output dims)
+// gathers every index entry of its KV head and writes its dims of the normalised
+// output: no partials, no combine launch.  The kDs workgroups of a head compute the
+// same logits and softmax (same operands, same order) and differ only in the V dims
+// they read, which cuts the bytes one workgroup pulls (K 256 B + V 256/kDs B per
+// bf16 row).  Its 64 row groups of 16 lanes take entries gi, gi + 64, ... (lane r
+// holds dims [8r, 8r+8) of the key and of the query, and 8/kDs of its workgroup's V
+// dims); each group runs its own online softmax and the groups merge through LDS in
+// a fixed order, so the output is bitwise reproducible.  blockIdx.x = row + rows *
+// (head + G * dim part) (workgroups go to the XCDs round-robin) keeps the workgroups
+// of one (token, KV head) on 8 / gcd(rows, 8) XCDs, one from 8 rows on, whose L2 then
+// serves the repeated row reads.  A workgroup reads about S * (256 + 256/kDs) bytes
+// itself, at ~80 GB/s per workgroup, so this form suits calls with few rows: the host
+// takes it for fewer than 64 rows, with the most dim parts that keep every workgroup
+// resident at once (one per CU).
 constexpr int kHeadThreads = 1024;
 constexpr int kHeadGroups = kHeadThreads / 16;
 // rows per group in flight: 2 (1,024 threads) measured fastest; 4 or 8 rows, 512 or 256
 // threads, or a second batch in flight were 2-50% slower on the million-token decode
 constexpr int kHeadBatch = 2;
 
-template <bool kFp8>
+// N bytes at p (N = 2, 4, 8, 16; p aligned to N) as little-endian words
+template <int N>
+__device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t (&w)[(N + 3) / 4]) {
+  if constexpr (N == 16) {
+    const uint4 x = *reinterpret_cast<const uint4*>(p);
+    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+  } else if constexpr (N == 8) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    w[0] = x.x; w[1] = x.y;
+  } else if constexpr (N == 4) {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else {
+    w[0] = *reinterpret_cast<const uint16_t*>(p);
+  }
+}
+
+template <bool kFp8, int kDs>
 __global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, int64_t n_sel, float* __restrict__ out) {
+  constexpr int kDw = kHeadDim / kDs;        // output dims of the workgroup
+  constexpr int kDl = kDw / 16;              // V dims of a lane
+  constexpr int kVB = kDl * (kFp8 ? 1 : 2);  // V bytes of a lane per row
+  constexpr int kVWords = (kVB + 3) / 4;
   __shared__ int32_t sidx[kMaxHeadPathS];
   __shared__ float smz[kHeadGroups][2];
-  __shared__ __attribute__((aligned(16))) float so[kHeadGroups][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float so[kHeadGroups][kDw];
 
   const int64_t wg = blockIdx.x;
   const int64_t sel = wg % n_sel;
-  const int h = (int)(wg / n_sel);   // head of the KV group, < G
+  const int64_t hd = wg / n_sel;
+  const int h = (int)(hd % a.G);   // head of the KV group
+  const int ds = (int)(hd / a.G);  // dim part, < kDs
   const int64_t bj = sel / a.Hkv;
   const int g = (int)(sel - bj * a.Hkv);
   const int64_t b = bj / a.Lq;
@@ -597,35 +624,47 @@ __global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, i
     const int32_t t = irow[e];
     sidx[e] = (t >= 0 && t < lim) ? t : -1;
   }
-  const uint4 qv = *reinterpret_cast<const uint4*>(a.q + (bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim + 8 * r);
+  const int64_t qrow = (bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim;
+  const uint4 qv = *reinterpret_cast<const uint4*>(a.q + qrow + 8 * r);
   const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
 
   const int64_t head_row0 = (b * a.Hkv + g) * a.cap;
   const int rowbytes = kFp8 ? 128 : 256;
   const uint8_t* kb = a.k + head_row0 * rowbytes;
-  const uint8_t* vb = a.v + head_row0 * rowbytes;
+  const uint8_t* vb = a.v + head_row0 * rowbytes + (kDw * ds + kDl * r) * (kFp8 ? 1 : 2);
   const float* ksb = kFp8 ? a.k_scale + head_row0 : nullptr;
   const float* vsb = kFp8 ? a.v_scale + head_row0 : nullptr;
   __syncthreads();
 
+  struct Row {
+    uint32_t k[kFp8 ? 2 : 4];
+    uint32_t v[kVWords];
+    float ks, vs;
+  };
   float m = kNegInf, z = 0.0f;
-  float o[8];
+  float o[kDl];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = 0.0f;
-  auto load_batch = [&](int e0, int32_t (&t)[kHeadBatch], RowData (&d)[kHeadBatch]) {
+  for (int i = 0; i < kDl; ++i) o[i] = 0.0f;
+  auto load_batch = [&](int e0, int32_t (&t)[kHeadBatch], Row (&d)[kHeadBatch]) {
 #pragma unroll
     for (int u = 0; u < kHeadBatch; ++u) {
       const int e = e0 + u * kHeadGroups;
       t[u] = e < a.S ? sidx[e] : -1;
-      load_row<kFp8>(kb, vb, ksb, vsb, t[u] >= 0 ? (uint32_t)t[u] : 0u, r, d[u]);
+      const uint32_t row = t[u] >= 0 ? (uint32_t)t[u] : 0u;
+      load_bytes<kFp8 ? 8 : 16>(kb + (uint64_t)row * rowbytes + (kFp8 ? 8 : 16) * r, d[u].k);
+      load_bytes<kVB>(vb + (uint64_t)row * rowbytes, d[u].v);
+      if constexpr (kFp8) {
+        d[u].ks = ksb[row];
+        d[u].vs = vsb[row];
+      }
     }
   };
-  auto use_batch = [&](const int32_t (&t)[kHeadBatch], const RowData (&d)[kHeadBatch]) {
+  auto use_batch = [&](const int32_t (&t)[kHeadBatch], const Row (&d)[kHeadBatch]) {
 #pragma unroll
     for (int u = 0; u < kHeadBatch; ++u) {
       if (t[u] < 0) continue;   // the 16 lanes of a group agree
       uint32_t kw[4];
-      if (kFp8) {
+      if constexpr (kFp8) {
         kw[0] = fp8x2_to_bf16x2(d[u].k[0], false);
         kw[1] = fp8x2_to_bf16x2(d[u].k[0], true);
         kw[2] = fp8x2_to_bf16x2(d[u].k[1], false);
@@ -639,39 +678,40 @@ __global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, i
       s = dot2_bf16(qw[3], kw[3], s);
       s = rowgroup_sum16(s);
       float l = s * a.scale_log2;
-      if (kFp8) l *= d[u].ks;
+      if constexpr (kFp8) l *= d[u].ks;
       if (l > m + kSlack) {   // raise the running maximum (rare)
         const float alpha = fast_exp2(m - l);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] *= alpha;
+        for (int i = 0; i < kDl; ++i) o[i] *= alpha;
         z *= alpha;
         m = l;
       }
       const float p = fast_exp2(l - m);
       z += p;
-      const float pv = kFp8 ? p * d[u].vs : p;
-      float vf[8];
-      if (kFp8) {
+      float pv = p;
+      if constexpr (kFp8) pv *= d[u].vs;
+      float vf[kDl];
+      if constexpr (kFp8) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < kDl / 2; ++c) {
           const f32x2_t x = fp8x2_to_f32(d[u].v[c >> 1], (c & 1) != 0);
           vf[2 * c] = x[0];
           vf[2 * c + 1] = x[1];
         }
       } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < kDl / 2; ++c) {
           vf[2 * c] = bf16_lo(d[u].v[c]);
           vf[2 * c + 1] = bf16_hi(d[u].v[c]);
         }
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = __builtin_fmaf(pv, vf[i], o[i]);
+      for (int i = 0; i < kDl; ++i) o[i] = __builtin_fmaf(pv, vf[i], o[i]);
     }
   };
   for (int e0 = gi; e0 < a.S; e0 += kHeadGroups * kHeadBatch) {
     int32_t t[kHeadBatch];
-    RowData d[kHeadBatch];
+    Row d[kHeadBatch];
     load_batch(e0, t, d);
     use_batch(t, d);
   }
@@ -681,10 +721,10 @@ __global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, i
     smz[gi][0] = m;
     smz[gi][1] = z;
   }
-  *reinterpret_cast<float4*>(&so[gi][8 * r]) = make_float4(o[0], o[1], o[2], o[3]);
-  *reinterpret_cast<float4*>(&so[gi][8 * r + 4]) = make_float4(o[4], o[5], o[6], o[7]);
+#pragma unroll
+  for (int i = 0; i < kDl; ++i) so[gi][kDl * r + i] = o[i];
   __syncthreads();
-  if (tid < kHeadDim) {
+  if (tid < kDw) {
     float M = kNegInf;
     for (int q = 0; q < kHeadGroups; ++q) M = fmaxf(M, smz[q][0]);
     float Z = 0.0f, acc = 0.0f;
@@ -696,8 +736,19 @@ __global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, i
         acc = __builtin_fmaf(f, so[q][tid], acc);
       }
     }
-    out[(bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim + tid] = Z > 0.0f ? acc / Z : 0.0f;
+    out[qrow + kDw * ds + tid] = Z > 0.0f ? acc / Z : 0.0f;
   }
+}
+
+template <bool kFp8>
+void launch_head_ds(const ScanArgs& a, int64_t n_sel, float* out, int ds, unsigned wgs, hipStream_t st,
+                    const KernelEvents* ev) {
+  if (ds == 4)
+    launch_on(ev, sparse_head_kernel<kFp8, 4>, dim3(wgs), dim3(kHeadThreads), 0, st, a, n_sel, out);
+  else if (ds == 2)
+    launch_on(ev, sparse_head_kernel<kFp8, 2>, dim3(wgs), dim3(kHeadThreads), 0, st, a, n_sel, out);
+  else
+    launch_on(ev, sparse_head_kernel<kFp8, 1>, dim3(wgs), dim3(kHeadThreads), 0, st, a, n_sel, out);
 }
 
 }  // namespace
@@ -705,12 +756,16 @@ __global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, i
 hipError_t launch_sparse_head(const ScanArgs& a, int64_t n_sel, float* out, bool fp8, hipStream_t st,
                               const KernelEvents* ev) {
   if (a.S > kMaxHeadPathS || n_sel < 1 || a.G < 1 || a.G > kMaxHeads) return hipErrorInvalidValue;
-  const int64_t wgs = n_sel * a.G;
+  // dim parts: as many as keep every workgroup resident at once (one per CU)
+  constexpr int64_t kResident = 256;
+  const int64_t heads = n_sel * a.G;
+  const int ds = heads * 4 <= kResident ? 4 : heads * 2 <= kResident ? 2 : 1;
+  const int64_t wgs = heads * ds;
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (fp8)
-    launch_on(ev, sparse_head_kernel<true>, dim3((unsigned)wgs), dim3(kHeadThreads), 0, st, a, n_sel, out);
+    launch_head_ds<true>(a, n_sel, out, ds, (unsigned)wgs, st, ev);
   else
-    launch_on(ev, sparse_head_kernel<false>, dim3((unsigned)wgs), dim3(kHeadThreads), 0, st, a, n_sel, out);
+    launch_head_ds<false>(a, n_sel, out, ds, (unsigned)wgs, st, ev);
   return hipGetLastError();
 }
 
