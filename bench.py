@@ -434,7 +434,7 @@ def bench_decode_loop(args):
         "scan_us": scan_s * 1e6,
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload),
             "kernel": "scan_mfma_kernel (each block's full-attention scan; eager pass, library events)",
             "algorithmic_bytes_per_launch": scan_bytes,
         },
@@ -449,20 +449,29 @@ def bench_decode_loop(args):
         # the oracle for one block of one sequence, and the bridge oracle for its token
         one = dict(inp, q_full=dec["q_full"][0][0], q_sparse=dec["q_sparse"][0][:w.n_sparse_layers])
         one["ctx_len"] = inp["ctx_len"].copy()
-        c0 = time.perf_counter()
-        oracle.hybrid_block_token(one, 0, 0)
-        t_block = time.perf_counter() - c0
+
+        def repeated(fn, min_s=8.0, min_reps=3, max_reps=1000):
+            """Seconds per call of fn, repeated to about min_s of CPU work."""
+            reps, total = 0, 0.0
+            while reps < max_reps and (total < min_s or reps < min_reps):
+                c0 = time.perf_counter()
+                fn()
+                total += time.perf_counter() - c0
+                reps += 1
+            return total / reps, reps
+
+        t_block, r_block = repeated(lambda: oracle.hybrid_block_token(one, 0, 0))
         shape = (n_blocks, 1, Hkv, 1, D)
         caches = dict(k=np.zeros(shape, np.uint16), v=np.zeros(shape, np.uint16))
-        c0 = time.perf_counter()
-        oracle.kv_bridge(dec["x"][0][:1], dec["w_bits"], np.zeros(1, np.int32), np.zeros(1, np.int32), caches)
-        t_bridge = time.perf_counter() - c0
+        t_bridge, r_bridge = repeated(lambda: oracle.kv_bridge(dec["x"][0][:1], dec["w_bits"], np.zeros(1, np.int32),
+                                                               np.zeros(1, np.int32), caches), min_s=2.0)
         per_seq = t_bridge + n_blocks * t_block
         result["cpu_baseline"] = {
             "value": 1.0 / per_seq, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "host": host_description(),
-            "sample": f"float64 oracle: one Hybrid Block for sequence 0 ({t_block:.2f}s) x {n_blocks} "
-                      f"blocks + the bridge for its token ({t_bridge:.2f}s), per sequence",
+            "sample": f"float64 oracle: one Hybrid Block for sequence 0 ({t_block:.3f}s, mean of {r_block} "
+                      f"repetitions) x {n_blocks} blocks + the bridge for its token ({t_bridge:.4f}s, mean of "
+                      f"{r_bridge}), per sequence",
         }
     print(json.dumps(result), flush=True)
 

@@ -560,8 +560,9 @@ __global__ __launch_bounds__(256) void combine_small_kernel(CombineArgs a) {
 // they read, which cuts the bytes one workgroup pulls (K 256 B + V 256/kDs B per
 // bf16 row).  Its 64 row groups of 16 lanes take entries gi, gi + 64, ... (lane r
 // holds dims [8r, 8r+8) of the key and of the query, and 8/kDs of its workgroup's V
-// dims); each group runs its own online softmax and the groups merge through LDS in
-// a fixed order, so the output is bitwise reproducible.  blockIdx.x = row + rows *
+// dims); each group runs its own online softmax and the groups merge in a fixed order
+// (the 4 of a wave by lane exchanges, then the waves through LDS), so the output is
+// bitwise reproducible.  blockIdx.x = row + rows *
 // (head + G * dim part) (workgroups go to the XCDs round-robin) keeps the workgroups
 // of one (token, KV head) on 8 / gcd(rows, 8) XCDs, one from 8 rows on, whose L2 then
 // serves the repeated row reads.  A workgroup reads about S * (256 + 256/kDs) bytes
@@ -570,6 +571,7 @@ __global__ __launch_bounds__(256) void combine_small_kernel(CombineArgs a) {
 // resident at once (one per CU).
 constexpr int kHeadThreads = 1024;
 constexpr int kHeadGroups = kHeadThreads / 16;
+constexpr int kHeadWaves = kHeadThreads / 64;
 // rows per group in flight: 2 (1,024 threads) measured fastest; 4 or 8 rows, 512 or 256
 // threads, or a second batch in flight were 2-50% slower on the million-token decode
 constexpr int kHeadBatch = 2;
@@ -597,8 +599,8 @@ __global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, i
   constexpr int kVB = kDl * (kFp8 ? 1 : 2);  // V bytes of a lane per row
   constexpr int kVWords = (kVB + 3) / 4;
   __shared__ int32_t sidx[kMaxHeadPathS];
-  __shared__ float smz[kHeadGroups][2];
-  __shared__ __attribute__((aligned(16))) float so[kHeadGroups][kDw];
+  __shared__ float smz[kHeadWaves][2];
+  __shared__ __attribute__((aligned(16))) float so[kHeadWaves][kDw];
 
   const int64_t wg = blockIdx.x;
   const int64_t sel = wg % n_sel;
@@ -716,24 +718,41 @@ __global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, i
     use_batch(t, d);
   }
 
-  // merge the 64 groups (fixed order)
-  if (r == 0) {
-    smz[gi][0] = m;
-    smz[gi][1] = z;
-  }
+  // merge (fixed order): the 4 groups of a wave (lanes r, r+16, r+32, r+48 hold the
+  // same dims) by lane exchanges, then the 16 waves through LDS
+  float M = fmaxf(m, shfl_xor(m, 16));
+  M = fmaxf(M, shfl_xor(M, 32));
+  const float f = m == kNegInf ? 0.0f : fast_exp2(m - M);
+  float zz = z * f;
+  zz += shfl_xor(zz, 16);
+  zz += shfl_xor(zz, 32);
 #pragma unroll
-  for (int i = 0; i < kDl; ++i) so[gi][kDl * r + i] = o[i];
+  for (int i = 0; i < kDl; ++i) {
+    float x = o[i] * f;
+    x += shfl_xor(x, 16);
+    x += shfl_xor(x, 32);
+    o[i] = x;
+  }
+  const int wave = tid >> 6;
+  if ((tid & 63) < 16) {
+    if (r == 0) {
+      smz[wave][0] = M;
+      smz[wave][1] = zz;
+    }
+#pragma unroll
+    for (int i = 0; i < kDl; ++i) so[wave][kDl * r + i] = o[i];
+  }
   __syncthreads();
   if (tid < kDw) {
-    float M = kNegInf;
-    for (int q = 0; q < kHeadGroups; ++q) M = fmaxf(M, smz[q][0]);
+    float Mw = kNegInf;
+    for (int q = 0; q < kHeadWaves; ++q) Mw = fmaxf(Mw, smz[q][0]);
     float Z = 0.0f, acc = 0.0f;
-    if (M != kNegInf) {
-      for (int q = 0; q < kHeadGroups; ++q) {
+    if (Mw != kNegInf) {
+      for (int q = 0; q < kHeadWaves; ++q) {
         const float mq = smz[q][0];
-        const float f = mq == kNegInf ? 0.0f : fast_exp2(mq - M);
-        Z = __builtin_fmaf(f, smz[q][1], Z);
-        acc = __builtin_fmaf(f, so[q][tid], acc);
+        const float fq = mq == kNegInf ? 0.0f : fast_exp2(mq - Mw);
+        Z = __builtin_fmaf(fq, smz[q][1], Z);
+        acc = __builtin_fmaf(fq, so[q][tid], acc);
       }
     }
     out[qrow + kDw * ds + tid] = Z > 0.0f ? acc / Z : 0.0f;
