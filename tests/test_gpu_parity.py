@@ -536,8 +536,10 @@ def test_smaller_groups(hq, hkv):
     run_and_compare(w, f"G{hq // hkv}")
 
 
-@pytest.mark.parametrize("window,topk", [(0, 64), (16, 8), (512, 2048)])
+@pytest.mark.parametrize("window,topk", [(0, 64), (16, 8), (512, 2048), (1024, 3072)])
 def test_other_window_and_topk(window, topk):
+    """Other index-row lengths S = window + topk, up to the 4,096 the boundary admits
+    (the decode sparse layer stages the whole row in LDS)."""
     w = wl.Workload("window/topk", 1, 1, 16, 2, ctx_lens=[6000], n_needles=8, seed=3600 + topk)
     run_and_compare(w, f"w{window}-k{topk}", window=window, topk=topk)
 
