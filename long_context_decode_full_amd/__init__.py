@@ -22,7 +22,8 @@ __all__ = [
     "hs2_validate", "hs2_workspace_size", "hs2_full_attn_select", "hs2_sparse_attn",
     "hs2_status_string", "hs2_full_attn_select_timed", "hs2_sparse_attn_timed", "Hs2KernelEvents",
     "hs2_build_id", "HS2_FLAG_DETERMINISTIC", "HS2_FLAG_FORCE_LOGITS", "HS2_FLAG_SCAN_VALU",
-    "HS2_FLAG_CHUNK_PER_TOKEN", "HS2_FLAG_SPARSE_FUSED", "HS2_FLAG_SPARSE_SPLIT", "HS2_FLAG_SPARSE_HEAD", "HS2_FLAGS_ALL",
+    "HS2_FLAG_CHUNK_PER_TOKEN", "HS2_FLAG_SPARSE_FUSED", "HS2_FLAG_SPARSE_SPLIT", "HS2_FLAG_SPARSE_HEAD", "HS2_FLAG_EXACT_PV",
+    "HS2_FLAGS_ALL",
     "library_path", "load_library", "Hs2BridgeDesc", "make_bridge_desc",
     "hs2_kv_bridge", "Hs2DecodePlan", "make_decode_plan", "hs2_decode_workspace_size",
     "hs2_decode_step", "hs2_sparse_attn_swa_workspace_size", "hs2_sparse_attn_swa",
@@ -50,7 +51,8 @@ HS2_FLAG_CHUNK_PER_TOKEN = 1 << 3
 HS2_FLAG_SPARSE_FUSED = 1 << 4
 HS2_FLAG_SPARSE_SPLIT = 1 << 5
 HS2_FLAG_SPARSE_HEAD = 1 << 6
-HS2_FLAGS_ALL = 0x7F
+HS2_FLAG_EXACT_PV = 1 << 7
+HS2_FLAGS_ALL = 0xFF
 SIZE_MAX = (1 << 64) - 1
 
 EXPORTED_SYMBOLS = ("hs2_validate", "hs2_workspace_size", "hs2_full_attn_select",

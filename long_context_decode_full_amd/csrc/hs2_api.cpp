@@ -353,6 +353,7 @@ static ScanArgs scan_args(const hs2_attn_desc* d, const Layout& L, const void* q
   a.S = L.S;
   a.scale_log2 = d->sm_scale * 1.44269504088896340736f;
   a.fixed_steps = has_flag(d, HS2_FLAG_DETERMINISTIC) ? 1 : 0;
+  a.exact_pv = has_flag(d, HS2_FLAG_EXACT_PV) ? 1 : 0;
   return a;
 }
 

@@ -25,8 +25,14 @@
 // row (i) and the probabilities are already in the B-operand layout of the second
 // product: O^T = V^T P^T with A = V^T read transposed from the V tile
 // (ds_read_b64_tr_b16, rows 4grp..4grp+3 of two position tiles per lane) and B = the
-// lane's own 8 probabilities of a 32-position block, as a bf16 high part and a bf16
-// residual (P never goes through LDS).
+// lane's own 8 probabilities of a 32-position block (P never goes through LDS).  With a
+// bf16 cache the V tile is staged as fp16 (exact: a bf16 value below 2^16 in magnitude
+// has 8 significant bits) and P is rounded to fp16, one MFMA per product (error <=
+// 2^-12 relative per term); a split whose V has a tile outside that range (some |v| >=
+// 2^16, or every |v| < 2^-6) starts again with P as a bf16 high part and a bf16
+// residual (two MFMAs, error ~2^-16), the form fp8 caches and HS2_FLAG_EXACT_PV always
+// take.  A block's P V is interleaved with the vector work of the next block (the
+// matrix core and the VALU overlap only in part, so this mostly keeps both busy).
 //   softmax per query row: the lane's 16 values per iteration, the running maximum
 //     raised lazily by 8 (log2 units) with a max over the 4 row groups.
 //   record per (token, position): log2 of the sum over the token's heads of 2^logit,
@@ -37,6 +43,8 @@
 //     a wave-uniform branch.
 #include "hs2_rowops.h"
 
+#include <type_traits>
+
 namespace hs2 {
 namespace {
 
@@ -44,6 +52,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2v_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kCThreads = 512;                 // 8 waves
@@ -74,11 +84,26 @@ constexpr int chunk_lds_bytes() {
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// the same product on fp16 operands (the bits of a and b are fp16 values)
+__device__ __forceinline__ f32x4_t mfma16h(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                               0, 0);
+}
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   const f32x2v_t x = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
 }
+// two floats to fp16 (round to nearest even), packed
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  const f32x2v_t x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2_t));
+}
+// V tile range for the fp16 form: every |v| below 2^16 (bf16 values there are exact in
+// fp16) and some |v| at least 2^-6 (fp16 subnormals then cost at most 2^-25 absolute,
+// far below the 2^-12 relative rounding of P at that magnitude)
+constexpr float kV16Max = 65536.0f;
+constexpr float kV16Min = 0x1p-6f;
 
 // Reductions over the lanes of one token's heads inside a 16-lane row: 4 lanes (each
 // quad separately), 8 (lanes 0-7 and 8-15 separately) or all 16.
@@ -190,6 +215,10 @@ template <int kGp, bool kBlockMode, bool kFp8>
 __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   constexpr int kTPW = tokens_per_wg<kGp>();
   __shared__ __attribute__((aligned(16))) uint8_t lds[chunk_lds_bytes<kGp, kBlockMode, kFp8>()];
+  // bf16 caches: V staged as fp16 unless the caller asks for the two-part form; per stage
+  // and wave, bit 0: some |v| >= kV16Max (or not finite), bit 1: some |v| >= kV16Min
+  constexpr bool kV16 = !kFp8;
+  __shared__ uint32_t vflags[2][kCThreads / 64];
   uint32_t* shist = reinterpret_cast<uint32_t*>(lds + 2 * kStage + (kFp8 ? kScaleBytes : 0));
   // per-position scales of stage st: K (kv = 0) or V (kv = 1)
   auto stage_scales = [&](int st, int kv) { return reinterpret_cast<float*>(lds + 2 * kStage) + (2 * st + kv) * kCPos; };
@@ -266,13 +295,6 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   f32x4_t o[2][8];     // O^T: dims 16 bb + 4 grp + v of the lane's query row
   float m[2], z[2];    // running maximum (log2 units, equal in the 4 row groups), this lane's share of Z
   float U[2], c[2];    // record scale: U = the token's largest running maximum, c = 2^(m - U) (0: no head)
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[qt][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m[qt] = kMFloor;   // finite, so exp2(l - m) needs no -inf test
-    z[qt] = 0.0f;
-  }
   auto record_scale = [&]() {
     float mv[2];
 #pragma unroll
@@ -281,7 +303,6 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) c[qt] = valid[qt] ? fast_exp2(m[qt] - U[qt]) : 0.0f;
   };
-  if constexpr (want_rec) record_scale();
 
   const int nit = p_end > p_begin ? (int)((p_end - p_begin + kCPos - 1) / kCPos) : 0;
   const int32_t last = (int32_t)(p_end - 1);
@@ -289,6 +310,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   // (tid & 15); fp8 row (tid >> 3), 16 codes at (tid & 7), and with tid < 64 the K and V
   // scales of position tid.  (Named registers, not arrays: small arrays live across the
   // loop got placed in LDS / scratch by the compiler.)
+  const bool f16v = kV16 && a.exact_pv == 0;   // workgroup-uniform
   const int lrow = kFp8 ? (tid >> 3) : (tid >> 4);
   const int lcol = kFp8 ? (tid & 7) * 16 : (tid & 15) * 16;
   uint4 kr0, kr1, vr0, vr1;
@@ -309,7 +331,9 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
       vr1 = *reinterpret_cast<const uint4*>(vb + (uint64_t)row1 * 256 + lcol);
     }
   };
-  auto store_tiles = [&](int stg) {
+  // kHt true: bf16 V rows go to LDS as fp16, with the stage's range flags
+  auto store_tiles = [&](int stg, auto kHt) {
+    constexpr bool kH = decltype(kHt)::value;
     uint8_t* st = lds + stg * kStage;
     if constexpr (kFp8) {
       // 16 codes -> 16 bf16 (exact), bytes 2 lcol .. 2 lcol + 31 of the staged row
@@ -333,274 +357,409 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
     } else {
       *reinterpret_cast<uint4*>(st + lrow * kKRow + lcol) = kr0;
       *reinterpret_cast<uint4*>(st + (lrow + 32) * kKRow + lcol) = kr1;
-      *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + lcol) = vr0;
-      *reinterpret_cast<uint4*>(st + kKTile + (lrow + 32) * kVRow + lcol) = vr1;
-    }
-  };
-  if (nit > 0) {
-    load_tiles((int32_t)p_begin);
-    store_tiles(0);
-    load_tiles((int32_t)p_begin + kCPos);
-  }
-  __syncthreads();   // stage 0 and the cleared histograms are ready
-  const float sl2 = a.scale_log2;
-  const int32_t first_pj = (int32_t)(ctx - a.Lq + tok0);   // the workgroup's first token sees least
-
-  // K fragments of the first position tile, read one iteration ahead (the next stage
-  // is visible once the barrier after its stores has passed)
-  auto read_kf = [&](const uint8_t* ks, int pt, bf16x8_t (&kf)[4]) {
+      if constexpr (kH) {
+        // 8 bf16 -> 8 fp16 per store (exact inside the range the flags check)
+        float vmax = 0.0f;
+        auto widen = [&](uint4 w) {
+          const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+          uint32_t h[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(ks + (pt * 16 + w16) * kKRow + 64 * s + 16 * grp));
-  };
-  bf16x8_t kpre[4];
-  if (nit > 0) read_kf(lds, 0, kpre);
-  for (int it = 0; it < nit; ++it) {
-    const int32_t P0 = (int32_t)p_begin + it * kCPos;
-    const uint8_t* ks = lds + (it & 1) * kStage;
-    const uint8_t* vs = ks + kKTile;
-    // the next iteration's tiles into the other stage (its last readers finished the
-    // previous iteration before the barrier that ended it), then the loads after them
-    store_tiles((it + 1) & 1);
-    load_tiles(P0 + 2 * kCPos);
-    __syncthreads();   // the next stage is complete
-
-    // ---- S^T = K Q^T for 4 position tiles x 2 query tiles
-    f32x4_t sacc[4][2];
-    // the MFMA groups run at raised wave priority: when the two waves of a SIMD are
-    // in different phases, the matrix core starts as soon as it is free and the
-    // other wave's vector work fills the issue slots in between
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      bf16x8_t kf[4];
-      if (pt == 0) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kf[s] = kpre[s];
+          for (int i = 0; i < 4; ++i) {
+            const float lo = __uint_as_float(x[i] << 16), hi = __uint_as_float(x[i] & 0xFFFF0000u);
+            vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
+            h[i] = pack_f16(lo, hi);
+          }
+          return make_uint4(h[0], h[1], h[2], h[3]);
+        };
+        *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + lcol) = widen(vr0);
+        *reinterpret_cast<uint4*>(st + kKTile + (lrow + 32) * kVRow + lcol) = widen(vr1);
+        // fmaxf drops NaN: a NaN in V stays NaN in fp16 as in bf16, so both forms agree
+        const bool over = !(vmax < kV16Max);
+        const bool some = vmax >= kV16Min;
+        const uint64_t ov = __builtin_amdgcn_ballot_w64(over);
+        const uint64_t sm = __builtin_amdgcn_ballot_w64(some);
+        if (lane == 0) vflags[stg][wave] = (ov != 0ull ? 1u : 0u) | (sm != 0ull ? 2u : 0u);
       } else {
-        read_kf(ks, pt, kf);
-      }
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) d = mfma16(kf[s], qf[qt][s], d);
-        sacc[pt][qt] = d;
+        *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + lcol) = vr0;
+        *reinterpret_cast<uint4*>(st + kKTile + (lrow + 32) * kVRow + lcol) = vr1;
       }
     }
-    __builtin_amdgcn_s_setprio(0);
-    // raw scores; the log2-domain logit is scale_log2 * s (scale_log2 > 0), formed
-    // inside the exp2 as fma(s, scale_log2, -m).  The causal mask only where some
-    // position lies beyond the first token's last visible one (wave-uniform branch).
-    // (fp8: the score of position i is scale_i * q.k_i, k_i the stored codes)
-    float l[2][4][4];
+  };
+  // One pass over the split: P V with fp16 V and P (kHt true) or with the two-part
+  // bf16 split of P.  The fp16 pass returns false, leaving at the first stage whose V
+  // lies outside the fp16 range; the split then runs again in the two-part form (the
+  // records it wrote are written again with the same values, the histograms restart).
+  auto run_split = [&](auto kHt) -> bool {
+    constexpr bool kH = decltype(kHt)::value;
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      float4 ksc = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-      if constexpr (kFp8) ksc = *reinterpret_cast<const float4*>(stage_scales(it & 1, 0) + pt * 16 + 4 * grp);
-      const float kv4[4] = {ksc.x, ksc.y, ksc.z, ksc.w};
+    for (int qt = 0; qt < 2; ++qt) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) l[qt][pt][v] = kFp8 ? sacc[pt][qt][v] * kv4[v] : sacc[pt][qt][v];
+      for (int d = 0; d < 8; ++d) o[qt][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m[qt] = kMFloor;   // finite, so exp2(l - m) needs no -inf test
+      z[qt] = 0.0f;
     }
-    if (P0 + kCPos - 1 > first_pj) {
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            l[qt][pt][v] = P0 + pt * 16 + 4 * grp + v <= pj[qt] ? l[qt][pt][v] : kNegInf;
+    if constexpr (want_rec) record_scale();
+    if (nit > 0) {
+      load_tiles((int32_t)p_begin);
+      store_tiles(0, kHt);
+      load_tiles((int32_t)p_begin + kCPos);
     }
+    __syncthreads();   // stage 0 and the cleared histograms are ready
+    const float sl2 = a.scale_log2;
+    const int32_t first_pj = (int32_t)(ctx - a.Lq + tok0);   // the workgroup's first token sees least
 
-    // ---- online softmax per query row: a lane test and one ballot per iteration; the
-    // exact row maximum (over the 4 row groups) only on the rare raise
-    {
-      float x[2];
-      bool up_any = false;
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) mx = fmaxf(mx, l[qt][pt][v]);
-        x[qt] = mx * sl2;
-        up_any |= x[qt] > m[qt] + kCSlack;
+    // K fragments of the first position tile, read one iteration ahead (the next stage
+    // is visible once the barrier after its stores has passed)
+    auto read_kf = [&](const uint8_t* ks, int pt, bf16x8_t (&kf)[4]) {
+  #pragma unroll
+      for (int s = 0; s < 4; ++s)
+        kf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(ks + (pt * 16 + w16) * kKRow + 64 * s + 16 * grp));
+    };
+    bf16x8_t kpre[4];
+    if (nit > 0) read_kf(lds, 0, kpre);
+    for (int it = 0; it < nit; ++it) {
+      const int32_t P0 = (int32_t)p_begin + it * kCPos;
+      const uint8_t* ks = lds + (it & 1) * kStage;
+      const uint8_t* vs = ks + kKTile;
+      // the next iteration's tiles into the other stage (its last readers finished the
+      // previous iteration before the barrier that ended it), then the loads after them
+      store_tiles((it + 1) & 1, kHt);
+      load_tiles(P0 + 2 * kCPos);
+      __syncthreads();   // the next stage is complete
+      if constexpr (kH) {
+        // this stage's V outside the fp16 range: the split is given up (every wave reads
+        // the same flags here, right after the barrier, so all leave together)
+        uint32_t f = 0u;
+  #pragma unroll
+        for (int w = 0; w < kCThreads / 64; ++w) f |= vflags[it & 1][w];
+        if ((f & 1u) != 0u || (f & 2u) == 0u) return false;
       }
-      if (wave_any(up_any)) {
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          const float mx = across_groups<true>(x[qt]);
-          const bool up = mx > m[qt] + kCSlack;
-          const float mn = up ? mx : m[qt];
-          const float alpha = up ? fast_exp2(m[qt] - mn) : 1.0f;
-#pragma unroll
-          for (int d = 0; d < 8; ++d) o[qt][d] *= alpha;
-          z[qt] *= alpha;
-          m[qt] = mn;
+
+      // ---- S^T = K Q^T for 4 position tiles x 2 query tiles
+      f32x4_t sacc[4][2];
+      // the MFMA groups run at raised wave priority: when the two waves of a SIMD are
+      // in different phases, the matrix core starts as soon as it is free and the
+      // other wave's vector work fills the issue slots in between
+      __builtin_amdgcn_s_setprio(1);
+  #pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        bf16x8_t kf[4];
+        if (pt == 0) {
+  #pragma unroll
+          for (int s = 0; s < 4; ++s) kf[s] = kpre[s];
+        } else {
+          read_kf(ks, pt, kf);
         }
-        if constexpr (want_rec) record_scale();
+  #pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int s = 0; s < 4; ++s) d = mfma16(kf[s], qf[qt][s], d);
+          sacc[pt][qt] = d;
+        }
       }
-    }
+      __builtin_amdgcn_s_setprio(0);
+      // raw scores; the log2-domain logit is scale_log2 * s (scale_log2 > 0), formed
+      // inside the exp2 as fma(s, scale_log2, -m).  The causal mask only where some
+      // position lies beyond the first token's last visible one (wave-uniform branch).
+      // (fp8: the score of position i is scale_i * q.k_i, k_i the stored codes)
+      float l[2][4][4];
+  #pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        float4 ksc = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        if constexpr (kFp8) ksc = *reinterpret_cast<const float4*>(stage_scales(it & 1, 0) + pt * 16 + 4 * grp);
+        const float kv4[4] = {ksc.x, ksc.y, ksc.z, ksc.w};
+  #pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) l[qt][pt][v] = kFp8 ? sacc[pt][qt][v] * kv4[v] : sacc[pt][qt][v];
+      }
+      if (P0 + kCPos - 1 > first_pj) {
+  #pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+  #pragma unroll
+          for (int pt = 0; pt < 4; ++pt)
+  #pragma unroll
+            for (int v = 0; v < 4; ++v)
+              l[qt][pt][v] = P0 + pt * 16 + 4 * grp + v <= pj[qt] ? l[qt][pt][v] : kNegInf;
+      }
 
-    // ---- probabilities, records / block sums, P^T V^T per 32-position block
-    float bsum[2] = {0.f, 0.f};
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      // A operands of the block's P V: V^T of dim block d, rows 4grp..4grp+3 of the
-      // block's two tiles; the first kVPre of them are read here, so that their LDS
-      // latency passes under the probabilities and records
-      const uint8_t* tr0 = vs + (32 * kb2 + 4 * grp + (w16 >> 2)) * kVRow + 8 * (w16 & 3);
-      const uint8_t* tr1 = tr0 + 16 * kVRow;
-      auto read_vt = [&](int d) {
-        const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tr0 + 32 * d));
-        const s16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tr1 + 32 * d));
+      // ---- online softmax per query row: a lane test and one ballot per iteration; the
+      // exact row maximum (over the 4 row groups) only on the rare raise
+      {
+        float x[2];
+        bool up_any = false;
+  #pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          float mx = kNegInf;
+  #pragma unroll
+          for (int pt = 0; pt < 4; ++pt)
+  #pragma unroll
+            for (int v = 0; v < 4; ++v) mx = fmaxf(mx, l[qt][pt][v]);
+          x[qt] = mx * sl2;
+          up_any |= x[qt] > m[qt] + kCSlack;
+        }
+        if (wave_any(up_any)) {
+  #pragma unroll
+          for (int qt = 0; qt < 2; ++qt) {
+            const float mx = across_groups<true>(x[qt]);
+            const bool up = mx > m[qt] + kCSlack;
+            const float mn = up ? mx : m[qt];
+            const float alpha = up ? fast_exp2(m[qt] - mn) : 1.0f;
+  #pragma unroll
+            for (int d = 0; d < 8; ++d) o[qt][d] *= alpha;
+            z[qt] *= alpha;
+            m[qt] = mn;
+          }
+          if constexpr (want_rec) record_scale();
+        }
+      }
+
+      // ---- probabilities, records / block sums, P^T V^T per 32-position block.
+      // The work of the two blocks is ordered so that each block's P V runs on the matrix
+      // cores while this wave's vector work continues: block 0's probabilities, operands
+      // and records first; then block 0's P V interleaved with block 1's probabilities,
+      // operands and record sums; then block 1's P V interleaved with its record
+      // reduction; block 1's records last.  (Each accumulator still takes the high part
+      // and then the residual of its block, so the sums are those of a plain loop.)
+      float bsum[2] = {0.f, 0.f};
+      // A operands of a block's P V: V^T of dim block d, rows 4grp..4grp+3 of the block's
+      // two tiles
+      auto read_vt = [&](int kb2, int d) {
+        const uint8_t* tr0 = vs + (32 * kb2 + 4 * grp + (w16 >> 2)) * kVRow + 8 * (w16 & 3) + 32 * d;
+        const uint8_t* tr1 = tr0 + 16 * kVRow;
+        const s16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)tr0);
+        const s16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)tr1);
         const uint2 w0 = __builtin_bit_cast(uint2, x0);
         const uint2 w1 = __builtin_bit_cast(uint2, x1);
         return as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
       };
-      bf16x8_t avp[kVPre];
-#pragma unroll
-      for (int d = 0; d < kVPre; ++d) avp[d] = read_vt(d);
-      float p[2][2][4];   // [qt][tile of the block][v]
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float x = fast_exp2(__builtin_fmaf(l[qt][2 * kb2 + tt][v], sl2, -m[qt]));   // -inf -> 0
-            p[qt][tt][v] = x;
-            z[qt] += x;
-            if constexpr (kBlockMode) bsum[qt] += x;
+      // p[qt][tile of the block][v]
+      auto probabilities = [&](int kb2, float (&p)[2][2][4]) {
+  #pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+  #pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+  #pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float x = fast_exp2(__builtin_fmaf(l[qt][2 * kb2 + tt][v], sl2, -m[qt]));   // -inf -> 0
+              p[qt][tt][v] = x;
+              z[qt] += x;
+              if constexpr (kBlockMode) bsum[qt] += x;
+            }
+      };
+      // B operands: P^T of the block, k slot 8 grp + u <-> tile u / 4, position 4 grp + u % 4
+      // (fp8: times the V scale of the position): fp16 (kH), or a bf16 high part and a bf16
+      // residual
+      auto operands = [&](auto kHt, int kb2, const float (&p)[2][2][4], bf16x8_t (&ph)[2], bf16x8_t (&pl)[2]) {
+        constexpr bool kH = decltype(kHt)::value;
+        float vsc[2][4] = {{1.0f, 1.0f, 1.0f, 1.0f}, {1.0f, 1.0f, 1.0f, 1.0f}};
+        if constexpr (kFp8) {
+  #pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const float4 s4 = *reinterpret_cast<const float4*>(stage_scales(it & 1, 1) + (2 * kb2 + tt) * 16 + 4 * grp);
+            vsc[tt][0] = s4.x;
+            vsc[tt][1] = s4.y;
+            vsc[tt][2] = s4.z;
+            vsc[tt][3] = s4.w;
           }
-      if constexpr (want_rec) {
-        // records of the block's 32 positions: per (token, position) the sum over the
-        // token's heads of c p (both tiles in-lane, then the head lanes), then the exact
-        // form where a sum underflowed; a token's rows share tokl, pj and w0j
-        constexpr int kOut = kRecOut<kGp>;
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = p[0][i >> 2][i & 3] * c[0] + p[1][i >> 2][i & 3] * c[1];
-        float sum[kOut];
-        reduce_scatter<kGp>(x, w16, sum);
-        const int tl = tokl[0];
+        }
+  #pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          uint32_t hw[4], lw[4];
+  #pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float x0 = p[qt][u >> 1][2 * (u & 1)] * (kFp8 ? vsc[u >> 1][2 * (u & 1)] : 1.0f);
+            const float x1 = p[qt][u >> 1][2 * (u & 1) + 1] * (kFp8 ? vsc[u >> 1][2 * (u & 1) + 1] : 1.0f);
+            if constexpr (kH) {
+              hw[u] = pack_f16(x0, x1);
+              lw[u] = 0u;
+            } else {
+              hw[u] = pack_bf16(x0, x1);
+              lw[u] = pack_bf16(x0 - __uint_as_float(hw[u] << 16), x1 - __uint_as_float(hw[u] & 0xFFFF0000u));
+            }
+          }
+          ph[qt] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+          pl[qt] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        }
+      };
+      auto pv = [&](auto kHt, int kb2, const bf16x8_t (&avp)[kVPre], const bf16x8_t (&ph)[2], const bf16x8_t (&pl)[2]) {
+        constexpr bool kH = decltype(kHt)::value;
+  #pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const bf16x8_t av = d < kVPre ? avp[d < kVPre ? d : 0] : read_vt(kb2, d);
+  #pragma unroll
+          for (int qt = 0; qt < 2; ++qt) {
+            if constexpr (kH) {
+              o[qt][d] = mfma16h(av, ph[qt], o[qt][d]);
+            } else {
+              o[qt][d] = mfma16(av, ph[qt], o[qt][d]);
+              o[qt][d] = mfma16(av, pl[qt], o[qt][d]);
+            }
+          }
+        }
+      };
+      // Records of a block's 32 positions: per (token, position) the sum over the token's
+      // heads of c p (both tiles in-lane: rec_sums; then the head lanes: rec_reduce), then
+      // the exact form where a sum underflowed (rec_write); a token's rows share tokl, pj
+      // and w0j.
+      constexpr int kOut = kRecOut<kGp>;
+      struct RecState {
         int32_t pos[kOut];
         bool live[kOut], tiny[kOut];
         float e[kOut];
-        bool any_tiny = false;
-#pragma unroll
+        bool any_tiny;
+      };
+      auto rec_sums = [&](const float (&p)[2][2][4], float (&x)[8]) {
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = p[0][i >> 2][i & 3] * c[0] + p[1][i >> 2][i & 3] * c[1];
+      };
+      auto rec_reduce = [&](int kb2, const float (&x)[8], RecState& r) {
+        float sum[kOut];
+        reduce_scatter<kGp>(x, w16, sum);
+        r.any_tiny = false;
+  #pragma unroll
         for (int j = 0; j < kOut; ++j) {
           const int idx = rec_index<kGp>(w16, j);
-          pos[j] = P0 + (2 * kb2 + (idx >> 2)) * 16 + 4 * grp + (idx & 3);
-          live[j] = rec_writer<kGp>(w16) && pos[j] <= pj[0] && tl < ntok;
-          tiny[j] = live[j] && !(sum[j] >= 0x1p-100f);
-          any_tiny |= tiny[j];
-          e[j] = U[0] + __builtin_amdgcn_logf(sum[j]);
+          r.pos[j] = P0 + (2 * kb2 + (idx >> 2)) * 16 + 4 * grp + (idx & 3);
+          r.live[j] = rec_writer<kGp>(w16) && r.pos[j] <= pj[0] && tokl[0] < ntok;
+          r.tiny[j] = r.live[j] && !(sum[j] >= 0x1p-100f);
+          r.any_tiny |= r.tiny[j];
+          r.e[j] = U[0] + __builtin_amdgcn_logf(sum[j]);
         }
-        if (wave_any(any_tiny)) {
+      };
+      auto rec_write = [&](int kb2, RecState& r) {
+        const int tl = tokl[0];
+        if (wave_any(r.any_tiny)) {
           // exact: max and sum of 2^(l - max) over the token's heads, for every value of
           // the lane (all-reduce: every lane takes part in the DPP reductions)
           float ex_own[kOut];
-#pragma unroll
+  #pragma unroll
           for (int j = 0; j < kOut; ++j) ex_own[j] = 0.0f;
-#pragma unroll
+  #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
+  #pragma unroll
             for (int v = 0; v < 4; ++v) {
               float lv[2], rmax[2], ex[2], sums[2];
-#pragma unroll
+  #pragma unroll
               for (int qt = 0; qt < 2; ++qt) lv[qt] = valid[qt] ? l[qt][2 * kb2 + tt][v] * sl2 : kNegInf;
               token_maxes<kGp>(lv, rmax);
-#pragma unroll
+  #pragma unroll
               for (int qt = 0; qt < 2; ++qt) {
                 rmax[qt] = fmaxf(rmax[qt], kMFloor);   // finite: exp2 of -inf is 0
                 ex[qt] = fast_exp2(lv[qt] - rmax[qt]);
               }
               token_sums<kGp>(ex, sums);
               const float val = rmax[0] + __builtin_amdgcn_logf(sums[0]);
-#pragma unroll
+  #pragma unroll
               for (int j = 0; j < kOut; ++j) ex_own[j] = rec_index<kGp>(w16, j) == 4 * tt + v ? val : ex_own[j];
             }
-#pragma unroll
-          for (int j = 0; j < kOut; ++j) e[j] = tiny[j] ? ex_own[j] : e[j];
+  #pragma unroll
+          for (int j = 0; j < kOut; ++j) r.e[j] = r.tiny[j] ? ex_own[j] : r.e[j];
         }
         uint16_t rec[kOut];
-#pragma unroll
-        for (int j = 0; j < kOut; ++j) rec[j] = __builtin_bit_cast(uint16_t, (_Float16)e[j]);
+  #pragma unroll
+        for (int j = 0; j < kOut; ++j) rec[j] = __builtin_bit_cast(uint16_t, (_Float16)r.e[j]);
         uint16_t* rrow = a.records + (sel_tok0 + (int64_t)tl * a.Hkv) * a.logit_stride;
         if constexpr (kOut == 2) {
           // adjacent positions (pos[0] is even): one 4-byte store where both are visible
           // (live[1] implies live[0])
-          if (live[1])
-            *reinterpret_cast<uint32_t*>(rrow + pos[0]) = (uint32_t)rec[0] | ((uint32_t)rec[1] << 16);
-          else if (live[0])
-            rrow[pos[0]] = rec[0];
+          if (r.live[1])
+            *reinterpret_cast<uint32_t*>(rrow + r.pos[0]) = (uint32_t)rec[0] | ((uint32_t)rec[1] << 16);
+          else if (r.live[0])
+            rrow[r.pos[0]] = rec[0];
         } else {
-          if (live[0]) rrow[pos[0]] = rec[0];
+          if (r.live[0]) rrow[r.pos[0]] = rec[0];
         }
-#pragma unroll
+  #pragma unroll
         for (int j = 0; j < kOut; ++j) {
-          if (live[j] && pos[j] < w0j[0]) {
+          if (r.live[j] && r.pos[j] < w0j[0]) {
             const uint32_t bin = half_order_key(rec[j]) >> kFastShift;
             atomicAdd(&shist[tl * kHistWords + (bin >> 1)], (bin & 1) ? 65536u : 1u);
           }
         }
-      }
-      // B operands: P^T of the block, k slot 8 grp + u <-> tile u / 4, position 4 grp + u % 4
-      // (fp8: times the V scale of the position)
-      float vsc[2][4] = {{1.0f, 1.0f, 1.0f, 1.0f}, {1.0f, 1.0f, 1.0f, 1.0f}};
-      if constexpr (kFp8) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const float4 s4 = *reinterpret_cast<const float4*>(stage_scales(it & 1, 1) + (2 * kb2 + tt) * 16 + 4 * grp);
-          vsc[tt][0] = s4.x;
-          vsc[tt][1] = s4.y;
-          vsc[tt][2] = s4.z;
-          vsc[tt][3] = s4.w;
+      };
+      // one matrix-core instruction, then three vector instructions, once per MFMA of a
+      // block's P V (16 fp16 or 32 bf16): the scheduler's order inside the current region
+      auto interleave_pv = [&](auto kHt) {
+        constexpr int kN = decltype(kHt)::value ? 16 : 32;
+  #pragma unroll
+        for (int i = 0; i < kN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
         }
-      }
-      bf16x8_t ph[2], pl[2];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float x0 = p[qt][u >> 1][2 * (u & 1)] * (kFp8 ? vsc[u >> 1][2 * (u & 1)] : 1.0f);
-          const float x1 = p[qt][u >> 1][2 * (u & 1) + 1] * (kFp8 ? vsc[u >> 1][2 * (u & 1) + 1] : 1.0f);
-          hw[u] = pack_bf16(x0, x1);
-          lw[u] = pack_bf16(x0 - __uint_as_float(hw[u] << 16), x1 - __uint_as_float(hw[u] & 0xFFFF0000u));
+      };
+
+      // the two blocks, with P V in fp16 (kHt true) or in the two-part bf16 form
+      auto blocks = [&](auto kHt) {
+        // block 0: V^T operands read ahead (their LDS latency passes under the vector
+        // work), probabilities, operands, records
+        bf16x8_t avp0[kVPre];
+    #pragma unroll
+        for (int d = 0; d < kVPre; ++d) avp0[d] = read_vt(0, d);
+        bf16x8_t ph0[2], pl0[2];
+        RecState r0{}, r1{};
+        {
+          float p0[2][2][4];
+          probabilities(0, p0);
+          operands(kHt, 0, p0, ph0, pl0);
+          if constexpr (want_rec) {
+            float x0[8];
+            rec_sums(p0, x0);
+            rec_reduce(0, x0, r0);
+          }
         }
-        ph[qt] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-        pl[qt] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
-      }
-      if (kb2 == 1 && it + 1 < nit) read_kf(lds + ((it + 1) & 1) * kStage, 0, kpre);
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const bf16x8_t av = d < kVPre ? avp[d < kVPre ? d : 0] : read_vt(d);
-#pragma unroll
+        if constexpr (want_rec) rec_write(0, r0);
+        // block 0's P V with block 1's probabilities, operands and record sums
+        bf16x8_t avp1[kVPre];
+    #pragma unroll
+        for (int d = 0; d < kVPre; ++d) avp1[d] = read_vt(1, d);
+        bf16x8_t ph1[2], pl1[2];
+        float x1[8];
+        {
+          float p1[2][2][4];
+          pv(kHt, 0, avp0, ph0, pl0);
+          probabilities(1, p1);
+          operands(kHt, 1, p1, ph1, pl1);
+          if constexpr (want_rec) rec_sums(p1, x1);
+          interleave_pv(kHt);
+        }
+        // the next iteration's first K fragments (the other stage is complete; on the last
+        // iteration this reads the other stage's stale rows, which nothing uses)
+        read_kf(lds + ((it + 1) & 1) * kStage, 0, kpre);
+        // block 1's P V with its record reduction
+        pv(kHt, 1, avp1, ph1, pl1);
+        if constexpr (want_rec) rec_reduce(1, x1, r1);
+        interleave_pv(kHt);
+        if constexpr (want_rec) rec_write(1, r1);
+      };
+      blocks(kHt);
+      if constexpr (kBlockMode) {
+        // log2 of the sum of 2^logit over this 64-position block, per (token, head)
+  #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-          o[qt][d] = mfma16(av, ph[qt], o[qt][d]);
-          o[qt][d] = mfma16(av, pl[qt], o[qt][d]);
+          const float sum = across_groups<false>(bsum[qt]);
+          const float lse = m[qt] + __builtin_amdgcn_logf(sum);   // -inf for an empty block
+          if (grp == 0 && valid[qt])
+            a.blse[((sel_tok0 + (int64_t)tokl[qt] * a.Hkv) * a.blse_stride + P0 / kCPos) * kGp + head[qt]] = lse;
         }
       }
-      __builtin_amdgcn_s_setprio(0);
+      __syncthreads();   // every wave is done with this stage; the next one is stored
     }
-    if constexpr (kBlockMode) {
-      // log2 of the sum of 2^logit over this 64-position block, per (token, head)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const float sum = across_groups<false>(bsum[qt]);
-        const float lse = m[qt] + __builtin_amdgcn_logf(sum);   // -inf for an empty block
-        if (grp == 0 && valid[qt])
-          a.blse[((sel_tok0 + (int64_t)tokl[qt] * a.Hkv) * a.blse_stride + P0 / kCPos) * kGp + head[qt]] = lse;
+    return true;
+  };
+  bool done = false;
+  if constexpr (kV16) {
+    if (f16v) {
+      done = run_split(std::true_type{});
+      if (!done) {
+        __syncthreads();   // every wave has left the fp16 pass
+        if constexpr (want_rec)
+          for (int i = tid; i < kTPW * kHistWords; i += kCThreads) shist[i] = 0u;
       }
     }
-    __syncthreads();   // every wave is done with this stage; the next one is stored
   }
+  if (!done) run_split(std::false_type{});
 
   // ---- partials per (token, head): O^T dims 16 d + 4 grp .. +3 of the lane's query row
 #pragma unroll

@@ -94,6 +94,8 @@ struct ScanArgs {
                             // reproducible), 0 = waves take steps from a shared counter
   int32_t slot_rows;        // sparse mode: 1 = index entries are rows of a local cache, taken
                             // when 0 <= entry < cap (no visibility limit); 0 = positions < n
+  int32_t exact_pv;         // chunk kernel, bf16 caches: 1 = P V always with the two-part bf16
+                            // split of P; 0 = fp16 V and P where the tile's V fits fp16
 };
 
 struct CombineArgs {

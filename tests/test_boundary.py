@@ -98,7 +98,7 @@ def test_build_id_names_the_current_sources(lib):
     (dict(batch=1100, q_len=64, kv_capacity=4096, max_ctx_len=4096), hs2.HS2_ERR_UNSUPPORTED),
     # options
     (dict(flags=hs2.HS2_FLAGS_ALL & ~(hs2.HS2_FLAG_SPARSE_FUSED | hs2.HS2_FLAG_SPARSE_HEAD)), hs2.HS2_OK),
-    (dict(flags=0x80), hs2.HS2_ERR_INVALID_ARG),                  # unknown flag bit
+    (dict(flags=0x100), hs2.HS2_ERR_INVALID_ARG),                 # unknown flag bit
     (dict(flags=1 << 31), hs2.HS2_ERR_INVALID_ARG),
     (dict(flags=hs2.HS2_FLAG_SPARSE_FUSED | hs2.HS2_FLAG_SPARSE_SPLIT), hs2.HS2_ERR_INVALID_ARG),
     (dict(flags=hs2.HS2_FLAG_SPARSE_HEAD | hs2.HS2_FLAG_SPARSE_SPLIT), hs2.HS2_ERR_INVALID_ARG),
