@@ -99,11 +99,13 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   const f32x2v_t x = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2_t));
 }
-// V tile range for the fp16 form: every |v| below 2^16 (bf16 values there are exact in
-// fp16) and some |v| at least 2^-6 (fp16 subnormals then cost at most 2^-25 absolute,
-// far below the 2^-12 relative rounding of P at that magnitude)
-constexpr float kV16Max = 65536.0f;
-constexpr float kV16Min = 0x1p-6f;
+// V tile range for the fp16 form, on the bf16 magnitude bits: every |v| below 2^16 (bf16
+// values there are exact in fp16; inf and NaN are above) and some |v| at least 2^-6
+// (fp16 subnormals then cost at most 2^-25 absolute, far below the 2^-12 relative
+// rounding of P at that magnitude)
+constexpr uint32_t kV16MaxBits = 0x4780u;   // 2^16
+constexpr uint32_t kV16MinBits = 0x3C80u;   // 2^-6
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 // Reductions over the lanes of one token's heads inside a 16-lane row: 4 lanes (each
 // quad separately), 8 (lanes 0-7 and 8-15 separately) or all 16.
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   constexpr int kTPW = tokens_per_wg<kGp>();
   __shared__ __attribute__((aligned(16))) uint8_t lds[chunk_lds_bytes<kGp, kBlockMode, kFp8>()];
   // bf16 caches: V staged as fp16 unless the caller asks for the two-part form; per stage
-  // and wave, bit 0: some |v| >= kV16Max (or not finite), bit 1: some |v| >= kV16Min
+  // and wave, bit 0: some |v| >= 2^16 (or not finite), bit 1: some |v| >= 2^-6
   constexpr bool kV16 = !kFp8;
   __shared__ uint32_t vflags[2][kCThreads / 64];
   uint32_t* shist = reinterpret_cast<uint32_t*>(lds + 2 * kStage + (kFp8 ? kScaleBytes : 0));
@@ -358,24 +360,24 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
       *reinterpret_cast<uint4*>(st + lrow * kKRow + lcol) = kr0;
       *reinterpret_cast<uint4*>(st + (lrow + 32) * kKRow + lcol) = kr1;
       if constexpr (kH) {
-        // 8 bf16 -> 8 fp16 per store (exact inside the range the flags check)
-        float vmax = 0.0f;
+        // 8 bf16 -> 8 fp16 per store (exact inside the range the flags check); the
+        // largest magnitude bits of each half-word lane
+        u16x2_t mmax = {0, 0};
         auto widen = [&](uint4 w) {
           const uint32_t x[4] = {w.x, w.y, w.z, w.w};
           uint32_t h[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float lo = __uint_as_float(x[i] << 16), hi = __uint_as_float(x[i] & 0xFFFF0000u);
-            vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
-            h[i] = pack_f16(lo, hi);
+            h[i] = pack_f16(__uint_as_float(x[i] << 16), __uint_as_float(x[i] & 0xFFFF0000u));
+            mmax = __builtin_elementwise_max(mmax, __builtin_bit_cast(u16x2_t, x[i] & 0x7FFF7FFFu));
           }
           return make_uint4(h[0], h[1], h[2], h[3]);
         };
         *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + lcol) = widen(vr0);
         *reinterpret_cast<uint4*>(st + kKTile + (lrow + 32) * kVRow + lcol) = widen(vr1);
-        // fmaxf drops NaN: a NaN in V stays NaN in fp16 as in bf16, so both forms agree
-        const bool over = !(vmax < kV16Max);
-        const bool some = vmax >= kV16Min;
+        const uint32_t mm = max((uint32_t)mmax[0], (uint32_t)mmax[1]);
+        const bool over = mm >= kV16MaxBits;
+        const bool some = mm >= kV16MinBits;
         const uint64_t ov = __builtin_amdgcn_ballot_w64(over);
         const uint64_t sm = __builtin_amdgcn_ballot_w64(some);
         if (lane == 0) vflags[stg][wave] = (ov != 0ull ? 1u : 0u) | (sm != 0ull ? 2u : 0u);
