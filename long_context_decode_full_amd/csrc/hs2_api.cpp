@@ -8,6 +8,7 @@
 
 #include "hs2.h"
 #include "hs2_internal.h"
+#include "hs2_swa.h"
 
 #define HS2_API extern "C" __attribute__((visibility("default")))
 
@@ -927,14 +928,32 @@ HS2_API hs2_status hs2_sparse_attn_swa(const hs2_attn_desc* desc, const void* q,
   int32_t* idx_local = reinterpret_cast<int32_t*>(ws + w.off_idx);
   float* out_local = reinterpret_cast<float*>(ws + w.off_out);
   // every check of both branches before anything is enqueued
-  Layout L;
-  s = check_common(desc, q, k, v, k_scale, v_scale, ctx_len, out, idx, workspace, w.attn, &L);
+  Layout Ls, L;   // the shared branch's layout, the local one's
+  s = check_common(desc, q, k, v, k_scale, v_scale, ctx_len, out, idx, workspace, w.attn, &Ls);
   if (s != HS2_OK) return s;
   s = check_common(&w.local, q, k_local, v_local, kl_scale, vl_scale, ctx_len, out_local, idx_local,
                    workspace, w.attn, &L);
   if (s != HS2_OK) return s;
 
   const int64_t n_sel = (int64_t)desc->batch * desc->q_len * desc->n_kv_heads;
+  // Decode sizes (the one-launch sparse layer, no route forced): both branches in one
+  // launch, the window rows derived in the kernel, the outputs added there.  The same
+  // arithmetic as the three-step form below with HS2_FLAG_SPARSE_HEAD.
+  const bool forced = has_flag(desc, HS2_FLAG_SPARSE_FUSED) || has_flag(desc, HS2_FLAG_SPARSE_SPLIT) ||
+                      has_flag(desc, HS2_FLAG_SPARSE_HEAD);
+  if (!forced && n_sel < kHeadPathRows && local_window <= kMaxHeadPathS) {
+    ScanArgs sa = scan_args(desc, Ls, q, k, v, k_scale, v_scale, ctx_len, ws);
+    sa.idx = idx;
+    SwaBranch sw{};
+    sw.k = static_cast<const uint8_t*>(k_local);
+    sw.v = static_cast<const uint8_t*>(v_local);
+    sw.k_scale = kl_scale;
+    sw.v_scale = vl_scale;
+    sw.W = local_window;
+    sw.R = local_rows;
+    const bool fp8 = desc->kv_dtype == HS2_KV_FP8_E4M3FN;
+    return launch_sparse_head_swa(sa, n_sel, out, fp8, sw, stream) == hipSuccess ? HS2_OK : HS2_ERR_LAUNCH;
+  }
   // 1. the block-selected rows of the shared cache
   s = sparse_impl(desc, q, k, v, k_scale, v_scale, ctx_len, idx, out, workspace, w.attn, stream, 0, nullptr);
   if (s != HS2_OK) return s;

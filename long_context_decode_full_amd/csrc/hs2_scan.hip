@@ -34,6 +34,7 @@
 //   units), so rescales are rare.  Streams are merged at the end of the split:
 //   shuffles across the 4 row groups, LDS across the 4 waves.
 #include "hs2_rowops.h"
+#include "hs2_swa.h"
 
 namespace hs2 {
 namespace {
@@ -592,8 +593,9 @@ __device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t (&w)[(N + 
   }
 }
 
-template <bool kFp8, int kDs>
-__global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, int64_t n_sel, float* __restrict__ out) {
+template <bool kFp8, int kDs, bool kSwa>
+__global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, int64_t n_sel, float* __restrict__ out,
+                                                                   SwaBranch sw) {
   constexpr int kDw = kHeadDim / kDs;        // output dims of the workgroup
   constexpr int kDl = kDw / 16;              // V dims of a lane
   constexpr int kVB = kDl * (kFp8 ? 1 : 2);  // V bytes of a lane per row
@@ -629,14 +631,19 @@ __global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, i
   const int64_t qrow = (bj * a.Hq + (int64_t)g * a.G + h) * kHeadDim;
   const uint4 qv = *reinterpret_cast<const uint4*>(a.q + qrow + 8 * r);
   const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-
-  const int64_t head_row0 = (b * a.Hkv + g) * a.cap;
   const int rowbytes = kFp8 ? 128 : 256;
-  const uint8_t* kb = a.k + head_row0 * rowbytes;
-  const uint8_t* vb = a.v + head_row0 * rowbytes + (kDw * ds + kDl * r) * (kFp8 ? 1 : 2);
-  const float* ksb = kFp8 ? a.k_scale + head_row0 : nullptr;
-  const float* vsb = kFp8 ? a.v_scale + head_row0 : nullptr;
+  const int wave = tid >> 6;
   __syncthreads();
+
+  // One attention over the rows sidx[0, S) names in a cache of `cap` rows per (sequence,
+  // KV head); returns, for threads tid < kDw, output dim kDw * ds + tid normalised.
+  auto attend = [&](const uint8_t* kc, const uint8_t* vc, const float* ksc, const float* vsc, int64_t cap,
+                    int S) -> float {
+  const int64_t head_row0 = (b * a.Hkv + g) * cap;
+  const uint8_t* kb = kc + head_row0 * rowbytes;
+  const uint8_t* vb = vc + head_row0 * rowbytes + (kDw * ds + kDl * r) * (kFp8 ? 1 : 2);
+  const float* ksb = kFp8 ? ksc + head_row0 : nullptr;
+  const float* vsb = kFp8 ? vsc + head_row0 : nullptr;
 
   struct Row {
     uint32_t k[kFp8 ? 2 : 4];
@@ -651,7 +658,7 @@ __global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, i
 #pragma unroll
     for (int u = 0; u < kHeadBatch; ++u) {
       const int e = e0 + u * kHeadGroups;
-      t[u] = e < a.S ? sidx[e] : -1;
+      t[u] = e < S ? sidx[e] : -1;
       const uint32_t row = t[u] >= 0 ? (uint32_t)t[u] : 0u;
       load_bytes<kFp8 ? 8 : 16>(kb + (uint64_t)row * rowbytes + (kFp8 ? 8 : 16) * r, d[u].k);
       load_bytes<kVB>(vb + (uint64_t)row * rowbytes, d[u].v);
@@ -711,7 +718,7 @@ __global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, i
       for (int i = 0; i < kDl; ++i) o[i] = __builtin_fmaf(pv, vf[i], o[i]);
     }
   };
-  for (int e0 = gi; e0 < a.S; e0 += kHeadGroups * kHeadBatch) {
+  for (int e0 = gi; e0 < S; e0 += kHeadGroups * kHeadBatch) {
     int32_t t[kHeadBatch];
     Row d[kHeadBatch];
     load_batch(e0, t, d);
@@ -733,7 +740,6 @@ __global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, i
     x += shfl_xor(x, 32);
     o[i] = x;
   }
-  const int wave = tid >> 6;
   if ((tid & 63) < 16) {
     if (r == 0) {
       smz[wave][0] = M;
@@ -743,6 +749,7 @@ __global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, i
     for (int i = 0; i < kDl; ++i) so[wave][kDl * r + i] = o[i];
   }
   __syncthreads();
+  float res = 0.0f;
   if (tid < kDw) {
     float Mw = kNegInf;
     for (int q = 0; q < kHeadWaves; ++q) Mw = fmaxf(Mw, smz[q][0]);
@@ -755,37 +762,71 @@ __global__ __launch_bounds__(kHeadThreads) void sparse_head_kernel(ScanArgs a, i
         acc = __builtin_fmaf(fq, so[q][tid], acc);
       }
     }
-    out[qrow + kDw * ds + tid] = Z > 0.0f ? acc / Z : 0.0f;
+    res = Z > 0.0f ? acc / Z : 0.0f;
   }
+  return res;
+  };
+
+  float res = attend(a.k, a.v, a.k_scale, a.v_scale, a.cap, a.S);
+  if constexpr (kSwa) {
+    // the first-generation comparator's sliding-window branch: the sw.W most recent
+    // visible positions, rows p % sw.R of the layer's own ring, its own softmax; the
+    // two normalised outputs are added
+    __syncthreads();   // every wave is done with sidx, smz and so
+    const int64_t cnt = n < sw.W ? n : sw.W;
+    for (int e = tid; e < sw.W; e += kHeadThreads) sidx[e] = e < cnt ? (int32_t)((n - cnt + e) % sw.R) : -1;
+    __syncthreads();
+    const float loc = attend(sw.k, sw.v, sw.k_scale, sw.v_scale, sw.R, sw.W);
+    res = res + loc;
+  }
+  if (tid < kDw) out[qrow + kDw * ds + tid] = res;
 }
 
-template <bool kFp8>
-void launch_head_ds(const ScanArgs& a, int64_t n_sel, float* out, int ds, unsigned wgs, hipStream_t st,
-                    const KernelEvents* ev) {
+template <bool kFp8, bool kSwa>
+void launch_head_ds(const ScanArgs& a, int64_t n_sel, float* out, int ds, unsigned wgs, const SwaBranch& sw,
+                    hipStream_t st, const KernelEvents* ev) {
   if (ds == 4)
-    launch_on(ev, sparse_head_kernel<kFp8, 4>, dim3(wgs), dim3(kHeadThreads), 0, st, a, n_sel, out);
+    launch_on(ev, sparse_head_kernel<kFp8, 4, kSwa>, dim3(wgs), dim3(kHeadThreads), 0, st, a, n_sel, out, sw);
   else if (ds == 2)
-    launch_on(ev, sparse_head_kernel<kFp8, 2>, dim3(wgs), dim3(kHeadThreads), 0, st, a, n_sel, out);
+    launch_on(ev, sparse_head_kernel<kFp8, 2, kSwa>, dim3(wgs), dim3(kHeadThreads), 0, st, a, n_sel, out, sw);
   else
-    launch_on(ev, sparse_head_kernel<kFp8, 1>, dim3(wgs), dim3(kHeadThreads), 0, st, a, n_sel, out);
+    launch_on(ev, sparse_head_kernel<kFp8, 1, kSwa>, dim3(wgs), dim3(kHeadThreads), 0, st, a, n_sel, out, sw);
 }
 
 }  // namespace
 
-hipError_t launch_sparse_head(const ScanArgs& a, int64_t n_sel, float* out, bool fp8, hipStream_t st,
-                              const KernelEvents* ev) {
+static hipError_t launch_head(const ScanArgs& a, int64_t n_sel, float* out, bool fp8, const SwaBranch* sw,
+                              hipStream_t st, const KernelEvents* ev) {
   if (a.S > kMaxHeadPathS || n_sel < 1 || a.G < 1 || a.G > kMaxHeads) return hipErrorInvalidValue;
+  if (sw != nullptr && (sw->W < 1 || sw->W > kMaxHeadPathS || sw->R < sw->W)) return hipErrorInvalidValue;
   // dim parts: as many as keep every workgroup resident at once (one per CU)
   constexpr int64_t kResident = 256;
   const int64_t heads = n_sel * a.G;
   const int ds = heads * 4 <= kResident ? 4 : heads * 2 <= kResident ? 2 : 1;
   const int64_t wgs = heads * ds;
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (fp8)
-    launch_head_ds<true>(a, n_sel, out, ds, (unsigned)wgs, st, ev);
-  else
-    launch_head_ds<false>(a, n_sel, out, ds, (unsigned)wgs, st, ev);
+  const SwaBranch none{};
+  if (sw != nullptr) {
+    if (fp8)
+      launch_head_ds<true, true>(a, n_sel, out, ds, (unsigned)wgs, *sw, st, ev);
+    else
+      launch_head_ds<false, true>(a, n_sel, out, ds, (unsigned)wgs, *sw, st, ev);
+  } else if (fp8) {
+    launch_head_ds<true, false>(a, n_sel, out, ds, (unsigned)wgs, none, st, ev);
+  } else {
+    launch_head_ds<false, false>(a, n_sel, out, ds, (unsigned)wgs, none, st, ev);
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_sparse_head(const ScanArgs& a, int64_t n_sel, float* out, bool fp8, hipStream_t st,
+                              const KernelEvents* ev) {
+  return launch_head(a, n_sel, out, fp8, nullptr, st, ev);
+}
+
+hipError_t launch_sparse_head_swa(const ScanArgs& a, int64_t n_sel, float* out, bool fp8, const SwaBranch& sw,
+                                  hipStream_t st) {
+  return launch_head(a, n_sel, out, fp8, &sw, st, nullptr);
 }
 
 hipError_t launch_scan_dense(const ScanArgs& a, bool fp8, bool records, int B, hipStream_t st,

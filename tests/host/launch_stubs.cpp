@@ -9,6 +9,7 @@
 #include <cstring>
 
 #include "hs2_internal.h"
+#include "hs2_swa.h"
 
 namespace {
 uintptr_t g_ws_lo = 0, g_ws_hi = 0;
@@ -157,6 +158,16 @@ hipError_t launch_scan_sparse(const ScanArgs& a, bool, int B, hipStream_t, const
 hipError_t launch_sparse_head(const ScanArgs& a, int64_t n_sel, float* out, bool, hipStream_t, const KernelEvents*) {
   if (a.S > kMaxHeadPathS) fail("sparse head: index row beyond its LDS");
   if (n_sel < 1 || out == nullptr) fail("sparse head: rows or output");
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_sparse_head_swa(const ScanArgs& a, int64_t n_sel, float* out, bool fp8, const SwaBranch& sw,
+                                  hipStream_t) {
+  if (a.S > kMaxHeadPathS || sw.W > kMaxHeadPathS) fail("sparse head + window: index rows beyond their LDS");
+  if (n_sel < 1 || out == nullptr) fail("sparse head + window: rows or output");
+  if (sw.W < 1 || sw.R < sw.W) fail("sparse head + window: ring shorter than the window");
+  if (sw.k == nullptr || sw.v == nullptr || (fp8 && (sw.k_scale == nullptr || sw.v_scale == nullptr)))
+    fail("sparse head + window: local cache");
   ++g_launches;
   return hipSuccess;
 }

@@ -57,3 +57,25 @@ def test_gen1_sparse_layers(name):
                     worst = max(worst, assert_out_close(got["out_sparse"][layer][b, j, heads], want,
                                                         what=f"{name} layer {layer} [{b},{j},{g}]"))
     print(f"[gen1] {name}: worst row relative error {worst:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["decode_bf16", "decode_fp8"])
+def test_gen1_decode_one_launch_equals_three_steps(name):
+    """At decode sizes both branches run in one launch (the window rows formed in the
+    kernel, the two normalised outputs added there); the result equals the three-step
+    form that HS2_FLAG_SPARSE_HEAD keeps (shared gather, window rows, local gather, sum)
+    bit for bit, since both take the same arithmetic in the same order."""
+    from long_context_decode_full_amd import HS2_FLAG_SPARSE_HEAD
+    w, R = CASES[name]
+    print(f"\n[gen1] {name}: one launch against three steps", flush=True)
+    inp = wl.make_inputs(w)
+    rings = wl.make_local_rings(w, R, seed=w.seed + 100)
+    outs = []
+    for flags in (0, HS2_FLAG_SPARSE_HEAD):
+        dev = HybridBlockDevice(inp, mode="gen1", local_rings=rings, local_window=W, flags=flags)
+        dev.step()
+        outs.append(dev.results())
+    a, b = outs
+    assert np.array_equal(a["idx"], b["idx"])
+    for layer in range(w.n_sparse_layers):
+        assert np.array_equal(a["out_sparse"][layer], b["out_sparse"][layer]), f"layer {layer}"

@@ -141,6 +141,18 @@ def test_bridge_and_first_generation_launch_sequences(lib):
     st = hs2.hs2_sparse_attn_swa(d, BUF, BUF, BUF, None, None, BUF, BUF, BUF, BUF, None, None, 128, 143, BUF,
                                  WS, need, stream=0)
     _expect_clean(lib, st, "first-generation sparse layer")
+    # decode sizes: both branches in one launch (the window rows formed in the kernel)
+    for fp8 in (False, True):
+        d = hs2.make_desc(2, 1, 32, 4, 9000, 9000, select_mode=hs2.HS2_SELECT_BLOCK,
+                          kv_dtype=hs2.HS2_KV_FP8_E4M3FN if fp8 else hs2.HS2_KV_BF16)
+        st, need = hs2.hs2_sparse_attn_swa_workspace_size(d, 128, 128)
+        assert st == hs2.HS2_OK
+        lib.hs2_stub_set_workspace(WS, need)
+        sc = BUF if fp8 else None
+        st = hs2.hs2_sparse_attn_swa(d, BUF, BUF, BUF, sc, sc, BUF, BUF, BUF, BUF, sc, sc, 128, 128, BUF,
+                                     WS, need, stream=0)
+        _expect_clean(lib, st, f"first-generation sparse layer at decode (fp8={fp8})")
+        assert lib.hs2_stub_launches() == 1
 
 
 def test_stub_catches_a_short_workspace(lib):
