@@ -127,13 +127,13 @@ enum {
   HS2_FLAG_SPARSE_FUSED = 1u << 4,
   HS2_FLAG_SPARSE_SPLIT = 1u << 5,
   HS2_FLAG_SPARSE_HEAD = 1u << 6,
-  /* Query chunks on the matrix-core chunk kernel with bf16 caches: P V with P split
-   * into a bf16 high part and a bf16 residual (two MFMAs, error ~2^-16 relative per
-   * product), the form the decode scan always uses.  By default such a chunk stages V as
-   * fp16 (exact for bf16 values within fp16's range) and rounds P to fp16 (one MFMA,
-   * error <= 2^-12 relative per product); tiles whose V lies outside that range take
-   * the two-part form anyway.  fp8 caches always take the two-part form.  idx never
-   * depends on this flag. */
+  /* Query chunks on the matrix-core chunk kernel: P V with P split into a bf16 high
+   * part and a bf16 residual (two MFMAs, error ~2^-16 relative per product), the form
+   * the decode scan always uses.  By default a chunk stages V as fp16 (bf16 values
+   * exactly within fp16's range; fp8 codes times their row's scale, rounded once) and
+   * rounds P to fp16 (one MFMA, error <= 2^-12 relative per product); a split whose V
+   * lies outside that range takes the two-part form anyway.  idx never depends on this
+   * flag. */
   HS2_FLAG_EXACT_PV = 1u << 7
 };
 #define HS2_FLAGS_ALL 0xFFu

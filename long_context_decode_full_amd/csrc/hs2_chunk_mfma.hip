@@ -25,13 +25,13 @@
 // row (i) and the probabilities are already in the B-operand layout of the second
 // product: O^T = V^T P^T with A = V^T read transposed from the V tile
 // (ds_read_b64_tr_b16, rows 4grp..4grp+3 of two position tiles per lane) and B = the
-// lane's own 8 probabilities of a 32-position block (P never goes through LDS).  With a
-// bf16 cache the V tile is staged as fp16 (exact: a bf16 value below 2^16 in magnitude
-// has 8 significant bits) and P is rounded to fp16, one MFMA per product (error <=
-// 2^-12 relative per term); a split whose V has a tile outside that range (some |v| >=
-// 2^16, or every |v| < 2^-6) starts again with P as a bf16 high part and a bf16
-// residual (two MFMAs, error ~2^-16), the form fp8 caches and HS2_FLAG_EXACT_PV always
-// take.  A block's P V is interleaved with the vector work of the next block (the
+// lane's own 8 probabilities of a 32-position block (P never goes through LDS).  The V
+// tile is staged as fp16 (a bf16 value below 2^16 in magnitude exactly; an fp8 code
+// times its row's scale with one rounding, <= 2^-12) and P is rounded to fp16, one MFMA
+// per product (error <= 2^-12 relative per term); a split whose V has a tile outside
+// that range (some |v| >= 2^16, or every |v| < 2^-6) starts again with P as a bf16 high
+// part and a bf16 residual (two MFMAs, error ~2^-16; fp8: V as exact bf16 codes, the
+// scale on P), the form HS2_FLAG_EXACT_PV always takes.  A block's P V is interleaved with the vector work of the next block (the
 // matrix core and the VALU overlap only in part, so this mostly keeps both busy).
 //   softmax per query row: the lane's 16 values per iteration, the running maximum
 //     raised lazily by 8 (log2 units) with a max over the 4 row groups.
@@ -105,6 +105,9 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 // rounding of P at that magnitude)
 constexpr uint32_t kV16MaxBits = 0x4780u;   // 2^16
 constexpr uint32_t kV16MinBits = 0x3C80u;   // 2^-6
+// the same tests on fp16 bits (fp8 V, scaled and rounded to fp16 as staged)
+constexpr uint32_t kF16InfBits = 0x7C00u;   // inf; NaN above
+constexpr uint32_t kF16MinBits = 0x2400u;   // 2^-6
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 // Reductions over the lanes of one token's heads inside a 16-lane row: 4 lanes (each
@@ -217,9 +220,10 @@ template <int kGp, bool kBlockMode, bool kFp8>
 __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   constexpr int kTPW = tokens_per_wg<kGp>();
   __shared__ __attribute__((aligned(16))) uint8_t lds[chunk_lds_bytes<kGp, kBlockMode, kFp8>()];
-  // bf16 caches: V staged as fp16 unless the caller asks for the two-part form; per stage
-  // and wave, bit 0: some |v| >= 2^16 (or not finite), bit 1: some |v| >= 2^-6
-  constexpr bool kV16 = !kFp8;
+  // V staged as fp16 (bf16 values as they are, fp8 codes times their row's scale) unless
+  // the caller asks for the two-part form; per stage and wave, bit 0: some staged value
+  // out of the fp16 range (or not finite), bit 1: some |v| >= 2^-6
+  constexpr bool kV16 = true;
   __shared__ uint32_t vflags[2][kCThreads / 64];
   uint32_t* shist = reinterpret_cast<uint32_t*>(lds + 2 * kStage + (kFp8 ? kScaleBytes : 0));
   // per-position scales of stage st: K (kv = 0) or V (kv = 1)
@@ -316,12 +320,13 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
   const int lrow = kFp8 ? (tid >> 3) : (tid >> 4);
   const int lcol = kFp8 ? (tid & 7) * 16 : (tid & 15) * 16;
   uint4 kr0, kr1, vr0, vr1;
-  float ksr = 0.0f, vsr = 0.0f;
+  float ksr = 0.0f, vsr = 0.0f, vsrow = 0.0f;   // vsrow: V scale of the row this thread stages (fp8)
   auto load_tiles = [&](int32_t base) {
     const uint32_t row0 = (uint32_t)min(base + lrow, last);
     kr0 = *reinterpret_cast<const uint4*>(kb + (uint64_t)row0 * kRowBytes + lcol);
     vr0 = *reinterpret_cast<const uint4*>(vb + (uint64_t)row0 * kRowBytes + lcol);
     if constexpr (kFp8) {
+      vsrow = vsb[row0];
       if (tid < kCPos) {
         const uint32_t srow = (uint32_t)min(base + tid, last);
         ksr = ksb[srow];
@@ -349,9 +354,34 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
       widen(kr0, lo, hi);
       *reinterpret_cast<uint4*>(st + lrow * kKRow + 2 * lcol) = lo;
       *reinterpret_cast<uint4*>(st + lrow * kKRow + 2 * lcol + 16) = hi;
-      widen(vr0, lo, hi);
-      *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + 2 * lcol) = lo;
-      *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + 2 * lcol + 16) = hi;
+      if constexpr (kH) {
+        // V: 16 codes times the row's scale, rounded to fp16 (one rounding, <= 2^-12
+        // relative); the range test on the fp16 magnitude bits (a value beyond fp16's
+        // range became inf, a NaN code stays NaN: both at or above 0x7C00)
+        u16x2_t mmax = {0, 0};
+        auto scaled = [&](uint32_t c, uint32_t& h0, uint32_t& h1) {
+          const f32x2_t a0 = fp8x2_to_f32(c, false), a1 = fp8x2_to_f32(c, true);
+          h0 = pack_f16(a0[0] * vsrow, a0[1] * vsrow);
+          h1 = pack_f16(a1[0] * vsrow, a1[1] * vsrow);
+          mmax = __builtin_elementwise_max(mmax, __builtin_bit_cast(u16x2_t, h0 & 0x7FFF7FFFu));
+          mmax = __builtin_elementwise_max(mmax, __builtin_bit_cast(u16x2_t, h1 & 0x7FFF7FFFu));
+        };
+        uint32_t h[8];
+        scaled(vr0.x, h[0], h[1]);
+        scaled(vr0.y, h[2], h[3]);
+        scaled(vr0.z, h[4], h[5]);
+        scaled(vr0.w, h[6], h[7]);
+        *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + 2 * lcol) = make_uint4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + 2 * lcol + 16) = make_uint4(h[4], h[5], h[6], h[7]);
+        const uint32_t mm = max((uint32_t)mmax[0], (uint32_t)mmax[1]);
+        const uint64_t ov = __builtin_amdgcn_ballot_w64(mm >= kF16InfBits);
+        const uint64_t sm = __builtin_amdgcn_ballot_w64(mm >= kF16MinBits);
+        if (lane == 0) vflags[stg][wave] = (ov != 0ull ? 1u : 0u) | (sm != 0ull ? 2u : 0u);
+      } else {
+        widen(vr0, lo, hi);
+        *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + 2 * lcol) = lo;
+        *reinterpret_cast<uint4*>(st + kKTile + lrow * kVRow + 2 * lcol + 16) = hi;
+      }
       if (tid < kCPos) {
         stage_scales(stg, 0)[tid] = ksr;
         stage_scales(stg, 1)[tid] = vsr;
@@ -556,7 +586,7 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
       auto operands = [&](auto kHt, int kb2, const float (&p)[2][2][4], bf16x8_t (&ph)[2], bf16x8_t (&pl)[2]) {
         constexpr bool kH = decltype(kHt)::value;
         float vsc[2][4] = {{1.0f, 1.0f, 1.0f, 1.0f}, {1.0f, 1.0f, 1.0f, 1.0f}};
-        if constexpr (kFp8) {
+        if constexpr (kFp8 && !kH) {   // fp16 form: the V scale is in the staged V
   #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             const float4 s4 = *reinterpret_cast<const float4*>(stage_scales(it & 1, 1) + (2 * kb2 + tt) * 16 + 4 * grp);
@@ -571,8 +601,8 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
           uint32_t hw[4], lw[4];
   #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const float x0 = p[qt][u >> 1][2 * (u & 1)] * (kFp8 ? vsc[u >> 1][2 * (u & 1)] : 1.0f);
-            const float x1 = p[qt][u >> 1][2 * (u & 1) + 1] * (kFp8 ? vsc[u >> 1][2 * (u & 1) + 1] : 1.0f);
+            const float x0 = p[qt][u >> 1][2 * (u & 1)] * ((kFp8 && !kH) ? vsc[u >> 1][2 * (u & 1)] : 1.0f);
+            const float x1 = p[qt][u >> 1][2 * (u & 1) + 1] * ((kFp8 && !kH) ? vsc[u >> 1][2 * (u & 1) + 1] : 1.0f);
             if constexpr (kH) {
               hw[u] = pack_f16(x0, x1);
               lw[u] = 0u;

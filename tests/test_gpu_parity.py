@@ -280,6 +280,27 @@ def test_chunk_v_outside_fp16_range(factor):
     assert np.array_equal(got["out_full"], exact["out_full"]), "fp16 pass not given up"
 
 
+@pytest.mark.parametrize("factor", [2.0 ** 18, 2.0 ** -14])
+def test_fp8_chunk_v_scale_outside_fp16_range(factor):
+    """fp8 caches: V is staged as fp16 codes times their row's scale; with every V scale
+    multiplied by 2^18 (some staged value beyond fp16's range in every tile) or 2^-14
+    (every staged value below 2^-6) each split leaves the fp16 pass and runs the
+    two-part form (exact bf16 codes, the scale on P): bitwise equal to
+    HS2_FLAG_EXACT_PV, and both match the oracle."""
+    from long_context_decode_full_amd.runner import HybridBlockDevice
+    w = wl.Workload(f"fp8 chunk v-scale x{factor:g}", 2, 64, 32, 4, ctx_lens=[3000, 7000], kv_dtype="fp8",
+                    n_needles=8, seed=2320)
+    inp = wl.make_inputs(w)
+    inp["v_scale"] = (inp["v_scale"] * np.float32(factor)).astype(np.float32)
+    got, _ = run_and_compare(w, f"fp8-chunk-vscale-{factor:g}", inp=inp,
+                             tokens=[(0, 0), (0, 63), (1, 7), (1, 32), (1, 63)])
+    dev = HybridBlockDevice(inp, flags=HS2_FLAG_EXACT_PV)
+    dev.step()
+    exact = dev.results()
+    assert np.array_equal(got["idx"], exact["idx"])
+    assert np.array_equal(got["out_full"], exact["out_full"]), "fp16 pass not given up"
+
+
 def test_chunk_v_partly_outside_fp16_range():
     """Large V rows in one region of one sequence only: the splits holding them fall back
     to the two-part form, the rest keep fp16; the whole chunk matches the oracle."""
