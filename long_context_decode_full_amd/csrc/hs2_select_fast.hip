@@ -1147,8 +1147,15 @@ hipError_t launch_fast_candidates(const FastSelArgs& a, bool fp8, hipStream_t st
 }
 
 hipError_t launch_fast_final(const FastSelArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((final_kernel<kFinThreads, kFinStage, kFinBnd, kMaxFastChunks>), dim3(a.n_sel),
-                     dim3(kFinThreads), 0, st, a);
+  // Many rows (query chunks): half-size workgroups with a 4,096-key stage (~60 KB of
+  // LDS: two workgroups per CU) for rows of up to 1,024 candidate chunks; larger sets
+  // take the global-memory path of the same kernel.  Few rows: the 1,024-thread form.
+  if (a.n_sel >= kTwoStepMinRows && a.n_chunks <= 1024) {
+    hipLaunchKernelGGL((final_kernel<512, 4096, 1024, 1024>), dim3(a.n_sel), dim3(512), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((final_kernel<kFinThreads, kFinStage, kFinBnd, kMaxFastChunks>), dim3(a.n_sel),
+                       dim3(kFinThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -301,6 +301,17 @@ def test_fp8_chunk_v_scale_outside_fp16_range(factor):
     assert np.array_equal(got["out_full"], exact["out_full"]), "fp16 pass not given up"
 
 
+def test_chunk_many_candidates():
+    """Query chunks (1,024 selection rows, the many-row final stage) whose queries are
+    unrelated to the planted keys: the top-k boundary falls among many similar scores,
+    so long rows keep large candidate sets (5-19K were measured for such queries at the
+    million-token context), the kind that outgrow the stage's 4,096-key LDS copy."""
+    import dataclasses
+    w = dataclasses.replace(wl.Workload("chunk unaligned", 4, 64, 32, 4, ctx_lens=[150000, 60000, 9000, 3000],
+                                        n_needles=8, seed=2330), unaligned_queries=True)
+    run_and_compare(w, "chunk-many-candidates", tokens=[(0, 0), (0, 31), (0, 63), (1, 10), (1, 63), (2, 40), (3, 63)])
+
+
 def test_chunk_v_partly_outside_fp16_range():
     """Large V rows in one region of one sequence only: the splits holding them fall back
     to the two-part form, the rest keep fp16; the whole chunk matches the oracle."""
