@@ -394,11 +394,11 @@ __device__ __forceinline__ int live_splits(const CombineArgs& a, int64_t sel) {
 // rule, and the block merges the 256 states (wave DPP reductions + LDS).  Workgroups
 // with blockIdx.y >= 4 instead sum kHistMergeSplits per-split key histograms
 // (records mode) into the selection's merged histogram.
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  const int sh = blockIdx.x;
+__device__ __forceinline__ void combine_block(const CombineArgs& a, int bx, int by) {
+  const int sh = bx;
   const int sel = sh / a.G;
   const int h = sh - sel * a.G;
-  const int chunk = blockIdx.y + (a.hist_only ? kHeadDim / 32 : 0);
+  const int chunk = by + (a.hist_only ? kHeadDim / 32 : 0);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -525,9 +525,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 // itself, four splits of loads in flight; no cross-thread reduction.
 constexpr int kSmallSplits = 32;
 constexpr int64_t kSmallPairs = 8192;   // (row, head) pairs from which rows give the parallelism
-__global__ __launch_bounds__(256) void combine_small_kernel(CombineArgs a) {
+__device__ __forceinline__ void combine_small_block(const CombineArgs& a, int64_t bx) {
   const int tid = threadIdx.x;
-  const int64_t pair = (int64_t)blockIdx.x * 8 + (tid >> 5);   // sel * G + h
+  const int64_t pair = bx * 8 + (tid >> 5);   // sel * G + h
   const int dq = tid & 31;
   if (pair >= (int64_t)a.n_sel * a.G) return;
   const int sel = (int)(pair / a.G);
@@ -548,6 +548,22 @@ __global__ __launch_bounds__(256) void combine_small_kernel(CombineArgs a) {
   if (a.sel_zero != nullptr && h == 0) {
     uint32_t* zp = a.sel_zero + (int64_t)sel * a.sel_zero_words;
     for (int w = dq; w < a.sel_zero_words; w += 32) zp[w] = 0u;
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) { combine_block(a, blockIdx.x, blockIdx.y); }
+__global__ __launch_bounds__(256) void combine_small_kernel(CombineArgs a) { combine_small_block(a, blockIdx.x); }
+// Both folds of a many-row call in one launch: blocks [0, n_small) fold the output
+// partials (combine_small_block), the rest merge the key histograms (combine_block with
+// h.hist_only), hist_x of them per histogram group; the two halves run side by side.
+__global__ __launch_bounds__(256) void combine_pair_kernel(CombineArgs a, CombineArgs h, uint32_t n_small,
+                                                           uint32_t hist_x) {
+  const uint32_t b = blockIdx.x;
+  if (b < n_small) {
+    combine_small_block(a, b);
+  } else {
+    const uint32_t k = b - n_small;
+    combine_block(h, (int)(k % hist_x), (int)(k / hist_x));
   }
 }
 
@@ -860,11 +876,17 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   const int extra = a.hist_part != nullptr ? (n_groups + a.G - 1) / a.G : 0;
   if (a.n_split <= kSmallSplits || (int64_t)a.n_sel * a.G >= kSmallPairs) {
     const int64_t pairs = (int64_t)a.n_sel * a.G;
-    hipLaunchKernelGGL(combine_small_kernel, dim3((unsigned)((pairs + 7) / 8)), dim3(256), 0, st, a);
-    if (extra > 0) {   // histogram merge only
+    const int64_t n_small = (pairs + 7) / 8;
+    if (extra > 0) {   // and the histogram merge, in the same launch
       CombineArgs h = a;
       h.hist_only = 1;
-      hipLaunchKernelGGL(combine_kernel, dim3(a.n_sel * a.G, extra), dim3(256), 0, st, h);
+      const int64_t hist_x = (int64_t)a.n_sel * a.G;
+      const int64_t total = n_small + hist_x * extra;
+      if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(combine_pair_kernel, dim3((unsigned)total), dim3(256), 0, st, a, h, (uint32_t)n_small,
+                         (uint32_t)hist_x);
+    } else {
+      hipLaunchKernelGGL(combine_small_kernel, dim3((unsigned)n_small), dim3(256), 0, st, a);
     }
     return hipGetLastError();
   }
