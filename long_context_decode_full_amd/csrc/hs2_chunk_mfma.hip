@@ -457,7 +457,9 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
       // previous iteration before the barrier that ended it), then the loads after them
       store_tiles((it + 1) & 1, kHt);
       load_tiles(P0 + 2 * kCPos);
-      __syncthreads();   // the next stage is complete
+      // this stage is complete (its stores came before the barrier that ended the last
+      // iteration); its first K fragments
+      if (it > 0) read_kf(ks, 0, kpre);
       if constexpr (kH) {
         // this stage's V outside the fp16 range: the split is given up (every wave reads
         // the same flags here, right after the barrier, so all leave together)
@@ -756,9 +758,6 @@ __global__ __launch_bounds__(kCThreads, 1) void chunk_mfma_kernel(ScanArgs a) {
           if constexpr (want_rec) rec_sums(p1, x1);
           interleave_pv(kHt);
         }
-        // the next iteration's first K fragments (the other stage is complete; on the last
-        // iteration this reads the other stage's stale rows, which nothing uses)
-        read_kf(lds + ((it + 1) & 1) * kStage, 0, kpre);
         // block 1's P V with its record reduction
         pv(kHt, 1, avp1, ph1, pl1);
         if constexpr (want_rec) rec_reduce(1, x1, r1);
