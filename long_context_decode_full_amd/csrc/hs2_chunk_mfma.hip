@@ -13,9 +13,8 @@
 // 256 / kGp tokens of kGp head slots each (kGp = 8, 16 or 32: the group size rounded
 // up; slots >= G are zero), so it reads every K/V row of its split once for all of
 // them.  Per iteration of 64 positions the K and V tiles go through LDS (two stages:
-// the next tiles are stored while the current ones are read; one barrier after those
-// stores, so that the first K fragments of the next tile can be read during the
-// current one, and one at the end of the iteration); fp8 K codes are widened to bf16
+// the next tiles are stored while the current ones are read; one barrier, at the end of
+// the iteration, which also completes the stores of the stage the next one reads); fp8 K codes are widened to bf16
 // as they are staged (V: see below).  Wave w owns 32 / kGp tokens as two query tiles of 16 rows, a
 // token's heads spread over both tiles (head = (kGp / 2) tile + lane % (kGp / 2)).
 // The scores are formed transposed, S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K
